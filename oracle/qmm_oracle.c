@@ -1,0 +1,521 @@
+/*
+ * qmm oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, scalar C implementation of the block-quantized weight x
+ * Q8_0 / Q8_K activation product.  Only the test suite, the smoke check and
+ * the CPU-baseline leg of the benchmark may load it.  It shares no source,
+ * header, table or helper with the HIP library; the two meet only at the
+ * byte layouts the pages define.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math (SSE arithmetic, so every
+ * float operation below is one correctly rounded IEEE binary32 operation).
+ *
+ * Sources (page titles; each function names the part it follows):
+ *   [minfer]  "10 . CPU matmul: quantized weights x Q8_0 activations"
+ *   [ggml]    "ggml Q4_0 vec_dot Walkthrough"
+ *   [krafla]  "Architecture" (krafla)
+ *   [kvad]    "kvad -- the same ideas, at scale"
+ *
+ * Readings taken where the pages are silent, garbled or disagree are listed
+ * in the repository design notes; the ones that shape arithmetic here are
+ * repeated at the function that applies them.
+ *
+ * Parity status: every exported function is pinned by a CPU test (values the
+ * pages print, closed forms, invariants, a library routine or brute force),
+ * except the Q2_K weight quantizer, whose rule the pages do not give at all:
+ * its output bytes are only test data, and its rule is "parity unpinned"
+ * (only the invariants of the format it must produce are checked).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define QK 32       /* values per Q4_0 / Q8_0 block                  */
+#define QKK 256     /* values per Q2_K / Q8_K super-block            */
+#define Q4_0_BYTES 18
+#define Q8_0_BYTES 34
+#define Q2_K_BYTES 84
+#define Q8_K_BYTES 292
+
+/* ------------------------------------------------------------------ */
+/* IEEE binary16 <-> binary32                                          */
+/* ------------------------------------------------------------------ */
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* binary16 -> binary32, exact for every finite half, inf and NaN. */
+float orc_f16_to_f32(uint16_t h) {
+    uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1fu;
+    uint32_t m = h & 0x3ffu;
+    if (e == 0) {
+        /* zero or subnormal: m * 2^-24, exact in binary32 */
+        float v = (float)m * 0x1p-24f;
+        return sign ? -v : v;
+    }
+    if (e == 31) return bits_f32(sign | 0x7f800000u | (m << 13));
+    return bits_f32(sign | ((e + 112u) << 23) | (m << 13));
+}
+
+/* binary32 -> binary16, round to nearest, ties to even, with subnormals.
+ * The scales are stored as f16 of an f32 value ([minfer] quantize_avx2:
+ * "f16(d)"); IEEE's default rounding is the reading. Values at or above
+ * 65520 in magnitude become infinity (outside the contract of the method). */
+uint16_t orc_f32_to_f16(float f) {
+    uint32_t x = f32_bits(f);
+    uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);
+    x &= 0x7fffffffu;
+    if (x >= 0x7f800000u) return sign | (x > 0x7f800000u ? 0x7e00u : 0x7c00u);
+    if (x >= 0x477ff000u) return sign | 0x7c00u;          /* >= 65520 */
+    if (x < 0x33000000u) return sign;                      /* < 2^-25  */
+    uint32_t e = x >> 23;
+    uint32_t mant = (x & 0x7fffffu) | 0x800000u;
+    uint32_t r, rem, half;
+    if (e >= 113u) {                                       /* normal half */
+        r = ((e - 112u) << 10) | ((mant >> 13) & 0x3ffu);
+        rem = mant & 0x1fffu;
+        half = 0x1000u;
+    } else {                                               /* subnormal half */
+        uint32_t sh = 126u - e;                            /* 14 .. 24 */
+        r = mant >> sh;
+        rem = mant & ((1u << sh) - 1u);
+        half = 1u << (sh - 1u);
+    }
+    if (rem > half || (rem == half && (r & 1u))) r += 1u;  /* may carry into exponent */
+    return sign | (uint16_t)r;
+}
+
+static float rd_f16(const uint8_t *p) { return orc_f16_to_f32((uint16_t)(p[0] | (p[1] << 8))); }
+static void wr_f16(uint8_t *p, float v) { uint16_t h = orc_f32_to_f16(v); p[0] = (uint8_t)h; p[1] = (uint8_t)(h >> 8); }
+static float rd_f32(const uint8_t *p) { float v; memcpy(&v, p, 4); return v; }
+
+/* Round to nearest integer, ties to even, computed without relying on the
+ * floating-point environment: for |v| < 2^23 the value floor(v) is exact and
+ * v - floor(v) is exact, so the comparison with 0.5 is exact. */
+static float rne(float v) {
+    if (!(fabsf(v) < 8388608.0f)) return v;               /* already integral */
+    float fl = floorf(v);
+    float frac = v - fl;
+    if (frac > 0.5f) return fl + 1.0f;
+    if (frac < 0.5f) return fl;
+    return (fmodf(fl, 2.0f) == 0.0f) ? fl : fl + 1.0f;     /* tie: to even */
+}
+
+/* ------------------------------------------------------------------ */
+/* Activation quantizers                                               */
+/* ------------------------------------------------------------------ */
+
+/* Q8_0, per 32 values ([minfer] "The activation quantizers", the
+ * quantize_avx2 listing; [ggml] section 1.1; [krafla] "Numerics": the rule
+ * is written as exact float32 operations):
+ *   amax = max |x_j|;  d = amax / 127 (f32), stored as f16;
+ *   id = amax != 0 ? 127 / amax : 0;   q_j = round-to-nearest-even(x_j * id).
+ * Block: f16 d (little-endian) at byte 0, int8 q[32] at bytes 2..33.
+ * Reading: the inverse scale is 127/amax (the only form printed as code);
+ * ties go to even (_MM_ROUND_NEAREST); no clamp (|q| <= 127 always holds). */
+void orc_quantize_q8_0(const float *x, uint8_t *out, int64_t M, int64_t K) {
+    int64_t nb = K / QK;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *xb = x + m * K + b * QK;
+            uint8_t *ob = out + (m * nb + b) * Q8_0_BYTES;
+            float amax = 0.0f;
+            for (int j = 0; j < QK; ++j) {
+                float a = fabsf(xb[j]);
+                if (a > amax) amax = a;
+            }
+            float d = amax / 127.0f;
+            float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;
+            wr_f16(ob, d);
+            for (int j = 0; j < QK; ++j) {
+                float v = xb[j] * id;
+                ob[2 + j] = (uint8_t)(int8_t)(int)rne(v);
+            }
+        }
+    }
+}
+
+/* Q8_K, per 256 values ([minfer] quantize_row_q8_k_buf_neon listing and the
+ * three details after it): amax; d = amax / 127; q_i = saturate[-128,127]
+ * (round(x_i * id)); bsums[g] = sum of the 16 saturated codes of group g.
+ * Reading: d is stored as f32 (the ggml-style "f32 d" struct the same page
+ * mentions), layout d @0, int8 q[256] @4, int16 bsums[16] @260 = 292 bytes. */
+void orc_quantize_q8_k(const float *x, uint8_t *out, int64_t M, int64_t K) {
+    int64_t ns = K / QKK;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t s = 0; s < ns; ++s) {
+            const float *xb = x + m * K + s * QKK;
+            uint8_t *ob = out + (m * ns + s) * Q8_K_BYTES;
+            float amax = 0.0f;
+            for (int i = 0; i < QKK; ++i) {
+                float a = fabsf(xb[i]);
+                if (a > amax) amax = a;
+            }
+            float d = amax / 127.0f;
+            float id = (amax != 0.0f) ? 127.0f / amax : 0.0f;
+            memcpy(ob, &d, 4);
+            int8_t q[QKK];
+            for (int i = 0; i < QKK; ++i) {
+                float r = rne(xb[i] * id);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -128.0f) r = -128.0f;
+                q[i] = (int8_t)(int)r;
+                ob[4 + i] = (uint8_t)q[i];
+            }
+            for (int g = 0; g < 16; ++g) {
+                int sum = 0;
+                for (int i = 0; i < 16; ++i) sum += q[16 * g + i];
+                int16_t s16 = (int16_t)sum;
+                memcpy(ob + 260 + 2 * g, &s16, 2);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Weight quantizers (test-data generation)                            */
+/* ------------------------------------------------------------------ */
+
+/* Q4_0, per 32 weights ([ggml] section 1.1, quantize_row_q4_0_ref prose;
+ * [kvad] "The scale that wasted a code"): take the value of largest
+ * magnitude with its sign (first index on ties), d = max / -8, so that value
+ * lands on code 0; code_j = clamp(round(x_j / d) + 8, 0, 15); f16 d stored.
+ * Packing ([ggml] section 2 probe, [minfer] scalar kernel): byte j of qs
+ * holds element j in its low nibble and element j+16 in its high nibble.
+ * Readings: the division uses the f32 d; round is to nearest, ties to even;
+ * an all-zero block gets d = 0 and every code 8. */
+void orc_quantize_q4_0_w(const float *w, uint8_t *out, int64_t N, int64_t K) {
+    int64_t nb = K / QK;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *xb = w + n * K + b * QK;
+            uint8_t *ob = out + (n * nb + b) * Q4_0_BYTES;
+            float amax = 0.0f, mx = 0.0f;
+            for (int j = 0; j < QK; ++j) {
+                float a = fabsf(xb[j]);
+                if (a > amax) { amax = a; mx = xb[j]; }
+            }
+            float d = (amax != 0.0f) ? mx / -8.0f : 0.0f;   /* +0 for a zero block */
+            wr_f16(ob, d);
+            int code[QK];
+            for (int j = 0; j < QK; ++j) {
+                int c = 8;
+                if (d != 0.0f) c = (int)rne(xb[j] / d) + 8;
+                if (c < 0) c = 0;
+                if (c > 15) c = 15;
+                code[j] = c;
+            }
+            for (int j = 0; j < 16; ++j) ob[2 + j] = (uint8_t)(code[j] | (code[j + 16] << 4));
+        }
+    }
+}
+
+/* Q2_K, per 256 weights in 16 groups of 16 (format: [ggml] section 1.2:
+ * scales[16] (low nibble sc, high nibble m), qs[64], f16 d, f16 dmin; a
+ * weight decodes as d*sc*q - dmin*m).  The pages give no quantizer; this is
+ * the simplest rule that fills the format:
+ *   per group: lo = min(0, min x), hi = max x, s = (hi - lo) / 3, mn = -lo;
+ *   d = max_g s / 15, dmin = max_g mn / 15 (stored f16);
+ *   sc = clamp(round(s / f16(d)), 0, 15), m = clamp(round(mn / f16(dmin)), 0, 15);
+ *   q = clamp(round((x + f16(dmin) * m) / (f16(d) * sc)), 0, 3), 0 if the divisor is 0.
+ * Bit order of qs (not on the pages; the reading shared by both sides):
+ * byte 32h + l holds, at bit shift 2s, the code of weight 128h + 32s + l. */
+void orc_quantize_q2_k_w(const float *w, uint8_t *out, int64_t N, int64_t K) {
+    int64_t ns = K / QKK;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t sb = 0; sb < ns; ++sb) {
+            const float *xb = w + n * K + sb * QKK;
+            uint8_t *ob = out + (n * ns + sb) * Q2_K_BYTES;
+            float s[16], mn[16];
+            float smax = 0.0f, mnmax = 0.0f;
+            for (int g = 0; g < 16; ++g) {
+                float lo = 0.0f, hi = xb[16 * g];
+                for (int i = 0; i < 16; ++i) {
+                    float v = xb[16 * g + i];
+                    if (v < lo) lo = v;
+                    if (v > hi) hi = v;
+                }
+                s[g] = (hi - lo) / 3.0f;
+                mn[g] = -lo;
+                if (s[g] > smax) smax = s[g];
+                if (mn[g] > mnmax) mnmax = mn[g];
+            }
+            float d = smax / 15.0f, dmin = mnmax / 15.0f;
+            wr_f16(ob + 80, d);
+            wr_f16(ob + 82, dmin);
+            float dh = rd_f16(ob + 80), dminh = rd_f16(ob + 82);
+            int sc[16], mm[16];
+            for (int g = 0; g < 16; ++g) {
+                int a = 0, c = 0;
+                if (dh != 0.0f) a = (int)rne(s[g] / dh);
+                if (dminh != 0.0f) c = (int)rne(mn[g] / dminh);
+                sc[g] = a < 0 ? 0 : (a > 15 ? 15 : a);
+                mm[g] = c < 0 ? 0 : (c > 15 ? 15 : c);
+                ob[g] = (uint8_t)(sc[g] | (mm[g] << 4));
+            }
+            uint8_t q[QKK];
+            for (int i = 0; i < QKK; ++i) {
+                int g = i / 16;
+                float off = dminh * (float)mm[g];
+                float div = dh * (float)sc[g];
+                int c = 0;
+                if (div != 0.0f) c = (int)rne((xb[i] + off) / div);
+                q[i] = (uint8_t)(c < 0 ? 0 : (c > 3 ? 3 : c));
+            }
+            memset(ob + 16, 0, 64);
+            for (int i = 0; i < QKK; ++i) {
+                int h = i / 128, sft = (i % 128) / 32, l = i % 32;
+                ob[16 + 32 * h + l] |= (uint8_t)(q[i] << (2 * sft));
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Decoders (each value exact in double)                               */
+/* ------------------------------------------------------------------ */
+
+/* Q8_0 value = d * q ([ggml] section 1.1). */
+void orc_dequantize_q8_0(const uint8_t *blk, double *out, int64_t rows, int64_t K) {
+    int64_t nb = K / QK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *p = blk + (r * nb + b) * Q8_0_BYTES;
+            double d = rd_f16(p);
+            for (int j = 0; j < QK; ++j) out[r * K + b * QK + j] = d * (double)(int8_t)p[2 + j];
+        }
+}
+
+/* Q4_0 value = d * (nibble - 8); low nibble of byte j is element j, high
+ * nibble is element j+16 ([minfer] scalar kernel and its worked byte 0x21;
+ * [ggml] section 2). */
+void orc_dequantize_q4_0(const uint8_t *blk, double *out, int64_t rows, int64_t K) {
+    int64_t nb = K / QK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *p = blk + (r * nb + b) * Q4_0_BYTES;
+            double d = rd_f16(p);
+            for (int j = 0; j < 16; ++j) {
+                out[r * K + b * QK + j] = d * (double)((p[2 + j] & 0x0f) - 8);
+                out[r * K + b * QK + j + 16] = d * (double)((p[2 + j] >> 4) - 8);
+            }
+        }
+}
+
+/* Q2_K value = d * sc_g * q - dmin * m_g, g = i / 16 ([ggml] section 1.2). */
+void orc_dequantize_q2_k(const uint8_t *blk, double *out, int64_t rows, int64_t K) {
+    int64_t ns = K / QKK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t sb = 0; sb < ns; ++sb) {
+            const uint8_t *p = blk + (r * ns + sb) * Q2_K_BYTES;
+            double d = rd_f16(p + 80), dmin = rd_f16(p + 82);
+            for (int i = 0; i < QKK; ++i) {
+                int g = i / 16, h = i / 128, sft = (i % 128) / 32, l = i % 32;
+                int q = (p[16 + 32 * h + l] >> (2 * sft)) & 3;
+                int sc = p[g] & 0x0f, m = p[g] >> 4;
+                out[r * K + sb * QKK + i] = d * sc * q - dmin * m;
+            }
+        }
+}
+
+/* Q8_K value = d * q with f32 d. */
+void orc_dequantize_q8_k(const uint8_t *blk, double *out, int64_t rows, int64_t K) {
+    int64_t ns = K / QKK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t sb = 0; sb < ns; ++sb) {
+            const uint8_t *p = blk + (r * ns + sb) * Q8_K_BYTES;
+            double d = rd_f32(p);
+            for (int i = 0; i < QKK; ++i) out[r * K + sb * QKK + i] = d * (double)(int8_t)p[4 + i];
+        }
+}
+
+/* ------------------------------------------------------------------ */
+/* Block dot products                                                  */
+/* ------------------------------------------------------------------ */
+
+/* One output of a row against one activation row, as the pages define it
+ * ([ggml] section 2, right-hand listing; [minfer] scalar kernel; [krafla]
+ * "Data flow": the int32 block sum is scaled by d_w * d_x):
+ *   y = sum_b d_w[b] * d_x[b] * I_b,   I_b = sum_j w_j * q_j  (exact int32).
+ * Terms are formed and summed in double (each term is exact in double);
+ * `mag` receives sum_b |d_w d_x| sum_j |w_j q_j|, the magnitude the
+ * tolerance is relative to ([krafla] "Numerics": agreement within 1e-5 of the
+ * dot product's magnitude). */
+static void dot_q4_0_q8_0(const uint8_t *w, const uint8_t *x, int64_t nb, double *y, double *mag) {
+    double s = 0.0, a = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *wb = w + b * Q4_0_BYTES, *xb = x + b * Q8_0_BYTES;
+        int32_t isum = 0, iabs = 0;
+        for (int j = 0; j < 16; ++j) {
+            int v0 = (wb[2 + j] & 0x0f) - 8, v1 = (wb[2 + j] >> 4) - 8;
+            int q0 = (int8_t)xb[2 + j], q1 = (int8_t)xb[2 + j + 16];
+            isum += v0 * q0 + v1 * q1;
+            iabs += abs(v0 * q0) + abs(v1 * q1);
+        }
+        double sc = (double)rd_f16(wb) * (double)rd_f16(xb);
+        s += sc * (double)isum;
+        a += fabs(sc) * (double)iabs;
+    }
+    *y = s;
+    if (mag) *mag = a;
+}
+
+/* Q8_0 weights: the same with int8 weight codes ([minfer] Q8_0 kernel). */
+static void dot_q8_0_q8_0(const uint8_t *w, const uint8_t *x, int64_t nb, double *y, double *mag) {
+    double s = 0.0, a = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *wb = w + b * Q8_0_BYTES, *xb = x + b * Q8_0_BYTES;
+        int32_t isum = 0, iabs = 0;
+        for (int j = 0; j < QK; ++j) {
+            int p = (int8_t)wb[2 + j] * (int8_t)xb[2 + j];
+            isum += p;
+            iabs += abs(p);
+        }
+        double sc = (double)rd_f16(wb) * (double)rd_f16(xb);
+        s += sc * (double)isum;
+        a += fabs(sc) * (double)iabs;
+    }
+    *y = s;
+    if (mag) *mag = a;
+}
+
+/* Q2_K x Q8_K, per super-block: the two-term form of the K-quant dot
+ * ([minfer] "The payoff: a K-quant dot kernel, walked": the min term is a sum
+ * over activations only, carried by bsums):
+ *   V  = sum_g sc_g * sum_{i in g} q_i * x_i,  Mn = sum_g m_g * bsums_g,
+ *   t  = d * d8 * V - dmin * d8 * Mn. */
+static void dot_q2_k_q8_k(const uint8_t *w, const uint8_t *x, int64_t ns, double *y, double *mag) {
+    double s = 0.0, a = 0.0;
+    for (int64_t sb = 0; sb < ns; ++sb) {
+        const uint8_t *wb = w + sb * Q2_K_BYTES, *xb = x + sb * Q8_K_BYTES;
+        double d = rd_f16(wb + 80), dmin = rd_f16(wb + 82), d8 = rd_f32(xb);
+        int64_t V = 0, Mn = 0;
+        double aa = 0.0;
+        for (int g = 0; g < 16; ++g) {
+            int sc = wb[g] & 0x0f, m = wb[g] >> 4;
+            int32_t gs = 0;
+            for (int t = 0; t < 16; ++t) {
+                int i = 16 * g + t, h = i / 128, sft = (i % 128) / 32, l = i % 32;
+                int q = (wb[16 + 32 * h + l] >> (2 * sft)) & 3;
+                int qx = (int8_t)xb[4 + i];
+                gs += q * qx;
+                aa += (fabs(d * sc * q) + fabs(dmin * m)) * fabs(d8 * qx);
+            }
+            int16_t bs;
+            memcpy(&bs, xb + 260 + 2 * g, 2);
+            V += (int64_t)sc * gs;
+            Mn += (int64_t)m * bs;
+        }
+        s += d * d8 * (double)V - dmin * d8 * (double)Mn;
+        a += aa;
+    }
+    *y = s;
+    if (mag) *mag = a;
+}
+
+enum { ORC_Q4_0 = 0, ORC_Q8_0 = 1, ORC_Q2_K = 2 };
+
+static void dot_any(int fmt, const uint8_t *w, const uint8_t *x, int64_t K, double *y, double *mag) {
+    if (fmt == ORC_Q4_0) dot_q4_0_q8_0(w, x, K / QK, y, mag);
+    else if (fmt == ORC_Q8_0) dot_q8_0_q8_0(w, x, K / QK, y, mag);
+    else dot_q2_k_q8_k(w, x, K / QKK, y, mag);
+}
+
+static int64_t w_row_bytes(int fmt, int64_t K) {
+    if (fmt == ORC_Q4_0) return K / QK * Q4_0_BYTES;
+    if (fmt == ORC_Q8_0) return K / QK * Q8_0_BYTES;
+    return K / QKK * Q2_K_BYTES;
+}
+static int64_t x_row_bytes(int fmt, int64_t K) {
+    if (fmt == ORC_Q2_K) return K / QKK * Q8_K_BYTES;
+    return K / QK * Q8_0_BYTES;
+}
+
+/* ------------------------------------------------------------------ */
+/* Matrix products                                                     */
+/* ------------------------------------------------------------------ */
+
+/* out[t][o] = dot(w row o, x row t): token-major output [M][N], each element
+ * written once ([minfer] mm_rows listing and "Pitfalls": the output is
+ * [nt][od]).  Work is split by output rows across threads; each element is
+ * computed by one thread in one fixed order, so the result does not depend
+ * on the thread count ([minfer] "Read the loop order carefully"). */
+typedef struct {
+    int fmt; const uint8_t *w, *x; float *y; double *y64, *mag;
+    int64_t M, N, K, n0, n1;
+} orc_job;
+
+static void *orc_rows(void *arg) {
+    orc_job *j = (orc_job *)arg;
+    int64_t wr = w_row_bytes(j->fmt, j->K), xr = x_row_bytes(j->fmt, j->K);
+    for (int64_t o = j->n0; o < j->n1; ++o)
+        for (int64_t t = 0; t < j->M; ++t) {
+            double v, a;
+            dot_any(j->fmt, j->w + o * wr, j->x + t * xr, j->K, &v, &a);
+            if (j->y) j->y[t * j->N + o] = (float)v;
+            if (j->y64) j->y64[t * j->N + o] = v;
+            if (j->mag) j->mag[t * j->N + o] = a;
+        }
+    return NULL;
+}
+
+/* fmt: 0 = Q4_0 weights x Q8_0, 1 = Q8_0 x Q8_0, 2 = Q2_K x Q8_K.
+ * y (f32), y64 (double) and mag (double) are [M][N]; any may be NULL. */
+int orc_matmul(int fmt, const uint8_t *w, const uint8_t *x, float *y, double *y64, double *mag,
+               int64_t M, int64_t N, int64_t K, int threads) {
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    if (threads > N) threads = (int)N;
+    orc_job jobs[256];
+    pthread_t tid[256];
+    for (int i = 0; i < threads; ++i) {
+        jobs[i] = (orc_job){fmt, w, x, y, y64, mag, M, N, K, N * i / threads, N * (i + 1) / threads};
+    }
+    int started = 0;
+    for (int i = 1; i < threads; ++i) {
+        if (pthread_create(&tid[i], NULL, orc_rows, &jobs[i]) != 0) break;
+        started = i;
+    }
+    orc_rows(&jobs[0]);
+    for (int i = 1; i <= started; ++i) pthread_join(tid[i], NULL);
+    for (int i = started + 1; i < threads; ++i) orc_rows(&jobs[i]);   /* any thread that failed to start */
+    return 0;
+}
+
+/* Selected outputs (mi[c], ni[c]) of the same product: for checking a full
+ * size GPU result on a sample of its elements. */
+int orc_matmul_sampled(int fmt, const uint8_t *w, const uint8_t *x, const int64_t *mi, const int64_t *ni,
+                       int64_t count, double *y64, double *mag, int64_t K) {
+    int64_t wr = w_row_bytes(fmt, K), xr = x_row_bytes(fmt, K);
+    for (int64_t c = 0; c < count; ++c) {
+        double v, a;
+        dot_any(fmt, w + ni[c] * wr, x + mi[c] * xr, K, &v, &a);
+        y64[c] = v;
+        if (mag) mag[c] = a;
+    }
+    return 0;
+}
+
+/* Single block dot, for the pins: returns the exact integer sum of one
+ * Q4_0 x Q8_0 (fmt 0) or Q8_0 x Q8_0 (fmt 1) block pair. */
+int32_t orc_block_isum(int fmt, const uint8_t *w, const uint8_t *x) {
+    int32_t isum = 0;
+    for (int j = 0; j < QK; ++j) {
+        int wv;
+        if (fmt == ORC_Q4_0) wv = (j < 16 ? (w[2 + j] & 0x0f) : (w[2 + j - 16] >> 4)) - 8;
+        else wv = (int8_t)w[2 + j];
+        isum += wv * (int8_t)x[2 + j];
+    }
+    return isum;
+}
+
+/* Element-wise conversions over arrays (for the exhaustive fp16 pins). */
+void orc_f32_to_f16_array(const float *x, uint16_t *h, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) h[i] = orc_f32_to_f16(x[i]);
+}
+void orc_f16_to_f32_array(const uint16_t *h, float *x, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) x[i] = orc_f16_to_f32(h[i]);
+}

@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-product hot path on one MI355X.
+
+Headline (one JSON line on stdout): Q4_0 x Q8_0 decode at the FFN-gate shape,
+M = 1, N = 12288, K = 4096.  One step = quantize the f32 activation to Q8_0
+on the GPU + the matvec over one copy of the 28.3 MB weight matrix.  Steps
+rotate over enough byte-identical weight copies (>= 512 MB) that every step
+streams its weights from HBM, not from the 256 MB last-level cache.
+`value` is weight bytes per step / step time (GB/s), inputs resident in HBM.
+
+Also in the line: the prefill matmul (M = 2048, same weights), int8 TOP/s;
+for each, the dominant kernel's roofline (achieved / MI355X peak, with the
+average kernel time from HIP events recorded around every launch in the
+timed region, on the launch stream) and the oracle timed on the host cores
+over a bounded sample of the same workload.
+
+Synthetic data: seeded Gaussian weights (std 0.02) and activations (std 1,
+1% outliers x20 for decode), quantized on the GPU by the library.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_0 matvec GB/s + %HBM peak (12288×4096, M=1); prefill int8 TOPS + %MFMA"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (no sparsity)
+
+DEC = dict(M=1, N=12288, K=4096)
+PRE = dict(M=2048, N=12288, K=4096)
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=40, help="untimed decode steps")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["all", "decode", "prefill"], default="all")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of each oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies-mb", type=float, default=600.0, help="total size of the rotated weight copies")
+    return ap.parse_args()
+
+
+def time_batches(torch, launch, count, batch):
+    """Mean duration of one launch: HIP events on the launch stream around
+    batches of `batch` back-to-back launches (launch(i), i = 0..count-1).
+    Back-to-back launches leave the kernel's own time plus the short dispatch
+    gap between kernels, which makes this a slight over-estimate."""
+    nb = max(1, count // batch)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nb)]
+    i = 0
+    for a, b in ev:
+        a.record()
+        for _ in range(batch):
+            launch(i)
+            i += 1
+        b.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) / batch for a, b in ev]
+    return sum(per) / len(per), min(per), i
+
+
+def bench_decode(args, torch, q, synth):
+    N, K = DEC["N"], DEC["K"]
+    wbytes = N * q.row_bytes("q4_0", K)
+    log(f"decode: generating weights {N}x{K} and quantizing on the GPU")
+    w = torch.from_numpy(synth.weights(N, K, config=1)).cuda()
+    wq0 = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q4_0(w, wq0, N, K)
+    del w
+    copies = max(2, int(args.copies_mb * 1e6 // wbytes) + 1)
+    wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+    x = torch.from_numpy(synth.activations(1, K, config=1, outlier_frac=0.01, outlier_factor=20.0)).cuda()
+    xq = torch.empty(q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(i):
+        q.qmm_quantize_q8_0(x, xq, 1, K)
+        q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: the decode steps as a user runs them
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    # the dominant kernel alone: batches of `copies` back-to-back launches
+    mv_ms, mv_min, n = time_batches(torch, lambda i: q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K),
+                                    args.steps, copies)
+    log(f"decode: {ms_step * 1e3:.2f} us/step, matvec {mv_ms * 1e3:.2f} us (best batch {mv_min * 1e3:.2f}) "
+        f"over {copies} weight copies, {n} launches")
+    gbs_step = wbytes / (ms_step * 1e-3) / 1e9
+    gbs_kernel = wbytes / (mv_ms * 1e-3) / 1e9
+    return dict(ms_step=ms_step, gbs=gbs_step, wbytes=wbytes, copies=copies,
+                roofline={"kernel": "qmm::k_matvec<Q4_0>", "bound": "hbm",
+                          "achieved": round(gbs_kernel, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbs_kernel / HBM_PEAK_GBS, 4), "traffic": None,
+                          "kernel_us_mean": round(mv_ms * 1e3, 3), "kernel_us_best_batch": round(mv_min * 1e3, 3),
+                          "algorithmic_bytes": wbytes + q.row_bytes("q8_0", K) + 4 * N})
+
+
+def bench_prefill(args, torch, q, synth):
+    M, N, K = PRE["M"], PRE["N"], PRE["K"]
+    wbytes = N * q.row_bytes("q4_0", K)
+    log(f"prefill: generating {N}x{K} weights and {M}x{K} activations")
+    w = torch.from_numpy(synth.weights(N, K, config=1)).cuda()
+    wq = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q4_0(w, wq, N, K)
+    del w
+    X = torch.from_numpy(synth.activations(M, K, config=4)).cuda()
+    Xq = torch.empty(M * q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        q.qmm_quantize_q8_0(X, Xq, M, K)
+        q.qmm_matmul_q4_0(wq, Xq, Y, M, N, K)
+
+    for _ in range(args.prefill_warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.prefill_steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.prefill_steps
+    mm_ms, mm_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q4_0(wq, Xq, Y, M, N, K),
+                                    args.prefill_steps, 5)
+    ops = 2.0 * M * N * K
+    log(f"prefill: {ms_step * 1e3:.1f} us/step, matmul {mm_ms * 1e3:.1f} us (best batch {mm_min * 1e3:.1f})")
+    tops_kernel = ops / (mm_ms * 1e-3) / 1e12
+    return dict(ms_step=ms_step, tops=ops / (ms_step * 1e-3) / 1e12,
+                roofline={"kernel": "qmm::k_matmul_q4_0", "bound": "mfma", "achieved": round(tops_kernel, 2),
+                          "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
+                          "traffic": None, "kernel_us_mean": round(mm_ms * 1e3, 2),
+                          "kernel_us_best_batch": round(mm_min * 1e3, 2), "algorithmic_ops": ops})
+
+
+def cpu_threads():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(n, 16))
+
+
+def cpu_baseline_decode(args, q, synth):
+    import oracle
+    N, K = DEC["N"], DEC["K"]
+    w = synth.weights(N, K, config=1)
+    x = synth.activations(1, K, config=1, outlier_frac=0.01, outlier_factor=20.0)
+    wq = oracle.quantize_q4_0_w(w)
+    thr = cpu_threads()
+    reps, t_total = 0, 0.0
+    while t_total < args.cpu_seconds or reps < 1:
+        t = time.perf_counter()
+        xq = oracle.quantize_q8_0(x)
+        oracle.matmul("q4_0", wq, xq, 1, N, K, threads=thr, want=("y",))
+        t_total += time.perf_counter() - t
+        reps += 1
+    per = t_total / reps
+    return {"value": round(wq.nbytes / per / 1e9, 3), "unit": "GB/s", "cores": thr, "kind": "oracle",
+            "sample": f"full {N}x{K} decode step (quantize + matvec), {reps} repeats, {per * 1e3:.1f} ms each"}
+
+
+def cpu_baseline_prefill(args, q, synth):
+    import oracle
+    M, N, K = PRE["M"], PRE["N"], PRE["K"]
+    w = synth.weights(N, K, config=1)
+    wq = oracle.quantize_q4_0_w(w)
+    thr = cpu_threads()
+    m = 8
+    while True:
+        x = synth.activations(m, K, config=4)
+        t = time.perf_counter()
+        xq = oracle.quantize_q8_0(x)
+        oracle.matmul("q4_0", wq, xq, m, N, K, threads=thr, want=("y",))
+        dt = time.perf_counter() - t
+        if dt * 4 > args.cpu_seconds or m >= M:
+            break
+        m = min(M, m * 4)
+    ops = 2.0 * m * N * K
+    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": thr, "kind": "oracle",
+            "sample": f"first {m} of {M} tokens of the {M}x{N}x{K} prefill ({dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on one "
+              "MI355X; the row-sharded multi-GPU design is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import matmul_quantize_q8_amd as q
+    import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    q.lib()
+    torch.cuda.set_device(0)
+    log(f"device {torch.cuda.get_device_name(0)}")
+
+    dec = bench_decode(args, torch, q, synth) if args.only in ("all", "decode") else None
+    pre = bench_prefill(args, torch, q, synth) if args.only in ("all", "prefill") else None
+
+    cpu_dec = cpu_pre = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the host cores")
+        if dec is not None:
+            cpu_dec = cpu_baseline_decode(args, q, synth)
+        if pre is not None:
+            cpu_pre = cpu_baseline_prefill(args, q, synth)
+
+    out = {"metric": METRIC, "n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "int8", "data": "synthetic"}
+    if dec is not None:
+        out.update({"value": round(dec["gbs"], 1), "unit": "GB/s", "steps": args.steps, "warmup": args.warmup,
+                    "ms_per_step": round(dec["ms_step"], 5),
+                    "config": {"workload": "q4_0_matvec_12288x4096", "M": 1, "N": DEC["N"], "K": DEC["K"],
+                               "weight_bytes": dec["wbytes"], "weight_copies": dec["copies"],
+                               "step": "quantize_q8_0 + matvec_q4_0", "hbm_frac_step": round(
+                                   dec["gbs"] / HBM_PEAK_GBS, 4)},
+                    "roofline": dec["roofline"], "cpu_baseline": cpu_dec})
+    if pre is not None:
+        pf = {"workload": "q4_0_matmul_2048x12288x4096", "value": round(pre["tops"], 2), "unit": "TOPS",
+              "steps": args.prefill_steps, "warmup": args.prefill_warmup, "ms_per_step": round(pre["ms_step"], 4),
+              "step": "quantize_q8_0 (2048x4096) + matmul_q4_0", "roofline": pre["roofline"],
+              "cpu_baseline": cpu_pre}
+        if dec is None:
+            out.update({"value": pf["value"], "unit": "TOPS", "steps": pf["steps"], "warmup": pf["warmup"],
+                        "ms_per_step": pf["ms_per_step"], "config": {"workload": pf["workload"]},
+                        "roofline": pf["roofline"], "cpu_baseline": cpu_pre})
+        else:
+            out["prefill"] = pf
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+/*
+ * qmm -- block-quantized weight x Q8_0 / Q8_K activation products on MI355X
+ * (gfx950).  C ABI of libqmm.so.
+ *
+ * The method (pages: "10 . CPU matmul: quantized weights x Q8_0 activations"
+ * (minfer), "ggml Q4_0 vec_dot Walkthrough", krafla "Architecture", "kvad --
+ * the same ideas, at scale"): weights stay in their GGUF block layouts;
+ * activations are quantized on the fly to Q8_0 (per 32 values) or Q8_K (per
+ * 256); each output is a sum over blocks of an exact int32 block dot product
+ * scaled by the two block scales, accumulated in f32.
+ *
+ * Byte layouts (little-endian; "f16" is IEEE binary16):
+ *   Q8_0  34 B / 32 values : f16 d @0, int8 q[32] @2.          value = d*q
+ *   Q4_0  18 B / 32 values : f16 d @0, uint8 qs[16] @2; byte j holds element
+ *                            j in its low nibble and j+16 in its high nibble.
+ *                                                               value = d*(nib-8)
+ *   Q2_K  84 B / 256 values: uint8 scales[16] @0 (low nibble sc, high nibble
+ *                            m, one byte per group of 16), uint8 qs[64] @16,
+ *                            f16 d @80, f16 dmin @82.   value = d*sc*q - dmin*m
+ *                            qs byte 32h+l holds, at bit shift 2s, the 2-bit
+ *                            code of value 128h+32s+l (h<2, s<4, l<32).
+ *   Q8_K 292 B / 256 values: f32 d @0, int8 q[256] @4, int16 bsums[16] @260
+ *                            (bsums[g] = sum of codes 16g..16g+15).
+ * A matrix of R rows and K columns in format F is R*K/blk(F) blocks, row-major
+ * (row r starts at byte r*(K/blk)*bytes(F)), with no padding.
+ *
+ * Conventions for every entry point below:
+ *   - All data pointers are DEVICE pointers on the current HIP device and must
+ *     be 16-byte aligned (QMM_E_ALIGN otherwise).  The caller owns every
+ *     buffer; the library never allocates, frees, synchronizes or keeps state
+ *     between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously; the return value reports argument and launch
+ *     errors only.
+ *   - Outputs must not alias inputs.  Outputs are overwritten, never
+ *     accumulated into.
+ *   - Kernels may read up to 15 bytes past the end of an input buffer (never
+ *     past the end of the 16-byte-aligned granule that holds its last byte, so
+ *     never into another page); those bytes do not affect any result.
+ *   - Calls are thread-safe.  No entry point aborts the process.
+ *   - Sizes: M, N >= 1, K >= one block, K a multiple of the block length of
+ *     the format (32, or 256 for Q8_K / Q2_K), every dimension < 2^31 and every
+ *     buffer < 2^40 bytes; QMM_E_SHAPE otherwise.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QMM_OK = 0,
+    QMM_E_SHAPE = 1,  /* bad M, N or K, or a byte size that overflows   */
+    QMM_E_NULL = 2,   /* a required pointer is NULL                      */
+    QMM_E_ALIGN = 3,  /* a pointer is not 16-byte aligned                */
+    QMM_E_DEVICE = 4, /* no current device, or it is not gfx950          */
+    QMM_E_LAUNCH = 5  /* the HIP runtime refused a kernel launch         */
+} qmm_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *qmm_status_string(qmm_status s);
+
+/* Version of this ABI (incremented on any incompatible change). */
+int qmm_abi_version(void);
+
+/* ---- activation quantizers ------------------------------------------------ */
+
+/* Q8_0 quantization of M rows of K f32 values (minfer "The activation
+ * quantizers", quantize_avx2; ggml section 1.1; krafla "Numerics").  For each
+ * block of 32: amax = max|x|, d = amax/127 (f32, stored as f16 rounded to
+ * nearest even), id = amax ? 127/amax : 0, q = round-half-even(x*id).
+ * Bit-exact: every step is one correctly rounded f32 operation.
+ *   x  : f32 [M][K], read only.
+ *   xq : Q8_0 [M][K/32] blocks, M*K/32*34 bytes, written.
+ * Also the quantizer of Q8_0 weight matrices (same rule, rows = N). */
+qmm_status qmm_quantize_q8_0(const float *x, void *xq, int64_t M, int64_t K, void *stream);
+
+/* Q8_K quantization (minfer quantize_row_q8_k_buf and its three details):
+ * per 256 values amax, d = amax/127 stored as f32, q = saturate[-128,127]
+ * (round-half-even(x*id)), bsums from the saturated codes.
+ *   x  : f32 [M][K], K % 256 == 0.   xq : Q8_K [M][K/256] blocks (292 B). */
+qmm_status qmm_quantize_q8_k(const float *x, void *xq, int64_t M, int64_t K, void *stream);
+
+/* ---- weight quantizers (prepare weight matrices; not on the product path) -- */
+
+/* Q4_0 quantization of N rows of K f32 weights (ggml section 1.1 prose;
+ * kvad "The scale that wasted a code"): per 32, the value of largest
+ * magnitude (first on ties) keeps its sign as max, d = max/-8 (d = 0 for an
+ * all-zero block), code = clamp(round-half-even(x/d)+8, 0, 15), f16 d.
+ *   w : f32 [N][K].   wq : Q4_0 [N][K/32] blocks (18 B). */
+qmm_status qmm_quantize_q4_0(const float *w, void *wq, int64_t N, int64_t K, void *stream);
+
+/* Q2_K quantization of N rows of K f32 weights, K % 256 == 0.  The pages
+ * define the format (ggml section 1.2) but no quantizer; the rule is: per
+ * group of 16, lo = min(0, min x), hi = max x, s = (hi-lo)/3, mn = -lo;
+ * d = max s / 15, dmin = max mn / 15 (f16); sc = clamp(rne(s/d),0,15),
+ * m = clamp(rne(mn/dmin),0,15); q = clamp(rne((x + dmin*m)/(d*sc)),0,3),
+ * with 0 for a zero divisor (d and dmin here are the stored f16 values).
+ *   w : f32 [N][K].   wq : Q2_K [N][K/256] blocks (84 B). */
+qmm_status qmm_quantize_q2_k(const float *w, void *wq, int64_t N, int64_t K, void *stream);
+
+/* ---- products ----------------------------------------------------------------
+ * y[t][n] = sum over blocks b of d_w[n,b] * d_x[t,b] * I_b[t,n], where I_b is
+ * the exact int32 dot product of the block's codes (minfer mm_rows and the
+ * scalar kernel; ggml section 2; krafla "Data flow for one token").  Integer
+ * block sums are exact; only the f32 accumulation order is free, so results
+ * agree with an exact evaluation within 1e-5 of sum |d_w d_x w_j q_j| per
+ * output (krafla "Numerics").  Output is token-major [M][N] f32 (minfer
+ * "Pitfalls": out[t*od + o]).
+ * Pairing (minfer "Two activation formats, one pairing rule"): Q4_0 and Q8_0
+ * weights take Q8_0 activations; Q2_K weights take Q8_K activations. */
+
+/* Decode matvec, one token (M = 1).
+ *   w  : N rows of K/32 weight blocks.   xq : one row of Q8_0 (or Q8_K) blocks.
+ *   y  : f32 [N], written. */
+qmm_status qmm_matvec_q8_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
+qmm_status qmm_matvec_q4_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
+qmm_status qmm_matvec_q2_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream);
+
+/* Prefill matmul, M tokens.
+ *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.
+ *   y  : f32 [M][N], written. */
+qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream);
+qmm_status qmm_matmul_q2_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

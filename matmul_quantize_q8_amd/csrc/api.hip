@@ -1,0 +1,169 @@
+// C ABI of libqmm: argument checks, device check, launch.  Declarations and
+// the contract of every entry point are in include/qmm.h.
+#include <atomic>
+#include <cstring>
+
+#include "qmm.h"
+#include "qmm_device.h"
+
+namespace qmm {
+hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_quantize_q8_k(const float *x, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_quantize_q4_0(const float *w, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_quantize_q2_k(const float *w, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_matvec_q4_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st);
+hipError_t launch_matvec_q8_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st);
+hipError_t launch_matvec_q2_k(const void *w, const void *xq, float *y, int N, int ns, hipStream_t st);
+hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st);
+hipError_t launch_matmul_q2_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
+}  // namespace qmm
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxBytes = int64_t(1) << 40;
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_device_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+qmm_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QMM_E_DEVICE;
+    int s = g_device_state[dev].load(std::memory_order_acquire);
+    if (s == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return QMM_E_DEVICE;
+        s = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_state[dev].store(s, std::memory_order_release);
+    }
+    return s == 1 ? QMM_OK : QMM_E_DEVICE;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// rows x (K / blk) blocks of `bytes` each must stay below kMaxBytes.
+bool size_ok(int64_t rows, int64_t K, int64_t blk, int64_t bytes) {
+    if (rows < 0 || rows > kMaxDim || K > kMaxDim) return false;
+    const int64_t nb = K / blk;
+    return nb == 0 || rows <= kMaxBytes / (nb * bytes);
+}
+
+// Shape checks shared by all entry points.  `work` is false for an empty
+// problem (M or N zero): nothing is launched and no pointer is touched.
+qmm_status check_shape(int64_t M, int64_t N, int64_t K, int64_t blk, bool &work) {
+    work = false;
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return QMM_E_SHAPE;
+    if (K < blk || K > kMaxDim || K % blk != 0) return QMM_E_SHAPE;
+    work = (M > 0 && N > 0);
+    return QMM_OK;
+}
+
+qmm_status check_ptrs(std::initializer_list<const void *> ps) {
+    for (const void *p : ps)
+        if (p == nullptr) return QMM_E_NULL;
+    for (const void *p : ps)
+        if (!aligned16(p)) return QMM_E_ALIGN;
+    return QMM_OK;
+}
+
+qmm_status launched(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_E_LAUNCH; }
+
+typedef hipError_t (*quant_launch)(const float *, void *, int64_t, hipStream_t);
+
+qmm_status quantize(quant_launch fn, const float *x, void *out, int64_t rows, int64_t K, int64_t blk,
+                    int64_t in_bytes, int64_t out_bytes, void *stream) {
+    bool work;
+    qmm_status s = check_shape(rows, 1, K, blk, work);
+    if (s != QMM_OK) return s;
+    if (!size_ok(rows, K, blk, in_bytes) || !size_ok(rows, K, blk, out_bytes)) return QMM_E_SHAPE;
+    if (!work) return QMM_OK;
+    if ((s = check_ptrs({x, out})) != QMM_OK) return s;
+    if ((s = check_device()) != QMM_OK) return s;
+    return launched(fn(x, out, rows * (K / blk), static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qmm_status_string(qmm_status s) {
+    switch (s) {
+        case QMM_OK: return "QMM_OK";
+        case QMM_E_SHAPE: return "QMM_E_SHAPE: bad M, N or K, or a byte size that overflows";
+        case QMM_E_NULL: return "QMM_E_NULL: a required pointer is NULL";
+        case QMM_E_ALIGN: return "QMM_E_ALIGN: a pointer is not 16-byte aligned";
+        case QMM_E_DEVICE: return "QMM_E_DEVICE: no current device, or it is not gfx950";
+        case QMM_E_LAUNCH: return "QMM_E_LAUNCH: the HIP runtime refused a kernel launch";
+    }
+    return "QMM: unknown status";
+}
+
+int qmm_abi_version(void) { return 1; }
+
+qmm_status qmm_quantize_q8_0(const float *x, void *xq, int64_t M, int64_t K, void *stream) {
+    return quantize(qmm::launch_quantize_q8_0, x, xq, M, K, 32, 128, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_quantize_q8_k(const float *x, void *xq, int64_t M, int64_t K, void *stream) {
+    return quantize(qmm::launch_quantize_q8_k, x, xq, M, K, 256, 1024, qmm::kQ8KBytes, stream);
+}
+
+qmm_status qmm_quantize_q4_0(const float *w, void *wq, int64_t N, int64_t K, void *stream) {
+    return quantize(qmm::launch_quantize_q4_0, w, wq, N, K, 32, 128, qmm::kQ40Bytes, stream);
+}
+
+qmm_status qmm_quantize_q2_k(const float *w, void *wq, int64_t N, int64_t K, void *stream) {
+    return quantize(qmm::launch_quantize_q2_k, w, wq, N, K, 256, 1024, qmm::kQ2KBytes, stream);
+}
+
+typedef hipError_t (*mv_launch)(const void *, const void *, float *, int, int, hipStream_t);
+
+static qmm_status matvec(mv_launch fn, const void *w, const void *xq, float *y, int64_t N, int64_t K, int64_t blk,
+                         int64_t wbytes, int64_t xbytes, void *stream) {
+    bool work;
+    qmm_status s = check_shape(1, N, K, blk, work);
+    if (s != QMM_OK) return s;
+    if (!size_ok(N, K, blk, wbytes) || !size_ok(1, K, blk, xbytes)) return QMM_E_SHAPE;
+    if (!work) return QMM_OK;
+    if ((s = check_ptrs({w, xq, y})) != QMM_OK) return s;
+    if ((s = check_device()) != QMM_OK) return s;
+    return launched(fn(w, xq, y, (int)N, (int)(K / blk), static_cast<hipStream_t>(stream)));
+}
+
+qmm_status qmm_matvec_q8_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream) {
+    return matvec(qmm::launch_matvec_q8_0, w, xq, y, N, K, 32, qmm::kQ80Bytes, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_matvec_q4_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream) {
+    return matvec(qmm::launch_matvec_q4_0, w, xq, y, N, K, 32, qmm::kQ40Bytes, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_matvec_q2_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream) {
+    return matvec(qmm::launch_matvec_q2_k, w, xq8k, y, N, K, 256, qmm::kQ2KBytes, qmm::kQ8KBytes, stream);
+}
+
+typedef hipError_t (*mm_launch)(const void *, const void *, float *, int, int, int, hipStream_t);
+
+static qmm_status matmul(mm_launch fn, const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
+                         int64_t blk, int64_t wbytes, int64_t xbytes, void *stream) {
+    bool work;
+    qmm_status s = check_shape(M, N, K, blk, work);
+    if (s != QMM_OK) return s;
+    if (!size_ok(N, K, blk, wbytes) || !size_ok(M, K, blk, xbytes)) return QMM_E_SHAPE;
+    if (N > 0 && M > kMaxBytes / 4 / N) return QMM_E_SHAPE;
+    if (!work) return QMM_OK;
+    if ((s = check_ptrs({w, xq, y})) != QMM_OK) return s;
+    if ((s = check_device()) != QMM_OK) return s;
+    return launched(fn(w, xq, y, (int)M, (int)N, (int)(K / blk), static_cast<hipStream_t>(stream)));
+}
+
+qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+    return matmul(qmm::launch_matmul_q4_0, w, xq, y, M, N, K, 32, qmm::kQ40Bytes, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_matmul_q2_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream) {
+    return matmul(qmm::launch_matmul_q2_k, w, xq8k, y, M, N, K, 256, qmm::kQ2KBytes, qmm::kQ8KBytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+// Quantizers: f32 rows -> Q8_0 / Q8_K activation blocks, and f32 weight rows
+// -> Q4_0 / Q2_K weight blocks.  Each block is independent, so every
+// quantizer treats its input as one flat sequence of blocks (row boundaries
+// coincide with block boundaries) and maps lanes to blocks.
+//
+// Bit-exactness: every floating-point step is a single correctly rounded f32
+// operation (hipcc's default f32 division is correctly rounded, the library
+// is built with -ffp-contract=off so no multiply-add is fused, f32 denormals
+// are kept), rounding to integer is v_rndne_f32 (ties to even) and the f16
+// store is v_cvt_f16_f32 (nearest even).  Reductions use max/min only, which
+// are exact in any order.
+#include "qmm_device.h"
+
+namespace qmm {
+
+// ---------------------------------------------------------------------------
+// Q8_0 (minfer "The activation quantizers"; ggml section 1.1):
+// per 32 values amax, d = amax/127 -> f16, id = amax ? 127/amax : 0,
+// q = rne(x * id).  Eight lanes share a block, four values each.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize_q8_0(const float4 *__restrict__ x, uint8_t *__restrict__ out,
+                                                       int64_t nblocks) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = t >> 3;
+    const int part = threadIdx.x & 7;
+    const bool valid = blk < nblocks;
+    float4 v = valid ? x[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = fmaxf(a, xor_shfl(a, 1));
+    a = fmaxf(a, xor_shfl(a, 2));
+    a = fmaxf(a, xor_shfl(a, 4));
+
+    const float d = a / 127.0f;
+    const float id = (a != 0.0f) ? 127.0f / a : 0.0f;
+    const int q0 = (int)rintf(v.x * id);
+    const int q1 = (int)rintf(v.y * id);
+    const int q2 = (int)rintf(v.z * id);
+    const int q3 = (int)rintf(v.w * id);
+    const uint32_t packed = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
+                            ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
+    if (valid) {
+        uint8_t *ob = out + blk * kQ80Bytes;
+        uint16_t *o16 = reinterpret_cast<uint16_t *>(ob + 2 + 4 * part);   // 2-byte aligned
+        o16[0] = (uint16_t)(packed & 0xffffu);
+        o16[1] = (uint16_t)(packed >> 16);
+        if (part == 0) *reinterpret_cast<uint16_t *>(ob) = (uint16_t)f32_to_f16_bits(d);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q8_K (minfer quantize_row_q8_k_buf): per 256 values amax, f32 d = amax/127,
+// q = saturate(rne(x*id)), bsums[g] = sum of the 16 saturated codes of g.
+// One wave per block; lane L holds values 4L..4L+3 (group L/4).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize_q8_k(const float4 *__restrict__ x, uint8_t *__restrict__ out,
+                                                       int64_t nblocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;                               // whole wave exits together
+    const float4 v = x[blk * 64 + lane];
+
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) a = fmaxf(a, xor_shfl(a, m));
+
+    const float d = a / 127.0f;
+    const float id = (a != 0.0f) ? 127.0f / a : 0.0f;
+    int q[4];
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float r = rintf(vv[k] * id);
+        r = fminf(fmaxf(r, -128.0f), 127.0f);
+        q[k] = (int)r;
+    }
+    const uint32_t packed = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
+                            ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
+    int s = q[0] + q[1] + q[2] + q[3];
+    s += xor_shfl(s, 1);
+    s += xor_shfl(s, 2);
+
+    uint8_t *ob = out + blk * kQ8KBytes;                      // 292 = 4 * 73: 4-byte aligned
+    *reinterpret_cast<uint32_t *>(ob + 4 + 4 * lane) = packed;
+    if ((lane & 3) == 0) *reinterpret_cast<int16_t *>(ob + 260 + 2 * (lane >> 2)) = (int16_t)s;
+    if (lane == 0) *reinterpret_cast<float *>(ob) = d;
+}
+
+// ---------------------------------------------------------------------------
+// Q4_0 weights (ggml section 1.1; kvad "The scale that wasted a code"):
+// the value of largest magnitude (first index on ties) keeps its sign as
+// max; d = max / -8 (0 for an all-zero block); code = clamp(rne(x/d)+8, 0, 15);
+// byte j of qs = code_j | code_{j+16} << 4.  Eight lanes per block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize_q4_0(const float4 *__restrict__ w, uint8_t *__restrict__ out,
+                                                       int64_t nblocks) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = t >> 3;
+    const int part = threadIdx.x & 7;
+    const bool valid = blk < nblocks;
+    const float4 v = valid ? w[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+
+    // (|value|, index, value) of this lane's four, first index on ties
+    float am = fabsf(vv[0]), mx = vv[0];
+    int ix = 4 * part;
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+        const float a = fabsf(vv[k]);
+        if (a > am) { am = a; mx = vv[k]; ix = 4 * part + k; }
+    }
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+        const float oam = xor_shfl(am, m);
+        const float omx = xor_shfl(mx, m);
+        const int oix = xor_shfl(ix, m);
+        if (oam > am || (oam == am && oix < ix)) { am = oam; mx = omx; ix = oix; }
+    }
+    const float d = (am != 0.0f) ? mx / -8.0f : 0.0f;
+    uint32_t codes = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int c = 8;
+        if (d != 0.0f) c = (int)rintf(vv[k] / d) + 8;
+        c = min(max(c, 0), 15);
+        codes |= (uint32_t)c << (8 * k);
+    }
+    // lanes 0..3 hold elements 0..15 (low nibbles), lanes 4..7 elements 16..31
+    const uint32_t hi = xor_shfl(codes, 4);
+    if (valid && part < 4) {
+        const uint32_t bytes = codes | (hi << 4);
+        uint8_t *ob = out + blk * kQ40Bytes;
+        uint16_t *o16 = reinterpret_cast<uint16_t *>(ob + 2 + 4 * part);
+        o16[0] = (uint16_t)(bytes & 0xffffu);
+        o16[1] = (uint16_t)(bytes >> 16);
+        if (part == 0) *reinterpret_cast<uint16_t *>(ob) = (uint16_t)f32_to_f16_bits(d);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q2_K weights.  Format: ggml section 1.2.  The pages give no quantizer; the
+// rule (the same in the header's contract) is, per group g of 16:
+//   lo = min(0, min x), hi = max x, s = (hi - lo)/3, mn = -lo;
+// per block: d = max_g s / 15, dmin = max_g mn / 15 (f16 stored; dh, dminh
+// below are the stored values), sc = clamp(rne(s/dh), 0, 15),
+// m = clamp(rne(mn/dminh), 0, 15), q = clamp(rne((x + dminh*m)/(dh*sc)), 0, 3).
+// qs bit order: byte 32h + l holds, at shift 2s, weight 128h + 32s + l.
+// One wave per block; lane L holds weights 4L..4L+3 (group L/4).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize_q2_k(const float4 *__restrict__ w, uint8_t *__restrict__ out,
+                                                       int64_t nblocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;
+    const float4 v = w[blk * 64 + lane];
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+
+    float lo = fminf(fminf(vv[0], vv[1]), fminf(vv[2], vv[3]));
+    float hi = fmaxf(fmaxf(vv[0], vv[1]), fmaxf(vv[2], vv[3]));
+    lo = fminf(lo, xor_shfl(lo, 1));
+    hi = fmaxf(hi, xor_shfl(hi, 1));
+    lo = fminf(lo, xor_shfl(lo, 2));
+    hi = fmaxf(hi, xor_shfl(hi, 2));
+    lo = fminf(lo, 0.0f);
+    const float s = (hi - lo) / 3.0f;
+    const float mn = -lo;
+
+    float smax = s, mmax = mn;
+#pragma unroll
+    for (int m = 4; m < 64; m <<= 1) {
+        smax = fmaxf(smax, xor_shfl(smax, m));
+        mmax = fmaxf(mmax, xor_shfl(mmax, m));
+    }
+    smax = (smax > 0.0f) ? smax : 0.0f;        // +0 when no group spans anything
+    mmax = (mmax > 0.0f) ? mmax : 0.0f;
+    const uint32_t dbits = f32_to_f16_bits(smax / 15.0f);
+    const uint32_t dminbits = f32_to_f16_bits(mmax / 15.0f);
+    const float dh = f16_bits_to_f32(dbits);
+    const float dminh = f16_bits_to_f32(dminbits);
+
+    int sc = 0, mq = 0;
+    if (dh != 0.0f) sc = min(max((int)rintf(s / dh), 0), 15);
+    if (dminh != 0.0f) mq = min(max((int)rintf(mn / dminh), 0), 15);
+    const float off = dminh * (float)mq;
+    const float div = dh * (float)sc;
+    uint32_t codes = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int c = 0;
+        if (div != 0.0f) c = min(max((int)rintf((vv[k] + off) / div), 0), 3);
+        codes |= (uint32_t)c << (8 * k);
+    }
+    // weights 4L..4L+3: h = L/32, s = (L%32)/8, l = 4(L%8)..+3; lanes that
+    // share (h, L%8) fill the same qs dword at shifts 0, 2, 4, 6.
+    const int sh = (lane >> 3) & 3;
+    uint32_t word = codes << (2 * sh);
+    word |= xor_shfl(word, 8);
+    word |= xor_shfl(word, 16);
+
+    uint8_t *ob = out + blk * kQ2KBytes;                      // 84 = 4 * 21: 4-byte aligned
+    if (sh == 0) *reinterpret_cast<uint32_t *>(ob + 16 + 32 * (lane >> 5) + 4 * (lane & 7)) = word;
+    if ((lane & 3) == 0) ob[lane >> 2] = (uint8_t)(sc | (mq << 4));
+    if (lane == 0) {
+        *reinterpret_cast<uint16_t *>(ob + 80) = (uint16_t)dbits;
+        *reinterpret_cast<uint16_t *>(ob + 82) = (uint16_t)dminbits;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (called by the C ABI after argument checks).
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipStream_t st) {
+    const int64_t grid = (nblocks + 31) / 32;
+    void *args[] = {(void *)&x, (void *)&out, (void *)&nblocks};
+    return hipLaunchKernel((const void *)k_quantize_q8_0, dim3((unsigned)grid), dim3(256), args, 0, st);
+}
+
+hipError_t launch_quantize_q8_k(const float *x, void *out, int64_t nblocks, hipStream_t st) {
+    const int64_t grid = (nblocks + 3) / 4;
+    void *args[] = {(void *)&x, (void *)&out, (void *)&nblocks};
+    return hipLaunchKernel((const void *)k_quantize_q8_k, dim3((unsigned)grid), dim3(256), args, 0, st);
+}
+
+hipError_t launch_quantize_q4_0(const float *w, void *out, int64_t nblocks, hipStream_t st) {
+    const int64_t grid = (nblocks + 31) / 32;
+    void *args[] = {(void *)&w, (void *)&out, (void *)&nblocks};
+    return hipLaunchKernel((const void *)k_quantize_q4_0, dim3((unsigned)grid), dim3(256), args, 0, st);
+}
+
+hipError_t launch_quantize_q2_k(const float *w, void *out, int64_t nblocks, hipStream_t st) {
+    const int64_t grid = (nblocks + 3) / 4;
+    void *args[] = {(void *)&w, (void *)&out, (void *)&nblocks};
+    return hipLaunchKernel((const void *)k_quantize_q2_k, dim3((unsigned)grid), dim3(256), args, 0, st);
+}
+
+}  // namespace qmm

@@ -1,0 +1,99 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    import matmul_quantize_q8_amd as q
+    q.lib()
+    return q
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("qmm_quantize_q8_0", "qmm_quantize_q8_k", "qmm_matvec_q8_0", "qmm_matvec_q4_0",
+              "qmm_matvec_q2_k", "qmm_matmul_q4_0", "qmm_matmul_q2_k"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(q):
+    lib = ctypes.CDLL(q.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(q.EXPORTS)
+    for n in q.EXPORTS:
+        assert callable(getattr(q, n, None)) or n in ("qmm_status_string", "qmm_abi_version")
+
+
+def test_library_is_gfx950_code(q):
+    data = open(q.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_status_strings_and_version(q):
+    L = q.lib()
+    assert L.qmm_abi_version() == 1
+    for code in range(6):
+        assert L.qmm_status_string(code).decode().startswith(q.STATUS[code])
+
+
+# Argument checks happen before any device call, so they run without a GPU.
+A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda L: L.qmm_quantize_q8_0(A, A, 1, 48, None), 1),        # K % 32
+    (lambda L: L.qmm_quantize_q8_0(A, A, 1, 0, None), 1),         # K = 0
+    (lambda L: L.qmm_quantize_q8_0(A, A, -1, 32, None), 1),       # M < 0
+    (lambda L: L.qmm_quantize_q8_k(A, A, 1, 32 * 3, None), 1),    # K % 256
+    (lambda L: L.qmm_quantize_q8_0(None, A, 1, 32, None), 2),     # NULL
+    (lambda L: L.qmm_quantize_q8_0(A + 4, A, 1, 32, None), 3),    # misaligned
+    (lambda L: L.qmm_matvec_q4_0(A, A, None, 8, 64, None), 2),
+    (lambda L: L.qmm_matvec_q4_0(A, A + 8, A, 8, 64, None), 3),
+    (lambda L: L.qmm_matvec_q2_k(A, A, A, 8, 128, None), 1),
+    (lambda L: L.qmm_matmul_q4_0(A, A, A, 4, 8, 33, None), 1),
+    (lambda L: L.qmm_matmul_q4_0(A, A, A, 1 << 31, 8, 32, None), 1),   # M >= 2^31
+    (lambda L: L.qmm_matmul_q2_k(A, A, A, 4, 8, 256 * 3 + 32, None), 1),
+    (lambda L: L.qmm_matmul_q4_0(A, A, A, 1 << 30, 1 << 30, 32, None), 1),   # output bytes overflow
+])
+def test_argument_errors_without_device(q, call, code):
+    assert call(q.lib()) == code
+
+
+def test_empty_problem_is_a_no_op(q):
+    L = q.lib()
+    assert L.qmm_matmul_q4_0(None, None, None, 0, 8, 32, None) == 0
+    assert L.qmm_matvec_q8_0(None, None, None, 0, 32, None) == 0
+    assert L.qmm_quantize_q8_0(None, None, 0, 64, None) == 0
+
+
+def test_python_binding_raises(q):
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_quantize_q8_0(A, A, 1, 33, stream=0)
+    assert e.value.code == "QMM_E_SHAPE"
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package never imports or loads the oracle."""
+    pkg = os.path.join(ROOT, "matmul_quantize_q8_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                for bad in ("import oracle", "from oracle", "liboracle", "qmm_oracle"):
+                    assert bad not in text, (f, bad)

@@ -1,0 +1,269 @@
+"""Parity of the HIP path with the oracle, through the C ABI, on an MI355X.
+
+Quantizers must be bit-exact.  Products must satisfy, per output,
+    |y_gpu - y_exact| <= 1e-5 * sum_i |d_w w_i d_x q_i|
+(the krafla "Numerics" bound: integer block sums are exact, only the f32
+accumulation order differs), where y_exact is the oracle's double result.
+
+Every input is seeded (synth) and every expected value comes from the oracle.
+"""
+import numpy as np
+import pytest
+
+import synth
+from conftest import golden
+
+pytestmark = pytest.mark.gpu
+
+TOL = golden("tolerance.json")["relative_to_magnitude"]
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import matmul_quantize_q8_amd as q
+    import oracle
+    q.lib()
+    oracle.lib()
+    return torch, q, oracle
+
+
+def _dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _gpu_quant(env, fmt, x, weights=False):
+    """Quantize f32 rows on the GPU with the format's product-side quantizer."""
+    torch, q, _ = env
+    rows, K = x.shape
+    out = torch.zeros(rows * q.row_bytes(fmt, K), dtype=torch.uint8, device="cuda")
+    fn = {"q8_0": q.qmm_quantize_q8_0, "q8_k": q.qmm_quantize_q8_k,
+          "q4_0": q.qmm_quantize_q4_0, "q2_k": q.qmm_quantize_q2_k}[fmt]
+    fn(_dev(torch, x), out, rows, K)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(rows, -1)
+
+
+def _edge_rows(rows, K, seed):
+    x = synth.with_outliers(synth.gaussian_f32((rows, K), 1.0, seed), 0.01, 20.0, seed + 1)
+    x[0, :32] = 0.0                                   # zero block
+    if K >= 64:
+        x[0, 32:64] = 0.0
+        x[0, 37] = -2.75                              # one nonzero value
+    if rows > 1 and K >= 96:
+        x[1, 64:96] *= 1e-30                          # tiny but inside the contract
+        x[1, :32] = np.arange(32, dtype=np.float32) - 15.5    # x * id lands exactly on .5: ties
+        x[1, 0] = 127.0                                        # amax 127, so id = 1 exactly
+    return x
+
+
+# ---------------------------------------------------------------------------
+# Quantizers: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,K", [(1, 32), (1, 1024), (3, 4096), (7, 96), (2048, 4096), (5, 11008)])
+def test_quantize_q8_0_bit_exact(env, rows, K):
+    _, _, orc = env
+    _say("quantize_q8_0", rows, K)
+    x = _edge_rows(rows, K, 1000 + rows + K)
+    assert np.array_equal(_gpu_quant(env, "q8_0", x), orc.quantize_q8_0(x))
+
+
+@pytest.mark.parametrize("rows,K", [(1, 256), (1, 4096), (9, 768), (64, 4096)])
+def test_quantize_q8_k_bit_exact(env, rows, K):
+    _, _, orc = env
+    _say("quantize_q8_k", rows, K)
+    x = _edge_rows(rows, K, 2000 + rows + K)
+    if rows > 2:
+        x[2, 256:512] = 0.0
+    assert np.array_equal(_gpu_quant(env, "q8_k", x), orc.quantize_q8_k(x))
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (512, 1024), (33, 96), (12288, 4096)])
+def test_quantize_q4_0_weights_bit_exact(env, rows, K):
+    _, _, orc = env
+    _say("quantize_q4_0", rows, K)
+    w = synth.gaussian_f32((rows, K), 0.02, 3000 + rows)
+    w[0, :32] = 0.0
+    if rows > 1 and K >= 32:
+        w[1, :32] = 0.01
+        w[1, 3] = -0.5
+        w[1, 10] = 0.5
+    assert np.array_equal(_gpu_quant(env, "q4_0", w), orc.quantize_q4_0_w(w))
+
+
+@pytest.mark.parametrize("rows,K", [(1, 256), (16, 1024), (12288, 4096)])
+def test_quantize_q2_k_weights_bit_exact(env, rows, K):
+    _, _, orc = env
+    _say("quantize_q2_k", rows, K)
+    w = synth.gaussian_f32((rows, K), 0.02, 4000 + rows)
+    w[0, :256] = 0.0
+    if rows > 1:
+        w[1, :16] = np.abs(w[1, :16])                 # a group with no negative value
+    assert np.array_equal(_gpu_quant(env, "q2_k", w), orc.quantize_q2_k_w(w))
+
+
+# ---------------------------------------------------------------------------
+# Products
+# ---------------------------------------------------------------------------
+def _inputs(fmt, M, N, K, seed, outliers=True):
+    import oracle
+    w = synth.gaussian_f32((N, K), 0.02, seed)
+    x = synth.gaussian_f32((M, K), 1.0, seed + 1)
+    if outliers:
+        x = synth.with_outliers(x, 0.01, 20.0, seed + 2)
+    return oracle.quantize_w(fmt, w), oracle.quantize_x(fmt, x)
+
+
+def _check(y, ref, mag, what):
+    y = np.asarray(y, dtype=np.float64).reshape(ref.shape)
+    err = np.abs(y - ref)
+    bound = TOL * mag
+    bad = np.nonzero(err > bound)
+    assert bad[0].size == 0, (what, bad[0].size, [(tuple(int(i) for i in ix), float(y[ix]), float(ref[ix]),
+                                                    float(bound[ix])) for ix in zip(*bad)][:5])
+
+
+def _run_matvec(env, fmt, wq, xq, N, K):
+    torch, q, _ = env
+    y = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    q.MATVEC[fmt](_dev(torch, wq), _dev(torch, xq), y, N, K)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _run_matmul(env, fmt, wq, xq, M, N, K):
+    torch, q, _ = env
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    q.MATMUL[fmt](_dev(torch, wq), _dev(torch, xq), y, M, N, K)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+MATVEC_CASES = [
+    ("q4_0", 512, 1024),     # 512 x 1024 decode (L2-resident)
+    ("q4_0", 12288, 4096),   # FFN-gate decode
+    ("q4_0", 1, 32), ("q4_0", 3, 96), ("q4_0", 17, 160), ("q4_0", 5, 2080), ("q4_0", 7, 8192),
+    ("q4_0", 9, 20480),      # two row segments
+    ("q8_0", 12288, 4096), ("q8_0", 22016, 4096), ("q8_0", 4096, 11008),   # one 7B-style layer
+    ("q8_0", 1, 32), ("q8_0", 5, 96), ("q8_0", 11, 4128), ("q8_0", 3, 20000),
+    ("q2_k", 12288, 4096),
+    ("q2_k", 1, 256), ("q2_k", 3, 768), ("q2_k", 13, 9216), ("q2_k", 2, 40960),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K", MATVEC_CASES)
+def test_matvec_matches_oracle(env, fmt, N, K):
+    _, _, orc = env
+    _say("matvec", fmt, N, K)
+    wq, xq = _inputs(fmt, 1, N, K, 5000 + N + K)
+    ref = orc.matmul(fmt, wq, xq, 1, N, K, threads=8, want=("y64", "mag"))
+    y = _run_matvec(env, fmt, wq, xq, N, K)
+    _check(y, ref["y64"][0], ref["mag"][0], (fmt, N, K))
+
+
+MATMUL_CASES = [
+    ("q4_0", 1, 8, 32), ("q4_0", 37, 200, 1024), ("q4_0", 128, 128, 4096), ("q4_0", 130, 129, 160),
+    ("q4_0", 64, 512, 1024), ("q4_0", 5, 3, 96), ("q4_0", 256, 384, 4128),
+    ("q2_k", 1, 8, 256), ("q2_k", 9, 70, 1024), ("q2_k", 33, 130, 4096),
+]
+
+
+@pytest.mark.parametrize("fmt,M,N,K", MATMUL_CASES)
+def test_matmul_matches_oracle(env, fmt, M, N, K):
+    _, _, orc = env
+    _say("matmul", fmt, M, N, K)
+    wq, xq = _inputs(fmt, M, N, K, 6000 + M + N + K)
+    ref = orc.matmul(fmt, wq, xq, M, N, K, threads=8, want=("y64", "mag"))
+    y = _run_matmul(env, fmt, wq, xq, M, N, K)
+    _check(y, ref["y64"], ref["mag"], (fmt, M, N, K))
+
+
+def test_matmul_prefill_full_size_sampled(env):
+    """The 2048 x 12288 x 4096 prefill, checked on 20000 sampled outputs plus
+    whole rows and columns at the tile edges."""
+    torch, q, orc = env
+    M, N, K = 2048, 12288, 4096
+    _say("matmul q4_0 full", M, N, K)
+    w = synth.weights(N, K, config=1)
+    x = synth.activations(M, K, config=4)
+    wq = orc.quantize_q4_0_w(w)
+    xq = orc.quantize_q8_0(x)
+    y = _run_matmul(env, "q4_0", wq, xq, M, N, K)
+    assert np.isfinite(y).all()
+    rng = synth.splitmix64(77, 0, 40000)
+    mi = (rng[:20000] % np.uint64(M)).astype(np.int64)
+    ni = (rng[20000:] % np.uint64(N)).astype(np.int64)
+    edge_m = np.array([0, 1, 127, 128, 1919, 2047])
+    edge_n = np.array([0, 31, 32, 127, 128, 12287])
+    mi = np.concatenate([mi, np.repeat(edge_m, N // 64), np.tile(np.arange(0, M, 7), len(edge_n))])
+    ni = np.concatenate([ni, np.tile(np.arange(0, N, 64), len(edge_m)), np.repeat(edge_n, len(range(0, M, 7)))])
+    ref, mag = orc.matmul_sampled("q4_0", wq, xq, mi, ni, K)
+    _check(y[mi, ni], ref, mag, "prefill sampled")
+
+
+def test_matmul_rows_equal_matvec(env):
+    """Row m of the prefill product and the decode product of token m are two
+    evaluations of the same outputs: both within the bound of the oracle."""
+    torch, q, orc = env
+    M, N, K = 6, 300, 2048
+    wq, xq = _inputs("q4_0", M, N, K, 7000)
+    ref = orc.matmul("q4_0", wq, xq, M, N, K, threads=8, want=("y64", "mag"))
+    y = _run_matmul(env, "q4_0", wq, xq, M, N, K)
+    xr = xq.reshape(M, -1)
+    for m in range(M):
+        yv = _run_matvec(env, "q4_0", wq, xr[m], N, K)
+        _check(yv, ref["y64"][m], ref["mag"][m], ("matvec row", m))
+        _check(y[m], ref["y64"][m], 2 * ref["mag"][m], ("matmul row", m))
+        assert np.all(np.abs(y[m].astype(np.float64) - yv) <= 2 * TOL * ref["mag"][m])
+
+
+def test_end_to_end_decode_gpu_quantized(env):
+    """Decode as deployed: f32 activation quantized on the GPU, then the matvec;
+    the activation bytes equal the oracle's, the output is within the bound."""
+    torch, q, orc = env
+    N, K = 12288, 4096
+    w = synth.weights(N, K, config=1)
+    x = synth.activations(1, K, config=1, outlier_frac=0.01, outlier_factor=20.0)
+    wq_d = torch.zeros(N * q.row_bytes("q4_0", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q4_0(_dev(torch, w), wq_d, N, K)
+    xq_d = torch.zeros(q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q8_0(_dev(torch, x), xq_d, 1, K)
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    q.qmm_matvec_q4_0(wq_d, xq_d, y, N, K)
+    torch.cuda.synchronize()
+    wq = orc.quantize_q4_0_w(w)
+    xq = orc.quantize_q8_0(x)
+    assert np.array_equal(wq_d.cpu().numpy().reshape(wq.shape), wq)
+    assert np.array_equal(xq_d.cpu().numpy().reshape(xq.shape), xq)
+    ref = orc.matmul("q4_0", wq, xq, 1, N, K, threads=8, want=("y64", "mag"))
+    _check(y.cpu().numpy(), ref["y64"][0], ref["mag"][0], "decode e2e")
+
+
+def test_outputs_are_overwritten_not_accumulated(env):
+    torch, q, orc = env
+    N, K = 64, 256
+    wq, xq = _inputs("q4_0", 1, N, K, 8000)
+    y1 = _run_matvec(env, "q4_0", wq, xq, N, K)
+    wd, xd = _dev(torch, wq), _dev(torch, xq)
+    y = torch.full((N,), 1e30, dtype=torch.float32, device="cuda")
+    q.qmm_matvec_q4_0(wd, xd, y, N, K)
+    q.qmm_matvec_q4_0(wd, xd, y, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y1)
+
+
+def test_device_errors_are_reported(env):
+    torch, q, _ = env
+    buf = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_matvec_q4_0(buf, buf[4:], buf, 4, 64)
+    assert e.value.code == "QMM_E_ALIGN"
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_matmul_q2_k(buf, buf, buf, 1, 1, 100)
+    assert e.value.code == "QMM_E_SHAPE"

@@ -2,138 +2,196 @@
 //
 // Decode is weight streaming: every weight byte is read once per token
 // (minfer section 2.1, "the decode physics"), so the kernel is bound by HBM
-// and is built around moving the weight bytes at full rate:
+// and is built to keep the weight stream moving at full rate:
 //   * a wave owns G consecutive rows (whole rows: every output is reduced
 //     inside one wave, in a fixed order, and written once -- minfer's row
-//     ownership);
-//   * the rows' bytes form one contiguous span; the wave copies it into its
-//     own LDS slice with coalesced 16-byte loads (Q4_0 / Q8_0 blocks are only
-//     2-byte aligned, so blocks are re-sliced from LDS instead of global);
-//   * each lane owns fixed block columns of the row, keeps the matching
-//     activation blocks in registers for the whole kernel, and runs packed
-//     int8 dot instructions (v_dot4c_i32_i8) on them;
-//   * the per-block scale product d_w*d_x is exact in f32 (two binary16
-//     values), so each block adds one correctly rounded term;
-//   * the lane partial sums of a row are combined with a shuffle tree.
-// For rows longer than one LDS slice (very large K) the wave walks the row in
-// segments and keeps its partial sums across them.
+//     ownership, the reason results do not depend on the launch shape);
+//   * the rows' bytes form one contiguous span, copied into the wave's own
+//     LDS slice by gfx950 LDS-DMA loads (global_load_lds_dwordx4: 16 bytes
+//     per lane, coalesced, no registers); Q4_0 / Q8_0 blocks are only 2-byte
+//     aligned, so blocks are re-sliced from LDS rather than loaded directly;
+//   * the activation row is DMA'd once per workgroup into LDS; each lane then
+//     owns fixed "units" of every row (a pair of blocks for Q4_0 / Q8_0 --
+//     with an even block count a pair starts 4-byte aligned -- or a quarter
+//     of a Q2_K super-block), keeps the matching activation codes in
+//     registers and reuses them for all G rows;
+//   * integer block sums come from v_dot4_i32_i8; the per-block scale product
+//     d_w*d_x of two binary16 values is exact in f32, so each block adds one
+//     correctly rounded term;
+//   * the G row sums are reduced across the wave by a transposing butterfly
+//     (log2(G) exchange steps that halve the live values, then plain steps).
+// Rows longer than one segment (64*MAXU units) are walked in segments with
+// the partial sums kept in registers (only with G = 1).
 #include "qmm_device.h"
 
 namespace qmm {
 
 enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2 };
 
-template <int F> struct MvTraits;
-template <> struct MvTraits<F_Q4_0> { static constexpr int BB = kQ40Bytes, XB = kQ80Bytes, UPB = 1, MAXU = 8; };
-template <> struct MvTraits<F_Q8_0> { static constexpr int BB = kQ80Bytes, XB = kQ80Bytes, UPB = 1, MAXU = 4; };
-template <> struct MvTraits<F_Q2_K> { static constexpr int BB = kQ2KBytes, XB = kQ8KBytes, UPB = 4, MAXU = 4; };
+template <int F> struct FmtBytes;
+template <> struct FmtBytes<F_Q4_0> { static constexpr int BB = kQ40Bytes, XB = kQ80Bytes; };
+template <> struct FmtBytes<F_Q8_0> { static constexpr int BB = kQ80Bytes, XB = kQ80Bytes; };
+template <> struct FmtBytes<F_Q2_K> { static constexpr int BB = kQ2KBytes, XB = kQ8KBytes; };
 
-// Activation registers for one unit a lane owns.
-template <int F> struct XUnit;
-template <> struct XUnit<F_Q4_0> { int q[8]; int sx8; float d; };
-template <> struct XUnit<F_Q8_0> { int q[8]; float d; };
-template <> struct XUnit<F_Q2_K> { int q[16]; int bs[4]; float d; };
+// A unit is what one lane handles per row: P blocks (P = 2 paired, 1 single)
+// of Q4_0 / Q8_0, or a quarter of a Q2_K super-block.
+template <int F, bool PAIRED> struct Unit {
+    static constexpr int BPU = PAIRED ? 2 : 1;        // blocks per unit
+    static constexpr int UPB = 1;                     // units per block
+};
+template <bool PAIRED> struct Unit<F_Q2_K, PAIRED> {
+    static constexpr int BPU = 1;
+    static constexpr int UPB = 4;
+};
 
-// --- activation loads (global, once per segment) ----------------------------
-// Q8_0 block c: f16 d at byte 34c, codes at 34c+2 (2-byte aligned).  Nine
-// aligned dwords cover the codes; the ninth is read only when needed and then
-// lies in the same aligned dword as the block's last byte.
-__device__ __forceinline__ void load_x_q8_0(const uint8_t *xq, int c, int *q, float &d) {
-    const uint32_t o = 34u * (uint32_t)c;
+// Activation registers of one unit.
+template <int F, bool PAIRED> struct XU {
+    int q[8 * Unit<F, PAIRED>::BPU];
+    float d[Unit<F, PAIRED>::BPU];
+    int sx8[Unit<F, PAIRED>::BPU];                    // 8 * sum of codes (Q4_0 only)
+};
+template <bool PAIRED> struct XU<F_Q2_K, PAIRED> {
+    int q[16];
+    int bs[4];
+    float d;
+};
+
+// --- LDS readers -------------------------------------------------------------
+// Q8_0 block (f16 d, 32 codes) at a 2-byte aligned LDS byte offset o.
+__device__ __forceinline__ void lds_q8_0_block(const uint8_t *l8, uint32_t o, int *q, float &d) {
+    const uint32_t *l32 = reinterpret_cast<const uint32_t *>(l8);
     const uint32_t qd = (o + 2) >> 2, qsh = (o + 2) & 3;
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(xq) + qd;
     uint32_t v[9];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = p[k];
-    v[8] = qsh ? p[8] : 0u;
+    for (int k = 0; k < 9; ++k) v[k] = l32[qd + k];
 #pragma unroll
     for (int k = 0; k < 8; ++k) q[k] = (int)align_bytes(v[k + 1], v[k], qsh);
-    d = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(xq + o));
+    d = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(l8 + o));
 }
 
-template <int F>
-__device__ __forceinline__ void load_x(const uint8_t *xq, int u, XUnit<F> &x);
-
-template <>
-__device__ __forceinline__ void load_x<F_Q4_0>(const uint8_t *xq, int u, XUnit<F_Q4_0> &x) {
-    load_x_q8_0(xq, u, x.q, x.d);
-    int s = 0;
+template <int F, bool PAIRED>
+__device__ __forceinline__ void load_xu(const uint8_t *xl, uint32_t xoff, int u, XU<F, PAIRED> &x) {
+    constexpr int P = Unit<F, PAIRED>::BPU;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s = dot4(x.q[k], 0x01010101, s);
-    x.sx8 = 8 * s;                 // sum_j (n_j - 8) q_j = sum_j n_j q_j - 8 sum_j q_j
+    for (int j = 0; j < P; ++j) {
+        lds_q8_0_block(xl, xoff + (uint32_t)(P * u + j) * kQ80Bytes, x.q + 8 * j, x.d[j]);
+        int s = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s = dot4(x.q[8 * j + k], 0x01010101, s);
+        x.sx8[j] = 8 * s;            // sum_j (n_j - 8) q_j = sum_j n_j q_j - 8 sum_j q_j
+    }
 }
 
+// Q8_K unit u = (super-block c, part p): part p covers qs bytes [16p, 16p+16) of
+// the weight block, i.e. values 128h + 32s + 16(p&1) + [0,16), s < 4, h = p/2,
+// which are groups g = 8h + 2s + (p&1).  Q8_K blocks are 4-byte aligned.
 template <>
-__device__ __forceinline__ void load_x<F_Q8_0>(const uint8_t *xq, int u, XUnit<F_Q8_0> &x) {
-    load_x_q8_0(xq, u, x.q, x.d);
-}
-
-// Q8_K unit (c, p): part p of super-block c covers qs bytes [16p, 16p+16) of
-// the weight block, i.e. values 128h + 32s + 16(p&1) + [0,16) for s < 4, h = p/2,
-// which are groups g = 8h + 2s + (p&1).
-template <>
-__device__ __forceinline__ void load_x<F_Q2_K>(const uint8_t *xq, int u, XUnit<F_Q2_K> &x) {
+__device__ __forceinline__ void load_xu<F_Q2_K, false>(const uint8_t *xl, uint32_t xoff, int u,
+                                                       XU<F_Q2_K, false> &x) {
     const int c = u >> 2, p = u & 3, h = p >> 1, odd = p & 1;
-    const uint8_t *b = xq + (int64_t)c * kQ8KBytes;
+    const uint8_t *b = xl + xoff + (uint32_t)c * kQ8KBytes;
     const uint32_t *q32 = reinterpret_cast<const uint32_t *>(b + 4 + 128 * h + 16 * odd);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int k = 0; k < 4; ++k) x.q[4 * s + k] = (int)q32[8 * s + k];
-    const int16_t *bs = reinterpret_cast<const int16_t *>(b + 260 + 16 * h + 2 * odd);
+    const uint32_t *bs32 = reinterpret_cast<const uint32_t *>(b + 260 + 16 * h);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) x.bs[s] = bs[2 * s];
+    for (int s = 0; s < 4; ++s) x.bs[s] = (int)(int16_t)(bs32[s] >> (16 * odd));
     x.d = *reinterpret_cast<const float *>(b);
 }
 
-// --- one unit's contribution, weights read from the LDS slice ---------------
-template <int F>
-__device__ __forceinline__ float unit_dot(const uint8_t *lds8, uint32_t bo, int p, const XUnit<F> &x, float acc);
+// --- one unit of one row ------------------------------------------------------
+// Q4_0 block: I = sum_j (nib_j - 8) q_j with low nibbles = elements 0..15 and
+// high nibbles = 16..31 (minfer scalar kernel; ggml section 2).
+__device__ __forceinline__ int q4_isum(const uint32_t *qs, const int *x, int sx8) {
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        s = dot4((int)(qs[k] & 0x0f0f0f0fu), x[k], s);
+        s = dot4((int)((qs[k] >> 4) & 0x0f0f0f0fu), x[k + 4], s);
+    }
+    return s - sx8;
+}
 
-// Q4_0 block at LDS byte bo (even): f16 d, then 16 nibble bytes.  Low nibbles
-// are elements 0..15, high nibbles 16..31 (minfer scalar kernel; ggml sec. 2).
+template <int F, bool PAIRED>
+__device__ __forceinline__ float unit_dot(const uint8_t *sl, uint32_t bo, int u, const XU<F, PAIRED> &x, float acc);
+
+// Paired Q4_0 at a 4-byte aligned offset: 36 bytes = d0, qs0 (2-byte shifted),
+// d1, qs1 (aligned).
 template <>
-__device__ __forceinline__ float unit_dot<F_Q4_0>(const uint8_t *lds8, uint32_t bo, int, const XUnit<F_Q4_0> &x,
-                                                  float acc) {
-    const uint32_t *l32 = reinterpret_cast<const uint32_t *>(lds8);
+__device__ __forceinline__ float unit_dot<F_Q4_0, true>(const uint8_t *sl, uint32_t bo, int,
+                                                        const XU<F_Q4_0, true> &x, float acc) {
+    const uint32_t *l32 = reinterpret_cast<const uint32_t *>(sl + bo);
+    uint32_t v[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) v[k] = l32[k];
+    uint32_t qs0[4], qs1[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        qs0[k] = align_bytes(v[k + 1], v[k], 2);
+        qs1[k] = v[5 + k];
+    }
+    const float dw0 = f16_bits_to_f32(v[0]), dw1 = f16_bits_to_f32(v[4] >> 16);
+    acc = fmaf(dw0 * x.d[0], (float)q4_isum(qs0, x.q, x.sx8[0]), acc);
+    return fmaf(dw1 * x.d[1], (float)q4_isum(qs1, x.q + 8, x.sx8[1]), acc);
+}
+
+template <>
+__device__ __forceinline__ float unit_dot<F_Q4_0, false>(const uint8_t *sl, uint32_t bo, int,
+                                                         const XU<F_Q4_0, false> &x, float acc) {
+    const uint32_t *l32 = reinterpret_cast<const uint32_t *>(sl);
     const uint32_t qd = (bo + 2) >> 2, qsh = (bo + 2) & 3;
     uint32_t v[5];
 #pragma unroll
     for (int k = 0; k < 5; ++k) v[k] = l32[qd + k];
-    const float dw = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(lds8 + bo));
-    int s = 0;
+    uint32_t qs[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t q = align_bytes(v[k + 1], v[k], qsh);
-        s = dot4((int)(q & 0x0f0f0f0fu), x.q[k], s);
-        s = dot4((int)((q >> 4) & 0x0f0f0f0fu), x.q[k + 4], s);
+    for (int k = 0; k < 4; ++k) qs[k] = align_bytes(v[k + 1], v[k], qsh);
+    const float dw = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sl + bo));
+    return fmaf(dw * x.d[0], (float)q4_isum(qs, x.q, x.sx8[0]), acc);
+}
+
+// Paired Q8_0 at a 4-byte aligned offset: 68 bytes = d0, codes0 (2-byte
+// shifted), d1, codes1 (aligned).
+template <>
+__device__ __forceinline__ float unit_dot<F_Q8_0, true>(const uint8_t *sl, uint32_t bo, int,
+                                                        const XU<F_Q8_0, true> &x, float acc) {
+    const uint32_t *l32 = reinterpret_cast<const uint32_t *>(sl + bo);
+    uint32_t v[17];
+#pragma unroll
+    for (int k = 0; k < 17; ++k) v[k] = l32[k];
+    int s0 = 0, s1 = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        s0 = dot4((int)align_bytes(v[k + 1], v[k], 2), x.q[k], s0);
+        s1 = dot4((int)v[9 + k], x.q[8 + k], s1);
     }
-    return fmaf(dw * x.d, (float)(s - x.sx8), acc);
+    const float dw0 = f16_bits_to_f32(v[0]), dw1 = f16_bits_to_f32(v[8] >> 16);
+    acc = fmaf(dw0 * x.d[0], (float)s0, acc);
+    return fmaf(dw1 * x.d[1], (float)s1, acc);
 }
 
 template <>
-__device__ __forceinline__ float unit_dot<F_Q8_0>(const uint8_t *lds8, uint32_t bo, int, const XUnit<F_Q8_0> &x,
-                                                  float acc) {
-    const uint32_t *l32 = reinterpret_cast<const uint32_t *>(lds8);
-    const uint32_t qd = (bo + 2) >> 2, qsh = (bo + 2) & 3;
-    uint32_t v[9];
-#pragma unroll
-    for (int k = 0; k < 9; ++k) v[k] = l32[qd + k];
-    const float dw = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(lds8 + bo));
+__device__ __forceinline__ float unit_dot<F_Q8_0, false>(const uint8_t *sl, uint32_t bo, int,
+                                                         const XU<F_Q8_0, false> &x, float acc) {
+    int q[8];
+    float dw;
+    lds_q8_0_block(sl, bo, q, dw);
     int s = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s = dot4((int)align_bytes(v[k + 1], v[k], qsh), x.q[k], s);
-    return fmaf(dw * x.d, (float)s, acc);
+    for (int k = 0; k < 8; ++k) s = dot4(q[k], x.q[k], s);
+    return fmaf(dw * x.d[0], (float)s, acc);
 }
 
-// Q2_K part p of the block at LDS byte bo (4-byte aligned):
+// Q2_K part p of the super-block at a 4-byte aligned offset:
 //   V = sum_s sc_s * sum q x,  Mn = sum_s m_s * bsum_s,
 //   t = d d8 V - dmin d8 Mn   (minfer "a K-quant dot kernel, walked").
 template <>
-__device__ __forceinline__ float unit_dot<F_Q2_K>(const uint8_t *lds8, uint32_t bo, int p, const XUnit<F_Q2_K> &x,
-                                                  float acc) {
-    const uint32_t *b32 = reinterpret_cast<const uint32_t *>(lds8 + bo);
-    const int h = p >> 1, odd = p & 1;
+__device__ __forceinline__ float unit_dot<F_Q2_K, false>(const uint8_t *sl, uint32_t bo, int u,
+                                                         const XU<F_Q2_K, false> &x, float acc) {
+    const int p = u & 3, h = p >> 1, odd = p & 1;
+    const uint32_t *b32 = reinterpret_cast<const uint32_t *>(sl + bo);
     uint32_t q[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) q[k] = b32[4 + 4 * p + k];
@@ -155,100 +213,205 @@ __device__ __forceinline__ float unit_dot<F_Q2_K>(const uint8_t *lds8, uint32_t 
     return fmaf(-(dmin * x.d), (float)Mn, acc);
 }
 
+// --- wave-uniform helpers -----------------------------------------------------
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+#define QMM_VMCNT_CASE(n) \
+    case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
+// Wait until at most n vector-memory loads of this wave are outstanding
+// (n wave-uniform; above 30 it waits for all of them, which is only stricter).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (uniform(n)) {
+        QMM_VMCNT_CASE(0) QMM_VMCNT_CASE(1) QMM_VMCNT_CASE(2) QMM_VMCNT_CASE(3) QMM_VMCNT_CASE(4)
+        QMM_VMCNT_CASE(5) QMM_VMCNT_CASE(6) QMM_VMCNT_CASE(7) QMM_VMCNT_CASE(8) QMM_VMCNT_CASE(9)
+        QMM_VMCNT_CASE(10) QMM_VMCNT_CASE(11) QMM_VMCNT_CASE(12) QMM_VMCNT_CASE(13) QMM_VMCNT_CASE(14)
+        QMM_VMCNT_CASE(15) QMM_VMCNT_CASE(16) QMM_VMCNT_CASE(17) QMM_VMCNT_CASE(18) QMM_VMCNT_CASE(19)
+        QMM_VMCNT_CASE(20) QMM_VMCNT_CASE(21) QMM_VMCNT_CASE(22) QMM_VMCNT_CASE(23) QMM_VMCNT_CASE(24)
+        QMM_VMCNT_CASE(25) QMM_VMCNT_CASE(26) QMM_VMCNT_CASE(27) QMM_VMCNT_CASE(28) QMM_VMCNT_CASE(29)
+        QMM_VMCNT_CASE(30)
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+#undef QMM_VMCNT_CASE
+
+// Copy bytes [lo, hi) of global memory into LDS at `dst` (16-byte aligned), as
+// the 16-byte chunks from lo & ~15 up to the chunk holding byte hi-1; chunk c
+// lands at dst + 16 c.  This wave issues the chunk groups (64 chunks, one
+// instruction each) k = first, first+step, ...; every lane of an issued
+// instruction loads (lanes past the end re-load the last chunk, into slots of
+// the group that are never read), so the number of instructions this wave
+// issued is exactly the return value.  Global reads never pass the 16-byte
+// granule that holds byte hi-1.
+__device__ __forceinline__ int dma_span(const uint8_t *src, int64_t lo, int64_t hi, uint4 *dst, int lane,
+                                        int first, int step) {
+    const int64_t A = lo & ~(int64_t)15;
+    const int nch = (int)((((hi + 15) & ~(int64_t)15) - A) >> 4);
+    int issued = 0;
+    for (int k = first; k * kWave < nch; k += step) {
+        const int c = min(k * kWave + lane, nch - 1);
+        global_to_lds16(src + A + 16 * (int64_t)c, dst + k * kWave);
+        ++issued;
+    }
+    return issued;
+}
+
 // --- the kernel ---------------------------------------------------------------
+// Dynamic LDS: [activation segment: xs bytes][4 wave slices of ss bytes].
 // gridDim.y tokens: token t reads activation row t (xrow bytes apart) and
 // writes output row t; the weight rows are re-read for every token.
-template <int F, int LPR>
+template <int F, bool PAIRED, int G, int MAXU>
 __global__ __launch_bounds__(256) void k_matvec(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
-                                                float *__restrict__ y, int N, int nb, int64_t xrow) {
-    using T = MvTraits<F>;
-    xq += (int64_t)blockIdx.y * xrow;
+                                                float *__restrict__ y, int N, int nb, int64_t xrow, int xs,
+                                                int ss) {
+    using FB = FmtBytes<F>;
+    using UT = Unit<F, PAIRED>;
+    extern __shared__ uint4 lds_dyn[];
+    constexpr int SEGU = kWave * MAXU;                 // units per segment
+
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int64_t xtok = (int64_t)blockIdx.y * xrow;   // byte offset of this token's activation row
     y += (int64_t)blockIdx.y * N;
-    constexpr int G = kWave / LPR;                       // rows per wave
-    constexpr int SEGU = LPR * T::MAXU;                  // units per segment
-    constexpr int SEGB = SEGU / T::UPB;                  // blocks per segment
-    constexpr int LDSW = ((G * SEGB * T::BB + 31) / 16 + 1) * 16;   // bytes per wave slice
-    constexpr int CH = (LDSW / 16 + kWave - 1) / kWave;  // 16-byte chunks per lane
-    __shared__ uint4 lds_all[4 * (LDSW / 16)];
-
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * G;
-    if (row0 >= N) return;                               // whole wave
-    const int nrows = (int)min((int64_t)G, (int64_t)N - row0);
-    const int lg = lane / LPR, li = lane % LPR;
-    const int64_t RB = (int64_t)nb * T::BB;
-    uint4 *lds = lds_all + wave * (LDSW / 16);
-    const uint8_t *lds8 = reinterpret_cast<const uint8_t *>(lds);
+    const int nrows = (int)max((int64_t)0, min((int64_t)G, (int64_t)N - row0));
+    const int64_t RB = (int64_t)nb * FB::BB;
+    const int nu = (nb / UT::BPU) * UT::UPB;           // units per row
+    uint4 *xlds = lds_dyn;
+    uint4 *slice = lds_dyn + xs / 16 + wave * (ss / 16);
+    const uint8_t *xl8 = reinterpret_cast<const uint8_t *>(xlds);
+    const uint8_t *sl8 = reinterpret_cast<const uint8_t *>(slice);
 
-    float acc = 0.0f;
-    for (int seg0 = 0; seg0 < nb; seg0 += SEGB) {
-        const int seg1 = min(nb, seg0 + SEGB);
-        const int64_t lo = row0 * RB + (int64_t)seg0 * T::BB;
-        const int64_t hi = (row0 + nrows - 1) * RB + (int64_t)seg1 * T::BB;
-        const int64_t A = lo & ~(int64_t)15;
-        const int nch = (int)((((hi + 15) & ~(int64_t)15) - A) >> 4);   // <= LDSW/16
-
-        // weights of the span -> this wave's LDS slice, straight from global
-        // (global_load_lds_dwordx4: lane i of a load fills bytes [16i, 16i+16)
-        // of the 1 KB at the wave-uniform LDS address; no VGPRs involved).
-        const uint8_t *src = w + A;
+    float acc[G];
 #pragma unroll
-        for (int k = 0; k < CH; ++k) {
-            const int c = k * kWave + lane;
-            if (c < nch) global_to_lds16(src + 16 * (int64_t)c, lds + k * kWave);
+    for (int r = 0; r < G; ++r) acc[r] = 0.0f;
+
+    for (int u0 = 0; u0 < nu; u0 += SEGU) {
+        const int u1 = min(nu, u0 + SEGU);
+        const int b0 = u0 / UT::UPB * UT::BPU, b1 = u1 / UT::UPB * UT::BPU;   // blocks of the segment
+        // activation bytes of the segment (all four waves share them)
+        const int64_t xlo = xtok + (int64_t)b0 * FB::XB, xhi = xtok + (int64_t)b1 * FB::XB;
+        const uint32_t xoff = (uint32_t)(xlo & 15);
+        dma_span(xq, xlo, xhi, xlds, lane, wave, 4);
+        // this wave's weight span
+        int wissued = 0;
+        int64_t A = 0;
+        if (nrows > 0) {
+            const int64_t lo = row0 * RB + (int64_t)b0 * FB::BB;
+            const int64_t hi = (row0 + nrows - 1) * RB + (int64_t)b1 * FB::BB;
+            A = lo & ~(int64_t)15;
+            wissued = dma_span(w, lo, hi, slice, lane, 0, 1);
         }
-        // this lane's activation units for the segment (L2-resident); a lane
-        // past the row end loads a valid unit and ignores it
-        XUnit<F> xu[T::MAXU];
-        const int ulast = seg1 * T::UPB - 1;
+        wait_vmcnt(wissued);                           // this wave's activation chunks have landed
+        __builtin_amdgcn_s_barrier();                  // ... and every other wave's
+        XU<F, PAIRED> xu[MAXU];
 #pragma unroll
-        for (int i = 0; i < T::MAXU; ++i) load_x<F>(xq, min(seg0 * T::UPB + li + i * LPR, ulast), xu[i]);
-        wait_global_loads();
-        __builtin_amdgcn_wave_barrier();
-
-        if (lg < nrows) {
-            const uint32_t rbase = (uint32_t)((row0 + lg) * RB + (int64_t)seg0 * T::BB - A);
+        for (int i = 0; i < MAXU; ++i) load_xu<F, PAIRED>(xl8, xoff, min(lane + kWave * i, u1 - u0 - 1), xu[i]);
+        if (nrows > 0) {
 #pragma unroll
-            for (int i = 0; i < T::MAXU; ++i) {
-                const int u = seg0 * T::UPB + li + i * LPR;
-                if (u < seg1 * T::UPB) {
-                    const int c = u / T::UPB - seg0;
-                    acc = unit_dot<F>(lds8, rbase + (uint32_t)c * T::BB, u % T::UPB, xu[i], acc);
+            for (int r = 0; r < G; ++r) {
+                if (r < nrows) {
+                    const uint32_t ro = (uint32_t)((row0 + r) * RB + (int64_t)b0 * FB::BB - A);
+                    // row r's bytes end in chunk group kr; the groups after it may
+                    // still be in flight while this row is computed
+                    const int64_t rend = (row0 + r) * RB + (int64_t)b1 * FB::BB;
+                    const int kr = (int)((rend - 1 - A) >> 10);
+                    wait_vmcnt(wissued - 1 - kr);
+#pragma unroll
+                    for (int i = 0; i < MAXU; ++i) {
+                        const int ul = lane + kWave * i;            // unit within the segment
+                        if (ul < u1 - u0) {
+                            const uint32_t bo = ro + (uint32_t)(ul / UT::UPB * UT::BPU) * FB::BB;
+                            acc[r] = unit_dot<F, PAIRED>(sl8, bo, u0 + ul, xu[i], acc[r]);
+                        }
+                    }
                 }
             }
         }
-        if (seg1 < nb) {      // the slice is rewritten by the next segment
+        wait_vmcnt(0);
+        if (u1 < nu) {                                 // the LDS is refilled for the next segment
             wait_lds_reads();
-            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_s_barrier();
         }
     }
+    if (nrows == 0) return;
+
+    // transposing butterfly: at step `bit` (32, 16, ...) a lane keeps half of its
+    // live row sums and adds its partner's copy of that half.
+    int cnt = G;
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) acc += xor_shfl(acc, m);
-    if (li == 0 && lg < nrows) y[row0 + lg] = acc;
+    for (int bit = 32; bit >= 1; bit >>= 1) {
+        if (cnt > 1) {
+            const bool hi = (lane & bit) != 0;
+#pragma unroll
+            for (int j = 0; j < G / 2; ++j) {
+                if (j < cnt / 2) {
+                    const float keep = hi ? acc[j + cnt / 2] : acc[j];
+                    const float send = hi ? acc[j] : acc[j + cnt / 2];
+                    acc[j] = keep + xor_shfl(send, bit);
+                }
+            }
+            cnt >>= 1;
+        } else {
+            acc[0] += xor_shfl(acc[0], bit);
+        }
+    }
+    constexpr int LPR = kWave / G;                     // lanes holding copies of one row's sum
+    const int r = lane / LPR;
+    if (lane % LPR == 0 && r < nrows) y[row0 + r] = acc[0];
 }
 
-template <int F, int LPR>
+// --- launch configuration -----------------------------------------------------
+template <int F, bool PAIRED, int G, int MAXU>
 static hipError_t launch_mv(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
-    constexpr int G = kWave / LPR;
+    using FB = FmtBytes<F>;
+    using UT = Unit<F, PAIRED>;
+    const int nu = (nb / UT::BPU) * UT::UPB;
+    const int segu = min(nu, kWave * MAXU);
+    const int segb = (segu + UT::UPB - 1) / UT::UPB * UT::BPU;
+    const int64_t span = (G == 1) ? (int64_t)segb * FB::BB : (int64_t)G * nb * FB::BB;
+    // whole 1 KB chunk groups (dma_span may fill a full last group) after up to
+    // 15 bytes of misalignment at each end
+    const int ss = (int)(((span + 32 + 1023) / 1024) * 1024);
+    const int xs = (int)((((int64_t)segb * FB::XB + 32 + 1023) / 1024) * 1024);
     const int64_t waves = ((int64_t)N + G - 1) / G;
     const int64_t grid = (waves + 3) / 4;
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
-    int64_t xrow = (int64_t)nb * MvTraits<F>::XB;
-    void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&N, (void *)&nb, (void *)&xrow};
-    return hipLaunchKernel((const void *)k_matvec<F, LPR>, dim3((unsigned)grid, (unsigned)M), dim3(256), args, 0,
-                           st);
+    int64_t xrow = (int64_t)nb * FB::XB;
+    void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&N, (void *)&nb,
+                    (void *)&xrow, (void *)&xs, (void *)&ss};
+    return hipLaunchKernel((const void *)k_matvec<F, PAIRED, G, MAXU>, dim3((unsigned)grid, (unsigned)M),
+                           dim3(256), args, (size_t)(xs + 4 * ss), st);
 }
 
-// Lanes per row: the smallest of 16 / 32 / 64 whose lanes cover a whole row
-// in one segment (so several rows share a wave and its loads), else 64.
+// Rows per wave: enough for a ~16 KB slice (fewer rows means more waves but
+// less reuse of the activation registers); one row when the row needs more
+// than one segment.
+template <int F, bool PAIRED>
+static hipError_t pick_mv(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    using FB = FmtBytes<F>;
+    using UT = Unit<F, PAIRED>;
+    const int nu = (nb / UT::BPU) * UT::UPB;
+    const int64_t rb = (int64_t)nb * FB::BB;
+    if (nu > kWave * 4) return launch_mv<F, PAIRED, 1, 4>(w, xq, y, M, N, nb, st);
+    const int64_t g = 16384 / rb;
+    if (nu <= kWave) {
+        if (g >= 8) return launch_mv<F, PAIRED, 8, 1>(w, xq, y, M, N, nb, st);
+        if (g >= 4) return launch_mv<F, PAIRED, 4, 1>(w, xq, y, M, N, nb, st);
+        if (g >= 2) return launch_mv<F, PAIRED, 2, 1>(w, xq, y, M, N, nb, st);
+        return launch_mv<F, PAIRED, 1, 1>(w, xq, y, M, N, nb, st);
+    }
+    if (g >= 4) return launch_mv<F, PAIRED, 4, 4>(w, xq, y, M, N, nb, st);
+    if (g >= 2) return launch_mv<F, PAIRED, 2, 4>(w, xq, y, M, N, nb, st);
+    return launch_mv<F, PAIRED, 1, 4>(w, xq, y, M, N, nb, st);
+}
+
 template <int F>
 static hipError_t dispatch_mv(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
-    using T = MvTraits<F>;
-    const int64_t units = (int64_t)nb * T::UPB;
-    if (units <= 16 * T::MAXU) return launch_mv<F, 16>(w, xq, y, M, N, nb, st);
-    if (units <= 32 * T::MAXU) return launch_mv<F, 32>(w, xq, y, M, N, nb, st);
-    return launch_mv<F, 64>(w, xq, y, M, N, nb, st);
+    if constexpr (F != F_Q2_K) {
+        if (nb % 2 == 0) return pick_mv<F, true>(w, xq, y, M, N, nb, st);
+    }
+    return pick_mv<F, false>(w, xq, y, M, N, nb, st);
 }
 
 hipError_t launch_matvec_q4_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st) {

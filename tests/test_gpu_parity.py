@@ -150,6 +150,7 @@ MATVEC_CASES = [
     ("q4_0", 12288, 4096),   # FFN-gate decode
     ("q4_0", 1, 32), ("q4_0", 3, 96), ("q4_0", 17, 160), ("q4_0", 5, 2080), ("q4_0", 7, 8192),
     ("q4_0", 9, 20480),      # two row segments
+    ("q4_0", 45, 1024), ("q8_0", 37, 256), ("q8_0", 3, 64),     # 8 rows per wave, ragged last wave
     ("q8_0", 12288, 4096), ("q8_0", 22016, 4096), ("q8_0", 4096, 11008),   # one 7B-style layer
     ("q8_0", 1, 32), ("q8_0", 5, 96), ("q8_0", 11, 4128), ("q8_0", 3, 20000),
     ("q2_k", 12288, 4096),
@@ -267,3 +268,42 @@ def test_device_errors_are_reported(env):
     with pytest.raises(q.QmmError) as e:
         q.qmm_matmul_q2_k(buf, buf, buf, 1, 1, 100)
     assert e.value.code == "QMM_E_SHAPE"
+
+
+def test_graph_replay_matches_eager(env):
+    """Decode and prefill launches captured into a HIP graph: every replay, with
+    eager work and synchronizations in between, equals the eager result bit for
+    bit (the kernels are deterministic and keep no state)."""
+    torch, q, orc = env
+    N, K, M = 1024, 4096, 64
+    w = synth.weights(N, K, config=1)
+    x = synth.activations(M, K, config=4)
+    wq = _dev(torch, orc.quantize_q4_0_w(w))
+    xd = _dev(torch, x)
+    xq = torch.empty(M * q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
+    yv = torch.empty(N, dtype=torch.float32, device="cuda")
+    ym = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def work():
+        q.qmm_quantize_q8_0(xd, xq, M, K)
+        q.qmm_matvec_q4_0(wq, xq, yv, N, K)
+        q.qmm_matmul_q4_0(wq, xq, ym, M, N, K)
+
+    work()
+    torch.cuda.synchronize()
+    ref_v, ref_m, ref_q = yv.clone(), ym.clone(), xq.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(4):
+        yv.fill_(float("nan"))
+        ym.fill_(float("nan"))
+        xq.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xq, ref_q), rep
+        assert torch.equal(yv, ref_v), rep
+        assert torch.equal(ym, ref_m), rep
+        work()                      # eager work between replays
+        torch.cuda.synchronize()

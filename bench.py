@@ -12,8 +12,8 @@ kernels per step from Python would measure the interpreter, not the GPU).
 
 Also in the line: the prefill matmul (M = 2048, same weights), int8 TOP/s;
 for each, the dominant kernel's roofline (achieved / MI355X peak, with the
-average kernel time from HIP events on the launch stream around batches of
-back-to-back launches of that kernel) and the oracle timed on the host cores
+average kernel time from HIP events on the launch stream around graph
+replays of batches of back-to-back launches of that kernel) and the oracle timed on the host cores
 over a bounded sample of the same workload.
 
 Synthetic data: seeded Gaussian weights (std 0.02) and activations (std 1,
@@ -51,26 +51,34 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of each oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies-mb", type=float, default=600.0, help="total size of the rotated weight copies")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run one plain 256 MiB device-to-device copy (scales HBM byte counters)")
     return ap.parse_args()
 
 
 def time_batches(torch, launch, count, batch):
-    """Mean duration of one launch: HIP events on the launch stream around
-    batches of `batch` back-to-back launches (launch(i), i = 0..count-1).
-    Back-to-back launches leave the kernel's own time plus the short dispatch
-    gap between kernels, which makes this a slight over-estimate."""
+    """Mean duration of one launch of a kernel: `batch` back-to-back launches
+    (launch(i), i = 0..batch-1) are captured into a HIP graph, the graph is
+    replayed count // batch times, and HIP events on the launch stream bracket
+    each replay.  The mean includes the short gap between consecutive kernels
+    of a graph, so it slightly over-states the kernel's own duration.  (Timing
+    Python launches instead would measure the interpreter for kernels of a few
+    microseconds.)"""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(batch):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
     nb = max(1, count // batch)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nb)]
-    i = 0
     for a, b in ev:
         a.record()
-        for _ in range(batch):
-            launch(i)
-            i += 1
+        g.replay()
         b.record()
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) / batch for a, b in ev]
-    return sum(per) / len(per), min(per), i
+    return sum(per) / len(per), min(per), nb * batch
 
 
 def bench_decode(args, torch, q, synth):
@@ -166,7 +174,7 @@ def bench_prefill(args, torch, q, synth):
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.prefill_steps
     mm_ms, mm_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q4_0(wq, Xq, Y, M, N, K),
-                                    args.prefill_steps, 5)
+                                    args.prefill_steps, 4)
     ops = 2.0 * M * N * K
     log(f"prefill: {ms_step * 1e3:.1f} us/step, matmul {mm_ms * 1e3:.1f} us (best batch {mm_min * 1e3:.1f})")
     tops_kernel = ops / (mm_ms * 1e-3) / 1e12
@@ -238,6 +246,15 @@ def main():
     q.lib()
     torch.cuda.set_device(0)
     log(f"device {torch.cuda.get_device_name(0)}")
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}), flush=True)
+        return
 
     dec = bench_decode(args, torch, q, synth) if args.only in ("all", "decode") else None
     pre = bench_prefill(args, torch, q, synth) if args.only in ("all", "prefill") else None

@@ -213,27 +213,6 @@ __device__ __forceinline__ float unit_dot<F_Q2_K, false>(const uint8_t *sl, uint
     return fmaf(-(dmin * x.d), (float)Mn, acc);
 }
 
-// --- wave-uniform helpers -----------------------------------------------------
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-#define QMM_VMCNT_CASE(n) \
-    case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
-// Wait until at most n vector-memory loads of this wave are outstanding
-// (n wave-uniform; above 30 it waits for all of them, which is only stricter).
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    switch (uniform(n)) {
-        QMM_VMCNT_CASE(0) QMM_VMCNT_CASE(1) QMM_VMCNT_CASE(2) QMM_VMCNT_CASE(3) QMM_VMCNT_CASE(4)
-        QMM_VMCNT_CASE(5) QMM_VMCNT_CASE(6) QMM_VMCNT_CASE(7) QMM_VMCNT_CASE(8) QMM_VMCNT_CASE(9)
-        QMM_VMCNT_CASE(10) QMM_VMCNT_CASE(11) QMM_VMCNT_CASE(12) QMM_VMCNT_CASE(13) QMM_VMCNT_CASE(14)
-        QMM_VMCNT_CASE(15) QMM_VMCNT_CASE(16) QMM_VMCNT_CASE(17) QMM_VMCNT_CASE(18) QMM_VMCNT_CASE(19)
-        QMM_VMCNT_CASE(20) QMM_VMCNT_CASE(21) QMM_VMCNT_CASE(22) QMM_VMCNT_CASE(23) QMM_VMCNT_CASE(24)
-        QMM_VMCNT_CASE(25) QMM_VMCNT_CASE(26) QMM_VMCNT_CASE(27) QMM_VMCNT_CASE(28) QMM_VMCNT_CASE(29)
-        QMM_VMCNT_CASE(30)
-        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    }
-}
-#undef QMM_VMCNT_CASE
-
 // Copy bytes [lo, hi) of global memory into LDS at `dst` (16-byte aligned), as
 // the 16-byte chunks from lo & ~15 up to the chunk holding byte hi-1; chunk c
 // lands at dst + 16 c.  This wave issues the chunk groups (64 chunks, one
@@ -378,15 +357,20 @@ static hipError_t launch_mv(const void *w, const void *xq, float *y, int M, int 
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
     int64_t xrow = (int64_t)nb * FB::XB;
+    static int lds_ok = 0;
+    const hipError_t e = allow_dynamic_lds((const void *)k_matvec<F, PAIRED, G, MAXU>, (size_t)(xs + 4 * ss), lds_ok);
+    if (e != hipSuccess) return e;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&N, (void *)&nb,
                     (void *)&xrow, (void *)&xs, (void *)&ss};
     return hipLaunchKernel((const void *)k_matvec<F, PAIRED, G, MAXU>, dim3((unsigned)grid, (unsigned)M),
                            dim3(256), args, (size_t)(xs + 4 * ss), st);
 }
 
-// Rows per wave: enough for a ~16 KB slice (fewer rows means more waves but
-// less reuse of the activation registers); one row when the row needs more
-// than one segment.
+// Rows per wave: a slice of about 5 KB.  Measured on MI355X over 28-96 MB
+// of weights, slices of 3-5 KB per wave (Q4_0 K=4096: 2 rows, Q8_0: 1 row,
+// Q2_K: 2 rows) beat larger ones: the work after the last byte lands is
+// smaller and all waves of the launch stay resident.  One row when the row
+// needs more than one segment.
 template <int F, bool PAIRED>
 static hipError_t pick_mv(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
     using FB = FmtBytes<F>;
@@ -394,7 +378,7 @@ static hipError_t pick_mv(const void *w, const void *xq, float *y, int M, int N,
     const int nu = (nb / UT::BPU) * UT::UPB;
     const int64_t rb = (int64_t)nb * FB::BB;
     if (nu > kWave * 4) return launch_mv<F, PAIRED, 1, 4>(w, xq, y, M, N, nb, st);
-    const int64_t g = 16384 / rb;
+    const int64_t g = 5000 / rb;
     if (nu <= kWave) {
         if (g >= 8) return launch_mv<F, PAIRED, 8, 1>(w, xq, y, M, N, nb, st);
         if (g >= 4) return launch_mv<F, PAIRED, 4, 1>(w, xq, y, M, N, nb, st);

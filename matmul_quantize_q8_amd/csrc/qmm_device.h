@@ -55,6 +55,36 @@ __device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vm
 // Wait for every outstanding LDS access of this wave.
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Launch helper: kernels that use more than 64 KB of dynamic LDS raise their
+// limit once (gfx950 has 160 KB per workgroup).
+inline hipError_t allow_dynamic_lds(const void *kernel, size_t bytes, int &done) {
+    if (bytes <= 65536 || __atomic_load_n(&done, __ATOMIC_ACQUIRE)) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) __atomic_store_n(&done, 1, __ATOMIC_RELEASE);
+    return e;
+}
+
+// Wave-uniform helpers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+#define QMM_VMCNT_CASE(n) \
+    case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
+// Wait until at most n vector-memory loads of this wave are outstanding
+// (n wave-uniform; above 30 it waits for all of them, which is only stricter).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (uniform(n)) {
+        QMM_VMCNT_CASE(0) QMM_VMCNT_CASE(1) QMM_VMCNT_CASE(2) QMM_VMCNT_CASE(3) QMM_VMCNT_CASE(4)
+        QMM_VMCNT_CASE(5) QMM_VMCNT_CASE(6) QMM_VMCNT_CASE(7) QMM_VMCNT_CASE(8) QMM_VMCNT_CASE(9)
+        QMM_VMCNT_CASE(10) QMM_VMCNT_CASE(11) QMM_VMCNT_CASE(12) QMM_VMCNT_CASE(13) QMM_VMCNT_CASE(14)
+        QMM_VMCNT_CASE(15) QMM_VMCNT_CASE(16) QMM_VMCNT_CASE(17) QMM_VMCNT_CASE(18) QMM_VMCNT_CASE(19)
+        QMM_VMCNT_CASE(20) QMM_VMCNT_CASE(21) QMM_VMCNT_CASE(22) QMM_VMCNT_CASE(23) QMM_VMCNT_CASE(24)
+        QMM_VMCNT_CASE(25) QMM_VMCNT_CASE(26) QMM_VMCNT_CASE(27) QMM_VMCNT_CASE(28) QMM_VMCNT_CASE(29)
+        QMM_VMCNT_CASE(30)
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+#undef QMM_VMCNT_CASE
+
 template <typename T>
 __device__ __forceinline__ T xor_shfl(T v, int mask) {
     return __shfl_xor(v, mask, kWave);

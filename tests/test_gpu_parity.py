@@ -151,6 +151,8 @@ MATVEC_CASES = [
     ("q4_0", 1, 32), ("q4_0", 3, 96), ("q4_0", 17, 160), ("q4_0", 5, 2080), ("q4_0", 7, 8192),
     ("q4_0", 9, 20480),      # two row segments
     ("q4_0", 45, 1024), ("q8_0", 37, 256), ("q8_0", 3, 64),     # 8 rows per wave, ragged last wave
+    ("q4_0", 13, 2048), ("q4_0", 7, 4000),                       # 4 rows x 1 unit; 2 rows x 4 single units
+    ("q8_0", 5, 16384), ("q8_0", 3, 40960),                      # > 64 KB of LDS; paired segments
     ("q8_0", 12288, 4096), ("q8_0", 22016, 4096), ("q8_0", 4096, 11008),   # one 7B-style layer
     ("q8_0", 1, 32), ("q8_0", 5, 96), ("q8_0", 11, 4128), ("q8_0", 3, 20000),
     ("q2_k", 12288, 4096),
@@ -170,7 +172,8 @@ def test_matvec_matches_oracle(env, fmt, N, K):
 
 MATMUL_CASES = [
     ("q4_0", 1, 8, 32), ("q4_0", 37, 200, 1024), ("q4_0", 128, 128, 4096), ("q4_0", 130, 129, 160),
-    ("q4_0", 64, 512, 1024), ("q4_0", 5, 3, 96), ("q4_0", 256, 384, 4128),
+    ("q4_0", 64, 512, 1024), ("q4_0", 5, 3, 96), ("q4_0", 256, 384, 4128), ("q4_0", 300, 700, 2080),
+    ("q4_0", 129, 257, 64),
     ("q2_k", 1, 8, 256), ("q2_k", 9, 70, 1024), ("q2_k", 33, 130, 4096),
 ]
 

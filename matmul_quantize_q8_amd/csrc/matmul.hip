@@ -60,7 +60,7 @@ struct MmShared {
 };
 static_assert(sizeof(MmShared) <= 81920, "two workgroups per CU");
 
-__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0_any(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
                                                         float *__restrict__ y, int M, int N, int nb, int tiles_m) {
     using namespace mm;
     extern __shared__ uint4 lds_dyn[];
@@ -282,17 +282,353 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
         }
 }
 
-hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
-    const uint8_t *wp = static_cast<const uint8_t *>(w);
-    const uint8_t *xp = static_cast<const uint8_t *>(xq);
+static hipError_t launch_matmul_q4_0_any(const uint8_t *wp, const uint8_t *xp, float *y, int M, int N, int nb,
+                                         hipStream_t st) {
     int tiles_m = (M + mm::BM - 1) / mm::BM;
     const int64_t tiles = (int64_t)tiles_m * ((N + mm::BN - 1) / mm::BN);
     static int lds_ok = 0;
-    const hipError_t e = allow_dynamic_lds((const void *)k_matmul_q4_0, sizeof(MmShared), lds_ok);
+    const hipError_t e = allow_dynamic_lds((const void *)k_matmul_q4_0_any, sizeof(MmShared), lds_ok);
     if (e != hipSuccess) return e;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
-    return hipLaunchKernel((const void *)k_matmul_q4_0, dim3((unsigned)tiles), dim3(mm::NT), args,
+    return hipLaunchKernel((const void *)k_matmul_q4_0_any, dim3((unsigned)tiles), dim3(mm::NT), args,
                            sizeof(MmShared), st);
+}
+
+// ---------------------------------------------------------------------------
+// Even block count, so every row starts on a 4-byte boundary.  The K loop
+// moves two blocks per stage: 68 bytes (17 dwords) of each activation row and
+// 36 bytes (9 dwords) of each weight row.  A stage is copied into LDS by
+// buffer LDS-DMA loads of one dword per lane, 64 consecutive dwords per
+// instruction: the activation rows row-major at a 17-dword stride, the weight
+// rows at a 9-dword stride (odd strides, so a wave reading one dword of 32
+// different rows touches 32 different banks), then two scale planes: the
+// dword holding dx of block 0 (dword 0) and of block 1 (dword 8) for each of
+// the 128 activation rows, so that four consecutive rows' scales are one
+// 16-byte read.  Each lane's global offset for each of its 14 loads is fixed
+// for the whole K loop; the stage position rides in the scalar offset.
+//
+// Nothing is re-laid out: each wave reads its MFMA operands from those rows.
+// The stage's second block is 4-byte aligned (codes in dwords 9..16); the
+// first is not (its codes start 2 bytes into dword 0), so for it the
+// contraction order inside the block is rotated by two: lane half 0 takes
+// codes 2..17 (dwords 1..4) and half 1 takes codes 18..31, 0, 1 (dwords 5..7
+// and one v_perm of dwords 8 and 0).  The weight codes are unpacked in the
+// same order; the MFMA sums over the 32 byte positions, so any order that
+// both operands share gives the same I_b.
+// Weight nibbles are unpacked per wave as in the kernel above (16*(nib-8)),
+// and the fold is the same, except that dw enters as f16 (v_fma_mix) without
+// the 1/16: every accumulator is 16x too large and the store scales it back
+// (a power of two, exact).
+namespace mmr {
+constexpr int BM = 128;                  // tokens per workgroup tile
+constexpr int BN = 128;                  // weight rows per workgroup tile
+constexpr int NT = 256;                  // 4 waves, 2 x 2 of 64 x 64
+constexpr int XD = 17;                   // activation dwords per row per stage
+constexpr int WD = 9;                    // weight dwords per row per stage
+constexpr int WOFF = BM * XD;            // weight rows start (dwords into a stage buffer)
+constexpr int SOFF = WOFF + BN * WD;     // scale planes start
+constexpr int STAGE = SOFF + 2 * BM;     // 3584 dwords = 14,336 bytes
+constexpr int XQ = BM * XD / kWave;      // 34 wave loads of activation rows
+constexpr int WQ = BN * WD / kWave;      // 18 of weight rows
+constexpr int NQ = STAGE / kWave;        // 56 in all (the last 4 are the scale planes)
+constexpr int PER_WAVE = NQ / 4;         // 14
+constexpr int NBUF = 3;                  // stage buffers: DMA runs two stages ahead
+constexpr float kBias = 12582912.0f;     // 1.5 * 2^23, bit pattern 0x4B400000
+}  // namespace mmr
+static_assert(mmr::BM * mmr::XD % kWave == 0 && mmr::BN * mmr::WD % kWave == 0 && mmr::NQ % 4 == 0,
+              "stage image splits into whole wave loads, evenly over the waves");
+
+// 4 bytes per lane from a buffer into LDS: lane i's dword lands at LDS byte
+// m0base + OFF + 4i (m0base wave-uniform); the write completes with the
+// vector-memory counter.  Issued as inline assembly so that the compiler does
+// not see an LDS store: for the intrinsic it conservatively waits for every
+// outstanding LDS-DMA load before each later LDS read and before every
+// barrier, which would serialise the copy of stage s+2 with the work on stage
+// s.  The waits are explicit instead (vmcnt before the barrier that publishes
+// a stage).  M0 is formed inside the statement so that the compiler does not
+// keep one LDS address per load and stage alive in scalar registers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int OFF>
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t r, uint32_t m0base, uint32_t voff, int soff) {
+    asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(m0base), "v"(voff), "s"(r), "s"(soff), "i"(OFF) : "memory", "m0", "scc");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier that orders LDS accesses but does not wait for
+// outstanding vector-memory loads (the LDS-DMA copies in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(mmr::NT, 2) void k_matmul_q4_0(const uint8_t *__restrict__ w,
+                                                            const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                            int M, int N, int nb, int tiles_m) {
+    using namespace mmr;
+    __shared__ __attribute__((aligned(16))) uint32_t lds[NBUF * STAGE];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = uniform(t >> 6);
+    const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
+    const int m0 = mt * BM, n0 = nt * BN;
+    const uint32_t xrow = (uint32_t)nb * kQ80Bytes, wrow = (uint32_t)nb * kQ40Bytes;
+    const int nst = nb >> 1;
+
+    // DMA: wave w issues wave loads q = w, w+4, ..., w+52 of each stage.  Rows
+    // past the matrix re-read its last row; their results are not stored.
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xq + (int64_t)m0 * xrow), 0, (int)((uint32_t)min(M - m0, BM) * xrow), 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(w + (int64_t)n0 * wrow), 0, (int)((uint32_t)min(N - n0, BN) * wrow), 0x00020000);
+    uint32_t voff[PER_WAVE];
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+        const int q = wave + 4 * k;
+        if (q < XQ) {
+            const int f = kWave * q + lane, row = f / XD;
+            voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + 4u * (uint32_t)(f - XD * row);
+        } else if (q < XQ + WQ) {
+            const int f = kWave * (q - XQ) + lane, row = f / WD;
+            voff[k] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + 4u * (uint32_t)(f - WD * row);
+        } else {
+            const int p = q - XQ - WQ, row = kWave * (p & 1) + lane;   // plane p >> 1, rows 64(p & 1)...
+            voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (p >> 1 ? 32u : 0u);
+        }
+    }
+    // Wave load q = w + 4k lands at dwords 64q.. of the stage buffer: loads
+    // k = 0..7 are activation rows, k = 8 too for waves 0 and 1 (weight rows
+    // for waves 2 and 3), k = 9..12 weight rows, k = 13 a scale plane.
+    // the low half of a generic LDS address is the LDS offset
+    const uint32_t lds_w = (uint32_t)uniform((int)((uint32_t)reinterpret_cast<uintptr_t>(lds) + 256u * wave));
+    auto dma_load = [&](auto kc, uint32_t base, int sx, int sw) {
+        constexpr int k = decltype(kc)::value;
+        const bool isw = k == 8 ? wave >= 2 : (k >= 9 && k <= 12);
+        buffer_to_lds4<k * 1024>(isw ? wr : xr, base, voff[k], isw ? sw : sx);
+    };
+    // loads 2p and 2p+1 of stage s into buffer b
+    auto dma_pair = [&](auto pc, int s, int b) {
+        constexpr int p = decltype(pc)::value;
+        const uint32_t base = lds_w + (uint32_t)(b * STAGE * 4);
+        const int sx = s * (2 * kQ80Bytes), sw = s * (2 * kQ40Bytes);
+        dma_load(std::integral_constant<int, 2 * p>(), base, sx, sw);
+        dma_load(std::integral_constant<int, 2 * p + 1>(), base, sx, sw);
+    };
+    auto dma = [&](int s, int b) {
+        dma_pair(std::integral_constant<int, 0>(), s, b);
+        dma_pair(std::integral_constant<int, 1>(), s, b);
+        dma_pair(std::integral_constant<int, 2>(), s, b);
+        dma_pair(std::integral_constant<int, 3>(), s, b);
+        dma_pair(std::integral_constant<int, 4>(), s, b);
+        dma_pair(std::integral_constant<int, 5>(), s, b);
+        dma_pair(std::integral_constant<int, 6>(), s, b);
+    };
+    static_assert(XQ == 34 && WQ == 18 && PER_WAVE == 14, "the load list above is written for this split");
+
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int xz = (64 * wm + lr) * XD;          // dword 0 of A row 64wm+lr (tile i: +32 rows)
+    const int xa = xz + 4 * lh;                  // the lane half's first code dword, less one
+    const int wb = WOFF + (64 * wn + lr) * WD;   // B row 64wn+lr (tile j: +32 rows)
+    const int xs = SOFF + 64 * wm + 4 * lh;      // scale plane: first of 4 rows a lane needs
+    // byte selectors (v_perm: 0-3 pick the second source, 4-7 the first)
+    const uint32_t selA = lh ? 0x03020504u : 0x07060504u;   // half 1: codes 30, 31 then 0, 1
+    const uint32_t selB = lh ? 0x07060100u : 0x03020504u;   // which bytes take the low nibble
+    const uint32_t shB = lh ? 0u : 4u;                       // half 0: low nibbles, half 1: high
+
+    v16i bias;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[r] = 0x4B400000;
+    float acc[2][2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // 16*(nib-8) as int8 from a nibble in the high half of each byte
+    auto nib = [](uint32_t v) { return (v & 0xF0F0F0F0u) ^ 0x80808080u; };
+    auto half_lo = [](uint32_t v) { return __builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); };
+    auto half_hi = [](uint32_t v) { return __builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); };
+    auto mfma = [&](const v4i &a, const v4i &b) { return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, bias, 0, 0, 0); };
+    // dx of the lane's 16 output rows of A tile i, block kb: rows 8a + 4lh + c
+    // of the tile are dwords c of four 16-byte reads of scale plane kb (dx in
+    // the low half for block 0, the high half for block 1)
+    auto load_dx = [&](const uint32_t *sb, int kb, int i, uint32_t (&d)[16]) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(sb + xs + kb * BM + 32 * i);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const uint4 q = p[2 * a];
+            d[4 * a] = q.x;
+            d[4 * a + 1] = q.y;
+            d[4 * a + 2] = q.z;
+            d[4 * a + 3] = q.w;
+        }
+    };
+    auto fold = [&](const v16i &d, int i, int j, const uint32_t (&dx)[16], int kb, _Float16 dw, float nbias) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int e = d[r];   // element first: see the bit_cast note above
+            const float u = fmaf(__int_as_float(e), (float)dw, nbias);
+            const _Float16 x = kb ? half_hi(dx[r]) : half_lo(dx[r]);
+            acc[i][j][r] = fmaf(u, (float)x, acc[i][j][r]);
+        }
+    };
+
+    // Operands of one block: two A tiles, two B tiles, the B rows' scales.
+    struct Ops {
+        v4i a[2], b[2];
+        _Float16 dw[2];
+        float nb[2];
+    };
+    // raw dwords of one block for this lane: A row dwords 1..4 or 5..8 and
+    // dword 0 (block 0) or 9..12 or 13..16 (block 1); B row dwords 0..4
+    // (block 0) or 4..8 (block 1)
+    struct Raw {
+        uint32_t a[2][5], w[2][5];
+    };
+    auto load_raw = [&](const uint32_t *sb, int kb, Raw &r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t *pa = sb + xa + 32 * XD * i + (kb ? 8 : 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r.a[i][k] = pa[1 + k];
+            r.a[i][4] = kb ? 0u : sb[xz + 32 * XD * i];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t *pw = sb + wb + 32 * WD * j + (kb ? 4 : 0);
+#pragma unroll
+            for (int e = 0; e < 5; ++e) r.w[j][e] = pw[e];
+        }
+    };
+    auto build = [&](const Raw &r, int kb, Ops &o) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t q3 = kb ? r.a[i][3] : __builtin_amdgcn_perm(r.a[i][3], r.a[i][4], selA);
+            o.a[i] = v4i{(int)r.a[i][0], (int)r.a[i][1], (int)r.a[i][2], (int)q3};
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t *E = r.w[j];
+            if (kb == 0) {
+                // nibble bytes 2..15 are dwords 1..3 and the first half of
+                // dword 4; bytes 0, 1 are the second half of dword 0
+                const uint32_t P = __builtin_amdgcn_perm(E[4], E[0], 0x03020504u);   // bytes 14, 15, 0, 1
+                const uint32_t Pm = __builtin_amdgcn_perm(P << 4, P, selB);
+                o.b[j] = v4i{(int)nib(E[1] << shB), (int)nib(E[2] << shB), (int)nib(E[3] << shB), (int)nib(Pm)};
+                o.dw[j] = half_lo(E[0]);
+            } else {
+                o.b[j] = v4i{(int)nib(E[1] << shB), (int)nib(E[2] << shB), (int)nib(E[3] << shB),
+                             (int)nib(E[4] << shB)};
+                o.dw[j] = half_hi(E[0]);
+            }
+            o.nb[j] = (float)o.dw[j] * -kBias;   // exact: 11 + 2 significant bits
+        }
+    };
+    // Explicit order, fenced against the scheduler: the MFMA of tile t+1 is
+    // issued before the fold of tile t (so a fold never waits for its MFMA
+    // and two MFMAs never queue back to back), and the dx reads of the next
+    // A tile go out one fold ahead.
+    // The DMA of stage sd into buffer bd is spread over the step, two loads
+    // after each of the first seven folds, so that the 56 loads of a
+    // workgroup do not queue up at the texture unit at once.
+    auto compute = [&](const uint32_t *sb, int sd, int bd) __attribute__((always_inline)) {
+        Raw r0, r1;
+        Ops o0, o1;
+        uint32_t dxa[16], dxb[16];
+        auto dma_after = [&](auto pc) {
+            dma_pair(pc, sd, bd);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        load_raw(sb, 0, r0);
+        load_dx(sb, 0, 0, dxa);
+        build(r0, 0, o0);
+        v16i d0 = mfma(o0.a[0], o0.b[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_raw(sb, 1, r1);
+        load_dx(sb, 0, 1, dxb);
+        v16i d1 = mfma(o0.a[0], o0.b[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(d0, 0, 0, dxa, 0, o0.dw[0], o0.nb[0]);
+        dma_after(std::integral_constant<int, 0>());
+        d0 = mfma(o0.a[1], o0.b[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(d1, 0, 1, dxa, 0, o0.dw[1], o0.nb[1]);
+        dma_after(std::integral_constant<int, 1>());
+        d1 = mfma(o0.a[1], o0.b[1]);
+        load_dx(sb, 1, 0, dxa);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(d0, 1, 0, dxb, 0, o0.dw[0], o0.nb[0]);
+        dma_after(std::integral_constant<int, 2>());
+        build(r1, 1, o1);
+        d0 = mfma(o1.a[0], o1.b[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(d1, 1, 1, dxb, 0, o0.dw[1], o0.nb[1]);
+        dma_after(std::integral_constant<int, 3>());
+        d1 = mfma(o1.a[0], o1.b[1]);
+        load_dx(sb, 1, 1, dxb);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(d0, 0, 0, dxa, 1, o1.dw[0], o1.nb[0]);
+        dma_after(std::integral_constant<int, 4>());
+        d0 = mfma(o1.a[1], o1.b[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(d1, 0, 1, dxa, 1, o1.dw[1], o1.nb[1]);
+        dma_after(std::integral_constant<int, 5>());
+        d1 = mfma(o1.a[1], o1.b[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(d0, 1, 0, dxb, 1, o1.dw[0], o1.nb[0]);
+        dma_after(std::integral_constant<int, 6>());
+        fold(d1, 1, 1, dxb, 1, o1.dw[1], o1.nb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Stage s lives in buffer s % 3.  At step s this wave's loads of stage s
+    // have landed once at most the 14 of stage s+1 are outstanding; the
+    // barrier publishes every wave's and frees buffer (s-1) % 3, which the
+    // DMA of stage s+2 then fills.  The last two steps have no stage s+2 and
+    // copy the last stage again into that idle buffer instead, so that every
+    // step issues the same 14 loads and waits for the same count.
+    static_assert(PER_WAVE == 14, "the wait below counts 14 loads per stage");
+    auto step = [&](int s, auto bc) {
+        constexpr int b = decltype(bc)::value;
+        asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+        lds_barrier();
+        compute(lds + b * STAGE, min(s + 2, nst - 1), (b + 2) % NBUF);
+    };
+    dma(0, 0);
+    dma(min(1, nst - 1), 1);
+    for (int s = 0; s < nst; s += NBUF) {
+        step(s, std::integral_constant<int, 0>());
+        if (s + 1 < nst) step(s + 1, std::integral_constant<int, 1>());
+        if (s + 2 < nst) step(s + 2, std::integral_constant<int, 2>());
+    }
+    // no LDS-DMA write may still be in flight when the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // store: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + 64 * wn + 32 * j + lr;
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (m < M) y[(int64_t)m * N + n] = acc[i][j][r] * 0.0625f;
+            }
+        }
+}
+
+hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    const uint8_t *wp = static_cast<const uint8_t *>(w);
+    const uint8_t *xp = static_cast<const uint8_t *>(xq);
+    // the plane kernel needs 4-byte aligned rows and 32-bit tile offsets
+    if ((nb & 1) || (int64_t)mmr::BM * nb * kQ80Bytes >= (int64_t(1) << 31))
+        return launch_matmul_q4_0_any(wp, xp, y, M, N, nb, st);
+    int tiles_m = (M + mmr::BM - 1) / mmr::BM;
+    const int64_t tiles = (int64_t)tiles_m * ((N + mmr::BN - 1) / mmr::BN);
+    void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
+    return hipLaunchKernel((const void *)k_matmul_q4_0, dim3((unsigned)tiles), dim3(mmr::NT), args, 0, st);
 }
 
 }  // namespace qmm

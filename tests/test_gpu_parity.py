@@ -174,6 +174,9 @@ MATMUL_CASES = [
     ("q4_0", 1, 8, 32), ("q4_0", 37, 200, 1024), ("q4_0", 128, 128, 4096), ("q4_0", 130, 129, 160),
     ("q4_0", 64, 512, 1024), ("q4_0", 5, 3, 96), ("q4_0", 256, 384, 4128), ("q4_0", 300, 700, 2080),
     ("q4_0", 129, 257, 64),
+    # even block counts (the dword-plane kernel): 1..7 stages, ragged tiles
+    ("q4_0", 1, 129, 64), ("q4_0", 131, 255, 128), ("q4_0", 70, 130, 192), ("q4_0", 257, 129, 256),
+    ("q4_0", 3, 300, 320), ("q4_0", 200, 100, 448),
     ("q2_k", 1, 8, 256), ("q2_k", 9, 70, 1024), ("q2_k", 33, 130, 4096),
 ]
 

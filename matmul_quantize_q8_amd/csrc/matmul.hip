@@ -301,11 +301,9 @@ static hipError_t launch_matmul_q4_0_any(const uint8_t *wp, const uint8_t *xp, f
 // buffer LDS-DMA loads of one dword per lane, 64 consecutive dwords per
 // instruction: the activation rows row-major at a 17-dword stride, the weight
 // rows at a 9-dword stride (odd strides, so a wave reading one dword of 32
-// different rows touches 32 different banks), then two scale planes: the
-// dword holding dx of block 0 (dword 0) and of block 1 (dword 8) for each of
-// the 128 activation rows, so that four consecutive rows' scales are one
-// 16-byte read.  Each lane's global offset for each of its 14 loads is fixed
-// for the whole K loop; the stage position rides in the scalar offset.
+// different rows touches 32 different banks).  Each lane's global offset for
+// each of its 13 loads is fixed for the whole K loop; the stage position
+// rides in the scalar offset.
 //
 // Nothing is re-laid out: each wave reads its MFMA operands from those rows.
 // The stage's second block is 4-byte aligned (codes in dwords 9..16); the
@@ -315,10 +313,14 @@ static hipError_t launch_matmul_q4_0_any(const uint8_t *wp, const uint8_t *xp, f
 // and one v_perm of dwords 8 and 0).  The weight codes are unpacked in the
 // same order; the MFMA sums over the 32 byte positions, so any order that
 // both operands share gives the same I_b.
-// Weight nibbles are unpacked per wave as in the kernel above (16*(nib-8)),
-// and the fold is the same, except that dw enters as f16 (v_fma_mix) without
-// the 1/16: every accumulator is 16x too large and the store scales it back
-// (a power of two, exact).
+// Weight nibbles are unpacked per wave as in the kernel above (16*(nib-8)).
+// The fold is the same two FMAs, in plain f32: on gfx950 v_fma_f32 issues at
+// twice the rate of v_fma_mix_f32 and v_cvt_f32_f16, so each scale is
+// converted once per stage instead of inside the fold.  Each wave converts
+// the dx of its 64 activation rows into a private f32 array in LDS (four
+// consecutive rows are then one 16-byte read); dw enters without the 1/16,
+// so every accumulator is 16x too large and the store scales it back (a
+// power of two, exact).
 namespace mmr {
 constexpr int BM = 128;                  // tokens per workgroup tile
 constexpr int BN = 128;                  // weight rows per workgroup tile
@@ -326,13 +328,13 @@ constexpr int NT = 256;                  // 4 waves, 2 x 2 of 64 x 64
 constexpr int XD = 17;                   // activation dwords per row per stage
 constexpr int WD = 9;                    // weight dwords per row per stage
 constexpr int WOFF = BM * XD;            // weight rows start (dwords into a stage buffer)
-constexpr int SOFF = WOFF + BN * WD;     // scale planes start
-constexpr int STAGE = SOFF + 2 * BM;     // 3584 dwords = 14,336 bytes
+constexpr int STAGE = WOFF + BN * WD;    // 3328 dwords = 13,312 bytes
 constexpr int XQ = BM * XD / kWave;      // 34 wave loads of activation rows
 constexpr int WQ = BN * WD / kWave;      // 18 of weight rows
-constexpr int NQ = STAGE / kWave;        // 56 in all (the last 4 are the scale planes)
-constexpr int PER_WAVE = NQ / 4;         // 14
+constexpr int NQ = STAGE / kWave;        // 52 in all
+constexpr int PER_WAVE = NQ / 4;         // 13
 constexpr int NBUF = 3;                  // stage buffers: DMA runs two stages ahead
+constexpr int DXF = NBUF * STAGE;        // per-wave f32 dx arrays: [wave][block][64 rows]
 constexpr float kBias = 12582912.0f;     // 1.5 * 2^23, bit pattern 0x4B400000
 }  // namespace mmr
 static_assert(mmr::BM * mmr::XD % kWave == 0 && mmr::BN * mmr::WD % kWave == 0 && mmr::NQ % 4 == 0,
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(mmr::NT, 2) void k_matmul_q4_0(const uint8_t *__res
                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                             int M, int N, int nb, int tiles_m) {
     using namespace mmr;
-    __shared__ __attribute__((aligned(16))) uint32_t lds[NBUF * STAGE];
+    __shared__ __attribute__((aligned(16))) uint32_t lds[NBUF * STAGE + 4 * 2 * 64];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = uniform(t >> 6);
     const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(mmr::NT, 2) void k_matmul_q4_0(const uint8_t *__res
     const uint32_t xrow = (uint32_t)nb * kQ80Bytes, wrow = (uint32_t)nb * kQ40Bytes;
     const int nst = nb >> 1;
 
-    // DMA: wave w issues wave loads q = w, w+4, ..., w+52 of each stage.  Rows
+    // DMA: wave w issues wave loads q = w, w+4, ..., w+48 of each stage.  Rows
     // past the matrix re-read its last row; their results are not stored.
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(xq + (int64_t)m0 * xrow), 0, (int)((uint32_t)min(M - m0, BM) * xrow), 0x00020000);
@@ -385,17 +387,14 @@ __global__ __launch_bounds__(mmr::NT, 2) void k_matmul_q4_0(const uint8_t *__res
         if (q < XQ) {
             const int f = kWave * q + lane, row = f / XD;
             voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + 4u * (uint32_t)(f - XD * row);
-        } else if (q < XQ + WQ) {
+        } else {
             const int f = kWave * (q - XQ) + lane, row = f / WD;
             voff[k] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + 4u * (uint32_t)(f - WD * row);
-        } else {
-            const int p = q - XQ - WQ, row = kWave * (p & 1) + lane;   // plane p >> 1, rows 64(p & 1)...
-            voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (p >> 1 ? 32u : 0u);
         }
     }
     // Wave load q = w + 4k lands at dwords 64q.. of the stage buffer: loads
     // k = 0..7 are activation rows, k = 8 too for waves 0 and 1 (weight rows
-    // for waves 2 and 3), k = 9..12 weight rows, k = 13 a scale plane.
+    // for waves 2 and 3), k = 9..12 weight rows.
     // the low half of a generic LDS address is the LDS offset
     const uint32_t lds_w = (uint32_t)uniform((int)((uint32_t)reinterpret_cast<uintptr_t>(lds) + 256u * wave));
     auto dma_load = [&](auto kc, uint32_t base, int sx, int sw) {
@@ -403,13 +402,13 @@ __global__ __launch_bounds__(mmr::NT, 2) void k_matmul_q4_0(const uint8_t *__res
         const bool isw = k == 8 ? wave >= 2 : (k >= 9 && k <= 12);
         buffer_to_lds4<k * 1024>(isw ? wr : xr, base, voff[k], isw ? sw : sx);
     };
-    // loads 2p and 2p+1 of stage s into buffer b
+    // loads 2p and 2p+1 (p < 6), or load 12 (p = 6), of stage s into buffer b
     auto dma_pair = [&](auto pc, int s, int b) {
         constexpr int p = decltype(pc)::value;
         const uint32_t base = lds_w + (uint32_t)(b * STAGE * 4);
         const int sx = s * (2 * kQ80Bytes), sw = s * (2 * kQ40Bytes);
         dma_load(std::integral_constant<int, 2 * p>(), base, sx, sw);
-        dma_load(std::integral_constant<int, 2 * p + 1>(), base, sx, sw);
+        if constexpr (2 * p + 1 < PER_WAVE) dma_load(std::integral_constant<int, 2 * p + 1>(), base, sx, sw);
     };
     auto dma = [&](int s, int b) {
         dma_pair(std::integral_constant<int, 0>(), s, b);
@@ -420,14 +419,15 @@ __global__ __launch_bounds__(mmr::NT, 2) void k_matmul_q4_0(const uint8_t *__res
         dma_pair(std::integral_constant<int, 5>(), s, b);
         dma_pair(std::integral_constant<int, 6>(), s, b);
     };
-    static_assert(XQ == 34 && WQ == 18 && PER_WAVE == 14, "the load list above is written for this split");
+    static_assert(XQ == 34 && WQ == 18 && PER_WAVE == 13, "the load list above is written for this split");
 
     const int wm = wave & 1, wn = wave >> 1;
     const int lr = lane & 31, lh = lane >> 5;
     const int xz = (64 * wm + lr) * XD;          // dword 0 of A row 64wm+lr (tile i: +32 rows)
     const int xa = xz + 4 * lh;                  // the lane half's first code dword, less one
     const int wb = WOFF + (64 * wn + lr) * WD;   // B row 64wn+lr (tile j: +32 rows)
-    const int xs = SOFF + 64 * wm + 4 * lh;      // scale plane: first of 4 rows a lane needs
+    const int dxw = DXF + 128 * wave;            // this wave's f32 dx: [block][64 rows 64wm..]
+    const int xd = (64 * wm + lane) * XD;        // dword 0 of the row whose dx this lane converts
     // byte selectors (v_perm: 0-3 pick the second source, 4-7 the first)
     const uint32_t selA = lh ? 0x03020504u : 0x07060504u;   // half 1: codes 30, 31 then 0, 1
     const uint32_t selB = lh ? 0x07060100u : 0x03020504u;   // which bytes take the low nibble
@@ -449,35 +449,40 @@ __global__ __launch_bounds__(mmr::NT, 2) void k_matmul_q4_0(const uint8_t *__res
     auto half_lo = [](uint32_t v) { return __builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); };
     auto half_hi = [](uint32_t v) { return __builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); };
     auto mfma = [&](const v4i &a, const v4i &b) { return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, bias, 0, 0, 0); };
+    // The wave's dx for one stage as f32: lane l converts row 64wm+l's scales
+    // (block 0: low half of dword 0, block 1: high half of dword 8).  Only this
+    // wave reads them back, and a wave's LDS accesses complete in order.
+    auto convert_dx = [&](const uint32_t *sb) {
+        float *d = reinterpret_cast<float *>(lds + dxw);
+        d[lane] = (float)half_lo(sb[xd]);
+        d[64 + lane] = (float)half_hi(sb[xd + 8]);
+    };
     // dx of the lane's 16 output rows of A tile i, block kb: rows 8a + 4lh + c
-    // of the tile are dwords c of four 16-byte reads of scale plane kb (dx in
-    // the low half for block 0, the high half for block 1)
-    auto load_dx = [&](const uint32_t *sb, int kb, int i, uint32_t (&d)[16]) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(sb + xs + kb * BM + 32 * i);
+    // of the tile, four 16-byte reads
+    auto load_dx = [&](int kb, int i, float (&d)[16]) {
+        const float4 *p = reinterpret_cast<const float4 *>(lds + dxw + 64 * kb + 32 * i + 4 * lh);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const uint4 q = p[2 * a];
+            const float4 q = p[2 * a];
             d[4 * a] = q.x;
             d[4 * a + 1] = q.y;
             d[4 * a + 2] = q.z;
             d[4 * a + 3] = q.w;
         }
     };
-    auto fold = [&](const v16i &d, int i, int j, const uint32_t (&dx)[16], int kb, _Float16 dw, float nbias) {
+    auto fold = [&](const v16i &d, int i, int j, const float (&dx)[16], float dw, float nbias) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int e = d[r];   // element first: see the bit_cast note above
-            const float u = fmaf(__int_as_float(e), (float)dw, nbias);
-            const _Float16 x = kb ? half_hi(dx[r]) : half_lo(dx[r]);
-            acc[i][j][r] = fmaf(u, (float)x, acc[i][j][r]);
+            const float u = fmaf(__int_as_float(e), dw, nbias);
+            acc[i][j][r] = fmaf(u, dx[r], acc[i][j][r]);
         }
     };
 
     // Operands of one block: two A tiles, two B tiles, the B rows' scales.
     struct Ops {
         v4i a[2], b[2];
-        _Float16 dw[2];
-        float nb[2];
+        float dw[2], nb[2];
     };
     // raw dwords of one block for this lane: A row dwords 1..4 or 5..8 and
     // dword 0 (block 0) or 9..12 or 13..16 (block 1); B row dwords 0..4
@@ -515,13 +520,16 @@ __global__ __launch_bounds__(mmr::NT, 2) void k_matmul_q4_0(const uint8_t *__res
                 const uint32_t P = __builtin_amdgcn_perm(E[4], E[0], 0x03020504u);   // bytes 14, 15, 0, 1
                 const uint32_t Pm = __builtin_amdgcn_perm(P << 4, P, selB);
                 o.b[j] = v4i{(int)nib(E[1] << shB), (int)nib(E[2] << shB), (int)nib(E[3] << shB), (int)nib(Pm)};
-                o.dw[j] = half_lo(E[0]);
+                o.dw[j] = (float)half_lo(E[0]);
             } else {
                 o.b[j] = v4i{(int)nib(E[1] << shB), (int)nib(E[2] << shB), (int)nib(E[3] << shB),
                              (int)nib(E[4] << shB)};
-                o.dw[j] = half_hi(E[0]);
+                o.dw[j] = (float)half_hi(E[0]);
             }
-            o.nb[j] = (float)o.dw[j] * -kBias;   // exact: 11 + 2 significant bits
+            // keep dw an f32 register: folded back into the fold, the f16
+            // conversion would turn each v_fma_f32 into a half-rate v_fma_mix
+            asm volatile("" : "+v"(o.dw[j]));
+            o.nb[j] = o.dw[j] * -kBias;   // exact: 11 + 2 significant bits
         }
     };
     // Explicit order, fenced against the scheduler: the MFMA of tile t+1 is
@@ -529,68 +537,69 @@ __global__ __launch_bounds__(mmr::NT, 2) void k_matmul_q4_0(const uint8_t *__res
     // and two MFMAs never queue back to back), and the dx reads of the next
     // A tile go out one fold ahead.
     // The DMA of stage sd into buffer bd is spread over the step, two loads
-    // after each of the first seven folds, so that the 56 loads of a
-    // workgroup do not queue up at the texture unit at once.
+    // after each of the first seven folds (one after the seventh), so that
+    // the 52 loads of a workgroup do not queue up at the texture unit at once.
     auto compute = [&](const uint32_t *sb, int sd, int bd) __attribute__((always_inline)) {
         Raw r0, r1;
         Ops o0, o1;
-        uint32_t dxa[16], dxb[16];
+        float dxa[16], dxb[16];
         auto dma_after = [&](auto pc) {
             dma_pair(pc, sd, bd);
             __builtin_amdgcn_sched_barrier(0);
         };
+        convert_dx(sb);
         load_raw(sb, 0, r0);
-        load_dx(sb, 0, 0, dxa);
+        load_dx(0, 0, dxa);
         build(r0, 0, o0);
         v16i d0 = mfma(o0.a[0], o0.b[0]);
         __builtin_amdgcn_sched_barrier(0);
         load_raw(sb, 1, r1);
-        load_dx(sb, 0, 1, dxb);
+        load_dx(0, 1, dxb);
         v16i d1 = mfma(o0.a[0], o0.b[1]);
         __builtin_amdgcn_sched_barrier(0);
-        fold(d0, 0, 0, dxa, 0, o0.dw[0], o0.nb[0]);
+        fold(d0, 0, 0, dxa, o0.dw[0], o0.nb[0]);
         dma_after(std::integral_constant<int, 0>());
         d0 = mfma(o0.a[1], o0.b[0]);
         __builtin_amdgcn_sched_barrier(0);
-        fold(d1, 0, 1, dxa, 0, o0.dw[1], o0.nb[1]);
+        fold(d1, 0, 1, dxa, o0.dw[1], o0.nb[1]);
         dma_after(std::integral_constant<int, 1>());
         d1 = mfma(o0.a[1], o0.b[1]);
-        load_dx(sb, 1, 0, dxa);
+        load_dx(1, 0, dxa);
         __builtin_amdgcn_sched_barrier(0);
-        fold(d0, 1, 0, dxb, 0, o0.dw[0], o0.nb[0]);
+        fold(d0, 1, 0, dxb, o0.dw[0], o0.nb[0]);
         dma_after(std::integral_constant<int, 2>());
         build(r1, 1, o1);
         d0 = mfma(o1.a[0], o1.b[0]);
         __builtin_amdgcn_sched_barrier(0);
-        fold(d1, 1, 1, dxb, 0, o0.dw[1], o0.nb[1]);
+        fold(d1, 1, 1, dxb, o0.dw[1], o0.nb[1]);
         dma_after(std::integral_constant<int, 3>());
         d1 = mfma(o1.a[0], o1.b[1]);
-        load_dx(sb, 1, 1, dxb);
+        load_dx(1, 1, dxb);
         __builtin_amdgcn_sched_barrier(0);
-        fold(d0, 0, 0, dxa, 1, o1.dw[0], o1.nb[0]);
+        fold(d0, 0, 0, dxa, o1.dw[0], o1.nb[0]);
         dma_after(std::integral_constant<int, 4>());
         d0 = mfma(o1.a[1], o1.b[0]);
         __builtin_amdgcn_sched_barrier(0);
-        fold(d1, 0, 1, dxa, 1, o1.dw[1], o1.nb[1]);
+        fold(d1, 0, 1, dxa, o1.dw[1], o1.nb[1]);
         dma_after(std::integral_constant<int, 5>());
         d1 = mfma(o1.a[1], o1.b[1]);
         __builtin_amdgcn_sched_barrier(0);
-        fold(d0, 1, 0, dxb, 1, o1.dw[0], o1.nb[0]);
+        fold(d0, 1, 0, dxb, o1.dw[0], o1.nb[0]);
         dma_after(std::integral_constant<int, 6>());
-        fold(d1, 1, 1, dxb, 1, o1.dw[1], o1.nb[1]);
+        fold(d1, 1, 1, dxb, o1.dw[1], o1.nb[1]);
         __builtin_amdgcn_sched_barrier(0);
     };
 
     // Stage s lives in buffer s % 3.  At step s this wave's loads of stage s
-    // have landed once at most the 14 of stage s+1 are outstanding; the
+    // have landed once at most the 13 of stage s+1 are outstanding; the
     // barrier publishes every wave's and frees buffer (s-1) % 3, which the
     // DMA of stage s+2 then fills.  The last two steps have no stage s+2 and
     // copy the last stage again into that idle buffer instead, so that every
-    // step issues the same 14 loads and waits for the same count.
-    static_assert(PER_WAVE == 14, "the wait below counts 14 loads per stage");
+    // step issues the same 13 loads and waits for the same count.
+    static_assert(PER_WAVE == 13, "the wait below counts 13 loads per stage");
     auto step = [&](int s, auto bc) {
         constexpr int b = decltype(bc)::value;
-        asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
         lds_barrier();
         compute(lds + b * STAGE, min(s + 2, nst - 1), (b + 2) % NBUF);
     };

@@ -215,16 +215,22 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
             d[4 * a + 3] = q.w;
         }
     };
+    // The 16 u values first, then the 16 accumulator updates, with a fence
+    // between: left to itself the scheduler pairs each u with its update
+    // through one temporary, and every pair then waits out the FMA latency.
     auto fold = [&](const v16i &d, int i, int j, const float (&dx)[16], float dw, float nbias) {
+        float u[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             // element first, then reinterpret: __builtin_bit_cast applied
             // directly to a vector element reads element 0 with this
             // toolchain (hipcc 7.2), so it must not be used here
             const int e = d[r];
-            const float u = fmaf(__int_as_float(e), dw, nbias);
-            acc[i][j][r] = fmaf(u, dx[r], acc[i][j][r]);
+            u[r] = fmaf(__int_as_float(e), dw, nbias);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(u[r], dx[r], acc[i][j][r]);
     };
 
     // Chunks of one stage for this lane: per A tile the block-0 and block-1

@@ -20,6 +20,7 @@ Synthetic data: seeded Gaussian weights (std 0.02) and activations (std 1,
 1% outliers x20 for decode), quantized on the GPU by the library.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -54,6 +55,34 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one plain 256 MiB device-to-device copy (scales HBM byte counters)")
     return ap.parse_args()
+
+
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the plain-copy calibration) from the committed rocprofv3
+    counter summary, or None when there is none or the kernel's sources no
+    longer hash to what was profiled."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    keys = ("traffic_bytes_per_launch", "kernel_sources", "kernel_source_sha256")
+    fields = {}
+    for line in text.splitlines():
+        k, _, v = line.partition(": ")
+        if k in keys:
+            fields[k] = v.strip()
+    if len(fields) != len(keys):
+        return None
+    h = hashlib.sha256()
+    try:
+        for f in fields["kernel_sources"].split():
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+    except OSError:
+        return None
+    return int(fields["traffic_bytes_per_launch"]) if h.hexdigest() == fields["kernel_source_sha256"] else None
 
 
 def time_batches(torch, launch, count, batch):
@@ -140,7 +169,8 @@ def bench_decode(args, torch, q, synth):
                 copies=copies,
                 roofline={"kernel": "qmm::k_matvec<Q4_0>", "bound": "hbm",
                           "achieved": round(gbs_kernel, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(gbs_kernel / HBM_PEAK_GBS, 4), "traffic": None,
+                          "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
+                          "traffic": committed_traffic("k_matvec_q4_0", "12288x4096"),
                           "kernel_us_mean": round(mv_ms * 1e3, 3), "kernel_us_best_batch": round(mv_min * 1e3, 3),
                           "algorithmic_bytes": wbytes + q.row_bytes("q8_0", K) + 4 * N})
 
@@ -181,7 +211,8 @@ def bench_prefill(args, torch, q, synth):
     return dict(ms_step=ms_step, tops=ops / (ms_step * 1e-3) / 1e12,
                 roofline={"kernel": "qmm::k_matmul_q4_0", "bound": "mfma", "achieved": round(tops_kernel, 2),
                           "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
-                          "traffic": None, "kernel_us_mean": round(mm_ms * 1e3, 2),
+                          "traffic": committed_traffic("k_matmul_q4_0", "2048x12288x4096"),
+                          "kernel_us_mean": round(mm_ms * 1e3, 2),
                           "kernel_us_best_batch": round(mm_min * 1e3, 2), "algorithmic_ops": ops})
 
 

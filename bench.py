@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=400, help="timed decode steps")
     ap.add_argument("--warmup", type=int, default=40, help="untimed decode steps")
     ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--prefill-warmup", type=int, default=3)
+    ap.add_argument("--prefill-warmup", type=int, default=30,
+                    help="untimed prefill steps (~10 ms: lets the clock settle under the MFMA load)")
     ap.add_argument("--only", choices=["all", "decode", "prefill"], default="all")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of each oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")

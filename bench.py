@@ -3,12 +3,14 @@
 
 Headline (one JSON line on stdout): Q4_0 x Q8_0 decode at the FFN-gate shape,
 M = 1, N = 12288, K = 4096.  One step = quantize the f32 activation to Q8_0
-on the GPU + the matvec over one copy of the 28.3 MB weight matrix.  Steps
-rotate over enough byte-identical weight copies (>= 512 MB) that every step
-streams its weights from HBM, not from the 256 MB last-level cache.
-`value` is weight bytes per step / step time (GB/s), inputs resident in HBM;
-the timed steps are replayed from a captured HIP graph (launching two small
-kernels per step from Python would measure the interpreter, not the GPU).
+and the matvec over one copy of the 28.3 MB weight matrix, in one launch
+(qmm_quantize_matvec_q4_0; the same step as two launches is reported beside
+it).  Steps rotate over enough byte-identical weight copies (>= 512 MB) that
+every step streams its weights from HBM, not from the 256 MB last-level
+cache.  `value` is weight bytes per step / step time (GB/s), inputs resident
+in HBM; the timed steps are replayed from a captured HIP graph (launching
+kernels of a few microseconds from Python would measure the interpreter, not
+the GPU).
 
 Also in the line: the prefill matmul (M = 2048, same weights), int8 TOP/s;
 for each, the dominant kernel's roofline (achieved / MI355X peak, with the
@@ -127,53 +129,68 @@ def bench_decode(args, torch, q, synth):
     torch.cuda.synchronize()
 
     def step(i):
+        """One decode step: quantize x and apply the weights, in one launch."""
+        q.qmm_quantize_matvec_q4_0(wqs[i % copies], x, None, y, N, K)
+
+    def step_two_launches(i):
+        """The same step as a quantize launch followed by a matvec launch."""
         q.qmm_quantize_q8_0(x, xq, 1, K)
         q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K)
 
-    # A decode loop is launch-bound when driven eagerly from Python (two
-    # launches per step), so the steps are captured once into a HIP graph
-    # (one step per weight copy) and the graph is replayed.
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(copies):
-            step(i)
-    reps = max(1, args.steps // copies)
-    graph.replay()
-    torch.cuda.synchronize()
+    def replayed(fn):
+        """ms per step of `fn` replayed from a captured HIP graph (one step per
+        weight copy); a decode loop driven eagerly from Python is launch-bound."""
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(copies):
+                fn(i)
+        reps = max(1, args.steps // copies)
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / (reps * copies), reps * copies
+
+    ms_step, nsteps = replayed(step)
+    ms_two, _ = replayed(step_two_launches)
+    # the step launched eagerly from Python, for reference
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    nsteps = reps * copies
-    ms_step = t0.elapsed_time(t1) / nsteps
-    # the same steps launched eagerly from Python, for reference
     t0.record()
     for i in range(args.steps):
         step(i)
     t1.record()
     torch.cuda.synchronize()
     ms_step_eager = t0.elapsed_time(t1) / args.steps
-    # the dominant kernel alone: batches of `copies` back-to-back launches
-    mv_ms, mv_min, n = time_batches(torch, lambda i: q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K),
+    # the dominant kernel alone (the fused kernel; the plain matvec beside it):
+    # batches of `copies` back-to-back launches
+    fz_ms, fz_min, n = time_batches(torch, step, args.steps, copies)
+    mv_ms, mv_min, _ = time_batches(torch, lambda i: q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K),
                                     args.steps, copies)
-    log(f"decode: {ms_step * 1e3:.2f} us/step in graph replay ({ms_step_eager * 1e3:.2f} eager), matvec "
-        f"{mv_ms * 1e3:.2f} us (best batch {mv_min * 1e3:.2f}) over {copies} weight copies, {n} launches")
+    log(f"decode: {ms_step * 1e3:.2f} us/step in graph replay ({ms_step_eager * 1e3:.2f} eager; two launches "
+        f"{ms_two * 1e3:.2f}), fused kernel {fz_ms * 1e3:.2f} us (best batch {fz_min * 1e3:.2f}), matvec alone "
+        f"{mv_ms * 1e3:.2f} us over {copies} weight copies, {n} launches")
     gbs_step = wbytes / (ms_step * 1e-3) / 1e9
-    gbs_kernel = wbytes / (mv_ms * 1e-3) / 1e9
-    return dict(ms_step=ms_step, ms_step_eager=ms_step_eager, nsteps=nsteps, gbs=gbs_step, wbytes=wbytes,
-                copies=copies,
-                roofline={"kernel": "qmm::k_matvec<Q4_0>", "bound": "hbm",
+    gbs_kernel = wbytes / (fz_ms * 1e-3) / 1e9
+    return dict(ms_step=ms_step, ms_step_eager=ms_step_eager, ms_two=ms_two, nsteps=nsteps, gbs=gbs_step,
+                wbytes=wbytes, copies=copies,
+                roofline={"kernel": "qmm::k_matvec<Q4_0, fused quantize>", "bound": "hbm",
                           "achieved": round(gbs_kernel, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
-                          "traffic": committed_traffic("k_matvec_q4_0", "12288x4096"),
-                          "kernel_us_mean": round(mv_ms * 1e3, 3), "kernel_us_best_batch": round(mv_min * 1e3, 3),
-                          "algorithmic_bytes": wbytes + q.row_bytes("q8_0", K) + 4 * N})
+                          "traffic": committed_traffic("k_matvec_q4_0_fused", "12288x4096"),
+                          "kernel_us_mean": round(fz_ms * 1e3, 3), "kernel_us_best_batch": round(fz_min * 1e3, 3),
+                          "algorithmic_bytes": wbytes + 4 * K + 4 * N,
+                          "matvec_only": {"kernel": "qmm::k_matvec<Q4_0>", "us_mean": round(mv_ms * 1e3, 3),
+                                          "achieved": round(wbytes / (mv_ms * 1e-3) / 1e9, 1),
+                                          "traffic": committed_traffic("k_matvec_q4_0", "12288x4096")}})
 
 
 def bench_prefill(args, torch, q, synth):
@@ -306,9 +323,11 @@ def main():
                     "ms_per_step": round(dec["ms_step"], 5),
                     "config": {"workload": "q4_0_matvec_12288x4096", "M": 1, "N": DEC["N"], "K": DEC["K"],
                                "weight_bytes": dec["wbytes"], "weight_copies": dec["copies"],
-                               "step": "quantize_q8_0 + matvec_q4_0, replayed from a HIP graph",
+                               "step": "quantize_matvec_q4_0 (quantize + matvec in one launch), replayed "
+                                       "from a HIP graph",
                                "hbm_frac_step": round(dec["gbs"] / HBM_PEAK_GBS, 4),
-                               "ms_per_step_eager_python": round(dec["ms_step_eager"], 5)},
+                               "ms_per_step_eager_python": round(dec["ms_step_eager"], 5),
+                               "ms_per_step_two_launches": round(dec["ms_two"], 5)},
                     "roofline": dec["roofline"], "cpu_baseline": cpu_dec})
     if pre is not None:
         pf = {"workload": "q4_0_matmul_2048x12288x4096", "value": round(pre["tops"], 2), "unit": "TOPS",

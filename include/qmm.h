@@ -120,6 +120,28 @@ qmm_status qmm_matvec_q8_0(const void *w, const void *xq, float *y, int64_t N, i
 qmm_status qmm_matvec_q4_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
 qmm_status qmm_matvec_q2_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream);
 
+/* Decode matvec with the activation quantization fused into the same launch
+ * (minfer section 3.3, "Design choices", on sibling products sharing one
+ * quantized row; krafla "Data flow for one token"): every workgroup quantizes
+ * the row it needs into LDS, so a decode step is one launch.  The result is the same as qmm_quantize_q8_0
+ * of x followed by qmm_matvec_q4_0 / qmm_matvec_q8_0 on its output, bit for
+ * bit.  For long rows (more than 4096 values, or more than 2048 with an odd
+ * block count) and a non-NULL xq, the library runs exactly those two launches
+ * instead, because re-quantizing a long row in every workgroup costs more
+ * than the second launch; with xq NULL it always runs the single launch.
+ *   w  : N rows of K/32 Q4_0 (or Q8_0) weight blocks.
+ *   x  : f32 [K], read only.
+ *   xq : NULL, or a Q8_0 row of K/32 blocks (K/32*34 bytes, 16-byte aligned)
+ *        that receives the quantized activation, bit-identical to
+ *        qmm_quantize_q8_0 -- for a caller that applies several weight
+ *        matrices to the same activation (QKV, gate and up) and runs the
+ *        others with qmm_matvec_* on it.
+ *   y  : f32 [N], written. */
+qmm_status qmm_quantize_matvec_q4_0(const void *w, const float *x, void *xq, float *y, int64_t N, int64_t K,
+                                    void *stream);
+qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, float *y, int64_t N, int64_t K,
+                                    void *stream);
+
 /* Prefill matmul, M tokens.
  *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.
  *   y  : f32 [M][N], written.

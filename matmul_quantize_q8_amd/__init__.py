@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
         for name in ("qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
+        for name in ("qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0"):
+            getattr(L, name).argtypes = [P, P, P, P, I64, I64, P]
+            getattr(L, name).restype = ctypes.c_int
         for name in ("qmm_matmul_q4_0", "qmm_matmul_q2_k"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
@@ -67,6 +70,7 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("qmm_status_string", "qmm_abi_version",
            "qmm_quantize_q8_0", "qmm_quantize_q8_k", "qmm_quantize_q4_0", "qmm_quantize_q2_k",
            "qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k",
+           "qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0",
            "qmm_matmul_q4_0", "qmm_matmul_q2_k")
 
 
@@ -136,6 +140,17 @@ def qmm_matvec_q2_k(w, xq8k, y, N: int, K: int, stream=None) -> None:
     _call("qmm_matvec_q2_k", _addr(w), _addr(xq8k), _addr(y), N, K, _stream(stream))
 
 
+def qmm_quantize_matvec_q4_0(w, x, xq, y, N: int, K: int, stream=None) -> None:
+    """Fused decode step: quantize f32 x [K] to Q8_0 (written to xq unless it
+    is None) and y = W x for Q4_0 weights, in one launch."""
+    _call("qmm_quantize_matvec_q4_0", _addr(w), _addr(x), _addr(xq), _addr(y), N, K, _stream(stream))
+
+
+def qmm_quantize_matvec_q8_0(w, x, xq, y, N: int, K: int, stream=None) -> None:
+    """As qmm_quantize_matvec_q4_0, for Q8_0 weights."""
+    _call("qmm_quantize_matvec_q8_0", _addr(w), _addr(x), _addr(xq), _addr(y), N, K, _stream(stream))
+
+
 def qmm_matmul_q4_0(w, xq, y, M: int, N: int, K: int, stream=None) -> None:
     _call("qmm_matmul_q4_0", _addr(w), _addr(xq), _addr(y), M, N, K, _stream(stream))
 
@@ -148,3 +163,4 @@ QUANTIZE_W = {"q4_0": qmm_quantize_q4_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_
 QUANTIZE_X = {"q4_0": qmm_quantize_q8_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_quantize_q8_k}
 MATVEC = {"q4_0": qmm_matvec_q4_0, "q8_0": qmm_matvec_q8_0, "q2_k": qmm_matvec_q2_k}
 MATMUL = {"q4_0": qmm_matmul_q4_0, "q2_k": qmm_matmul_q2_k}
+QUANTIZE_MATVEC = {"q4_0": qmm_quantize_matvec_q4_0, "q8_0": qmm_quantize_matvec_q8_0}

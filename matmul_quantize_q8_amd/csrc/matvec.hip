@@ -19,12 +19,27 @@
 //     d_w*d_x of two binary16 values is exact in f32, so each block adds one
 //     correctly rounded term;
 //   * the G row sums are reduced across the wave by a transposing butterfly
-//     (log2(G) exchange steps that halve the live values, then plain steps).
+//     (log2(G) exchange steps that halve the live values, then plain steps),
+//     all in VALU lane exchanges: gfx950's permlane32/permlane16 swaps for
+//     lane bits 5 and 4, DPP for bits 3..0.
 // Rows longer than one segment (64*MAXU units) are walked in segments with
 // the partial sums kept in registers (only with G = 1).
+//
+// Fused variant (XF32): the workgroup takes the f32 activation row instead of
+// its Q8_0 blocks and quantizes it itself, so a decode step is one launch
+// (minfer section 3.3, "Design choices": the quantized row is derived data of
+// the product, shared by sibling products; here the quantizer moves into the
+// product's launch): each thread loads
+// 16-byte pieces of the row before the weight copies are issued, waits for
+// those loads alone, quantizes them with the same arithmetic as the Q8_0
+// quantizer kernel, and writes the codes to LDS in a lane-friendly layout
+// (per unit: the blocks' 32 codes, then their scales as f32).  One workgroup
+// per token also stores the Q8_0 row to global memory when asked to.
 #include "qmm_device.h"
 
 namespace qmm {
+
+hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipStream_t st);
 
 enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2 };
 
@@ -99,6 +114,29 @@ __device__ __forceinline__ void load_xu<F_Q2_K, false>(const uint8_t *xl, uint32
 #pragma unroll
     for (int s = 0; s < 4; ++s) x.bs[s] = (int)(int16_t)(bs32[s] >> (16 * odd));
     x.d = *reinterpret_cast<const float *>(b);
+}
+
+// Fused-variant activation layout in LDS: unit u at (32*P + 16)*u bytes holds
+// the P blocks' codes (32 bytes each), then their f16-rounded scales as f32.
+template <int P> struct XLayout { static constexpr int US = 32 * P + 16; };
+
+template <int F, bool PAIRED>
+__device__ __forceinline__ void load_xu_q(const uint8_t *xl, int u, XU<F, PAIRED> &x) {
+    constexpr int P = Unit<F, PAIRED>::BPU;
+    const uint8_t *ub = xl + XLayout<P>::US * u;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        const uint4 a = reinterpret_cast<const uint4 *>(ub + 32 * j)[0];
+        const uint4 b = reinterpret_cast<const uint4 *>(ub + 32 * j)[1];
+        int *q = x.q + 8 * j;
+        q[0] = (int)a.x; q[1] = (int)a.y; q[2] = (int)a.z; q[3] = (int)a.w;
+        q[4] = (int)b.x; q[5] = (int)b.y; q[6] = (int)b.z; q[7] = (int)b.w;
+        x.d[j] = reinterpret_cast<const float *>(ub + 32 * P)[j];
+        int s = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s = dot4(q[k], 0x01010101, s);
+        x.sx8[j] = 8 * s;
+    }
 }
 
 // --- one unit of one row ------------------------------------------------------
@@ -234,24 +272,88 @@ __device__ __forceinline__ int dma_span(const uint8_t *src, int64_t lo, int64_t 
     return issued;
 }
 
+// --- row-sum reduction across the wave -----------------------------------------
+__device__ __forceinline__ uint32_t f_as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u_as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+template <int BIT> struct LaneXchg;       // DPP control pairing lanes across lane bit BIT
+template <> struct LaneXchg<8> { static constexpr int CTRL = kDppRowRor8; };        // l ^ 8
+template <> struct LaneXchg<4> { static constexpr int CTRL = kDppHalfRowMirror; };  // l ^ 7 within 8
+template <> struct LaneXchg<2> { static constexpr int CTRL = kDppQuadXor2; };       // l ^ 2
+template <> struct LaneXchg<1> { static constexpr int CTRL = kDppQuadXor1; };       // l ^ 1
+
+// Halving step at lane bit BIT: a lane with the bit clear keeps `lo` plus its
+// partner's `lo`, a lane with the bit set keeps `hi` plus its partner's `hi`
+// (the partner is a lane with the opposite bit).  For bits 5 and 4 the
+// permlane swap of (lo, hi) hands every lane exactly those two values.
+template <int BIT>
+__device__ __forceinline__ float xsum_half(float lo, float hi, int lane) {
+    if constexpr (BIT == 32 || BIT == 16) {
+        const auto r = (BIT == 32) ? __builtin_amdgcn_permlane32_swap(f_as_u(lo), f_as_u(hi), false, false)
+                                   : __builtin_amdgcn_permlane16_swap(f_as_u(lo), f_as_u(hi), false, false);
+        return u_as_f(r[0]) + u_as_f(r[1]);
+    } else {
+        const bool h = (lane & BIT) != 0;
+        const float keep = h ? hi : lo, send = h ? lo : hi;
+        return keep + dpp_f32<LaneXchg<BIT>::CTRL>(send);
+    }
+}
+
+// Plain step at lane bit BIT: the sum of a lane's value and its partner's.
+template <int BIT>
+__device__ __forceinline__ float xsum(float a) {
+    if constexpr (BIT == 32 || BIT == 16) {
+        const auto r = (BIT == 32) ? __builtin_amdgcn_permlane32_swap(f_as_u(a), f_as_u(a), false, false)
+                                   : __builtin_amdgcn_permlane16_swap(f_as_u(a), f_as_u(a), false, false);
+        return u_as_f(r[0]) + u_as_f(r[1]);
+    } else {
+        return a + dpp_f32<LaneXchg<BIT>::CTRL>(a);
+    }
+}
+
+// Transposing butterfly over GP row sums (GP a power of two): afterwards lane
+// l holds the full sum of row l / (64 / GP).
+template <int BIT, int CNT, int GP>
+__device__ __forceinline__ void row_butterfly(float (&acc)[GP], int lane) {
+    if constexpr (BIT >= 1) {
+        if constexpr (CNT > 1) {
+#pragma unroll
+            for (int j = 0; j < CNT / 2; ++j) acc[j] = xsum_half<BIT>(acc[j], acc[j + CNT / 2], lane);
+            row_butterfly<BIT / 2, CNT / 2, GP>(acc, lane);
+        } else {
+            acc[0] = xsum<BIT>(acc[0]);
+            row_butterfly<BIT / 2, 1, GP>(acc, lane);
+        }
+    }
+}
+
+template <int G> struct Pow2Ceil { static constexpr int V = G <= 1 ? 1 : 2 * Pow2Ceil<(G + 1) / 2>::V; };
+template <> struct Pow2Ceil<1> { static constexpr int V = 1; };
+
 // --- the kernel ---------------------------------------------------------------
-// Dynamic LDS: [activation segment: xs bytes][4 wave slices of ss bytes].
+// Dynamic LDS: [activation segment: xs bytes][NW wave slices of ss bytes].
 // gridDim.y tokens: token t reads activation row t (xrow bytes apart) and
 // writes output row t; the weight rows are re-read for every token.
-template <int F, bool PAIRED, int G, int MAXU>
-__global__ __launch_bounds__(256) void k_matvec(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+// XF32: `xin` is f32 activations and xq_out (may be null) receives the Q8_0
+// rows; otherwise `xin` is Q8_0 / Q8_K activation blocks.
+template <int F, bool PAIRED, int G, int MAXU, bool XF32, int NW>
+__global__ __launch_bounds__(64 * NW) void k_matvec(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xin,
                                                 float *__restrict__ y, int N, int nb, int64_t xrow, int xs,
-                                                int ss) {
+                                                int ss, uint8_t *__restrict__ xq_out) {
     using FB = FmtBytes<F>;
     using UT = Unit<F, PAIRED>;
+    static_assert(!XF32 || F != F_Q2_K, "the fused quantizer produces Q8_0 activations");
     extern __shared__ uint4 lds_dyn[];
     constexpr int SEGU = kWave * MAXU;                 // units per segment
+    constexpr int NT = kWave * NW;                     // threads per workgroup
+    // 16-byte f32 activation pieces per thread and segment (XF32)
+    constexpr int XL = XF32 ? (8 * MAXU * UT::BPU + NW - 1) / NW : 1;
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int64_t xtok = (int64_t)blockIdx.y * xrow;   // byte offset of this token's activation row
     y += (int64_t)blockIdx.y * N;
-    const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * G;
+    const int64_t row0 = ((int64_t)blockIdx.x * NW + wave) * G;
     const int nrows = (int)max((int64_t)0, min((int64_t)G, (int64_t)N - row0));
     const int64_t RB = (int64_t)nb * FB::BB;
     const int nu = (nb / UT::BPU) * UT::UPB;           // units per row
@@ -260,17 +362,28 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t *__restrict__ w, c
     const uint8_t *xl8 = reinterpret_cast<const uint8_t *>(xlds);
     const uint8_t *sl8 = reinterpret_cast<const uint8_t *>(slice);
 
-    float acc[G];
+    constexpr int GP = Pow2Ceil<G>::V;                 // row sums, padded to a power of two
+    float acc[GP];
 #pragma unroll
-    for (int r = 0; r < G; ++r) acc[r] = 0.0f;
+    for (int r = 0; r < GP; ++r) acc[r] = 0.0f;
 
     for (int u0 = 0; u0 < nu; u0 += SEGU) {
         const int u1 = min(nu, u0 + SEGU);
         const int b0 = u0 / UT::UPB * UT::BPU, b1 = u1 / UT::UPB * UT::BPU;   // blocks of the segment
-        // activation bytes of the segment (all four waves share them)
-        const int64_t xlo = xtok + (int64_t)b0 * FB::XB, xhi = xtok + (int64_t)b1 * FB::XB;
-        const uint32_t xoff = (uint32_t)(xlo & 15);
-        dma_span(xq, xlo, xhi, xlds, lane, wave, 4);
+        // activation of the segment (all waves of the workgroup share it)
+        uint32_t xoff = 0;
+        const int nch = 8 * (b1 - b0);                 // its 16-byte f32 pieces (XF32)
+        v4f xv[XL];
+        if constexpr (XF32) {
+            const uint8_t *xseg = xin + xtok + (int64_t)b0 * 128;
+#pragma unroll
+            for (int i = 0; i < XL; ++i)
+                xv[i] = global_load16_async(xseg, 16u * (uint32_t)min((int)threadIdx.x + NT * i, nch - 1));
+        } else {
+            const int64_t xlo = xtok + (int64_t)b0 * FB::XB, xhi = xtok + (int64_t)b1 * FB::XB;
+            xoff = (uint32_t)(xlo & 15);
+            dma_span(xin, xlo, xhi, xlds, lane, wave, NW);
+        }
         // this wave's weight span
         int wissued = 0;
         int64_t A = 0;
@@ -280,11 +393,41 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t *__restrict__ w, c
             A = lo & ~(int64_t)15;
             wissued = dma_span(w, lo, hi, slice, lane, 0, 1);
         }
-        wait_vmcnt(wissued);                           // this wave's activation chunks have landed
+        wait_vmcnt(wissued);                           // this wave's activation loads have landed
+        if constexpr (XF32) {
+            constexpr int US = XLayout<UT::BPU>::US;
+            uint8_t *xw8 = reinterpret_cast<uint8_t *>(xlds);
+            uint8_t *xq_row = (xq_out != nullptr && blockIdx.x == 0)
+                                  ? xq_out + (int64_t)blockIdx.y * nb * kQ80Bytes + (int64_t)b0 * kQ80Bytes
+                                  : nullptr;
+#pragma unroll
+            for (int i = 0; i < XL; ++i) {
+                pin_after_wait(xv[i]);
+                const int c = (int)threadIdx.x + NT * i;    // piece c = part c%8 of segment block c/8
+                float d;
+                const uint32_t packed = q8_0_part(make_float4(xv[i][0], xv[i][1], xv[i][2], xv[i][3]), d);
+                if (c < nch) {
+                    const int jb = c >> 3, part = c & 7;
+                    uint8_t *ub = xw8 + US * (jb / UT::BPU);
+                    const int j = jb % UT::BPU;
+                    *reinterpret_cast<uint32_t *>(ub + 32 * j + 4 * part) = packed;
+                    if (part == 0)
+                        reinterpret_cast<float *>(ub + 32 * UT::BPU)[j] = f16_bits_to_f32(f32_to_f16_bits(d));
+                    if (xq_row != nullptr) store_q8_0_part(xq_row + (int64_t)jb * kQ80Bytes, part, packed, d);
+                }
+            }
+            wait_lds_reads();                          // the codes are in LDS
+        }
         __builtin_amdgcn_s_barrier();                  // ... and every other wave's
         XU<F, PAIRED> xu[MAXU];
 #pragma unroll
-        for (int i = 0; i < MAXU; ++i) load_xu<F, PAIRED>(xl8, xoff, min(lane + kWave * i, u1 - u0 - 1), xu[i]);
+        for (int i = 0; i < MAXU; ++i) {
+            const int ul = min(lane + kWave * i, u1 - u0 - 1);
+            if constexpr (XF32)
+                load_xu_q<F, PAIRED>(xl8, ul, xu[i]);
+            else
+                load_xu<F, PAIRED>(xl8, xoff, ul, xu[i]);
+        }
         if (nrows > 0) {
 #pragma unroll
             for (int r = 0; r < G; ++r) {
@@ -314,34 +457,16 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t *__restrict__ w, c
     }
     if (nrows == 0) return;
 
-    // transposing butterfly: at step `bit` (32, 16, ...) a lane keeps half of its
-    // live row sums and adds its partner's copy of that half.
-    int cnt = G;
-#pragma unroll
-    for (int bit = 32; bit >= 1; bit >>= 1) {
-        if (cnt > 1) {
-            const bool hi = (lane & bit) != 0;
-#pragma unroll
-            for (int j = 0; j < G / 2; ++j) {
-                if (j < cnt / 2) {
-                    const float keep = hi ? acc[j + cnt / 2] : acc[j];
-                    const float send = hi ? acc[j] : acc[j + cnt / 2];
-                    acc[j] = keep + xor_shfl(send, bit);
-                }
-            }
-            cnt >>= 1;
-        } else {
-            acc[0] += xor_shfl(acc[0], bit);
-        }
-    }
-    constexpr int LPR = kWave / G;                     // lanes holding copies of one row's sum
+    row_butterfly<32, GP, GP>(acc, lane);
+    constexpr int LPR = kWave / GP;                    // lanes holding copies of one row's sum
     const int r = lane / LPR;
     if (lane % LPR == 0 && r < nrows) y[row0 + r] = acc[0];
 }
 
 // --- launch configuration -----------------------------------------------------
-template <int F, bool PAIRED, int G, int MAXU>
-static hipError_t launch_mv(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+template <int F, bool PAIRED, int G, int MAXU, bool XF32, int NW = 4>
+static hipError_t launch_mv(const void *w, const void *xin, uint8_t *xq_out, float *y, int M, int N, int nb,
+                            hipStream_t st) {
     using FB = FmtBytes<F>;
     using UT = Unit<F, PAIRED>;
     const int nu = (nb / UT::BPU) * UT::UPB;
@@ -351,19 +476,21 @@ static hipError_t launch_mv(const void *w, const void *xq, float *y, int M, int 
     // whole 1 KB chunk groups (dma_span may fill a full last group) after up to
     // 15 bytes of misalignment at each end
     const int ss = (int)(((span + 32 + 1023) / 1024) * 1024);
-    const int xs = (int)((((int64_t)segb * FB::XB + 32 + 1023) / 1024) * 1024);
+    const int xs = XF32 ? (XLayout<UT::BPU>::US * segu + 15) / 16 * 16
+                        : (int)((((int64_t)segb * FB::XB + 32 + 1023) / 1024) * 1024);
     const int64_t waves = ((int64_t)N + G - 1) / G;
-    const int64_t grid = (waves + 3) / 4;
+    const int64_t grid = (waves + NW - 1) / NW;
     const uint8_t *wp = static_cast<const uint8_t *>(w);
-    const uint8_t *xp = static_cast<const uint8_t *>(xq);
-    int64_t xrow = (int64_t)nb * FB::XB;
+    const uint8_t *xp = static_cast<const uint8_t *>(xin);
+    int64_t xrow = XF32 ? (int64_t)nb * 128 : (int64_t)nb * FB::XB;
+    const auto kern = k_matvec<F, PAIRED, G, MAXU, XF32, NW>;
+    const size_t lds = (size_t)xs + (size_t)NW * ss;
     static int lds_ok = 0;
-    const hipError_t e = allow_dynamic_lds((const void *)k_matvec<F, PAIRED, G, MAXU>, (size_t)(xs + 4 * ss), lds_ok);
+    const hipError_t e = allow_dynamic_lds((const void *)kern, lds, lds_ok);
     if (e != hipSuccess) return e;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&N, (void *)&nb,
-                    (void *)&xrow, (void *)&xs, (void *)&ss};
-    return hipLaunchKernel((const void *)k_matvec<F, PAIRED, G, MAXU>, dim3((unsigned)grid, (unsigned)M),
-                           dim3(256), args, (size_t)(xs + 4 * ss), st);
+                    (void *)&xrow, (void *)&xs, (void *)&ss, (void *)&xq_out};
+    return hipLaunchKernel((const void *)kern, dim3((unsigned)grid, (unsigned)M), dim3(kWave * NW), args, lds, st);
 }
 
 // Rows per wave: a slice of about 5 KB.  Measured on MI355X over 28-96 MB
@@ -371,42 +498,78 @@ static hipError_t launch_mv(const void *w, const void *xq, float *y, int M, int 
 // Q2_K: 2 rows) beat larger ones: the work after the last byte lands is
 // smaller and all waves of the launch stay resident.  One row when the row
 // needs more than one segment.
-template <int F, bool PAIRED>
-static hipError_t pick_mv(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+template <int F, bool PAIRED, bool XF32>
+static hipError_t pick_mv(const void *w, const void *xin, uint8_t *xq_out, float *y, int M, int N, int nb,
+                          hipStream_t st) {
     using FB = FmtBytes<F>;
     using UT = Unit<F, PAIRED>;
+    // The fused kernel runs eight waves per workgroup when a row fits one
+    // segment: every workgroup quantizes the whole activation row, so fewer,
+    // larger workgroups do less of that redundant work (measured on MI355X,
+    // Q4_0 12288x4096: 7.5 us with eight waves against 8.4 us with four; the
+    // LDS of eight slices still fits three workgroups per CU).
+    constexpr int NW1 = XF32 ? 8 : 4;
     const int nu = (nb / UT::BPU) * UT::UPB;
     const int64_t rb = (int64_t)nb * FB::BB;
-    if (nu > kWave * 4) return launch_mv<F, PAIRED, 1, 4>(w, xq, y, M, N, nb, st);
+    if (nu > kWave * 4) return launch_mv<F, PAIRED, 1, 4, XF32>(w, xin, xq_out, y, M, N, nb, st);
     const int64_t g = 5000 / rb;
     if (nu <= kWave) {
-        if (g >= 8) return launch_mv<F, PAIRED, 8, 1>(w, xq, y, M, N, nb, st);
-        if (g >= 4) return launch_mv<F, PAIRED, 4, 1>(w, xq, y, M, N, nb, st);
-        if (g >= 2) return launch_mv<F, PAIRED, 2, 1>(w, xq, y, M, N, nb, st);
-        return launch_mv<F, PAIRED, 1, 1>(w, xq, y, M, N, nb, st);
+        if (g >= 8) return launch_mv<F, PAIRED, 8, 1, XF32, NW1>(w, xin, xq_out, y, M, N, nb, st);
+        if (g >= 4) return launch_mv<F, PAIRED, 4, 1, XF32, NW1>(w, xin, xq_out, y, M, N, nb, st);
+        if (g >= 2) return launch_mv<F, PAIRED, 2, 1, XF32, NW1>(w, xin, xq_out, y, M, N, nb, st);
+        return launch_mv<F, PAIRED, 1, 1, XF32, NW1>(w, xin, xq_out, y, M, N, nb, st);
     }
-    if (g >= 4) return launch_mv<F, PAIRED, 4, 4>(w, xq, y, M, N, nb, st);
-    if (g >= 2) return launch_mv<F, PAIRED, 2, 4>(w, xq, y, M, N, nb, st);
-    return launch_mv<F, PAIRED, 1, 4>(w, xq, y, M, N, nb, st);
+    if (g >= 4) return launch_mv<F, PAIRED, 4, 4, XF32>(w, xin, xq_out, y, M, N, nb, st);
+    if (g >= 2) return launch_mv<F, PAIRED, 2, 4, XF32>(w, xin, xq_out, y, M, N, nb, st);
+    return launch_mv<F, PAIRED, 1, 4, XF32>(w, xin, xq_out, y, M, N, nb, st);
 }
 
-template <int F>
-static hipError_t dispatch_mv(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+template <int F, bool XF32 = false>
+static hipError_t dispatch_mv(const void *w, const void *xin, uint8_t *xq_out, float *y, int M, int N, int nb,
+                              hipStream_t st) {
     if constexpr (F != F_Q2_K) {
-        if (nb % 2 == 0) return pick_mv<F, true>(w, xq, y, M, N, nb, st);
+        if (nb % 2 == 0) return pick_mv<F, true, XF32>(w, xin, xq_out, y, M, N, nb, st);
     }
-    return pick_mv<F, false>(w, xq, y, M, N, nb, st);
+    return pick_mv<F, false, XF32>(w, xin, xq_out, y, M, N, nb, st);
 }
 
 hipError_t launch_matvec_q4_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st) {
-    return dispatch_mv<F_Q4_0>(w, xq, y, 1, N, nb, st);
+    return dispatch_mv<F_Q4_0>(w, xq, nullptr, y, 1, N, nb, st);
 }
 hipError_t launch_matvec_q8_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st) {
-    return dispatch_mv<F_Q8_0>(w, xq, y, 1, N, nb, st);
+    return dispatch_mv<F_Q8_0>(w, xq, nullptr, y, 1, N, nb, st);
 }
 hipError_t launch_matvec_q2_k(const void *w, const void *xq, float *y, int N, int ns, hipStream_t st) {
-    return dispatch_mv<F_Q2_K>(w, xq, y, 1, N, ns, st);
+    return dispatch_mv<F_Q2_K>(w, xq, nullptr, y, 1, N, ns, st);
 }
+// Fused decode step.  A row of more than one segment (more than 64 units)
+// makes every workgroup quantize a long activation row, as many bytes as its
+// weights (Q8_0 4096 x 11008 on MI355X: 16.0 us fused against 13.9 us for two
+// launches); there, when the caller supplies the Q8_0 output row, the
+// activation is quantized into it once and the plain matvec reads it.  The
+// result is the same either way: the same codes, the same per-row order.
+template <int F>
+static hipError_t quantize_matvec(const void *w, const float *x, void *xq, float *y, int N, int nb,
+                                  hipStream_t st) {
+    const bool paired = F != F_Q2_K && nb % 2 == 0;
+    const int nu = paired ? nb / 2 : nb;
+    if (xq != nullptr && nu > kWave) {
+        const hipError_t e = launch_quantize_q8_0(x, xq, nb, st);
+        if (e != hipSuccess) return e;
+        return dispatch_mv<F>(w, xq, nullptr, y, 1, N, nb, st);
+    }
+    return dispatch_mv<F, true>(w, x, static_cast<uint8_t *>(xq), y, 1, N, nb, st);
+}
+
+hipError_t launch_quantize_matvec_q4_0(const void *w, const float *x, void *xq, float *y, int N, int nb,
+                                       hipStream_t st) {
+    return quantize_matvec<F_Q4_0>(w, x, xq, y, N, nb, st);
+}
+hipError_t launch_quantize_matvec_q8_0(const void *w, const float *x, void *xq, float *y, int N, int nb,
+                                       hipStream_t st) {
+    return quantize_matvec<F_Q8_0>(w, x, xq, y, N, nb, st);
+}
+
 // Q2_K prefill: the matvec kernel with one grid row per token (the weights are
 // re-read from cache for each token; correct for any M, not tuned).
 hipError_t launch_matmul_q2_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
@@ -414,7 +577,7 @@ hipError_t launch_matmul_q2_k(const void *w, const void *xq, float *y, int M, in
     for (int m0 = 0; m0 < M; m0 += kMaxY) {
         const int mc = min(kMaxY, M - m0);
         const uint8_t *xp = static_cast<const uint8_t *>(xq) + (int64_t)m0 * ns * kQ8KBytes;
-        const hipError_t e = dispatch_mv<F_Q2_K>(w, xp, y + (int64_t)m0 * N, mc, N, ns, st);
+        const hipError_t e = dispatch_mv<F_Q2_K>(w, xp, nullptr, y + (int64_t)m0 * N, mc, N, ns, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -15,6 +15,7 @@ constexpr int kQ8KBytes = 292;            // f32 d + int8[256] + int16[16]
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 // binary32 -> binary16 bits: v_cvt_f16_f32 rounds to nearest even under the
 // default MODE and keeps f16 denormals.
@@ -48,6 +49,20 @@ typedef __attribute__((address_space(1))) void global_void;
 __device__ __forceinline__ void global_to_lds16(const void *src, void *dst) {
     __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)dst, 16, 0, 0);
 }
+
+// 16 bytes per lane from global memory into registers, issued as inline
+// assembly so that the compiler neither tracks nor waits for it: the caller
+// waits with wait_vmcnt() and then passes the value through pin_after_wait()
+// before any use.  Loads and LDS-DMA copies complete in issue order, so a load
+// issued before a run of LDS-DMA copies can be waited for alone.
+__device__ __forceinline__ v4f global_load16_async(const void *base, uint32_t off) {
+    v4f v;
+    asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(v) : "v"(off), "s"(base));
+    return v;
+}
+
+// Orders every use of v after the preceding (volatile) wait.
+__device__ __forceinline__ void pin_after_wait(v4f &v) { asm volatile("" : "+v"(v)); }
 
 // Wait for every outstanding vector-memory load of this wave (including LDS DMA).
 __device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -88,6 +103,55 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 template <typename T>
 __device__ __forceinline__ T xor_shfl(T v, int mask) {
     return __shfl_xor(v, mask, kWave);
+}
+
+// Q8_0 quantization of one 32-value block held by 8 consecutive lanes (lane
+// part p = lane & 7 holds values 4p..4p+3): amax over the block by three lane
+// exchanges, d = amax/127, id = amax ? 127/amax : 0, q = rne(x*id).  Returns
+// the lane's four codes packed little-endian and sets d (f32, not yet rounded
+// to f16).  Every step is one correctly rounded f32 operation (division is
+// correctly rounded, no contraction, denormals kept), so any kernel using it
+// yields the same codes.  All 64 lanes must call it together.
+// Lane l reads lane (l & ~7) + 7 - (l & 7) of v, or v's lane l ^ 1 / l ^ 2 within its
+// quad (DPP row_half_mirror / quad_perm: a VALU operand modifier, no LDS trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                                 false));
+}
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfRowMirror = 0x141;  // row_half_mirror: lane i of 8 reads lane 7 - i
+constexpr int kDppRowRor8 = 0x128;        // row_ror:8: lane i of 16 reads lane i ^ 8
+
+// Maximum over each aligned group of 8 lanes (every lane of the group gets
+// it): the quad maxima, then the other quad's through the half-row mirror.
+__device__ __forceinline__ float max8_lanes(float a) {
+    a = fmaxf(a, dpp_f32<kDppQuadXor1>(a));
+    a = fmaxf(a, dpp_f32<kDppQuadXor2>(a));
+    return fmaxf(a, dpp_f32<kDppHalfRowMirror>(a));
+}
+
+__device__ __forceinline__ uint32_t q8_0_part(float4 v, float &d) {
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = max8_lanes(a);
+    d = a / 127.0f;
+    const float id = (a != 0.0f) ? 127.0f / a : 0.0f;
+    const int q0 = (int)rintf(v.x * id);
+    const int q1 = (int)rintf(v.y * id);
+    const int q2 = (int)rintf(v.z * id);
+    const int q3 = (int)rintf(v.w * id);
+    return (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) | ((uint32_t)(q2 & 0xff) << 16) |
+           ((uint32_t)(q3 & 0xff) << 24);
+}
+
+// Store one lane's part of a Q8_0 block at `blk` (a 2-byte aligned 34-byte
+// block): its four codes at byte 2 + 4*part, and the f16 scale from part 0.
+__device__ __forceinline__ void store_q8_0_part(uint8_t *blk, int part, uint32_t packed, float d) {
+    uint16_t *o16 = reinterpret_cast<uint16_t *>(blk + 2 + 4 * part);
+    o16[0] = (uint16_t)(packed & 0xffffu);
+    o16[1] = (uint16_t)(packed >> 16);
+    if (part == 0) *reinterpret_cast<uint16_t *>(blk) = (uint16_t)f32_to_f16_bits(d);
 }
 
 }  // namespace qmm

@@ -25,27 +25,9 @@ __global__ __launch_bounds__(256) void k_quantize_q8_0(const float4 *__restrict_
     const int part = threadIdx.x & 7;
     const bool valid = blk < nblocks;
     float4 v = valid ? x[t] : make_float4(0.f, 0.f, 0.f, 0.f);
-
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    a = fmaxf(a, xor_shfl(a, 1));
-    a = fmaxf(a, xor_shfl(a, 2));
-    a = fmaxf(a, xor_shfl(a, 4));
-
-    const float d = a / 127.0f;
-    const float id = (a != 0.0f) ? 127.0f / a : 0.0f;
-    const int q0 = (int)rintf(v.x * id);
-    const int q1 = (int)rintf(v.y * id);
-    const int q2 = (int)rintf(v.z * id);
-    const int q3 = (int)rintf(v.w * id);
-    const uint32_t packed = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
-                            ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
-    if (valid) {
-        uint8_t *ob = out + blk * kQ80Bytes;
-        uint16_t *o16 = reinterpret_cast<uint16_t *>(ob + 2 + 4 * part);   // 2-byte aligned
-        o16[0] = (uint16_t)(packed & 0xffffu);
-        o16[1] = (uint16_t)(packed >> 16);
-        if (part == 0) *reinterpret_cast<uint16_t *>(ob) = (uint16_t)f32_to_f16_bits(d);
-    }
+    float d;
+    const uint32_t packed = q8_0_part(v, d);
+    if (valid) store_q8_0_part(out + blk * kQ80Bytes, part, packed, d);
 }
 
 // ---------------------------------------------------------------------------

@@ -70,6 +70,11 @@ A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced
     (lambda L: L.qmm_matmul_q4_0(A, A, A, 1 << 31, 8, 32, None), 1),   # M >= 2^31
     (lambda L: L.qmm_matmul_q2_k(A, A, A, 4, 8, 256 * 3 + 32, None), 1),
     (lambda L: L.qmm_matmul_q4_0(A, A, A, 1 << 30, 1 << 30, 32, None), 1),   # output bytes overflow
+    (lambda L: L.qmm_quantize_matvec_q4_0(A, A, A, A, 8, 48, None), 1),      # K % 32
+    (lambda L: L.qmm_quantize_matvec_q4_0(A, None, A, A, 8, 64, None), 2),   # x NULL
+    (lambda L: L.qmm_quantize_matvec_q8_0(A, A, A, None, 8, 64, None), 2),   # y NULL
+    (lambda L: L.qmm_quantize_matvec_q8_0(A, A, A + 2, A, 8, 64, None), 3),  # xq misaligned
+    (lambda L: L.qmm_quantize_matvec_q4_0(A, A + 4, None, A, 8, 64, None), 3),
 ])
 def test_argument_errors_without_device(q, call, code):
     assert call(q.lib()) == code
@@ -80,6 +85,7 @@ def test_empty_problem_is_a_no_op(q):
     assert L.qmm_matmul_q4_0(None, None, None, 0, 8, 32, None) == 0
     assert L.qmm_matvec_q8_0(None, None, None, 0, 32, None) == 0
     assert L.qmm_quantize_q8_0(None, None, 0, 64, None) == 0
+    assert L.qmm_quantize_matvec_q4_0(None, None, None, None, 0, 64, None) == 0
 
 
 def test_python_binding_raises(q):

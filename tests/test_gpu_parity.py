@@ -170,6 +170,73 @@ def test_matvec_matches_oracle(env, fmt, N, K):
     _check(y, ref["y64"][0], ref["mag"][0], (fmt, N, K))
 
 
+FUSED_CASES = [
+    ("q4_0", 512, 1024), ("q4_0", 12288, 4096),
+    ("q4_0", 1, 32), ("q4_0", 3, 96), ("q4_0", 17, 160), ("q4_0", 5, 2080), ("q4_0", 7, 8192),
+    ("q4_0", 9, 20480), ("q4_0", 45, 1024), ("q4_0", 13, 2048), ("q4_0", 7, 4000),
+    ("q8_0", 37, 256), ("q8_0", 3, 64), ("q8_0", 5, 16384), ("q8_0", 3, 40960),
+    ("q8_0", 12288, 4096), ("q8_0", 22016, 4096), ("q8_0", 4096, 11008),
+    ("q8_0", 1, 32), ("q8_0", 11, 4128), ("q8_0", 3, 20000),
+]
+
+
+def _run_fused(env, fmt, wq, x, N, K, want_xq=True):
+    torch, q, _ = env
+    y = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    xq = torch.full((q.row_bytes("q8_0", K),), 0xA5, dtype=torch.uint8, device="cuda") if want_xq else None
+    q.QUANTIZE_MATVEC[fmt](_dev(torch, wq), _dev(torch, x), xq, y, N, K)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), (xq.cpu().numpy() if want_xq else None)
+
+
+@pytest.mark.parametrize("fmt,N,K", FUSED_CASES)
+def test_fused_quantize_matvec_matches_oracle(env, fmt, N, K):
+    """One launch quantizes the f32 activation and applies the weights: the
+    Q8_0 row it writes is the oracle's byte for byte, the output is within the
+    bound of the oracle's product on that row."""
+    _, _, orc = env
+    _say("quantize_matvec", fmt, N, K)
+    seed = 9000 + N + K
+    wq = orc.quantize_w(fmt, synth.gaussian_f32((N, K), 0.02, seed))
+    x = synth.with_outliers(synth.gaussian_f32((1, K), 1.0, seed + 1), 0.01, 20.0, seed + 2)
+    x[0, :32] = 0.0                                   # zero block
+    if K >= 64:
+        x[0, 32:64] = 0.0
+        x[0, 37] = -2.75                              # one nonzero value
+    if K >= 96:
+        x[0, 64:96] = np.arange(32, dtype=np.float32) - 15.5   # ties at .5
+        x[0, 64] = 127.0
+    if K >= 128:
+        x[0, 96:128] *= 1e-30                         # tiny but inside the contract
+    xq_ref = orc.quantize_q8_0(x)
+    y, xq = _run_fused(env, fmt, wq, x, N, K)
+    assert np.array_equal(xq, xq_ref.reshape(-1))
+    ref = orc.matmul(fmt, wq, xq_ref, 1, N, K, threads=8, want=("y64", "mag"))
+    _check(y, ref["y64"][0], ref["mag"][0], ("fused", fmt, N, K))
+
+
+@pytest.mark.parametrize("fmt,N,K", [("q4_0", 1000, 4096), ("q4_0", 37, 8192), ("q4_0", 9, 20480),
+                                     ("q4_0", 5, 2080), ("q4_0", 45, 1024), ("q8_0", 300, 4096),
+                                     ("q8_0", 3, 40960), ("q8_0", 11, 4128)])
+def test_fused_without_xq_output_equals_two_launches(env, fmt, N, K):
+    """xq = NULL (always the single fused launch, also for long rows): y is
+    within the bound of the oracle and bit-identical to the two-launch path
+    (same codes, same per-row summation order)."""
+    torch, q, orc = env
+    _say("quantize_matvec no xq", fmt, N, K)
+    wq = orc.quantize_w(fmt, synth.gaussian_f32((N, K), 0.02, 9500 + K))
+    x = synth.with_outliers(synth.gaussian_f32((1, K), 1.0, 9501 + K), 0.01, 20.0, 9502 + K)
+    y, _ = _run_fused(env, fmt, wq, x, N, K, want_xq=False)
+    xq_d = torch.empty(q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q8_0(_dev(torch, x), xq_d, 1, K)
+    y2 = torch.empty(N, dtype=torch.float32, device="cuda")
+    q.MATVEC[fmt](_dev(torch, wq), xq_d, y2, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(y, y2.cpu().numpy())
+    ref = orc.matmul(fmt, wq, orc.quantize_q8_0(x), 1, N, K, threads=8, want=("y64", "mag"))
+    _check(y, ref["y64"][0], ref["mag"][0], ("fused no xq", fmt, N, K))
+
+
 MATMUL_CASES = [
     ("q4_0", 1, 8, 32), ("q4_0", 37, 200, 1024), ("q4_0", 128, 128, 4096), ("q4_0", 130, 129, 160),
     ("q4_0", 64, 512, 1024), ("q4_0", 5, 3, 96), ("q4_0", 256, 384, 4128), ("q4_0", 300, 700, 2080),
@@ -274,6 +341,12 @@ def test_device_errors_are_reported(env):
     with pytest.raises(q.QmmError) as e:
         q.qmm_matmul_q2_k(buf, buf, buf, 1, 1, 100)
     assert e.value.code == "QMM_E_SHAPE"
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_quantize_matvec_q4_0(buf, buf, buf[2:], buf, 4, 64)
+    assert e.value.code == "QMM_E_ALIGN"
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_quantize_matvec_q8_0(buf, buf, None, buf, 4, 48)
+    assert e.value.code == "QMM_E_SHAPE"
 
 
 def test_graph_replay_matches_eager(env):
@@ -287,29 +360,36 @@ def test_graph_replay_matches_eager(env):
     wq = _dev(torch, orc.quantize_q4_0_w(w))
     xd = _dev(torch, x)
     xq = torch.empty(M * q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
+    xq1 = torch.empty(q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
     yv = torch.empty(N, dtype=torch.float32, device="cuda")
+    yf = torch.empty(N, dtype=torch.float32, device="cuda")
     ym = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
     def work():
         q.qmm_quantize_q8_0(xd, xq, M, K)
         q.qmm_matvec_q4_0(wq, xq, yv, N, K)
+        q.qmm_quantize_matvec_q4_0(wq, xd[1], xq1, yf, N, K)
         q.qmm_matmul_q4_0(wq, xq, ym, M, N, K)
 
     work()
     torch.cuda.synchronize()
-    ref_v, ref_m, ref_q = yv.clone(), ym.clone(), xq.clone()
+    ref_v, ref_m, ref_q, ref_f, ref_q1 = yv.clone(), ym.clone(), xq.clone(), yf.clone(), xq1.clone()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         work()
     for rep in range(4):
         yv.fill_(float("nan"))
+        yf.fill_(float("nan"))
         ym.fill_(float("nan"))
         xq.zero_()
+        xq1.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(xq, ref_q), rep
         assert torch.equal(yv, ref_v), rep
         assert torch.equal(ym, ref_m), rep
+        assert torch.equal(yf, ref_f), rep
+        assert torch.equal(xq1, ref_q1), rep
         work()                      # eager work between replays
         torch.cuda.synchronize()

@@ -20,10 +20,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmm_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q4_0, Q8_0, Q2_K = 0, 1, 2
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q2_k": 84, "q8_k": 292}
-BLOCK_VALUES = {"q4_0": 32, "q8_0": 32, "q2_k": 256, "q8_k": 256}
-FMT_ID = {"q4_0": Q4_0, "q8_0": Q8_0, "q2_k": Q2_K}
+Q4_0, Q8_0, Q2_K, Q4_K, Q6_K = 0, 1, 2, 3, 4
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q2_k": 84, "q8_k": 292, "q4_k": 144, "q6_k": 210}
+BLOCK_VALUES = {"q4_0": 32, "q8_0": 32, "q2_k": 256, "q8_k": 256, "q4_k": 256, "q6_k": 256}
+FMT_ID = {"q4_0": Q4_0, "q8_0": Q8_0, "q2_k": Q2_K, "q4_k": Q4_K, "q6_k": Q6_K}
+K_QUANTS = ("q2_k", "q4_k", "q6_k")
 
 _lib = None
 
@@ -49,7 +50,9 @@ def lib():
         L.orc_f16_to_f32.argtypes = [U16]
         L.orc_f16_to_f32.restype = ctypes.c_float
         for name in ("orc_quantize_q8_0", "orc_quantize_q8_k", "orc_quantize_q4_0_w", "orc_quantize_q2_k_w",
-                     "orc_dequantize_q8_0", "orc_dequantize_q4_0", "orc_dequantize_q2_k", "orc_dequantize_q8_k"):
+                     "orc_quantize_q4_k_w", "orc_quantize_q6_k_w",
+                     "orc_dequantize_q8_0", "orc_dequantize_q4_0", "orc_dequantize_q2_k", "orc_dequantize_q8_k",
+                     "orc_dequantize_q4_k", "orc_dequantize_q6_k"):
             getattr(L, name).argtypes = [P, P, I64, I64]
             getattr(L, name).restype = None
         L.orc_matmul.argtypes = [I32, P, P, P, P, P, I64, I64, I64, I32]
@@ -137,13 +140,29 @@ def quantize_q2_k_w(w) -> np.ndarray:
     return _quant("orc_quantize_q2_k_w", "q2_k", w)
 
 
+def quantize_q4_k_w(w) -> np.ndarray:
+    """f32 weights [N][K] -> Q4_K bytes [N][K/256*144]."""
+    return _quant("orc_quantize_q4_k_w", "q4_k", w)
+
+
+def quantize_q6_k_w(w) -> np.ndarray:
+    """f32 weights [N][K] -> Q6_K bytes [N][K/256*210]."""
+    return _quant("orc_quantize_q6_k_w", "q6_k", w)
+
+
 def quantize_w(fmt: str, w) -> np.ndarray:
-    return {"q4_0": quantize_q4_0_w, "q8_0": quantize_q8_0, "q2_k": quantize_q2_k_w}[fmt](w)
+    return {"q4_0": quantize_q4_0_w, "q8_0": quantize_q8_0, "q2_k": quantize_q2_k_w,
+            "q4_k": quantize_q4_k_w, "q6_k": quantize_q6_k_w}[fmt](w)
+
+
+def act_format(fmt: str) -> str:
+    """Activation format paired with weight format `fmt` (Q8_K for the K-quants, else Q8_0)."""
+    return "q8_k" if fmt in K_QUANTS else "q8_0"
 
 
 def quantize_x(fmt: str, x) -> np.ndarray:
-    """Activation quantizer paired with weight format `fmt` (Q8_K for Q2_K, else Q8_0)."""
-    return quantize_q8_k(x) if fmt == "q2_k" else quantize_q8_0(x)
+    """Activation quantizer paired with weight format `fmt`."""
+    return quantize_q8_k(x) if fmt in K_QUANTS else quantize_q8_0(x)
 
 
 def dequantize(fmt: str, blocks, K: int) -> np.ndarray:
@@ -164,7 +183,7 @@ def matmul(fmt: str, w, xq, M: int, N: int, K: int, threads: int = 1, want=("y",
     w = _u8(w)
     xq = _u8(xq)
     assert w.size == N * row_bytes(fmt, K)
-    assert xq.size == M * row_bytes("q8_k" if fmt == "q2_k" else "q8_0", K)
+    assert xq.size == M * row_bytes(act_format(fmt), K)
     res = {}
     y = np.zeros((M, N), dtype=np.float32) if "y" in want else None
     y64 = np.zeros((M, N), dtype=np.float64) if "y64" in want else None

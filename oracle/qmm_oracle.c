@@ -22,9 +22,14 @@
  *
  * Parity status: every exported function is pinned by a CPU test (values the
  * pages print, closed forms, invariants, a library routine or brute force),
- * except the Q2_K weight quantizer, whose rule the pages do not give at all:
- * its output bytes are only test data, and its rule is "parity unpinned"
- * (only the invariants of the format it must produce are checked).
+ * except where the pages give no rule at all, which is "parity unpinned":
+ *   - the Q2_K, Q4_K and Q6_K weight quantizers (their output bytes are only
+ *     test data; only the invariants of the format they fill are checked);
+ *   - the packing of Q4_K's eight 6-bit scales and mins into 12 bytes, and the
+ *     whole Q6_K block layout: the pages give the block sizes (144 and 210
+ *     bytes), Q4_K's field order and its two-term dot, but not these bits; the
+ *     reading is GGUF's layout, pinned only by round trips and by brute force
+ *     against the decoded values (which checks the dot, not the layout).
  */
 #include <math.h>
 #include <pthread.h>
@@ -38,6 +43,8 @@
 #define Q8_0_BYTES 34
 #define Q2_K_BYTES 84
 #define Q8_K_BYTES 292
+#define Q4_K_BYTES 144
+#define Q6_K_BYTES 210
 
 /* ------------------------------------------------------------------ */
 /* IEEE binary16 <-> binary32                                          */
@@ -274,6 +281,152 @@ void orc_quantize_q2_k_w(const float *w, uint8_t *out, int64_t N, int64_t K) {
     }
 }
 
+/* Q4_K layout ([minfer] block.rs sizes: 144 bytes; the K-quant dot kernel
+ * walked in "The payoff": f16 d @0, f16 dmin @2, 12 bytes of scales @4, 128
+ * bytes of nibbles @16; 32-byte chunk j holds values 64j + l in its low
+ * nibbles and 64j + 32 + l in its high nibbles, l < 32; sub-block s of 32
+ * values uses scales[s] and mins[s]).  The packing of the eight 6-bit scales
+ * and eight 6-bit mins into the 12 bytes is not on the pages; the reading is
+ * GGUF's: for s < 4, scale = b[s] & 63 and min = b[s+4] & 63; for s >= 4,
+ * scale = (b[s+4] & 15) | (b[s-4] >> 6) << 4 and min = (b[s+4] >> 4) |
+ * (b[s] >> 6) << 4. */
+static void q4k_scale_min(const uint8_t *b, int s, int *sc, int *m) {
+    if (s < 4) {
+        *sc = b[s] & 63;
+        *m = b[s + 4] & 63;
+    } else {
+        *sc = (b[s + 4] & 15) | ((b[s - 4] >> 6) << 4);
+        *m = (b[s + 4] >> 4) | ((b[s] >> 6) << 4);
+    }
+}
+
+static void q4k_pack_scale_min(uint8_t *b, const int *sc, const int *m) {
+    for (int s = 0; s < 4; ++s) {
+        b[s] = (uint8_t)((sc[s] & 63) | ((sc[s + 4] >> 4) << 6));
+        b[s + 4] = (uint8_t)((m[s] & 63) | ((m[s + 4] >> 4) << 6));
+        b[s + 8] = (uint8_t)((sc[s + 4] & 15) | ((m[s + 4] & 15) << 4));
+    }
+}
+
+/* The 4-bit code of value i of a Q4_K block (the chunk order above). */
+static int q4k_code(const uint8_t *blk, int i) {
+    int j = i / 64, hi = (i % 64) / 32, l = i % 32;
+    uint8_t byte = blk[16 + 32 * j + l];
+    return hi ? byte >> 4 : byte & 15;
+}
+
+/* Q4_K weights, per 256 in 8 sub-blocks of 32 (format above; a weight
+ * decodes as d * sc_s * q - dmin * m_s, [minfer] "The payoff": value =
+ * q * d_s - min_s).  The pages give no quantizer; the rule here, like Q2_K's:
+ *   per sub-block: lo = min(0, min x), hi = max x, s = (hi - lo) / 15, mn = -lo;
+ *   d = max s / 63, dmin = max mn / 63 (stored f16);
+ *   sc = clamp(round(s / f16(d)), 0, 63), m = clamp(round(mn / f16(dmin)), 0, 63);
+ *   q = clamp(round((x + f16(dmin) * m) / (f16(d) * sc)), 0, 15), 0 if the divisor is 0. */
+void orc_quantize_q4_k_w(const float *w, uint8_t *out, int64_t N, int64_t K) {
+    int64_t ns = K / QKK;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t sb = 0; sb < ns; ++sb) {
+            const float *xb = w + n * K + sb * QKK;
+            uint8_t *ob = out + (n * ns + sb) * Q4_K_BYTES;
+            float sv[8], mn[8], smax = 0.0f, mnmax = 0.0f;
+            for (int t = 0; t < 8; ++t) {
+                float lo = 0.0f, hi = xb[32 * t];
+                for (int i = 0; i < 32; ++i) {
+                    float v = xb[32 * t + i];
+                    if (v < lo) lo = v;
+                    if (v > hi) hi = v;
+                }
+                sv[t] = (hi - lo) / 15.0f;
+                mn[t] = -lo;
+                if (sv[t] > smax) smax = sv[t];
+                if (mn[t] > mnmax) mnmax = mn[t];
+            }
+            wr_f16(ob, smax / 63.0f);
+            wr_f16(ob + 2, mnmax / 63.0f);
+            float dh = rd_f16(ob), dminh = rd_f16(ob + 2);
+            int sc[8], mm[8];
+            for (int t = 0; t < 8; ++t) {
+                int a = 0, c = 0;
+                if (dh != 0.0f) a = (int)rne(sv[t] / dh);
+                if (dminh != 0.0f) c = (int)rne(mn[t] / dminh);
+                sc[t] = a < 0 ? 0 : (a > 63 ? 63 : a);
+                mm[t] = c < 0 ? 0 : (c > 63 ? 63 : c);
+            }
+            q4k_pack_scale_min(ob + 4, sc, mm);
+            memset(ob + 16, 0, 128);
+            for (int i = 0; i < QKK; ++i) {
+                int t = i / 32;
+                float off = dminh * (float)mm[t];
+                float div = dh * (float)sc[t];
+                int c = 0;
+                if (div != 0.0f) c = (int)rne((xb[i] + off) / div);
+                c = c < 0 ? 0 : (c > 15 ? 15 : c);
+                int j = i / 64, hi = (i % 64) / 32, l = i % 32;
+                ob[16 + 32 * j + l] |= (uint8_t)(hi ? c << 4 : c);
+            }
+        }
+    }
+}
+
+/* Q6_K layout ([minfer] block.rs sizes: 210 bytes; the rest is not on the
+ * pages, the reading is GGUF's): low 4 bits ql[128] @0, high 2 bits qh[64]
+ * @128, int8 scales[16] @192, f16 d @208.  Value i (h = i / 128, r = i % 128,
+ * k = r / 32, l = r % 32): low bits from ql[64h + l + 32 (k & 1)] (low nibble
+ * for k < 2, high nibble for k >= 2), high bits (qh[32h + l] >> 2k) & 3;
+ * q = low | high << 4 in [0, 63]; group g = i / 16; value = d * sc_g * (q - 32). */
+static int q6k_code(const uint8_t *blk, int i) {
+    int h = i / 128, r = i % 128, k = r / 32, l = r % 32;
+    uint8_t lb = blk[64 * h + l + 32 * (k & 1)];
+    int lo = (k < 2) ? (lb & 15) : (lb >> 4);
+    int hi = (blk[128 + 32 * h + l] >> (2 * k)) & 3;
+    return lo | (hi << 4);
+}
+
+/* Q6_K weights, per 256 in 16 groups of 16.  The pages give no quantizer; the
+ * rule here follows Q4_0's signed maximum (kvad "The scale that wasted a
+ * code"): per group the value of largest magnitude mx (first on ties) lands
+ * on code 0, s = mx / -32; d = max |s| / 127 (stored f16); sc = clamp(round(
+ * s / f16(d)), -128, 127); q = clamp(round(x / (f16(d) * sc)) + 32, 0, 63),
+ * 32 if the divisor is 0. */
+void orc_quantize_q6_k_w(const float *w, uint8_t *out, int64_t N, int64_t K) {
+    int64_t ns = K / QKK;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t sb = 0; sb < ns; ++sb) {
+            const float *xb = w + n * K + sb * QKK;
+            uint8_t *ob = out + (n * ns + sb) * Q6_K_BYTES;
+            float sv[16], smax = 0.0f;
+            for (int g = 0; g < 16; ++g) {
+                float amax = 0.0f, mx = 0.0f;
+                for (int i = 0; i < 16; ++i) {
+                    float a = fabsf(xb[16 * g + i]);
+                    if (a > amax) { amax = a; mx = xb[16 * g + i]; }
+                }
+                sv[g] = mx / -32.0f;
+                if (fabsf(sv[g]) > smax) smax = fabsf(sv[g]);
+            }
+            wr_f16(ob + 208, smax / 127.0f);
+            float dh = rd_f16(ob + 208);
+            int sc[16];
+            for (int g = 0; g < 16; ++g) {
+                int a = 0;
+                if (dh != 0.0f) a = (int)rne(sv[g] / dh);
+                sc[g] = a < -128 ? -128 : (a > 127 ? 127 : a);
+                ob[192 + g] = (uint8_t)(int8_t)sc[g];
+            }
+            memset(ob, 0, 192);
+            for (int i = 0; i < QKK; ++i) {
+                float div = dh * (float)sc[i / 16];
+                int c = 32;
+                if (div != 0.0f) c = (int)rne(xb[i] / div) + 32;
+                c = c < 0 ? 0 : (c > 63 ? 63 : c);
+                int h = i / 128, r = i % 128, k = r / 32, l = r % 32;
+                ob[64 * h + l + 32 * (k & 1)] |= (uint8_t)((k < 2) ? (c & 15) : ((c & 15) << 4));
+                ob[128 + 32 * h + l] |= (uint8_t)((c >> 4) << (2 * k));
+            }
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Decoders (each value exact in double)                               */
 /* ------------------------------------------------------------------ */
@@ -318,6 +471,33 @@ void orc_dequantize_q2_k(const uint8_t *blk, double *out, int64_t rows, int64_t 
                 int sc = p[g] & 0x0f, m = p[g] >> 4;
                 out[r * K + sb * QKK + i] = d * sc * q - dmin * m;
             }
+        }
+}
+
+/* Q4_K value = d * sc_s * q - dmin * m_s, s = i / 32 (layout above). */
+void orc_dequantize_q4_k(const uint8_t *blk, double *out, int64_t rows, int64_t K) {
+    int64_t ns = K / QKK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t sb = 0; sb < ns; ++sb) {
+            const uint8_t *p = blk + (r * ns + sb) * Q4_K_BYTES;
+            double d = rd_f16(p), dmin = rd_f16(p + 2);
+            for (int i = 0; i < QKK; ++i) {
+                int sc, m;
+                q4k_scale_min(p + 4, i / 32, &sc, &m);
+                out[r * K + sb * QKK + i] = d * sc * q4k_code(p, i) - dmin * m;
+            }
+        }
+}
+
+/* Q6_K value = d * sc_g * (q - 32), g = i / 16 (layout above). */
+void orc_dequantize_q6_k(const uint8_t *blk, double *out, int64_t rows, int64_t K) {
+    int64_t ns = K / QKK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t sb = 0; sb < ns; ++sb) {
+            const uint8_t *p = blk + (r * ns + sb) * Q6_K_BYTES;
+            double d = rd_f16(p + 208);
+            for (int i = 0; i < QKK; ++i)
+                out[r * K + sb * QKK + i] = d * (int8_t)p[192 + i / 16] * (q6k_code(p, i) - 32);
         }
 }
 
@@ -416,22 +596,87 @@ static void dot_q2_k_q8_k(const uint8_t *w, const uint8_t *x, int64_t ns, double
     if (mag) *mag = a;
 }
 
-enum { ORC_Q4_0 = 0, ORC_Q8_0 = 1, ORC_Q2_K = 2 };
+/* Q4_K x Q8_K, per super-block, as [minfer] "The payoff: a K-quant dot
+ * kernel, walked" writes it: the min term Mn = sum_s m_s * (bsums[2s] +
+ * bsums[2s+1]) (a sub-block of 32 is two bsum groups of 16), the value term
+ * V = sum_s sc_s * sum_{i in s} q_i * x_i, then
+ *   t = d * d8 * V - dmin * d8 * Mn. */
+static void dot_q4_k_q8_k(const uint8_t *w, const uint8_t *x, int64_t ns, double *y, double *mag) {
+    double s = 0.0, a = 0.0;
+    for (int64_t sb = 0; sb < ns; ++sb) {
+        const uint8_t *wb = w + sb * Q4_K_BYTES, *xb = x + sb * Q8_K_BYTES;
+        double d = rd_f16(wb), dmin = rd_f16(wb + 2), d8 = rd_f32(xb);
+        int64_t V = 0, Mn = 0;
+        double aa = 0.0;
+        for (int t = 0; t < 8; ++t) {
+            int sc, m;
+            q4k_scale_min(wb + 4, t, &sc, &m);
+            int32_t ts = 0;
+            for (int u = 0; u < 32; ++u) {
+                int i = 32 * t + u, q = q4k_code(wb, i), qx = (int8_t)xb[4 + i];
+                ts += q * qx;
+                aa += (fabs(d * sc * q) + fabs(dmin * m)) * fabs(d8 * qx);
+            }
+            int16_t b0, b1;
+            memcpy(&b0, xb + 260 + 2 * (2 * t), 2);
+            memcpy(&b1, xb + 260 + 2 * (2 * t + 1), 2);
+            V += (int64_t)sc * ts;
+            Mn += (int64_t)m * (b0 + b1);
+        }
+        s += d * d8 * (double)V - dmin * d8 * (double)Mn;
+        a += aa;
+    }
+    *y = s;
+    if (mag) *mag = a;
+}
+
+/* Q6_K x Q8_K, per super-block: the plain sum of decoded products (the pages
+ * give no Q6_K kernel), grouped as the format groups it:
+ *   t = d * d8 * sum_g sc_g * sum_{i in g} (q_i - 32) * x_i. */
+static void dot_q6_k_q8_k(const uint8_t *w, const uint8_t *x, int64_t ns, double *y, double *mag) {
+    double s = 0.0, a = 0.0;
+    for (int64_t sb = 0; sb < ns; ++sb) {
+        const uint8_t *wb = w + sb * Q6_K_BYTES, *xb = x + sb * Q8_K_BYTES;
+        double d = rd_f16(wb + 208), d8 = rd_f32(xb);
+        int64_t V = 0;
+        double aa = 0.0;
+        for (int g = 0; g < 16; ++g) {
+            int sc = (int8_t)wb[192 + g];
+            int32_t gs = 0;
+            for (int u = 0; u < 16; ++u) {
+                int i = 16 * g + u, q = q6k_code(wb, i) - 32, qx = (int8_t)xb[4 + i];
+                gs += q * qx;
+                aa += fabs(d * sc * q) * fabs(d8 * qx);
+            }
+            V += (int64_t)sc * gs;
+        }
+        s += d * d8 * (double)V;
+        a += aa;
+    }
+    *y = s;
+    if (mag) *mag = a;
+}
+
+enum { ORC_Q4_0 = 0, ORC_Q8_0 = 1, ORC_Q2_K = 2, ORC_Q4_K = 3, ORC_Q6_K = 4 };
 
 static void dot_any(int fmt, const uint8_t *w, const uint8_t *x, int64_t K, double *y, double *mag) {
     if (fmt == ORC_Q4_0) dot_q4_0_q8_0(w, x, K / QK, y, mag);
     else if (fmt == ORC_Q8_0) dot_q8_0_q8_0(w, x, K / QK, y, mag);
-    else dot_q2_k_q8_k(w, x, K / QKK, y, mag);
+    else if (fmt == ORC_Q2_K) dot_q2_k_q8_k(w, x, K / QKK, y, mag);
+    else if (fmt == ORC_Q4_K) dot_q4_k_q8_k(w, x, K / QKK, y, mag);
+    else dot_q6_k_q8_k(w, x, K / QKK, y, mag);
 }
 
 static int64_t w_row_bytes(int fmt, int64_t K) {
     if (fmt == ORC_Q4_0) return K / QK * Q4_0_BYTES;
     if (fmt == ORC_Q8_0) return K / QK * Q8_0_BYTES;
-    return K / QKK * Q2_K_BYTES;
+    if (fmt == ORC_Q2_K) return K / QKK * Q2_K_BYTES;
+    if (fmt == ORC_Q4_K) return K / QKK * Q4_K_BYTES;
+    return K / QKK * Q6_K_BYTES;
 }
 static int64_t x_row_bytes(int fmt, int64_t K) {
-    if (fmt == ORC_Q2_K) return K / QKK * Q8_K_BYTES;
-    return K / QK * Q8_0_BYTES;
+    if (fmt == ORC_Q4_0 || fmt == ORC_Q8_0) return K / QK * Q8_0_BYTES;
+    return K / QKK * Q8_K_BYTES;
 }
 
 /* ------------------------------------------------------------------ */
@@ -462,7 +707,8 @@ static void *orc_rows(void *arg) {
     return NULL;
 }
 
-/* fmt: 0 = Q4_0 weights x Q8_0, 1 = Q8_0 x Q8_0, 2 = Q2_K x Q8_K.
+/* fmt: 0 = Q4_0 weights x Q8_0, 1 = Q8_0 x Q8_0, 2 = Q2_K x Q8_K,
+ * 3 = Q4_K x Q8_K, 4 = Q6_K x Q8_K.
  * y (f32), y64 (double) and mag (double) are [M][N]; any may be NULL. */
 int orc_matmul(int fmt, const uint8_t *w, const uint8_t *x, float *y, double *y64, double *mag,
                int64_t M, int64_t N, int64_t K, int threads) {

@@ -199,6 +199,11 @@ def test_block_sizes(orc):
     assert orc.BLOCK_BYTES["q4_0"] == g["q4_0_bytes"]
     assert orc.BLOCK_BYTES["q8_0"] == g["q8_0_bytes"]
     assert orc.BLOCK_BYTES["q2_k"] == g["q2_k_bytes"]
+    assert orc.BLOCK_BYTES["q4_k"] == g["q4_k_bytes"]
+    assert orc.BLOCK_BYTES["q6_k"] == g["q6_k_bytes"]
+    w = synth.gaussian_f32((2, 512), 0.02, 6)
+    assert orc.quantize_q4_k_w(w).shape == (2, 2 * g["q4_k_bytes"])
+    assert orc.quantize_q6_k_w(w).shape == (2, 2 * g["q6_k_bytes"])
     assert orc.BLOCK_BYTES["q4_0"] / 32 == g["q4_0_bytes_per_weight"]
     assert orc.BLOCK_BYTES["q2_k"] * 8 / 256 == g["q2_k_bits_per_weight"]
     ex = g["row_example"]
@@ -301,6 +306,140 @@ def test_q2_k_quantizer_format_invariants(orc):
 
 
 # ---------------------------------------------------------------------------
+# Q4_K: the chunk order and the two-term dot are the pages' (minfer "The
+# payoff: a K-quant dot kernel, walked"); the 12-byte packing of the 6-bit
+# scales and mins is a reading (GGUF's), checked here only for consistency.
+# ---------------------------------------------------------------------------
+def _q4k_block(d, dmin, sc, m, qs):
+    """A Q4_K block from 8 scales, 8 mins (6 bits each) and 128 nibble bytes,
+    the scales packed as the reading says (s < 4: low 6 bits of bytes s and
+    s + 4; s >= 4: low / high nibble of byte s + 4 and the top 2 bits of bytes
+    s - 4 and s)."""
+    blk = np.zeros(144, dtype=np.uint8)
+    blk[0:2] = np.array([np.float16(d)], dtype=np.float16).view(np.uint8)
+    blk[2:4] = np.array([np.float16(dmin)], dtype=np.float16).view(np.uint8)
+    b = np.zeros(12, dtype=np.int64)
+    for s in range(4):
+        b[s] = sc[s] | (sc[s + 4] >> 4) << 6
+        b[s + 4] = m[s] | (m[s + 4] >> 4) << 6
+        b[s + 8] = (sc[s + 4] & 15) | (m[s + 4] & 15) << 4
+    blk[4:16] = b.astype(np.uint8)
+    blk[16:144] = qs
+    return blk
+
+
+@pytest.mark.parametrize("j,l,hi", [(0, 0, 0), (0, 31, 1), (1, 7, 0), (2, 16, 1), (3, 31, 0), (3, 0, 1)])
+def test_q4_k_chunk_order_is_the_pages(orc, j, l, hi):
+    """Byte l of 32-byte chunk j: its low nibble is value 64j + l, its high
+    nibble value 64j + 32 + l (the kernel's q8 offsets q8off + l and
+    q8off + 32 + l)."""
+    qs = np.zeros(128, dtype=np.uint8)
+    qs[32 * j + l] = (5 << 4) if hi else 5
+    vals = orc.dequantize("q4_k", _q4k_block(1.0, 0.0, [1] * 8, [0] * 8, qs), 256)[0]
+    nz = np.nonzero(vals)[0]
+    assert list(nz) == [64 * j + 32 * hi + l] and vals[nz[0]] == 5.0
+
+
+def test_q4_k_decode_closed_form_and_scale_packing(orc):
+    """value = d * sc_s * q - dmin * m_s with s = i / 32, for scales and mins
+    that use all six bits (so every packed bit is exercised)."""
+    rng = synth.splitmix64(131, 0, 160)
+    sc = [int(v) for v in (rng[:8] % np.uint64(64))]
+    m = [int(v) for v in (rng[8:16] % np.uint64(64))]
+    sc[4], m[7] = 63, 63
+    qs = (rng[16:144] & np.uint64(0xFF)).astype(np.uint8)
+    vals = orc.dequantize("q4_k", _q4k_block(0.5, 0.25, sc, m, qs), 256)[0]
+    for i in range(256):
+        j, hi, l = i // 64, (i % 64) // 32, i % 32
+        q = (int(qs[32 * j + l]) >> 4) if hi else (int(qs[32 * j + l]) & 15)
+        assert vals[i] == 0.5 * sc[i // 32] * q - 0.25 * m[i // 32], i
+
+
+def test_q4_k_min_term_pairs_two_bsum_groups(orc):
+    """All codes zero: the product is the min term alone, -dmin * d8 *
+    sum_s m_s * (bsums[2s] + bsums[2s+1]), which equals -dmin * sum over each
+    sub-block of its decoded activations."""
+    m = [1, 2, 3, 4, 5, 6, 7, 8]
+    wq = _q4k_block(0.0, 0.5, [0] * 8, m, np.zeros(128, dtype=np.uint8))
+    x = synth.gaussian_f32((1, 256), 1.0, 141)
+    xq = orc.quantize_q8_k(x)
+    X = orc.dequantize("q8_k", xq, 256)[0]
+    y = orc.matmul("q4_k", wq, xq, 1, 1, 256, want=("y64",))["y64"][0, 0]
+    expect = -0.5 * sum(m[s] * X[32 * s:32 * s + 32].sum() for s in range(8))
+    assert abs(y - expect) <= 1e-12 * np.abs(X).sum() * 8
+
+
+def test_q4_k_quantizer_format_invariants(orc):
+    """The Q4_K weight quantizer's rule is not on the pages (parity unpinned)."""
+    w = synth.gaussian_f32((8, 1024), 0.02, 151)
+    q = orc.quantize_q4_k_w(w)
+    vals = orc.dequantize("q4_k", q, 1024)
+    assert np.linalg.norm(vals - w) / np.linalg.norm(w) < 0.12
+    assert np.corrcoef(vals.ravel(), w.ravel())[0, 1] > 0.99
+    d = q.reshape(-1, 144)[:, 0:2].copy().view(np.float16).astype(np.float64)
+    assert np.all(d >= 0)
+
+
+# ---------------------------------------------------------------------------
+# Q6_K: the pages give the block size only; the layout is a reading (GGUF's).
+# ---------------------------------------------------------------------------
+def _q6k_block(d, scales, ql, qh):
+    blk = np.zeros(210, dtype=np.uint8)
+    blk[0:128] = ql
+    blk[128:192] = qh
+    blk[192:208] = np.asarray(scales, dtype=np.int8).view(np.uint8)
+    blk[208:210] = np.array([np.float16(d)], dtype=np.float16).view(np.uint8)
+    return blk
+
+
+@pytest.mark.parametrize("i", [0, 17, 40, 70, 100, 127, 128, 161, 200, 255])
+def test_q6_k_layout_reading(orc, i):
+    """Value i's six bits: low four in ql[64h + l + 32 (k & 1)] (low nibble for
+    k < 2, high for k >= 2), high two at bit 2k of qh[32h + l], with h = i / 128,
+    k = (i % 128) / 32, l = i % 32; the code 32 decodes to zero."""
+    h, k, l = i // 128, (i % 128) // 32, i % 32
+    ql = np.zeros(128, dtype=np.uint8)
+    qh = np.zeros(64, dtype=np.uint8)
+    # every value at code 32 (= 0 after the offset) except value i at code 45
+    for v in range(256):
+        hv, kv, lv = v // 128, (v % 128) // 32, v % 32
+        c = 45 if v == i else 32
+        ql[64 * hv + lv + 32 * (kv & 1)] |= (c & 15) << (4 if kv >= 2 else 0)
+        qh[32 * hv + lv] |= (c >> 4) << (2 * kv)
+    vals = orc.dequantize("q6_k", _q6k_block(1.0, [1] * 16, ql, qh), 256)[0]
+    nz = np.nonzero(vals)[0]
+    assert list(nz) == [i] and vals[i] == 13.0
+
+
+def test_q6_k_decode_closed_form(orc):
+    """value = d * sc_g * (q - 32), g = i / 16, signed int8 scales."""
+    rng = synth.splitmix64(161, 0, 208)
+    ql = (rng[:128] & np.uint64(0xFF)).astype(np.uint8)
+    qh = (rng[128:192] & np.uint64(0xFF)).astype(np.uint8)
+    sc = ((rng[192:208] % np.uint64(256)).astype(np.int64) - 128).astype(np.int8)
+    vals = orc.dequantize("q6_k", _q6k_block(0.25, sc, ql, qh), 256)[0]
+    for i in range(256):
+        h, k, l = i // 128, (i % 128) // 32, i % 32
+        lb = int(ql[64 * h + l + 32 * (k & 1)])
+        q = ((lb & 15) if k < 2 else (lb >> 4)) | (((int(qh[32 * h + l]) >> (2 * k)) & 3) << 4)
+        assert vals[i] == 0.25 * int(sc[i // 16]) * (q - 32), i
+
+
+def test_q6_k_quantizer_format_invariants(orc):
+    """The Q6_K weight quantizer's rule is not on the pages (parity unpinned)."""
+    w = synth.gaussian_f32((8, 1024), 0.02, 171)
+    q = orc.quantize_q6_k_w(w)
+    vals = orc.dequantize("q6_k", q, 1024)
+    assert np.linalg.norm(vals - w) / np.linalg.norm(w) < 0.03
+    # a group's largest magnitude lands near code 0 (value -32 * d * sc)
+    wg = w.reshape(-1, 16)
+    vg = vals.reshape(-1, 16)
+    first = np.argmax(np.abs(wg), axis=1)
+    rows = np.arange(wg.shape[0])
+    assert np.all(np.abs(vg[rows, first] - wg[rows, first]) <= 0.05 * np.abs(wg[rows, first]))
+
+
+# ---------------------------------------------------------------------------
 # Products: brute force on decoded values, layout, thread invariance
 # ---------------------------------------------------------------------------
 def _case(fmt, M, N, K, seed):
@@ -320,25 +459,26 @@ def test_single_block_dot_is_exact(orc, fmt):
     assert np.array_equal(r["y64"][0], brute)
 
 
-@pytest.mark.parametrize("fmt,K", [("q4_0", 96), ("q8_0", 160), ("q2_k", 512), ("q4_0", 4096)])
+@pytest.mark.parametrize("fmt,K", [("q4_0", 96), ("q8_0", 160), ("q2_k", 512), ("q4_0", 4096), ("q4_k", 512),
+                                   ("q6_k", 768)])
 def test_matmul_matches_decoded_float64_product(orc, fmt, K):
     M, N = 3, 5
     wq, xq = _case(fmt, M, N, K, 101)
     r = orc.matmul(fmt, wq, xq, M, N, K, want=("y", "y64", "mag"))
     W = orc.dequantize(fmt, wq, K)
-    X = orc.dequantize("q8_k" if fmt == "q2_k" else "q8_0", xq, K)
+    X = orc.dequantize(orc.act_format(fmt), xq, K)
     ref = X @ W.T                                       # [M][N]: token-major output
     assert r["y64"].shape == (M, N)
     assert np.all(np.abs(r["y64"] - ref) <= 1e-12 * r["mag"])
     assert np.array_equal(r["y"], r["y64"].astype(np.float32))
     absprod = np.abs(X) @ np.abs(W).T
-    if fmt == "q2_k":
+    if fmt in ("q2_k", "q4_k"):                       # |d sc q| + |dmin m| >= |d sc q - dmin m|
         assert np.all(r["mag"] >= absprod * (1 - 1e-12))
     else:
         assert np.all(np.abs(r["mag"] - absprod) <= 1e-12 * absprod)
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q2_k"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q2_k", "q4_k", "q6_k"])
 def test_matmul_rows_equal_matvec_and_threads_invariant(orc, fmt):
     M, N, K = 4, 37, 512
     wq, xq = _case(fmt, M, N, K, 111)

@@ -12,7 +12,9 @@ in HBM; the timed steps are replayed from a captured HIP graph (launching
 kernels of a few microseconds from Python would measure the interpreter, not
 the GPU).
 
-Also in the line: the prefill matmul (M = 2048, same weights), int8 TOP/s;
+Also in the line: the other decode workloads (the Q8_0 matrices of one
+7B-style layer, Q2_K, Q4_K and Q6_K at 12288x4096), kernel time and GB/s
+each; the prefill matmul (M = 2048, same weights), int8 TOP/s;
 for each, the dominant kernel's roofline (achieved / MI355X peak, with the
 average kernel time from HIP events on the launch stream around graph
 replays of batches of back-to-back launches of that kernel) and the oracle timed on the host cores
@@ -51,7 +53,7 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=30,
                     help="untimed prefill steps (~10 ms: lets the clock settle under the MFMA load)")
-    ap.add_argument("--only", choices=["all", "decode", "prefill"], default="all")
+    ap.add_argument("--only", choices=["all", "decode", "prefill", "configs"], default="all")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of each oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies-mb", type=float, default=600.0, help="total size of the rotated weight copies")
@@ -234,6 +236,57 @@ def bench_prefill(args, torch, q, synth):
                           "kernel_us_best_batch": round(mm_min * 1e3, 2), "algorithmic_ops": ops})
 
 
+# The other decode workloads, one matvec launch each, weights rotated like the
+# headline's: the Q8_0 set of one 7B-style layer (fused QKV and gate+up share
+# the 4096-wide activation, down takes an independent 11008-wide one), Q2_K,
+# and the K-quants of q4_K_M files.  (format, N, K, workload id, weight
+# stream, activation stream, name); the ids seed the synthetic inputs.
+MATVEC_CONFIGS = [
+    ("q8_0", 12288, 4096, 2, 0, 1, "q8_0_qkv_12288x4096"),
+    ("q8_0", 22016, 4096, 2, 3, 1, "q8_0_gate_up_22016x4096"),
+    ("q8_0", 4096, 11008, 2, 4, 5, "q8_0_down_4096x11008"),
+    ("q2_k", 12288, 4096, 3, 0, 1, "q2_k_12288x4096"),
+    ("q4_k", 12288, 4096, 5, 0, 1, "q4_k_12288x4096"),
+    ("q6_k", 12288, 4096, 6, 0, 1, "q6_k_12288x4096"),
+]
+
+
+def bench_matvec_configs(args, torch, q, synth):
+    """Kernel time and weight-stream GB/s of each matvec workload above."""
+    rows = []
+    for fmt, N, K, cfg, wstream, xstream, name in MATVEC_CONFIGS:
+        wbytes = N * q.row_bytes(fmt, K)
+        w = torch.from_numpy(synth.weights(N, K, config=cfg, stream=wstream)).cuda()
+        wq0 = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
+        q.QUANTIZE_W[fmt](w, wq0, N, K)
+        del w
+        copies = max(2, int(args.copies_mb * 1e6 // wbytes) + 1)
+        wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+        x = torch.from_numpy(synth.activations(1, K, config=cfg, stream=xstream)).cuda()
+        act = q.ACT_FORMAT[fmt]
+        xq = torch.empty(q.row_bytes(act, K), dtype=torch.uint8, device="cuda")
+        q.QUANTIZE_X[fmt](x, xq, 1, K)
+        y = torch.empty(N, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        mv = q.MATVEC[fmt]
+        ms, ms_min, _ = time_batches(torch, lambda i: mv(wqs[i % copies], xq, y, N, K), args.steps, copies)
+        gbs = wbytes / (ms * 1e-3) / 1e9
+        log(f"matvec {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM) over "
+            f"{copies} weight copies")
+        rows.append({"workload": name, "format": fmt, "N": N, "K": K, "weight_bytes": wbytes,
+                     "kernel_us_mean": round(ms * 1e3, 3), "kernel_us_best_batch": round(ms_min * 1e3, 3),
+                     "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        del wqs, wq0
+        torch.cuda.empty_cache()
+    layer = [r for r in rows if r["workload"].startswith("q8_0_")]
+    tot_b = sum(r["weight_bytes"] for r in layer)
+    tot_us = sum(r["kernel_us_mean"] for r in layer)
+    return {"unit": "GB/s", "bound": "hbm", "peak": HBM_PEAK_GBS, "rows": rows,
+            "q8_0_layer_sum": {"weight_bytes": tot_b, "kernel_us": round(tot_us, 3),
+                               "achieved_gbs": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
+                               "hbm_frac": round(tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_threads():
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     return max(1, min(n, 16))
@@ -307,6 +360,7 @@ def main():
 
     dec = bench_decode(args, torch, q, synth) if args.only in ("all", "decode") else None
     pre = bench_prefill(args, torch, q, synth) if args.only in ("all", "prefill") else None
+    cfgs = bench_matvec_configs(args, torch, q, synth) if args.only in ("all", "configs") else None
 
     cpu_dec = cpu_pre = None
     if not args.no_cpu_baseline:
@@ -340,6 +394,8 @@ def main():
                         "roofline": pf["roofline"], "cpu_baseline": cpu_pre})
         else:
             out["prefill"] = pf
+    if cfgs is not None:
+        out["matvec_configs"] = cfgs
     print(json.dumps(out), flush=True)
 
 

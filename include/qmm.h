@@ -21,6 +21,23 @@
  *                            code of value 128h+32s+l (h<2, s<4, l<32).
  *   Q8_K 292 B / 256 values: f32 d @0, int8 q[256] @4, int16 bsums[16] @260
  *                            (bsums[g] = sum of codes 16g..16g+15).
+ *   Q4_K 144 B / 256 values: f16 d @0, f16 dmin @2, 12 B of 6-bit scales and
+ *                            mins @4, uint8 qs[128] @16; byte l of 32-byte
+ *                            chunk j holds value 64j+l (low nibble) and
+ *                            64j+32+l (high nibble); sub-block s = i/32 has
+ *                            scale sc_s and min m_s: for s < 4 sc = b[s] & 63,
+ *                            m = b[s+4] & 63; for s >= 4 sc = (b[s+4] & 15) |
+ *                            (b[s-4] >> 6) << 4, m = (b[s+4] >> 4) |
+ *                            (b[s] >> 6) << 4 (b = the 12 bytes).
+ *                                                  value = d*sc_s*q - dmin*m_s
+ *   Q6_K 210 B / 256 values: ql[128] @0 (low 4 bits), qh[64] @128 (high 2
+ *                            bits), int8 scales[16] @192, f16 d @208; value
+ *                            i (h = i/128, k = (i%128)/32, l = i%32): low bits
+ *                            in ql[64h + l + 32(k&1)] (low nibble for k < 2,
+ *                            high for k >= 2), high bits at bit 2k of
+ *                            qh[32h + l].        value = d*scales[i/16]*(q-32)
+ *   (The Q4_K scale packing and the Q6_K layout are GGUF's; the pages give
+ *   the block sizes, Q4_K's field and chunk order and its two-term dot.)
  * A matrix of R rows and K columns in format F is R*K/blk(F) blocks, row-major
  * (row r starts at byte r*(K/blk)*bytes(F)), with no padding.
  *
@@ -39,7 +56,7 @@
  *     never into another page); those bytes do not affect any result.
  *   - Calls are thread-safe.  No entry point aborts the process.
  *   - Sizes: M, N >= 1, K >= one block, K a multiple of the block length of
- *     the format (32, or 256 for Q8_K / Q2_K), every dimension < 2^31 and every
+ *     the format (32, or 256 for Q8_K and the K-quants), every dimension < 2^31 and every
  *     buffer < 2^40 bytes; QMM_E_SHAPE otherwise.
  */
 #ifndef QMM_H
@@ -102,6 +119,19 @@ qmm_status qmm_quantize_q4_0(const float *w, void *wq, int64_t N, int64_t K, voi
  *   w : f32 [N][K].   wq : Q2_K [N][K/256] blocks (84 B). */
 qmm_status qmm_quantize_q2_k(const float *w, void *wq, int64_t N, int64_t K, void *stream);
 
+/* Q4_K and Q6_K quantization of N rows of K f32 weights, K % 256 == 0 (test
+ * and benchmark data; the pages give no quantizer).  Q4_K: Q2_K's rule with
+ * 15 levels, s = (hi-lo)/15, and 6-bit sc, m: d = max s / 63, dmin = max mn /
+ * 63, sc = clamp(rne(s/d), 0, 63), m = clamp(rne(mn/dmin), 0, 63),
+ * q = clamp(rne((x + dmin*m)/(d*sc)), 0, 15), per sub-block of 32.  Q6_K, per
+ * group of 16: the value of largest magnitude (first on ties) mx gives
+ * s = mx / -32; d = max |s| / 127; sc = clamp(rne(s/d), -128, 127);
+ * q = clamp(rne(x/(d*sc)) + 32, 0, 63), 32 for a zero divisor.  d, dmin are
+ * the stored f16 values in every step after they are stored.
+ *   w : f32 [N][K].   wq : Q4_K (144 B) / Q6_K (210 B) blocks, N*K/256 of them. */
+qmm_status qmm_quantize_q4_k(const float *w, void *wq, int64_t N, int64_t K, void *stream);
+qmm_status qmm_quantize_q6_k(const float *w, void *wq, int64_t N, int64_t K, void *stream);
+
 /* ---- products ----------------------------------------------------------------
  * y[t][n] = sum over blocks b of d_w[n,b] * d_x[t,b] * I_b[t,n], where I_b is
  * the exact int32 dot product of the block's codes (minfer mm_rows and the
@@ -111,7 +141,11 @@ qmm_status qmm_quantize_q2_k(const float *w, void *wq, int64_t N, int64_t K, voi
  * output (krafla "Numerics").  Output is token-major [M][N] f32 (minfer
  * "Pitfalls": out[t*od + o]).
  * Pairing (minfer "Two activation formats, one pairing rule"): Q4_0 and Q8_0
- * weights take Q8_0 activations; Q2_K weights take Q8_K activations. */
+ * weights take Q8_0 activations; the K-quants (Q2_K, Q4_K, Q6_K) take Q8_K
+ * activations.  K-quant dots (minfer "The payoff: a K-quant dot kernel,
+ * walked"): per super-block d*d8*sum_s sc_s*sum q x, minus dmin*d8*sum_s m_s *
+ * (the bsums of s) for the formats with mins; Q6_K: d*d8*sum_g sc_g *
+ * sum (q-32) x. */
 
 /* Decode matvec, one token (M = 1).
  *   w  : N rows of K/32 weight blocks.   xq : one row of Q8_0 (or Q8_K) blocks.
@@ -119,6 +153,8 @@ qmm_status qmm_quantize_q2_k(const float *w, void *wq, int64_t N, int64_t K, voi
 qmm_status qmm_matvec_q8_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
 qmm_status qmm_matvec_q4_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
 qmm_status qmm_matvec_q2_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream);
+qmm_status qmm_matvec_q4_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream);
+qmm_status qmm_matvec_q6_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream);
 
 /* Decode matvec with the activation quantization fused into the same launch
  * (minfer section 3.3, "Design choices", on sibling products sharing one
@@ -150,6 +186,10 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
 qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
 qmm_status qmm_matmul_q2_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream);
+qmm_status qmm_matmul_q4_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream);
+qmm_status qmm_matmul_q6_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
 
 #ifdef __cplusplus

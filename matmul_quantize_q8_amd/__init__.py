@@ -19,9 +19,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmm.so")
 
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q2_k": 84, "q8_k": 292}
-BLOCK_VALUES = {"q4_0": 32, "q8_0": 32, "q2_k": 256, "q8_k": 256}
-ACT_FORMAT = {"q4_0": "q8_0", "q8_0": "q8_0", "q2_k": "q8_k"}
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q2_k": 84, "q8_k": 292, "q4_k": 144, "q6_k": 210}
+BLOCK_VALUES = {"q4_0": 32, "q8_0": 32, "q2_k": 256, "q8_k": 256, "q4_k": 256, "q6_k": 256}
+ACT_FORMAT = {"q4_0": "q8_0", "q8_0": "q8_0", "q2_k": "q8_k", "q4_k": "q8_k", "q6_k": "q8_k"}
 
 STATUS = {0: "QMM_OK", 1: "QMM_E_SHAPE", 2: "QMM_E_NULL", 3: "QMM_E_ALIGN", 4: "QMM_E_DEVICE", 5: "QMM_E_LAUNCH"}
 
@@ -51,16 +51,18 @@ def lib() -> ctypes.CDLL:
         L.qmm_status_string.restype = ctypes.c_char_p
         L.qmm_abi_version.argtypes = []
         L.qmm_abi_version.restype = ctypes.c_int
-        for name in ("qmm_quantize_q8_0", "qmm_quantize_q8_k", "qmm_quantize_q4_0", "qmm_quantize_q2_k"):
+        for name in ("qmm_quantize_q8_0", "qmm_quantize_q8_k", "qmm_quantize_q4_0", "qmm_quantize_q2_k",
+                     "qmm_quantize_q4_k", "qmm_quantize_q6_k"):
             getattr(L, name).argtypes = [P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
-        for name in ("qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k"):
+        for name in ("qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k", "qmm_matvec_q4_k",
+                     "qmm_matvec_q6_k"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
         for name in ("qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0"):
             getattr(L, name).argtypes = [P, P, P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
-        for name in ("qmm_matmul_q4_0", "qmm_matmul_q2_k"):
+        for name in ("qmm_matmul_q4_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -69,9 +71,10 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("qmm_status_string", "qmm_abi_version",
            "qmm_quantize_q8_0", "qmm_quantize_q8_k", "qmm_quantize_q4_0", "qmm_quantize_q2_k",
-           "qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k",
+           "qmm_quantize_q4_k", "qmm_quantize_q6_k",
+           "qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k", "qmm_matvec_q4_k", "qmm_matvec_q6_k",
            "qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0",
-           "qmm_matmul_q4_0", "qmm_matmul_q2_k")
+           "qmm_matmul_q4_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k")
 
 
 def row_bytes(fmt: str, K: int) -> int:
@@ -127,6 +130,16 @@ def qmm_quantize_q2_k(w, wq, N: int, K: int, stream=None) -> None:
     _call("qmm_quantize_q2_k", _addr(w), _addr(wq), N, K, _stream(stream))
 
 
+def qmm_quantize_q4_k(w, wq, N: int, K: int, stream=None) -> None:
+    """f32 weights [N][K] -> Q4_K blocks."""
+    _call("qmm_quantize_q4_k", _addr(w), _addr(wq), N, K, _stream(stream))
+
+
+def qmm_quantize_q6_k(w, wq, N: int, K: int, stream=None) -> None:
+    """f32 weights [N][K] -> Q6_K blocks."""
+    _call("qmm_quantize_q6_k", _addr(w), _addr(wq), N, K, _stream(stream))
+
+
 # -- products -------------------------------------------------------------------
 def qmm_matvec_q8_0(w, xq, y, N: int, K: int, stream=None) -> None:
     _call("qmm_matvec_q8_0", _addr(w), _addr(xq), _addr(y), N, K, _stream(stream))
@@ -138,6 +151,14 @@ def qmm_matvec_q4_0(w, xq, y, N: int, K: int, stream=None) -> None:
 
 def qmm_matvec_q2_k(w, xq8k, y, N: int, K: int, stream=None) -> None:
     _call("qmm_matvec_q2_k", _addr(w), _addr(xq8k), _addr(y), N, K, _stream(stream))
+
+
+def qmm_matvec_q4_k(w, xq8k, y, N: int, K: int, stream=None) -> None:
+    _call("qmm_matvec_q4_k", _addr(w), _addr(xq8k), _addr(y), N, K, _stream(stream))
+
+
+def qmm_matvec_q6_k(w, xq8k, y, N: int, K: int, stream=None) -> None:
+    _call("qmm_matvec_q6_k", _addr(w), _addr(xq8k), _addr(y), N, K, _stream(stream))
 
 
 def qmm_quantize_matvec_q4_0(w, x, xq, y, N: int, K: int, stream=None) -> None:
@@ -159,8 +180,19 @@ def qmm_matmul_q2_k(w, xq8k, y, M: int, N: int, K: int, stream=None) -> None:
     _call("qmm_matmul_q2_k", _addr(w), _addr(xq8k), _addr(y), M, N, K, _stream(stream))
 
 
-QUANTIZE_W = {"q4_0": qmm_quantize_q4_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_quantize_q2_k}
-QUANTIZE_X = {"q4_0": qmm_quantize_q8_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_quantize_q8_k}
-MATVEC = {"q4_0": qmm_matvec_q4_0, "q8_0": qmm_matvec_q8_0, "q2_k": qmm_matvec_q2_k}
-MATMUL = {"q4_0": qmm_matmul_q4_0, "q2_k": qmm_matmul_q2_k}
+def qmm_matmul_q4_k(w, xq8k, y, M: int, N: int, K: int, stream=None) -> None:
+    _call("qmm_matmul_q4_k", _addr(w), _addr(xq8k), _addr(y), M, N, K, _stream(stream))
+
+
+def qmm_matmul_q6_k(w, xq8k, y, M: int, N: int, K: int, stream=None) -> None:
+    _call("qmm_matmul_q6_k", _addr(w), _addr(xq8k), _addr(y), M, N, K, _stream(stream))
+
+
+QUANTIZE_W = {"q4_0": qmm_quantize_q4_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_quantize_q2_k,
+              "q4_k": qmm_quantize_q4_k, "q6_k": qmm_quantize_q6_k}
+QUANTIZE_X = {"q4_0": qmm_quantize_q8_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_quantize_q8_k,
+              "q4_k": qmm_quantize_q8_k, "q6_k": qmm_quantize_q8_k}
+MATVEC = {"q4_0": qmm_matvec_q4_0, "q8_0": qmm_matvec_q8_0, "q2_k": qmm_matvec_q2_k, "q4_k": qmm_matvec_q4_k,
+          "q6_k": qmm_matvec_q6_k}
+MATMUL = {"q4_0": qmm_matmul_q4_0, "q2_k": qmm_matmul_q2_k, "q4_k": qmm_matmul_q4_k, "q6_k": qmm_matmul_q6_k}
 QUANTIZE_MATVEC = {"q4_0": qmm_quantize_matvec_q4_0, "q8_0": qmm_quantize_matvec_q8_0}

@@ -11,9 +11,13 @@ hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipS
 hipError_t launch_quantize_q8_k(const float *x, void *out, int64_t nblocks, hipStream_t st);
 hipError_t launch_quantize_q4_0(const float *w, void *out, int64_t nblocks, hipStream_t st);
 hipError_t launch_quantize_q2_k(const float *w, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_quantize_q4_k(const float *w, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_quantize_q6_k(const float *w, void *out, int64_t nblocks, hipStream_t st);
 hipError_t launch_matvec_q4_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st);
 hipError_t launch_matvec_q8_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st);
 hipError_t launch_matvec_q2_k(const void *w, const void *xq, float *y, int N, int ns, hipStream_t st);
+hipError_t launch_matvec_q4_k(const void *w, const void *xq, float *y, int N, int ns, hipStream_t st);
+hipError_t launch_matvec_q6_k(const void *w, const void *xq, float *y, int N, int ns, hipStream_t st);
 hipError_t launch_quantize_matvec_q4_0(const void *w, const float *x, void *xq, float *y, int N, int nb,
                                        hipStream_t st);
 hipError_t launch_quantize_matvec_q8_0(const void *w, const float *x, void *xq, float *y, int N, int nb,
@@ -21,6 +25,8 @@ hipError_t launch_quantize_matvec_q8_0(const void *w, const float *x, void *xq, 
 hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st);
 int64_t matmul_q4_0_max_blocks();
 hipError_t launch_matmul_q2_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
+hipError_t launch_matmul_q4_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
+hipError_t launch_matmul_q6_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
 }  // namespace qmm
 
 namespace {
@@ -121,6 +127,14 @@ qmm_status qmm_quantize_q2_k(const float *w, void *wq, int64_t N, int64_t K, voi
     return quantize(qmm::launch_quantize_q2_k, w, wq, N, K, 256, 1024, qmm::kQ2KBytes, stream);
 }
 
+qmm_status qmm_quantize_q4_k(const float *w, void *wq, int64_t N, int64_t K, void *stream) {
+    return quantize(qmm::launch_quantize_q4_k, w, wq, N, K, 256, 1024, qmm::kQ4KBytes, stream);
+}
+
+qmm_status qmm_quantize_q6_k(const float *w, void *wq, int64_t N, int64_t K, void *stream) {
+    return quantize(qmm::launch_quantize_q6_k, w, wq, N, K, 256, 1024, qmm::kQ6KBytes, stream);
+}
+
 typedef hipError_t (*mv_launch)(const void *, const void *, float *, int, int, hipStream_t);
 
 static qmm_status matvec(mv_launch fn, const void *w, const void *xq, float *y, int64_t N, int64_t K, int64_t blk,
@@ -145,6 +159,14 @@ qmm_status qmm_matvec_q4_0(const void *w, const void *xq, float *y, int64_t N, i
 
 qmm_status qmm_matvec_q2_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream) {
     return matvec(qmm::launch_matvec_q2_k, w, xq8k, y, N, K, 256, qmm::kQ2KBytes, qmm::kQ8KBytes, stream);
+}
+
+qmm_status qmm_matvec_q4_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream) {
+    return matvec(qmm::launch_matvec_q4_k, w, xq8k, y, N, K, 256, qmm::kQ4KBytes, qmm::kQ8KBytes, stream);
+}
+
+qmm_status qmm_matvec_q6_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream) {
+    return matvec(qmm::launch_matvec_q6_k, w, xq8k, y, N, K, 256, qmm::kQ6KBytes, qmm::kQ8KBytes, stream);
 }
 
 typedef hipError_t (*qmv_launch)(const void *, const float *, void *, float *, int, int, hipStream_t);
@@ -195,6 +217,16 @@ qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, i
 qmm_status qmm_matmul_q2_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream) {
     return matmul(qmm::launch_matmul_q2_k, w, xq8k, y, M, N, K, 256, qmm::kQ2KBytes, qmm::kQ8KBytes, stream);
+}
+
+qmm_status qmm_matmul_q4_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream) {
+    return matmul(qmm::launch_matmul_q4_k, w, xq8k, y, M, N, K, 256, qmm::kQ4KBytes, qmm::kQ8KBytes, stream);
+}
+
+qmm_status qmm_matmul_q6_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream) {
+    return matmul(qmm::launch_matmul_q6_k, w, xq8k, y, M, N, K, 256, qmm::kQ6KBytes, qmm::kQ8KBytes, stream);
 }
 
 }  // extern "C"

@@ -41,33 +41,34 @@ namespace qmm {
 
 hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipStream_t st);
 
-enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2 };
+enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4 };
+// K-quant weights (256-value super-blocks) pair with Q8_K activations, the
+// 32-value formats with Q8_0 (minfer "Two activation formats, one pairing rule").
+template <int F> constexpr bool kIsK = F >= F_Q2_K;
 
 template <int F> struct FmtBytes;
 template <> struct FmtBytes<F_Q4_0> { static constexpr int BB = kQ40Bytes, XB = kQ80Bytes; };
 template <> struct FmtBytes<F_Q8_0> { static constexpr int BB = kQ80Bytes, XB = kQ80Bytes; };
 template <> struct FmtBytes<F_Q2_K> { static constexpr int BB = kQ2KBytes, XB = kQ8KBytes; };
+template <> struct FmtBytes<F_Q4_K> { static constexpr int BB = kQ4KBytes, XB = kQ8KBytes; };
+template <> struct FmtBytes<F_Q6_K> { static constexpr int BB = kQ6KBytes, XB = kQ8KBytes; };
 
 // A unit is what one lane handles per row: P blocks (P = 2 paired, 1 single)
-// of Q4_0 / Q8_0, or a quarter of a Q2_K super-block.
+// of Q4_0 / Q8_0, or a quarter (64 values) of a K-quant super-block.
 template <int F, bool PAIRED> struct Unit {
-    static constexpr int BPU = PAIRED ? 2 : 1;        // blocks per unit
-    static constexpr int UPB = 1;                     // units per block
-};
-template <bool PAIRED> struct Unit<F_Q2_K, PAIRED> {
-    static constexpr int BPU = 1;
-    static constexpr int UPB = 4;
+    static constexpr int BPU = kIsK<F> ? 1 : (PAIRED ? 2 : 1);   // blocks per unit
+    static constexpr int UPB = kIsK<F> ? 4 : 1;                  // units per block
 };
 
 // Activation registers of one unit.
-template <int F, bool PAIRED> struct XU {
+template <int F, bool PAIRED, bool K = kIsK<F>> struct XU {
     int q[8 * Unit<F, PAIRED>::BPU];
     float d[Unit<F, PAIRED>::BPU];
     int sx8[Unit<F, PAIRED>::BPU];                    // 8 * sum of codes (Q4_0 only)
 };
-template <bool PAIRED> struct XU<F_Q2_K, PAIRED> {
-    int q[16];
-    int bs[4];
+template <int F, bool PAIRED> struct XU<F, PAIRED, true> {
+    int q[16];                                        // the unit's 64 Q8_K codes
+    int bs[4];                                        // the bsums of its four groups of 16
     float d;
 };
 
@@ -86,34 +87,45 @@ __device__ __forceinline__ void lds_q8_0_block(const uint8_t *l8, uint32_t o, in
 
 template <int F, bool PAIRED>
 __device__ __forceinline__ void load_xu(const uint8_t *xl, uint32_t xoff, int u, XU<F, PAIRED> &x) {
-    constexpr int P = Unit<F, PAIRED>::BPU;
+    if constexpr (!kIsK<F>) {
+        constexpr int P = Unit<F, PAIRED>::BPU;
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-        lds_q8_0_block(xl, xoff + (uint32_t)(P * u + j) * kQ80Bytes, x.q + 8 * j, x.d[j]);
-        int s = 0;
+        for (int j = 0; j < P; ++j) {
+            lds_q8_0_block(xl, xoff + (uint32_t)(P * u + j) * kQ80Bytes, x.q + 8 * j, x.d[j]);
+            int s = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) s = dot4(x.q[8 * j + k], 0x01010101, s);
-        x.sx8[j] = 8 * s;            // sum_j (n_j - 8) q_j = sum_j n_j q_j - 8 sum_j q_j
+            for (int k = 0; k < 8; ++k) s = dot4(x.q[8 * j + k], 0x01010101, s);
+            x.sx8[j] = 8 * s;        // sum_j (n_j - 8) q_j = sum_j n_j q_j - 8 sum_j q_j
+        }
+    } else {
+        // Q8_K unit u = (super-block c, part p); Q8_K blocks are 4-byte aligned.
+        const int c = u >> 2, p = u & 3;
+        const uint8_t *b = xl + xoff + (uint32_t)c * kQ8KBytes;
+        if constexpr (F == F_Q4_K) {
+            // part p = chunk j: values 64j + [0, 64), groups 4j .. 4j+3
+            const uint32_t *q32 = reinterpret_cast<const uint32_t *>(b + 4 + 64 * p);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) x.q[k] = (int)q32[k];
+            const uint32_t *bs32 = reinterpret_cast<const uint32_t *>(b + 260 + 8 * p);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x.bs[k] = (int)(int16_t)(bs32[k >> 1] >> (16 * (k & 1)));
+        } else {
+            // Q2_K: part p covers weight qs bytes [16p, 16p+16), i.e. values
+            // 128h + 32s + 16(p&1) + [0,16), s < 4, h = p/2 (groups 8h + 2s + (p&1)).
+            // Q6_K: part p = (h, g2) covers values 128h + 32k + 16 g2 + [0,16),
+            // k < 4 (groups 8h + 2k + g2) -- the same sets of values.
+            const int h = p >> 1, odd = p & 1;
+            const uint32_t *q32 = reinterpret_cast<const uint32_t *>(b + 4 + 128 * h + 16 * odd);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) x.q[4 * s + k] = (int)q32[8 * s + k];
+            const uint32_t *bs32 = reinterpret_cast<const uint32_t *>(b + 260 + 16 * h);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) x.bs[s] = (int)(int16_t)(bs32[s] >> (16 * odd));
+        }
+        x.d = *reinterpret_cast<const float *>(b);
     }
-}
-
-// Q8_K unit u = (super-block c, part p): part p covers qs bytes [16p, 16p+16) of
-// the weight block, i.e. values 128h + 32s + 16(p&1) + [0,16), s < 4, h = p/2,
-// which are groups g = 8h + 2s + (p&1).  Q8_K blocks are 4-byte aligned.
-template <>
-__device__ __forceinline__ void load_xu<F_Q2_K, false>(const uint8_t *xl, uint32_t xoff, int u,
-                                                       XU<F_Q2_K, false> &x) {
-    const int c = u >> 2, p = u & 3, h = p >> 1, odd = p & 1;
-    const uint8_t *b = xl + xoff + (uint32_t)c * kQ8KBytes;
-    const uint32_t *q32 = reinterpret_cast<const uint32_t *>(b + 4 + 128 * h + 16 * odd);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x.q[4 * s + k] = (int)q32[8 * s + k];
-    const uint32_t *bs32 = reinterpret_cast<const uint32_t *>(b + 260 + 16 * h);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) x.bs[s] = (int)(int16_t)(bs32[s] >> (16 * odd));
-    x.d = *reinterpret_cast<const float *>(b);
 }
 
 // Fused-variant activation layout in LDS: unit u at (32*P + 16)*u bytes holds
@@ -251,6 +263,95 @@ __device__ __forceinline__ float unit_dot<F_Q2_K, false>(const uint8_t *sl, uint
     return fmaf(-(dmin * x.d), (float)Mn, acc);
 }
 
+// Q4_K chunk j = u & 3 of the super-block at a 16-byte aligned offset (minfer
+// "The payoff: a K-quant dot kernel, walked"): low nibbles of the chunk's 32
+// bytes are sub-block 2j, high nibbles sub-block 2j+1;
+//   V = sc_2j * sum_lo + sc_2j+1 * sum_hi,
+//   Mn = m_2j * (bsum_4j + bsum_4j+1) + m_2j+1 * (bsum_4j+2 + bsum_4j+3),
+//   t = d d8 V - dmin d8 Mn.
+// The 6-bit scales and mins of sub-block s sit in bytes A = s & 3, B = A + 4,
+// C = A + 8 of the 12-byte field: s < 4: sc = A & 63, m = B & 63; s >= 4:
+// sc = (C & 15) | (A >> 6) << 4, m = (C >> 4) | (B >> 6) << 4.
+__device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int s, int &sc, int &m) {
+    const uint32_t sh = 8u * (uint32_t)(s & 3);
+    const uint32_t A = (s0 >> sh) & 0xffu, B = (s1 >> sh) & 0xffu, C = (s2 >> sh) & 0xffu;
+    if (s < 4) {
+        sc = (int)(A & 63u);
+        m = (int)(B & 63u);
+    } else {
+        sc = (int)((C & 15u) | ((A >> 6) << 4));
+        m = (int)((C >> 4) | ((B >> 6) << 4));
+    }
+}
+
+template <>
+__device__ __forceinline__ float unit_dot<F_Q4_K, false>(const uint8_t *sl, uint32_t bo, int u,
+                                                         const XU<F_Q4_K, false> &x, float acc) {
+    const int j = u & 3;
+    const uint32_t *b32 = reinterpret_cast<const uint32_t *>(sl + bo);
+    const uint32_t dd = b32[0], s0 = b32[1], s1 = b32[2], s2 = b32[3];
+    int lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t q = b32[4 + 8 * j + k];
+        lo = dot4((int)(q & 0x0f0f0f0fu), x.q[k], lo);
+        hi = dot4((int)((q >> 4) & 0x0f0f0f0fu), x.q[8 + k], hi);
+    }
+    int sc0, m0, sc1, m1;
+    q4k_scale_min(s0, s1, s2, 2 * j, sc0, m0);
+    q4k_scale_min(s0, s1, s2, 2 * j + 1, sc1, m1);
+    const int V = sc0 * lo + sc1 * hi;
+    const int Mn = m0 * (x.bs[0] + x.bs[1]) + m1 * (x.bs[2] + x.bs[3]);
+    const float d = f16_bits_to_f32(dd), dmin = f16_bits_to_f32(dd >> 16);
+    acc = fmaf(d * x.d, (float)V, acc);
+    return fmaf(-(dmin * x.d), (float)Mn, acc);
+}
+
+// n dwords of LDS starting at a 2-byte aligned byte offset `off`.
+template <int NW>
+__device__ __forceinline__ void lds_dwords(const uint8_t *sl, uint32_t off, uint32_t (&out)[NW]) {
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(sl + (off & ~3u));
+    const uint32_t sh = off & 3u;
+    uint32_t v[NW + 1];
+#pragma unroll
+    for (int k = 0; k <= NW; ++k) v[k] = p[k];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) out[k] = align_bytes(v[k + 1], v[k], sh);
+}
+
+// Q6_K part p = (h, g2) of the super-block at a 2-byte aligned offset: values
+// 128h + 32k + 16 g2 + l (k < 4, l < 16) take their low 4 bits from ql run A =
+// ql[64h + 16 g2 ..] (k = 0 low nibble, k = 2 high) or run B = ql[64h + 32 +
+// 16 g2 ..] (k = 1 low, k = 3 high), their high 2 bits from qh[32h + 16 g2 ..]
+// at bit 2k; group 8h + 2k + g2.  t = d d8 sum_k sc_k (sum q x - 32 bsum_k).
+template <>
+__device__ __forceinline__ float unit_dot<F_Q6_K, false>(const uint8_t *sl, uint32_t bo, int u,
+                                                         const XU<F_Q6_K, false> &x, float acc) {
+    const int p = u & 3, h = p >> 1, g2 = p & 1;
+    uint32_t ra[4], rb[4], qh[4], sw[2];
+    lds_dwords<4>(sl, bo + 64 * h + 16 * g2, ra);
+    lds_dwords<4>(sl, bo + 64 * h + 32 + 16 * g2, rb);
+    lds_dwords<4>(sl, bo + 128 + 32 * h + 16 * g2, qh);
+    lds_dwords<2>(sl, bo + 192 + 8 * h, sw);           // scales 8h .. 8h+7
+    const uint32_t dbits = *reinterpret_cast<const uint16_t *>(sl + bo + 208);
+    int V = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int s = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t src = (k & 1) ? rb[e] : ra[e];
+            const uint32_t lo4 = (k < 2) ? (src & 0x0f0f0f0fu) : ((src >> 4) & 0x0f0f0f0fu);
+            const uint32_t hi2 = ((qh[e] >> (2 * k)) & 0x03030303u) << 4;
+            s = dot4((int)(lo4 | hi2), x.q[4 * k + e], s);
+        }
+        // scale of group 8h + 2k + g2: byte 2k + g2 of the 8-byte window
+        const int sc = __builtin_amdgcn_sbfe((int)sw[k >> 1], 8 * (2 * (k & 1) + g2), 8);
+        V += sc * (s - 32 * x.bs[k]);
+    }
+    return fmaf(f16_bits_to_f32(dbits) * x.d, (float)V, acc);
+}
+
 // Copy bytes [lo, hi) of global memory into LDS at `dst` (16-byte aligned), as
 // the 16-byte chunks from lo & ~15 up to the chunk holding byte hi-1; chunk c
 // lands at dst + 16 c.  This wave issues the chunk groups (64 chunks, one
@@ -342,7 +443,7 @@ __global__ __launch_bounds__(64 * NW) void k_matvec(const uint8_t *__restrict__ 
                                                 int ss, uint8_t *__restrict__ xq_out) {
     using FB = FmtBytes<F>;
     using UT = Unit<F, PAIRED>;
-    static_assert(!XF32 || F != F_Q2_K, "the fused quantizer produces Q8_0 activations");
+    static_assert(!XF32 || !kIsK<F>, "the fused quantizer produces Q8_0 activations");
     extern __shared__ uint4 lds_dyn[];
     constexpr int SEGU = kWave * MAXU;                 // units per segment
     constexpr int NT = kWave * NW;                     // threads per workgroup
@@ -527,7 +628,7 @@ static hipError_t pick_mv(const void *w, const void *xin, uint8_t *xq_out, float
 template <int F, bool XF32 = false>
 static hipError_t dispatch_mv(const void *w, const void *xin, uint8_t *xq_out, float *y, int M, int N, int nb,
                               hipStream_t st) {
-    if constexpr (F != F_Q2_K) {
+    if constexpr (!kIsK<F>) {
         if (nb % 2 == 0) return pick_mv<F, true, XF32>(w, xin, xq_out, y, M, N, nb, st);
     }
     return pick_mv<F, false, XF32>(w, xin, xq_out, y, M, N, nb, st);
@@ -551,7 +652,7 @@ hipError_t launch_matvec_q2_k(const void *w, const void *xq, float *y, int N, in
 template <int F>
 static hipError_t quantize_matvec(const void *w, const float *x, void *xq, float *y, int N, int nb,
                                   hipStream_t st) {
-    const bool paired = F != F_Q2_K && nb % 2 == 0;
+    const bool paired = !kIsK<F> && nb % 2 == 0;
     const int nu = paired ? nb / 2 : nb;
     if (xq != nullptr && nu > kWave) {
         const hipError_t e = launch_quantize_q8_0(x, xq, nb, st);
@@ -570,17 +671,34 @@ hipError_t launch_quantize_matvec_q8_0(const void *w, const float *x, void *xq, 
     return quantize_matvec<F_Q8_0>(w, x, xq, y, N, nb, st);
 }
 
-// Q2_K prefill: the matvec kernel with one grid row per token (the weights are
-// re-read from cache for each token; correct for any M, not tuned).
-hipError_t launch_matmul_q2_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
+hipError_t launch_matvec_q4_k(const void *w, const void *xq, float *y, int N, int ns, hipStream_t st) {
+    return dispatch_mv<F_Q4_K>(w, xq, nullptr, y, 1, N, ns, st);
+}
+hipError_t launch_matvec_q6_k(const void *w, const void *xq, float *y, int N, int ns, hipStream_t st) {
+    return dispatch_mv<F_Q6_K>(w, xq, nullptr, y, 1, N, ns, st);
+}
+
+// K-quant prefill: the matvec kernel with one grid row per token (the weights
+// are re-read from cache for each token; correct for any M, not tuned).
+template <int F>
+static hipError_t matmul_by_tokens(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
     constexpr int kMaxY = 65535;
     for (int m0 = 0; m0 < M; m0 += kMaxY) {
         const int mc = min(kMaxY, M - m0);
         const uint8_t *xp = static_cast<const uint8_t *>(xq) + (int64_t)m0 * ns * kQ8KBytes;
-        const hipError_t e = dispatch_mv<F_Q2_K>(w, xp, nullptr, y + (int64_t)m0 * N, mc, N, ns, st);
+        const hipError_t e = dispatch_mv<F>(w, xp, nullptr, y + (int64_t)m0 * N, mc, N, ns, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+hipError_t launch_matmul_q2_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
+    return matmul_by_tokens<F_Q2_K>(w, xq, y, M, N, ns, st);
+}
+hipError_t launch_matmul_q4_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
+    return matmul_by_tokens<F_Q4_K>(w, xq, y, M, N, ns, st);
+}
+hipError_t launch_matmul_q6_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
+    return matmul_by_tokens<F_Q6_K>(w, xq, y, M, N, ns, st);
 }
 
 }  // namespace qmm

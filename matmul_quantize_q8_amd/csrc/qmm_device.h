@@ -12,6 +12,8 @@ constexpr int kQ80Bytes = 34;             // f16 d + int8[32]
 constexpr int kQ40Bytes = 18;             // f16 d + uint8[16]
 constexpr int kQ2KBytes = 84;             // scales[16] + qs[64] + f16 d + f16 dmin
 constexpr int kQ8KBytes = 292;            // f32 d + int8[256] + int16[16]
+constexpr int kQ4KBytes = 144;            // f16 d + f16 dmin + 12 B scales/mins + qs[128]
+constexpr int kQ6KBytes = 210;            // ql[128] + qh[64] + int8 scales[16] + f16 d
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));

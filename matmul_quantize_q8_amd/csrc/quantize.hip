@@ -189,6 +189,158 @@ __global__ __launch_bounds__(256) void k_quantize_q2_k(const float4 *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Q4_K weights.  Format: 144 bytes, f16 d @0, f16 dmin @2, 12 bytes of 6-bit
+// scales and mins @4, 128 bytes of nibbles @16; 32-byte chunk j holds values
+// 64j + l (low nibble of byte l) and 64j + 32 + l (high nibble) (minfer "The
+// payoff: a K-quant dot kernel, walked"); the 12-byte packing is GGUF's: for
+// s < 4, scale = b[s] & 63, min = b[s+4] & 63; for s >= 4, scale =
+// (b[s+4] & 15) | (b[s-4] >> 6) << 4, min = (b[s+4] >> 4) | (b[s] >> 6) << 4.
+// The pages give no quantizer; the rule (the same as the header's) is, per
+// sub-block t of 32: lo = min(0, min x), hi = max x, s = (hi - lo)/15,
+// mn = -lo; d = max s / 63, dmin = max mn / 63 (f16; dh, dminh the stored
+// values); sc = clamp(rne(s/dh), 0, 63), m = clamp(rne(mn/dminh), 0, 63);
+// q = clamp(rne((x + dminh*m)/(dh*sc)), 0, 15).  One wave per block; lane L
+// holds values 4L..4L+3 (sub-block L/8).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize_q4_k(const float4 *__restrict__ w, uint8_t *__restrict__ out,
+                                                       int64_t nblocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;
+    const float4 v = w[blk * 64 + lane];
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+
+    float lo = fminf(fminf(vv[0], vv[1]), fminf(vv[2], vv[3]));
+    float hi = fmaxf(fmaxf(vv[0], vv[1]), fmaxf(vv[2], vv[3]));
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+        lo = fminf(lo, xor_shfl(lo, m));
+        hi = fmaxf(hi, xor_shfl(hi, m));
+    }
+    lo = fminf(lo, 0.0f);
+    const float s = (hi - lo) / 15.0f;
+    const float mn = -lo;
+    float smax = s, mmax = mn;
+#pragma unroll
+    for (int m = 8; m < 64; m <<= 1) {
+        smax = fmaxf(smax, xor_shfl(smax, m));
+        mmax = fmaxf(mmax, xor_shfl(mmax, m));
+    }
+    smax = (smax > 0.0f) ? smax : 0.0f;        // +0 when no sub-block spans anything
+    mmax = (mmax > 0.0f) ? mmax : 0.0f;
+    const uint32_t dbits = f32_to_f16_bits(smax / 63.0f);
+    const uint32_t dminbits = f32_to_f16_bits(mmax / 63.0f);
+    const float dh = f16_bits_to_f32(dbits);
+    const float dminh = f16_bits_to_f32(dminbits);
+
+    int sc = 0, mq = 0;
+    if (dh != 0.0f) sc = min(max((int)rintf(s / dh), 0), 63);
+    if (dminh != 0.0f) mq = min(max((int)rintf(mn / dminh), 0), 63);
+    const float off = dminh * (float)mq;
+    const float div = dh * (float)sc;
+    uint32_t codes = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int c = 0;
+        if (div != 0.0f) c = min(max((int)rintf((vv[k] + off) / div), 0), 15);
+        codes |= (uint32_t)c << (8 * k);
+    }
+    // values 4L..4L+3 are chunk j = L/16, nibble half (L/8)&1, bytes 4(L%8)..+3:
+    // lane L (low half) and lane L+8 (high half) fill one qs dword.
+    const uint32_t word = codes | (xor_shfl(codes, 8) << 4);
+    uint8_t *ob = out + blk * kQ4KBytes;                     // 144 = 16 * 9: 16-byte aligned
+    if ((lane & 8) == 0) *reinterpret_cast<uint32_t *>(ob + 16 + 32 * (lane >> 4) + 4 * (lane & 7)) = word;
+    // scales: sub-block t = L/8; lanes 8t (t < 4) also hold sub-block t+4's via xor 32
+    const int sc4 = xor_shfl(sc, 32), m4 = xor_shfl(mq, 32);
+    if (lane < 32 && (lane & 7) == 0) {
+        const int t = lane >> 3;
+        ob[4 + t] = (uint8_t)((sc & 63) | ((sc4 >> 4) << 6));
+        ob[8 + t] = (uint8_t)((mq & 63) | ((m4 >> 4) << 6));
+        ob[12 + t] = (uint8_t)((sc4 & 15) | ((m4 & 15) << 4));
+    }
+    if (lane == 0) {
+        *reinterpret_cast<uint16_t *>(ob) = (uint16_t)dbits;
+        *reinterpret_cast<uint16_t *>(ob + 2) = (uint16_t)dminbits;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q6_K weights.  Format (GGUF's; the pages give only the 210-byte size): low
+// 4 bits ql[128] @0, high 2 bits qh[64] @128, int8 scales[16] @192, f16 d
+// @208; value i (h = i/128, k = (i%128)/32, l = i%32) has its low bits in
+// ql[64h + l + 32(k&1)] (low nibble for k < 2, high for k >= 2) and its high
+// bits at bit 2k of qh[32h + l]; value = d * sc_{i/16} * (q - 32).  The pages
+// give no quantizer; the rule (the same as the header's) is, per group g of
+// 16: mx = the value of largest magnitude (first on ties), s = mx / -32;
+// d = max |s| / 127 (f16; dh the stored value); sc = clamp(rne(s/dh), -128,
+// 127); q = clamp(rne(x/(dh*sc)) + 32, 0, 63), 32 if the divisor is 0.  One
+// wave per block; lane L holds values 4L..4L+3 (group L/4).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize_q6_k(const float4 *__restrict__ w, uint8_t *__restrict__ out,
+                                                       int64_t nblocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;
+    const float4 v = w[blk * 64 + lane];
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+
+    // (|value|, index, value) of the group's largest magnitude, first index on ties
+    float am = fabsf(vv[0]), mx = vv[0];
+    int ix = 4 * lane;
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+        const float a = fabsf(vv[k]);
+        if (a > am) { am = a; mx = vv[k]; ix = 4 * lane + k; }
+    }
+#pragma unroll
+    for (int m = 1; m < 4; m <<= 1) {
+        const float oam = xor_shfl(am, m);
+        const float omx = xor_shfl(mx, m);
+        const int oix = xor_shfl(ix, m);
+        if (oam > am || (oam == am && oix < ix)) { am = oam; mx = omx; ix = oix; }
+    }
+    const float s = (am != 0.0f) ? mx / -32.0f : 0.0f;
+    float smax = fabsf(s);
+#pragma unroll
+    for (int m = 4; m < 64; m <<= 1) smax = fmaxf(smax, xor_shfl(smax, m));
+    const uint32_t dbits = f32_to_f16_bits(smax / 127.0f);
+    const float dh = f16_bits_to_f32(dbits);
+    int sc = 0;
+    if (dh != 0.0f) sc = min(max((int)rintf(s / dh), -128), 127);
+    const float div = dh * (float)sc;
+    uint32_t codes = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int c = 32;
+        if (div != 0.0f) c = min(max((int)rintf(vv[k] / div) + 32, 0), 63);
+        codes |= (uint32_t)c << (8 * k);
+    }
+    // values 4L..4L+3: h = L/32, k = (L%32)/8, l = 4(L%8)..+3.  ql dword at
+    // 64h + 32(k&1) + 4(L%8): low nibbles from lane L (k < 2), high nibbles
+    // from lane L+16 (k + 2); qh dword at 128 + 32h + 4(L%8) gathers the four k.
+    const int kq = (lane >> 3) & 3;
+    const uint32_t lo4 = codes & 0x0f0f0f0fu;
+    const uint32_t qlw = lo4 | (xor_shfl(lo4, 16) << 4);
+    uint32_t qhw = ((codes >> 4) & 0x03030303u) << (2 * kq);
+    qhw |= xor_shfl(qhw, 8);
+    qhw |= xor_shfl(qhw, 16);
+    uint8_t *ob = out + blk * kQ6KBytes;                      // 210: only 2-byte aligned
+    const int h = lane >> 5;
+    if (kq < 2) {
+        uint16_t *o16 = reinterpret_cast<uint16_t *>(ob + 64 * h + 32 * kq + 4 * (lane & 7));
+        o16[0] = (uint16_t)(qlw & 0xffffu);
+        o16[1] = (uint16_t)(qlw >> 16);
+    }
+    if (kq == 0) {
+        uint16_t *o16 = reinterpret_cast<uint16_t *>(ob + 128 + 32 * h + 4 * (lane & 7));
+        o16[0] = (uint16_t)(qhw & 0xffffu);
+        o16[1] = (uint16_t)(qhw >> 16);
+    }
+    if ((lane & 3) == 0) ob[192 + (lane >> 2)] = (uint8_t)(int8_t)sc;
+    if (lane == 0) *reinterpret_cast<uint16_t *>(ob + 208) = (uint16_t)dbits;
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (called by the C ABI after argument checks).
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipStream_t st) {
@@ -213,6 +365,18 @@ hipError_t launch_quantize_q2_k(const float *w, void *out, int64_t nblocks, hipS
     const int64_t grid = (nblocks + 3) / 4;
     void *args[] = {(void *)&w, (void *)&out, (void *)&nblocks};
     return hipLaunchKernel((const void *)k_quantize_q2_k, dim3((unsigned)grid), dim3(256), args, 0, st);
+}
+
+hipError_t launch_quantize_q4_k(const float *w, void *out, int64_t nblocks, hipStream_t st) {
+    const int64_t grid = (nblocks + 3) / 4;
+    void *args[] = {(void *)&w, (void *)&out, (void *)&nblocks};
+    return hipLaunchKernel((const void *)k_quantize_q4_k, dim3((unsigned)grid), dim3(256), args, 0, st);
+}
+
+hipError_t launch_quantize_q6_k(const float *w, void *out, int64_t nblocks, hipStream_t st) {
+    const int64_t grid = (nblocks + 3) / 4;
+    void *args[] = {(void *)&w, (void *)&out, (void *)&nblocks};
+    return hipLaunchKernel((const void *)k_quantize_q6_k, dim3((unsigned)grid), dim3(256), args, 0, st);
 }
 
 }  // namespace qmm

@@ -75,6 +75,10 @@ A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced
     (lambda L: L.qmm_quantize_matvec_q8_0(A, A, A, None, 8, 64, None), 2),   # y NULL
     (lambda L: L.qmm_quantize_matvec_q8_0(A, A, A + 2, A, 8, 64, None), 3),  # xq misaligned
     (lambda L: L.qmm_quantize_matvec_q4_0(A, A + 4, None, A, 8, 64, None), 3),
+    (lambda L: L.qmm_matvec_q4_k(A, A, A, 8, 32 * 9, None), 1),                # K % 256
+    (lambda L: L.qmm_matmul_q6_k(A, A, A, 2, 8, 256 + 32, None), 1),
+    (lambda L: L.qmm_quantize_q6_k(A, A, 1, 128, None), 1),
+    (lambda L: L.qmm_matvec_q6_k(A, None, A, 8, 256, None), 2),
 ])
 def test_argument_errors_without_device(q, call, code):
     assert call(q.lib()) == code

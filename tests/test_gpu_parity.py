@@ -43,8 +43,8 @@ def _gpu_quant(env, fmt, x, weights=False):
     torch, q, _ = env
     rows, K = x.shape
     out = torch.zeros(rows * q.row_bytes(fmt, K), dtype=torch.uint8, device="cuda")
-    fn = {"q8_0": q.qmm_quantize_q8_0, "q8_k": q.qmm_quantize_q8_k,
-          "q4_0": q.qmm_quantize_q4_0, "q2_k": q.qmm_quantize_q2_k}[fmt]
+    fn = {"q8_0": q.qmm_quantize_q8_0, "q8_k": q.qmm_quantize_q8_k, "q4_0": q.qmm_quantize_q4_0,
+          "q2_k": q.qmm_quantize_q2_k, "q4_k": q.qmm_quantize_q4_k, "q6_k": q.qmm_quantize_q6_k}[fmt]
     fn(_dev(torch, x), out, rows, K)
     torch.cuda.synchronize()
     return out.cpu().numpy().reshape(rows, -1)
@@ -108,6 +108,20 @@ def test_quantize_q2_k_weights_bit_exact(env, rows, K):
     assert np.array_equal(_gpu_quant(env, "q2_k", w), orc.quantize_q2_k_w(w))
 
 
+@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+@pytest.mark.parametrize("rows,K", [(1, 256), (16, 1024), (12288, 4096), (3, 1280)])
+def test_quantize_k_weights_bit_exact(env, fmt, rows, K):
+    _, _, orc = env
+    _say("quantize", fmt, rows, K)
+    w = synth.gaussian_f32((rows, K), 0.02, 4100 + rows + K)
+    w[0, :256] = 0.0                                  # zero super-block
+    if rows > 1:
+        w[1, :32] = np.abs(w[1, :32])                 # a sub-block with no negative value
+        w[1, 40] = -0.5                               # magnitude tie inside a group: first index wins
+        w[1, 44] = 0.5
+    assert np.array_equal(_gpu_quant(env, fmt, w), orc.quantize_w(fmt, w))
+
+
 # ---------------------------------------------------------------------------
 # Products
 # ---------------------------------------------------------------------------
@@ -157,6 +171,10 @@ MATVEC_CASES = [
     ("q8_0", 1, 32), ("q8_0", 5, 96), ("q8_0", 11, 4128), ("q8_0", 3, 20000),
     ("q2_k", 12288, 4096),
     ("q2_k", 1, 256), ("q2_k", 3, 768), ("q2_k", 13, 9216), ("q2_k", 2, 40960),
+    ("q4_k", 12288, 4096), ("q4_k", 1, 256), ("q4_k", 3, 768), ("q4_k", 45, 512),   # 8 rows per wave
+    ("q4_k", 13, 9216), ("q4_k", 2, 40960), ("q4_k", 7, 1280),                      # 4 units per lane; segments
+    ("q6_k", 12288, 4096), ("q6_k", 1, 256), ("q6_k", 3, 768), ("q6_k", 37, 512),
+    ("q6_k", 13, 9216), ("q6_k", 2, 40960), ("q6_k", 5, 1280),   # odd super-block count: rows 2 mod 4
 ]
 
 
@@ -245,6 +263,8 @@ MATMUL_CASES = [
     ("q4_0", 1, 129, 64), ("q4_0", 131, 255, 128), ("q4_0", 70, 130, 192), ("q4_0", 257, 129, 256),
     ("q4_0", 3, 300, 320), ("q4_0", 200, 100, 448),
     ("q2_k", 1, 8, 256), ("q2_k", 9, 70, 1024), ("q2_k", 33, 130, 4096),
+    ("q4_k", 1, 8, 256), ("q4_k", 9, 70, 1024), ("q4_k", 33, 130, 4096),
+    ("q6_k", 1, 8, 256), ("q6_k", 9, 70, 1024), ("q6_k", 5, 33, 1280),
 ]
 
 

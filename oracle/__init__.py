@@ -63,6 +63,8 @@ def lib():
         L.orc_f32_to_f16_array.restype = None
         L.orc_f16_to_f32_array.argtypes = [P, P, I64]
         L.orc_f16_to_f32_array.restype = None
+        L.orc_get_rows.argtypes = [I32, P, P, I64, I64, I64, P]
+        L.orc_get_rows.restype = I32
         L.orc_block_isum.argtypes = [I32, P, P]
         L.orc_block_isum.restype = ctypes.c_int32
         _lib = L
@@ -209,6 +211,16 @@ def matmul_sampled(fmt: str, w, xq, mi, ni, K: int):
     lib().orc_matmul_sampled(FMT_ID[fmt], _ptr(w), _ptr(xq), _ptr(mi), _ptr(ni), mi.size,
                              _ptr(y64), _ptr(mag), K)
     return y64, mag
+
+
+def get_rows(fmt: str, w, ids, N: int, K: int) -> np.ndarray:
+    """f32 [len(ids)][K]: the decoded rows ids of the [N][K] table `w` (NaN rows for ids outside [0, N))."""
+    w = _u8(w)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    assert w.size == N * row_bytes(fmt, K)
+    out = np.zeros((ids.size, K), dtype=np.float32)
+    assert lib().orc_get_rows(FMT_ID[fmt], _ptr(w), _ptr(ids), ids.size, N, K, _ptr(out)) == 0
+    return out
 
 
 def block_isum(fmt: str, wblock, xblock) -> int:

@@ -489,7 +489,10 @@ void orc_dequantize_q4_k(const uint8_t *blk, double *out, int64_t rows, int64_t 
         }
 }
 
-/* Q6_K value = d * sc_g * (q - 32), g = i / 16 (layout above). */
+/* Q6_K value = d * sc_g * (q - 32), g = i / 16 (layout above), formed as the
+ * binary16 scale times the integer sc_g * (q - 32) (reading: the pages' row
+ * getter decodes every format as "scale x integer"; with a negative sc_g this
+ * fixes the sign of a decoded zero to that of d). */
 void orc_dequantize_q6_k(const uint8_t *blk, double *out, int64_t rows, int64_t K) {
     int64_t ns = K / QKK;
     for (int64_t r = 0; r < rows; ++r)
@@ -497,7 +500,7 @@ void orc_dequantize_q6_k(const uint8_t *blk, double *out, int64_t rows, int64_t 
             const uint8_t *p = blk + (r * ns + sb) * Q6_K_BYTES;
             double d = rd_f16(p + 208);
             for (int i = 0; i < QKK; ++i)
-                out[r * K + sb * QKK + i] = d * (int8_t)p[192 + i / 16] * (q6k_code(p, i) - 32);
+                out[r * K + sb * QKK + i] = d * (double)((int8_t)p[192 + i / 16] * (q6k_code(p, i) - 32));
         }
 }
 
@@ -742,6 +745,35 @@ int orc_matmul_sampled(int fmt, const uint8_t *w, const uint8_t *x, const int64_
         y64[c] = v;
         if (mag) mag[c] = a;
     }
+    return 0;
+}
+
+/* Embedding rows ([minfer] "The embedding matmul": for each token id the
+ * quantized row of the table is walked block by block and dequantized into
+ * the output row; the same row getter serves every backend, so the rows are
+ * byte-for-byte identical).  out[t][:] = f32 of the decoded row ids[t] (each
+ * value exact in double, rounded once); an id outside [0, N) gives a row of
+ * quiet NaNs (reading: the page's code indexes the table directly, an id out
+ * of range is outside its contract). */
+int orc_get_rows(int fmt, const uint8_t *w, const int32_t *ids, int64_t n, int64_t N, int64_t K, float *out) {
+    int64_t rb = w_row_bytes(fmt, K);
+    double *row = (double *)malloc(sizeof(double) * (size_t)K);
+    if (!row) return -1;
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t id = ids[t];
+        if (id < 0 || id >= N) {
+            for (int64_t i = 0; i < K; ++i) out[t * K + i] = bits_f32(0x7fc00000u);
+            continue;
+        }
+        const uint8_t *wr = w + id * rb;
+        if (fmt == ORC_Q4_0) orc_dequantize_q4_0(wr, row, 1, K);
+        else if (fmt == ORC_Q8_0) orc_dequantize_q8_0(wr, row, 1, K);
+        else if (fmt == ORC_Q2_K) orc_dequantize_q2_k(wr, row, 1, K);
+        else if (fmt == ORC_Q4_K) orc_dequantize_q4_k(wr, row, 1, K);
+        else orc_dequantize_q6_k(wr, row, 1, K);
+        for (int64_t i = 0; i < K; ++i) out[t * K + i] = (float)row[i];
+    }
+    free(row);
     return 0;
 }
 

@@ -496,6 +496,41 @@ def test_matmul_rows_equal_matvec_and_threads_invariant(orc, fmt):
 
 
 # ---------------------------------------------------------------------------
+# Embedding rows (minfer "The embedding matmul")
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt,K", [("q4_0", 96), ("q8_0", 64), ("q2_k", 512), ("q4_k", 256), ("q6_k", 768)])
+def test_get_rows_is_the_decoded_row(orc, fmt, K):
+    """Row t of the output is row ids[t] of the table, every value the exactly
+    decoded one rounded once to f32; repeated ids repeat the row; ids outside
+    the table give NaN rows."""
+    N = 7
+    w = orc.quantize_w(fmt, synth.gaussian_f32((N, K), 0.02, 181))
+    ids = np.array([3, 0, 6, 3, -1, 7], dtype=np.int32)
+    out = orc.get_rows(fmt, w, ids, N, K)
+    dec = orc.dequantize(fmt, w, K)
+    for t, i in enumerate(ids):
+        if 0 <= i < N:
+            assert np.array_equal(out[t], dec[i].astype(np.float32))
+            assert np.array_equal(out[t].astype(np.float64), dec[i]) or fmt in ("q2_k", "q4_k")
+        else:
+            assert np.all(np.isnan(out[t]))
+    assert np.array_equal(out[0], out[3])
+
+
+def test_get_rows_worked_byte(orc):
+    """The worked Q4_0 byte 0x21 (minfer section 3.2) through the row getter:
+    scale 1.0 gives -7 at element j and -6 at element j + 16."""
+    g = golden("worked_byte.json")
+    blk = np.zeros(18, dtype=np.uint8)
+    blk[0:2] = np.array([np.float16(1.0)], dtype=np.float16).view(np.uint8)
+    blk[2:18] = 0x88                                  # every other element decodes to 0
+    blk[2 + 5] = g["byte"]
+    row = orc.get_rows("q4_0", blk, np.array([0], dtype=np.int32), 1, 32)[0] * g["scale_w"]
+    assert row[5] == g["element_j"] and row[5 + 16] == g["element_j_plus_16"]
+    assert np.count_nonzero(row) == 2
+
+
+# ---------------------------------------------------------------------------
 # The seeded input stream
 # ---------------------------------------------------------------------------
 def test_splitmix64_counter_form_equals_sequential_definition():

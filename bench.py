@@ -278,6 +278,26 @@ def bench_matvec_configs(args, torch, q, synth):
                      "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
         del wqs, wq0
         torch.cuda.empty_cache()
+    # embedding rows: 2048 token ids into a Q4_0 table of 151936 x 896 (the
+    # vocabulary shape of the 0.5B model the pages measure)
+    Nt, Kt, nid = 151936, 896, 2048
+    tb = Nt * q.row_bytes("q4_0", Kt)
+    w = torch.from_numpy(synth.weights(Nt, Kt, config=7)).cuda()
+    table = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q4_0(w, table, Nt, Kt)
+    del w
+    ids = torch.from_numpy((synth.splitmix64(synth.seed_for(7, 1), 0, nid) % Nt).astype("int32")).cuda()
+    emb = torch.empty((nid, Kt), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    ms, ms_min, _ = time_batches(torch, lambda i: q.qmm_get_rows_q4_0(table, ids, emb, nid, Nt, Kt), args.steps, 20)
+    moved = nid * (q.row_bytes("q4_0", Kt) + 4 * Kt + 4)
+    gbs = moved / (ms * 1e-3) / 1e9
+    log(f"get_rows q4_0 {nid} of {Nt}x{Kt}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s of rows read + written")
+    rows.append({"workload": f"q4_0_get_rows_{nid}_of_{Nt}x{Kt}", "format": "q4_0", "N": Nt, "K": Kt,
+                 "ids": nid, "bytes_moved": moved, "kernel_us_mean": round(ms * 1e3, 3),
+                 "kernel_us_best_batch": round(ms_min * 1e3, 3), "achieved_gbs": round(gbs, 1),
+                 "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    del table
     layer = [r for r in rows if r["workload"].startswith("q8_0_")]
     tot_b = sum(r["weight_bytes"] for r in layer)
     tot_us = sum(r["kernel_us_mean"] for r in layer)

@@ -192,6 +192,28 @@ qmm_status qmm_matmul_q4_k(const void *w, const void *xq8k, float *y, int64_t M,
 qmm_status qmm_matmul_q6_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
 
+/* ---- embedding rows ---------------------------------------------------------
+ * out[t][:] = the decoded row ids[t] of the quantized table w (N rows of K
+ * values), as f32: minfer "The embedding matmul" (a lookup, not a product: the
+ * token's row is dequantized block by block; one row getter for every backend
+ * keeps the embeddings byte-for-byte identical).  Every value is the exactly
+ * decoded one rounded once to f32 (Q4_0, Q8_0, Q6_K values are exact in f32;
+ * Q2_K and Q4_K subtract two exact products).
+ *   w   : N rows of blocks in the entry point's format.
+ *   ids : int32 [n_ids], device memory; an id outside [0, N) yields a row of
+ *         quiet NaNs (no read outside the table).
+ *   out : f32 [n_ids][K], written. */
+qmm_status qmm_get_rows_q4_0(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream);
+qmm_status qmm_get_rows_q8_0(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream);
+qmm_status qmm_get_rows_q2_k(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream);
+qmm_status qmm_get_rows_q4_k(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream);
+qmm_status qmm_get_rows_q6_k(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         for name in ("qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0"):
             getattr(L, name).argtypes = [P, P, P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
+        for name in ("qmm_get_rows_q4_0", "qmm_get_rows_q8_0", "qmm_get_rows_q2_k", "qmm_get_rows_q4_k",
+                     "qmm_get_rows_q6_k"):
+            getattr(L, name).argtypes = [P, P, P, I64, I64, I64, P]
+            getattr(L, name).restype = ctypes.c_int
         for name in ("qmm_matmul_q4_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
@@ -74,7 +78,8 @@ EXPORTS = ("qmm_status_string", "qmm_abi_version",
            "qmm_quantize_q4_k", "qmm_quantize_q6_k",
            "qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k", "qmm_matvec_q4_k", "qmm_matvec_q6_k",
            "qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0",
-           "qmm_matmul_q4_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k")
+           "qmm_matmul_q4_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k",
+           "qmm_get_rows_q4_0", "qmm_get_rows_q8_0", "qmm_get_rows_q2_k", "qmm_get_rows_q4_k", "qmm_get_rows_q6_k")
 
 
 def row_bytes(fmt: str, K: int) -> int:
@@ -188,6 +193,23 @@ def qmm_matmul_q6_k(w, xq8k, y, M: int, N: int, K: int, stream=None) -> None:
     _call("qmm_matmul_q6_k", _addr(w), _addr(xq8k), _addr(y), M, N, K, _stream(stream))
 
 
+def _get_rows(fmt):
+    name = "qmm_get_rows_" + fmt
+
+    def get_rows(w, ids, out, n_ids: int, N: int, K: int, stream=None) -> None:
+        """out[t][:] = decoded row ids[t] of the table w (f32; NaN rows for ids outside [0, N))."""
+        _call(name, _addr(w), _addr(ids), _addr(out), n_ids, N, K, _stream(stream))
+    get_rows.__name__ = name
+    return get_rows
+
+
+qmm_get_rows_q4_0 = _get_rows("q4_0")
+qmm_get_rows_q8_0 = _get_rows("q8_0")
+qmm_get_rows_q2_k = _get_rows("q2_k")
+qmm_get_rows_q4_k = _get_rows("q4_k")
+qmm_get_rows_q6_k = _get_rows("q6_k")
+
+
 QUANTIZE_W = {"q4_0": qmm_quantize_q4_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_quantize_q2_k,
               "q4_k": qmm_quantize_q4_k, "q6_k": qmm_quantize_q6_k}
 QUANTIZE_X = {"q4_0": qmm_quantize_q8_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_quantize_q8_k,
@@ -196,3 +218,5 @@ MATVEC = {"q4_0": qmm_matvec_q4_0, "q8_0": qmm_matvec_q8_0, "q2_k": qmm_matvec_q
           "q6_k": qmm_matvec_q6_k}
 MATMUL = {"q4_0": qmm_matmul_q4_0, "q2_k": qmm_matmul_q2_k, "q4_k": qmm_matmul_q4_k, "q6_k": qmm_matmul_q6_k}
 QUANTIZE_MATVEC = {"q4_0": qmm_quantize_matvec_q4_0, "q8_0": qmm_quantize_matvec_q8_0}
+GET_ROWS = {"q4_0": qmm_get_rows_q4_0, "q8_0": qmm_get_rows_q8_0, "q2_k": qmm_get_rows_q2_k,
+            "q4_k": qmm_get_rows_q4_k, "q6_k": qmm_get_rows_q6_k}

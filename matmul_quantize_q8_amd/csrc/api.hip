@@ -24,6 +24,8 @@ hipError_t launch_quantize_matvec_q8_0(const void *w, const float *x, void *xq, 
                                        hipStream_t st);
 hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st);
 int64_t matmul_q4_0_max_blocks();
+hipError_t launch_get_rows(int fmt, const void *w, const int32_t *ids, float *out, int64_t n, int64_t N, int64_t K,
+                           int64_t row_bytes, hipStream_t st);
 hipError_t launch_matmul_q2_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
 hipError_t launch_matmul_q4_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
 hipError_t launch_matmul_q6_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
@@ -227,6 +229,40 @@ qmm_status qmm_matmul_q4_k(const void *w, const void *xq8k, float *y, int64_t M,
 qmm_status qmm_matmul_q6_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream) {
     return matmul(qmm::launch_matmul_q6_k, w, xq8k, y, M, N, K, 256, qmm::kQ6KBytes, qmm::kQ8KBytes, stream);
+}
+
+static qmm_status get_rows(int fmt, const void *w, const int32_t *ids, float *out, int64_t n, int64_t N, int64_t K,
+                           int64_t blk, int64_t wbytes, void *stream) {
+    bool work;
+    qmm_status s = check_shape(n, N, K, blk, work);
+    if (s != QMM_OK) return s;
+    if (!size_ok(N, K, blk, wbytes) || !size_ok(n, K, 1, 4)) return QMM_E_SHAPE;
+    if ((n * (K / 4) + 255) / 256 > kMaxDim) return QMM_E_SHAPE;
+    if (!work) return QMM_OK;
+    if ((s = check_ptrs({w, ids, out})) != QMM_OK) return s;
+    if ((s = check_device()) != QMM_OK) return s;
+    return launched(qmm::launch_get_rows(fmt, w, ids, out, n, N, K, K / blk * wbytes, static_cast<hipStream_t>(stream)));
+}
+
+qmm_status qmm_get_rows_q4_0(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream) {
+    return get_rows(qmm::F_Q4_0, w, ids, out, n_ids, N, K, 32, qmm::kQ40Bytes, stream);
+}
+qmm_status qmm_get_rows_q8_0(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream) {
+    return get_rows(qmm::F_Q8_0, w, ids, out, n_ids, N, K, 32, qmm::kQ80Bytes, stream);
+}
+qmm_status qmm_get_rows_q2_k(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream) {
+    return get_rows(qmm::F_Q2_K, w, ids, out, n_ids, N, K, 256, qmm::kQ2KBytes, stream);
+}
+qmm_status qmm_get_rows_q4_k(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream) {
+    return get_rows(qmm::F_Q4_K, w, ids, out, n_ids, N, K, 256, qmm::kQ4KBytes, stream);
+}
+qmm_status qmm_get_rows_q6_k(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream) {
+    return get_rows(qmm::F_Q6_K, w, ids, out, n_ids, N, K, 256, qmm::kQ6KBytes, stream);
 }
 
 }  // extern "C"

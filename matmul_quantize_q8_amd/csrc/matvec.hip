@@ -41,11 +41,6 @@ namespace qmm {
 
 hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipStream_t st);
 
-enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4 };
-// K-quant weights (256-value super-blocks) pair with Q8_K activations, the
-// 32-value formats with Q8_0 (minfer "Two activation formats, one pairing rule").
-template <int F> constexpr bool kIsK = F >= F_Q2_K;
-
 template <int F> struct FmtBytes;
 template <> struct FmtBytes<F_Q4_0> { static constexpr int BB = kQ40Bytes, XB = kQ80Bytes; };
 template <> struct FmtBytes<F_Q8_0> { static constexpr int BB = kQ80Bytes, XB = kQ80Bytes; };

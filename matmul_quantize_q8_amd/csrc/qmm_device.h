@@ -15,6 +15,12 @@ constexpr int kQ8KBytes = 292;            // f32 d + int8[256] + int16[16]
 constexpr int kQ4KBytes = 144;            // f16 d + f16 dmin + 12 B scales/mins + qs[128]
 constexpr int kQ6KBytes = 210;            // ql[128] + qh[64] + int8 scales[16] + f16 d
 
+// Weight formats.  K-quant weights (256-value super-blocks) pair with Q8_K
+// activations, the 32-value formats with Q8_0 (minfer "Two activation
+// formats, one pairing rule").
+enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4 };
+template <int F> constexpr bool kIsK = F >= F_Q2_K;
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));

@@ -79,6 +79,9 @@ A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced
     (lambda L: L.qmm_matmul_q6_k(A, A, A, 2, 8, 256 + 32, None), 1),
     (lambda L: L.qmm_quantize_q6_k(A, A, 1, 128, None), 1),
     (lambda L: L.qmm_matvec_q6_k(A, None, A, 8, 256, None), 2),
+    (lambda L: L.qmm_get_rows_q4_0(A, A, A, 4, 8, 48, None), 1),
+    (lambda L: L.qmm_get_rows_q4_k(A, A + 4, A, 4, 8, 256, None), 3),
+    (lambda L: L.qmm_get_rows_q8_0(A, None, A, 4, 8, 64, None), 2),
 ])
 def test_argument_errors_without_device(q, call, code):
     assert call(q.lib()) == code

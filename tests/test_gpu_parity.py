@@ -255,6 +255,22 @@ def test_fused_without_xq_output_equals_two_launches(env, fmt, N, K):
     _check(y, ref["y64"][0], ref["mag"][0], ("fused no xq", fmt, N, K))
 
 
+@pytest.mark.parametrize("fmt,N,K", [("q4_0", 151, 896), ("q8_0", 64, 1024), ("q2_k", 33, 512),
+                                     ("q4_k", 40, 4096), ("q6_k", 17, 1280), ("q4_0", 3000, 4096)])
+def test_get_rows_bit_exact(env, fmt, N, K):
+    """Embedding rows are byte-for-byte the oracle's (minfer "The embedding
+    matmul"), repeated ids included; ids outside the table give NaN rows."""
+    torch, q, orc = env
+    _say("get_rows", fmt, N, K)
+    w = orc.quantize_w(fmt, synth.gaussian_f32((N, K), 0.02, 9700 + N))
+    ids = np.array([0, N - 1, 5 % N, 0, -1, N, 2 % N, N - 1], dtype=np.int32)
+    ref = orc.get_rows(fmt, w, ids, N, K)
+    out = torch.full((ids.size, K), 1.0, dtype=torch.float32, device="cuda")
+    q.GET_ROWS[fmt](_dev(torch, w), _dev(torch, ids), out, ids.size, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
 MATMUL_CASES = [
     ("q4_0", 1, 8, 32), ("q4_0", 37, 200, 1024), ("q4_0", 128, 128, 4096), ("q4_0", 130, 129, 160),
     ("q4_0", 64, 512, 1024), ("q4_0", 5, 3, 96), ("q4_0", 256, 384, 4128), ("q4_0", 300, 700, 2080),

@@ -228,12 +228,25 @@ def bench_prefill(args, torch, q, synth):
     ops = 2.0 * M * N * K
     log(f"prefill: {ms_step * 1e3:.1f} us/step, matmul {mm_ms * 1e3:.1f} us (best batch {mm_min * 1e3:.1f})")
     tops_kernel = ops / (mm_ms * 1e-3) / 1e12
+    # the same prefill with Q8_0 weights (same activations, weights from the same stream)
+    w = torch.from_numpy(synth.weights(N, K, config=1)).cuda()
+    wq8 = torch.empty(N * q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q8_0(w, wq8, N, K)
+    del w
+    for _ in range(4):
+        q.qmm_matmul_q8_0(wq8, Xq, Y, M, N, K)
+    m8_ms, m8_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q8_0(wq8, Xq, Y, M, N, K), args.prefill_steps, 4)
+    log(f"prefill q8_0 weights: matmul {m8_ms * 1e3:.1f} us (best batch {m8_min * 1e3:.1f})")
+    del wq8
     return dict(ms_step=ms_step, tops=ops / (ms_step * 1e-3) / 1e12,
                 roofline={"kernel": "qmm::k_matmul_q4_0", "bound": "mfma", "achieved": round(tops_kernel, 2),
                           "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
                           "traffic": committed_traffic("k_matmul_q4_0", "2048x12288x4096"),
                           "kernel_us_mean": round(mm_ms * 1e3, 2),
-                          "kernel_us_best_batch": round(mm_min * 1e3, 2), "algorithmic_ops": ops})
+                          "kernel_us_best_batch": round(mm_min * 1e3, 2), "algorithmic_ops": ops},
+                q8_0_weights={"kernel": "qmm::k_matmul_q8_0", "kernel_us_mean": round(m8_ms * 1e3, 2),
+                              "achieved": round(ops / (m8_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
+                              "frac": round(ops / (m8_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)})
 
 
 # The other decode workloads, one matvec launch each, weights rotated like the
@@ -407,7 +420,7 @@ def main():
         pf = {"workload": "q4_0_matmul_2048x12288x4096", "value": round(pre["tops"], 2), "unit": "TOPS",
               "steps": args.prefill_steps, "warmup": args.prefill_warmup, "ms_per_step": round(pre["ms_step"], 4),
               "step": "quantize_q8_0 (2048x4096) + matmul_q4_0", "roofline": pre["roofline"],
-              "cpu_baseline": cpu_pre}
+              "q8_0_weights": pre["q8_0_weights"], "cpu_baseline": cpu_pre}
         if dec is None:
             out.update({"value": pf["value"], "unit": "TOPS", "steps": pf["steps"], "warmup": pf["warmup"],
                         "ms_per_step": pf["ms_per_step"], "config": {"workload": pf["workload"]},

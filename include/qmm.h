@@ -181,9 +181,12 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
 /* Prefill matmul, M tokens.
  *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.
  *   y  : f32 [M][N], written.
- * qmm_matmul_q4_0 also returns QMM_E_SHAPE when 128 rows of Q8_0 activations
+ * qmm_matmul_q4_0 and qmm_matmul_q8_0 (int8 MFMA) also return QMM_E_SHAPE when
+ * 128 rows of Q8_0 activations
  * (128 * K/32 * 34 bytes) exceed 2^31 - 1 bytes, i.e. K > 15,790,304. */
 qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream);
+qmm_status qmm_matmul_q8_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
 qmm_status qmm_matmul_q2_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);

@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
                      "qmm_get_rows_q6_k"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
-        for name in ("qmm_matmul_q4_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k"):
+        for name in ("qmm_matmul_q4_0", "qmm_matmul_q8_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -78,7 +78,7 @@ EXPORTS = ("qmm_status_string", "qmm_abi_version",
            "qmm_quantize_q4_k", "qmm_quantize_q6_k",
            "qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k", "qmm_matvec_q4_k", "qmm_matvec_q6_k",
            "qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0",
-           "qmm_matmul_q4_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k",
+           "qmm_matmul_q4_0", "qmm_matmul_q8_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k",
            "qmm_get_rows_q4_0", "qmm_get_rows_q8_0", "qmm_get_rows_q2_k", "qmm_get_rows_q4_k", "qmm_get_rows_q6_k")
 
 
@@ -181,6 +181,10 @@ def qmm_matmul_q4_0(w, xq, y, M: int, N: int, K: int, stream=None) -> None:
     _call("qmm_matmul_q4_0", _addr(w), _addr(xq), _addr(y), M, N, K, _stream(stream))
 
 
+def qmm_matmul_q8_0(w, xq, y, M: int, N: int, K: int, stream=None) -> None:
+    _call("qmm_matmul_q8_0", _addr(w), _addr(xq), _addr(y), M, N, K, _stream(stream))
+
+
 def qmm_matmul_q2_k(w, xq8k, y, M: int, N: int, K: int, stream=None) -> None:
     _call("qmm_matmul_q2_k", _addr(w), _addr(xq8k), _addr(y), M, N, K, _stream(stream))
 
@@ -216,7 +220,7 @@ QUANTIZE_X = {"q4_0": qmm_quantize_q8_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_
               "q4_k": qmm_quantize_q8_k, "q6_k": qmm_quantize_q8_k}
 MATVEC = {"q4_0": qmm_matvec_q4_0, "q8_0": qmm_matvec_q8_0, "q2_k": qmm_matvec_q2_k, "q4_k": qmm_matvec_q4_k,
           "q6_k": qmm_matvec_q6_k}
-MATMUL = {"q4_0": qmm_matmul_q4_0, "q2_k": qmm_matmul_q2_k, "q4_k": qmm_matmul_q4_k, "q6_k": qmm_matmul_q6_k}
+MATMUL = {"q4_0": qmm_matmul_q4_0, "q8_0": qmm_matmul_q8_0, "q2_k": qmm_matmul_q2_k, "q4_k": qmm_matmul_q4_k, "q6_k": qmm_matmul_q6_k}
 QUANTIZE_MATVEC = {"q4_0": qmm_quantize_matvec_q4_0, "q8_0": qmm_quantize_matvec_q8_0}
 GET_ROWS = {"q4_0": qmm_get_rows_q4_0, "q8_0": qmm_get_rows_q8_0, "q2_k": qmm_get_rows_q2_k,
             "q4_k": qmm_get_rows_q4_k, "q6_k": qmm_get_rows_q6_k}

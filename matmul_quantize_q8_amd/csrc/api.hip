@@ -23,6 +23,7 @@ hipError_t launch_quantize_matvec_q4_0(const void *w, const float *x, void *xq, 
 hipError_t launch_quantize_matvec_q8_0(const void *w, const float *x, void *xq, float *y, int N, int nb,
                                        hipStream_t st);
 hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st);
+hipError_t launch_matmul_q8_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st);
 int64_t matmul_q4_0_max_blocks();
 hipError_t launch_get_rows(int fmt, const void *w, const int32_t *ids, float *out, int64_t n, int64_t N, int64_t K,
                            int64_t row_bytes, hipStream_t st);
@@ -214,6 +215,11 @@ static qmm_status matmul(mm_launch fn, const void *w, const void *xq, float *y, 
 qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K, void *stream) {
     if (K / 32 > qmm::matmul_q4_0_max_blocks()) return QMM_E_SHAPE;
     return matmul(qmm::launch_matmul_q4_0, w, xq, y, M, N, K, 32, qmm::kQ40Bytes, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_matmul_q8_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+    if (K / 32 > qmm::matmul_q4_0_max_blocks()) return QMM_E_SHAPE;
+    return matmul(qmm::launch_matmul_q8_0, w, xq, y, M, N, K, 32, qmm::kQ80Bytes, qmm::kQ80Bytes, stream);
 }
 
 qmm_status qmm_matmul_q2_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,

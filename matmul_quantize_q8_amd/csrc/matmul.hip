@@ -1,6 +1,7 @@
-// Prefill matmul, Q4_0 weights x Q8_0 activations, on int8 MFMA.
+// Prefill matmul, Q4_0 or Q8_0 weights x Q8_0 activations, on int8 MFMA.
 //
-//   Y[m][n] = sum_b dx[m,b] dw[n,b] I_b[m,n],   I_b = sum_{k<32} q[m,32b+k] (w[n,32b+k]-8)
+//   Y[m][n] = sum_b dx[m,b] dw[n,b] I_b[m,n],   I_b = sum_{k<32} q[m,32b+k] w'[n,32b+k]
+//   (w' = nibble - 8 for Q4_0, the int8 code for Q8_0)
 //
 // Once a weight tile is reused across many tokens the product is a dense
 // contraction (kvad "Batched prefill, and i8mm"; krafla "Batched prompt
@@ -52,6 +53,15 @@
 // f32 array in LDS, where four consecutive rows are one 16-byte read.
 // Output lane layout of a 32x32 MFMA tile: lane l, register r holds row
 // 8(r/4) + 4(l/32) + r%4 and column l%32.
+//
+// Q8_0 weights (minfer Q8_0 kernel: both operands are 34-byte blocks): the
+// weight rows are staged exactly like the activation rows (five chunks, 80
+// bytes per row, so a stage is 20 KB and every wave issues five loads), the
+// B operand is built like the A operand (the same code order per lane half,
+// so the pairing agrees), with no nibble transform; each lane reads its
+// weight rows' two scales from chunk 0 and chunk 2.  |I| <= 32*127*127 <
+// 2^22, so the bias trick holds with F = 1.5*2^23 + I and the store does not
+// rescale.
 #include "qmm_device.h"
 
 #include <type_traits>
@@ -63,19 +73,28 @@ constexpr int BM = 128;                   // tokens per workgroup tile
 constexpr int BN = 128;                   // weight rows per workgroup tile
 constexpr int NT = 256;                   // 4 waves, 2 x 2 of 64 x 64
 constexpr int XC = 5;                     // 16-byte chunks per activation row per stage
-constexpr int WC = 3;                     // per weight row
 constexpr int XQ = BM * XC / kWave;       // 10 wave loads of activation chunks
-constexpr int WQ = BN * WC / kWave;       // 6 of weight chunks
 constexpr int WOFF = BM * XC * 16;        // weight chunks start (bytes into a stage buffer)
-constexpr int STAGE = (BM * XC + BN * WC) * 16;   // 16,384 bytes
-constexpr int PER_WAVE = (XQ + WQ) / 4;   // 4 DMA loads per wave per stage
 constexpr int NBUF = 3;                   // stage buffers: DMA runs two stages ahead
-constexpr int DXF = NBUF * STAGE;         // per-wave f32 dx: [wave][block][64 rows]
-constexpr int LDS_BYTES = DXF + 4 * 2 * 64 * 4;
 constexpr float kBias = 12582912.0f;      // 1.5 * 2^23, bit pattern 0x4B400000
-// segment offsets of the chunks
+// segment offsets of the activation chunks (and of Q8_0 weight chunks)
 constexpr int xchunk(int c) { return c < 4 ? 16 * c : 52; }
-constexpr int wchunk(int c) { return c < 2 ? 16 * c : 20; }
+
+// Per weight format (Q8W: Q8_0 weights, else Q4_0).
+template <bool Q8W> struct WF {
+    static constexpr int WB = Q8W ? kQ80Bytes : kQ40Bytes;   // bytes per weight block
+    static constexpr int WC = Q8W ? 5 : 3;                    // 16-byte chunks per weight row per stage
+    static constexpr int WQ = BN * WC / kWave;                // 10 or 6 wave loads of weight chunks
+    static constexpr int STAGE = (BM * XC + BN * WC) * 16;    // 20,480 or 16,384 bytes
+    static constexpr int PER_WAVE = (XQ + WQ) / 4;            // 5 or 4 DMA loads per wave per stage
+    static constexpr int DXF = NBUF * STAGE;                  // per-wave f32 dx: [wave][block][64 rows]
+    static constexpr int LDS_BYTES = DXF + 4 * 2 * 64 * 4;
+    static constexpr float OUT_SCALE = Q8W ? 1.0f : 0.0625f;  // Q4_0 codes enter as 16*(nib-8)
+    // segment offsets of the weight chunks: Q4_0 rows of 36 bytes in chunks at 0, 16, 20
+    static constexpr int wchunk(int c) { return Q8W ? xchunk(c) : (c < 2 ? 16 * c : 20); }
+    static_assert(XQ * kWave == BM * XC && WQ * kWave == BN * WC && (XQ + WQ) % 4 == 0,
+                  "stage splits into whole wave loads, evenly over the waves");
+};
 }  // namespace mm
 
 // BYTES (4 or 16) per lane from a buffer into LDS: lane i's bytes land at LDS
@@ -104,19 +123,18 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
 // Workgroup barrier that orders LDS accesses but does not wait for
 // outstanding vector-memory loads (the LDS-DMA copies in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-static_assert(mm::XQ * kWave == mm::BM * mm::XC && mm::WQ * kWave == mm::BN * mm::WC &&
-                  (mm::XQ + mm::WQ) % 4 == 0, "stage splits into whole wave loads, evenly over the waves");
-
-__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__restrict__ w,
-                                                          const uint8_t *__restrict__ xq, float *__restrict__ y,
-                                                          int M, int N, int nb, int tiles_m) {
+template <bool Q8W>
+__device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restrict__ w,
+                                            const uint8_t *__restrict__ xq, float *__restrict__ y, int M, int N,
+                                            int nb, int tiles_m) {
     using namespace mm;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+    using F = WF<Q8W>;
+    constexpr int WC = F::WC, WQ = F::WQ, STAGE = F::STAGE, PER_WAVE = F::PER_WAVE, DXF = F::DXF;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = uniform(t >> 6);
     const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
     const int m0 = mt * BM, n0 = nt * BN;
-    const uint32_t xrow = (uint32_t)nb * kQ80Bytes, wrow = (uint32_t)nb * kQ40Bytes;
+    const uint32_t xrow = (uint32_t)nb * kQ80Bytes, wrow = (uint32_t)nb * F::WB;
     const int nst = (nb + 1) >> 1;   // an odd block count leaves a last stage of one block
 
     // DMA: wave load q = w + 4k (k < 4) of a stage is chunk load q of the
@@ -140,7 +158,7 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
             voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (uint32_t)xchunk(c);
         } else {
             const int f = kWave * (q - XQ) + lane, row = f / WC, c = f - WC * row;
-            voff[k] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + (uint32_t)wchunk(c);
+            voff[k] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + (uint32_t)F::wchunk(c);
         }
     }
     // the low half of a generic LDS address is the LDS offset
@@ -150,18 +168,20 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
     auto seg = [&](int s) { return 2 * s - (2 * s + 1 == nb ? 1 : 0); };
     auto dma_load = [&](auto kc, int s, int b) {
         constexpr int k = decltype(kc)::value;
-        const int sx = seg(s) * kQ80Bytes, sw = seg(s) * kQ40Bytes;
+        const int sx = seg(s) * kQ80Bytes, sw = seg(s) * F::WB;
         const uint32_t base = m0w + (uint32_t)(b * STAGE);
         // load 2: activation chunks for waves 0 and 1, weight chunks for 2 and 3
-        const bool isw = k == 2 ? wave >= 2 : k == 3;
+        const bool isw = k == 2 ? wave >= 2 : k >= 3;
         buffer_to_lds<16, 4096 * k>(isw ? wr : xr, base, voff[k], isw ? sw : sx);
     };
-    static_assert(XQ == 10 && WQ == 6 && PER_WAVE == 4, "the load roles above are written for this split");
+    static_assert(XQ == 10 && (WQ == 6 || WQ == 10) && PER_WAVE == (XQ + WQ) / 4,
+                  "the load roles above are written for these splits");
     auto dma = [&](int s, int b) {
         dma_load(std::integral_constant<int, 0>(), s, b);
         dma_load(std::integral_constant<int, 1>(), s, b);
         dma_load(std::integral_constant<int, 2>(), s, b);
         dma_load(std::integral_constant<int, 3>(), s, b);
+        if constexpr (PER_WAVE == 5) dma_load(std::integral_constant<int, 4>(), s, b);
     };
 
     const int wm = wave & 1, wn = wave >> 1;
@@ -169,6 +189,7 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
     const int xa = 16 * XC * (64 * wm + lr);             // A row 64wm+lr (tile i: +32 rows)
     const int xa_main = xa + (lh ? 0 : 16);              // block 0: chunk 1 (half 0) or 0 (half 1); block 1: +32
     const int wb = WOFF + 16 * WC * (64 * wn + lr);      // B row 64wn+lr (tile j: +32 rows)
+    const int wb_main = wb + (lh ? 0 : 16);              // Q8_0 weights: as xa_main
     const int xd = 16 * XC * (64 * wm + lane);           // the row whose dx this lane converts
     const int dxw = DXF + 512 * wave;                    // this wave's f32 dx: [block][64 rows 64wm..]
     const uint32_t selA = lh ? 0x03020504u : 0x03020100u;   // half 1: codes 30, 31 into bytes 0, 1
@@ -234,10 +255,16 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
     };
 
     // Chunks of one stage for this lane: per A tile the block-0 and block-1
-    // main chunks and chunk 4; per B tile the three weight chunks.
-    struct Raw {
+    // main chunks and chunk 4; per B tile the three Q4_0 weight chunks, or for
+    // Q8_0 weights the same three chunks as for A plus the two scale dwords.
+    struct RawQ4 {
         uint4 a0[2], a1[2], a4[2], w0[2], w1[2], w2[2];
     };
+    struct RawQ8 {
+        uint4 a0[2], a1[2], a4[2], b0[2], b1[2], b4[2];
+        uint32_t s0[2], s2[2];
+    };
+    using Raw = std::conditional_t<Q8W, RawQ8, RawQ4>;
     struct Ops {
         v4i a[2], b[2];
         float dw[2], nb[2];
@@ -251,9 +278,17 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            r.w0[j] = rd16(sb + wb + 16 * WC * 32 * j);
-            r.w1[j] = rd16(sb + wb + 16 + 16 * WC * 32 * j);
-            r.w2[j] = rd16(sb + wb + 32 + 16 * WC * 32 * j);
+            if constexpr (Q8W) {
+                r.b0[j] = rd16(sb + wb_main + 16 * WC * 32 * j);
+                r.b1[j] = rd16(sb + wb_main + 32 + 16 * WC * 32 * j);
+                r.b4[j] = rd16(sb + wb + 64 + 16 * WC * 32 * j);
+                r.s0[j] = rd4(sb + wb + 16 * WC * 32 * j);
+                r.s2[j] = rd4(sb + wb + 32 + 16 * WC * 32 * j);
+            } else {
+                r.w0[j] = rd16(sb + wb + 16 * WC * 32 * j);
+                r.w1[j] = rd16(sb + wb + 16 + 16 * WC * 32 * j);
+                r.w2[j] = rd16(sb + wb + 32 + 16 * WC * 32 * j);
+            }
         }
     };
     auto set_scale = [&](Ops &o, int j, float dw) {
@@ -271,11 +306,17 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint4 c0 = r.w0[j];
-            const uint32_t P = __builtin_amdgcn_perm(r.w1[j].x, c0.x, 0x03020504u);   // nibble bytes 14, 15, 0, 1
-            const uint32_t Pm = __builtin_amdgcn_perm(P << 4, P, selB);
-            o.b[j] = v4i{(int)nib(Pm), (int)nib(c0.y << shHi), (int)nib(c0.z << shHi), (int)nib(c0.w << shHi)};
-            set_scale(o, j, absent ? 0.0f : half_lo(c0.x));
+            if constexpr (Q8W) {
+                const uint4 c = r.b0[j];
+                o.b[j] = v4i{(int)__builtin_amdgcn_perm(r.b1[j].x, c.x, selA), (int)c.y, (int)c.z, (int)c.w};
+                set_scale(o, j, absent ? 0.0f : half_lo(r.s0[j]));
+            } else {
+                const uint4 c0 = r.w0[j];
+                const uint32_t P = __builtin_amdgcn_perm(r.w1[j].x, c0.x, 0x03020504u);   // nibble bytes 14, 15, 0, 1
+                const uint32_t Pm = __builtin_amdgcn_perm(P << 4, P, selB);
+                o.b[j] = v4i{(int)nib(Pm), (int)nib(c0.y << shHi), (int)nib(c0.z << shHi), (int)nib(c0.w << shHi)};
+                set_scale(o, j, absent ? 0.0f : half_lo(c0.x));
+            }
         }
     };
     auto build1 = [&](const Raw &r, Ops &o) {
@@ -287,9 +328,17 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint4 c2 = r.w2[j];   // nibble bytes 0..15 of block 1
-            o.b[j] = v4i{(int)nib(c2.w << shLo), (int)nib(c2.x << shHi), (int)nib(c2.y << shHi), (int)nib(c2.z << shHi)};
-            set_scale(o, j, half_hi(r.w1[j].x));
+            if constexpr (Q8W) {
+                const uint4 c = r.b1[j];
+                const uint32_t d0 = lh ? r.b4[j].w : c.x;
+                o.b[j] = v4i{(int)d0, (int)c.y, (int)c.z, (int)c.w};
+                set_scale(o, j, half_hi(r.s2[j]));
+            } else {
+                const uint4 c2 = r.w2[j];   // nibble bytes 0..15 of block 1
+                o.b[j] = v4i{(int)nib(c2.w << shLo), (int)nib(c2.x << shHi), (int)nib(c2.y << shHi),
+                             (int)nib(c2.z << shHi)};
+                set_scale(o, j, half_hi(r.w1[j].x));
+            }
         }
     };
 
@@ -336,6 +385,7 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
         load_dx(1, 1, dxb);
         __builtin_amdgcn_sched_barrier(0);
         fold(d0, 0, 0, dxa, o1.dw[0], o1.nb[0]);
+        if constexpr (PER_WAVE == 5) dma_load(std::integral_constant<int, 4>(), sd, bd);
         __builtin_amdgcn_sched_barrier(0);
         d0 = mfma(o1.a[1], o1.b[0]);
         __builtin_amdgcn_sched_barrier(0);
@@ -355,10 +405,12 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
     // DMA of stage s+2 then fills.  The last two steps have no stage s+2 and
     // copy the last stage again into that idle buffer instead, so that every
     // step issues the same 4 loads and waits for the same count.
-    static_assert(PER_WAVE == 4, "the wait below counts 4 loads per stage");
     auto step = [&](int s, auto bc) {
         constexpr int b = decltype(bc)::value;
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        if constexpr (PER_WAVE == 5)
+            asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         lds_barrier();
         compute(lds + b * STAGE, 2 * s + 1 == nb, min(s + 2, nst - 1), (b + 2) % NBUF);
     };
@@ -382,9 +434,23 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (m < M) y[(int64_t)m * N + n] = acc[i][j][r] * 0.0625f;
+                if (m < M) y[(int64_t)m * N + n] = acc[i][j][r] * F::OUT_SCALE;
             }
         }
+}
+
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__restrict__ w,
+                                                          const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                          int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<false>::LDS_BYTES];
+    matmul_body<false>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q8_0(const uint8_t *__restrict__ w,
+                                                          const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                          int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<true>::LDS_BYTES];
+    matmul_body<true>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 // K = 32: one block per row, too short for the two-block stages above (the
@@ -408,13 +474,29 @@ __global__ __launch_bounds__(256) void k_matmul_q4_0_one_block(const uint8_t *__
     y[o] = (float)isum * dw * dx;
 }
 
+__global__ __launch_bounds__(256) void k_matmul_q8_0_one_block(const uint8_t *__restrict__ w,
+                                                               const uint8_t *__restrict__ xq,
+                                                               float *__restrict__ y, int M, int N) {
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (o >= (int64_t)M * N) return;
+    const int m = (int)(o / N), n = (int)(o - (int64_t)m * N);
+    const uint8_t *xb = xq + (int64_t)m * kQ80Bytes;
+    const uint8_t *wb = w + (int64_t)n * kQ80Bytes;
+    int isum = 0;
+    for (int j = 0; j < 32; ++j) isum += (int)(int8_t)xb[2 + j] * (int)(int8_t)wb[2 + j];
+    const float dx = f16_bits_to_f32((uint32_t)xb[0] | (uint32_t)xb[1] << 8);
+    const float dw = f16_bits_to_f32((uint32_t)wb[0] | (uint32_t)wb[1] << 8);
+    y[o] = (float)isum * dw * dx;
+}
+
 // Largest block count whose tile offsets fit the 32-bit buffer offsets
-// (128 activation rows of nb * 34 bytes).
+// (128 activation or Q8_0 weight rows of nb * 34 bytes).
 constexpr int64_t kMatmulMaxBlocks = (((int64_t)1 << 31) - 1) / (mm::BM * kQ80Bytes);
 
 int64_t matmul_q4_0_max_blocks() { return kMatmulMaxBlocks; }
 
-hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+template <bool Q8W>
+static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
     if (nb > kMatmulMaxBlocks) return hipErrorInvalidValue;
@@ -422,13 +504,23 @@ hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, in
         const int64_t outs = (int64_t)M * N;
         const int64_t grid = (outs + 255) / 256;
         if (grid > 0x7fffffff) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_matmul_q4_0_one_block, dim3((unsigned)grid), dim3(256), 0, st, wp, xp, y, M, N);
+        hipLaunchKernelGGL(Q8W ? k_matmul_q8_0_one_block : k_matmul_q4_0_one_block, dim3((unsigned)grid), dim3(256),
+                           0, st, wp, xp, y, M, N);
         return hipGetLastError();
     }
     int tiles_m = (M + mm::BM - 1) / mm::BM;
     const int64_t tiles = (int64_t)tiles_m * ((N + mm::BN - 1) / mm::BN);
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
-    return hipLaunchKernel((const void *)k_matmul_q4_0, dim3((unsigned)tiles), dim3(mm::NT), args, 0, st);
+    return hipLaunchKernel(Q8W ? (const void *)k_matmul_q8_0 : (const void *)k_matmul_q4_0, dim3((unsigned)tiles),
+                           dim3(mm::NT), args, 0, st);
+}
+
+hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    return launch_mm<false>(w, xq, y, M, N, nb, st);
+}
+
+hipError_t launch_matmul_q8_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    return launch_mm<true>(w, xq, y, M, N, nb, st);
 }
 
 }  // namespace qmm

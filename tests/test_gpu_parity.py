@@ -278,6 +278,9 @@ MATMUL_CASES = [
     # even block counts (the dword-plane kernel): 1..7 stages, ragged tiles
     ("q4_0", 1, 129, 64), ("q4_0", 131, 255, 128), ("q4_0", 70, 130, 192), ("q4_0", 257, 129, 256),
     ("q4_0", 3, 300, 320), ("q4_0", 200, 100, 448),
+    ("q8_0", 1, 8, 32), ("q8_0", 37, 200, 1024), ("q8_0", 128, 128, 4096), ("q8_0", 130, 129, 160),
+    ("q8_0", 5, 3, 96), ("q8_0", 131, 255, 128), ("q8_0", 257, 129, 256), ("q8_0", 300, 700, 2080),
+    ("q8_0", 3, 300, 320), ("q8_0", 129, 257, 64),
     ("q2_k", 1, 8, 256), ("q2_k", 9, 70, 1024), ("q2_k", 33, 130, 4096),
     ("q4_k", 1, 8, 256), ("q4_k", 9, 70, 1024), ("q4_k", 33, 130, 4096),
     ("q6_k", 1, 8, 256), ("q6_k", 9, 70, 1024), ("q6_k", 5, 33, 1280),
@@ -315,6 +318,27 @@ def test_matmul_prefill_full_size_sampled(env):
     ni = np.concatenate([ni, np.tile(np.arange(0, N, 64), len(edge_m)), np.repeat(edge_n, len(range(0, M, 7)))])
     ref, mag = orc.matmul_sampled("q4_0", wq, xq, mi, ni, K)
     _check(y[mi, ni], ref, mag, "prefill sampled")
+
+
+def test_matmul_q8_0_full_size_sampled(env):
+    """A 2048 x 4096 x 4096 Q8_0 prefill, checked on sampled outputs and whole
+    rows and columns at the tile edges."""
+    torch, q, orc = env
+    M, N, K = 2048, 4096, 4096
+    _say("matmul q8_0 full", M, N, K)
+    wq = orc.quantize_q8_0(synth.weights(N, K, config=8))
+    xq = orc.quantize_q8_0(synth.activations(M, K, config=8))
+    y = _run_matmul(env, "q8_0", wq, xq, M, N, K)
+    assert np.isfinite(y).all()
+    rng = synth.splitmix64(78, 0, 20000)
+    mi = (rng[:10000] % np.uint64(M)).astype(np.int64)
+    ni = (rng[10000:] % np.uint64(N)).astype(np.int64)
+    edge_m = np.array([0, 127, 128, 2047])
+    edge_n = np.array([0, 31, 32, 127, 128, 4095])
+    mi = np.concatenate([mi, np.repeat(edge_m, N // 16), np.tile(np.arange(0, M, 5), len(edge_n))])
+    ni = np.concatenate([ni, np.tile(np.arange(0, N, 16), len(edge_m)), np.repeat(edge_n, len(range(0, M, 5)))])
+    ref, mag = orc.matmul_sampled("q8_0", wq, xq, mi, ni, K)
+    _check(y[mi, ni], ref, mag, "q8_0 prefill sampled")
 
 
 def test_matmul_rows_equal_matvec(env):

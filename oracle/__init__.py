@@ -20,10 +20,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmm_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q4_0, Q8_0, Q2_K, Q4_K, Q6_K = 0, 1, 2, 3, 4
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q2_k": 84, "q8_k": 292, "q4_k": 144, "q6_k": 210}
-BLOCK_VALUES = {"q4_0": 32, "q8_0": 32, "q2_k": 256, "q8_k": 256, "q4_k": 256, "q6_k": 256}
-FMT_ID = {"q4_0": Q4_0, "q8_0": Q8_0, "q2_k": Q2_K, "q4_k": Q4_K, "q6_k": Q6_K}
+Q4_0, Q8_0, Q2_K, Q4_K, Q6_K, Q4_1, Q5_0, Q5_1 = 0, 1, 2, 3, 4, 5, 6, 7
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q2_k": 84, "q8_k": 292, "q4_k": 144, "q6_k": 210,
+               "q4_1": 20, "q5_0": 22, "q5_1": 24}
+BLOCK_VALUES = {"q4_0": 32, "q8_0": 32, "q2_k": 256, "q8_k": 256, "q4_k": 256, "q6_k": 256,
+                "q4_1": 32, "q5_0": 32, "q5_1": 32}
+FMT_ID = {"q4_0": Q4_0, "q8_0": Q8_0, "q2_k": Q2_K, "q4_k": Q4_K, "q6_k": Q6_K, "q4_1": Q4_1, "q5_0": Q5_0,
+          "q5_1": Q5_1}
 K_QUANTS = ("q2_k", "q4_k", "q6_k")
 
 _lib = None
@@ -50,7 +53,8 @@ def lib():
         L.orc_f16_to_f32.argtypes = [U16]
         L.orc_f16_to_f32.restype = ctypes.c_float
         for name in ("orc_quantize_q8_0", "orc_quantize_q8_k", "orc_quantize_q4_0_w", "orc_quantize_q2_k_w",
-                     "orc_quantize_q4_k_w", "orc_quantize_q6_k_w",
+                     "orc_quantize_q4_k_w", "orc_quantize_q6_k_w", "orc_quantize_q4_1_w", "orc_quantize_q5_0_w",
+                     "orc_quantize_q5_1_w", "orc_dequantize_q4_1", "orc_dequantize_q5_0", "orc_dequantize_q5_1",
                      "orc_dequantize_q8_0", "orc_dequantize_q4_0", "orc_dequantize_q2_k", "orc_dequantize_q8_k",
                      "orc_dequantize_q4_k", "orc_dequantize_q6_k"):
             getattr(L, name).argtypes = [P, P, I64, I64]
@@ -152,9 +156,25 @@ def quantize_q6_k_w(w) -> np.ndarray:
     return _quant("orc_quantize_q6_k_w", "q6_k", w)
 
 
+def quantize_q4_1_w(w) -> np.ndarray:
+    """f32 weights [N][K] -> Q4_1 bytes [N][K/32*20]."""
+    return _quant("orc_quantize_q4_1_w", "q4_1", w)
+
+
+def quantize_q5_0_w(w) -> np.ndarray:
+    """f32 weights [N][K] -> Q5_0 bytes [N][K/32*22]."""
+    return _quant("orc_quantize_q5_0_w", "q5_0", w)
+
+
+def quantize_q5_1_w(w) -> np.ndarray:
+    """f32 weights [N][K] -> Q5_1 bytes [N][K/32*24]."""
+    return _quant("orc_quantize_q5_1_w", "q5_1", w)
+
+
 def quantize_w(fmt: str, w) -> np.ndarray:
     return {"q4_0": quantize_q4_0_w, "q8_0": quantize_q8_0, "q2_k": quantize_q2_k_w,
-            "q4_k": quantize_q4_k_w, "q6_k": quantize_q6_k_w}[fmt](w)
+            "q4_k": quantize_q4_k_w, "q6_k": quantize_q6_k_w, "q4_1": quantize_q4_1_w,
+            "q5_0": quantize_q5_0_w, "q5_1": quantize_q5_1_w}[fmt](w)
 
 
 def act_format(fmt: str) -> str:

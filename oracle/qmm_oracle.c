@@ -43,6 +43,9 @@
 #define Q8_0_BYTES 34
 #define Q2_K_BYTES 84
 #define Q8_K_BYTES 292
+#define Q4_1_BYTES 20
+#define Q5_0_BYTES 22
+#define Q5_1_BYTES 24
 #define Q4_K_BYTES 144
 #define Q6_K_BYTES 210
 
@@ -280,6 +283,106 @@ void orc_quantize_q2_k_w(const float *w, uint8_t *out, int64_t N, int64_t K) {
         }
     }
 }
+
+/* The 32-value formats with an offset or a fifth bit ([ggml] section 1.1:
+ * the _1 formats add a per-block offset, value = d * q + m; [minfer]: Q5_0 and
+ * Q5_1 add a high-bit plane, 22- and 24-byte blocks).  Field order and bit
+ * order are not on the pages; the reading is GGUF's:
+ *   Q4_1 (20 B): f16 d @0, f16 m @2, qs[16] @4            value = d * q + m,        q in [0, 15]
+ *   Q5_0 (22 B): f16 d @0, qh[4] @2, qs[16] @6            value = d * (q - 16),     q in [0, 31]
+ *   Q5_1 (24 B): f16 d @0, f16 m @2, qh[4] @4, qs[16] @8  value = d * q + m,        q in [0, 31]
+ * qs byte j holds value j's low four bits (low nibble) and value j+16's (high
+ * nibble), as in Q4_0; bit j of the little-endian 32-bit qh is value j's
+ * fifth bit. */
+static int q41_code(const uint8_t *blk, int j) {
+    uint8_t b = blk[4 + (j & 15)];
+    return j < 16 ? (b & 15) : (b >> 4);
+}
+static int q5_code(const uint8_t *qh4, const uint8_t *qs, int j) {
+    uint32_t qh = (uint32_t)qh4[0] | ((uint32_t)qh4[1] << 8) | ((uint32_t)qh4[2] << 16) | ((uint32_t)qh4[3] << 24);
+    uint8_t b = qs[j & 15];
+    int lo = j < 16 ? (b & 15) : (b >> 4);
+    return lo | (int)(((qh >> j) & 1u) << 4);
+}
+
+/* Value j of a block of format fmt (4 = Q4_1, 5 = Q5_0, 6 = Q5_1), exact in double. */
+static double val32(int fmt, const uint8_t *blk, int j) {
+    double d = rd_f16(blk);
+    if (fmt == 5) return d * (double)(q5_code(blk + 2, blk + 6, j) - 16);
+    double m = rd_f16(blk + 2);
+    if (fmt == 4) return d * (double)q41_code(blk, j) + m;
+    return d * (double)q5_code(blk + 4, blk + 8, j) + m;
+}
+
+/* Weight quantizers for the three (test data; the pages give no rule):
+ *   Q4_1 / Q5_1: lo = min x, hi = max x over the block; d = (hi - lo) / L
+ *     (L = 15 or 31), m = lo (both stored f16); q = clamp(round((x - m) / d),
+ *     0, L) with the stored d and m, 0 if d is 0.
+ *   Q5_0: Q4_0's rule with 32 levels: the value of largest magnitude (first
+ *     on ties) lands on code 0, d = max / -16; q = clamp(round(x / d) + 16, 0,
+ *     31), 16 if d is 0. */
+static void quant_block32(int fmt, const float *xb, uint8_t *ob) {
+    int code[QK];
+    if (fmt == 5) {
+        float amax = 0.0f, mx = 0.0f;
+        for (int j = 0; j < QK; ++j) {
+            float a = fabsf(xb[j]);
+            if (a > amax) { amax = a; mx = xb[j]; }
+        }
+        float d = (amax != 0.0f) ? mx / -16.0f : 0.0f;
+        wr_f16(ob, d);
+        for (int j = 0; j < QK; ++j) {
+            int c = 16;
+            if (d != 0.0f) c = (int)rne(xb[j] / d) + 16;
+            code[j] = c < 0 ? 0 : (c > 31 ? 31 : c);
+        }
+    } else {
+        int L = (fmt == 4) ? 15 : 31;
+        float lo = xb[0], hi = xb[0];
+        for (int j = 1; j < QK; ++j) {
+            if (xb[j] < lo) lo = xb[j];
+            if (xb[j] > hi) hi = xb[j];
+        }
+        wr_f16(ob, (hi - lo) / (float)L);
+        wr_f16(ob + 2, lo);
+        float dh = rd_f16(ob), mh = rd_f16(ob + 2);
+        for (int j = 0; j < QK; ++j) {
+            int c = 0;
+            if (dh != 0.0f) c = (int)rne((xb[j] - mh) / dh);
+            code[j] = c < 0 ? 0 : (c > L ? L : c);
+        }
+    }
+    uint8_t *qs = ob + (fmt == 4 ? 4 : (fmt == 5 ? 6 : 8));
+    for (int j = 0; j < 16; ++j) qs[j] = (uint8_t)((code[j] & 15) | ((code[j + 16] & 15) << 4));
+    if (fmt != 4) {
+        uint32_t qh = 0;
+        for (int j = 0; j < QK; ++j) qh |= (uint32_t)((code[j] >> 4) & 1) << j;
+        uint8_t *q4 = ob + (fmt == 5 ? 2 : 4);
+        for (int k = 0; k < 4; ++k) q4[k] = (uint8_t)(qh >> (8 * k));
+    }
+}
+
+static int bytes32(int fmt) { return fmt == 4 ? Q4_1_BYTES : (fmt == 5 ? Q5_0_BYTES : Q5_1_BYTES); }
+
+static void quantize32_w(int fmt, const float *w, uint8_t *out, int64_t N, int64_t K) {
+    int64_t nb = K / QK;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < nb; ++b) quant_block32(fmt, w + n * K + b * QK, out + (n * nb + b) * bytes32(fmt));
+}
+void orc_quantize_q4_1_w(const float *w, uint8_t *out, int64_t N, int64_t K) { quantize32_w(4, w, out, N, K); }
+void orc_quantize_q5_0_w(const float *w, uint8_t *out, int64_t N, int64_t K) { quantize32_w(5, w, out, N, K); }
+void orc_quantize_q5_1_w(const float *w, uint8_t *out, int64_t N, int64_t K) { quantize32_w(6, w, out, N, K); }
+
+static void dequantize32(int fmt, const uint8_t *blk, double *out, int64_t rows, int64_t K) {
+    int64_t nb = K / QK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b)
+            for (int j = 0; j < QK; ++j)
+                out[r * K + b * QK + j] = val32(fmt, blk + (r * nb + b) * bytes32(fmt), j);
+}
+void orc_dequantize_q4_1(const uint8_t *b, double *o, int64_t rows, int64_t K) { dequantize32(4, b, o, rows, K); }
+void orc_dequantize_q5_0(const uint8_t *b, double *o, int64_t rows, int64_t K) { dequantize32(5, b, o, rows, K); }
+void orc_dequantize_q5_1(const uint8_t *b, double *o, int64_t rows, int64_t K) { dequantize32(6, b, o, rows, K); }
 
 /* Q4_K layout ([minfer] block.rs sizes: 144 bytes; the K-quant dot kernel
  * walked in "The payoff": f16 d @0, f16 dmin @2, 12 bytes of scales @4, 128
@@ -660,14 +763,42 @@ static void dot_q6_k_q8_k(const uint8_t *w, const uint8_t *x, int64_t ns, double
     if (mag) *mag = a;
 }
 
-enum { ORC_Q4_0 = 0, ORC_Q8_0 = 1, ORC_Q2_K = 2, ORC_Q4_K = 3, ORC_Q6_K = 4 };
+/* Q4_1 / Q5_0 / Q5_1 weights x Q8_0: the plain sum of decoded products per
+ * block, grouped as the format is (scale x integer sum, plus the offset times
+ * the activation's code sum for the _1 formats):
+ *   t_b = d_w d_x sum_j q'_j x_j + m d_x sum_j x_j,   q' = q (Q5_0: q - 16). */
+static void dot_32(int fmt, const uint8_t *w, const uint8_t *x, int64_t nb, double *y, double *mag) {
+    double s = 0.0, a = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *wb = w + b * bytes32(fmt), *xb = x + b * Q8_0_BYTES;
+        double dw = rd_f16(wb), dx = rd_f16(xb), m = (fmt == 5) ? 0.0 : rd_f16(wb + 2);
+        int32_t isum = 0, xsum = 0;
+        double aa = 0.0;
+        for (int j = 0; j < QK; ++j) {
+            int qx = (int8_t)xb[2 + j];
+            int q = (fmt == 4) ? q41_code(wb, j) : q5_code(wb + (fmt == 5 ? 2 : 4), wb + (fmt == 5 ? 6 : 8), j);
+            if (fmt == 5) q -= 16;
+            isum += q * qx;
+            xsum += qx;
+            aa += fabs(val32(fmt, wb, j)) * fabs(dx * qx);
+        }
+        s += dw * dx * (double)isum + m * dx * (double)xsum;
+        a += aa;
+    }
+    *y = s;
+    if (mag) *mag = a;
+}
+
+enum { ORC_Q4_0 = 0, ORC_Q8_0 = 1, ORC_Q2_K = 2, ORC_Q4_K = 3, ORC_Q6_K = 4, ORC_Q4_1 = 5, ORC_Q5_0 = 6,
+       ORC_Q5_1 = 7 };
 
 static void dot_any(int fmt, const uint8_t *w, const uint8_t *x, int64_t K, double *y, double *mag) {
     if (fmt == ORC_Q4_0) dot_q4_0_q8_0(w, x, K / QK, y, mag);
     else if (fmt == ORC_Q8_0) dot_q8_0_q8_0(w, x, K / QK, y, mag);
     else if (fmt == ORC_Q2_K) dot_q2_k_q8_k(w, x, K / QKK, y, mag);
     else if (fmt == ORC_Q4_K) dot_q4_k_q8_k(w, x, K / QKK, y, mag);
-    else dot_q6_k_q8_k(w, x, K / QKK, y, mag);
+    else if (fmt == ORC_Q6_K) dot_q6_k_q8_k(w, x, K / QKK, y, mag);
+    else dot_32(fmt - 1, w, x, K / QK, y, mag);     /* 5, 6, 7 -> the local ids 4, 5, 6 */
 }
 
 static int64_t w_row_bytes(int fmt, int64_t K) {
@@ -675,11 +806,12 @@ static int64_t w_row_bytes(int fmt, int64_t K) {
     if (fmt == ORC_Q8_0) return K / QK * Q8_0_BYTES;
     if (fmt == ORC_Q2_K) return K / QKK * Q2_K_BYTES;
     if (fmt == ORC_Q4_K) return K / QKK * Q4_K_BYTES;
-    return K / QKK * Q6_K_BYTES;
+    if (fmt == ORC_Q6_K) return K / QKK * Q6_K_BYTES;
+    return K / QK * bytes32(fmt - 1);
 }
 static int64_t x_row_bytes(int fmt, int64_t K) {
-    if (fmt == ORC_Q4_0 || fmt == ORC_Q8_0) return K / QK * Q8_0_BYTES;
-    return K / QKK * Q8_K_BYTES;
+    if (fmt == ORC_Q2_K || fmt == ORC_Q4_K || fmt == ORC_Q6_K) return K / QKK * Q8_K_BYTES;
+    return K / QK * Q8_0_BYTES;
 }
 
 /* ------------------------------------------------------------------ */
@@ -711,7 +843,8 @@ static void *orc_rows(void *arg) {
 }
 
 /* fmt: 0 = Q4_0 weights x Q8_0, 1 = Q8_0 x Q8_0, 2 = Q2_K x Q8_K,
- * 3 = Q4_K x Q8_K, 4 = Q6_K x Q8_K.
+ * 3 = Q4_K x Q8_K, 4 = Q6_K x Q8_K, 5 = Q4_1 x Q8_0, 6 = Q5_0 x Q8_0,
+ * 7 = Q5_1 x Q8_0.
  * y (f32), y64 (double) and mag (double) are [M][N]; any may be NULL. */
 int orc_matmul(int fmt, const uint8_t *w, const uint8_t *x, float *y, double *y64, double *mag,
                int64_t M, int64_t N, int64_t K, int threads) {
@@ -770,7 +903,8 @@ int orc_get_rows(int fmt, const uint8_t *w, const int32_t *ids, int64_t n, int64
         else if (fmt == ORC_Q8_0) orc_dequantize_q8_0(wr, row, 1, K);
         else if (fmt == ORC_Q2_K) orc_dequantize_q2_k(wr, row, 1, K);
         else if (fmt == ORC_Q4_K) orc_dequantize_q4_k(wr, row, 1, K);
-        else orc_dequantize_q6_k(wr, row, 1, K);
+        else if (fmt == ORC_Q6_K) orc_dequantize_q6_k(wr, row, 1, K);
+        else dequantize32(fmt - 1, wr, row, 1, K);
         for (int64_t i = 0; i < K; ++i) out[t * K + i] = (float)row[i];
     }
     free(row);

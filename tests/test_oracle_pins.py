@@ -201,7 +201,11 @@ def test_block_sizes(orc):
     assert orc.BLOCK_BYTES["q2_k"] == g["q2_k_bytes"]
     assert orc.BLOCK_BYTES["q4_k"] == g["q4_k_bytes"]
     assert orc.BLOCK_BYTES["q6_k"] == g["q6_k_bytes"]
+    assert orc.BLOCK_BYTES["q5_0"] == g["q5_0_bytes"]
+    assert orc.BLOCK_BYTES["q5_1"] == g["q5_1_bytes"]
     w = synth.gaussian_f32((2, 512), 0.02, 6)
+    assert orc.quantize_q5_0_w(w).shape == (2, 16 * g["q5_0_bytes"])
+    assert orc.quantize_q5_1_w(w).shape == (2, 16 * g["q5_1_bytes"])
     assert orc.quantize_q4_k_w(w).shape == (2, 2 * g["q4_k_bytes"])
     assert orc.quantize_q6_k_w(w).shape == (2, 2 * g["q6_k_bytes"])
     assert orc.BLOCK_BYTES["q4_0"] / 32 == g["q4_0_bytes_per_weight"]
@@ -440,6 +444,65 @@ def test_q6_k_quantizer_format_invariants(orc):
 
 
 # ---------------------------------------------------------------------------
+# Q4_1 / Q5_0 / Q5_1: the _1 formats decode as d*q + m (ggml section 1.1), the
+# Q5 formats carry a fifth bit per value (minfer: high-bit planes); field and
+# bit order are readings (GGUF's), checked for consistency.
+# ---------------------------------------------------------------------------
+def _blk32(fmt, d, m, codes):
+    """A block of `fmt` from f16 d, f16 m (ignored by Q5_0) and 32 codes, laid
+    out as the reading says."""
+    nbytes = {"q4_1": 20, "q5_0": 22, "q5_1": 24}[fmt]
+    blk = np.zeros(nbytes, dtype=np.uint8)
+    blk[0:2] = np.array([np.float16(d)], dtype=np.float16).view(np.uint8)
+    if fmt != "q5_0":
+        blk[2:4] = np.array([np.float16(m)], dtype=np.float16).view(np.uint8)
+    qs0 = {"q4_1": 4, "q5_0": 6, "q5_1": 8}[fmt]
+    c = np.asarray(codes, dtype=np.int64)
+    blk[qs0:qs0 + 16] = ((c[:16] & 15) | ((c[16:] & 15) << 4)).astype(np.uint8)
+    if fmt != "q4_1":
+        qh = int(sum(((int(c[j]) >> 4) & 1) << j for j in range(32)))
+        o = 2 if fmt == "q5_0" else 4
+        blk[o:o + 4] = np.array([qh], dtype="<u4").view(np.uint8)
+    return blk
+
+
+@pytest.mark.parametrize("fmt", ["q4_1", "q5_0", "q5_1"])
+def test_32_value_offset_formats_closed_form(orc, fmt):
+    """Q4_1 / Q5_1: value = d * q + m (the per-block offset); Q5_0: value =
+    d * (q - 16); codes use all their bits."""
+    rng = synth.splitmix64(191, 0, 32)
+    L = 15 if fmt == "q4_1" else 31
+    codes = (rng % np.uint64(L + 1)).astype(np.int64)
+    codes[0], codes[31] = L, 0
+    vals = orc.dequantize(fmt, _blk32(fmt, 0.5, -0.25, codes), 32)[0]
+    if fmt == "q5_0":
+        assert np.array_equal(vals, 0.5 * (codes - 16))
+    else:
+        assert np.array_equal(vals, 0.5 * codes - 0.25)
+
+
+@pytest.mark.parametrize("fmt", ["q5_0", "q5_1"])
+@pytest.mark.parametrize("j", [0, 7, 15, 16, 31])
+def test_q5_fifth_bit_position(orc, fmt, j):
+    """Bit j of qh is value j's fifth bit (reading): all nibbles 0, only that
+    bit set, so only value j moves by 16 d."""
+    codes = np.zeros(32, dtype=np.int64)
+    codes[j] = 16
+    vals = orc.dequantize(fmt, _blk32(fmt, 1.0, 0.0, codes), 32)[0]
+    base = -16.0 if fmt == "q5_0" else 0.0
+    assert vals[j] == base + 16.0
+    assert np.all(np.delete(vals, j) == base)
+
+
+@pytest.mark.parametrize("fmt,tol", [("q4_1", 0.12), ("q5_0", 0.06), ("q5_1", 0.05)])
+def test_32_value_quantizers_format_invariants(orc, fmt, tol):
+    """The weight quantizers' rules are not on the pages (parity unpinned)."""
+    w = synth.gaussian_f32((8, 1024), 0.02, 201)
+    vals = orc.dequantize(fmt, orc.quantize_w(fmt, w), 1024)
+    assert np.linalg.norm(vals - w) / np.linalg.norm(w) < tol
+
+
+# ---------------------------------------------------------------------------
 # Products: brute force on decoded values, layout, thread invariance
 # ---------------------------------------------------------------------------
 def _case(fmt, M, N, K, seed):
@@ -460,7 +523,7 @@ def test_single_block_dot_is_exact(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt,K", [("q4_0", 96), ("q8_0", 160), ("q2_k", 512), ("q4_0", 4096), ("q4_k", 512),
-                                   ("q6_k", 768)])
+                                   ("q6_k", 768), ("q4_1", 96), ("q5_0", 160), ("q5_1", 128)])
 def test_matmul_matches_decoded_float64_product(orc, fmt, K):
     M, N = 3, 5
     wq, xq = _case(fmt, M, N, K, 101)
@@ -474,11 +537,13 @@ def test_matmul_matches_decoded_float64_product(orc, fmt, K):
     absprod = np.abs(X) @ np.abs(W).T
     if fmt in ("q2_k", "q4_k"):                       # |d sc q| + |dmin m| >= |d sc q - dmin m|
         assert np.all(r["mag"] >= absprod * (1 - 1e-12))
+    elif fmt in ("q4_1", "q5_1"):                     # sum |(dq + m) x|, in double
+        assert np.all(np.abs(r["mag"] - absprod) <= 1e-12 * absprod)
     else:
         assert np.all(np.abs(r["mag"] - absprod) <= 1e-12 * absprod)
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q2_k", "q4_k", "q6_k"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q2_k", "q4_k", "q6_k", "q4_1", "q5_0", "q5_1"])
 def test_matmul_rows_equal_matvec_and_threads_invariant(orc, fmt):
     M, N, K = 4, 37, 512
     wq, xq = _case(fmt, M, N, K, 111)
@@ -498,7 +563,8 @@ def test_matmul_rows_equal_matvec_and_threads_invariant(orc, fmt):
 # ---------------------------------------------------------------------------
 # Embedding rows (minfer "The embedding matmul")
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("fmt,K", [("q4_0", 96), ("q8_0", 64), ("q2_k", 512), ("q4_k", 256), ("q6_k", 768)])
+@pytest.mark.parametrize("fmt,K", [("q4_0", 96), ("q8_0", 64), ("q2_k", 512), ("q4_k", 256), ("q6_k", 768),
+                                   ("q4_1", 64), ("q5_0", 96), ("q5_1", 32)])
 def test_get_rows_is_the_decoded_row(orc, fmt, K):
     """Row t of the output is row ids[t] of the table, every value the exactly
     decoded one rounded once to f32; repeated ids repeat the row; ids outside
@@ -511,7 +577,7 @@ def test_get_rows_is_the_decoded_row(orc, fmt, K):
     for t, i in enumerate(ids):
         if 0 <= i < N:
             assert np.array_equal(out[t], dec[i].astype(np.float32))
-            assert np.array_equal(out[t].astype(np.float64), dec[i]) or fmt in ("q2_k", "q4_k")
+            assert np.array_equal(out[t].astype(np.float64), dec[i]) or fmt in ("q2_k", "q4_k", "q4_1", "q5_1")
         else:
             assert np.all(np.isnan(out[t]))
     assert np.array_equal(out[0], out[3])

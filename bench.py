@@ -252,7 +252,7 @@ def bench_prefill(args, torch, q, synth):
 # The other decode workloads, one matvec launch each, weights rotated like the
 # headline's: the Q8_0 set of one 7B-style layer (fused QKV and gate+up share
 # the 4096-wide activation, down takes an independent 11008-wide one), Q2_K,
-# and the K-quants of q4_K_M files.  (format, N, K, workload id, weight
+# the K-quants of q4_K_M files and the other 32-value formats.  (format, N, K, workload id, weight
 # stream, activation stream, name); the ids seed the synthetic inputs.
 MATVEC_CONFIGS = [
     ("q8_0", 12288, 4096, 2, 0, 1, "q8_0_qkv_12288x4096"),
@@ -261,6 +261,9 @@ MATVEC_CONFIGS = [
     ("q2_k", 12288, 4096, 3, 0, 1, "q2_k_12288x4096"),
     ("q4_k", 12288, 4096, 5, 0, 1, "q4_k_12288x4096"),
     ("q6_k", 12288, 4096, 6, 0, 1, "q6_k_12288x4096"),
+    ("q4_1", 12288, 4096, 9, 0, 1, "q4_1_12288x4096"),
+    ("q5_0", 12288, 4096, 10, 0, 1, "q5_0_12288x4096"),
+    ("q5_1", 12288, 4096, 11, 0, 1, "q5_1_12288x4096"),
 ]
 
 

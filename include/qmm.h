@@ -36,8 +36,15 @@
  *                            in ql[64h + l + 32(k&1)] (low nibble for k < 2,
  *                            high for k >= 2), high bits at bit 2k of
  *                            qh[32h + l].        value = d*scales[i/16]*(q-32)
- *   (The Q4_K scale packing and the Q6_K layout are GGUF's; the pages give
- *   the block sizes, Q4_K's field and chunk order and its two-term dot.)
+ *   Q4_1  20 B / 32 values : f16 d @0, f16 m @2, uint8 qs[16] @4   value = d*q + m
+ *   Q5_0  22 B / 32 values : f16 d @0, uint32 qh @2, uint8 qs[16] @6
+ *                                                          value = d*(q-16)
+ *   Q5_1  24 B / 32 values : f16 d @0, f16 m @2, uint32 qh @4, uint8 qs[16] @8
+ *                                                          value = d*q + m
+ *                            (qs as Q4_0; bit j of qh is value j's fifth bit)
+ *   (The Q4_K scale packing, the Q6_K layout and the Q4_1 / Q5 field and bit
+ *   order are GGUF's; the pages give the block sizes, Q4_K's field and chunk
+ *   order and its two-term dot, and the d*q + m form of the _1 formats.)
  * A matrix of R rows and K columns in format F is R*K/blk(F) blocks, row-major
  * (row r starts at byte r*(K/blk)*bytes(F)), with no padding.
  *
@@ -130,6 +137,16 @@ qmm_status qmm_quantize_q2_k(const float *w, void *wq, int64_t N, int64_t K, voi
  * the stored f16 values in every step after they are stored.
  *   w : f32 [N][K].   wq : Q4_K (144 B) / Q6_K (210 B) blocks, N*K/256 of them. */
 qmm_status qmm_quantize_q4_k(const float *w, void *wq, int64_t N, int64_t K, void *stream);
+
+/* Q4_1 / Q5_0 / Q5_1 quantization of N rows of K f32 weights (test and
+ * benchmark data; the pages give no quantizer).  Q4_1 / Q5_1, per block of 32:
+ * lo = min x, hi = max x (a zero of either sign as +0), d = (hi - lo)/L with
+ * L = 15 / 31, m = lo, q = clamp(rne((x - m)/d), 0, L) (0 for d = 0); Q5_0:
+ * Q4_0's rule with 32 levels, d = max/-16, q = clamp(rne(x/d) + 16, 0, 31)
+ * (16 for d = 0); d and m are the stored f16 values after they are stored. */
+qmm_status qmm_quantize_q4_1(const float *w, void *wq, int64_t N, int64_t K, void *stream);
+qmm_status qmm_quantize_q5_0(const float *w, void *wq, int64_t N, int64_t K, void *stream);
+qmm_status qmm_quantize_q5_1(const float *w, void *wq, int64_t N, int64_t K, void *stream);
 qmm_status qmm_quantize_q6_k(const float *w, void *wq, int64_t N, int64_t K, void *stream);
 
 /* ---- products ----------------------------------------------------------------
@@ -140,9 +157,10 @@ qmm_status qmm_quantize_q6_k(const float *w, void *wq, int64_t N, int64_t K, voi
  * agree with an exact evaluation within 1e-5 of sum |d_w d_x w_j q_j| per
  * output (krafla "Numerics").  Output is token-major [M][N] f32 (minfer
  * "Pitfalls": out[t*od + o]).
- * Pairing (minfer "Two activation formats, one pairing rule"): Q4_0 and Q8_0
- * weights take Q8_0 activations; the K-quants (Q2_K, Q4_K, Q6_K) take Q8_K
- * activations.  K-quant dots (minfer "The payoff: a K-quant dot kernel,
+ * Pairing (minfer "Two activation formats, one pairing rule"): the 32-value
+ * formats (Q4_0, Q8_0, Q4_1, Q5_0, Q5_1) take Q8_0 activations; the K-quants
+ * (Q2_K, Q4_K, Q6_K) take Q8_K activations.  The _1 formats add the offset
+ * term m*dx*sum q per block.  K-quant dots (minfer "The payoff: a K-quant dot kernel,
  * walked"): per super-block d*d8*sum_s sc_s*sum q x, minus dmin*d8*sum_s m_s *
  * (the bsums of s) for the formats with mins; Q6_K: d*d8*sum_g sc_g *
  * sum (q-32) x. */
@@ -152,6 +170,9 @@ qmm_status qmm_quantize_q6_k(const float *w, void *wq, int64_t N, int64_t K, voi
  *   y  : f32 [N], written. */
 qmm_status qmm_matvec_q8_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
 qmm_status qmm_matvec_q4_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
+qmm_status qmm_matvec_q4_1(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
+qmm_status qmm_matvec_q5_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
+qmm_status qmm_matvec_q5_1(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream);
 qmm_status qmm_matvec_q2_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream);
 qmm_status qmm_matvec_q4_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream);
 qmm_status qmm_matvec_q6_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream);
@@ -181,12 +202,19 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
 /* Prefill matmul, M tokens.
  *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.
  *   y  : f32 [M][N], written.
- * qmm_matmul_q4_0 and qmm_matmul_q8_0 (int8 MFMA) also return QMM_E_SHAPE when
- * 128 rows of Q8_0 activations
- * (128 * K/32 * 34 bytes) exceed 2^31 - 1 bytes, i.e. K > 15,790,304. */
+ * qmm_matmul_q4_0 and qmm_matmul_q8_0 run on int8 MFMA and also return
+ * QMM_E_SHAPE when 128 rows of Q8_0 activations (128 * K/32 * 34 bytes) exceed
+ * 2^31 - 1 bytes, i.e. K > 15,790,304.  The other formats run the matvec
+ * kernel once per token (correct for any M, not tuned for prefill). */
 qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
 qmm_status qmm_matmul_q8_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream);
+qmm_status qmm_matmul_q4_1(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream);
+qmm_status qmm_matmul_q5_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
+                           void *stream);
+qmm_status qmm_matmul_q5_1(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
 qmm_status qmm_matmul_q2_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
@@ -215,6 +243,12 @@ qmm_status qmm_get_rows_q2_k(const void *w, const int32_t *ids, float *out, int6
 qmm_status qmm_get_rows_q4_k(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
                              void *stream);
 qmm_status qmm_get_rows_q6_k(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream);
+qmm_status qmm_get_rows_q4_1(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream);
+qmm_status qmm_get_rows_q5_0(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream);
+qmm_status qmm_get_rows_q5_1(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
                              void *stream);
 
 #ifdef __cplusplus

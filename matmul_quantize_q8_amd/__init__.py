@@ -19,9 +19,13 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmm.so")
 
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q2_k": 84, "q8_k": 292, "q4_k": 144, "q6_k": 210}
-BLOCK_VALUES = {"q4_0": 32, "q8_0": 32, "q2_k": 256, "q8_k": 256, "q4_k": 256, "q6_k": 256}
-ACT_FORMAT = {"q4_0": "q8_0", "q8_0": "q8_0", "q2_k": "q8_k", "q4_k": "q8_k", "q6_k": "q8_k"}
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "q2_k": 84, "q8_k": 292, "q4_k": 144, "q6_k": 210,
+               "q4_1": 20, "q5_0": 22, "q5_1": 24}
+BLOCK_VALUES = {"q4_0": 32, "q8_0": 32, "q2_k": 256, "q8_k": 256, "q4_k": 256, "q6_k": 256,
+                "q4_1": 32, "q5_0": 32, "q5_1": 32}
+ACT_FORMAT = {"q4_0": "q8_0", "q8_0": "q8_0", "q2_k": "q8_k", "q4_k": "q8_k", "q6_k": "q8_k",
+              "q4_1": "q8_0", "q5_0": "q8_0", "q5_1": "q8_0"}
+WEIGHT_FORMATS = ("q4_0", "q8_0", "q4_1", "q5_0", "q5_1", "q2_k", "q4_k", "q6_k")
 
 STATUS = {0: "QMM_OK", 1: "QMM_E_SHAPE", 2: "QMM_E_NULL", 3: "QMM_E_ALIGN", 4: "QMM_E_DEVICE", 5: "QMM_E_LAUNCH"}
 
@@ -51,35 +55,29 @@ def lib() -> ctypes.CDLL:
         L.qmm_status_string.restype = ctypes.c_char_p
         L.qmm_abi_version.argtypes = []
         L.qmm_abi_version.restype = ctypes.c_int
-        for name in ("qmm_quantize_q8_0", "qmm_quantize_q8_k", "qmm_quantize_q4_0", "qmm_quantize_q2_k",
-                     "qmm_quantize_q4_k", "qmm_quantize_q6_k"):
+        for name in ["qmm_quantize_q8_k"] + ["qmm_quantize_" + f for f in WEIGHT_FORMATS]:
             getattr(L, name).argtypes = [P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
-        for name in ("qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k", "qmm_matvec_q4_k",
-                     "qmm_matvec_q6_k"):
+        for name in ["qmm_matvec_" + f for f in WEIGHT_FORMATS]:
             getattr(L, name).argtypes = [P, P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
         for name in ("qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0"):
             getattr(L, name).argtypes = [P, P, P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
-        for name in ("qmm_get_rows_q4_0", "qmm_get_rows_q8_0", "qmm_get_rows_q2_k", "qmm_get_rows_q4_k",
-                     "qmm_get_rows_q6_k"):
+        for name in ["qmm_get_rows_" + f for f in WEIGHT_FORMATS]:
             getattr(L, name).argtypes = [P, P, P, I64, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
-        for name in ("qmm_matmul_q4_0", "qmm_matmul_q8_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k"):
+        for name in ["qmm_matmul_" + f for f in WEIGHT_FORMATS]:
             getattr(L, name).argtypes = [P, P, P, I64, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
 
 
-EXPORTS = ("qmm_status_string", "qmm_abi_version",
-           "qmm_quantize_q8_0", "qmm_quantize_q8_k", "qmm_quantize_q4_0", "qmm_quantize_q2_k",
-           "qmm_quantize_q4_k", "qmm_quantize_q6_k",
-           "qmm_matvec_q8_0", "qmm_matvec_q4_0", "qmm_matvec_q2_k", "qmm_matvec_q4_k", "qmm_matvec_q6_k",
-           "qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0",
-           "qmm_matmul_q4_0", "qmm_matmul_q8_0", "qmm_matmul_q2_k", "qmm_matmul_q4_k", "qmm_matmul_q6_k",
-           "qmm_get_rows_q4_0", "qmm_get_rows_q8_0", "qmm_get_rows_q2_k", "qmm_get_rows_q4_k", "qmm_get_rows_q6_k")
+EXPORTS = tuple(["qmm_status_string", "qmm_abi_version", "qmm_quantize_q8_k",
+                 "qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0"] +
+                [p + f for p in ("qmm_quantize_", "qmm_matvec_", "qmm_matmul_", "qmm_get_rows_")
+                 for f in WEIGHT_FORMATS])
 
 
 def row_bytes(fmt: str, K: int) -> int:
@@ -197,6 +195,39 @@ def qmm_matmul_q6_k(w, xq8k, y, M: int, N: int, K: int, stream=None) -> None:
     _call("qmm_matmul_q6_k", _addr(w), _addr(xq8k), _addr(y), M, N, K, _stream(stream))
 
 
+def _quantize_w(fmt):
+    name = "qmm_quantize_" + fmt
+
+    def quantize(w, wq, N: int, K: int, stream=None) -> None:
+        _call(name, _addr(w), _addr(wq), N, K, _stream(stream))
+    quantize.__name__ = name
+    quantize.__doc__ = f"f32 weights [N][K] -> {fmt.upper()} blocks."
+    return quantize
+
+
+def _matvec(fmt):
+    name = "qmm_matvec_" + fmt
+
+    def matvec(w, xq, y, N: int, K: int, stream=None) -> None:
+        _call(name, _addr(w), _addr(xq), _addr(y), N, K, _stream(stream))
+    matvec.__name__ = name
+    return matvec
+
+
+def _matmul(fmt):
+    name = "qmm_matmul_" + fmt
+
+    def matmul(w, xq, y, M: int, N: int, K: int, stream=None) -> None:
+        _call(name, _addr(w), _addr(xq), _addr(y), M, N, K, _stream(stream))
+    matmul.__name__ = name
+    return matmul
+
+
+qmm_quantize_q4_1, qmm_quantize_q5_0, qmm_quantize_q5_1 = (_quantize_w(f) for f in ("q4_1", "q5_0", "q5_1"))
+qmm_matvec_q4_1, qmm_matvec_q5_0, qmm_matvec_q5_1 = (_matvec(f) for f in ("q4_1", "q5_0", "q5_1"))
+qmm_matmul_q4_1, qmm_matmul_q5_0, qmm_matmul_q5_1 = (_matmul(f) for f in ("q4_1", "q5_0", "q5_1"))
+
+
 def _get_rows(fmt):
     name = "qmm_get_rows_" + fmt
 
@@ -212,15 +243,14 @@ qmm_get_rows_q8_0 = _get_rows("q8_0")
 qmm_get_rows_q2_k = _get_rows("q2_k")
 qmm_get_rows_q4_k = _get_rows("q4_k")
 qmm_get_rows_q6_k = _get_rows("q6_k")
+qmm_get_rows_q4_1 = _get_rows("q4_1")
+qmm_get_rows_q5_0 = _get_rows("q5_0")
+qmm_get_rows_q5_1 = _get_rows("q5_1")
 
 
-QUANTIZE_W = {"q4_0": qmm_quantize_q4_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_quantize_q2_k,
-              "q4_k": qmm_quantize_q4_k, "q6_k": qmm_quantize_q6_k}
-QUANTIZE_X = {"q4_0": qmm_quantize_q8_0, "q8_0": qmm_quantize_q8_0, "q2_k": qmm_quantize_q8_k,
-              "q4_k": qmm_quantize_q8_k, "q6_k": qmm_quantize_q8_k}
-MATVEC = {"q4_0": qmm_matvec_q4_0, "q8_0": qmm_matvec_q8_0, "q2_k": qmm_matvec_q2_k, "q4_k": qmm_matvec_q4_k,
-          "q6_k": qmm_matvec_q6_k}
-MATMUL = {"q4_0": qmm_matmul_q4_0, "q8_0": qmm_matmul_q8_0, "q2_k": qmm_matmul_q2_k, "q4_k": qmm_matmul_q4_k, "q6_k": qmm_matmul_q6_k}
+QUANTIZE_W = {f: globals()["qmm_quantize_" + f] for f in WEIGHT_FORMATS}
+QUANTIZE_X = {f: (qmm_quantize_q8_k if ACT_FORMAT[f] == "q8_k" else qmm_quantize_q8_0) for f in WEIGHT_FORMATS}
+MATVEC = {f: globals()["qmm_matvec_" + f] for f in WEIGHT_FORMATS}
+MATMUL = {f: globals()["qmm_matmul_" + f] for f in WEIGHT_FORMATS}
 QUANTIZE_MATVEC = {"q4_0": qmm_quantize_matvec_q4_0, "q8_0": qmm_quantize_matvec_q8_0}
-GET_ROWS = {"q4_0": qmm_get_rows_q4_0, "q8_0": qmm_get_rows_q8_0, "q2_k": qmm_get_rows_q2_k,
-            "q4_k": qmm_get_rows_q4_k, "q6_k": qmm_get_rows_q6_k}
+GET_ROWS = {f: globals()["qmm_get_rows_" + f] for f in WEIGHT_FORMATS}

@@ -12,6 +12,15 @@ hipError_t launch_quantize_q8_k(const float *x, void *out, int64_t nblocks, hipS
 hipError_t launch_quantize_q4_0(const float *w, void *out, int64_t nblocks, hipStream_t st);
 hipError_t launch_quantize_q2_k(const float *w, void *out, int64_t nblocks, hipStream_t st);
 hipError_t launch_quantize_q4_k(const float *w, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_quantize_q4_1(const float *w, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_quantize_q5_0(const float *w, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_quantize_q5_1(const float *w, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_matvec_q4_1(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st);
+hipError_t launch_matvec_q5_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st);
+hipError_t launch_matvec_q5_1(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st);
+hipError_t launch_matmul_q4_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st);
+hipError_t launch_matmul_q5_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st);
+hipError_t launch_matmul_q5_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st);
 hipError_t launch_quantize_q6_k(const float *w, void *out, int64_t nblocks, hipStream_t st);
 hipError_t launch_matvec_q4_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st);
 hipError_t launch_matvec_q8_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st);
@@ -130,6 +139,18 @@ qmm_status qmm_quantize_q2_k(const float *w, void *wq, int64_t N, int64_t K, voi
     return quantize(qmm::launch_quantize_q2_k, w, wq, N, K, 256, 1024, qmm::kQ2KBytes, stream);
 }
 
+qmm_status qmm_quantize_q4_1(const float *w, void *wq, int64_t N, int64_t K, void *stream) {
+    return quantize(qmm::launch_quantize_q4_1, w, wq, N, K, 32, 128, qmm::kQ41Bytes, stream);
+}
+
+qmm_status qmm_quantize_q5_0(const float *w, void *wq, int64_t N, int64_t K, void *stream) {
+    return quantize(qmm::launch_quantize_q5_0, w, wq, N, K, 32, 128, qmm::kQ50Bytes, stream);
+}
+
+qmm_status qmm_quantize_q5_1(const float *w, void *wq, int64_t N, int64_t K, void *stream) {
+    return quantize(qmm::launch_quantize_q5_1, w, wq, N, K, 32, 128, qmm::kQ51Bytes, stream);
+}
+
 qmm_status qmm_quantize_q4_k(const float *w, void *wq, int64_t N, int64_t K, void *stream) {
     return quantize(qmm::launch_quantize_q4_k, w, wq, N, K, 256, 1024, qmm::kQ4KBytes, stream);
 }
@@ -162,6 +183,18 @@ qmm_status qmm_matvec_q4_0(const void *w, const void *xq, float *y, int64_t N, i
 
 qmm_status qmm_matvec_q2_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream) {
     return matvec(qmm::launch_matvec_q2_k, w, xq8k, y, N, K, 256, qmm::kQ2KBytes, qmm::kQ8KBytes, stream);
+}
+
+qmm_status qmm_matvec_q4_1(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream) {
+    return matvec(qmm::launch_matvec_q4_1, w, xq, y, N, K, 32, qmm::kQ41Bytes, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_matvec_q5_0(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream) {
+    return matvec(qmm::launch_matvec_q5_0, w, xq, y, N, K, 32, qmm::kQ50Bytes, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_matvec_q5_1(const void *w, const void *xq, float *y, int64_t N, int64_t K, void *stream) {
+    return matvec(qmm::launch_matvec_q5_1, w, xq, y, N, K, 32, qmm::kQ51Bytes, qmm::kQ80Bytes, stream);
 }
 
 qmm_status qmm_matvec_q4_k(const void *w, const void *xq8k, float *y, int64_t N, int64_t K, void *stream) {
@@ -222,6 +255,18 @@ qmm_status qmm_matmul_q8_0(const void *w, const void *xq, float *y, int64_t M, i
     return matmul(qmm::launch_matmul_q8_0, w, xq, y, M, N, K, 32, qmm::kQ80Bytes, qmm::kQ80Bytes, stream);
 }
 
+qmm_status qmm_matmul_q4_1(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+    return matmul(qmm::launch_matmul_q4_1, w, xq, y, M, N, K, 32, qmm::kQ41Bytes, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_matmul_q5_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+    return matmul(qmm::launch_matmul_q5_0, w, xq, y, M, N, K, 32, qmm::kQ50Bytes, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_matmul_q5_1(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+    return matmul(qmm::launch_matmul_q5_1, w, xq, y, M, N, K, 32, qmm::kQ51Bytes, qmm::kQ80Bytes, stream);
+}
+
 qmm_status qmm_matmul_q2_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream) {
     return matmul(qmm::launch_matmul_q2_k, w, xq8k, y, M, N, K, 256, qmm::kQ2KBytes, qmm::kQ8KBytes, stream);
@@ -269,6 +314,18 @@ qmm_status qmm_get_rows_q4_k(const void *w, const int32_t *ids, float *out, int6
 qmm_status qmm_get_rows_q6_k(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
                              void *stream) {
     return get_rows(qmm::F_Q6_K, w, ids, out, n_ids, N, K, 256, qmm::kQ6KBytes, stream);
+}
+qmm_status qmm_get_rows_q4_1(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream) {
+    return get_rows(qmm::F_Q4_1, w, ids, out, n_ids, N, K, 32, qmm::kQ41Bytes, stream);
+}
+qmm_status qmm_get_rows_q5_0(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream) {
+    return get_rows(qmm::F_Q5_0, w, ids, out, n_ids, N, K, 32, qmm::kQ50Bytes, stream);
+}
+qmm_status qmm_get_rows_q5_1(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
+                             void *stream) {
+    return get_rows(qmm::F_Q5_1, w, ids, out, n_ids, N, K, 32, qmm::kQ51Bytes, stream);
 }
 
 }  // extern "C"

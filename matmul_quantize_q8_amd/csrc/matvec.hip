@@ -47,6 +47,9 @@ template <> struct FmtBytes<F_Q8_0> { static constexpr int BB = kQ80Bytes, XB = 
 template <> struct FmtBytes<F_Q2_K> { static constexpr int BB = kQ2KBytes, XB = kQ8KBytes; };
 template <> struct FmtBytes<F_Q4_K> { static constexpr int BB = kQ4KBytes, XB = kQ8KBytes; };
 template <> struct FmtBytes<F_Q6_K> { static constexpr int BB = kQ6KBytes, XB = kQ8KBytes; };
+template <> struct FmtBytes<F_Q4_1> { static constexpr int BB = kQ41Bytes, XB = kQ80Bytes; };
+template <> struct FmtBytes<F_Q5_0> { static constexpr int BB = kQ50Bytes, XB = kQ80Bytes; };
+template <> struct FmtBytes<F_Q5_1> { static constexpr int BB = kQ51Bytes, XB = kQ80Bytes; };
 
 // A unit is what one lane handles per row: P blocks (P = 2 paired, 1 single)
 // of Q4_0 / Q8_0, or a quarter (64 values) of a K-quant super-block.
@@ -345,6 +348,114 @@ __device__ __forceinline__ float unit_dot<F_Q6_K, false>(const uint8_t *sl, uint
         V += sc * (s - 32 * x.bs[k]);
     }
     return fmaf(f16_bits_to_f32(dbits) * x.d, (float)V, acc);
+}
+
+// --- Q4_1 / Q5_0 / Q5_1 (ggml section 1.1: the _1 formats add a per-block
+// offset, value = d*q + m; minfer: the Q5 formats add a fifth-bit plane) --------
+// One block given as dwords of its fields: the codes of values 4k..4k+3 and
+// 16+4k..16+4k+3 come from qs dword k (low / high nibbles) and, for the Q5
+// formats, bits 4k.. and 16+4k.. of qh; returns sum_j q_j x_j.
+template <bool Q5>
+__device__ __forceinline__ int block32_isum(const uint32_t (&qs)[4], uint32_t qh, const int *x) {
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t lo = qs[k] & 0x0f0f0f0fu, hi = (qs[k] >> 4) & 0x0f0f0f0fu;
+        if constexpr (Q5) {
+            lo |= bits_to_bytes(__builtin_amdgcn_ubfe(qh, 4 * k, 4)) << 4;
+            hi |= bits_to_bytes(__builtin_amdgcn_ubfe(qh, 16 + 4 * k, 4)) << 4;
+        }
+        s = dot4((int)lo, x[k], s);
+        s = dot4((int)hi, x[k + 4], s);
+    }
+    return s;
+}
+
+// t = dw dx I (+ m dx S for the _1 formats); S = sum of the block's
+// activation codes = sx8 / 8; Q5_0's codes carry +16: I = sum q x - 16 S.
+template <int F>
+__device__ __forceinline__ float block32_term(uint32_t dm, const uint32_t (&qs)[4], uint32_t qh, const int *x,
+                                              float dx, int sx8, float acc) {
+    constexpr bool Q5 = F != F_Q4_1;
+    int I = block32_isum<Q5>(qs, qh, x);
+    const float dw = f16_bits_to_f32(dm);
+    if constexpr (F == F_Q5_0) {
+        I -= 2 * sx8;
+        return fmaf(dw * dx, (float)I, acc);
+    } else {
+        acc = fmaf(dw * dx, (float)I, acc);
+        return fmaf(f16_bits_to_f32(dm >> 16) * dx, (float)(sx8 >> 3), acc);
+    }
+}
+
+// Fields of the block at a 2-byte aligned LDS offset o: d (and m) dword, qh, qs.
+template <int F>
+__device__ __forceinline__ void block32_fields(const uint8_t *sl, uint32_t o, uint32_t &dm, uint32_t &qh,
+                                               uint32_t (&qs)[4]) {
+    // Q4_1 (20 bytes) and Q5_1 (24 bytes) blocks are 4-byte aligned in a
+    // row, and rows land in LDS at their global alignment: direct reads.
+    if constexpr (F == F_Q4_1) {          // d m | qs
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(sl + o);
+        dm = w[0];
+        qh = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qs[k] = w[1 + k];
+    } else if constexpr (F == F_Q5_1) {   // d m | qh | qs
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(sl + o);
+        dm = w[0];
+        qh = w[1];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qs[k] = w[2 + k];
+    } else {                              // 22 bytes: d | qh | qs, fields 2 bytes off the dwords
+        uint32_t w[6];
+        lds_dwords<6>(sl, o, w);
+        dm = w[0] & 0xffffu;
+        qh = align_bytes(w[1], w[0], 2);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qs[k] = align_bytes(w[2 + k], w[1 + k], 2);
+    }
+}
+
+template <int F, bool PAIRED>
+__device__ __forceinline__ float unit_dot32(const uint8_t *sl, uint32_t bo, const XU<F, PAIRED> &x, float acc) {
+    constexpr int P = Unit<F, PAIRED>::BPU;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        uint32_t dm, qh, qs[4];
+        block32_fields<F>(sl, bo + (uint32_t)j * FmtBytes<F>::BB, dm, qh, qs);
+        acc = block32_term<F>(dm, qs, qh, x.q + 8 * j, x.d[j], x.sx8[j], acc);
+    }
+    return acc;
+}
+template <>
+__device__ __forceinline__ float unit_dot<F_Q4_1, true>(const uint8_t *sl, uint32_t bo, int,
+                                                        const XU<F_Q4_1, true> &x, float acc) {
+    return unit_dot32<F_Q4_1, true>(sl, bo, x, acc);
+}
+template <>
+__device__ __forceinline__ float unit_dot<F_Q4_1, false>(const uint8_t *sl, uint32_t bo, int,
+                                                         const XU<F_Q4_1, false> &x, float acc) {
+    return unit_dot32<F_Q4_1, false>(sl, bo, x, acc);
+}
+template <>
+__device__ __forceinline__ float unit_dot<F_Q5_0, true>(const uint8_t *sl, uint32_t bo, int,
+                                                        const XU<F_Q5_0, true> &x, float acc) {
+    return unit_dot32<F_Q5_0, true>(sl, bo, x, acc);
+}
+template <>
+__device__ __forceinline__ float unit_dot<F_Q5_0, false>(const uint8_t *sl, uint32_t bo, int,
+                                                         const XU<F_Q5_0, false> &x, float acc) {
+    return unit_dot32<F_Q5_0, false>(sl, bo, x, acc);
+}
+template <>
+__device__ __forceinline__ float unit_dot<F_Q5_1, true>(const uint8_t *sl, uint32_t bo, int,
+                                                        const XU<F_Q5_1, true> &x, float acc) {
+    return unit_dot32<F_Q5_1, true>(sl, bo, x, acc);
+}
+template <>
+__device__ __forceinline__ float unit_dot<F_Q5_1, false>(const uint8_t *sl, uint32_t bo, int,
+                                                         const XU<F_Q5_1, false> &x, float acc) {
+    return unit_dot32<F_Q5_1, false>(sl, bo, x, acc);
 }
 
 // Copy bytes [lo, hi) of global memory into LDS at `dst` (16-byte aligned), as
@@ -666,6 +777,15 @@ hipError_t launch_quantize_matvec_q8_0(const void *w, const float *x, void *xq, 
     return quantize_matvec<F_Q8_0>(w, x, xq, y, N, nb, st);
 }
 
+hipError_t launch_matvec_q4_1(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st) {
+    return dispatch_mv<F_Q4_1>(w, xq, nullptr, y, 1, N, nb, st);
+}
+hipError_t launch_matvec_q5_0(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st) {
+    return dispatch_mv<F_Q5_0>(w, xq, nullptr, y, 1, N, nb, st);
+}
+hipError_t launch_matvec_q5_1(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st) {
+    return dispatch_mv<F_Q5_1>(w, xq, nullptr, y, 1, N, nb, st);
+}
 hipError_t launch_matvec_q4_k(const void *w, const void *xq, float *y, int N, int ns, hipStream_t st) {
     return dispatch_mv<F_Q4_K>(w, xq, nullptr, y, 1, N, ns, st);
 }
@@ -673,14 +793,15 @@ hipError_t launch_matvec_q6_k(const void *w, const void *xq, float *y, int N, in
     return dispatch_mv<F_Q6_K>(w, xq, nullptr, y, 1, N, ns, st);
 }
 
-// K-quant prefill: the matvec kernel with one grid row per token (the weights
-// are re-read from cache for each token; correct for any M, not tuned).
+// Prefill of the formats without an MFMA kernel (the K-quants, Q4_1, Q5_0,
+// Q5_1): the matvec kernel with one grid row per token (the weights are
+// re-read from cache for each token; correct for any M, not tuned).
 template <int F>
 static hipError_t matmul_by_tokens(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
     constexpr int kMaxY = 65535;
     for (int m0 = 0; m0 < M; m0 += kMaxY) {
         const int mc = min(kMaxY, M - m0);
-        const uint8_t *xp = static_cast<const uint8_t *>(xq) + (int64_t)m0 * ns * kQ8KBytes;
+        const uint8_t *xp = static_cast<const uint8_t *>(xq) + (int64_t)m0 * ns * FmtBytes<F>::XB;
         const hipError_t e = dispatch_mv<F>(w, xp, nullptr, y + (int64_t)m0 * N, mc, N, ns, st);
         if (e != hipSuccess) return e;
     }
@@ -694,6 +815,15 @@ hipError_t launch_matmul_q4_k(const void *w, const void *xq, float *y, int M, in
 }
 hipError_t launch_matmul_q6_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
     return matmul_by_tokens<F_Q6_K>(w, xq, y, M, N, ns, st);
+}
+hipError_t launch_matmul_q4_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    return matmul_by_tokens<F_Q4_1>(w, xq, y, M, N, nb, st);
+}
+hipError_t launch_matmul_q5_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    return matmul_by_tokens<F_Q5_0>(w, xq, y, M, N, nb, st);
+}
+hipError_t launch_matmul_q5_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    return matmul_by_tokens<F_Q5_1>(w, xq, y, M, N, nb, st);
 }
 
 }  // namespace qmm

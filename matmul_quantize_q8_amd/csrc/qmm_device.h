@@ -12,14 +12,17 @@ constexpr int kQ80Bytes = 34;             // f16 d + int8[32]
 constexpr int kQ40Bytes = 18;             // f16 d + uint8[16]
 constexpr int kQ2KBytes = 84;             // scales[16] + qs[64] + f16 d + f16 dmin
 constexpr int kQ8KBytes = 292;            // f32 d + int8[256] + int16[16]
+constexpr int kQ41Bytes = 20;             // f16 d + f16 m + uint8[16]
+constexpr int kQ50Bytes = 22;             // f16 d + qh[4] + uint8[16]
+constexpr int kQ51Bytes = 24;             // f16 d + f16 m + qh[4] + uint8[16]
 constexpr int kQ4KBytes = 144;            // f16 d + f16 dmin + 12 B scales/mins + qs[128]
 constexpr int kQ6KBytes = 210;            // ql[128] + qh[64] + int8 scales[16] + f16 d
 
 // Weight formats.  K-quant weights (256-value super-blocks) pair with Q8_K
 // activations, the 32-value formats with Q8_0 (minfer "Two activation
 // formats, one pairing rule").
-enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4 };
-template <int F> constexpr bool kIsK = F >= F_Q2_K;
+enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4, F_Q4_1 = 5, F_Q5_0 = 6, F_Q5_1 = 7 };
+template <int F> constexpr bool kIsK = F == F_Q2_K || F == F_Q4_K || F == F_Q6_K;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -152,6 +155,11 @@ __device__ __forceinline__ uint32_t q8_0_part(float4 v, float &d) {
     return (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) | ((uint32_t)(q2 & 0xff) << 16) |
            ((uint32_t)(q3 & 0xff) << 24);
 }
+
+// Four bits b (b < 16) to bit 0 of four bytes: byte k gets bit k of b.  The
+// shifted copies b, b << 7, b << 14, b << 21 do not overlap, so the product
+// is their OR.
+__device__ __forceinline__ uint32_t bits_to_bytes(uint32_t b) { return (b * 0x00204081u) & 0x01010101u; }
 
 // Store one lane's part of a Q8_0 block at `blk` (a 2-byte aligned 34-byte
 // block): its four codes at byte 2 + 4*part, and the f16 scale from part 0.

@@ -341,6 +341,111 @@ __global__ __launch_bounds__(256) void k_quantize_q6_k(const float4 *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Q4_1 / Q5_0 / Q5_1 weights (formats: ggml section 1.1, the _1 formats add a
+// per-block offset; minfer, the Q5 formats add a fifth-bit plane; field and
+// bit order GGUF's: Q4_1 d m qs, Q5_0 d qh qs, Q5_1 d m qh qs, qs byte j =
+// value j | value j+16 << 4, bit j of qh = value j's fifth bit).  The pages
+// give no quantizer; the rule (the same as the header's):
+//   _1: lo = min x, hi = max x (a zero of either sign as +0); d = (hi - lo)/L
+//       (L = 15, 31), m = lo (f16; dh, mh the stored values);
+//       q = clamp(rne((x - mh)/dh), 0, L), 0 if dh is 0;
+//   Q5_0: the value of largest magnitude (first on ties) gives d = max / -16;
+//       q = clamp(rne(x/d) + 16, 0, 31), 16 if d is 0.
+// Eight lanes per block, four values each (lane part p: values 4p..4p+3).
+// ---------------------------------------------------------------------------
+template <int F> struct W32 {
+    static constexpr int BYTES = F == F_Q4_1 ? kQ41Bytes : (F == F_Q5_0 ? kQ50Bytes : kQ51Bytes);
+    static constexpr int QS = F == F_Q4_1 ? 4 : (F == F_Q5_0 ? 6 : 8);   // qs offset
+    static constexpr int QH = F == F_Q5_0 ? 2 : 4;                        // qh offset (Q5 only)
+};
+
+template <int F>
+__global__ __launch_bounds__(256) void k_quantize_w32(const float4 *__restrict__ w, uint8_t *__restrict__ out,
+                                                      int64_t nblocks) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = t >> 3;
+    const int part = threadIdx.x & 7;
+    const bool valid = blk < nblocks;
+    const float4 v = valid ? w[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    int code[4];
+    uint32_t dbits, mbits = 0;
+    if constexpr (F == F_Q5_0) {
+        float am = fabsf(vv[0]), mx = vv[0];
+        int ix = 4 * part;
+#pragma unroll
+        for (int k = 1; k < 4; ++k) {
+            const float a = fabsf(vv[k]);
+            if (a > am) { am = a; mx = vv[k]; ix = 4 * part + k; }
+        }
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {
+            const float oam = xor_shfl(am, m);
+            const float omx = xor_shfl(mx, m);
+            const int oix = xor_shfl(ix, m);
+            if (oam > am || (oam == am && oix < ix)) { am = oam; mx = omx; ix = oix; }
+        }
+        const float d = (am != 0.0f) ? mx / -16.0f : 0.0f;
+        dbits = f32_to_f16_bits(d);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int c = 16;
+            if (d != 0.0f) c = min(max((int)rintf(vv[k] / d) + 16, 0), 31);
+            code[k] = c;
+        }
+    } else {
+        constexpr int L = F == F_Q4_1 ? 15 : 31;
+        float lo = fminf(fminf(vv[0], vv[1]), fminf(vv[2], vv[3]));
+        float hi = fmaxf(fmaxf(vv[0], vv[1]), fmaxf(vv[2], vv[3]));
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {
+            lo = fminf(lo, xor_shfl(lo, m));
+            hi = fmaxf(hi, xor_shfl(hi, m));
+        }
+        lo += 0.0f;
+        hi += 0.0f;
+        dbits = f32_to_f16_bits((hi - lo) / (float)L);
+        mbits = f32_to_f16_bits(lo);
+        const float dh = f16_bits_to_f32(dbits), mh = f16_bits_to_f32(mbits);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int c = 0;
+            if (dh != 0.0f) c = min(max((int)rintf((vv[k] - mh) / dh), 0), L);
+            code[k] = c;
+        }
+    }
+    uint32_t c4 = 0, qb = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        c4 |= (uint32_t)(code[k] & 15) << (8 * k);
+        qb |= (uint32_t)((code[k] >> 4) & 1) << (4 * part + k);
+    }
+    // lanes 0..3 hold values 0..15 (low nibbles), lanes 4..7 values 16..31
+    const uint32_t hi4 = xor_shfl(c4, 4);
+    qb |= xor_shfl(qb, 1);
+    qb |= xor_shfl(qb, 2);
+    qb |= xor_shfl(qb, 4);
+    if (valid) {
+        uint8_t *ob = out + blk * W32<F>::BYTES;                   // 2-byte aligned at least
+        if (part < 4) {
+            const uint32_t bytes = c4 | (hi4 << 4);
+            uint16_t *o16 = reinterpret_cast<uint16_t *>(ob + W32<F>::QS + 4 * part);
+            o16[0] = (uint16_t)(bytes & 0xffffu);
+            o16[1] = (uint16_t)(bytes >> 16);
+        }
+        if (part == 0) {
+            *reinterpret_cast<uint16_t *>(ob) = (uint16_t)dbits;
+            if constexpr (F != F_Q5_0) *reinterpret_cast<uint16_t *>(ob + 2) = (uint16_t)mbits;
+            if constexpr (F != F_Q4_1) {
+                uint16_t *q16 = reinterpret_cast<uint16_t *>(ob + W32<F>::QH);
+                q16[0] = (uint16_t)(qb & 0xffffu);
+                q16[1] = (uint16_t)(qb >> 16);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (called by the C ABI after argument checks).
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipStream_t st) {
@@ -365,6 +470,22 @@ hipError_t launch_quantize_q2_k(const float *w, void *out, int64_t nblocks, hipS
     const int64_t grid = (nblocks + 3) / 4;
     void *args[] = {(void *)&w, (void *)&out, (void *)&nblocks};
     return hipLaunchKernel((const void *)k_quantize_q2_k, dim3((unsigned)grid), dim3(256), args, 0, st);
+}
+
+template <int F>
+static hipError_t launch_w32(const float *w, void *out, int64_t nblocks, hipStream_t st) {
+    const int64_t grid = (nblocks + 31) / 32;
+    void *args[] = {(void *)&w, (void *)&out, (void *)&nblocks};
+    return hipLaunchKernel((const void *)k_quantize_w32<F>, dim3((unsigned)grid), dim3(256), args, 0, st);
+}
+hipError_t launch_quantize_q4_1(const float *w, void *out, int64_t nb, hipStream_t st) {
+    return launch_w32<F_Q4_1>(w, out, nb, st);
+}
+hipError_t launch_quantize_q5_0(const float *w, void *out, int64_t nb, hipStream_t st) {
+    return launch_w32<F_Q5_0>(w, out, nb, st);
+}
+hipError_t launch_quantize_q5_1(const float *w, void *out, int64_t nb, hipStream_t st) {
+    return launch_w32<F_Q5_1>(w, out, nb, st);
 }
 
 hipError_t launch_quantize_q4_k(const float *w, void *out, int64_t nblocks, hipStream_t st) {

@@ -5,7 +5,7 @@
 //
 // Bit-exactness: each decoded value is a binary16 scale times a small integer
 // (exact in f32: at most 11 + 13 significant bits), or for the formats with
-// mins the difference of two such exact products, rounded once (the library is
+// mins or offsets the difference or sum of two such exact values, rounded once (the library is
 // built without contraction, so no fused multiply-add changes that rounding).
 // The result is the exactly decoded value rounded to f32, as the oracle's.
 #include "qmm_device.h"
@@ -35,6 +35,29 @@ __device__ __forceinline__ void decode4(const uint8_t *row, int64_t i0, float (&
                 c = (int8_t)blk[2 + e];
             }
             v[k] = d * (float)c;
+        }
+    } else if constexpr (F == F_Q4_1 || F == F_Q5_0 || F == F_Q5_1) {
+        // d*q + m (_1) or d*(q - 16) (Q5_0); qs byte j = value j | value j+16 << 4,
+        // bit j of the little-endian qh = value j's fifth bit
+        constexpr int BB = F == F_Q4_1 ? kQ41Bytes : (F == F_Q5_0 ? kQ50Bytes : kQ51Bytes);
+        constexpr int QS = F == F_Q4_1 ? 4 : (F == F_Q5_0 ? 6 : 8);
+        constexpr int QH = F == F_Q5_0 ? 2 : 4;
+        const uint8_t *blk = row + (i0 >> 5) * BB;
+        const int j = (int)(i0 & 31);
+        const float d = rd_f16(blk);
+        uint32_t qh = 0;
+        if constexpr (F != F_Q4_1)
+            qh = (uint32_t)blk[QH] | ((uint32_t)blk[QH + 1] << 8) | ((uint32_t)blk[QH + 2] << 16) |
+                 ((uint32_t)blk[QH + 3] << 24);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = j + k;
+            const int byte = blk[QS + (e & 15)];
+            const int q = (e < 16 ? (byte & 15) : (byte >> 4)) | (int)(((qh >> e) & 1u) << 4);
+            if constexpr (F == F_Q5_0)
+                v[k] = d * (float)(q - 16);
+            else
+                v[k] = d * (float)q + rd_f16(blk + 2);
         }
     } else if constexpr (F == F_Q2_K) {
         const uint8_t *blk = row + (i0 >> 8) * kQ2KBytes;
@@ -121,6 +144,9 @@ hipError_t launch_get_rows(int fmt, const void *w, const int32_t *ids, float *ou
         case F_Q2_K: return launch_rows<F_Q2_K>(w, ids, out, n, N, K, row_bytes, st);
         case F_Q4_K: return launch_rows<F_Q4_K>(w, ids, out, n, N, K, row_bytes, st);
         case F_Q6_K: return launch_rows<F_Q6_K>(w, ids, out, n, N, K, row_bytes, st);
+        case F_Q4_1: return launch_rows<F_Q4_1>(w, ids, out, n, N, K, row_bytes, st);
+        case F_Q5_0: return launch_rows<F_Q5_0>(w, ids, out, n, N, K, row_bytes, st);
+        case F_Q5_1: return launch_rows<F_Q5_1>(w, ids, out, n, N, K, row_bytes, st);
     }
     return hipErrorInvalidValue;
 }

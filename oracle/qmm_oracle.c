@@ -315,7 +315,8 @@ static double val32(int fmt, const uint8_t *blk, int j) {
 }
 
 /* Weight quantizers for the three (test data; the pages give no rule):
- *   Q4_1 / Q5_1: lo = min x, hi = max x over the block; d = (hi - lo) / L
+ *   Q4_1 / Q5_1: lo = min x, hi = max x over the block (a zero of either sign
+ *     taken as +0); d = (hi - lo) / L
  *     (L = 15 or 31), m = lo (both stored f16); q = clamp(round((x - m) / d),
  *     0, L) with the stored d and m, 0 if d is 0.
  *   Q5_0: Q4_0's rule with 32 levels: the value of largest magnitude (first
@@ -343,6 +344,8 @@ static void quant_block32(int fmt, const float *xb, uint8_t *ob) {
             if (xb[j] < lo) lo = xb[j];
             if (xb[j] > hi) hi = xb[j];
         }
+        lo += 0.0f;                      /* a zero of either sign counts as +0 */
+        hi += 0.0f;
         wr_f16(ob, (hi - lo) / (float)L);
         wr_f16(ob + 2, lo);
         float dh = rd_f16(ob), mh = rd_f16(ob + 2);

@@ -43,8 +43,7 @@ def _gpu_quant(env, fmt, x, weights=False):
     torch, q, _ = env
     rows, K = x.shape
     out = torch.zeros(rows * q.row_bytes(fmt, K), dtype=torch.uint8, device="cuda")
-    fn = {"q8_0": q.qmm_quantize_q8_0, "q8_k": q.qmm_quantize_q8_k, "q4_0": q.qmm_quantize_q4_0,
-          "q2_k": q.qmm_quantize_q2_k, "q4_k": q.qmm_quantize_q4_k, "q6_k": q.qmm_quantize_q6_k}[fmt]
+    fn = dict(q.QUANTIZE_W, q8_k=q.qmm_quantize_q8_k)[fmt]
     fn(_dev(torch, x), out, rows, K)
     torch.cuda.synchronize()
     return out.cpu().numpy().reshape(rows, -1)
@@ -122,6 +121,20 @@ def test_quantize_k_weights_bit_exact(env, fmt, rows, K):
     assert np.array_equal(_gpu_quant(env, fmt, w), orc.quantize_w(fmt, w))
 
 
+@pytest.mark.parametrize("fmt", ["q4_1", "q5_0", "q5_1"])
+@pytest.mark.parametrize("rows,K", [(1, 32), (16, 1024), (12288, 4096), (3, 96)])
+def test_quantize_32_value_offset_weights_bit_exact(env, fmt, rows, K):
+    _, _, orc = env
+    _say("quantize", fmt, rows, K)
+    w = synth.gaussian_f32((rows, K), 0.02, 4200 + rows + K)
+    w[0, :32] = 0.0                                   # zero block
+    if rows > 1:
+        w[1, :32] = np.abs(w[1, :32])                 # no negative value
+        w[1, 3] = -0.5                                # magnitude tie: first index wins
+        w[1, 10] = 0.5
+    assert np.array_equal(_gpu_quant(env, fmt, w), orc.quantize_w(fmt, w))
+
+
 # ---------------------------------------------------------------------------
 # Products
 # ---------------------------------------------------------------------------
@@ -175,7 +188,8 @@ MATVEC_CASES = [
     ("q4_k", 13, 9216), ("q4_k", 2, 40960), ("q4_k", 7, 1280),                      # 4 units per lane; segments
     ("q6_k", 12288, 4096), ("q6_k", 1, 256), ("q6_k", 3, 768), ("q6_k", 37, 512),
     ("q6_k", 13, 9216), ("q6_k", 2, 40960), ("q6_k", 5, 1280),   # odd super-block count: rows 2 mod 4
-]
+] + [(f, N, K) for f in ("q4_1", "q5_0", "q5_1")
+     for N, K in ((12288, 4096), (1, 32), (3, 96), (17, 160), (5, 2080), (7, 8192), (9, 20480), (45, 1024))]
 
 
 @pytest.mark.parametrize("fmt,N,K", MATVEC_CASES)
@@ -256,7 +270,8 @@ def test_fused_without_xq_output_equals_two_launches(env, fmt, N, K):
 
 
 @pytest.mark.parametrize("fmt,N,K", [("q4_0", 151, 896), ("q8_0", 64, 1024), ("q2_k", 33, 512),
-                                     ("q4_k", 40, 4096), ("q6_k", 17, 1280), ("q4_0", 3000, 4096)])
+                                     ("q4_k", 40, 4096), ("q6_k", 17, 1280), ("q4_0", 3000, 4096),
+                                     ("q4_1", 20, 96), ("q5_0", 31, 160), ("q5_1", 9, 4096)])
 def test_get_rows_bit_exact(env, fmt, N, K):
     """Embedding rows are byte-for-byte the oracle's (minfer "The embedding
     matmul"), repeated ids included; ids outside the table give NaN rows."""
@@ -284,6 +299,7 @@ MATMUL_CASES = [
     ("q2_k", 1, 8, 256), ("q2_k", 9, 70, 1024), ("q2_k", 33, 130, 4096),
     ("q4_k", 1, 8, 256), ("q4_k", 9, 70, 1024), ("q4_k", 33, 130, 4096),
     ("q6_k", 1, 8, 256), ("q6_k", 9, 70, 1024), ("q6_k", 5, 33, 1280),
+    ("q4_1", 9, 70, 1024), ("q5_0", 9, 70, 1024), ("q5_1", 9, 70, 1024), ("q5_0", 5, 3, 96),
 ]
 
 

@@ -24,12 +24,19 @@ stream 0 = weights, 1 = activations, 2 = outlier picks, 3+ = extra matrices.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
-_CHUNK = 1 << 22
+# Entries are drawn in cache-sized chunks, several chunks at a time on host
+# threads (numpy releases the interpreter lock inside its array loops).  Each
+# entry depends only on (seed, index), so the bytes do not depend on either.
+_CHUNK = 1 << 18
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 SEED_BASE = 0x514D4D00
 
@@ -74,9 +81,18 @@ def gaussian_f32(shape, sigma: float, seed: int) -> np.ndarray:
     """float32 array of the given shape, entries float32(sigma * N(0,1)) in C order."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32)
-    for c0 in range(0, n, _CHUNK):
+
+    def fill(c0):
         c1 = min(n, c0 + _CHUNK)
         out[c0:c1] = (sigma * normal(seed, c1 - c0, start=c0)).astype(np.float32)
+
+    starts = range(0, n, _CHUNK)
+    if len(starts) <= 1 or _THREADS == 1:
+        for c0 in starts:
+            fill(c0)
+    else:
+        with ThreadPoolExecutor(max_workers=_THREADS) as ex:
+            list(ex.map(fill, starts))
     return out.reshape(shape)
 
 

@@ -238,6 +238,18 @@ def bench_prefill(args, torch, q, synth):
     m8_ms, m8_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q8_0(wq8, Xq, Y, M, N, K), args.prefill_steps, 4)
     log(f"prefill q8_0 weights: matmul {m8_ms * 1e3:.1f} us (best batch {m8_min * 1e3:.1f})")
     del wq8
+    # Q2_K weights x Q8_K activations (same shape, inputs of the Q2_K workload)
+    w = torch.from_numpy(synth.weights(N, K, config=3)).cuda()
+    wq2 = torch.empty(N * q.row_bytes("q2_k", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q2_k(w, wq2, N, K)
+    del w
+    X8k = torch.empty(M * q.row_bytes("q8_k", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q8_k(X, X8k, M, K)
+    for _ in range(4):
+        q.qmm_matmul_q2_k(wq2, X8k, Y, M, N, K)
+    m2_ms, m2_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q2_k(wq2, X8k, Y, M, N, K), args.prefill_steps, 4)
+    log(f"prefill q2_k weights: matmul {m2_ms * 1e3:.1f} us (best batch {m2_min * 1e3:.1f})")
+    del wq2, X8k
     return dict(ms_step=ms_step, tops=ops / (ms_step * 1e-3) / 1e12,
                 roofline={"kernel": "qmm::k_matmul_q4_0", "bound": "mfma", "achieved": round(tops_kernel, 2),
                           "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
@@ -246,7 +258,10 @@ def bench_prefill(args, torch, q, synth):
                           "kernel_us_best_batch": round(mm_min * 1e3, 2), "algorithmic_ops": ops},
                 q8_0_weights={"kernel": "qmm::k_matmul_q8_0", "kernel_us_mean": round(m8_ms * 1e3, 2),
                               "achieved": round(ops / (m8_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
-                              "frac": round(ops / (m8_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)})
+                              "frac": round(ops / (m8_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)},
+                q2_k_weights={"kernel": "qmm::k_matmul_q2_k", "kernel_us_mean": round(m2_ms * 1e3, 2),
+                              "achieved": round(ops / (m2_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
+                              "frac": round(ops / (m2_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)})
 
 
 # The other decode workloads, one matvec launch each, weights rotated like the
@@ -423,7 +438,7 @@ def main():
         pf = {"workload": "q4_0_matmul_2048x12288x4096", "value": round(pre["tops"], 2), "unit": "TOPS",
               "steps": args.prefill_steps, "warmup": args.prefill_warmup, "ms_per_step": round(pre["ms_step"], 4),
               "step": "quantize_q8_0 (2048x4096) + matmul_q4_0", "roofline": pre["roofline"],
-              "q8_0_weights": pre["q8_0_weights"], "cpu_baseline": cpu_pre}
+              "q8_0_weights": pre["q8_0_weights"], "q2_k_weights": pre["q2_k_weights"], "cpu_baseline": cpu_pre}
         if dec is None:
             out.update({"value": pf["value"], "unit": "TOPS", "steps": pf["steps"], "warmup": pf["warmup"],
                         "ms_per_step": pf["ms_per_step"], "config": {"workload": pf["workload"]},

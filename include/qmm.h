@@ -204,8 +204,12 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
  *   y  : f32 [M][N], written.
  * qmm_matmul_q4_0 and qmm_matmul_q8_0 run on int8 MFMA and also return
  * QMM_E_SHAPE when 128 rows of Q8_0 activations (128 * K/32 * 34 bytes) exceed
- * 2^31 - 1 bytes, i.e. K > 15,790,304.  The other formats run the matvec
- * kernel once per token (correct for any M, not tuned for prefill). */
+ * 2^31 - 1 bytes, i.e. K > 15,790,304.  qmm_matmul_q2_k runs on int8 MFMA
+ * (the group scales folded into the codes, one scale fold per 256 values)
+ * plus an f16 MFMA for the min term, and returns QMM_E_SHAPE when 128 rows of
+ * Q8_K activations (128 * K/256 * 292 bytes) exceed 2^31 - 1 bytes.  The other
+ * formats run the matvec kernel once per token (correct for any M, not tuned
+ * for prefill). */
 qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
 qmm_status qmm_matmul_q8_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,

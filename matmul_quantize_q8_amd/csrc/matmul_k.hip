@@ -11,8 +11,11 @@
 // contraction of bsums (|b| <= 2048, exact in f16) with mins (<= 15): one
 // v_mfma_f32_32x32x16_f16, exact (|Mn| < 2^24).
 //
-// Workgroup tile 128 tokens x 128 weight rows, 4 waves of 64 x 64 (2 x 2 MFMA
-// tiles of 32 x 32), one workgroup per CU (two stage buffers of 52 KB).
+// Workgroup tile 128 tokens x 256 weight rows, 8 waves of all 128 tokens x
+// 32 weight rows (four MFMA tiles of 32 x 32 sharing one B operand, so each
+// B operand is built once per workgroup), one workgroup per CU: two waves per
+// SIMD, so that one issues while the other waits, and two stage buffers of
+// 66 KB (the DMA of stage s+1 runs while stage s is computed).
 // Staging: a stage is one super-block.  Each activation row's 292 bytes
 // arrive as 19 chunks of 16 bytes (LDS row: codes 0..255 at 0, bsums at 256,
 // the chunk holding d8 at 288; 304-byte stride, so the 32 rows of a 16-byte
@@ -20,8 +23,7 @@
 // (scales at 0, qs at 16, the chunk holding d and dmin at 80, one spare;
 // 112-byte stride).  Consecutive lanes take consecutive chunks of a row, so
 // every load is coalesced; each lane's global offsets are fixed for the
-// whole K loop and the stage position rides in the scalar offset.  The DMA of
-// stage s+1 runs while stage s is computed.
+// whole K loop and the stage position rides in the scalar offset.
 //
 // Operands.  K-step t of a super-block covers values 32t .. 32t+31, which are
 // the 2-bit fields at shift 2(t%4) of qs bytes 32(t/4) .. +31 (the qs bit
@@ -45,26 +47,29 @@ namespace qmm {
 
 namespace mk {
 constexpr int BM = 128;                        // tokens per workgroup tile
-constexpr int BN = 128;                        // weight rows per workgroup tile
-constexpr int NT = 256;                        // 4 waves, 2 x 2 of 64 x 64
+constexpr int BN = 256;                        // weight rows per workgroup tile
+constexpr int NW = 8;                          // waves, each all 128 tokens x 32 weight rows
+constexpr int NT = NW * kWave;
 constexpr int XC = 19;                         // 16-byte chunks per activation row per stage
 constexpr int WC = 7;                          // per weight row
 constexpr int XQ = BM * XC / kWave;            // 38 wave loads of activation chunks
-constexpr int WQ = BN * WC / kWave;            // 14 of weight chunks
-constexpr int PER_WAVE = (XQ + WQ) / 4;        // 13 DMA loads per wave per stage
+constexpr int WQ = BN * WC / kWave;            // 28 of weight chunks
+constexpr int NQ = XQ + WQ;                    // 66 wave loads per stage
+constexpr int PER_WAVE = (NQ + NW - 1) / NW;   // 9 (waves 2..7 repeat one in the last round)
 constexpr int XROW = 16 * XC;                  // 304-byte LDS activation row
 constexpr int WROW = 16 * WC;                  // 112-byte LDS weight row
 constexpr int WOFF = BM * XROW;                // weight rows start (bytes into a stage buffer)
-constexpr int STAGE = (BM * XC + BN * WC) * 16;   // 53,248 bytes
+constexpr int STAGE = (BM * XC + BN * WC) * 16;   // 67,584 bytes
 constexpr int NBUF = 2;
-constexpr int D8 = NBUF * STAGE;               // per-wave f32 d8 of its 64 rows
-constexpr int LDS_BYTES = D8 + 4 * 64 * 4;     // 107,520
+constexpr int D8 = NBUF * STAGE;               // per-wave f32 d8 of the 128 rows
+constexpr int LDS_BYTES = D8 + NW * BM * 4;    // 139,264
 constexpr float kBias = 12582912.0f;           // 1.5 * 2^23, bit pattern 0x4B400000
 // global offsets (within a super-block) of the chunks of a row
 constexpr int xchunk(int c) { return c < 16 ? 4 + 16 * c : (c == 16 ? 260 : (c == 17 ? 276 : 0)); }
 constexpr int wchunk(int c) { return c < 5 ? 16 * c : 68; }
-static_assert(XQ * kWave == BM * XC && WQ * kWave == BN * WC && (XQ + WQ) % 4 == 0,
-              "a stage splits into whole wave loads, evenly over the waves");
+static_assert(XQ * kWave == BM * XC && WQ * kWave == BN * WC && NQ > NW * (PER_WAVE - 1),
+              "a stage splits into whole wave loads; only the last round of loads has gaps");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 }  // namespace mk
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -82,9 +87,9 @@ __device__ __forceinline__ void buffer16_to_lds(__amdgpu_buffer_rsrc_t r, uint32
 }
 #pragma clang diagnostic pop
 
-__global__ __launch_bounds__(mk::NT, 1) void k_matmul_q2_k(const uint8_t *__restrict__ w,
-                                                          const uint8_t *__restrict__ xq, float *__restrict__ y,
-                                                          int M, int N, int ns, int tiles_m) {
+__global__ __launch_bounds__(mk::NT) void k_matmul_q2_k(const uint8_t *__restrict__ w,
+                                                        const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                        int M, int N, int ns, int tiles_m) {
     using namespace mk;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63;
@@ -93,10 +98,12 @@ __global__ __launch_bounds__(mk::NT, 1) void k_matmul_q2_k(const uint8_t *__rest
     const int m0 = mt * BM, n0 = nt * BN;
     const uint32_t xrow = (uint32_t)ns * kQ8KBytes, wrow = (uint32_t)ns * kQ2KBytes;
 
-    // DMA: wave load q = wave + 4k (k < 13) of a stage is chunk load q of the
+    // DMA: wave load q = wave + 8k (k < 9) of a stage is chunk load q of the
     // stage image (activation chunks for q < 38, weight chunks after) and
-    // lands at byte 1024 q of the stage buffer.  Rows past the matrix re-read
-    // its last row (their results are not stored).
+    // lands at byte 1024 q of the stage buffer; waves 2..7 have no load
+    // q = 66..71 and repeat their load k = 7 instead (same bytes to the same
+    // place), so that every wave issues the same count.  Rows past the matrix
+    // re-read its last row (their results are not stored).
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(xq + (int64_t)m0 * xrow), 0, (int)((uint32_t)min(M - m0, BM) * xrow), 0x00020000);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -104,8 +111,10 @@ __global__ __launch_bounds__(mk::NT, 1) void k_matmul_q2_k(const uint8_t *__rest
     uint32_t voff[PER_WAVE];
 #pragma unroll
     for (int k = 0; k < PER_WAVE; ++k) {
-        const int q = wave + 4 * k;
-        if (q < XQ) {
+        const int q = wave + NW * k;
+        if (q >= NQ) {
+            voff[k] = voff[k - 1];
+        } else if (q < XQ) {
             const int f = kWave * q + lane, row = f / XC, c = f - XC * row;
             voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (uint32_t)xchunk(c);
         } else {
@@ -115,16 +124,21 @@ __global__ __launch_bounds__(mk::NT, 1) void k_matmul_q2_k(const uint8_t *__rest
     }
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
     const uint32_t m0w = (uint32_t)uniform((int)(lds0 + 1024u * wave));
-    static_assert(XQ == 38 && PER_WAVE == 13, "the load roles below are written for this split");
+    constexpr int KL = PER_WAVE - 1;
+    // LDS offset of the last load of a stage (or of the load it repeats)
+    const uint32_t last_off = (uint32_t)uniform(1024 * NW * (wave + NW * KL >= NQ ? KL - 1 : KL));
+    static_assert(PER_WAVE == 9, "the load calls below are written for this split");
     auto dma = [&](int s, int b) __attribute__((always_inline)) {
         const int sx = s * kQ8KBytes, sw = s * kQ2KBytes;
         const uint32_t base = m0w + (uint32_t)(b * STAGE);
-        // loads 0..8 are activation chunks for every wave; load 9 for waves 0
-        // and 1 (q = 36, 37), weight chunks for waves 2 and 3; loads 10..12 weights
         auto one = [&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
-            const bool isw = k == 9 ? wave >= 2 : k >= 10;
-            buffer16_to_lds<4096 * k>(isw ? wr : xr, base, voff[k], isw ? sw : sx);
+            const bool isw = wave + NW * k >= XQ;   // a repeated load is a weight load
+            const int soff = uniform(isw ? sw : sx);
+            if constexpr (k == KL)
+                buffer16_to_lds<0>(isw ? wr : xr, base + last_off, voff[k], soff);
+            else
+                buffer16_to_lds<1024 * NW * k>(isw ? wr : xr, base, voff[k], soff);
         };
         one(std::integral_constant<int, 0>());
         one(std::integral_constant<int, 1>());
@@ -135,29 +149,21 @@ __global__ __launch_bounds__(mk::NT, 1) void k_matmul_q2_k(const uint8_t *__rest
         one(std::integral_constant<int, 6>());
         one(std::integral_constant<int, 7>());
         one(std::integral_constant<int, 8>());
-        one(std::integral_constant<int, 9>());
-        one(std::integral_constant<int, 10>());
-        one(std::integral_constant<int, 11>());
-        one(std::integral_constant<int, 12>());
     };
 
-    const int wm = wave & 1, wn = wave >> 1;
     const int lr = lane & 31, lh = lane >> 5;
-    const int xa = XROW * (64 * wm + lr);                // A row 64wm+lr (tile i: +32 rows)
-    const int wb = WOFF + WROW * (64 * wn + lr);         // B row 64wn+lr (tile j: +32 rows)
-    const int xd = XROW * (64 * wm + lane) + 288;        // the d8 chunk of the row this lane converts
-    float *d8w = reinterpret_cast<float *>(lds + D8 + 256 * wave);
+    const int xa = XROW * lr;                            // A row lr (tile i: +32i rows)
+    const int wb = WOFF + WROW * (32 * wave + lr);       // B row 32 wave + lr
+    float *d8w = reinterpret_cast<float *>(lds + D8 + 4 * BM * wave);
 
     v16i bias;
 #pragma unroll
     for (int r = 0; r < 16; ++r) bias[r] = 0x4B400000;
-    float acc[2][2][16];
+    float acc[4][16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
     auto rd16 = [](const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); };
     auto rd4 = [](const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); };
@@ -186,103 +192,78 @@ __global__ __launch_bounds__(mk::NT, 1) void k_matmul_q2_k(const uint8_t *__rest
     auto half_lo = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); };
     auto half_hi = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); };
 
+    // One stage: the wave's B tile (32 weight rows) against all four A tiles
+    // (128 tokens), so that each B operand is built once per workgroup.
     auto compute = [&](const uint8_t *sb) __attribute__((always_inline)) {
-        // d8 of the wave's 64 activation rows into its private array
-        d8w[lane] = *reinterpret_cast<const float *>(sb + xd);
-        // per B tile: the 16 scale bytes and d, dmin
-        uint4 scl[2];
-        float dw[2], nbw[2], ndm[2];
+        // d8 of the 128 activation rows into the wave's private array
+        d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * lane + 288);
+        d8w[64 + lane] = *reinterpret_cast<const float *>(sb + XROW * (64 + lane) + 288);
+        // the B tile's 16 scale bytes and d, dmin
+        const uint4 scl = rd16(sb + wb);
+        const uint32_t dd = rd4(sb + wb + 92);
+        uint4 qs = rd16(sb + wb + 16 + 16 * lh);
+        // B operand of K-step kt: group 2kt + lh, table [0, sc, 2sc, 3sc]
+        auto build_b = [&](int kt, const uint4 &q) __attribute__((always_inline)) {
+            const int g = 2 * kt + lh, sft = 2 * (kt & 3);
+            const uint32_t sw = (g < 4) ? scl.x : (g < 8) ? scl.y : (g < 12) ? scl.z : scl.w;
+            const uint32_t sc = (sw >> (8 * (g & 3))) & 15u;
+            const uint32_t tab = __umul24(sc << 8, 0x030201u);   // sc * 0x03020100
+            const uint32_t d4[4] = {q.x, q.y, q.z, q.w};
+            v4i b;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            scl[j] = rd16(sb + wb + WROW * 32 * j);
-            const uint32_t dd = rd4(sb + wb + WROW * 32 * j + 92);
-            dw[j] = half_lo(dd);
-            asm volatile("" : "+v"(dw[j]));          // keep the f32 value (see the Q4_0 kernel)
-            nbw[j] = dw[j] * -kBias;                 // exact: 11 + 2 significant bits
-            ndm[j] = -half_hi(dd);
-        }
-        // min term: one f16 MFMA per tile
-        v16f mn[2][2];
-        {
-            v8h am[2], bm[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) am[i] = i16x8_to_h(rd16(sb + xa + XROW * 32 * i + 256 + 16 * lh));
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint32_t lo = lh ? scl[j].z : scl[j].x, hi = lh ? scl[j].w : scl[j].y;   // groups 8h .. 8h+7
-                bm[j] = mins_to_h(lo, hi);
-            }
-            const v16f z = {};
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) mn[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[i], bm[j], z, 0, 0, 0);
-        }
+            for (int e = 0; e < 4; ++e) b[e] = (int)__builtin_amdgcn_perm(0u, tab, (d4[e] >> sft) & 0x03030303u);
+            return b;
+        };
         // value term: eight K-steps of int8 MFMA, int32 accumulation from the bias
-        v16i v[2][2];
+        v16i v[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) v[i][j] = bias;
-        uint4 qs[2];
+        for (int i = 0; i < 4; ++i) v[i] = bias;
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
-            const int h = kt >> 2, sft = 2 * (kt & 3);
-            if ((kt & 3) == 0) {
+            if (kt == 4) qs = rd16(sb + wb + 16 + 32 + 16 * lh);
+            const v4i b = build_b(kt, qs);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) qs[j] = rd16(sb + wb + WROW * 32 * j + 16 + 32 * h + 16 * lh);
+            for (int i = 0; i < 4; ++i) {
+                const v4i a = as_v4i(rd16(sb + xa + XROW * 32 * i + 32 * kt + 16 * lh));
+                v[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v[i], 0, 0, 0);
             }
-            v4i a[2], b[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = as_v4i(rd16(sb + xa + XROW * 32 * i + 32 * kt + 16 * lh));
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                // group 2kt + lh: scale byte, table [0, sc, 2sc, 3sc]
-                const int g = 2 * kt + lh;
-                const uint32_t sw = (g < 4) ? scl[j].x : (g < 8) ? scl[j].y : (g < 12) ? scl[j].z : scl[j].w;
-                const uint32_t sc = (sw >> (8 * (g & 3))) & 15u;
-                const uint32_t tab = sc * 0x03020100u;
-                const uint32_t d4[4] = {qs[j].x, qs[j].y, qs[j].z, qs[j].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t qb = (d4[e] >> sft) & 0x03030303u;
-                    b[j][e] = (int)__builtin_amdgcn_perm(0u, tab, qb);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) v[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], v[i][j], 0, 0, 0);
         }
-        // fold: acc += d8 * (d * V - dmin * Mn)
+        float dw = half_lo(dd), ndm = -half_hi(dd);
+        // keep the f32 values (an f16 operand would make each fold FMA a
+        // half-rate v_fma_mix)
+        asm volatile("" : "+v"(dw), "+v"(ndm));
+        const float nbw = dw * -kBias;   // exact: 11 + 2 significant bits
+        // min term, one f16 MFMA per A tile, and the fold:
+        // acc += d8 * (d * V - dmin * Mn)
+        const uint32_t mlo = lh ? scl.z : scl.x, mhi = lh ? scl.w : scl.y;   // groups 8h .. 8h+7
+        const v8h bm = mins_to_h(mlo, mhi);
+        const v16f z = {};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            float d8[16];
+        for (int i = 0; i < 4; ++i) {
+            const v8h am = i16x8_to_h(rd16(sb + xa + XROW * 32 * i + 256 + 16 * lh));
+            const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(am, bm, z, 0, 0, 0);
+            // d8 of output rows 8a4 + 4lh + c, four at a time
             const float4 *p = reinterpret_cast<const float4 *>(d8w + 32 * i + 4 * lh);
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
                 const float4 qd = p[2 * a4];
-                d8[4 * a4] = qd.x;
-                d8[4 * a4 + 1] = qd.y;
-                d8[4 * a4 + 2] = qd.z;
-                d8[4 * a4 + 3] = qd.w;
-            }
+                const float d8[4] = {qd.x, qd.y, qd.z, qd.w};
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int e = v[i][j][r];
-                    const float u = fmaf(__int_as_float(e), dw[j], nbw[j]);
-                    const float tt = fmaf(ndm[j], mn[i][j][r], u);
-                    acc[i][j][r] = fmaf(tt, d8[r], acc[i][j][r]);
+                for (int c = 0; c < 4; ++c) {
+                    const int r = 4 * a4 + c;
+                    const int e = v[i][r];
+                    const float u = fmaf(__int_as_float(e), dw, nbw);
+                    const float tt = fmaf(ndm, mn[r], u);
+                    acc[i][r] = fmaf(tt, d8[c], acc[i][r]);
                 }
+            }
         }
     };
 
-    // Stage s lives in buffer s % 2.  At step s: wait for this wave's loads of
-    // stage s, the barrier publishes every wave's (and tells that stage s-1's
-    // buffer is free), the DMA of stage s+1 goes into it, then stage s is
-    // computed.
+    // Stage s lives in buffer s % 2.  At step s: wait for this wave's loads
+    // of stage s, the barrier publishes every wave's (and tells that stage
+    // s-1's buffer is free), the DMA of stage s+1 goes into it, then stage s
+    // is computed.
     dma(0, 0);
     for (int s = 0; s < ns; ++s) {
         asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -292,18 +273,16 @@ __global__ __launch_bounds__(mk::NT, 1) void k_matmul_q2_k(const uint8_t *__rest
     // no LDS-DMA write may still be in flight when the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    const int n = n0 + 32 * wave + lr;
+    if (n < N) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + 64 * wn + 32 * j + lr;
-            if (n >= N) continue;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (m < M) y[(int64_t)m * N + n] = acc[i][j][r];
+                const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (m < M) y[(int64_t)m * N + n] = acc[i][r];
             }
-        }
+    }
 }
 
 // Largest super-block count whose tile offsets fit the 32-bit buffer offsets

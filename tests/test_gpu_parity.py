@@ -293,6 +293,8 @@ MATMUL_CASES = [
     # even block counts (the dword-plane kernel): 1..7 stages, ragged tiles
     ("q4_0", 1, 129, 64), ("q4_0", 131, 255, 128), ("q4_0", 70, 130, 192), ("q4_0", 257, 129, 256),
     ("q4_0", 3, 300, 320), ("q4_0", 200, 100, 448),
+    # token counts one past and one short of 64 (half a 128-token tile)
+    ("q4_0", 65, 130, 96), ("q4_0", 63, 127, 2048), ("q8_0", 65, 129, 160), ("q8_0", 63, 255, 2048),
     ("q8_0", 1, 8, 32), ("q8_0", 37, 200, 1024), ("q8_0", 128, 128, 4096), ("q8_0", 130, 129, 160),
     ("q8_0", 5, 3, 96), ("q8_0", 131, 255, 128), ("q8_0", 257, 129, 256), ("q8_0", 300, 700, 2080),
     ("q8_0", 3, 300, 320), ("q8_0", 129, 257, 64),

@@ -258,10 +258,12 @@ def bench_prefill(args, torch, q, synth):
                           "kernel_us_best_batch": round(mm_min * 1e3, 2), "algorithmic_ops": ops},
                 q8_0_weights={"kernel": "qmm::k_matmul_q8_0", "kernel_us_mean": round(m8_ms * 1e3, 2),
                               "achieved": round(ops / (m8_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
-                              "frac": round(ops / (m8_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)},
+                              "frac": round(ops / (m8_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                              "traffic": committed_traffic("k_matmul_q8_0", "2048x12288x4096")},
                 q2_k_weights={"kernel": "qmm::k_matmul_q2_k", "kernel_us_mean": round(m2_ms * 1e3, 2),
                               "achieved": round(ops / (m2_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
-                              "frac": round(ops / (m2_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)})
+                              "frac": round(ops / (m2_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                              "traffic": committed_traffic("k_matmul_q2_k", "2048x12288x4096")})
 
 
 # The other decode workloads, one matvec launch each, weights rotated like the

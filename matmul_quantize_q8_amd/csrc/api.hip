@@ -37,8 +37,9 @@ int64_t matmul_q4_0_max_blocks();
 hipError_t launch_get_rows(int fmt, const void *w, const int32_t *ids, float *out, int64_t n, int64_t N, int64_t K,
                            int64_t row_bytes, hipStream_t st);
 hipError_t launch_matmul_q2_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
-int64_t matmul_q2_k_max_blocks();
-hipError_t launch_matmul_q4_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
+hipError_t launch_matmul_q4_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
+int64_t matmul_k_max_blocks();
+
 hipError_t launch_matmul_q6_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
 }  // namespace qmm
 
@@ -270,13 +271,14 @@ qmm_status qmm_matmul_q5_1(const void *w, const void *xq, float *y, int64_t M, i
 
 qmm_status qmm_matmul_q2_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream) {
-    if (K / 256 > qmm::matmul_q2_k_max_blocks()) return QMM_E_SHAPE;
+    if (K / 256 > qmm::matmul_k_max_blocks()) return QMM_E_SHAPE;
     return matmul(qmm::launch_matmul_q2_k_mfma, w, xq8k, y, M, N, K, 256, qmm::kQ2KBytes, qmm::kQ8KBytes, stream);
 }
 
 qmm_status qmm_matmul_q4_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream) {
-    return matmul(qmm::launch_matmul_q4_k, w, xq8k, y, M, N, K, 256, qmm::kQ4KBytes, qmm::kQ8KBytes, stream);
+    if (K / 256 > qmm::matmul_k_max_blocks()) return QMM_E_SHAPE;
+    return matmul(qmm::launch_matmul_q4_k_mfma, w, xq8k, y, M, N, K, 256, qmm::kQ4KBytes, qmm::kQ8KBytes, stream);
 }
 
 qmm_status qmm_matmul_q6_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,

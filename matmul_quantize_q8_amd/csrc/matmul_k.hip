@@ -1,4 +1,4 @@
-// Prefill matmul, Q2_K weights x Q8_K activations, on MFMA.
+// Prefill matmul, Q2_K or Q4_K weights x Q8_K activations, on MFMA.
 //
 // Per super-block s of 256 values (minfer "The payoff: a K-quant dot kernel,
 // walked": a value term and a min term):
@@ -37,6 +37,16 @@
 // starts at 0x4B400000, so the result read as f32 is F = 1.5*2^23 + V
 // (|V| <= 256*45*128 < 2^22); u = fma(F, d, -1.5*2^23*d) = V*d (one rounding),
 // t = fma(-dmin, Mn, u), acc = fma(t, d8, acc).
+//
+// Q4_K weights (the same staging, weight rows of 144 bytes in nine chunks):
+// sub-block j of 32 values has a 6-bit scale sc_j and min m_j (minfer "The
+// payoff: a K-quant dot kernel, walked"), and sc_j q <= 63 * 15 is no int8,
+// so K-step t (= sub-block t) gets its own exact int32 tile
+// I_t = sum q x (one v_mfma_i32_32x32x32_i8 on the 4-bit codes) and
+// V = sum_t sc_t I_t accumulates in int32 with one v_mad_i32_i24 per output
+// (|I_t| <= 32*15*128 < 2^23, |V| < 2^25); the min term is the same f16
+// MFMA over the block sums (m <= 63, |Mn| < 2^22, exact), and the fold is
+// acc += d8 * ((float)V * d - dmin * Mn).
 // Output lane layout of a 32x32 MFMA tile: lane l, register r holds row
 // 8(r/4) + 4(l/32) + r%4 and column l%32.
 #include "qmm_device.h"
@@ -51,25 +61,32 @@ constexpr int BN = 256;                        // weight rows per workgroup tile
 constexpr int NW = 8;                          // waves, each all 128 tokens x 32 weight rows
 constexpr int NT = NW * kWave;
 constexpr int XC = 19;                         // 16-byte chunks per activation row per stage
-constexpr int WC = 7;                          // per weight row
 constexpr int XQ = BM * XC / kWave;            // 38 wave loads of activation chunks
-constexpr int WQ = BN * WC / kWave;            // 28 of weight chunks
-constexpr int NQ = XQ + WQ;                    // 66 wave loads per stage
-constexpr int PER_WAVE = (NQ + NW - 1) / NW;   // 9 (waves 2..7 repeat one in the last round)
 constexpr int XROW = 16 * XC;                  // 304-byte LDS activation row
-constexpr int WROW = 16 * WC;                  // 112-byte LDS weight row
 constexpr int WOFF = BM * XROW;                // weight rows start (bytes into a stage buffer)
-constexpr int STAGE = (BM * XC + BN * WC) * 16;   // 67,584 bytes
 constexpr int NBUF = 2;
-constexpr int D8 = NBUF * STAGE;               // per-wave f32 d8 of the 128 rows
-constexpr int LDS_BYTES = D8 + NW * BM * 4;    // 139,264
 constexpr float kBias = 12582912.0f;           // 1.5 * 2^23, bit pattern 0x4B400000
-// global offsets (within a super-block) of the chunks of a row
+// global offsets (within a super-block) of the chunks of an activation row
 constexpr int xchunk(int c) { return c < 16 ? 4 + 16 * c : (c == 16 ? 260 : (c == 17 ? 276 : 0)); }
-constexpr int wchunk(int c) { return c < 5 ? 16 * c : 68; }
-static_assert(XQ * kWave == BM * XC && WQ * kWave == BN * WC && NQ > NW * (PER_WAVE - 1),
-              "a stage splits into whole wave loads; only the last round of loads has gaps");
-static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
+
+// Per weight format: Q2_K rows of 84 bytes in 7 chunks (scales at 0, qs at
+// 16, the chunk holding d and dmin at 80, one spare), Q4_K rows of 144 bytes
+// in 9 chunks (d, dmin, scales, qs: the super-block as it is).
+template <int F> struct KW {
+    static constexpr int WB = F == F_Q2_K ? kQ2KBytes : kQ4KBytes;
+    static constexpr int WC = F == F_Q2_K ? 7 : 9;              // 16-byte chunks per weight row
+    static constexpr int WROW = 16 * WC;                        // 112- or 144-byte LDS weight row
+    static constexpr int WQ = BN * WC / kWave;                  // 28 or 36 wave loads of weight chunks
+    static constexpr int NQ = XQ + WQ;                          // 66 or 74 wave loads per stage
+    static constexpr int PER_WAVE = (NQ + NW - 1) / NW;         // 9 or 10
+    static constexpr int STAGE = (BM * XC + BN * WC) * 16;      // 67,584 or 75,776 bytes
+    static constexpr int D8 = NBUF * STAGE;                     // per-wave f32 d8 of the 128 rows
+    static constexpr int LDS_BYTES = D8 + NW * BM * 4;          // 139,264 or 155,648
+    static constexpr int wchunk(int c) { return F == F_Q2_K ? (c < 5 ? 16 * c : 68) : 16 * c; }
+    static_assert(XQ * kWave == BM * XC && WQ * kWave == BN * WC && NQ > NW * (PER_WAVE - 1),
+                  "a stage splits into whole wave loads; only the last round of loads has gaps");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
+};
 }  // namespace mk
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -87,21 +104,45 @@ __device__ __forceinline__ void buffer16_to_lds(__amdgpu_buffer_rsrc_t r, uint32
 }
 #pragma clang diagnostic pop
 
-__global__ __launch_bounds__(mk::NT) void k_matmul_q2_k(const uint8_t *__restrict__ w,
-                                                        const uint8_t *__restrict__ xq, float *__restrict__ y,
-                                                        int M, int N, int ns, int tiles_m) {
+// f(integral_constant<int, K>) for K = 0 .. N-1, in order.
+template <class Fn, int... K>
+__device__ __forceinline__ void for_each_index(Fn &&f, std::integer_sequence<int, K...>) {
+    (f(std::integral_constant<int, K>()), ...);
+}
+
+// Q4_K's packed 6-bit scales: scale and min of sub-block s from the three
+// scale dwords (bytes 4..15 of the super-block).
+__device__ __forceinline__ void q4k_sc_m(uint32_t s0, uint32_t s1, uint32_t s2, int s, int &sc, int &m) {
+    const uint32_t sh = 8u * (uint32_t)(s & 3);
+    const uint32_t A = (s0 >> sh) & 0xffu, B = (s1 >> sh) & 0xffu, C = (s2 >> sh) & 0xffu;
+    if (s < 4) {
+        sc = (int)(A & 63u);
+        m = (int)(B & 63u);
+    } else {
+        sc = (int)((C & 15u) | ((A >> 6) << 4));
+        m = (int)((C >> 4) | ((B >> 6) << 4));
+    }
+}
+
+template <int F>
+__global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+                                                     float *__restrict__ y, int M, int N, int ns, int tiles_m) {
     using namespace mk;
+    using W = KW<F>;
+    constexpr int WC = W::WC, WQ = W::WQ, NQ = W::NQ, PER_WAVE = W::PER_WAVE, WROW = W::WROW, STAGE = W::STAGE,
+                  D8 = W::D8;
+    (void)WQ;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = uniform(t >> 6);
     const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
     const int m0 = mt * BM, n0 = nt * BN;
-    const uint32_t xrow = (uint32_t)ns * kQ8KBytes, wrow = (uint32_t)ns * kQ2KBytes;
+    const uint32_t xrow = (uint32_t)ns * kQ8KBytes, wrow = (uint32_t)ns * W::WB;
 
-    // DMA: wave load q = wave + 8k (k < 9) of a stage is chunk load q of the
-    // stage image (activation chunks for q < 38, weight chunks after) and
-    // lands at byte 1024 q of the stage buffer; waves 2..7 have no load
-    // q = 66..71 and repeat their load k = 7 instead (same bytes to the same
+    // DMA: wave load q = wave + 8k (k < PER_WAVE) of a stage is chunk load q
+    // of the stage image (activation chunks for q < 38, weight chunks after)
+    // and lands at byte 1024 q of the stage buffer; a wave whose last q is
+    // past NQ repeats its previous load instead (same bytes to the same
     // place), so that every wave issues the same count.  Rows past the matrix
     // re-read its last row (their results are not stored).
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
@@ -119,7 +160,7 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_q2_k(const uint8_t *__restric
             voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (uint32_t)xchunk(c);
         } else {
             const int f = kWave * (q - XQ) + lane, row = f / WC, c = f - WC * row;
-            voff[k] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + (uint32_t)wchunk(c);
+            voff[k] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + (uint32_t)W::wchunk(c);
         }
     }
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
@@ -127,9 +168,8 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_q2_k(const uint8_t *__restric
     constexpr int KL = PER_WAVE - 1;
     // LDS offset of the last load of a stage (or of the load it repeats)
     const uint32_t last_off = (uint32_t)uniform(1024 * NW * (wave + NW * KL >= NQ ? KL - 1 : KL));
-    static_assert(PER_WAVE == 9, "the load calls below are written for this split");
     auto dma = [&](int s, int b) __attribute__((always_inline)) {
-        const int sx = s * kQ8KBytes, sw = s * kQ2KBytes;
+        const int sx = s * kQ8KBytes, sw = s * W::WB;
         const uint32_t base = m0w + (uint32_t)(b * STAGE);
         auto one = [&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
@@ -140,15 +180,7 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_q2_k(const uint8_t *__restric
             else
                 buffer16_to_lds<1024 * NW * k>(isw ? wr : xr, base, voff[k], soff);
         };
-        one(std::integral_constant<int, 0>());
-        one(std::integral_constant<int, 1>());
-        one(std::integral_constant<int, 2>());
-        one(std::integral_constant<int, 3>());
-        one(std::integral_constant<int, 4>());
-        one(std::integral_constant<int, 5>());
-        one(std::integral_constant<int, 6>());
-        one(std::integral_constant<int, 7>());
-        one(std::integral_constant<int, 8>());
+        for_each_index(one, std::make_integer_sequence<int, PER_WAVE>());
     };
 
     const int lr = lane & 31, lh = lane >> 5;
@@ -195,66 +227,139 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_q2_k(const uint8_t *__restric
     // One stage: the wave's B tile (32 weight rows) against all four A tiles
     // (128 tokens), so that each B operand is built once per workgroup.
     auto compute = [&](const uint8_t *sb) __attribute__((always_inline)) {
-        // d8 of the 128 activation rows into the wave's private array
-        d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * lane + 288);
-        d8w[64 + lane] = *reinterpret_cast<const float *>(sb + XROW * (64 + lane) + 288);
-        // the B tile's 16 scale bytes and d, dmin
-        const uint4 scl = rd16(sb + wb);
-        const uint32_t dd = rd4(sb + wb + 92);
-        uint4 qs = rd16(sb + wb + 16 + 16 * lh);
-        // B operand of K-step kt: group 2kt + lh, table [0, sc, 2sc, 3sc]
-        auto build_b = [&](int kt, const uint4 &q) __attribute__((always_inline)) {
-            const int g = 2 * kt + lh, sft = 2 * (kt & 3);
-            const uint32_t sw = (g < 4) ? scl.x : (g < 8) ? scl.y : (g < 12) ? scl.z : scl.w;
-            const uint32_t sc = (sw >> (8 * (g & 3))) & 15u;
-            const uint32_t tab = __umul24(sc << 8, 0x030201u);   // sc * 0x03020100
-            const uint32_t d4[4] = {q.x, q.y, q.z, q.w};
-            v4i b;
+        if constexpr (F == F_Q2_K) {
+            // d8 of the 128 activation rows into the wave's private array
+            d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * lane + 288);
+            d8w[64 + lane] = *reinterpret_cast<const float *>(sb + XROW * (64 + lane) + 288);
+            // the B tile's 16 scale bytes and d, dmin
+            const uint4 scl = rd16(sb + wb);
+            const uint32_t dd = rd4(sb + wb + 92);
+            uint4 qs = rd16(sb + wb + 16 + 16 * lh);
+            // B operand of K-step kt: group 2kt + lh, table [0, sc, 2sc, 3sc]
+            auto build_b = [&](int kt, const uint4 &q) __attribute__((always_inline)) {
+                const int g = 2 * kt + lh, sft = 2 * (kt & 3);
+                const uint32_t sw = (g < 4) ? scl.x : (g < 8) ? scl.y : (g < 12) ? scl.z : scl.w;
+                const uint32_t sc = (sw >> (8 * (g & 3))) & 15u;
+                const uint32_t tab = __umul24(sc << 8, 0x030201u);   // sc * 0x03020100
+                const uint32_t d4[4] = {q.x, q.y, q.z, q.w};
+                v4i b;
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) b[e] = (int)__builtin_amdgcn_perm(0u, tab, (d4[e] >> sft) & 0x03030303u);
+                return b;
+            };
+            // value term: eight K-steps of int8 MFMA, int32 accumulation from the bias
+            v16i v[4];
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = bias;
+    #pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                if (kt == 4) qs = rd16(sb + wb + 16 + 32 + 16 * lh);
+                const v4i b = build_b(kt, qs);
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v4i a = as_v4i(rd16(sb + xa + XROW * 32 * i + 32 * kt + 16 * lh));
+                    v[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v[i], 0, 0, 0);
+                }
+            }
+            float dw = half_lo(dd), ndm = -half_hi(dd);
+            // keep the f32 values (an f16 operand would make each fold FMA a
+            // half-rate v_fma_mix)
+            asm volatile("" : "+v"(dw), "+v"(ndm));
+            const float nbw = dw * -kBias;   // exact: 11 + 2 significant bits
+            // min term, one f16 MFMA per A tile, and the fold:
+            // acc += d8 * (d * V - dmin * Mn)
+            const uint32_t mlo = lh ? scl.z : scl.x, mhi = lh ? scl.w : scl.y;   // groups 8h .. 8h+7
+            const v8h bm = mins_to_h(mlo, mhi);
+            const v16f z = {};
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const v8h am = i16x8_to_h(rd16(sb + xa + XROW * 32 * i + 256 + 16 * lh));
+                const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(am, bm, z, 0, 0, 0);
+                // d8 of output rows 8a4 + 4lh + c, four at a time
+                const float4 *p = reinterpret_cast<const float4 *>(d8w + 32 * i + 4 * lh);
+    #pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const float4 qd = p[2 * a4];
+                    const float d8[4] = {qd.x, qd.y, qd.z, qd.w};
+    #pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int r = 4 * a4 + c;
+                        const int e = v[i][r];
+                        const float u = fmaf(__int_as_float(e), dw, nbw);
+                        const float tt = fmaf(ndm, mn[r], u);
+                        acc[i][r] = fmaf(tt, d8[c], acc[i][r]);
+                    }
+                }
+            }
+        } else {
+            // d8 of the 128 activation rows into the wave's private array
+            d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * lane + 288);
+            d8w[64 + lane] = *reinterpret_cast<const float *>(sb + XROW * (64 + lane) + 288);
+            // the B tile row's d, dmin and packed scales
+            const uint32_t dd = rd4(sb + wb), s0 = rd4(sb + wb + 4), s1 = rd4(sb + wb + 8), s2 = rd4(sb + wb + 12);
+            int sc[8], mm[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) b[e] = (int)__builtin_amdgcn_perm(0u, tab, (d4[e] >> sft) & 0x03030303u);
-            return b;
-        };
-        // value term: eight K-steps of int8 MFMA, int32 accumulation from the bias
-        v16i v[4];
+            for (int j = 0; j < 8; ++j) q4k_sc_m(s0, s1, s2, j, sc[j], mm[j]);
+            // value term: sub-block kt is K-step kt, the 4-bit codes of qs
+            // chunk kt/2 (low nibbles for even kt, high for odd); one exact
+            // int32 tile per sub-block, V += sc * I in int32
+            int V[4][16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = bias;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt) {
-            if (kt == 4) qs = rd16(sb + wb + 16 + 32 + 16 * lh);
-            const v4i b = build_b(kt, qs);
+                for (int r = 0; r < 16; ++r) V[i][r] = 0;
+            uint4 qs = {};
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                if ((kt & 1) == 0) qs = rd16(sb + wb + 16 + 32 * (kt >> 1) + 16 * lh);
+                const uint32_t sh = 4u * (uint32_t)(kt & 1);
+                const v4i b = v4i{(int)((qs.x >> sh) & 0x0f0f0f0fu), (int)((qs.y >> sh) & 0x0f0f0f0fu),
+                                  (int)((qs.z >> sh) & 0x0f0f0f0fu), (int)((qs.w >> sh) & 0x0f0f0f0fu)};
+                const v16i zero = {};
+                // one tile at a time (one int32 tile live): the other wave
+                // of the SIMD covers the MFMA latency
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v4i a = as_v4i(rd16(sb + xa + XROW * 32 * i + 32 * kt + 16 * lh));
+                    const v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int e = I[r];
+                        V[i][r] = __mul24(sc[kt], e) + V[i][r];   // v_mad_i32_i24
+                        // pin the running sum: left to itself the compiler
+                        // re-associates the accumulation across K-steps and
+                        // keeps the products of several steps live
+                        asm volatile("" : "+v"(V[i][r]));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            float dw = half_lo(dd), ndm = -half_hi(dd);
+            // keep the f32 values (an f16 operand would make each fold FMA a
+            // half-rate v_fma_mix)
+            asm volatile("" : "+v"(dw), "+v"(ndm));
+            // min term, one f16 MFMA per A tile: groups 8h .. 8h+7 are
+            // sub-blocks 4h .. 4h+3, two groups each
+            v8h bm;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bm[e] = (_Float16)(lh ? mm[4 + (e >> 1)] : mm[e >> 1]);
+            const v16f z = {};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const v4i a = as_v4i(rd16(sb + xa + XROW * 32 * i + 32 * kt + 16 * lh));
-                v[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v[i], 0, 0, 0);
-            }
-        }
-        float dw = half_lo(dd), ndm = -half_hi(dd);
-        // keep the f32 values (an f16 operand would make each fold FMA a
-        // half-rate v_fma_mix)
-        asm volatile("" : "+v"(dw), "+v"(ndm));
-        const float nbw = dw * -kBias;   // exact: 11 + 2 significant bits
-        // min term, one f16 MFMA per A tile, and the fold:
-        // acc += d8 * (d * V - dmin * Mn)
-        const uint32_t mlo = lh ? scl.z : scl.x, mhi = lh ? scl.w : scl.y;   // groups 8h .. 8h+7
-        const v8h bm = mins_to_h(mlo, mhi);
-        const v16f z = {};
+                const v8h am = i16x8_to_h(rd16(sb + xa + XROW * 32 * i + 256 + 16 * lh));
+                const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(am, bm, z, 0, 0, 0);
+                // d8 of output rows 8a4 + 4lh + c, four at a time
+                const float4 *p = reinterpret_cast<const float4 *>(d8w + 32 * i + 4 * lh);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const v8h am = i16x8_to_h(rd16(sb + xa + XROW * 32 * i + 256 + 16 * lh));
-            const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(am, bm, z, 0, 0, 0);
-            // d8 of output rows 8a4 + 4lh + c, four at a time
-            const float4 *p = reinterpret_cast<const float4 *>(d8w + 32 * i + 4 * lh);
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const float4 qd = p[2 * a4];
+                    const float d8[4] = {qd.x, qd.y, qd.z, qd.w};
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const float4 qd = p[2 * a4];
-                const float d8[4] = {qd.x, qd.y, qd.z, qd.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int r = 4 * a4 + c;
-                    const int e = v[i][r];
-                    const float u = fmaf(__int_as_float(e), dw, nbw);
-                    const float tt = fmaf(ndm, mn[r], u);
-                    acc[i][r] = fmaf(tt, d8[c], acc[i][r]);
+                    for (int c = 0; c < 4; ++c) {
+                        const int r = 4 * a4 + c;
+                        const float tt = fmaf(ndm, mn[r], (float)V[i][r] * dw);
+                        acc[i][r] = fmaf(tt, d8[c], acc[i][r]);
+                    }
                 }
             }
         }
@@ -286,23 +391,32 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_q2_k(const uint8_t *__restric
 }
 
 // Largest super-block count whose tile offsets fit the 32-bit buffer offsets
-// (128 activation rows of ns * 292 bytes).
+// (128 activation rows of ns * 292 bytes; 256 weight rows take fewer).
 constexpr int64_t kMatmulKMaxBlocks = (((int64_t)1 << 31) - 1) / (mk::BM * kQ8KBytes);
 
-int64_t matmul_q2_k_max_blocks() { return kMatmulKMaxBlocks; }
+int64_t matmul_k_max_blocks() { return kMatmulKMaxBlocks; }
 
-hipError_t launch_matmul_q2_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
+template <int F>
+static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
     if (ns > kMatmulKMaxBlocks) return hipErrorInvalidValue;
     static int lds_ok = 0;
-    const hipError_t e = allow_dynamic_lds((const void *)k_matmul_q2_k, (size_t)mk::LDS_BYTES, lds_ok);
+    const hipError_t e = allow_dynamic_lds((const void *)k_matmul_k<F>, (size_t)mk::KW<F>::LDS_BYTES, lds_ok);
     if (e != hipSuccess) return e;
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
     int tiles_m = (M + mk::BM - 1) / mk::BM;
     const int64_t tiles = (int64_t)tiles_m * ((N + mk::BN - 1) / mk::BN);
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&ns, (void *)&tiles_m};
-    return hipLaunchKernel((const void *)k_matmul_q2_k, dim3((unsigned)tiles), dim3(mk::NT), args,
-                           (size_t)mk::LDS_BYTES, st);
+    return hipLaunchKernel((const void *)k_matmul_k<F>, dim3((unsigned)tiles), dim3(mk::NT), args,
+                           (size_t)mk::KW<F>::LDS_BYTES, st);
+}
+
+hipError_t launch_matmul_q2_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
+    return launch_k<F_Q2_K>(w, xq, y, M, N, ns, st);
+}
+
+hipError_t launch_matmul_q4_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
+    return launch_k<F_Q4_K>(w, xq, y, M, N, ns, st);
 }
 
 }  // namespace qmm

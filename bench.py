@@ -259,7 +259,17 @@ def bench_prefill(args, torch, q, synth):
         q.qmm_matmul_q4_k(wq4k, X8k, Y, M, N, K)
     m4_ms, m4_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q4_k(wq4k, X8k, Y, M, N, K), args.prefill_steps, 4)
     log(f"prefill q4_k weights: matmul {m4_ms * 1e3:.1f} us (best batch {m4_min * 1e3:.1f})")
-    del wq4k, X8k
+    del wq4k
+    # Q6_K weights x Q8_K activations (weights of the Q6_K workload)
+    w = torch.from_numpy(synth.weights(N, K, config=6)).cuda()
+    wq6k = torch.empty(N * q.row_bytes("q6_k", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q6_k(w, wq6k, N, K)
+    del w
+    for _ in range(4):
+        q.qmm_matmul_q6_k(wq6k, X8k, Y, M, N, K)
+    m6_ms, m6_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q6_k(wq6k, X8k, Y, M, N, K), args.prefill_steps, 4)
+    log(f"prefill q6_k weights: matmul {m6_ms * 1e3:.1f} us (best batch {m6_min * 1e3:.1f})")
+    del wq6k, X8k
     return dict(ms_step=ms_step, tops=ops / (ms_step * 1e-3) / 1e12,
                 roofline={"kernel": "qmm::k_matmul_q4_0", "bound": "mfma", "achieved": round(tops_kernel, 2),
                           "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
@@ -277,7 +287,11 @@ def bench_prefill(args, torch, q, synth):
                 q4_k_weights={"kernel": "qmm::k_matmul_k<Q4_K>", "kernel_us_mean": round(m4_ms * 1e3, 2),
                               "achieved": round(ops / (m4_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m4_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
-                              "traffic": committed_traffic("k_matmul_q4_k", "2048x12288x4096")})
+                              "traffic": committed_traffic("k_matmul_q4_k", "2048x12288x4096")},
+                q6_k_weights={"kernel": "qmm::k_matmul_k<Q6_K>", "kernel_us_mean": round(m6_ms * 1e3, 2),
+                              "achieved": round(ops / (m6_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
+                              "frac": round(ops / (m6_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                              "traffic": committed_traffic("k_matmul_q6_k", "2048x12288x4096")})
 
 
 # The other decode workloads, one matvec launch each, weights rotated like the
@@ -455,7 +469,7 @@ def main():
               "steps": args.prefill_steps, "warmup": args.prefill_warmup, "ms_per_step": round(pre["ms_step"], 4),
               "step": "quantize_q8_0 (2048x4096) + matmul_q4_0", "roofline": pre["roofline"],
               "q8_0_weights": pre["q8_0_weights"], "q2_k_weights": pre["q2_k_weights"],
-              "q4_k_weights": pre["q4_k_weights"], "cpu_baseline": cpu_pre}
+              "q4_k_weights": pre["q4_k_weights"], "q6_k_weights": pre["q6_k_weights"], "cpu_baseline": cpu_pre}
         if dec is None:
             out.update({"value": pf["value"], "unit": "TOPS", "steps": pf["steps"], "warmup": pf["warmup"],
                         "ms_per_step": pf["ms_per_step"], "config": {"workload": pf["workload"]},

@@ -209,10 +209,12 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
  * plus an f16 MFMA for the min term; qmm_matmul_q4_k runs one int8 MFMA tile
  * per 32-value sub-block on the 4-bit codes, applies the 6-bit sub-block
  * scales in int32 and takes the min term from the same f16 MFMA over the
- * activation's block sums.  Both return QMM_E_SHAPE when 128 rows of Q8_K
- * activations (128 * K/256 * 292 bytes) exceed 2^31 - 1 bytes.  The other
- * formats run the matvec kernel once per token (correct for any M, not tuned
- * for prefill). */
+ * activation's block sums; qmm_matmul_q6_k runs one int8 MFMA tile per
+ * 16-value group on the unsigned 6-bit codes, applies the signed group scales
+ * in int32 and takes the offset of 32 from an f16 MFMA over the block sums.
+ * All three return QMM_E_SHAPE when 128 rows of Q8_K activations
+ * (128 * K/256 * 292 bytes) exceed 2^31 - 1 bytes.  The other formats run the
+ * matvec kernel once per token (correct for any M, not tuned for prefill). */
 qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
 qmm_status qmm_matmul_q8_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,

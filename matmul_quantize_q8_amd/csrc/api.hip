@@ -38,9 +38,9 @@ hipError_t launch_get_rows(int fmt, const void *w, const int32_t *ids, float *ou
                            int64_t row_bytes, hipStream_t st);
 hipError_t launch_matmul_q2_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
 hipError_t launch_matmul_q4_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
+hipError_t launch_matmul_q6_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
 int64_t matmul_k_max_blocks();
 
-hipError_t launch_matmul_q6_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
 }  // namespace qmm
 
 namespace {
@@ -283,7 +283,8 @@ qmm_status qmm_matmul_q4_k(const void *w, const void *xq8k, float *y, int64_t M,
 
 qmm_status qmm_matmul_q6_k(const void *w, const void *xq8k, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream) {
-    return matmul(qmm::launch_matmul_q6_k, w, xq8k, y, M, N, K, 256, qmm::kQ6KBytes, qmm::kQ8KBytes, stream);
+    if (K / 256 > qmm::matmul_k_max_blocks()) return QMM_E_SHAPE;
+    return matmul(qmm::launch_matmul_q6_k_mfma, w, xq8k, y, M, N, K, 256, qmm::kQ6KBytes, qmm::kQ8KBytes, stream);
 }
 
 static qmm_status get_rows(int fmt, const void *w, const int32_t *ids, float *out, int64_t n, int64_t N, int64_t K,

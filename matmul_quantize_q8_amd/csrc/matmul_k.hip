@@ -1,4 +1,4 @@
-// Prefill matmul, Q2_K or Q4_K weights x Q8_K activations, on MFMA.
+// Prefill matmul, Q2_K, Q4_K or Q6_K weights x Q8_K activations, on MFMA.
 //
 // Per super-block s of 256 values (minfer "The payoff: a K-quant dot kernel,
 // walked": a value term and a min term):
@@ -57,8 +57,7 @@ namespace qmm {
 
 namespace mk {
 constexpr int BM = 128;                        // tokens per workgroup tile
-constexpr int BN = 256;                        // weight rows per workgroup tile
-constexpr int NW = 8;                          // waves, each all 128 tokens x 32 weight rows
+constexpr int NW = 8;                          // waves per workgroup
 constexpr int NT = NW * kWave;
 constexpr int XC = 19;                         // 16-byte chunks per activation row per stage
 constexpr int XQ = BM * XC / kWave;            // 38 wave loads of activation chunks
@@ -71,20 +70,30 @@ constexpr int xchunk(int c) { return c < 16 ? 4 + 16 * c : (c == 16 ? 260 : (c =
 
 // Per weight format: Q2_K rows of 84 bytes in 7 chunks (scales at 0, qs at
 // 16, the chunk holding d and dmin at 80, one spare), Q4_K rows of 144 bytes
-// in 9 chunks (d, dmin, scales, qs: the super-block as it is).
+// in 9 chunks (d, dmin, scales, qs: the super-block as it is), Q6_K rows of
+// 210 bytes in 14 (ql at 0, qh at 128, scales at 192, the chunk holding d at
+// 208).  Q2_K and Q4_K: 256 weight rows per workgroup, each wave all 128
+// tokens (four A tiles) x 32 rows; Q6_K, whose rows do not leave room for
+// 256 in two stage buffers: 128 weight rows, each wave 64 tokens (two A
+// tiles) x 32 rows.
 template <int F> struct KW {
-    static constexpr int WB = F == F_Q2_K ? kQ2KBytes : kQ4KBytes;
-    static constexpr int WC = F == F_Q2_K ? 7 : 9;              // 16-byte chunks per weight row
-    static constexpr int WROW = 16 * WC;                        // 112- or 144-byte LDS weight row
-    static constexpr int WQ = BN * WC / kWave;                  // 28 or 36 wave loads of weight chunks
-    static constexpr int NQ = XQ + WQ;                          // 66 or 74 wave loads per stage
-    static constexpr int PER_WAVE = (NQ + NW - 1) / NW;         // 9 or 10
-    static constexpr int STAGE = (BM * XC + BN * WC) * 16;      // 67,584 or 75,776 bytes
-    static constexpr int D8 = NBUF * STAGE;                     // per-wave f32 d8 of the 128 rows
-    static constexpr int LDS_BYTES = D8 + NW * BM * 4;          // 139,264 or 155,648
-    static constexpr int wchunk(int c) { return F == F_Q2_K ? (c < 5 ? 16 * c : 68) : 16 * c; }
+    static constexpr int WB = F == F_Q2_K ? kQ2KBytes : F == F_Q4_K ? kQ4KBytes : kQ6KBytes;
+    static constexpr int WC = F == F_Q2_K ? 7 : F == F_Q4_K ? 9 : 14;   // 16-byte chunks per weight row
+    static constexpr int BN = F == F_Q6_K ? 128 : 256;          // weight rows per workgroup tile
+    static constexpr int TI = F == F_Q6_K ? 2 : 4;              // A tiles (of 32 tokens) per wave
+    static constexpr int WROW = 16 * WC;                        // LDS weight row
+    static constexpr int WQ = BN * WC / kWave;                  // wave loads of weight chunks
+    static constexpr int NQ = XQ + WQ;                          // 66, 74 or 66 wave loads per stage
+    static constexpr int PER_WAVE = (NQ + NW - 1) / NW;         // 9, 10 or 9
+    static constexpr int STAGE = (BM * XC + BN * WC) * 16;      // 67,584, 75,776 or 67,584 bytes
+    static constexpr int D8 = NBUF * STAGE;                     // per-wave f32 d8 of its 32 TI rows
+    static constexpr int LDS_BYTES = D8 + NW * 32 * TI * 4;
+    static constexpr int wchunk(int c) {
+        return F == F_Q2_K ? (c < 5 ? 16 * c : 68) : F == F_Q4_K ? 16 * c : (c < 13 ? 16 * c : 194);
+    }
     static_assert(XQ * kWave == BM * XC && WQ * kWave == BN * WC && NQ > NW * (PER_WAVE - 1),
                   "a stage splits into whole wave loads; only the last round of loads has gaps");
+    static_assert(NW * 32 * TI == BM * BN / 32, "the waves cover the workgroup tile");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
 }  // namespace mk
@@ -130,7 +139,7 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
     using namespace mk;
     using W = KW<F>;
     constexpr int WC = W::WC, WQ = W::WQ, NQ = W::NQ, PER_WAVE = W::PER_WAVE, WROW = W::WROW, STAGE = W::STAGE,
-                  D8 = W::D8;
+                  D8 = W::D8, BN = W::BN, TI = W::TI;
     (void)WQ;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63;
@@ -184,16 +193,18 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
     };
 
     const int lr = lane & 31, lh = lane >> 5;
-    const int xa = XROW * lr;                            // A row lr (tile i: +32i rows)
-    const int wb = WOFF + WROW * (32 * wave + lr);       // B row 32 wave + lr
-    float *d8w = reinterpret_cast<float *>(lds + D8 + 4 * BM * wave);
+    // the wave's tokens 32 TI wm .. and weight rows 32 wn ..
+    const int wm = TI == 4 ? 0 : wave & 1, wn = TI == 4 ? wave : wave >> 1;
+    const int xa = XROW * (32 * TI * wm + lr);           // A row lr of the wave (tile i: +32i rows)
+    const int wb = WOFF + WROW * (32 * wn + lr);         // B row 32 wn + lr
+    float *d8w = reinterpret_cast<float *>(lds + D8 + 4 * 32 * TI * wave);
 
     v16i bias;
 #pragma unroll
     for (int r = 0; r < 16; ++r) bias[r] = 0x4B400000;
-    float acc[4][16];
+    float acc[TI][16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
@@ -291,7 +302,7 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
                     }
                 }
             }
-        } else {
+        } else if constexpr (F == F_Q4_K) {
             // d8 of the 128 activation rows into the wave's private array
             d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * lane + 288);
             d8w[64 + lane] = *reinterpret_cast<const float *>(sb + XROW * (64 + lane) + 288);
@@ -362,6 +373,88 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
                     }
                 }
             }
+        } else {
+            // Q6_K: value 128hh + 32k + l of a super-block takes its low 4 bits
+            // from ql[64hh + 32(k&1) + l] (low nibble for k < 2, high for
+            // k >= 2) and its high 2 bits from qh[32hh + l] >> 2k, and group
+            // g = 8hh + 2k + l/16 of 16 values has the signed scale sc[g].
+            // A K=16 MFMA per group on the unsigned codes q (0..63) gives
+            // I_g = sum q x; V = sum_g sc_g I_g in int32 (v_mad_i32_i24), and
+            // the offset of 32 is sum_g 32 sc_g bsum_g, one f16 MFMA over the
+            // block sums: the product is d8 d (V - Mn).
+            // d8 of the wave's 64 activation rows into its private array
+            d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * (64 * wm + lane) + 288);
+            const uint4 scl = rd16(sb + wb + 192);
+            auto scale = [&](int g) __attribute__((always_inline)) {
+                const uint32_t sw = g < 4 ? scl.x : g < 8 ? scl.y : g < 12 ? scl.z : scl.w;
+                return (int)(int8_t)(sw >> (8 * (g & 3)));
+            };
+            auto rd8 = [](const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); };
+            int V[2][16];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) V[i][r] = 0;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int gg = 0; gg < 2; ++gg) {
+                    // this lane's 8 values of groups 8hh + 2k + gg: l = 16gg + 8lh ..
+                    const uint2 qa = rd8(sb + wb + 64 * hh + 16 * gg + 8 * lh);
+                    const uint2 qb = rd8(sb + wb + 64 * hh + 32 + 16 * gg + 8 * lh);
+                    const uint2 qh = rd8(sb + wb + 128 + 32 * hh + 16 * gg + 8 * lh);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int g = 8 * hh + 2 * k + gg;
+                        const uint2 ql = (k & 1) ? qb : qa;
+                        const uint32_t nsh = 4u * (uint32_t)(k >> 1), hsh = 2u * (uint32_t)k;
+                        const uint32_t b0 = ((ql.x >> nsh) & 0x0f0f0f0fu) | (((qh.x >> hsh) & 0x03030303u) << 4);
+                        const uint32_t b1 = ((ql.y >> nsh) & 0x0f0f0f0fu) | (((qh.y >> hsh) & 0x03030303u) << 4);
+                        const long b = (long)(((uint64_t)b1 << 32) | b0);
+                        const int sc = scale(g);
+                        const v16i zero = {};
+                        // one tile at a time (one int32 tile live); the other
+                        // wave of the SIMD covers the MFMA latency
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const uint2 av = rd8(sb + xa + XROW * 32 * i + 16 * g + 8 * lh);
+                            const long a = (long)(((uint64_t)av.y << 32) | av.x);
+                            const v16i I = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, b, zero, 0, 0, 0);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int e = I[r];
+                                V[i][r] = __mul24(sc, e) + V[i][r];   // v_mad_i32_i24
+                                asm volatile("" : "+v"(V[i][r]));    // keep the running sum (see Q4_K)
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                }
+            float dw = half_hi(rd4(sb + wb + 220));   // d: bytes 208..209 of the super-block
+            asm volatile("" : "+v"(dw));
+            const float ndw = -dw;
+            // offset term: groups 8h .. 8h+7, 32 sc_g exact in f16
+            v8h bm;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bm[e] = (_Float16)(32 * (lh ? scale(8 + e) : scale(e)));
+            const v16f z = {};
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const v8h am = i16x8_to_h(rd16(sb + xa + XROW * 32 * i + 256 + 16 * lh));
+                const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(am, bm, z, 0, 0, 0);
+                const float4 *p = reinterpret_cast<const float4 *>(d8w + 32 * i + 4 * lh);
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const float4 qd = p[2 * a4];
+                    const float d8[4] = {qd.x, qd.y, qd.z, qd.w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int r = 4 * a4 + c;
+                        const float tt = fmaf(ndw, mn[r], (float)V[i][r] * dw);
+                        acc[i][r] = fmaf(tt, d8[c], acc[i][r]);
+                    }
+                }
+            }
         }
     };
 
@@ -378,13 +471,13 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
     // no LDS-DMA write may still be in flight when the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    const int n = n0 + 32 * wave + lr;
+    const int n = n0 + 32 * wn + lr;
     if (n < N) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const int m = m0 + 32 * TI * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
                 if (m < M) y[(int64_t)m * N + n] = acc[i][r];
             }
     }
@@ -405,7 +498,7 @@ static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
     int tiles_m = (M + mk::BM - 1) / mk::BM;
-    const int64_t tiles = (int64_t)tiles_m * ((N + mk::BN - 1) / mk::BN);
+    const int64_t tiles = (int64_t)tiles_m * ((N + mk::KW<F>::BN - 1) / mk::KW<F>::BN);
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&ns, (void *)&tiles_m};
     return hipLaunchKernel((const void *)k_matmul_k<F>, dim3((unsigned)tiles), dim3(mk::NT), args,
                            (size_t)mk::KW<F>::LDS_BYTES, st);
@@ -417,6 +510,10 @@ hipError_t launch_matmul_q2_k_mfma(const void *w, const void *xq, float *y, int 
 
 hipError_t launch_matmul_q4_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
     return launch_k<F_Q4_K>(w, xq, y, M, N, ns, st);
+}
+
+hipError_t launch_matmul_q6_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
+    return launch_k<F_Q6_K>(w, xq, y, M, N, ns, st);
 }
 
 }  // namespace qmm

@@ -793,9 +793,9 @@ hipError_t launch_matvec_q6_k(const void *w, const void *xq, float *y, int N, in
     return dispatch_mv<F_Q6_K>(w, xq, nullptr, y, 1, N, ns, st);
 }
 
-// Prefill of the formats without an MFMA kernel (Q4_K, Q6_K, Q4_1, Q5_0,
-// Q5_1): the matvec kernel with one grid row per token (the weights are
-// re-read from cache for each token; correct for any M, not tuned).
+// Prefill of the formats without an MFMA kernel (Q4_1, Q5_0, Q5_1): the
+// matvec kernel with one grid row per token (the weights are re-read from
+// cache for each token; correct for any M, not tuned).
 template <int F>
 static hipError_t matmul_by_tokens(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
     constexpr int kMaxY = 65535;
@@ -806,12 +806,6 @@ static hipError_t matmul_by_tokens(const void *w, const void *xq, float *y, int 
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
-}
-hipError_t launch_matmul_q4_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
-    return matmul_by_tokens<F_Q4_K>(w, xq, y, M, N, ns, st);
-}
-hipError_t launch_matmul_q6_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
-    return matmul_by_tokens<F_Q6_K>(w, xq, y, M, N, ns, st);
 }
 hipError_t launch_matmul_q4_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
     return matmul_by_tokens<F_Q4_1>(w, xq, y, M, N, nb, st);

@@ -303,6 +303,7 @@ MATMUL_CASES = [
     ("q4_k", 1, 8, 256), ("q4_k", 9, 70, 1024), ("q4_k", 33, 130, 4096),
     ("q4_k", 128, 256, 256), ("q4_k", 130, 257, 512), ("q4_k", 257, 300, 2304), ("q4_k", 3, 520, 7936),
     ("q6_k", 1, 8, 256), ("q6_k", 9, 70, 1024), ("q6_k", 5, 33, 1280),
+    ("q6_k", 128, 128, 256), ("q6_k", 130, 257, 512), ("q6_k", 257, 129, 2304), ("q6_k", 65, 300, 7936),
     ("q4_1", 9, 70, 1024), ("q5_0", 9, 70, 1024), ("q5_1", 9, 70, 1024), ("q5_0", 5, 3, 96),
 ]
 
@@ -402,6 +403,29 @@ def test_matmul_q4_k_full_size_sampled(env):
     ni = np.concatenate([ni, np.tile(np.arange(0, N, 64), len(edge_m)), np.repeat(edge_n, len(range(0, M, 7)))])
     ref, mag = orc.matmul_sampled("q4_k", wq, xq, mi, ni, K)
     _check(y[mi, ni], ref, mag, "q4_k prefill sampled")
+
+
+def test_matmul_q6_k_full_size_sampled(env):
+    """The 2048 x 12288 x 4096 prefill with Q6_K weights (one int8 MFMA tile
+    per 16-value group on the unsigned codes, signed scales applied in int32,
+    the offset of 32 from an f16 MFMA over the block sums), checked on
+    sampled outputs and whole rows and columns at the tile edges."""
+    torch, q, orc = env
+    M, N, K = 2048, 12288, 4096
+    _say("matmul q6_k full", M, N, K)
+    wq = orc.quantize_q6_k_w(synth.weights(N, K, config=6))
+    xq = orc.quantize_q8_k(synth.activations(M, K, config=6))
+    y = _run_matmul(env, "q6_k", wq, xq, M, N, K)
+    assert np.isfinite(y).all()
+    rng = synth.splitmix64(89, 0, 20000)
+    mi = (rng[:10000] % np.uint64(M)).astype(np.int64)
+    ni = (rng[10000:] % np.uint64(N)).astype(np.int64)
+    edge_m = np.array([0, 63, 64, 127, 128, 2047])
+    edge_n = np.array([0, 31, 32, 127, 128, 12287])
+    mi = np.concatenate([mi, np.repeat(edge_m, N // 64), np.tile(np.arange(0, M, 7), len(edge_n))])
+    ni = np.concatenate([ni, np.tile(np.arange(0, N, 64), len(edge_m)), np.repeat(edge_n, len(range(0, M, 7)))])
+    ref, mag = orc.matmul_sampled("q6_k", wq, xq, mi, ni, K)
+    _check(y[mi, ni], ref, mag, "q6_k prefill sampled")
 
 
 def test_matmul_rows_equal_matvec(env):

@@ -511,16 +511,24 @@ def test_graph_replay_matches_eager(env):
     yv = torch.empty(N, dtype=torch.float32, device="cuda")
     yf = torch.empty(N, dtype=torch.float32, device="cuda")
     ym = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    # the K-quant prefill kernels (dynamic LDS of up to 152 KB) in the same graph
+    wk = {f: _dev(torch, orc.quantize_w(f, w)) for f in ("q2_k", "q4_k", "q6_k")}
+    x8k = torch.empty(M * q.row_bytes("q8_k", K), dtype=torch.uint8, device="cuda")
+    yk = {f: torch.empty((M, N), dtype=torch.float32, device="cuda") for f in wk}
 
     def work():
         q.qmm_quantize_q8_0(xd, xq, M, K)
         q.qmm_matvec_q4_0(wq, xq, yv, N, K)
         q.qmm_quantize_matvec_q4_0(wq, xd[1], xq1, yf, N, K)
         q.qmm_matmul_q4_0(wq, xq, ym, M, N, K)
+        q.qmm_quantize_q8_k(xd, x8k, M, K)
+        for f in wk:
+            q.MATMUL[f](wk[f], x8k, yk[f], M, N, K)
 
     work()
     torch.cuda.synchronize()
     ref_v, ref_m, ref_q, ref_f, ref_q1 = yv.clone(), ym.clone(), xq.clone(), yf.clone(), xq1.clone()
+    ref_k = {f: yk[f].clone() for f in yk}
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         work()
@@ -528,6 +536,8 @@ def test_graph_replay_matches_eager(env):
         yv.fill_(float("nan"))
         yf.fill_(float("nan"))
         ym.fill_(float("nan"))
+        for f in yk:
+            yk[f].fill_(float("nan"))
         xq.zero_()
         xq1.zero_()
         torch.cuda.synchronize()
@@ -538,5 +548,7 @@ def test_graph_replay_matches_eager(env):
         assert torch.equal(ym, ref_m), rep
         assert torch.equal(yf, ref_f), rep
         assert torch.equal(xq1, ref_q1), rep
+        for f in yk:
+            assert torch.equal(yk[f], ref_k[f]), (f, rep)
         work()                      # eager work between replays
         torch.cuda.synchronize()

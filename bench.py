@@ -416,8 +416,9 @@ def cpu_baseline_prefill(args, q, synth):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on one "
-              "MI355X; the row-sharded multi-GPU design is described, not built)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the kernels run on one "
+              "MI355X; sharding the weight rows over several GPUs is a documented design, not implemented)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -82,6 +82,13 @@ A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced
     (lambda L: L.qmm_get_rows_q4_0(A, A, A, 4, 8, 48, None), 1),
     (lambda L: L.qmm_get_rows_q4_k(A, A + 4, A, 4, 8, 256, None), 3),
     (lambda L: L.qmm_get_rows_q8_0(A, None, A, 4, 8, 64, None), 2),
+    # the smallest K whose 128-row activation tile (Q8_0 or Q8_K) exceeds the
+    # 32-bit buffer offsets of the MFMA prefill kernels
+    (lambda L: L.qmm_matmul_q4_0(A, A, A, 4, 8, 32 * ((2**31 - 1) // (128 * 34) + 1), None), 1),
+    (lambda L: L.qmm_matmul_q8_0(A, A, A, 4, 8, 32 * ((2**31 - 1) // (128 * 34) + 1), None), 1),
+    (lambda L: L.qmm_matmul_q2_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
+    (lambda L: L.qmm_matmul_q4_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
+    (lambda L: L.qmm_matmul_q6_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
 ])
 def test_argument_errors_without_device(q, call, code):
     assert call(q.lib()) == code

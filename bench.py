@@ -238,6 +238,16 @@ def bench_prefill(args, torch, q, synth):
     m8_ms, m8_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q8_0(wq8, Xq, Y, M, N, K), args.prefill_steps, 4)
     log(f"prefill q8_0 weights: matmul {m8_ms * 1e3:.1f} us (best batch {m8_min * 1e3:.1f})")
     del wq8
+    # Q5_0 weights (weights of the Q5_0 workload, the same Q8_0 activations)
+    w = torch.from_numpy(synth.weights(N, K, config=10)).cuda()
+    wq5 = torch.empty(N * q.row_bytes("q5_0", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q5_0(w, wq5, N, K)
+    del w
+    for _ in range(4):
+        q.qmm_matmul_q5_0(wq5, Xq, Y, M, N, K)
+    m5_ms, m5_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q5_0(wq5, Xq, Y, M, N, K), args.prefill_steps, 4)
+    log(f"prefill q5_0 weights: matmul {m5_ms * 1e3:.1f} us (best batch {m5_min * 1e3:.1f})")
+    del wq5
     # Q2_K weights x Q8_K activations (same shape, inputs of the Q2_K workload)
     w = torch.from_numpy(synth.weights(N, K, config=3)).cuda()
     wq2 = torch.empty(N * q.row_bytes("q2_k", K), dtype=torch.uint8, device="cuda")
@@ -280,6 +290,10 @@ def bench_prefill(args, torch, q, synth):
                               "achieved": round(ops / (m8_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m8_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                               "traffic": committed_traffic("k_matmul_q8_0", "2048x12288x4096")},
+                q5_0_weights={"kernel": "qmm::k_matmul_q5_0", "kernel_us_mean": round(m5_ms * 1e3, 2),
+                              "achieved": round(ops / (m5_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
+                              "frac": round(ops / (m5_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                              "traffic": committed_traffic("k_matmul_q5_0", "2048x12288x4096")},
                 q2_k_weights={"kernel": "qmm::k_matmul_k<Q2_K>", "kernel_us_mean": round(m2_ms * 1e3, 2),
                               "achieved": round(ops / (m2_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m2_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
@@ -470,7 +484,8 @@ def main():
               "steps": args.prefill_steps, "warmup": args.prefill_warmup, "ms_per_step": round(pre["ms_step"], 4),
               "step": "quantize_q8_0 (2048x4096) + matmul_q4_0", "roofline": pre["roofline"],
               "q8_0_weights": pre["q8_0_weights"], "q2_k_weights": pre["q2_k_weights"],
-              "q4_k_weights": pre["q4_k_weights"], "q6_k_weights": pre["q6_k_weights"], "cpu_baseline": cpu_pre}
+              "q5_0_weights": pre["q5_0_weights"], "q4_k_weights": pre["q4_k_weights"],
+              "q6_k_weights": pre["q6_k_weights"], "cpu_baseline": cpu_pre}
         if dec is None:
             out.update({"value": pf["value"], "unit": "TOPS", "steps": pf["steps"], "warmup": pf["warmup"],
                         "ms_per_step": pf["ms_per_step"], "config": {"workload": pf["workload"]},

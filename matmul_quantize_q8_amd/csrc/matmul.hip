@@ -80,18 +80,21 @@ constexpr float kBias = 12582912.0f;      // 1.5 * 2^23, bit pattern 0x4B400000
 // segment offsets of the activation chunks (and of Q8_0 weight chunks)
 constexpr int xchunk(int c) { return c < 4 ? 16 * c : 52; }
 
-// Per weight format (Q8W: Q8_0 weights, else Q4_0).
-template <bool Q8W> struct WF {
-    static constexpr int WB = Q8W ? kQ80Bytes : kQ40Bytes;   // bytes per weight block
+// Per weight format (Q4_0, Q8_0 or Q5_0).
+template <int WFMT> struct WF {
+    static constexpr bool Q8W = WFMT == F_Q8_0, Q50 = WFMT == F_Q5_0;
+    static constexpr int WB = Q8W ? kQ80Bytes : Q50 ? kQ50Bytes : kQ40Bytes;   // bytes per weight block
     static constexpr int WC = Q8W ? 5 : 3;                    // 16-byte chunks per weight row per stage
     static constexpr int WQ = BN * WC / kWave;                // 10 or 6 wave loads of weight chunks
     static constexpr int STAGE = (BM * XC + BN * WC) * 16;    // 20,480 or 16,384 bytes
     static constexpr int PER_WAVE = (XQ + WQ) / 4;            // 5 or 4 DMA loads per wave per stage
     static constexpr int DXF = NBUF * STAGE;                  // per-wave f32 dx: [wave][block][64 rows]
     static constexpr int LDS_BYTES = DXF + 4 * 2 * 64 * 4;
-    static constexpr float OUT_SCALE = Q8W ? 1.0f : 0.0625f;  // Q4_0 codes enter as 16*(nib-8)
+    // Q4_0 codes enter as 16*(nib-8), Q5_0 codes as 8*(q-16)
+    static constexpr float OUT_SCALE = Q8W ? 1.0f : Q50 ? 0.125f : 0.0625f;
     // segment offsets of the weight chunks: Q4_0 rows of 36 bytes in chunks at 0, 16, 20
-    static constexpr int wchunk(int c) { return Q8W ? xchunk(c) : (c < 2 ? 16 * c : 20); }
+    // Q5_0 rows of 44 bytes in chunks at 0, 16, 28
+    static constexpr int wchunk(int c) { return Q8W ? xchunk(c) : (c < 2 ? 16 * c : Q50 ? 28 : 20); }
     static_assert(XQ * kWave == BM * XC && WQ * kWave == BN * WC && (XQ + WQ) % 4 == 0,
                   "stage splits into whole wave loads, evenly over the waves");
 };
@@ -123,12 +126,13 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
 // Workgroup barrier that orders LDS accesses but does not wait for
 // outstanding vector-memory loads (the LDS-DMA copies in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-template <bool Q8W>
+template <int WFMT>
 __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restrict__ w,
                                             const uint8_t *__restrict__ xq, float *__restrict__ y, int M, int N,
                                             int nb, int tiles_m) {
     using namespace mm;
-    using F = WF<Q8W>;
+    using F = WF<WFMT>;
+    constexpr bool Q8W = F::Q8W, Q50 = F::Q50;
     constexpr int WC = F::WC, WQ = F::WQ, STAGE = F::STAGE, PER_WAVE = F::PER_WAVE, DXF = F::DXF;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = uniform(t >> 6);
@@ -210,6 +214,16 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
 
     // 16*(nib-8) as int8 from a nibble in the high half of each byte
     auto nib = [](uint32_t v) { return (v & 0xF0F0F0F0u) ^ 0x80808080u; };
+    // Q5_0: 8*(q-16) as int8, q = nibble + 16 * fifth bit, from the nibbles in
+    // the high half of each byte of v and the inverted fifth bits nq of the
+    // lane's 16 codes (dword k: bits 4k..4k+3): 8*nib in bits 3..6, bit 7 set
+    // when the fifth bit is clear (8*nib - 128 as a byte).  The multiply by
+    // 0x204081 spreads four bits to the low bit of four bytes (the shifted
+    // copies never overlap); the shift by 7 moves them to bit 7.
+    auto q5code = [](uint32_t v, uint32_t nq, int k) {
+        const uint32_t b = (nq >> (4 * k)) & 15u;
+        return ((v >> 1) & 0x78787878u) | (((b * 0x00204081u) << 7) & 0x80808080u);
+    };
     auto half_lo = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); };
     auto half_hi = [](uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); };
     auto rd16 = [](const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); };
@@ -310,6 +324,18 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
                 const uint4 c = r.b0[j];
                 o.b[j] = v4i{(int)__builtin_amdgcn_perm(r.b1[j].x, c.x, selA), (int)c.y, (int)c.z, (int)c.w};
                 set_scale(o, j, absent ? 0.0f : half_lo(r.s0[j]));
+            } else if constexpr (Q50) {
+                // block 0 of the 44-byte segment: d at 0, qh at 2..5, qs at
+                // 6..21; its nibble bytes 14, 15, 0..13 are segment bytes
+                // 20, 21, 6..19
+                const uint4 c0 = r.w0[j], c1 = r.w1[j];
+                const uint32_t P = __builtin_amdgcn_perm(c1.y, c0.y, 0x03020504u);
+                const uint32_t Pm = __builtin_amdgcn_perm(P << 4, P, selB);
+                const uint32_t qh = __builtin_amdgcn_alignbyte(c0.y, c0.x, 2);
+                const uint32_t nq = ~__builtin_amdgcn_alignbit(qh, qh, lh ? 30u : 14u);   // codes 14.. or 30, 31, 0..
+                o.b[j] = v4i{(int)q5code(Pm, nq, 0), (int)q5code(c0.z << shHi, nq, 1),
+                             (int)q5code(c0.w << shHi, nq, 2), (int)q5code(c1.x << shHi, nq, 3)};
+                set_scale(o, j, absent ? 0.0f : half_lo(c0.x));
             } else {
                 const uint4 c0 = r.w0[j];
                 const uint32_t P = __builtin_amdgcn_perm(r.w1[j].x, c0.x, 0x03020504u);   // nibble bytes 14, 15, 0, 1
@@ -333,6 +359,13 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
                 const uint32_t d0 = lh ? r.b4[j].w : c.x;
                 o.b[j] = v4i{(int)d0, (int)c.y, (int)c.z, (int)c.w};
                 set_scale(o, j, half_hi(r.s2[j]));
+            } else if constexpr (Q50) {
+                // block 1: d at segment 22, qh at 24..27, qs at 28..43 (chunk 2)
+                const uint4 c1 = r.w1[j], c2 = r.w2[j];
+                const uint32_t nq = ~__builtin_amdgcn_alignbit(c1.z, c1.z, lh ? 28u : 12u);   // codes 12.. or 28..31, 0..
+                o.b[j] = v4i{(int)q5code(c2.w << shLo, nq, 0), (int)q5code(c2.x << shHi, nq, 1),
+                             (int)q5code(c2.y << shHi, nq, 2), (int)q5code(c2.z << shHi, nq, 3)};
+                set_scale(o, j, half_hi(c1.y));
             } else {
                 const uint4 c2 = r.w2[j];   // nibble bytes 0..15 of block 1
                 o.b[j] = v4i{(int)nib(c2.w << shLo), (int)nib(c2.x << shHi), (int)nib(c2.y << shHi),
@@ -442,15 +475,22 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
 __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                           int M, int N, int nb, int tiles_m) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<false>::LDS_BYTES];
-    matmul_body<false>(lds, w, xq, y, M, N, nb, tiles_m);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q4_0>::LDS_BYTES];
+    matmul_body<F_Q4_0>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q8_0(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                           int M, int N, int nb, int tiles_m) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<true>::LDS_BYTES];
-    matmul_body<true>(lds, w, xq, y, M, N, nb, tiles_m);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q8_0>::LDS_BYTES];
+    matmul_body<F_Q8_0>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_0(const uint8_t *__restrict__ w,
+                                                          const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                          int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q5_0>::LDS_BYTES];
+    matmul_body<F_Q5_0>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 // K = 32: one block per row, too short for the two-block stages above (the
@@ -489,13 +529,33 @@ __global__ __launch_bounds__(256) void k_matmul_q8_0_one_block(const uint8_t *__
     y[o] = (float)isum * dw * dx;
 }
 
+__global__ __launch_bounds__(256) void k_matmul_q5_0_one_block(const uint8_t *__restrict__ w,
+                                                               const uint8_t *__restrict__ xq,
+                                                               float *__restrict__ y, int M, int N) {
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (o >= (int64_t)M * N) return;
+    const int m = (int)(o / N), n = (int)(o - (int64_t)m * N);
+    const uint8_t *xb = xq + (int64_t)m * kQ80Bytes;
+    const uint8_t *wb = w + (int64_t)n * kQ50Bytes;
+    const uint32_t qh = (uint32_t)wb[2] | (uint32_t)wb[3] << 8 | (uint32_t)wb[4] << 16 | (uint32_t)wb[5] << 24;
+    int isum = 0;
+    for (int j = 0; j < 16; ++j) {
+        const int b = wb[6 + j];
+        const int lo = (b & 15) | (int)((qh >> j) & 1u) << 4, hi = (b >> 4) | (int)((qh >> (j + 16)) & 1u) << 4;
+        isum += (int)(int8_t)xb[2 + j] * (lo - 16) + (int)(int8_t)xb[18 + j] * (hi - 16);
+    }
+    const float dx = f16_bits_to_f32((uint32_t)xb[0] | (uint32_t)xb[1] << 8);
+    const float dw = f16_bits_to_f32((uint32_t)wb[0] | (uint32_t)wb[1] << 8);
+    y[o] = (float)isum * dw * dx;
+}
+
 // Largest block count whose tile offsets fit the 32-bit buffer offsets
 // (128 activation or Q8_0 weight rows of nb * 34 bytes).
 constexpr int64_t kMatmulMaxBlocks = (((int64_t)1 << 31) - 1) / (mm::BM * kQ80Bytes);
 
 int64_t matmul_q4_0_max_blocks() { return kMatmulMaxBlocks; }
 
-template <bool Q8W>
+template <int WFMT>
 static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
@@ -504,23 +564,31 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
         const int64_t outs = (int64_t)M * N;
         const int64_t grid = (outs + 255) / 256;
         if (grid > 0x7fffffff) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(Q8W ? k_matmul_q8_0_one_block : k_matmul_q4_0_one_block, dim3((unsigned)grid), dim3(256),
-                           0, st, wp, xp, y, M, N);
+        hipLaunchKernelGGL(WFMT == F_Q8_0   ? k_matmul_q8_0_one_block
+                           : WFMT == F_Q5_0 ? k_matmul_q5_0_one_block
+                                            : k_matmul_q4_0_one_block,
+                           dim3((unsigned)grid), dim3(256), 0, st, wp, xp, y, M, N);
         return hipGetLastError();
     }
     int tiles_m = (M + mm::BM - 1) / mm::BM;
     const int64_t tiles = (int64_t)tiles_m * ((N + mm::BN - 1) / mm::BN);
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
-    return hipLaunchKernel(Q8W ? (const void *)k_matmul_q8_0 : (const void *)k_matmul_q4_0, dim3((unsigned)tiles),
-                           dim3(mm::NT), args, 0, st);
+    const void *kern = WFMT == F_Q8_0   ? (const void *)k_matmul_q8_0
+                       : WFMT == F_Q5_0 ? (const void *)k_matmul_q5_0
+                                        : (const void *)k_matmul_q4_0;
+    return hipLaunchKernel(kern, dim3((unsigned)tiles), dim3(mm::NT), args, 0, st);
 }
 
 hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
-    return launch_mm<false>(w, xq, y, M, N, nb, st);
+    return launch_mm<F_Q4_0>(w, xq, y, M, N, nb, st);
 }
 
 hipError_t launch_matmul_q8_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
-    return launch_mm<true>(w, xq, y, M, N, nb, st);
+    return launch_mm<F_Q8_0>(w, xq, y, M, N, nb, st);
+}
+
+hipError_t launch_matmul_q5_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    return launch_mm<F_Q5_0>(w, xq, y, M, N, nb, st);
 }
 
 }  // namespace qmm

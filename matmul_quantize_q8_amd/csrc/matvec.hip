@@ -793,7 +793,7 @@ hipError_t launch_matvec_q6_k(const void *w, const void *xq, float *y, int N, in
     return dispatch_mv<F_Q6_K>(w, xq, nullptr, y, 1, N, ns, st);
 }
 
-// Prefill of the formats without an MFMA kernel (Q4_1, Q5_0, Q5_1): the
+// Prefill of the formats without an MFMA kernel (Q4_1, Q5_1): the
 // matvec kernel with one grid row per token (the weights are re-read from
 // cache for each token; correct for any M, not tuned).
 template <int F>
@@ -809,9 +809,6 @@ static hipError_t matmul_by_tokens(const void *w, const void *xq, float *y, int 
 }
 hipError_t launch_matmul_q4_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
     return matmul_by_tokens<F_Q4_1>(w, xq, y, M, N, nb, st);
-}
-hipError_t launch_matmul_q5_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
-    return matmul_by_tokens<F_Q5_0>(w, xq, y, M, N, nb, st);
 }
 hipError_t launch_matmul_q5_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
     return matmul_by_tokens<F_Q5_1>(w, xq, y, M, N, nb, st);

@@ -18,7 +18,9 @@ each; the prefill matmul (M = 2048, same weights), int8 TOP/s;
 for each, the dominant kernel's roofline (achieved / MI355X peak, with the
 average kernel time from HIP events on the launch stream around graph
 replays of batches of back-to-back launches of that kernel) and the oracle timed on the host cores
-over a bounded sample of the same workload.
+over a bounded sample of the same workload.  `attainable` holds the measured
+ceilings (a streaming read, at 1 GiB and at the decode's 28.3 MB, and an int8
+MFMA loop); each roofline also gives its fraction of the matching one.
 
 Synthetic data: seeded Gaussian weights (std 0.02) and activations (std 1,
 1% outliers x20 for decode), quantized on the GPU by the library.
@@ -382,6 +384,46 @@ def bench_matvec_configs(args, torch, q, synth):
                                "hbm_frac": round(tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
+def bench_peaks(args, torch, q):
+    """Measured ceilings (library probes): a streaming read of 1 GiB in one
+    pass; passes of the decode's 28,311,552 weight bytes over rotating slices
+    of that buffer (37 slices, 1 GiB > the 256 MB last-level cache, so each
+    pass is cold, as each decode step is); and back-to-back int8 MFMAs on
+    register operands at two and three waves per SIMD."""
+    size = 1 << 30
+    buf = torch.arange(size // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(size // 8192, dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+    for _ in range(3):
+        q.qmm_peak_read(base, size, sink)
+    big_ms, _, _ = time_batches(torch, lambda i: q.qmm_peak_read(base, size, sink), 24, 4)
+    S = DEC["N"] * q.row_bytes("q4_0", DEC["K"])
+    ns = size // S
+    for i in range(ns):
+        q.qmm_peak_read(base + (i % ns) * S, S, sink)
+    sl_ms, sl_min, _ = time_batches(torch, lambda i: q.qmm_peak_read(base + (i % ns) * S, S, sink), args.steps, ns)
+    del buf
+    mfma = []
+    for wg, iters in ((512, 4000), (768, 2700)):
+        out = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+        q.qmm_peak_mfma_i8(out, wg, iters)
+        torch.cuda.synchronize()
+        if not bool((out == 2048 * iters).all()):
+            raise RuntimeError("int8 MFMA probe returned wrong sums")
+        ms, _, _ = time_batches(torch, lambda i: q.qmm_peak_mfma_i8(out, wg, iters), 8, 2)
+        ops = wg * 4 * 4 * iters * 2.0 * 32 * 32 * 32
+        mfma.append((ops / (ms * 1e-3) / 1e12, wg * 4 // 1024, ms))   # 4 waves per workgroup, 1024 SIMDs
+    tops, waves, mms = max(mfma)
+    res = {"hbm_read_1GiB_gbs": round(size / (big_ms * 1e-3) / 1e9, 1),
+           "hbm_read_28MB_gbs": round(S / (sl_ms * 1e-3) / 1e9, 1),
+           "hbm_read_28MB_us_mean": round(sl_ms * 1e3, 3), "hbm_read_28MB_us_best_batch": round(sl_min * 1e3, 3),
+           "int8_mfma_tops": round(tops, 1), "int8_mfma_waves_per_simd": waves,
+           "kernels": ["qmm::k_peak_read", "qmm::k_peak_mfma_i8"]}
+    log(f"peaks: read 1 GiB {res['hbm_read_1GiB_gbs']} GB/s, 28 MB passes {res['hbm_read_28MB_gbs']} GB/s "
+        f"({sl_ms * 1e3:.2f} us), int8 MFMA {tops:.0f} TOPS at {waves} waves/SIMD")
+    return res
+
+
 def cpu_threads():
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     return max(1, min(n, 16))
@@ -454,6 +496,7 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}), flush=True)
         return
 
+    peaks = bench_peaks(args, torch, q) if args.only in ("all", "decode", "prefill") else None
     dec = bench_decode(args, torch, q, synth) if args.only in ("all", "decode") else None
     pre = bench_prefill(args, torch, q, synth) if args.only in ("all", "prefill") else None
     cfgs = bench_matvec_configs(args, torch, q, synth) if args.only in ("all", "configs") else None
@@ -468,6 +511,11 @@ def main():
 
     out = {"metric": METRIC, "n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "int8", "data": "synthetic"}
+    if peaks is not None:
+        if dec is not None:
+            dec["roofline"]["frac_of_attainable"] = round(dec["roofline"]["achieved"] / peaks["hbm_read_28MB_gbs"], 4)
+        if pre is not None:
+            pre["roofline"]["frac_of_attainable"] = round(pre["roofline"]["achieved"] / peaks["int8_mfma_tops"], 4)
     if dec is not None:
         out.update({"value": round(dec["gbs"], 1), "unit": "GB/s", "steps": dec["nsteps"], "warmup": args.warmup,
                     "ms_per_step": round(dec["ms_step"], 5),
@@ -494,6 +542,8 @@ def main():
             out["prefill"] = pf
     if cfgs is not None:
         out["matvec_configs"] = cfgs
+    if peaks is not None:
+        out["attainable"] = peaks
     print(json.dumps(out), flush=True)
 
 

@@ -90,6 +90,18 @@ A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced
     (lambda L: L.qmm_matmul_q2_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
     (lambda L: L.qmm_matmul_q4_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
     (lambda L: L.qmm_matmul_q6_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
+    # the attainable-peak probes
+    (lambda L: L.qmm_peak_read(A, 0, A, None), 1),
+    (lambda L: L.qmm_peak_read(A, 24, A, None), 1),            # not a multiple of 16
+    (lambda L: L.qmm_peak_read(None, 32, A, None), 2),
+    (lambda L: L.qmm_peak_read(A, 32, None, None), 2),
+    (lambda L: L.qmm_peak_read(A + 8, 32, A, None), 3),
+    (lambda L: L.qmm_peak_read(A, 32, A + 2, None), 3),
+    (lambda L: L.qmm_peak_mfma_i8(A, 0, 10, None), 1),
+    (lambda L: L.qmm_peak_mfma_i8(A, 8, 1000001, None), 1),      # out would pass 2^31
+    (lambda L: L.qmm_peak_mfma_i8(A, (1 << 20) + 1, 10, None), 1),
+    (lambda L: L.qmm_peak_mfma_i8(None, 8, 10, None), 2),
+    (lambda L: L.qmm_peak_mfma_i8(A + 4, 8, 10, None), 3),
 ])
 def test_argument_errors_without_device(q, call, code):
     assert call(q.lib()) == code

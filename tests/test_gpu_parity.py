@@ -504,6 +504,36 @@ def test_outputs_are_overwritten_not_accumulated(env):
     assert np.array_equal(y.cpu().numpy(), y1)
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 1025, 1 << 20, (28311552 // 16 + 3) * 16])
+def test_peak_read_probe_reads_every_word(env, nbytes):
+    """The streaming-read probe XORs every 32-bit word of the buffer (one
+    grid-stride pass, ragged tails included)."""
+    torch, q, _ = env
+    _say("peak_read", nbytes)
+    words = synth.splitmix64(101, 0, nbytes // 4).astype(np.uint32)
+    buf = _dev(torch, words.view(np.int32))
+    nchunk = -(-nbytes // 8192)
+    sink = torch.full((nchunk + 1,), -1, dtype=torch.int32, device="cuda")
+    q.qmm_peak_read(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    padded = np.zeros(nchunk * 2048, dtype=np.uint32)
+    padded[:words.size] = words
+    assert np.array_equal(got[:nchunk], np.bitwise_xor.reduce(padded.reshape(nchunk, 2048), axis=1))
+    assert got[nchunk] == 0xFFFFFFFF   # nothing written past the last chunk
+
+
+@pytest.mark.parametrize("wg,iters", [(1, 1), (3, 17), (512, 100)])
+def test_peak_mfma_probe_sums(env, wg, iters):
+    """Every lane of the int8 MFMA probe ends with 4 chains x 16 results x 32 x iters."""
+    torch, q, _ = env
+    _say("peak_mfma", wg, iters)
+    out = torch.full((wg * 256,), -1, dtype=torch.int32, device="cuda")
+    q.qmm_peak_mfma_i8(out, wg, iters)
+    torch.cuda.synchronize()
+    assert bool((out == 2048 * iters).all())
+
+
 def test_device_errors_are_reported(env):
     torch, q, _ = env
     buf = torch.zeros(4096, dtype=torch.uint8, device="cuda")

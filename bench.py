@@ -250,6 +250,22 @@ def bench_prefill(args, torch, q, synth):
     m5_ms, m5_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q5_0(wq5, Xq, Y, M, N, K), args.prefill_steps, 4)
     log(f"prefill q5_0 weights: matmul {m5_ms * 1e3:.1f} us (best batch {m5_min * 1e3:.1f})")
     del wq5
+    # Q4_1 and Q5_1 weights (weights of their decode workloads, the same Q8_0 activations)
+    off = {}
+    for fmt, cfg in (("q4_1", 9), ("q5_1", 11)):
+        w = torch.from_numpy(synth.weights(N, K, config=cfg)).cuda()
+        wqf = torch.empty(N * q.row_bytes(fmt, K), dtype=torch.uint8, device="cuda")
+        q.QUANTIZE_W[fmt](w, wqf, N, K)
+        del w
+        for _ in range(4):
+            q.MATMUL[fmt](wqf, Xq, Y, M, N, K)
+        f_ms, f_min, _ = time_batches(torch, lambda i: q.MATMUL[fmt](wqf, Xq, Y, M, N, K), args.prefill_steps, 4)
+        log(f"prefill {fmt} weights: matmul {f_ms * 1e3:.1f} us (best batch {f_min * 1e3:.1f})")
+        off[fmt] = {"kernel": f"qmm::k_matmul_{fmt}", "kernel_us_mean": round(f_ms * 1e3, 2),
+                    "achieved": round(ops / (f_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
+                    "frac": round(ops / (f_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                    "traffic": committed_traffic(f"k_matmul_{fmt}", "2048x12288x4096")}
+        del wqf
     # Q2_K weights x Q8_K activations (same shape, inputs of the Q2_K workload)
     w = torch.from_numpy(synth.weights(N, K, config=3)).cuda()
     wq2 = torch.empty(N * q.row_bytes("q2_k", K), dtype=torch.uint8, device="cuda")
@@ -296,6 +312,7 @@ def bench_prefill(args, torch, q, synth):
                               "achieved": round(ops / (m5_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m5_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                               "traffic": committed_traffic("k_matmul_q5_0", "2048x12288x4096")},
+                q4_1_weights=off["q4_1"], q5_1_weights=off["q5_1"],
                 q2_k_weights={"kernel": "qmm::k_matmul_k<Q2_K>", "kernel_us_mean": round(m2_ms * 1e3, 2),
                               "achieved": round(ops / (m2_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m2_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
@@ -532,7 +549,8 @@ def main():
               "steps": args.prefill_steps, "warmup": args.prefill_warmup, "ms_per_step": round(pre["ms_step"], 4),
               "step": "quantize_q8_0 (2048x4096) + matmul_q4_0", "roofline": pre["roofline"],
               "q8_0_weights": pre["q8_0_weights"], "q2_k_weights": pre["q2_k_weights"],
-              "q5_0_weights": pre["q5_0_weights"], "q4_k_weights": pre["q4_k_weights"],
+              "q5_0_weights": pre["q5_0_weights"], "q4_1_weights": pre["q4_1_weights"],
+              "q5_1_weights": pre["q5_1_weights"], "q4_k_weights": pre["q4_k_weights"],
               "q6_k_weights": pre["q6_k_weights"], "cpu_baseline": cpu_pre}
         if dec is None:
             out.update({"value": pf["value"], "unit": "TOPS", "steps": pf["steps"], "warmup": pf["warmup"],

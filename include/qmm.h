@@ -202,10 +202,11 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
 /* Prefill matmul, M tokens.
  *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.
  *   y  : f32 [M][N], written.
- * qmm_matmul_q4_0, qmm_matmul_q8_0 and qmm_matmul_q5_0 run on int8 MFMA (Q5_0
- * codes enter as 8 * (q - 16)) and also return QMM_E_SHAPE when 128 rows of
- * Q8_0 activations (128 * K/32 * 34 bytes) exceed 2^31 - 1 bytes, i.e.
- * K > 15,790,304.  qmm_matmul_q2_k runs on int8 MFMA
+ * The 32-value formats (Q4_0, Q8_0, Q4_1, Q5_0, Q5_1) run on int8 MFMA (4-bit
+ * codes enter as 16 * (q - 8), 5-bit codes as 8 * (q - 16); the offset term
+ * of Q4_1 / Q5_1, m * dx * sum x per block, runs on an f32 MFMA) and also
+ * return QMM_E_SHAPE when 128 rows of Q8_0 activations (128 * K/32 * 34
+ * bytes) exceed 2^31 - 1 bytes, i.e. K > 15,790,304.  qmm_matmul_q2_k runs on int8 MFMA
  * (the group scales folded into the codes, one scale fold per 256 values)
  * plus an f16 MFMA for the min term; qmm_matmul_q4_k runs one int8 MFMA tile
  * per 32-value sub-block on the 4-bit codes, applies the 6-bit sub-block
@@ -214,8 +215,7 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
  * 16-value group on the unsigned 6-bit codes, applies the signed group scales
  * in int32 and takes the offset of 32 from an f16 MFMA over the block sums.
  * All three return QMM_E_SHAPE when 128 rows of Q8_K activations
- * (128 * K/256 * 292 bytes) exceed 2^31 - 1 bytes.  Q4_1 and Q5_1 run the
- * matvec kernel once per token (correct for any M, not tuned for prefill). */
+ * (128 * K/256 * 292 bytes) exceed 2^31 - 1 bytes. */
 qmm_status qmm_matmul_q4_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
                            void *stream);
 qmm_status qmm_matmul_q8_0(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,

@@ -260,6 +260,7 @@ qmm_status qmm_matmul_q8_0(const void *w, const void *xq, float *y, int64_t M, i
 }
 
 qmm_status qmm_matmul_q4_1(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+    if (K / 32 > qmm::matmul_q4_0_max_blocks()) return QMM_E_SHAPE;
     return matmul(qmm::launch_matmul_q4_1, w, xq, y, M, N, K, 32, qmm::kQ41Bytes, qmm::kQ80Bytes, stream);
 }
 
@@ -269,6 +270,7 @@ qmm_status qmm_matmul_q5_0(const void *w, const void *xq, float *y, int64_t M, i
 }
 
 qmm_status qmm_matmul_q5_1(const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+    if (K / 32 > qmm::matmul_q4_0_max_blocks()) return QMM_E_SHAPE;
     return matmul(qmm::launch_matmul_q5_1, w, xq, y, M, N, K, 32, qmm::kQ51Bytes, qmm::kQ80Bytes, stream);
 }
 

@@ -80,21 +80,27 @@ constexpr float kBias = 12582912.0f;      // 1.5 * 2^23, bit pattern 0x4B400000
 // segment offsets of the activation chunks (and of Q8_0 weight chunks)
 constexpr int xchunk(int c) { return c < 4 ? 16 * c : 52; }
 
-// Per weight format (Q4_0, Q8_0 or Q5_0).
+// Per weight format (Q4_0, Q8_0, Q5_0, Q4_1 or Q5_1).
 template <int WFMT> struct WF {
-    static constexpr bool Q8W = WFMT == F_Q8_0, Q50 = WFMT == F_Q5_0;
-    static constexpr int WB = Q8W ? kQ80Bytes : Q50 ? kQ50Bytes : kQ40Bytes;   // bytes per weight block
+    static constexpr bool Q8W = WFMT == F_Q8_0, Q41 = WFMT == F_Q4_1, Q51 = WFMT == F_Q5_1;
+    static constexpr bool Q5 = WFMT == F_Q5_0 || Q51;          // five-bit codes, high bits in qh
+    static constexpr bool MIN = Q41 || Q51;                    // value d q + m: an offset term per block
+    static constexpr int WB = Q8W ? kQ80Bytes : WFMT == F_Q5_0 ? kQ50Bytes : Q41 ? kQ41Bytes : Q51 ? kQ51Bytes
+                                                                                          : kQ40Bytes;
     static constexpr int WC = Q8W ? 5 : 3;                    // 16-byte chunks per weight row per stage
     static constexpr int WQ = BN * WC / kWave;                // 10 or 6 wave loads of weight chunks
     static constexpr int STAGE = (BM * XC + BN * WC) * 16;    // 20,480 or 16,384 bytes
     static constexpr int PER_WAVE = (XQ + WQ) / 4;            // 5 or 4 DMA loads per wave per stage
-    static constexpr int DXF = NBUF * STAGE;                  // per-wave f32 dx: [wave][block][64 rows]
-    static constexpr int LDS_BYTES = DXF + 4 * 2 * 64 * 4;
-    // Q4_0 codes enter as 16*(nib-8), Q5_0 codes as 8*(q-16)
-    static constexpr float OUT_SCALE = Q8W ? 1.0f : Q50 ? 0.125f : 0.0625f;
-    // segment offsets of the weight chunks: Q4_0 rows of 36 bytes in chunks at 0, 16, 20
-    // Q5_0 rows of 44 bytes in chunks at 0, 16, 28
-    static constexpr int wchunk(int c) { return Q8W ? xchunk(c) : (c < 2 ? 16 * c : Q50 ? 28 : 20); }
+    // per-wave f32 dx (and dx * code sum with an offset term): [wave][kind][block][64 rows]
+    static constexpr int DXF = NBUF * STAGE;
+    static constexpr int DXW = (MIN ? 4 : 2) * 64 * 4;        // bytes per wave
+    static constexpr int LDS_BYTES = DXF + 4 * DXW;
+    // 4-bit codes enter as 16*(q-8), 5-bit codes as 8*(q-16)
+    static constexpr float OUT_SCALE = Q8W ? 1.0f : Q5 ? 0.125f : 0.0625f;
+    // segment offsets of the weight chunks (segment = two blocks): Q4_0 36
+    // bytes in chunks at 0, 16, 20; Q5_0 44 at 0, 16, 28; Q4_1 40 at 0, 16,
+    // 24; Q5_1 48 at 0, 16, 32
+    static constexpr int wchunk(int c) { return Q8W ? xchunk(c) : c < 2 ? 16 * c : 2 * WB - 16; }
     static_assert(XQ * kWave == BM * XC && WQ * kWave == BN * WC && (XQ + WQ) % 4 == 0,
                   "stage splits into whole wave loads, evenly over the waves");
 };
@@ -132,7 +138,7 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
                                             int nb, int tiles_m) {
     using namespace mm;
     using F = WF<WFMT>;
-    constexpr bool Q8W = F::Q8W, Q50 = F::Q50;
+    constexpr bool Q8W = F::Q8W, Q5 = F::Q5, MIN = F::MIN;
     constexpr int WC = F::WC, WQ = F::WQ, STAGE = F::STAGE, PER_WAVE = F::PER_WAVE, DXF = F::DXF;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = uniform(t >> 6);
@@ -195,7 +201,7 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const int wb = WOFF + 16 * WC * (64 * wn + lr);      // B row 64wn+lr (tile j: +32 rows)
     const int wb_main = wb + (lh ? 0 : 16);              // Q8_0 weights: as xa_main
     const int xd = 16 * XC * (64 * wm + lane);           // the row whose dx this lane converts
-    const int dxw = DXF + 512 * wave;                    // this wave's f32 dx: [block][64 rows 64wm..]
+    const int dxw = DXF + F::DXW * wave;                 // this wave's f32 dx: [block][64 rows 64wm..]
     const uint32_t selA = lh ? 0x03020504u : 0x03020100u;   // half 1: codes 30, 31 into bytes 0, 1
     const uint32_t selB = lh ? 0x07060100u : 0x03020504u;   // block 0, first dword: which bytes take low nibbles
     const uint32_t shHi = lh ? 4u : 0u;                  // shift for a dword that half 0 takes high nibbles of
@@ -232,10 +238,33 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     // The wave's dx for one stage as f32: lane l converts row 64wm+l's scale
     // of each block (bytes 0..1 of chunk 0 and 2..3 of chunk 2).  Only this
     // wave reads them back, and a wave's LDS accesses complete in order.
+    // With an offset term it also stores dx * sx (sx = the block's code sum,
+    // exact in f32: 11 + 12 significant bits) at [2 + block][64 rows]: the
+    // row's segment bytes 0..63 sit at row offsets 0..63 and bytes 64..67 at
+    // 76..79 (chunk 4); block 0's codes are bytes 2..33, block 1's 36..67.
     auto convert_dx = [&](const uint8_t *sb) {
         float *d = reinterpret_cast<float *>(lds + dxw);
-        d[lane] = half_lo(rd4(sb + xd));
-        d[64 + lane] = half_hi(rd4(sb + xd + 32));
+        if constexpr (MIN) {
+            const uint4 q0 = rd16(sb + xd), q1 = rd16(sb + xd + 16), q2 = rd16(sb + xd + 32),
+                        q3 = rd16(sb + xd + 48);
+            const uint32_t q19 = rd4(sb + xd + 76);
+            constexpr int ones = 0x01010101;
+            int s0 = dot4((int)q0.x, 0x01010000, 0);
+            s0 = dot4((int)q0.y, ones, dot4((int)q0.z, ones, dot4((int)q0.w, ones, s0)));
+            s0 = dot4((int)q1.x, ones, dot4((int)q1.y, ones, dot4((int)q1.z, ones, dot4((int)q1.w, ones, s0))));
+            s0 = dot4((int)q2.x, 0x00000101, s0);
+            int s1 = dot4((int)q2.y, ones, dot4((int)q2.z, ones, dot4((int)q2.w, ones, 0)));
+            s1 = dot4((int)q3.x, ones, dot4((int)q3.y, ones, dot4((int)q3.z, ones, dot4((int)q3.w, ones, s1))));
+            s1 = dot4((int)q19, ones, s1);
+            const float dx0 = half_lo(q0.x), dx1 = half_hi(q2.x);
+            d[lane] = dx0;
+            d[64 + lane] = dx1;
+            d[128 + lane] = dx0 * (float)s0;
+            d[192 + lane] = dx1 * (float)s1;
+        } else {
+            d[lane] = half_lo(rd4(sb + xd));
+            d[64 + lane] = half_hi(rd4(sb + xd + 32));
+        }
     };
     // dx of the lane's 16 output rows of A tile i, block kb: rows 8a + 4lh + c
     // of the tile, four 16-byte reads
@@ -324,7 +353,26 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
                 const uint4 c = r.b0[j];
                 o.b[j] = v4i{(int)__builtin_amdgcn_perm(r.b1[j].x, c.x, selA), (int)c.y, (int)c.z, (int)c.w};
                 set_scale(o, j, absent ? 0.0f : half_lo(r.s0[j]));
-            } else if constexpr (Q50) {
+            } else if constexpr (F::Q41 || F::Q51) {
+                // block 0: d, m at 0, 2, then (Q5_1) qh at 4..7, and qs at 4
+                // (Q4_1) or 8 (Q5_1); the rotated nibble bytes 14, 15, 0..13
+                // are two bytes off the dword grid
+                const uint4 c0 = r.w0[j], c1 = r.w1[j];
+                const uint32_t a = F::Q41 ? c0.y : c0.z, b = F::Q41 ? c0.z : c0.w, c = F::Q41 ? c0.w : c1.x,
+                               e = F::Q41 ? c1.x : c1.y;   // nibble bytes 0..3, 4..7, 8..11, 12..15
+                const uint32_t P = __builtin_amdgcn_perm(e, a, 0x01000706u);   // bytes 14, 15, 0, 1
+                const uint32_t Pm = __builtin_amdgcn_perm(P << 4, P, selB);
+                const uint32_t D1 = __builtin_amdgcn_alignbyte(b, a, 2), D2 = __builtin_amdgcn_alignbyte(c, b, 2),
+                               D3 = __builtin_amdgcn_alignbyte(e, c, 2);
+                if constexpr (F::Q51) {
+                    const uint32_t nq = ~__builtin_amdgcn_alignbit(c0.y, c0.y, lh ? 30u : 14u);
+                    o.b[j] = v4i{(int)q5code(Pm, nq, 0), (int)q5code(D1 << shHi, nq, 1),
+                                 (int)q5code(D2 << shHi, nq, 2), (int)q5code(D3 << shHi, nq, 3)};
+                } else {
+                    o.b[j] = v4i{(int)nib(Pm), (int)nib(D1 << shHi), (int)nib(D2 << shHi), (int)nib(D3 << shHi)};
+                }
+                set_scale(o, j, absent ? 0.0f : half_lo(c0.x));
+            } else if constexpr (Q5) {
                 // block 0 of the 44-byte segment: d at 0, qh at 2..5, qs at
                 // 6..21; its nibble bytes 14, 15, 0..13 are segment bytes
                 // 20, 21, 6..19
@@ -359,7 +407,20 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
                 const uint32_t d0 = lh ? r.b4[j].w : c.x;
                 o.b[j] = v4i{(int)d0, (int)c.y, (int)c.z, (int)c.w};
                 set_scale(o, j, half_hi(r.s2[j]));
-            } else if constexpr (Q50) {
+            } else if constexpr (F::Q41 || F::Q51) {
+                // block 1: d, m at segment 20 (Q4_1) or 24 (Q5_1), Q5_1's qh
+                // at 28..31, the nibble bytes in chunk 2
+                const uint4 c1 = r.w1[j], c2 = r.w2[j];
+                if constexpr (F::Q51) {
+                    const uint32_t nq = ~__builtin_amdgcn_alignbit(c1.w, c1.w, lh ? 28u : 12u);
+                    o.b[j] = v4i{(int)q5code(c2.w << shLo, nq, 0), (int)q5code(c2.x << shHi, nq, 1),
+                                 (int)q5code(c2.y << shHi, nq, 2), (int)q5code(c2.z << shHi, nq, 3)};
+                } else {
+                    o.b[j] = v4i{(int)nib(c2.w << shLo), (int)nib(c2.x << shHi), (int)nib(c2.y << shHi),
+                                 (int)nib(c2.z << shHi)};
+                }
+                set_scale(o, j, half_lo(F::Q41 ? c1.y : c1.z));
+            } else if constexpr (Q5) {
                 // block 1: d at segment 22, qh at 24..27, qs at 28..43 (chunk 2)
                 const uint4 c1 = r.w1[j], c2 = r.w2[j];
                 const uint32_t nq = ~__builtin_amdgcn_alignbit(c1.z, c1.z, lh ? 28u : 12u);   // codes 12.. or 28..31, 0..
@@ -373,6 +434,38 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
                 set_scale(o, j, half_hi(r.w1[j].x));
             }
         }
+    };
+
+    // Offset term of the formats whose value is d q + m (Q4_1, Q5_1).  With
+    // the codes entering as 16 (q - 8) (Q4_1) or 8 (q - 16) (Q5_1) the MFMA
+    // gives I' = sum q' x, and the block adds (to the accumulator, which the
+    // store scales by S = OUT_SCALE)
+    //   dx d I' + (dx sx) (128 d + m / S),   sx = the activation's code sum.
+    // The second part is an outer product summed over the stage's two blocks:
+    // one v_mfma_f32_32x32x2_f32 per tile and stage, straight into the f32
+    // accumulator, K = block.  Lane half h supplies block h: A = dx sx of row
+    // lr of the tile (from convert_dx), B = 128 d + m/S of column lr (one
+    // rounding; 0 for the duplicated block 0 of an odd last stage).
+    auto offset_operands = [&](const Raw &r, bool absent0, float (&ao)[2], float (&bo)[2]) {
+        const float *d = reinterpret_cast<const float *>(lds + dxw);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ao[i] = d[128 + 64 * lh + 32 * i + lr];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if constexpr (MIN) {
+                const uint32_t sc = lh ? (F::Q41 ? r.w1[j].y : r.w1[j].z) : r.w0[j].x;
+                const float c = fmaf(half_lo(sc), 128.0f, half_hi(sc) * (1.0f / F::OUT_SCALE));
+                bo[j] = (absent0 && !lh) ? 0.0f : c;
+            }
+        }
+    };
+    auto offset_mfma = [&](int i, int j, float a, float b) {
+        v16f c;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[r] = acc[i][j][r];
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = c[r];
     };
 
     // One stage: 2 blocks x 4 tiles in an explicit order, fenced against the
@@ -389,8 +482,10 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
             dma_load(kc, sd, bd);
             __builtin_amdgcn_sched_barrier(0);
         };
+        float ao[2], bo[2];
         convert_dx(sb);
         load_raw(sb, r);
+        if constexpr (MIN) offset_operands(r, absent0, ao, bo);
         load_dx(0, 0, dxa);
         build0(r, absent0, o0);
         v16i d0 = mfma(o0.a[0], o0.b[0]);
@@ -430,6 +525,13 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
         __builtin_amdgcn_sched_barrier(0);
         fold(d1, 1, 1, dxb, o1.dw[1], o1.nb[1]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MIN) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) offset_mfma(i, j, ao[i], bo[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // Stage s lives in buffer s % 3.  At step s this wave's loads of stage s
@@ -493,6 +595,20 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_0(const uint8_t *__rest
     matmul_body<F_Q5_0>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_1(const uint8_t *__restrict__ w,
+                                                          const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                          int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q4_1>::LDS_BYTES];
+    matmul_body<F_Q4_1>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_1(const uint8_t *__restrict__ w,
+                                                          const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                          int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q5_1>::LDS_BYTES];
+    matmul_body<F_Q5_1>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
 // K = 32: one block per row, too short for the two-block stages above (the
 // window of an odd last stage would start before the row).  One thread per
 // output: Y[m][n] = dx dw I with I the exact int32 block dot.
@@ -529,24 +645,37 @@ __global__ __launch_bounds__(256) void k_matmul_q8_0_one_block(const uint8_t *__
     y[o] = (float)isum * dw * dx;
 }
 
-__global__ __launch_bounds__(256) void k_matmul_q5_0_one_block(const uint8_t *__restrict__ w,
-                                                               const uint8_t *__restrict__ xq,
-                                                               float *__restrict__ y, int M, int N) {
+// The same for the 32-value formats with a fifth bit or an offset (Q4_1,
+// Q5_0, Q5_1): Y[m][n] = dx (dw sum q' x + m sum x), q' = q (Q5_0: q - 16),
+// both integer sums exact.
+template <int WFMT>
+__global__ __launch_bounds__(256) void k_matmul_32_one_block(const uint8_t *__restrict__ w,
+                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                             int M, int N) {
+    constexpr int WB = WFMT == F_Q4_1 ? kQ41Bytes : WFMT == F_Q5_0 ? kQ50Bytes : kQ51Bytes;
+    constexpr int QH = WFMT == F_Q5_0 ? 2 : 4;                               // qh offset (Q5_0, Q5_1)
+    constexpr int QS = WFMT == F_Q4_1 ? 4 : WFMT == F_Q5_0 ? 6 : 8;          // qs offset
+    constexpr int OFF = WFMT == F_Q5_0 ? 16 : 0;
     const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (o >= (int64_t)M * N) return;
     const int m = (int)(o / N), n = (int)(o - (int64_t)m * N);
     const uint8_t *xb = xq + (int64_t)m * kQ80Bytes;
-    const uint8_t *wb = w + (int64_t)n * kQ50Bytes;
-    const uint32_t qh = (uint32_t)wb[2] | (uint32_t)wb[3] << 8 | (uint32_t)wb[4] << 16 | (uint32_t)wb[5] << 24;
-    int isum = 0;
+    const uint8_t *wb = w + (int64_t)n * WB;
+    const uint32_t qh = WFMT == F_Q4_1 ? 0u
+                                        : (uint32_t)wb[QH] | (uint32_t)wb[QH + 1] << 8 |
+                                              (uint32_t)wb[QH + 2] << 16 | (uint32_t)wb[QH + 3] << 24;
+    int isum = 0, xsum = 0;
     for (int j = 0; j < 16; ++j) {
-        const int b = wb[6 + j];
+        const int b = wb[QS + j];
         const int lo = (b & 15) | (int)((qh >> j) & 1u) << 4, hi = (b >> 4) | (int)((qh >> (j + 16)) & 1u) << 4;
-        isum += (int)(int8_t)xb[2 + j] * (lo - 16) + (int)(int8_t)xb[18 + j] * (hi - 16);
+        const int x0 = (int8_t)xb[2 + j], x1 = (int8_t)xb[18 + j];
+        isum += x0 * (lo - OFF) + x1 * (hi - OFF);
+        xsum += x0 + x1;
     }
     const float dx = f16_bits_to_f32((uint32_t)xb[0] | (uint32_t)xb[1] << 8);
     const float dw = f16_bits_to_f32((uint32_t)wb[0] | (uint32_t)wb[1] << 8);
-    y[o] = (float)isum * dw * dx;
+    const float mw = WFMT == F_Q5_0 ? 0.0f : f16_bits_to_f32((uint32_t)wb[2] | (uint32_t)wb[3] << 8);
+    y[o] = fmaf(dw, (float)isum, mw * (float)xsum) * dx;
 }
 
 // Largest block count whose tile offsets fit the 32-bit buffer offsets
@@ -564,10 +693,10 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
         const int64_t outs = (int64_t)M * N;
         const int64_t grid = (outs + 255) / 256;
         if (grid > 0x7fffffff) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(WFMT == F_Q8_0   ? k_matmul_q8_0_one_block
-                           : WFMT == F_Q5_0 ? k_matmul_q5_0_one_block
-                                            : k_matmul_q4_0_one_block,
-                           dim3((unsigned)grid), dim3(256), 0, st, wp, xp, y, M, N);
+        const auto one = WFMT == F_Q8_0 ? k_matmul_q8_0_one_block
+                         : WFMT == F_Q4_0 ? k_matmul_q4_0_one_block
+                                          : k_matmul_32_one_block<WFMT>;
+        hipLaunchKernelGGL(one, dim3((unsigned)grid), dim3(256), 0, st, wp, xp, y, M, N);
         return hipGetLastError();
     }
     int tiles_m = (M + mm::BM - 1) / mm::BM;
@@ -575,6 +704,8 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
     const void *kern = WFMT == F_Q8_0   ? (const void *)k_matmul_q8_0
                        : WFMT == F_Q5_0 ? (const void *)k_matmul_q5_0
+                       : WFMT == F_Q4_1 ? (const void *)k_matmul_q4_1
+                       : WFMT == F_Q5_1 ? (const void *)k_matmul_q5_1
                                         : (const void *)k_matmul_q4_0;
     return hipLaunchKernel(kern, dim3((unsigned)tiles), dim3(mm::NT), args, 0, st);
 }
@@ -589,6 +720,14 @@ hipError_t launch_matmul_q8_0(const void *w, const void *xq, float *y, int M, in
 
 hipError_t launch_matmul_q5_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
     return launch_mm<F_Q5_0>(w, xq, y, M, N, nb, st);
+}
+
+hipError_t launch_matmul_q4_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    return launch_mm<F_Q4_1>(w, xq, y, M, N, nb, st);
+}
+
+hipError_t launch_matmul_q5_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    return launch_mm<F_Q5_1>(w, xq, y, M, N, nb, st);
 }
 
 }  // namespace qmm

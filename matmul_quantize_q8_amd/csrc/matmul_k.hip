@@ -99,7 +99,6 @@ template <int F> struct KW {
 }  // namespace mk
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 
 // BYTES per lane from a buffer into LDS at m0base + OFF + 16 * lane (see the
 // Q4_0 prefill kernel: inline assembly so that the compiler neither waits for

@@ -793,25 +793,4 @@ hipError_t launch_matvec_q6_k(const void *w, const void *xq, float *y, int N, in
     return dispatch_mv<F_Q6_K>(w, xq, nullptr, y, 1, N, ns, st);
 }
 
-// Prefill of the formats without an MFMA kernel (Q4_1, Q5_1): the
-// matvec kernel with one grid row per token (the weights are re-read from
-// cache for each token; correct for any M, not tuned).
-template <int F>
-static hipError_t matmul_by_tokens(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
-    constexpr int kMaxY = 65535;
-    for (int m0 = 0; m0 < M; m0 += kMaxY) {
-        const int mc = min(kMaxY, M - m0);
-        const uint8_t *xp = static_cast<const uint8_t *>(xq) + (int64_t)m0 * ns * FmtBytes<F>::XB;
-        const hipError_t e = dispatch_mv<F>(w, xp, nullptr, y + (int64_t)m0 * N, mc, N, ns, st);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-}
-hipError_t launch_matmul_q4_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
-    return matmul_by_tokens<F_Q4_1>(w, xq, y, M, N, nb, st);
-}
-hipError_t launch_matmul_q5_1(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
-    return matmul_by_tokens<F_Q5_1>(w, xq, y, M, N, nb, st);
-}
-
 }  // namespace qmm

@@ -27,6 +27,7 @@ template <int F> constexpr bool kIsK = F == F_Q2_K || F == F_Q4_K || F == F_Q6_K
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 // binary32 -> binary16 bits: v_cvt_f16_f32 rounds to nearest even under the
 // default MODE and keeps f16 denormals.

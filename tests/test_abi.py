@@ -87,6 +87,8 @@ A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced
     (lambda L: L.qmm_matmul_q4_0(A, A, A, 4, 8, 32 * ((2**31 - 1) // (128 * 34) + 1), None), 1),
     (lambda L: L.qmm_matmul_q8_0(A, A, A, 4, 8, 32 * ((2**31 - 1) // (128 * 34) + 1), None), 1),
     (lambda L: L.qmm_matmul_q5_0(A, A, A, 4, 8, 32 * ((2**31 - 1) // (128 * 34) + 1), None), 1),
+    (lambda L: L.qmm_matmul_q4_1(A, A, A, 4, 8, 32 * ((2**31 - 1) // (128 * 34) + 1), None), 1),
+    (lambda L: L.qmm_matmul_q5_1(A, A, A, 4, 8, 32 * ((2**31 - 1) // (128 * 34) + 1), None), 1),
     (lambda L: L.qmm_matmul_q2_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
     (lambda L: L.qmm_matmul_q4_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
     (lambda L: L.qmm_matmul_q6_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),

@@ -304,7 +304,11 @@ MATMUL_CASES = [
     ("q4_k", 128, 256, 256), ("q4_k", 130, 257, 512), ("q4_k", 257, 300, 2304), ("q4_k", 3, 520, 7936),
     ("q6_k", 1, 8, 256), ("q6_k", 9, 70, 1024), ("q6_k", 5, 33, 1280),
     ("q6_k", 128, 128, 256), ("q6_k", 130, 257, 512), ("q6_k", 257, 129, 2304), ("q6_k", 65, 300, 7936),
-    ("q4_1", 9, 70, 1024), ("q5_1", 9, 70, 1024),
+    # Q4_1 and Q5_1 on the same kernel, the offset term on an f32 MFMA
+    ("q4_1", 1, 8, 32), ("q4_1", 9, 70, 1024), ("q4_1", 5, 3, 96), ("q4_1", 130, 129, 160),
+    ("q4_1", 131, 255, 128), ("q4_1", 65, 130, 96), ("q4_1", 63, 127, 2048), ("q4_1", 129, 257, 64),
+    ("q5_1", 1, 8, 32), ("q5_1", 9, 70, 1024), ("q5_1", 5, 3, 96), ("q5_1", 130, 129, 160),
+    ("q5_1", 131, 255, 128), ("q5_1", 65, 130, 96), ("q5_1", 63, 127, 2048), ("q5_1", 300, 700, 2080),
     # Q5_0 on the Q4_0 MFMA kernel: one block, odd and even block counts, ragged tiles
     ("q5_0", 1, 8, 32), ("q5_0", 9, 70, 1024), ("q5_0", 5, 3, 96), ("q5_0", 130, 129, 160),
     ("q5_0", 131, 255, 128), ("q5_0", 65, 130, 96), ("q5_0", 63, 127, 2048), ("q5_0", 300, 700, 2080),
@@ -385,6 +389,29 @@ def test_matmul_q5_0_full_size_sampled(env):
     ni = np.concatenate([ni, np.tile(np.arange(0, N, 64), len(edge_m)), np.repeat(edge_n, len(range(0, M, 7)))])
     ref, mag = orc.matmul_sampled("q5_0", wq, xq, mi, ni, K)
     _check(y[mi, ni], ref, mag, "q5_0 prefill sampled")
+
+
+@pytest.mark.parametrize("fmt,cfg,seed", [("q4_1", 9, 98), ("q5_1", 11, 99)])
+def test_matmul_offset_formats_full_size_sampled(env, fmt, cfg, seed):
+    """The 2048 x 12288 x 4096 prefill with Q4_1 / Q5_1 weights (int8 MFMA
+    plus the offset term on an f32 MFMA), checked on sampled outputs and whole
+    rows and columns at the tile edges."""
+    torch, q, orc = env
+    M, N, K = 2048, 12288, 4096
+    _say("matmul", fmt, "full", M, N, K)
+    wq = orc.quantize_w(fmt, synth.weights(N, K, config=cfg))
+    xq = orc.quantize_q8_0(synth.activations(M, K, config=cfg))
+    y = _run_matmul(env, fmt, wq, xq, M, N, K)
+    assert np.isfinite(y).all()
+    rng = synth.splitmix64(seed, 0, 20000)
+    mi = (rng[:10000] % np.uint64(M)).astype(np.int64)
+    ni = (rng[10000:] % np.uint64(N)).astype(np.int64)
+    edge_m = np.array([0, 63, 64, 127, 128, 2047])
+    edge_n = np.array([0, 31, 32, 127, 128, 12287])
+    mi = np.concatenate([mi, np.repeat(edge_m, N // 64), np.tile(np.arange(0, M, 7), len(edge_n))])
+    ni = np.concatenate([ni, np.tile(np.arange(0, N, 64), len(edge_m)), np.repeat(edge_n, len(range(0, M, 7)))])
+    ref, mag = orc.matmul_sampled(fmt, wq, xq, mi, ni, K)
+    _check(y[mi, ni], ref, mag, fmt + " prefill sampled")
 
 
 def test_matmul_q2_k_full_size_sampled(env):

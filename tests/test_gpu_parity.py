@@ -480,6 +480,54 @@ def test_matmul_q6_k_full_size_sampled(env):
     _check(y[mi, ni], ref, mag, "q6_k prefill sampled")
 
 
+def _degenerate_weights(N, K, seed):
+    """Weight rows that hit the formats' corner cases, then Gaussian rows."""
+    w = synth.gaussian_f32((N, K), 0.02, seed)
+    w[0] = 0.0                                        # all-zero blocks (d = 0)
+    w[1] = 0.05                                       # constant: the extreme code in every block
+    w[2] = -0.05
+    w[3] = 0.0
+    w[3, ::32] = 0.7                                  # one nonzero per 32 values
+    w[4] *= 1e-4                                      # f16 scales in the subnormal range
+    w[5] *= 5e4                                       # large values
+    w[6, : K // 2] = 0.0                              # half a row zero
+    return w
+
+
+def _degenerate_activations(M, K, seed):
+    """Activation rows that hit the quantizer's corner cases, then Gaussian rows."""
+    x = synth.with_outliers(synth.gaussian_f32((M, K), 1.0, seed), 0.01, 20.0, seed + 1)
+    x[0] = 0.0                                        # zero blocks: d = 0, codes 0
+    x[1] = 1.0                                        # every code +127
+    x[2] = -1.0                                       # every code -127
+    x[3, 0::2], x[3, 1::2] = 1.0, -1.0                # alternating signs: block sums 0
+    x[4] *= 1e-7                                      # d rounds to 0 in f16, codes do not
+    x[5] *= 1e4                                       # large scales
+    x[6, :32] = np.arange(32, dtype=np.float32) - 15.5   # exact ties in x * id
+    x[6, 0] = 127.0
+    return x
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q4_1", "q5_0", "q5_1", "q2_k", "q4_k", "q6_k"])
+def test_products_on_degenerate_inputs(env, fmt):
+    """Matvec and matmul on corner-case weights and activations: zero and
+    constant rows, extreme codes (|I| at its largest), f16 scales that are
+    subnormal or round to zero, large scales, exact rounding ties."""
+    torch, q, orc = env
+    K = 768 if fmt in orc.K_QUANTS else 288          # 3 super-blocks, or 9 blocks (an odd count)
+    M, N = 130, 70
+    _say("degenerate", fmt, M, N, K)
+    wq = orc.quantize_w(fmt, _degenerate_weights(N, K, 7100 + K))
+    xq = orc.quantize_x(fmt, _degenerate_activations(M, K, 7200 + K))
+    ref = orc.matmul(fmt, wq, xq, M, N, K, threads=8, want=("y64", "mag"))
+    y = _run_matmul(env, fmt, wq, xq, M, N, K)
+    _check(y, ref["y64"], ref["mag"], (fmt, "matmul"))
+    assert np.all(y[0] == 0.0) and np.all(y[:, 0] == 0.0)   # a zero row or column gives exact zeros
+    for m in range(8):
+        yv = _run_matvec(env, fmt, wq, xq[m], N, K)
+        _check(yv, ref["y64"][m], ref["mag"][m], (fmt, "matvec", m))
+
+
 def test_matmul_rows_equal_matvec(env):
     """Row m of the prefill product and the decode product of token m are two
     evaluations of the same outputs: both within the bound of the oracle."""

@@ -313,6 +313,8 @@ MATMUL_CASES = [
     ("q5_0", 1, 8, 32), ("q5_0", 9, 70, 1024), ("q5_0", 5, 3, 96), ("q5_0", 130, 129, 160),
     ("q5_0", 131, 255, 128), ("q5_0", 65, 130, 96), ("q5_0", 63, 127, 2048), ("q5_0", 300, 700, 2080),
     ("q5_0", 129, 257, 64), ("q5_0", 128, 128, 4096),
+    # long rows: 1025 blocks (an odd count), 128 super-blocks
+    ("q4_0", 129, 65, 32800), ("q5_1", 65, 33, 32800), ("q2_k", 65, 129, 32768), ("q6_k", 33, 65, 32768),
 ]
 
 

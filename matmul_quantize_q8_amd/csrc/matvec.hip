@@ -703,8 +703,11 @@ static hipError_t launch_mv(const void *w, const void *xin, uint8_t *xq_out, flo
 // Rows per wave: a slice of about 5 KB.  Measured on MI355X over 28-96 MB
 // of weights, slices of 3-5 KB per wave (Q4_0 K=4096: 2 rows, Q8_0: 1 row,
 // Q2_K: 2 rows) beat larger ones: the work after the last byte lands is
-// smaller and all waves of the launch stay resident.  One row when the row
-// needs more than one segment.
+// smaller and all waves of the launch stay resident.  A row longer than
+// that is walked by one wave in segments of 64 units (4.4 KB of Q8_0), so
+// that the slices stay small and every workgroup fits in LDS at once (Q8_0
+// 4096 x 11008: 11.3 us against 12.4 us with whole-row slices of 11.7 KB,
+// which left room for two workgroups per CU and ran in two rounds).
 template <int F, bool PAIRED, bool XF32>
 static hipError_t pick_mv(const void *w, const void *xin, uint8_t *xq_out, float *y, int M, int N, int nb,
                           hipStream_t st) {
@@ -718,8 +721,8 @@ static hipError_t pick_mv(const void *w, const void *xin, uint8_t *xq_out, float
     constexpr int NW1 = XF32 ? 8 : 4;
     const int nu = (nb / UT::BPU) * UT::UPB;
     const int64_t rb = (int64_t)nb * FB::BB;
-    if (nu > kWave * 4) return launch_mv<F, PAIRED, 1, 4, XF32>(w, xin, xq_out, y, M, N, nb, st);
     const int64_t g = 5000 / rb;
+    if (nu > kWave && g == 0) return launch_mv<F, PAIRED, 1, 1, XF32>(w, xin, xq_out, y, M, N, nb, st);
     if (nu <= kWave) {
         if (g >= 8) return launch_mv<F, PAIRED, 8, 1, XF32, NW1>(w, xin, xq_out, y, M, N, nb, st);
         if (g >= 4) return launch_mv<F, PAIRED, 4, 1, XF32, NW1>(w, xin, xq_out, y, M, N, nb, st);

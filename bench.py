@@ -401,12 +401,13 @@ def bench_matvec_configs(args, torch, q, synth):
                                "hbm_frac": round(tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
-def bench_peaks(args, torch, q):
+def bench_peaks(args, torch, q, sizes=()):
     """Measured ceilings (library probes): a streaming read of 1 GiB in one
     pass; passes of the decode's 28,311,552 weight bytes over rotating slices
     of that buffer (37 slices, 1 GiB > the 256 MB last-level cache, so each
-    pass is cold, as each decode step is); and back-to-back int8 MFMAs on
-    register operands at two and three waves per SIMD."""
+    pass is cold, as each decode step is), and the same for every other decode
+    workload's weight size in `sizes`; and back-to-back int8 MFMAs on register
+    operands at two and three waves per SIMD."""
     size = 1 << 30
     buf = torch.arange(size // 4, dtype=torch.int32, device="cuda")
     sink = torch.zeros(size // 8192, dtype=torch.int32, device="cuda")
@@ -419,6 +420,11 @@ def bench_peaks(args, torch, q):
     for i in range(ns):
         q.qmm_peak_read(base + (i % ns) * S, S, sink)
     sl_ms, sl_min, _ = time_batches(torch, lambda i: q.qmm_peak_read(base + (i % ns) * S, S, sink), args.steps, ns)
+    by_size = {}
+    for B in sorted(set(sizes)):
+        nb_ = size // B
+        b_ms, _, _ = time_batches(torch, lambda i: q.qmm_peak_read(base + (i % nb_) * B, B, sink), args.steps, nb_)
+        by_size[str(B)] = round(b_ms * 1e3, 3)
     del buf
     mfma = []
     for wg, iters in ((512, 4000), (768, 2700)):
@@ -434,6 +440,7 @@ def bench_peaks(args, torch, q):
     res = {"hbm_read_1GiB_gbs": round(size / (big_ms * 1e-3) / 1e9, 1),
            "hbm_read_28MB_gbs": round(S / (sl_ms * 1e-3) / 1e9, 1),
            "hbm_read_28MB_us_mean": round(sl_ms * 1e3, 3), "hbm_read_28MB_us_best_batch": round(sl_min * 1e3, 3),
+           "hbm_read_us_by_bytes": by_size,
            "int8_mfma_tops": round(tops, 1), "int8_mfma_waves_per_simd": waves,
            "kernels": ["qmm::k_peak_read", "qmm::k_peak_mfma_i8"]}
     log(f"peaks: read 1 GiB {res['hbm_read_1GiB_gbs']} GB/s, 28 MB passes {res['hbm_read_28MB_gbs']} GB/s "
@@ -513,7 +520,8 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}), flush=True)
         return
 
-    peaks = bench_peaks(args, torch, q) if args.only in ("all", "decode", "prefill") else None
+    sizes = [N * q.row_bytes(fmt, K) for fmt, N, K, *_ in MATVEC_CONFIGS] if args.only in ("all", "configs") else []
+    peaks = bench_peaks(args, torch, q, sizes)
     dec = bench_decode(args, torch, q, synth) if args.only in ("all", "decode") else None
     pre = bench_prefill(args, torch, q, synth) if args.only in ("all", "prefill") else None
     cfgs = bench_matvec_configs(args, torch, q, synth) if args.only in ("all", "configs") else None
@@ -528,11 +536,10 @@ def main():
 
     out = {"metric": METRIC, "n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "int8", "data": "synthetic"}
-    if peaks is not None:
-        if dec is not None:
-            dec["roofline"]["frac_of_attainable"] = round(dec["roofline"]["achieved"] / peaks["hbm_read_28MB_gbs"], 4)
-        if pre is not None:
-            pre["roofline"]["frac_of_attainable"] = round(pre["roofline"]["achieved"] / peaks["int8_mfma_tops"], 4)
+    if dec is not None:
+        dec["roofline"]["frac_of_attainable"] = round(dec["roofline"]["achieved"] / peaks["hbm_read_28MB_gbs"], 4)
+    if pre is not None:
+        pre["roofline"]["frac_of_attainable"] = round(pre["roofline"]["achieved"] / peaks["int8_mfma_tops"], 4)
     if dec is not None:
         out.update({"value": round(dec["gbs"], 1), "unit": "GB/s", "steps": dec["nsteps"], "warmup": args.warmup,
                     "ms_per_step": round(dec["ms_step"], 5),
@@ -559,9 +566,13 @@ def main():
         else:
             out["prefill"] = pf
     if cfgs is not None:
+        for r in cfgs["rows"]:
+            att = peaks["hbm_read_us_by_bytes"].get(str(r.get("weight_bytes")))
+            if att is not None:
+                r["attainable_read_us"] = att
+                r["frac_of_attainable"] = round(att / r["kernel_us_mean"], 4)
         out["matvec_configs"] = cfgs
-    if peaks is not None:
-        out["attainable"] = peaks
+    out["attainable"] = peaks
     print(json.dumps(out), flush=True)
 
 

@@ -245,19 +245,29 @@ __device__ __forceinline__ float unit_dot<F_Q2_K, false>(const uint8_t *sl, uint
     for (int k = 0; k < 4; ++k) q[k] = b32[4 + 4 * p + k];
     const uint32_t sc01 = b32[2 * h], sc23 = b32[2 * h + 1];
     const uint32_t dd = b32[20];
-    int V = 0, Mn = 0;
+    // Bit pair s of each byte is used in place: q & (3 << 2s) is 4^s times
+    // the code (at most 48, a positive int8, for s < 3); pair 3 is shifted
+    // down by two first (16 times the code).  The group dots are then
+    // G = (g0, 4 g1, 16 g2, 16 g3) and 16 V = 16 sc0 G0 + 4 sc1 G1 + sc2 G2
+    // + sc3 G3 (|16 V| < 2^23, exact in f32).
+    int G0 = 0, G1 = 0, G2 = 0, G3 = 0;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const uint32_t sw = (s < 2) ? sc01 : sc23;
-        const uint32_t scm = (sw >> (8 * (2 * (s & 1) + odd))) & 0xffu;
-        int g = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) g = dot4((int)((q[k] >> (2 * s)) & 0x03030303u), x.q[4 * s + k], g);
-        V += (int)(scm & 0x0f) * g;
-        Mn += (int)(scm >> 4) * x.bs[s];
+    for (int k = 0; k < 4; ++k) {
+        G0 = dot4((int)(q[k] & 0x03030303u), x.q[k], G0);
+        G1 = dot4((int)(q[k] & 0x0c0c0c0cu), x.q[4 + k], G1);
+        G2 = dot4((int)(q[k] & 0x30303030u), x.q[8 + k], G2);
+        G3 = dot4((int)((q[k] >> 2) & 0x30303030u), x.q[12 + k], G3);
     }
+    // group s's scale byte: byte 2 (s & 1) + odd of sc01 (s < 2) or sc23
+    const uint32_t o0 = 8u * (uint32_t)odd, o1 = o0 + 16u;
+    const int sc0 = (int)__builtin_amdgcn_ubfe(sc01, o0, 4), m0 = (int)__builtin_amdgcn_ubfe(sc01, o0 + 4u, 4);
+    const int sc1 = (int)__builtin_amdgcn_ubfe(sc01, o1, 4), m1 = (int)__builtin_amdgcn_ubfe(sc01, o1 + 4u, 4);
+    const int sc2 = (int)__builtin_amdgcn_ubfe(sc23, o0, 4), m2 = (int)__builtin_amdgcn_ubfe(sc23, o0 + 4u, 4);
+    const int sc3 = (int)__builtin_amdgcn_ubfe(sc23, o1, 4), m3 = (int)__builtin_amdgcn_ubfe(sc23, o1 + 4u, 4);
+    const int V16 = 16 * sc0 * G0 + 4 * sc1 * G1 + sc2 * G2 + sc3 * G3;
+    const int Mn = m0 * x.bs[0] + m1 * x.bs[1] + m2 * x.bs[2] + m3 * x.bs[3];
     const float d = f16_bits_to_f32(dd), dmin = f16_bits_to_f32(dd >> 16);
-    acc = fmaf(d * x.d, (float)V, acc);
+    acc = fmaf(d * x.d * 0.0625f, (float)V16, acc);
     return fmaf(-(dmin * x.d), (float)Mn, acc);
 }
 

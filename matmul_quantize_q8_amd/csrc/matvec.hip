@@ -702,7 +702,7 @@ static hipError_t launch_mv(const void *w, const void *xin, uint8_t *xq_out, flo
     int64_t xrow = XF32 ? (int64_t)nb * 128 : (int64_t)nb * FB::XB;
     const auto kern = k_matvec<F, PAIRED, G, MAXU, XF32, NW>;
     const size_t lds = (size_t)xs + (size_t)NW * ss;
-    static int lds_ok = 0;
+    static int lds_ok[kLdsDevices] = {};
     const hipError_t e = allow_dynamic_lds((const void *)kern, lds, lds_ok);
     if (e != hipSuccess) return e;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&N, (void *)&nb,

@@ -82,12 +82,21 @@ __device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vm
 // Wait for every outstanding LDS access of this wave.
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Launch helper: kernels that use more than 64 KB of dynamic LDS raise their
-// limit once (gfx950 has 160 KB per workgroup).
-inline hipError_t allow_dynamic_lds(const void *kernel, size_t bytes, int &done) {
-    if (bytes <= 65536 || __atomic_load_n(&done, __ATOMIC_ACQUIRE)) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) __atomic_store_n(&done, 1, __ATOMIC_RELEASE);
+// Launch helper for kernels with only dynamic LDS: a launch that asks for
+// more than 64 KB first raises the kernel's limit, once per device, to the
+// whole 160 KB a gfx950 workgroup may use (the attribute is a permission,
+// not an allocation, so later launches of any size up to that need nothing
+// more).  `done` is the call site's per-device flag array.
+constexpr int kMaxLdsBytes = 160 * 1024;
+constexpr int kLdsDevices = 64;
+inline hipError_t allow_dynamic_lds(const void *kernel, size_t bytes, int (&done)[kLdsDevices]) {
+    if (bytes <= 65536) return hipSuccess;
+    if (bytes > (size_t)kMaxLdsBytes) return hipErrorInvalidValue;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kLdsDevices) return hipErrorInvalidDevice;
+    if (__atomic_load_n(&done[dev], __ATOMIC_ACQUIRE)) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
+    if (e == hipSuccess) __atomic_store_n(&done[dev], 1, __ATOMIC_RELEASE);
     return e;
 }
 

@@ -550,7 +550,8 @@ template <> struct Pow2Ceil<1> { static constexpr int V = 1; };
 // --- the kernel ---------------------------------------------------------------
 // Dynamic LDS: [activation segment: xs bytes][NW wave slices of ss bytes].
 // gridDim.y tokens: token t reads activation row t (xrow bytes apart) and
-// writes output row t; the weight rows are re-read for every token.
+// writes output row t; the weight rows are re-read for every token (every
+// entry point launches one token; prefill has its own MFMA kernels).
 // XF32: `xin` is f32 activations and xq_out (may be null) receives the Q8_0
 // rows; otherwise `xin` is Q8_0 / Q8_K activation blocks.
 template <int F, bool PAIRED, int G, int MAXU, bool XF32, int NW>

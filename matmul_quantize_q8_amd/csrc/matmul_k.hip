@@ -318,31 +318,47 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) V[i][r] = 0;
-            uint4 qs = {};
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {
-                if ((kt & 1) == 0) qs = rd16(sb + wb + 16 + 32 * (kt >> 1) + 16 * lh);
+            // The 32 steps t = 4 kt + i are software-pipelined: the MFMA of
+            // step t+1 is issued before the scale mads of step t (two int32
+            // tiles live), its A operand is read one step ahead and each
+            // 16-byte code chunk (K-steps 2c, 2c+1) three steps before its
+            // first use, so that neither the LDS reads nor the MFMA latency
+            // stall the wave.
+            auto nibbles = [](const uint4 &q, int kt) __attribute__((always_inline)) {
                 const uint32_t sh = 4u * (uint32_t)(kt & 1);
-                const v4i b = v4i{(int)((qs.x >> sh) & 0x0f0f0f0fu), (int)((qs.y >> sh) & 0x0f0f0f0fu),
-                                  (int)((qs.z >> sh) & 0x0f0f0f0fu), (int)((qs.w >> sh) & 0x0f0f0f0fu)};
-                const v16i zero = {};
-                // one tile at a time (one int32 tile live): the other wave
-                // of the SIMD covers the MFMA latency
+                return v4i{(int)((q.x >> sh) & 0x0f0f0f0fu), (int)((q.y >> sh) & 0x0f0f0f0fu),
+                           (int)((q.z >> sh) & 0x0f0f0f0fu), (int)((q.w >> sh) & 0x0f0f0f0fu)};
+            };
+            auto read_a = [&](int t) __attribute__((always_inline)) {
+                return as_v4i(rd16(sb + xa + XROW * 32 * (t & 3) + 32 * (t >> 2) + 16 * lh));
+            };
+            const v16i zero = {};
+            uint4 qs = rd16(sb + wb + 16 + 16 * lh);   // chunk 0
+            v4i b = nibbles(qs, 0);
+            v4i an = read_a(1);
+            v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(read_a(0), b, zero, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const v4i a = as_v4i(rd16(sb + xa + XROW * 32 * i + 32 * kt + 16 * lh));
-                    const v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, zero, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int e = I[r];
-                        V[i][r] = __mul24(sc[kt], e) + V[i][r];   // v_mad_i32_i24
-                        // pin the running sum: left to itself the compiler
-                        // re-associates the accumulation across K-steps and
-                        // keeps the products of several steps live
-                        asm volatile("" : "+v"(V[i][r]));
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < 32; ++t) {
+                const int kt = t >> 2, i = t & 3;
+                v16i In = zero;
+                if (t + 1 < 32) {
+                    if (((t + 1) & 3) == 0) b = nibbles(qs, (t + 1) >> 2);
+                    In = __builtin_amdgcn_mfma_i32_32x32x32_i8(an, b, zero, 0, 0, 0);
+                    if (t + 2 < 32) an = read_a(t + 2);
+                    // the next chunk, once the last B operand built from this one is out
+                    if (i == 0 && (kt & 1) == 1 && kt < 7) qs = rd16(sb + wb + 16 + 32 * ((kt + 1) >> 1) + 16 * lh);
                 }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int e = I[r];
+                    V[i][r] = __mul24(sc[kt], e) + V[i][r];   // v_mad_i32_i24
+                    // pin the running sum: left to itself the compiler
+                    // re-associates the accumulation across K-steps and
+                    // keeps the products of several steps live
+                    asm volatile("" : "+v"(V[i][r]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                I = In;
             }
             float dw = half_lo(dd), ndm = -half_hi(dd);
             // keep the f32 values (an f16 operand would make each fold FMA a
@@ -394,41 +410,62 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) V[i][r] = 0;
+            // Steps t = 8 (2 hh + gg) + 2 k + i, software-pipelined as for
+            // Q4_K: the MFMA of step t+1 goes out before the mads of step t,
+            // A operands are read one step ahead, and the code bytes of the
+            // next (hh, gg) pair (this lane's 8 values of its groups 8hh + 2k
+            // + gg: l = 16gg + 8lh ..) one pair ahead.
+            struct Codes {
+                uint2 qa, qb, qh;
+            };
+            auto read_codes = [&](int p) __attribute__((always_inline)) {
+                const int hh = p >> 1, gg = p & 1;
+                return Codes{rd8(sb + wb + 64 * hh + 16 * gg + 8 * lh), rd8(sb + wb + 64 * hh + 32 + 16 * gg + 8 * lh),
+                             rd8(sb + wb + 128 + 32 * hh + 16 * gg + 8 * lh)};
+            };
+            auto group = [](int t) { return 8 * (t >> 4) + 2 * ((t >> 1) & 3) + ((t >> 3) & 1); };
+            auto build_b = [](const Codes &q, int k) __attribute__((always_inline)) {
+                const uint2 ql = (k & 1) ? q.qb : q.qa;
+                const uint32_t nsh = 4u * (uint32_t)(k >> 1), hsh = 2u * (uint32_t)k;
+                const uint32_t b0 = ((ql.x >> nsh) & 0x0f0f0f0fu) | (((q.qh.x >> hsh) & 0x03030303u) << 4);
+                const uint32_t b1 = ((ql.y >> nsh) & 0x0f0f0f0fu) | (((q.qh.y >> hsh) & 0x03030303u) << 4);
+                return (long)(((uint64_t)b1 << 32) | b0);
+            };
+            auto read_a = [&](int t) __attribute__((always_inline)) {
+                const uint2 av = rd8(sb + xa + XROW * 32 * (t & 1) + 16 * group(t) + 8 * lh);
+                return (long)(((uint64_t)av.y << 32) | av.x);
+            };
+            const v16i zero = {};
+            Codes qc = read_codes(0), qn = read_codes(1);
+            long b = build_b(qc, 0);
+            long an = read_a(1);
+            v16i I = __builtin_amdgcn_mfma_i32_32x32x16_i8(read_a(0), b, zero, 0, 0, 0);
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int gg = 0; gg < 2; ++gg) {
-                    // this lane's 8 values of groups 8hh + 2k + gg: l = 16gg + 8lh ..
-                    const uint2 qa = rd8(sb + wb + 64 * hh + 16 * gg + 8 * lh);
-                    const uint2 qb = rd8(sb + wb + 64 * hh + 32 + 16 * gg + 8 * lh);
-                    const uint2 qh = rd8(sb + wb + 128 + 32 * hh + 16 * gg + 8 * lh);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int g = 8 * hh + 2 * k + gg;
-                        const uint2 ql = (k & 1) ? qb : qa;
-                        const uint32_t nsh = 4u * (uint32_t)(k >> 1), hsh = 2u * (uint32_t)k;
-                        const uint32_t b0 = ((ql.x >> nsh) & 0x0f0f0f0fu) | (((qh.x >> hsh) & 0x03030303u) << 4);
-                        const uint32_t b1 = ((ql.y >> nsh) & 0x0f0f0f0fu) | (((qh.y >> hsh) & 0x03030303u) << 4);
-                        const long b = (long)(((uint64_t)b1 << 32) | b0);
-                        const int sc = scale(g);
-                        const v16i zero = {};
-                        // one tile at a time (one int32 tile live); the other
-                        // wave of the SIMD covers the MFMA latency
-#pragma unroll
-                        for (int i = 0; i < 2; ++i) {
-                            const uint2 av = rd8(sb + xa + XROW * 32 * i + 16 * g + 8 * lh);
-                            const long a = (long)(((uint64_t)av.y << 32) | av.x);
-                            const v16i I = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, b, zero, 0, 0, 0);
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int e = I[r];
-                                V[i][r] = __mul24(sc, e) + V[i][r];   // v_mad_i32_i24
-                                asm volatile("" : "+v"(V[i][r]));    // keep the running sum (see Q4_K)
-                            }
-                            __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < 32; ++t) {
+                const int i = t & 1;
+                v16i In = zero;
+                if (t + 1 < 32) {
+                    const int t1 = t + 1;
+                    if ((t1 & 1) == 0) {                       // a new group: new B operand
+                        if ((t1 & 7) == 0) {                   // and a new (hh, gg) pair
+                            qc = qn;
+                            if ((t1 >> 3) + 1 < 4) qn = read_codes((t1 >> 3) + 1);
                         }
+                        b = build_b(qc, (t1 >> 1) & 3);
                     }
+                    In = __builtin_amdgcn_mfma_i32_32x32x16_i8(an, b, zero, 0, 0, 0);
+                    if (t + 2 < 32) an = read_a(t + 2);
                 }
+                const int sc = scale(group(t));
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int e = I[r];
+                    V[i][r] = __mul24(sc, e) + V[i][r];   // v_mad_i32_i24
+                    asm volatile("" : "+v"(V[i][r]));    // keep the running sum (see Q4_K)
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                I = In;
+            }
             float dw = half_hi(rd4(sb + wb + 220));   // d: bytes 208..209 of the super-block
             asm volatile("" : "+v"(dw));
             const float ndw = -dw;

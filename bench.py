@@ -468,8 +468,19 @@ def cpu_baseline_decode(args, q, synth):
         t_total += time.perf_counter() - t
         reps += 1
     per = t_total / reps
+    # the scalar oracle on one core, over a quarter of the budget
+    reps1, t1 = 0, 0.0
+    while t1 < args.cpu_seconds / 4 or reps1 < 1:
+        t = time.perf_counter()
+        xq = oracle.quantize_q8_0(x)
+        oracle.matmul("q4_0", wq, xq, 1, N, K, threads=1, want=("y",))
+        t1 += time.perf_counter() - t
+        reps1 += 1
+    per1 = t1 / reps1
     return {"value": round(wq.nbytes / per / 1e9, 3), "unit": "GB/s", "cores": thr, "kind": "oracle",
-            "sample": f"full {N}x{K} decode step (quantize + matvec), {reps} repeats, {per * 1e3:.1f} ms each"}
+            "sample": f"full {N}x{K} decode step (quantize + matvec), {reps} repeats, {per * 1e3:.1f} ms each",
+            "single_core": {"value": round(wq.nbytes / per1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                            "sample": f"the same step, {reps1} repeats, {per1 * 1e3:.1f} ms each"}}
 
 
 def cpu_baseline_prefill(args, q, synth):
@@ -489,8 +500,21 @@ def cpu_baseline_prefill(args, q, synth):
             break
         m = min(M, m * 4)
     ops = 2.0 * m * N * K
+    # the scalar oracle on one core: token count grown the same way within a quarter of the budget
+    m1 = 1
+    while True:
+        x = synth.activations(m1, K, config=4)
+        t = time.perf_counter()
+        xq = oracle.quantize_q8_0(x)
+        oracle.matmul("q4_0", wq, xq, m1, N, K, threads=1, want=("y",))
+        dt1 = time.perf_counter() - t
+        if dt1 * 4 > args.cpu_seconds / 4 or m1 >= M:
+            break
+        m1 = min(M, m1 * 4)
     return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": thr, "kind": "oracle",
-            "sample": f"first {m} of {M} tokens of the {M}x{N}x{K} prefill ({dt:.1f} s)"}
+            "sample": f"first {m} of {M} tokens of the {M}x{N}x{K} prefill ({dt:.1f} s)",
+            "single_core": {"value": round(2.0 * m1 * N * K / dt1 / 1e12, 6), "unit": "TOPS", "cores": 1,
+                            "sample": f"first {m1} of {M} tokens ({dt1:.1f} s)"}}
 
 
 def main():

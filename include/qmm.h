@@ -199,9 +199,15 @@ qmm_status qmm_quantize_matvec_q4_0(const void *w, const float *x, void *xq, flo
 qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, float *y, int64_t N, int64_t K,
                                     void *stream);
 
-/* Prefill matmul, M tokens.
+/* Matmul, M tokens (prefill, or a few tokens at once).
  *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.
  *   y  : f32 [M][N], written.
+ * Up to 16 tokens run on the decode matvec kernel, which streams each weight
+ * slice once per group of 4 or 8 tokens (one token: the decode launch
+ * itself); more tokens run on the MFMA kernels below, whose 128-token tiles
+ * would leave most CUs idle for a few tokens.  Results agree within the
+ * same tolerance either way (they are not bitwise identical: the two paths
+ * sum the blocks in different orders).
  * The 32-value formats (Q4_0, Q8_0, Q4_1, Q5_0, Q5_1) run on int8 MFMA (4-bit
  * codes enter as 16 * (q - 8), 5-bit codes as 8 * (q - 16); the offset term
  * of Q4_1 / Q5_1, m * dx * sum x per block, runs on an f32 MFMA) and also

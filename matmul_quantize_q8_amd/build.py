@@ -2,14 +2,18 @@
 
 Flags: -O3; -ffp-contract=off so no multiply and add are fused unless the
 source asks for fmaf (the quantizers are bit-exact only without contraction);
-f32 denormals kept; packed-FP32 instructions disabled.
+f32 denormals kept; packed-FP32 instructions disabled.  Each source compiles
+to an object in its own hipcc process (in parallel), then one hipcc links the
+shared library.
 """
 from __future__ import annotations
 
 import glob
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -17,7 +21,7 @@ LIB = os.path.join(HERE, "libqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -28,21 +32,43 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
+def _filtered(text: str) -> str:
+    # hipcc's host pass does not know the packed-FP32 target feature; harmless
+    return "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libqmm.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-                             "-o", tmp] + sources()
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if proc.returncode != 0:
-        sys.stderr.write(out + "\n")
-        raise RuntimeError("hipcc failed building libqmm.so")
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
+    """Compile every HIP source and link libqmm.so (always recompiles)."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    tmpdir = tempfile.mkdtemp(prefix="qmm_build_", dir=HERE)
+    try:
+        jobs = []
+        for src in sources():
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [HIPCC] + FLAGS + inc + ["-c", "-o", obj, src]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            jobs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                    text=True)))
+        failed = False
+        for src, _, proc in jobs:
+            out = _filtered(proc.communicate()[0])
+            if proc.returncode != 0:
+                failed = True
+                sys.stderr.write(f"{src}:\n{out}\n")
+            elif verbose and out.strip():
+                print(out)
+        if failed:
+            raise RuntimeError("hipcc failed building libqmm.so")
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [obj for _, obj, _ in jobs]
+        proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if proc.returncode != 0:
+            sys.stderr.write(_filtered(proc.stdout) + "\n")
+            raise RuntimeError("hipcc failed linking libqmm.so")
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

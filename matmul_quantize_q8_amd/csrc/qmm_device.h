@@ -22,6 +22,14 @@ constexpr int kQ6KBytes = 210;            // ql[128] + qh[64] + int8 scales[16] 
 // activations, the 32-value formats with Q8_0 (minfer "Two activation
 // formats, one pairing rule").
 enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4, F_Q4_1 = 5, F_Q5_0 = 6, F_Q5_1 = 7 };
+
+// Token counts up to this run the products on the decode kernel with several
+// tokens per weight pass; larger counts run the MFMA prefill kernels, whose
+// 128-token tiles leave most CUs idle below it (N = 12288, K = 4096: about
+// 64 us for any M <= 128).
+constexpr int kSmallTokens = 16;
+hipError_t launch_matvec_tokens(int fmt, const void *w, const void *xq, float *y, int M, int N, int nb,
+                                hipStream_t st);
 template <int F> constexpr bool kIsK = F == F_Q2_K || F == F_Q4_K || F == F_Q6_K;
 
 typedef int v4i __attribute__((ext_vector_type(4)));

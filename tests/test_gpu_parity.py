@@ -318,6 +318,31 @@ MATMUL_CASES = [
 ]
 
 
+# Few tokens (M <= 16): the decode kernel with 4 or 8 tokens per weight pass;
+# ragged token groups, odd block counts (unpaired units), rows walked in
+# segments (K = 8192 and 11008), every format.
+SMALL_M_CASES = [
+    ("q4_0", 2, 130, 4096), ("q4_0", 3, 77, 4128), ("q4_0", 8, 12288, 4096), ("q4_0", 9, 65, 8192),
+    ("q4_0", 15, 33, 11008), ("q4_0", 16, 129, 1024), ("q4_0", 5, 9, 32), ("q4_0", 17, 65, 4096),
+    ("q8_0", 4, 257, 4096), ("q8_0", 7, 70, 11008), ("q8_0", 16, 33, 2080), ("q8_0", 13, 64, 96),
+    ("q4_1", 6, 130, 4096), ("q4_1", 12, 17, 4128), ("q5_0", 6, 130, 4096), ("q5_0", 14, 9, 8192),
+    ("q5_1", 6, 130, 4096), ("q5_1", 2, 31, 160),
+    ("q2_k", 2, 130, 4096), ("q2_k", 11, 70, 2304), ("q2_k", 16, 33, 11008),
+    ("q4_k", 3, 130, 4096), ("q4_k", 8, 12288, 4096), ("q4_k", 10, 31, 11008),
+    ("q6_k", 5, 130, 4096), ("q6_k", 16, 65, 2304), ("q6_k", 9, 33, 11008),
+]
+
+
+@pytest.mark.parametrize("fmt,M,N,K", SMALL_M_CASES)
+def test_matmul_few_tokens_matches_oracle(env, fmt, M, N, K):
+    _, _, orc = env
+    _say("matmul few tokens", fmt, M, N, K)
+    wq, xq = _inputs(fmt, M, N, K, 9000 + M + N + K)
+    ref = orc.matmul(fmt, wq, xq, M, N, K, threads=8, want=("y64", "mag"))
+    y = _run_matmul(env, fmt, wq, xq, M, N, K)
+    _check(y, ref["y64"], ref["mag"], (fmt, M, N, K))
+
+
 @pytest.mark.parametrize("fmt,M,N,K", MATMUL_CASES)
 def test_matmul_matches_oracle(env, fmt, M, N, K):
     _, _, orc = env

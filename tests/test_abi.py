@@ -123,6 +123,22 @@ def test_python_binding_raises(q):
     assert e.value.code == "QMM_E_SHAPE"
 
 
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libqmm.so the binding raises instead of computing anything
+    (there is no CPU fallback)."""
+    import subprocess
+    import sys
+    code = ("import matmul_quantize_q8_amd as q\n"
+            "q.LIB_PATH = q.os.path.join(%r, 'libqmm.so')\n"
+            "q._lib = None\n"
+            "try:\n"
+            "    q.qmm_quantize_q8_0(1 << 20, 1 << 20, 1, 32, stream=0)\n"
+            "except ImportError as e:\n"
+            "    print('raised', 'no fallback' in str(e))\n" % str(tmp_path))
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert out.stdout.strip() == "raised True", (out.stdout, out.stderr)
+
+
 def test_product_path_has_no_oracle_dependency():
     """The package never imports or loads the oracle."""
     pkg = os.path.join(ROOT, "matmul_quantize_q8_amd")

@@ -488,6 +488,86 @@ __device__ __forceinline__ int dma_span(const uint8_t *src, int64_t lo, int64_t 
     return issued;
 }
 
+// --- a row's weight unit held for several tokens -------------------------------
+// The few-token path dots one weight unit with every token.  In general the
+// unit is re-read from LDS for each token; a paired Q4_0 or Q8_0 unit keeps
+// its codes and scales in registers (18 VGPRs), so each further token costs
+// its 16 dot products and two folds.  Same integer sums and the same fmaf
+// order as unit_dot.
+template <int F, bool PAIRED> struct UnitW {
+    const uint8_t *sl;
+    uint32_t bo;
+    int u;
+    __device__ __forceinline__ void load(const uint8_t *s, uint32_t o, int uu) {
+        sl = s;
+        bo = o;
+        u = uu;
+    }
+    __device__ __forceinline__ float dot(const XU<F, PAIRED> &x, float acc) const {
+        return unit_dot<F, PAIRED>(sl, bo, u, x, acc);
+    }
+};
+template <> struct UnitW<F_Q4_0, true> {
+    uint32_t c[16];   // block j: low nibbles of qs bytes 4k.. in c[8j + k], high nibbles in c[8j + 4 + k]
+    float dw[2];
+    __device__ __forceinline__ void load(const uint8_t *sl, uint32_t bo, int) {
+        const uint32_t *l32 = reinterpret_cast<const uint32_t *>(sl + bo);
+        uint32_t v[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) v[k] = l32[k];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t q0 = align_bytes(v[k + 1], v[k], 2), q1 = v[5 + k];
+            c[k] = q0 & 0x0f0f0f0fu;
+            c[4 + k] = (q0 >> 4) & 0x0f0f0f0fu;
+            c[8 + k] = q1 & 0x0f0f0f0fu;
+            c[12 + k] = (q1 >> 4) & 0x0f0f0f0fu;
+        }
+        dw[0] = f16_bits_to_f32(v[0]);
+        dw[1] = f16_bits_to_f32(v[4] >> 16);
+    }
+    __device__ __forceinline__ float dot(const XU<F_Q4_0, true> &x, float acc) const {
+        int s0 = 0, s1 = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            s0 = dot4((int)c[k], x.q[k], s0);
+            s0 = dot4((int)c[4 + k], x.q[k + 4], s0);
+            s1 = dot4((int)c[8 + k], x.q[8 + k], s1);
+            s1 = dot4((int)c[12 + k], x.q[12 + k], s1);
+        }
+        acc = fmaf(dw[0] * x.d[0], (float)(s0 - x.sx8[0]), acc);
+        return fmaf(dw[1] * x.d[1], (float)(s1 - x.sx8[1]), acc);
+    }
+};
+
+template <> struct UnitW<F_Q8_0, true> {
+    int c[16];        // block j's 32 codes in c[8j .. 8j + 7]
+    float dw[2];
+    __device__ __forceinline__ void load(const uint8_t *sl, uint32_t bo, int) {
+        const uint32_t *l32 = reinterpret_cast<const uint32_t *>(sl + bo);
+        uint32_t v[17];
+#pragma unroll
+        for (int k = 0; k < 17; ++k) v[k] = l32[k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            c[k] = (int)align_bytes(v[k + 1], v[k], 2);
+            c[8 + k] = (int)v[9 + k];
+        }
+        dw[0] = f16_bits_to_f32(v[0]);
+        dw[1] = f16_bits_to_f32(v[8] >> 16);
+    }
+    __device__ __forceinline__ float dot(const XU<F_Q8_0, true> &x, float acc) const {
+        int s0 = 0, s1 = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            s0 = dot4(c[k], x.q[k], s0);
+            s1 = dot4(c[8 + k], x.q[8 + k], s1);
+        }
+        acc = fmaf(dw[0] * x.d[0], (float)s0, acc);
+        return fmaf(dw[1] * x.d[1], (float)s1, acc);
+    }
+};
+
 // --- row-sum reduction across the wave -----------------------------------------
 __device__ __forceinline__ uint32_t f_as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float u_as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -650,30 +730,27 @@ __global__ __launch_bounds__(64 * NW) void k_matvec(const uint8_t *__restrict__ 
         }
         __builtin_amdgcn_s_barrier();                  // ... and every other wave's
         if constexpr (TT > 1) {
-            // every token against the whole slice: wait for it, then one
-            // token's activation registers at a time
+            // every token against the whole slice: wait for it, take each
+            // row's weight unit once, then one token's activation registers
+            // at a time
+            static_assert(MAXU == 1, "the few-token path runs one unit per lane and segment");
             wait_vmcnt(0);
             if (nrows > 0) {
+                const int ul = lane;                   // unit within the segment
+                const bool live = ul < u1 - u0;
+                UnitW<F, PAIRED> wu[G];
+#pragma unroll
+                for (int r = 0; r < G; ++r) {
+                    const uint32_t ro = (uint32_t)((min(row0 + r, row0 + nrows - 1)) * RB + (int64_t)b0 * FB::BB - A);
+                    wu[r].load(sl8, ro + (uint32_t)(min(ul, u1 - u0 - 1) / UT::UPB * UT::BPU) * FB::BB, u0 + ul);
+                }
 #pragma unroll
                 for (int t = 0; t < TT; ++t) {
-                    XU<F, PAIRED> xu[MAXU];
+                    XU<F, PAIRED> xu;
+                    load_xu<F, PAIRED>(xl8 + t * xs, xofft[t], min(ul, u1 - u0 - 1), xu);
 #pragma unroll
-                    for (int i = 0; i < MAXU; ++i)
-                        load_xu<F, PAIRED>(xl8 + t * xs, xofft[t], min(lane + kWave * i, u1 - u0 - 1), xu[i]);
-#pragma unroll
-                    for (int r = 0; r < G; ++r) {
-                        if (r < nrows) {
-                            const uint32_t ro = (uint32_t)((row0 + r) * RB + (int64_t)b0 * FB::BB - A);
-#pragma unroll
-                            for (int i = 0; i < MAXU; ++i) {
-                                const int ul = lane + kWave * i;
-                                if (ul < u1 - u0) {
-                                    const uint32_t bo = ro + (uint32_t)(ul / UT::UPB * UT::BPU) * FB::BB;
-                                    acc[r * TT + t] = unit_dot<F, PAIRED>(sl8, bo, u0 + ul, xu[i], acc[r * TT + t]);
-                                }
-                            }
-                        }
-                    }
+                    for (int r = 0; r < G; ++r)
+                        if (r < nrows && live) acc[r * TT + t] = wu[r].dot(xu, acc[r * TT + t]);
                 }
             }
             if (u1 < nu) {

@@ -689,7 +689,7 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
     if (nb > kMatmulMaxBlocks) return hipErrorInvalidValue;
-    if (M <= kSmallTokens) return launch_matvec_tokens(WFMT, w, xq, y, M, N, nb, st);
+    if (M <= small_tokens(WFMT)) return launch_matvec_tokens(WFMT, w, xq, y, M, N, nb, st);
     if (nb == 1) {
         const int64_t outs = (int64_t)M * N;
         const int64_t grid = (outs + 255) / 256;

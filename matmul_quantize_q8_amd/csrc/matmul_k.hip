@@ -528,7 +528,7 @@ int64_t matmul_k_max_blocks() { return kMatmulKMaxBlocks; }
 template <int F>
 static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
     if (ns > kMatmulKMaxBlocks) return hipErrorInvalidValue;
-    if (M <= kSmallTokens) return launch_matvec_tokens(F, w, xq, y, M, N, ns, st);
+    if (M <= small_tokens(F)) return launch_matvec_tokens(F, w, xq, y, M, N, ns, st);
     static int lds_ok[kLdsDevices] = {};
     const hipError_t e = allow_dynamic_lds((const void *)k_matmul_k<F>, (size_t)mk::KW<F>::LDS_BYTES, lds_ok);
     if (e != hipSuccess) return e;

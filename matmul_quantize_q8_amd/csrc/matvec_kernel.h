@@ -490,10 +490,10 @@ __device__ __forceinline__ int dma_span(const uint8_t *src, int64_t lo, int64_t 
 
 // --- a row's weight unit held for several tokens -------------------------------
 // The few-token path dots one weight unit with every token.  In general the
-// unit is re-read from LDS for each token; a paired Q4_0 or Q8_0 unit keeps
-// its codes and scales in registers (18 VGPRs), so each further token costs
-// its 16 dot products and two folds.  Same integer sums and the same fmaf
-// order as unit_dot.
+// unit is re-read from LDS for each token; a paired Q4_0 or Q8_0 unit and a
+// Q4_K quarter super-block keep their codes and scales in registers (18 to
+// 22 VGPRs), so each further token costs its 16 dot products and the folds.
+// Same integer sums and the same fmaf order as unit_dot.
 template <int F, bool PAIRED> struct UnitW {
     const uint8_t *sl;
     uint32_t bo;
@@ -565,6 +565,39 @@ template <> struct UnitW<F_Q8_0, true> {
         }
         acc = fmaf(dw[0] * x.d[0], (float)s0, acc);
         return fmaf(dw[1] * x.d[1], (float)s1, acc);
+    }
+};
+
+template <> struct UnitW<F_Q4_K, false> {
+    int c[16];        // quarter u & 3 of the super-block: low nibbles in c[0..7], high in c[8..15]
+    int sc0, m0, sc1, m1;
+    float d, dmin;
+    __device__ __forceinline__ void load(const uint8_t *sl, uint32_t bo, int u) {
+        const int j = u & 3;
+        const uint32_t *b32 = reinterpret_cast<const uint32_t *>(sl + bo);
+        const uint32_t dd = b32[0], s0 = b32[1], s1 = b32[2], s2 = b32[3];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t q = b32[4 + 8 * j + k];
+            c[k] = (int)(q & 0x0f0f0f0fu);
+            c[8 + k] = (int)((q >> 4) & 0x0f0f0f0fu);
+        }
+        q4k_scale_min(s0, s1, s2, 2 * j, sc0, m0);
+        q4k_scale_min(s0, s1, s2, 2 * j + 1, sc1, m1);
+        d = f16_bits_to_f32(dd);
+        dmin = f16_bits_to_f32(dd >> 16);
+    }
+    __device__ __forceinline__ float dot(const XU<F_Q4_K, false> &x, float acc) const {
+        int lo = 0, hi = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            lo = dot4(c[k], x.q[k], lo);
+            hi = dot4(c[8 + k], x.q[8 + k], hi);
+        }
+        const int V = sc0 * lo + sc1 * hi;
+        const int Mn = m0 * (x.bs[0] + x.bs[1]) + m1 * (x.bs[2] + x.bs[3]);
+        acc = fmaf(d * x.d, (float)V, acc);
+        return fmaf(-(dmin * x.d), (float)Mn, acc);
     }
 };
 

@@ -1,4 +1,4 @@
-// Products of a few tokens (M <= kSmallTokens) on the decode kernel: TT tokens
+// Products of a few tokens (M <= small_tokens(format)) on the decode kernel: TT tokens
 // per grid row, each wave's weight slice streamed once per TT tokens (kernel:
 // matvec_kernel.h).
 #include "matvec_kernel.h"
@@ -48,7 +48,7 @@ static hipError_t matvec_tokens(const void *w, const void *xq, float *y, int M, 
 
 hipError_t launch_matvec_tokens(int fmt, const void *w, const void *xq, float *y, int M, int N, int nb,
                                 hipStream_t st) {
-    if (M < 1 || M > kSmallTokens) return hipErrorInvalidValue;
+    if (M < 1 || M > small_tokens(fmt)) return hipErrorInvalidValue;
     if (M == 1) {   // one token: the decode launch itself
         switch (fmt) {
             case F_Q4_0: return launch_matvec_q4_0(w, xq, y, N, nb, st);

@@ -26,8 +26,11 @@ enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4, F_Q4_1 = 
 // Token counts up to this run the products on the decode kernel with several
 // tokens per weight pass; larger counts run the MFMA prefill kernels, whose
 // 128-token tiles leave most CUs idle below it (N = 12288, K = 4096: about
-// 64 us for any M <= 128).
+// 64 us for any M <= 128).  Q4_K, whose few-token units stay in registers
+// and whose MFMA kernel is slower at small M, switches at 32.
 constexpr int kSmallTokens = 16;
+constexpr int kSmallTokensQ4K = 32;
+constexpr int small_tokens(int fmt) { return fmt == F_Q4_K ? kSmallTokensQ4K : kSmallTokens; }
 hipError_t launch_matvec_tokens(int fmt, const void *w, const void *xq, float *y, int M, int N, int nb,
                                 hipStream_t st);
 template <int F> constexpr bool kIsK = F == F_Q2_K || F == F_Q4_K || F == F_Q6_K;

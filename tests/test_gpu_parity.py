@@ -318,7 +318,7 @@ MATMUL_CASES = [
 ]
 
 
-# Few tokens (M <= 16): the decode kernel with 4 or 8 tokens per weight pass;
+# Few tokens (M <= 16, Q4_K M <= 32): the decode kernel with 4 or 8 tokens per weight pass;
 # ragged token groups, odd block counts (unpaired units), rows walked in
 # segments (K = 8192 and 11008), every format.
 SMALL_M_CASES = [
@@ -328,7 +328,8 @@ SMALL_M_CASES = [
     ("q4_1", 6, 130, 4096), ("q4_1", 12, 17, 4128), ("q5_0", 6, 130, 4096), ("q5_0", 14, 9, 8192),
     ("q5_1", 6, 130, 4096), ("q5_1", 2, 31, 160),
     ("q2_k", 2, 130, 4096), ("q2_k", 11, 70, 2304), ("q2_k", 16, 33, 11008),
-    ("q4_k", 3, 130, 4096), ("q4_k", 8, 12288, 4096), ("q4_k", 10, 31, 11008),
+    ("q4_k", 3, 130, 4096), ("q4_k", 8, 12288, 4096), ("q4_k", 10, 31, 11008), ("q4_k", 32, 65, 2304),
+    ("q4_k", 25, 129, 4096), ("q4_k", 33, 33, 4096),
     ("q6_k", 5, 130, 4096), ("q6_k", 16, 65, 2304), ("q6_k", 9, 33, 11008),
 ]
 

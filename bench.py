@@ -448,6 +448,39 @@ def bench_peaks(args, torch, q, sizes=()):
     return res
 
 
+def bench_few_tokens(args, torch, q, synth):
+    """qmm_matmul_* for a few tokens (M = 2, 8, 16) at 12288 x 4096, Q4_0 and
+    Q4_K weights (the decode workloads' weights, rotated over copies like the
+    decode bench): kernel time, and the time of M decode launches beside it."""
+    N, K = DEC["N"], DEC["K"]
+    rows = []
+    for fmt, cfg in (("q4_0", 1), ("q4_k", 5)):
+        w = torch.from_numpy(synth.weights(N, K, config=cfg)).cuda()
+        wbytes = N * q.row_bytes(fmt, K)
+        wq0 = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
+        q.QUANTIZE_W[fmt](w, wq0, N, K)
+        del w
+        copies = max(2, int(args.copies_mb * 1e6 // wbytes) + 1)
+        wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+        for M in (2, 8, 16):
+            x = torch.from_numpy(synth.activations(M, K, config=cfg)).cuda()
+            xq = torch.empty(M * q.row_bytes(q.ACT_FORMAT[fmt], K), dtype=torch.uint8, device="cuda")
+            q.QUANTIZE_X[fmt](x, xq, M, K)
+            y = torch.empty(M * N, dtype=torch.float32, device="cuda")
+            ms, ms_min, _ = time_batches(torch, lambda i: q.MATMUL[fmt](wqs[i % copies], xq, y, M, N, K),
+                                         args.steps, copies)
+            mv, _, _ = time_batches(torch, lambda i: q.MATVEC[fmt](wqs[i % copies], xq, y, N, K),
+                                    args.steps, copies)
+            log(f"few tokens {fmt} M={M}: {ms * 1e3:.2f} us ({M} decode launches {M * mv * 1e3:.2f} us)")
+            rows.append({"format": fmt, "M": M, "N": N, "K": K, "kernel_us_mean": round(ms * 1e3, 3),
+                         "kernel_us_best_batch": round(ms_min * 1e3, 3),
+                         "tops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 3),
+                         "m_decode_launches_us": round(M * mv * 1e3, 3)})
+        del wqs, wq0
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_threads():
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     return max(1, min(n, 16))
@@ -549,6 +582,7 @@ def main():
     dec = bench_decode(args, torch, q, synth) if args.only in ("all", "decode") else None
     pre = bench_prefill(args, torch, q, synth) if args.only in ("all", "prefill") else None
     cfgs = bench_matvec_configs(args, torch, q, synth) if args.only in ("all", "configs") else None
+    few = bench_few_tokens(args, torch, q, synth) if args.only in ("all", "configs") else None
 
     cpu_dec = cpu_pre = None
     if not args.no_cpu_baseline:
@@ -596,6 +630,8 @@ def main():
                 r["attainable_read_us"] = att
                 r["frac_of_attainable"] = round(att / r["kernel_us_mean"], 4)
         out["matvec_configs"] = cfgs
+    if few is not None:
+        out["few_tokens"] = few
     out["attainable"] = peaks
     print(json.dumps(out), flush=True)
 

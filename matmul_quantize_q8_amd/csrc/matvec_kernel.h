@@ -491,8 +491,9 @@ __device__ __forceinline__ int dma_span(const uint8_t *src, int64_t lo, int64_t 
 // --- a row's weight unit held for several tokens -------------------------------
 // The few-token path dots one weight unit with every token.  In general the
 // unit is re-read from LDS for each token; a paired Q4_0 or Q8_0 unit and a
-// Q4_K quarter super-block keep their codes and scales in registers (18 to
-// 22 VGPRs), so each further token costs its 16 dot products and the folds.
+// Q4_K or Q6_K quarter super-block keep their codes and scales in registers
+// (18 to 22 VGPRs), so each further token costs its 16 dot products and the
+// folds.
 // Same integer sums and the same fmaf order as unit_dot.
 template <int F, bool PAIRED> struct UnitW {
     const uint8_t *sl;
@@ -598,6 +599,43 @@ template <> struct UnitW<F_Q4_K, false> {
         const int Mn = m0 * (x.bs[0] + x.bs[1]) + m1 * (x.bs[2] + x.bs[3]);
         acc = fmaf(d * x.d, (float)V, acc);
         return fmaf(-(dmin * x.d), (float)Mn, acc);
+    }
+};
+
+template <> struct UnitW<F_Q6_K, false> {
+    int c[16];        // group k's 16 six-bit codes in c[4k .. 4k + 3]
+    int sc[4];
+    float d;
+    __device__ __forceinline__ void load(const uint8_t *sl, uint32_t bo, int u) {
+        const int p = u & 3, h = p >> 1, g2 = p & 1;
+        uint32_t ra[4], rb[4], qh[4], sw[2];
+        lds_dwords<4>(sl, bo + 64 * h + 16 * g2, ra);
+        lds_dwords<4>(sl, bo + 64 * h + 32 + 16 * g2, rb);
+        lds_dwords<4>(sl, bo + 128 + 32 * h + 16 * g2, qh);
+        lds_dwords<2>(sl, bo + 192 + 8 * h, sw);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t src = (k & 1) ? rb[e] : ra[e];
+                const uint32_t lo4 = (k < 2) ? (src & 0x0f0f0f0fu) : ((src >> 4) & 0x0f0f0f0fu);
+                const uint32_t hi2 = ((qh[e] >> (2 * k)) & 0x03030303u) << 4;
+                c[4 * k + e] = (int)(lo4 | hi2);
+            }
+            sc[k] = __builtin_amdgcn_sbfe((int)sw[k >> 1], 8 * (2 * (k & 1) + g2), 8);
+        }
+        d = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sl + bo + 208));
+    }
+    __device__ __forceinline__ float dot(const XU<F_Q6_K, false> &x, float acc) const {
+        int V = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int s = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s = dot4(c[4 * k + e], x.q[4 * k + e], s);
+            V += sc[k] * (s - 32 * x.bs[k]);
+        }
+        return fmaf(d * x.d, (float)V, acc);
     }
 };
 

@@ -491,9 +491,9 @@ __device__ __forceinline__ int dma_span(const uint8_t *src, int64_t lo, int64_t 
 // --- a row's weight unit held for several tokens -------------------------------
 // The few-token path dots one weight unit with every token.  In general the
 // unit is re-read from LDS for each token; a paired Q4_0 or Q8_0 unit and a
-// Q4_K or Q6_K quarter super-block keep their codes and scales in registers
-// (18 to 22 VGPRs), so each further token costs its 16 dot products and the
-// folds.
+// Q2_K, Q4_K or Q6_K quarter super-block keep their codes and scales in
+// registers (18 to 26 VGPRs), so each further token costs its 16 dot
+// products and the folds.
 // Same integer sums and the same fmaf order as unit_dot.
 template <int F, bool PAIRED> struct UnitW {
     const uint8_t *sl;
@@ -636,6 +636,51 @@ template <> struct UnitW<F_Q6_K, false> {
             V += sc[k] * (s - 32 * x.bs[k]);
         }
         return fmaf(d * x.d, (float)V, acc);
+    }
+};
+
+template <> struct UnitW<F_Q2_K, false> {
+    int c[16];        // the in-place bit pairs of unit_dot: group s in c[4s .. 4s + 3]
+    int sc16[4], m[4];
+    float d, dmin;
+    __device__ __forceinline__ void load(const uint8_t *sl, uint32_t bo, int u) {
+        const int p = u & 3, h = p >> 1, odd = p & 1;
+        const uint32_t *b32 = reinterpret_cast<const uint32_t *>(sl + bo);
+        const uint32_t sc01 = b32[2 * h], sc23 = b32[2 * h + 1], dd = b32[20];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t q = b32[4 + 4 * p + k];
+            c[k] = (int)(q & 0x03030303u);
+            c[4 + k] = (int)(q & 0x0c0c0c0cu);
+            c[8 + k] = (int)(q & 0x30303030u);
+            c[12 + k] = (int)((q >> 2) & 0x30303030u);
+        }
+        const uint32_t o0 = 8u * (uint32_t)odd, o1 = o0 + 16u;
+        // 16 V = 16 sc0 G0 + 4 sc1 G1 + sc2 G2 + sc3 G3 (see unit_dot)
+        sc16[0] = 16 * (int)__builtin_amdgcn_ubfe(sc01, o0, 4);
+        sc16[1] = 4 * (int)__builtin_amdgcn_ubfe(sc01, o1, 4);
+        sc16[2] = (int)__builtin_amdgcn_ubfe(sc23, o0, 4);
+        sc16[3] = (int)__builtin_amdgcn_ubfe(sc23, o1, 4);
+        m[0] = (int)__builtin_amdgcn_ubfe(sc01, o0 + 4u, 4);
+        m[1] = (int)__builtin_amdgcn_ubfe(sc01, o1 + 4u, 4);
+        m[2] = (int)__builtin_amdgcn_ubfe(sc23, o0 + 4u, 4);
+        m[3] = (int)__builtin_amdgcn_ubfe(sc23, o1 + 4u, 4);
+        d = f16_bits_to_f32(dd);
+        dmin = f16_bits_to_f32(dd >> 16);
+    }
+    __device__ __forceinline__ float dot(const XU<F_Q2_K, false> &x, float acc) const {
+        int G0 = 0, G1 = 0, G2 = 0, G3 = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            G0 = dot4(c[k], x.q[k], G0);
+            G1 = dot4(c[4 + k], x.q[4 + k], G1);
+            G2 = dot4(c[8 + k], x.q[8 + k], G2);
+            G3 = dot4(c[12 + k], x.q[12 + k], G3);
+        }
+        const int V16 = sc16[0] * G0 + sc16[1] * G1 + sc16[2] * G2 + sc16[3] * G3;
+        const int Mn = m[0] * x.bs[0] + m[1] * x.bs[1] + m[2] * x.bs[2] + m[3] * x.bs[3];
+        acc = fmaf(d * x.d * 0.0625f, (float)V16, acc);
+        return fmaf(-(dmin * x.d), (float)Mn, acc);
     }
 };
 

@@ -383,10 +383,7 @@ __device__ __forceinline__ int block32_isum(const uint32_t (&qs)[4], uint32_t qh
 // t = dw dx I (+ m dx S for the _1 formats); S = sum of the block's
 // activation codes = sx8 / 8; Q5_0's codes carry +16: I = sum q x - 16 S.
 template <int F>
-__device__ __forceinline__ float block32_term(uint32_t dm, const uint32_t (&qs)[4], uint32_t qh, const int *x,
-                                              float dx, int sx8, float acc) {
-    constexpr bool Q5 = F != F_Q4_1;
-    int I = block32_isum<Q5>(qs, qh, x);
+__device__ __forceinline__ float block32_fold(int I, uint32_t dm, float dx, int sx8, float acc) {
     const float dw = f16_bits_to_f32(dm);
     if constexpr (F == F_Q5_0) {
         I -= 2 * sx8;
@@ -395,6 +392,13 @@ __device__ __forceinline__ float block32_term(uint32_t dm, const uint32_t (&qs)[
         acc = fmaf(dw * dx, (float)I, acc);
         return fmaf(f16_bits_to_f32(dm >> 16) * dx, (float)(sx8 >> 3), acc);
     }
+}
+
+template <int F>
+__device__ __forceinline__ float block32_term(uint32_t dm, const uint32_t (&qs)[4], uint32_t qh, const int *x,
+                                              float dx, int sx8, float acc) {
+    constexpr bool Q5 = F != F_Q4_1;
+    return block32_fold<F>(block32_isum<Q5>(qs, qh, x), dm, dx, sx8, acc);
 }
 
 // Fields of the block at a 2-byte aligned LDS offset o: d (and m) dword, qh, qs.
@@ -490,10 +494,10 @@ __device__ __forceinline__ int dma_span(const uint8_t *src, int64_t lo, int64_t 
 
 // --- a row's weight unit held for several tokens -------------------------------
 // The few-token path dots one weight unit with every token.  In general the
-// unit is re-read from LDS for each token; a paired Q4_0 or Q8_0 unit and a
-// Q2_K, Q4_K or Q6_K quarter super-block keep their codes and scales in
-// registers (18 to 26 VGPRs), so each further token costs its 16 dot
-// products and the folds.
+// unit is re-read from LDS for each token (unpaired Q4_0 and Q8_0 units);
+// the other units keep their codes (expanded to bytes) and scales in
+// registers (up to 26 VGPRs), so each further token costs its dot products
+// and the folds.
 // Same integer sums and the same fmaf order as unit_dot.
 template <int F, bool PAIRED> struct UnitW {
     const uint8_t *sl;
@@ -683,6 +687,50 @@ template <> struct UnitW<F_Q2_K, false> {
         return fmaf(-(dmin * x.d), (float)Mn, acc);
     }
 };
+
+// The 32-value formats with an offset or a fifth bit: the unit's blocks with
+// their codes expanded to bytes (fifth bits included) and the d (m) dword.
+template <int F, bool PAIRED> struct UnitW32 {
+    static constexpr int P = Unit<F, PAIRED>::BPU;
+    uint32_t c[P][8];   // block j: codes of values 4k.. in c[j][k], of 16 + 4k.. in c[j][4 + k]
+    uint32_t dm[P];
+    __device__ __forceinline__ void load(const uint8_t *sl, uint32_t bo, int) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            uint32_t qh, qs[4];
+            block32_fields<F>(sl, bo + (uint32_t)j * FmtBytes<F>::BB, dm[j], qh, qs);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t lo = qs[k] & 0x0f0f0f0fu, hi = (qs[k] >> 4) & 0x0f0f0f0fu;
+                if constexpr (F != F_Q4_1) {
+                    lo |= bits_to_bytes(__builtin_amdgcn_ubfe(qh, 4 * k, 4)) << 4;
+                    hi |= bits_to_bytes(__builtin_amdgcn_ubfe(qh, 16 + 4 * k, 4)) << 4;
+                }
+                c[j][k] = lo;
+                c[j][4 + k] = hi;
+            }
+        }
+    }
+    __device__ __forceinline__ float dot(const XU<F, PAIRED> &x, float acc) const {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            int I = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                I = dot4((int)c[j][k], x.q[8 * j + k], I);
+                I = dot4((int)c[j][4 + k], x.q[8 * j + k + 4], I);
+            }
+            acc = block32_fold<F>(I, dm[j], x.d[j], x.sx8[j], acc);
+        }
+        return acc;
+    }
+};
+template <> struct UnitW<F_Q4_1, true> : UnitW32<F_Q4_1, true> {};
+template <> struct UnitW<F_Q4_1, false> : UnitW32<F_Q4_1, false> {};
+template <> struct UnitW<F_Q5_0, true> : UnitW32<F_Q5_0, true> {};
+template <> struct UnitW<F_Q5_0, false> : UnitW32<F_Q5_0, false> {};
+template <> struct UnitW<F_Q5_1, true> : UnitW32<F_Q5_1, true> {};
+template <> struct UnitW<F_Q5_1, false> : UnitW32<F_Q5_1, false> {};
 
 // --- row-sum reduction across the wave -----------------------------------------
 __device__ __forceinline__ uint32_t f_as_u(float f) { return __builtin_bit_cast(uint32_t, f); }

@@ -33,6 +33,7 @@ static hipError_t pick_mv_tokens(const void *w, const void *xq, float *y, int M,
 
 template <int F, bool PAIRED>
 static hipError_t mv_tokens(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
+    if (M <= 2) return pick_mv_tokens<F, PAIRED, 2>(w, xq, y, M, N, nb, st);
     if (M <= 4) return pick_mv_tokens<F, PAIRED, 4>(w, xq, y, M, N, nb, st);
     return pick_mv_tokens<F, PAIRED, 8>(w, xq, y, M, N, nb, st);
 }

@@ -203,8 +203,8 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
  *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.
  *   y  : f32 [M][N], written.
  * Up to 16 tokens (32 for Q4_K) run on the decode matvec kernel, which
- * streams each weight slice once per group of 2, 4 or 8 tokens (one token: the
- * decode launch itself); more tokens run on the MFMA kernels below, whose 128-token tiles
+ * streams each weight slice once per group of 2, 4 or 8 tokens (one token:
+ * the decode launch itself); more tokens run on the MFMA kernels below, whose 128-token tiles
  * would leave most CUs idle for a few tokens.  Results agree within the
  * same tolerance either way (they are not bitwise identical: the two paths
  * sum the blocks in different orders).

@@ -61,7 +61,10 @@ def parse():
     ap.add_argument("--copies-mb", type=float, default=600.0, help="total size of the rotated weight copies")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one plain 256 MiB device-to-device copy (scales HBM byte counters)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps < 1 or args.prefill_steps < 1:
+        ap.error("--steps and --prefill-steps must be at least 1")
+    return args
 
 
 def committed_traffic(kernel, workload):
@@ -142,16 +145,25 @@ def bench_decode(args, torch, q, synth):
         q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K)
 
     def replayed(fn):
-        """ms per step of `fn` replayed from a captured HIP graph (one step per
-        weight copy); a decode loop driven eagerly from Python is launch-bound."""
+        """ms per step of exactly args.steps steps of `fn`, replayed from captured
+        HIP graphs (one of a step per weight copy, one of the remaining
+        args.steps mod copies steps); a decode loop driven eagerly from Python is
+        launch-bound."""
         for i in range(args.warmup):
             fn(i)
         torch.cuda.synchronize()
+        reps, rem = divmod(args.steps, copies)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(copies):
                 fn(i)
-        reps = max(1, args.steps // copies)
+        tail = None
+        if rem:
+            tail = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(tail):
+                for i in range(rem):
+                    fn(i)
+            tail.replay()
         graph.replay()
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
@@ -159,9 +171,11 @@ def bench_decode(args, torch, q, synth):
         t0.record()
         for _ in range(reps):
             graph.replay()
+        if tail is not None:
+            tail.replay()
         t1.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / (reps * copies), reps * copies
+        return t0.elapsed_time(t1) / args.steps, args.steps
 
     ms_step, nsteps = replayed(step)
     ms_two, _ = replayed(step_two_launches)

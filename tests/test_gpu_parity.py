@@ -654,6 +654,60 @@ def test_device_errors_are_reported(env):
     assert e.value.code == "QMM_E_SHAPE"
 
 
+def test_concurrent_calls_from_host_threads(env):
+    """Calls are thread-safe: four host threads, each on a stream of its own,
+    quantize, run a decode matvec and a prefill matmul at the same time, five
+    times over; every output equals the same calls made alone on one stream,
+    bit for bit (the kernels are deterministic and keep no state)."""
+    import threading
+    torch, q, orc = env
+    N, K, M, reps = 1024, 4096, 40, 5
+    _say("threads", N, K, M)
+    w = synth.weights(N, K, config=1)
+    xd = _dev(torch, synth.activations(M, K, config=4))
+    fmts = ("q4_0", "q8_0", "q2_k", "q4_k")
+    wq = {f: _dev(torch, orc.quantize_w(f, w)) for f in fmts}
+
+    def job(f):
+        act = "q8_k" if f in ("q2_k", "q4_k") else "q8_0"
+        rb = q.row_bytes(act, K)
+        xq = torch.empty(M * rb, dtype=torch.uint8, device="cuda")
+        yv = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        ym = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        (q.qmm_quantize_q8_k if act == "q8_k" else q.qmm_quantize_q8_0)(xd, xq, M, K)
+        q.MATVEC[f](wq[f], xq[:rb], yv, N, K)
+        q.MATMUL[f](wq[f], xq, ym, M, N, K)
+        return xq, yv, ym
+
+    ref = {f: job(f) for f in fmts}
+    torch.cuda.synchronize()
+    got, errors = {}, []
+    start = threading.Barrier(len(fmts))
+
+    def worker(f):
+        try:
+            s = torch.cuda.Stream()
+            start.wait()
+            with torch.cuda.stream(s):
+                got[f] = [job(f) for _ in range(reps)]
+            s.synchronize()
+        except Exception as e:          # reported by the main thread
+            errors.append((f, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(f,)) for f in fmts]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for f in fmts:
+        for rep, outs in enumerate(got[f]):
+            for name, a, b in zip(("xq", "matvec", "matmul"), outs, ref[f]):
+                assert torch.equal(a, b), (f, rep, name)
+
+
 def test_graph_replay_matches_eager(env):
     """Decode and prefill launches captured into a HIP graph: every replay, with
     eager work and synchronizations in between, equals the eager result bit for

@@ -463,7 +463,7 @@ def bench_peaks(args, torch, q, sizes=()):
 
 
 def bench_few_tokens(args, torch, q, synth):
-    """qmm_matmul_* for a few tokens (M = 2, 8, 16) at 12288 x 4096, Q4_0 and
+    """qmm_matmul_* for a few tokens (M = 2 ... 128) at 12288 x 4096, Q4_0 and
     Q4_K weights (the decode workloads' weights, rotated over copies like the
     decode bench): kernel time, and the time of M decode launches beside it."""
     N, K = DEC["N"], DEC["K"]
@@ -476,7 +476,7 @@ def bench_few_tokens(args, torch, q, synth):
         del w
         copies = max(2, int(args.copies_mb * 1e6 // wbytes) + 1)
         wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
-        for M in (2, 8, 16):
+        for M in (2, 8, 16, 32, 64, 128):
             x = torch.from_numpy(synth.activations(M, K, config=cfg)).cuda()
             xq = torch.empty(M * q.row_bytes(q.ACT_FORMAT[fmt], K), dtype=torch.uint8, device="cuda")
             q.QUANTIZE_X[fmt](x, xq, M, K)

@@ -208,6 +208,11 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
  * would leave most CUs idle for a few tokens.  Results agree within the
  * same tolerance either way (they are not bitwise identical: the two paths
  * sum the blocks in different orders).
+ * An MFMA launch of at most 256 output tiles (128 tokens x 128 or 256 weight
+ * rows) splits K in two: y is first zeroed on the stream, then the two
+ * halves of each output are added into it with f32 atomic adds (device
+ * memory from hipMalloc; two addends give the same bits in either order, so
+ * repeated calls are bitwise reproducible).
  * The 32-value formats (Q4_0, Q8_0, Q4_1, Q5_0, Q5_1) run on int8 MFMA (4-bit
  * codes enter as 16 * (q - 8), 5-bit codes as 8 * (q - 16); the offset term
  * of Q4_1 / Q5_1, m * dx * sum x per block, runs on an f32 MFMA) and also

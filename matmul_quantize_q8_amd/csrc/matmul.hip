@@ -132,7 +132,7 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
 // Workgroup barrier that orders LDS accesses but does not wait for
 // outstanding vector-memory loads (the LDS-DMA copies in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-template <int WFMT>
+template <int WFMT, bool SPLIT>
 __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restrict__ w,
                                             const uint8_t *__restrict__ xq, float *__restrict__ y, int M, int N,
                                             int nb, int tiles_m) {
@@ -142,10 +142,18 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     constexpr int WC = F::WC, WQ = F::WQ, STAGE = F::STAGE, PER_WAVE = F::PER_WAVE, DXF = F::DXF;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = uniform(t >> 6);
-    const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
+    // SPLIT: the grid holds every tile twice; part 0 takes the first kb1
+    // blocks of each row (whole stages), part 1 the rest, and both add into
+    // the zeroed output.
+    constexpr int ksplit = SPLIT ? 2 : 1;
+    const int tiles = (int)gridDim.x / ksplit;
+    const int tile = (int)blockIdx.x % tiles, part = (int)blockIdx.x / tiles;
+    const int mt = tile % tiles_m, nt = tile / tiles_m;
     const int m0 = mt * BM, n0 = nt * BN;
     const uint32_t xrow = (uint32_t)nb * kQ80Bytes, wrow = (uint32_t)nb * F::WB;
-    const int nst = (nb + 1) >> 1;   // an odd block count leaves a last stage of one block
+    const int kb1 = SPLIT ? 2 * ((nb + 2) / 4) : nb;
+    const int kb0 = part ? kb1 : 0, nbp = part ? nb - kb1 : kb1;   // this part's first block and count
+    const int nst = (nbp + 1) >> 1;   // an odd block count leaves a last stage of one block
 
     // DMA: wave load q = w + 4k (k < 4) of a stage is chunk load q of the
     // stage image (activation chunks for q < 10, weight chunks after) and
@@ -174,8 +182,9 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     // the low half of a generic LDS address is the LDS offset
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
     const uint32_t m0w = (uint32_t)uniform((int)(lds0 + 1024u * wave));
-    // stage s starts at segment 2s, or 2s-1 for the last stage of an odd count
-    auto seg = [&](int s) { return 2 * s - (2 * s + 1 == nb ? 1 : 0); };
+    // stage s starts at block kb0 + 2s, or one block earlier for the last
+    // stage of an odd count (kb0 >= 2 whenever part 1 has an odd count)
+    auto seg = [&](int s) { return kb0 + 2 * s - (2 * s + 1 == nbp ? 1 : 0); };
     auto dma_load = [&](auto kc, int s, int b) {
         constexpr int k = decltype(kc)::value;
         const int sx = seg(s) * kQ80Bytes, sw = seg(s) * F::WB;
@@ -547,7 +556,7 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
         else
             asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         lds_barrier();
-        compute(lds + b * STAGE, 2 * s + 1 == nb, min(s + 2, nst - 1), (b + 2) % NBUF);
+        compute(lds + b * STAGE, 2 * s + 1 == nbp, min(s + 2, nst - 1), (b + 2) % NBUF);
     };
     dma(0, 0);
     dma(min(1, nst - 1), 1);
@@ -569,7 +578,12 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (m < M) y[(int64_t)m * N + n] = acc[i][j][r] * F::OUT_SCALE;
+                if (m >= M) continue;
+                // two addends on a zeroed output: the same sum in either order
+                if constexpr (SPLIT)
+                    atomicAdd(y + (int64_t)m * N + n, acc[i][j][r] * F::OUT_SCALE);
+                else
+                    y[(int64_t)m * N + n] = acc[i][j][r] * F::OUT_SCALE;
             }
         }
 }
@@ -578,35 +592,70 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0(const uint8_t *__rest
                                                           const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                           int M, int N, int nb, int tiles_m) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q4_0>::LDS_BYTES];
-    matmul_body<F_Q4_0>(lds, w, xq, y, M, N, nb, tiles_m);
+    matmul_body<F_Q4_0, false>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_0_split(const uint8_t *__restrict__ w,
+                                                                const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                                int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q4_0>::LDS_BYTES];
+    matmul_body<F_Q4_0, true>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q8_0(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                           int M, int N, int nb, int tiles_m) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q8_0>::LDS_BYTES];
-    matmul_body<F_Q8_0>(lds, w, xq, y, M, N, nb, tiles_m);
+    matmul_body<F_Q8_0, false>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q8_0_split(const uint8_t *__restrict__ w,
+                                                                const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                                int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q8_0>::LDS_BYTES];
+    matmul_body<F_Q8_0, true>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_0(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                           int M, int N, int nb, int tiles_m) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q5_0>::LDS_BYTES];
-    matmul_body<F_Q5_0>(lds, w, xq, y, M, N, nb, tiles_m);
+    matmul_body<F_Q5_0, false>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_0_split(const uint8_t *__restrict__ w,
+                                                                const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                                int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q5_0>::LDS_BYTES];
+    matmul_body<F_Q5_0, true>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_1(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                           int M, int N, int nb, int tiles_m) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q4_1>::LDS_BYTES];
-    matmul_body<F_Q4_1>(lds, w, xq, y, M, N, nb, tiles_m);
+    matmul_body<F_Q4_1, false>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q4_1_split(const uint8_t *__restrict__ w,
+                                                                const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                                int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q4_1>::LDS_BYTES];
+    matmul_body<F_Q4_1, true>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_1(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                           int M, int N, int nb, int tiles_m) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q5_1>::LDS_BYTES];
-    matmul_body<F_Q5_1>(lds, w, xq, y, M, N, nb, tiles_m);
+    matmul_body<F_Q5_1, false>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_1_split(const uint8_t *__restrict__ w,
+                                                                const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                                int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q5_1>::LDS_BYTES];
+    matmul_body<F_Q5_1, true>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 // K = 32: one block per row, too short for the two-block stages above (the
@@ -684,6 +733,23 @@ constexpr int64_t kMatmulMaxBlocks = (((int64_t)1 << 31) - 1) / (mm::BM * kQ80By
 
 int64_t matmul_q4_0_max_blocks() { return kMatmulMaxBlocks; }
 
+__global__ __launch_bounds__(256) void k_zero_f32(float *__restrict__ y, int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i + 4 <= n) {
+        *reinterpret_cast<float4 *>(y + i) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else {
+        for (int64_t k = i; k < n; ++k) y[k] = 0.0f;
+    }
+}
+
+hipError_t launch_zero_f32(float *y, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t grid = (n + 1023) / 1024;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)grid), dim3(256), 0, st, y, n);
+    return hipGetLastError();
+}
+
 template <int WFMT>
 static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
     const uint8_t *wp = static_cast<const uint8_t *>(w);
@@ -702,13 +768,23 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
     }
     int tiles_m = (M + mm::BM - 1) / mm::BM;
     const int64_t tiles = (int64_t)tiles_m * ((N + mm::BN - 1) / mm::BN);
+    // A launch of at most one workgroup per CU leaves the CUs half idle and
+    // each workgroup alone on its CU: split K in two, the parts adding into
+    // an output zeroed first.
+    const bool split = tiles <= kSplitTiles && nb >= 4;
+    if (split) {
+        const hipError_t e = launch_zero_f32(y, (int64_t)M * N, st);
+        if (e != hipSuccess) return e;
+    }
+    const int ksplit = split ? 2 : 1;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
-    const void *kern = WFMT == F_Q8_0   ? (const void *)k_matmul_q8_0
-                       : WFMT == F_Q5_0 ? (const void *)k_matmul_q5_0
-                       : WFMT == F_Q4_1 ? (const void *)k_matmul_q4_1
-                       : WFMT == F_Q5_1 ? (const void *)k_matmul_q5_1
+    const void *kern = WFMT == F_Q8_0   ? (split ? (const void *)k_matmul_q8_0_split : (const void *)k_matmul_q8_0)
+                       : WFMT == F_Q5_0 ? (split ? (const void *)k_matmul_q5_0_split : (const void *)k_matmul_q5_0)
+                       : WFMT == F_Q4_1 ? (split ? (const void *)k_matmul_q4_1_split : (const void *)k_matmul_q4_1)
+                       : WFMT == F_Q5_1 ? (split ? (const void *)k_matmul_q5_1_split : (const void *)k_matmul_q5_1)
+                       : split          ? (const void *)k_matmul_q4_0_split
                                         : (const void *)k_matmul_q4_0;
-    return hipLaunchKernel(kern, dim3((unsigned)tiles), dim3(mm::NT), args, 0, st);
+    return hipLaunchKernel(kern, dim3((unsigned)(tiles * ksplit)), dim3(mm::NT), args, 0, st);
 }
 
 hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {

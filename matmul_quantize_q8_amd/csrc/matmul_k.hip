@@ -132,9 +132,9 @@ __device__ __forceinline__ void q4k_sc_m(uint32_t s0, uint32_t s1, uint32_t s2, 
     }
 }
 
-template <int F>
-__global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
-                                                     float *__restrict__ y, int M, int N, int ns, int tiles_m) {
+template <int F, bool SPLIT>
+__device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+                                              float *__restrict__ y, int M, int N, int ns, int tiles_m) {
     using namespace mk;
     using W = KW<F>;
     constexpr int WC = W::WC, WQ = W::WQ, NQ = W::NQ, PER_WAVE = W::PER_WAVE, WROW = W::WROW, STAGE = W::STAGE,
@@ -143,8 +143,16 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = uniform(t >> 6);
-    const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
+    // SPLIT: the grid holds every tile twice; part 0 takes the first half
+    // of each row's super-blocks, part 1 the rest, and both add into the
+    // zeroed output.
+    constexpr int ksplit = SPLIT ? 2 : 1;
+    const int tiles = (int)gridDim.x / ksplit;
+    const int tile = (int)blockIdx.x % tiles, part = (int)blockIdx.x / tiles;
+    const int mt = tile % tiles_m, nt = tile / tiles_m;
     const int m0 = mt * BM, n0 = nt * BN;
+    const int sh = SPLIT ? (ns + 1) / 2 : ns;
+    const int s0 = part ? sh : 0, s1 = part ? ns : sh;   // this part's super-blocks [s0, s1)
     const uint32_t xrow = (uint32_t)ns * kQ8KBytes, wrow = (uint32_t)ns * W::WB;
 
     // DMA: wave load q = wave + 8k (k < PER_WAVE) of a stage is chunk load q
@@ -494,15 +502,14 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
         }
     };
 
-    // Stage s lives in buffer s % 2.  At step s: wait for this wave's loads
-    // of stage s, the barrier publishes every wave's (and tells that stage
-    // s-1's buffer is free), the DMA of stage s+1 goes into it, then stage s
-    // is computed.
-    dma(0, 0);
-    for (int s = 0; s < ns; ++s) {
+    // Super-block s lives in buffer (s - s0) % 2.  At step s: wait for this
+    // wave's loads of s, the barrier publishes every wave's (and tells that
+    // s-1's buffer is free), the DMA of s+1 goes into it, then s is computed.
+    dma(s0, 0);
+    for (int s = s0; s < s1; ++s) {
         asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (s + 1 < ns) dma(s + 1, (s + 1) & 1);
-        compute(lds + (s & 1) * STAGE);
+        if (s + 1 < s1) dma(s + 1, (s + 1 - s0) & 1);
+        compute(lds + ((s - s0) & 1) * STAGE);
     }
     // no LDS-DMA write may still be in flight when the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -514,9 +521,27 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + 32 * TI * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (m < M) y[(int64_t)m * N + n] = acc[i][r];
+                if (m >= M) continue;
+                // two addends on a zeroed output: the same sum in either order
+                if constexpr (SPLIT)
+                    atomicAdd(y + (int64_t)m * N + n, acc[i][r]);
+                else
+                    y[(int64_t)m * N + n] = acc[i][r];
             }
     }
+}
+
+template <int F>
+__global__ __launch_bounds__(mk::NT) void k_matmul_k(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+                                                     float *__restrict__ y, int M, int N, int ns, int tiles_m) {
+    matmul_k_body<F, false>(w, xq, y, M, N, ns, tiles_m);
+}
+
+template <int F>
+__global__ __launch_bounds__(mk::NT) void k_matmul_k_split(const uint8_t *__restrict__ w,
+                                                           const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                           int M, int N, int ns, int tiles_m) {
+    matmul_k_body<F, true>(w, xq, y, M, N, ns, tiles_m);
 }
 
 // Largest super-block count whose tile offsets fit the 32-bit buffer offsets
@@ -529,16 +554,23 @@ template <int F>
 static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {
     if (ns > kMatmulKMaxBlocks) return hipErrorInvalidValue;
     if (M <= small_tokens(F)) return launch_matvec_tokens(F, w, xq, y, M, N, ns, st);
-    static int lds_ok[kLdsDevices] = {};
-    const hipError_t e = allow_dynamic_lds((const void *)k_matmul_k<F>, (size_t)mk::KW<F>::LDS_BYTES, lds_ok);
-    if (e != hipSuccess) return e;
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
     int tiles_m = (M + mk::BM - 1) / mk::BM;
     const int64_t tiles = (int64_t)tiles_m * ((N + mk::KW<F>::BN - 1) / mk::KW<F>::BN);
+    const bool split = tiles <= kSplitTiles && ns >= 2;
+    const void *kern = split ? (const void *)k_matmul_k_split<F> : (const void *)k_matmul_k<F>;
+    static int lds_ok[kLdsDevices] = {}, lds_ok_split[kLdsDevices] = {};
+    const hipError_t e = allow_dynamic_lds(kern, (size_t)mk::KW<F>::LDS_BYTES, split ? lds_ok_split : lds_ok);
+    if (e != hipSuccess) return e;
+    if (split) {
+        const hipError_t ez = launch_zero_f32(y, (int64_t)M * N, st);
+        if (ez != hipSuccess) return ez;
+    }
+    const int ksplit = split ? 2 : 1;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&ns, (void *)&tiles_m};
-    return hipLaunchKernel((const void *)k_matmul_k<F>, dim3((unsigned)tiles), dim3(mk::NT), args,
-                           (size_t)mk::KW<F>::LDS_BYTES, st);
+    return hipLaunchKernel(kern, dim3((unsigned)(tiles * ksplit)), dim3(mk::NT), args, (size_t)mk::KW<F>::LDS_BYTES,
+                           st);
 }
 
 hipError_t launch_matmul_q2_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {

@@ -111,6 +111,12 @@ inline hipError_t allow_dynamic_lds(const void *kernel, size_t bytes, int (&done
     return e;
 }
 
+// Prefill launches of at most this many output tiles (one workgroup per CU
+// or fewer) split K in two, the parts adding into an output zeroed first.
+constexpr int64_t kSplitTiles = 256;
+// Zero n floats at y (16-byte aligned) on stream st.
+hipError_t launch_zero_f32(float *y, int64_t n, hipStream_t st);
+
 // Wave-uniform helpers.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

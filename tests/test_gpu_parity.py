@@ -315,6 +315,11 @@ MATMUL_CASES = [
     ("q5_0", 129, 257, 64), ("q5_0", 128, 128, 4096),
     # long rows: 1025 blocks (an odd count), 128 super-blocks
     ("q4_0", 129, 65, 32800), ("q5_1", 65, 33, 32800), ("q2_k", 65, 129, 32768), ("q6_k", 33, 65, 32768),
+    # more than 256 output tiles of 128 x 128: K in one part (the cases above
+    # with 4 blocks or more have at most 256 tiles and split K in two)
+    ("q4_0", 129, 16640, 160), ("q8_0", 130, 16512, 128), ("q5_0", 257, 8320, 224),
+    # exactly 256 tiles: the largest split launch
+    ("q5_1", 100, 32768, 128),
 ]
 
 
@@ -605,6 +610,30 @@ def test_outputs_are_overwritten_not_accumulated(env):
     q.qmm_matvec_q4_0(wd, xd, y, N, K)
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy(), y1)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q5_1", "q2_k", "q4_k", "q6_k"])
+def test_split_k_matmul_overwrites_and_is_deterministic(env, fmt):
+    """A prefill launch of few tiles splits K in two and adds the halves into
+    a zeroed output: calling it twice on a garbage-filled output gives the
+    same bits each time (two addends sum the same in either order)."""
+    torch, q, orc = env
+    M, N, K = 40, 1000, 4096
+    _say("split-k repeat", fmt, M, N, K)
+    wq, xq = _inputs(fmt, M, N, K, 8100)
+    wd, xd = _dev(torch, wq), _dev(torch, xq)
+    y = torch.full((M, N), 1e30, dtype=torch.float32, device="cuda")
+    q.MATMUL[fmt](wd, xd, y, M, N, K)
+    torch.cuda.synchronize()
+    first = y.clone()
+    for _ in range(3):
+        y.fill_(float("nan"))
+        q.MATMUL[fmt](wd, xd, y, M, N, K)
+        q.MATMUL[fmt](wd, xd, y, M, N, K)
+        torch.cuda.synchronize()
+        assert torch.equal(y, first)
+    ref = orc.matmul(fmt, wq, xq, M, N, K, threads=8, want=("y64", "mag"))
+    _check(first.cpu().numpy(), ref["y64"], ref["mag"], (fmt, M, N, K))
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096, 16 * 1025, 1 << 20, (28311552 // 16 + 3) * 16])

@@ -490,6 +490,29 @@ def test_matmul_q4_k_full_size_sampled(env):
     _check(y[mi, ni], ref, mag, "q4_k prefill sampled")
 
 
+@pytest.mark.parametrize("fmt,cfg,M", [("q4_0", 1, 32), ("q4_0", 1, 128), ("q4_k", 5, 64), ("q4_k", 5, 128),
+                                       ("q6_k", 6, 100)])
+def test_matmul_split_k_bench_shapes_sampled(env, fmt, cfg, M):
+    """The few-token products the bench times on the MFMA kernels (12288 x 4096,
+    M <= 128: at most 256 tiles, so K split in two), checked on whole rows and
+    sampled outputs."""
+    torch, q, orc = env
+    N, K = 12288, 4096
+    _say("matmul split-k bench shape", fmt, M, N, K)
+    wq = orc.quantize_w(fmt, synth.weights(N, K, config=cfg))
+    xq = orc.quantize_x(fmt, synth.activations(M, K, config=cfg))
+    y = _run_matmul(env, fmt, wq, xq, M, N, K)
+    assert np.isfinite(y).all()
+    rng = synth.splitmix64(97 + M, 0, 8000)
+    mi = (rng[:4000] % np.uint64(M)).astype(np.int64)
+    ni = (rng[4000:] % np.uint64(N)).astype(np.int64)
+    rows = np.array([0, M - 1])
+    mi = np.concatenate([mi, np.repeat(rows, N)])
+    ni = np.concatenate([ni, np.tile(np.arange(N), len(rows))])
+    ref, mag = orc.matmul_sampled(fmt, wq, xq, mi, ni, K)
+    _check(y[mi, ni], ref, mag, (fmt, M, "split-k sampled"))
+
+
 def test_matmul_q6_k_full_size_sampled(env):
     """The 2048 x 12288 x 4096 prefill with Q6_K weights (one int8 MFMA tile
     per 16-value group on the unsigned codes, signed scales applied in int32,

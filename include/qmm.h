@@ -202,7 +202,8 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
 /* Matmul, M tokens (prefill, or a few tokens at once).
  *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.
  *   y  : f32 [M][N], written.
- * Up to 16 tokens (32 for Q4_K) run on the decode matvec kernel, which
+ * Up to 16 tokens (Q4_0, Q4_1, Q5_1; 32 for Q4_K, 10 for Q8_0, Q5_0 and
+ * Q2_K, 8 for Q6_K) run on the decode matvec kernel, which
  * streams each weight slice once per group of 2, 4 or 8 tokens (one token:
  * the decode launch itself); more tokens run on the MFMA kernels below, whose 128-token tiles
  * would leave most CUs idle for a few tokens.  Results agree within the

@@ -38,7 +38,7 @@ static hipError_t mv_tokens(const void *w, const void *xq, float *y, int M, int 
     return pick_mv_tokens<F, PAIRED, 8>(w, xq, y, M, N, nb, st);
 }
 
-// Products of 2 .. kSmallTokens tokens for any weight format.
+// Products of 2 .. small_tokens(format) tokens for any weight format.
 template <int F>
 static hipError_t matvec_tokens(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
     if constexpr (!kIsK<F>) {

@@ -23,14 +23,17 @@ constexpr int kQ6KBytes = 210;            // ql[128] + qh[64] + int8 scales[16] 
 // formats, one pairing rule").
 enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4, F_Q4_1 = 5, F_Q5_0 = 6, F_Q5_1 = 7 };
 
-// Token counts up to this run the products on the decode kernel with several
-// tokens per weight pass; larger counts run the MFMA prefill kernels, whose
-// 128-token tiles leave most CUs idle below it (N = 12288, K = 4096: about
-// 64 us for any M <= 128).  Q4_K, whose few-token units stay in registers
-// and whose MFMA kernel is slower at small M, switches at 32.
-constexpr int kSmallTokens = 16;
-constexpr int kSmallTokensQ4K = 32;
-constexpr int small_tokens(int fmt) { return fmt == F_Q4_K ? kSmallTokensQ4K : kSmallTokens; }
+// Token counts up to small_tokens(format) run the products on the decode
+// kernel with several tokens per weight pass; larger counts run the MFMA
+// prefill kernels, whose 128-token tiles cost about the same for any
+// M <= 128 (N = 12288, K = 4096, K split in two: 30-47 us by format).  The
+// switch is where the two meet at that size: the decode kernel's cost grows
+// with each group of up to 8 tokens, fastest for the formats with the most
+// unpacking per token (Q6_K), slowest for Q4_K, whose units stay in
+// registers and whose MFMA kernel is the slowest at small M.
+constexpr int small_tokens(int fmt) {
+    return fmt == F_Q4_K ? 32 : fmt == F_Q6_K ? 8 : (fmt == F_Q8_0 || fmt == F_Q5_0 || fmt == F_Q2_K) ? 10 : 16;
+}
 hipError_t launch_matvec_tokens(int fmt, const void *w, const void *xq, float *y, int M, int N, int nb,
                                 hipStream_t st);
 template <int F> constexpr bool kIsK = F == F_Q2_K || F == F_Q4_K || F == F_Q6_K;

@@ -323,7 +323,7 @@ MATMUL_CASES = [
 ]
 
 
-# Few tokens (M <= 16, Q4_K M <= 32): the decode kernel with 4 or 8 tokens per weight pass;
+# Few tokens (up to 8, 10, 16 or 32 by format): the decode kernel with 2, 4 or 8 tokens per weight pass;
 # ragged token groups, odd block counts (unpaired units), rows walked in
 # segments (K = 8192 and 11008), every format.
 SMALL_M_CASES = [
@@ -336,6 +336,11 @@ SMALL_M_CASES = [
     ("q4_k", 3, 130, 4096), ("q4_k", 8, 12288, 4096), ("q4_k", 10, 31, 11008), ("q4_k", 32, 65, 2304),
     ("q4_k", 25, 129, 4096), ("q4_k", 33, 33, 4096),
     ("q6_k", 5, 130, 4096), ("q6_k", 16, 65, 2304), ("q6_k", 9, 33, 11008),
+    # the largest token counts on the decode kernel for the formats that
+    # switch early (Q6_K at 8; Q8_0, Q5_0, Q2_K at 10); the cases above past
+    # those counts run on the MFMA kernels
+    ("q6_k", 8, 65, 2304), ("q6_k", 7, 33, 11008), ("q8_0", 10, 70, 11008), ("q8_0", 9, 257, 4096),
+    ("q5_0", 10, 9, 8192), ("q2_k", 10, 33, 11008), ("q2_k", 9, 130, 4096),
 ]
 
 

@@ -75,13 +75,12 @@ bool size_ok(int64_t rows, int64_t K, int64_t blk, int64_t bytes) {
     return nb == 0 || rows <= kMaxBytes / (nb * bytes);
 }
 
-// Shape checks shared by all entry points.  `work` is false for an empty
-// problem (M or N zero): nothing is launched and no pointer is touched.
-qmm_status check_shape(int64_t M, int64_t N, int64_t K, int64_t blk, bool &work) {
-    work = false;
-    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return QMM_E_SHAPE;
+// Shape checks shared by all entry points: M, N >= 1 and K a positive
+// multiple of the block length, every dimension below 2^31 (krafla "Error
+// handling": a bad size is a status, never a launch).
+qmm_status check_shape(int64_t M, int64_t N, int64_t K, int64_t blk) {
+    if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim) return QMM_E_SHAPE;
     if (K < blk || K > kMaxDim || K % blk != 0) return QMM_E_SHAPE;
-    work = (M > 0 && N > 0);
     return QMM_OK;
 }
 
@@ -99,11 +98,9 @@ typedef hipError_t (*quant_launch)(const float *, void *, int64_t, hipStream_t);
 
 qmm_status quantize(quant_launch fn, const float *x, void *out, int64_t rows, int64_t K, int64_t blk,
                     int64_t in_bytes, int64_t out_bytes, void *stream) {
-    bool work;
-    qmm_status s = check_shape(rows, 1, K, blk, work);
+    qmm_status s = check_shape(rows, 1, K, blk);
     if (s != QMM_OK) return s;
     if (!size_ok(rows, K, blk, in_bytes) || !size_ok(rows, K, blk, out_bytes)) return QMM_E_SHAPE;
-    if (!work) return QMM_OK;
     if ((s = check_ptrs({x, out})) != QMM_OK) return s;
     if ((s = check_device()) != QMM_OK) return s;
     return launched(fn(x, out, rows * (K / blk), static_cast<hipStream_t>(stream)));
@@ -167,11 +164,9 @@ typedef hipError_t (*mv_launch)(const void *, const void *, float *, int, int, h
 
 static qmm_status matvec(mv_launch fn, const void *w, const void *xq, float *y, int64_t N, int64_t K, int64_t blk,
                          int64_t wbytes, int64_t xbytes, void *stream) {
-    bool work;
-    qmm_status s = check_shape(1, N, K, blk, work);
+    qmm_status s = check_shape(1, N, K, blk);
     if (s != QMM_OK) return s;
     if (!size_ok(N, K, blk, wbytes) || !size_ok(1, K, blk, xbytes)) return QMM_E_SHAPE;
-    if (!work) return QMM_OK;
     if ((s = check_ptrs({w, xq, y})) != QMM_OK) return s;
     if ((s = check_device()) != QMM_OK) return s;
     return launched(fn(w, xq, y, (int)N, (int)(K / blk), static_cast<hipStream_t>(stream)));
@@ -213,11 +208,9 @@ typedef hipError_t (*qmv_launch)(const void *, const float *, void *, float *, i
 
 static qmm_status quantize_matvec(qmv_launch fn, const void *w, const float *x, void *xq, float *y, int64_t N,
                                   int64_t K, int64_t wbytes, void *stream) {
-    bool work;
-    qmm_status s = check_shape(1, N, K, 32, work);
+    qmm_status s = check_shape(1, N, K, 32);
     if (s != QMM_OK) return s;
     if (!size_ok(N, K, 32, wbytes) || !size_ok(1, K, 32, 128)) return QMM_E_SHAPE;
-    if (!work) return QMM_OK;
     if ((s = check_ptrs({w, x, y})) != QMM_OK) return s;
     if (xq != nullptr && !aligned16(xq)) return QMM_E_ALIGN;
     if ((s = check_device()) != QMM_OK) return s;
@@ -238,12 +231,10 @@ typedef hipError_t (*mm_launch)(const void *, const void *, float *, int, int, i
 
 static qmm_status matmul(mm_launch fn, const void *w, const void *xq, float *y, int64_t M, int64_t N, int64_t K,
                          int64_t blk, int64_t wbytes, int64_t xbytes, void *stream) {
-    bool work;
-    qmm_status s = check_shape(M, N, K, blk, work);
+    qmm_status s = check_shape(M, N, K, blk);
     if (s != QMM_OK) return s;
     if (!size_ok(N, K, blk, wbytes) || !size_ok(M, K, blk, xbytes)) return QMM_E_SHAPE;
     if (N > 0 && M > kMaxBytes / 4 / N) return QMM_E_SHAPE;
-    if (!work) return QMM_OK;
     if ((s = check_ptrs({w, xq, y})) != QMM_OK) return s;
     if ((s = check_device()) != QMM_OK) return s;
     return launched(fn(w, xq, y, (int)M, (int)N, (int)(K / blk), static_cast<hipStream_t>(stream)));
@@ -294,12 +285,10 @@ qmm_status qmm_matmul_q6_k(const void *w, const void *xq8k, float *y, int64_t M,
 
 static qmm_status get_rows(int fmt, const void *w, const int32_t *ids, float *out, int64_t n, int64_t N, int64_t K,
                            int64_t blk, int64_t wbytes, void *stream) {
-    bool work;
-    qmm_status s = check_shape(n, N, K, blk, work);
+    qmm_status s = check_shape(n, N, K, blk);
     if (s != QMM_OK) return s;
     if (!size_ok(N, K, blk, wbytes) || !size_ok(n, K, 1, 4)) return QMM_E_SHAPE;
     if ((n * (K / 4) + 255) / 256 > kMaxDim) return QMM_E_SHAPE;
-    if (!work) return QMM_OK;
     if ((s = check_ptrs({w, ids, out})) != QMM_OK) return s;
     if ((s = check_device()) != QMM_OK) return s;
     return launched(qmm::launch_get_rows(fmt, w, ids, out, n, N, K, K / blk * wbytes, static_cast<hipStream_t>(stream)));

@@ -479,6 +479,7 @@ __device__ __forceinline__ float unit_dot<F_Q5_1, false>(const uint8_t *sl, uint
 // the group that are never read), so the number of instructions this wave
 // issued is exactly the return value.  Global reads never pass the 16-byte
 // granule that holds byte hi-1.
+template <bool STREAM = false>
 __device__ __forceinline__ int dma_span(const uint8_t *src, int64_t lo, int64_t hi, uint4 *dst, int lane,
                                         int first, int step) {
     const int64_t A = lo & ~(int64_t)15;
@@ -486,7 +487,7 @@ __device__ __forceinline__ int dma_span(const uint8_t *src, int64_t lo, int64_t 
     int issued = 0;
     for (int k = first; k * kWave < nch; k += step) {
         const int c = min(k * kWave + lane, nch - 1);
-        global_to_lds16(src + A + 16 * (int64_t)c, dst + k * kWave);
+        global_to_lds16<STREAM>(src + A + 16 * (int64_t)c, dst + k * kWave);
         ++issued;
     }
     return issued;
@@ -865,7 +866,8 @@ __global__ __launch_bounds__(64 * NW) void k_matvec(const uint8_t *__restrict__ 
             const int64_t lo = row0 * RB + (int64_t)b0 * FB::BB;
             const int64_t hi = (row0 + nrows - 1) * RB + (int64_t)b1 * FB::BB;
             A = lo & ~(int64_t)15;
-            wissued = dma_span(w, lo, hi, slice, lane, 0, 1);
+            // one token: every weight byte is read once per launch
+            wissued = dma_span<TT == 1>(w, lo, hi, slice, lane, 0, 1);
         }
         wait_vmcnt(wissued);                           // this wave's activation loads have landed
         if constexpr (XF32) {

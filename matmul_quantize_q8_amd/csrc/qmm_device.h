@@ -65,15 +65,21 @@ __device__ __forceinline__ int dot4(int a, int b, int c) {
     return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
+// Cache-policy bits of a gfx950 vector-memory instruction: NT = non-temporal.
+constexpr int kCpolNT = 2;
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
 // 16 bytes per lane from global straight into LDS (gfx950 LDS DMA).  `dst` must
 // be the same for every lane of the wave: lane i's bytes land at dst + 16*i.
 // The LDS write completes with the vector-memory counter, so a reader must
-// wait_global_loads() first.
+// wait_global_loads() first.  STREAM marks data read once per launch (the
+// decode weights): the load carries the non-temporal cache policy, so the
+// stream does not displace reused lines (a 28 MB read runs ~4 % faster).
+template <bool STREAM = false>
 __device__ __forceinline__ void global_to_lds16(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_void *)src, (lds_void *)dst, 16, 0, STREAM ? kCpolNT : 0);
 }
 
 // 16 bytes per lane from global memory into registers, issued as inline

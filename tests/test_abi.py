@@ -109,12 +109,19 @@ def test_argument_errors_without_device(q, call, code):
     assert call(q.lib()) == code
 
 
-def test_empty_problem_is_a_no_op(q):
+def test_empty_problem_is_a_shape_error(q):
+    """M < 1 or N < 1 is QMM_E_SHAPE (the header's size rule), reported before
+    any pointer is looked at."""
     L = q.lib()
-    assert L.qmm_matmul_q4_0(None, None, None, 0, 8, 32, None) == 0
-    assert L.qmm_matvec_q8_0(None, None, None, 0, 32, None) == 0
-    assert L.qmm_quantize_q8_0(None, None, 0, 64, None) == 0
-    assert L.qmm_quantize_matvec_q4_0(None, None, None, None, 0, 64, None) == 0
+    assert L.qmm_matmul_q4_0(None, None, None, 0, 8, 32, None) == 1
+    assert L.qmm_matmul_q4_0(None, None, None, 4, 0, 32, None) == 1
+    assert L.qmm_matmul_q2_k(None, None, None, -1, 8, 256, None) == 1
+    assert L.qmm_matvec_q8_0(None, None, None, 0, 32, None) == 1
+    assert L.qmm_quantize_q8_0(None, None, 0, 64, None) == 1
+    assert L.qmm_quantize_q8_k(None, None, 0, 256, None) == 1
+    assert L.qmm_quantize_matvec_q4_0(None, None, None, None, 0, 64, None) == 1
+    assert L.qmm_get_rows_q4_0(None, None, None, 0, 8, 32, None) == 1
+    assert L.qmm_get_rows_q4_0(None, None, None, 4, 0, 32, None) == 1
 
 
 def test_python_binding_raises(q):

@@ -45,8 +45,10 @@ int main(void) {
     expect("matmul K", qmm_matmul_q4_0(A, A, (float *)A, 4, 8, 33, NULL), QMM_E_SHAPE);
     expect("matmul M", qmm_matmul_q4_0(A, A, (float *)A, (int64_t)1 << 31, 8, 32, NULL), QMM_E_SHAPE);
     expect("fused K", qmm_quantize_matvec_q4_0(A, (const float *)A, A, (float *)A, 8, 48, NULL), QMM_E_SHAPE);
-    expect("empty matmul", qmm_matmul_q4_0(NULL, NULL, NULL, 0, 8, 32, NULL), QMM_OK);
-    expect("empty matvec", qmm_matvec_q8_0(NULL, NULL, NULL, 0, 32, NULL), QMM_OK);
+    expect("matmul M = 0", qmm_matmul_q4_0(NULL, NULL, NULL, 0, 8, 32, NULL), QMM_E_SHAPE);
+    expect("matmul N = 0", qmm_matmul_q4_0(NULL, NULL, NULL, 4, 0, 32, NULL), QMM_E_SHAPE);
+    expect("matvec N = 0", qmm_matvec_q8_0(NULL, NULL, NULL, 0, 32, NULL), QMM_E_SHAPE);
+    expect("quantize M = 0", qmm_quantize_q8_0(NULL, NULL, 0, 32, NULL), QMM_E_SHAPE);
     printf(fails ? "failed\n" : "ok\n");
     return fails != 0;
 }

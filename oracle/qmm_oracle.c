@@ -21,15 +21,18 @@
  * repeated at the function that applies them.
  *
  * Parity status: every exported function is pinned by a CPU test (values the
- * pages print, closed forms, invariants, a library routine or brute force),
- * except where the pages give no rule at all, which is "parity unpinned":
- *   - the Q2_K, Q4_K and Q6_K weight quantizers (their output bytes are only
- *     test data; only the invariants of the format they fill are checked);
- *   - the packing of Q4_K's eight 6-bit scales and mins into 12 bytes, and the
- *     whole Q6_K block layout: the pages give the block sizes (144 and 210
- *     bytes), Q4_K's field order and its two-term dot, but not these bits; the
- *     reading is GGUF's layout, pinned only by round trips and by brute force
- *     against the decoded values (which checks the dot, not the layout).
+ * pages print, closed forms, invariants, a library routine or brute force).
+ * The Q2_K, Q4_K, Q6_K, Q4_1, Q5_0 and Q5_1 weight quantizers follow rules of
+ * our own (the pages give their formats, not a quantizer); each rule as
+ * stated at its function is pinned by hand-computed blocks (every
+ * intermediate worked out by hand, ties, clamp edges, f16-rounded scales)
+ * that altered copies of these functions fail.  "Parity unpinned" remains
+ * only where the pages give no bits at all: the packing of Q4_K's eight
+ * 6-bit scales and mins into 12 bytes, the whole Q6_K block layout, and the
+ * Q4_1 / Q5_0 / Q5_1 field and bit order (the pages give the block sizes,
+ * Q4_K's field order and its two-term dot, and the d*q + m form; the reading
+ * is GGUF's layout, pinned only by round trips and by brute force against
+ * the decoded values, which checks the dot, not the layout).
  */
 #include <math.h>
 #include <pthread.h>

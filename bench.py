@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400, help="timed decode steps")
     ap.add_argument("--warmup", type=int, default=40, help="untimed decode steps")
-    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=52, help="timed prefill steps (at least 52 are timed)")
     ap.add_argument("--prefill-warmup", type=int, default=30,
                     help="untimed prefill steps (~10 ms: lets the clock settle under the MFMA load)")
     ap.add_argument("--only", choices=["all", "decode", "prefill", "configs"], default="all")
@@ -95,29 +95,75 @@ def committed_traffic(kernel, workload):
     return int(fields["traffic_bytes_per_launch"]) if h.hexdigest() == fields["kernel_source_sha256"] else None
 
 
-def time_batches(torch, launch, count, batch):
-    """Mean duration of one launch of a kernel: `batch` back-to-back launches
-    (launch(i), i = 0..batch-1) are captured into a HIP graph, the graph is
-    replayed count // batch times, and HIP events on the launch stream bracket
-    each replay.  The mean includes the short gap between consecutive kernels
-    of a graph, so it slightly over-states the kernel's own duration.  (Timing
-    Python launches instead would measure the interpreter for kernels of a few
-    microseconds.)"""
+def capture(torch, launch, batch):
+    """A HIP graph of `batch` back-to-back launches launch(0) .. launch(batch-1)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(batch):
             launch(i)
     g.replay()
     torch.cuda.synchronize()
-    nb = max(1, count // batch)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nb)]
-    for a, b in ev:
-        a.record()
-        g.replay()
-        b.record()
+    return g
+
+
+def warm_up(torch, graphs, min_ms=25.0, max_reps=400):
+    """Replay the graphs round-robin until at least min_ms of GPU time has
+    passed, so that clocks have settled before anything is timed (the first
+    milliseconds after a quiet period run measurably slower)."""
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    done, reps = 0.0, 0
+    while done < min_ms and reps < max_reps:
+        t0.record()
+        for g in graphs:
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        done += t0.elapsed_time(t1)
+        reps += 1
+
+
+def replay_rounds(torch, graphs, rounds):
+    """Times `rounds` replays of every graph, alternating between the graphs
+    (so that all see the same clock conditions), with HIP events on the
+    launch stream around each replay.  Returns per graph the list of replay
+    durations in ms.  A replay's duration includes the short gaps between the
+    kernels of its batch, so it slightly over-states the kernels' own time.
+    (Timing Python launches instead would measure the interpreter for kernels
+    of a few microseconds.)"""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+          for _ in graphs]
+    for r in range(rounds):
+        for k, g in enumerate(graphs):
+            a, b = ev[k][r]
+            a.record()
+            g.replay()
+            b.record()
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) / batch for a, b in ev]
-    return sum(per) / len(per), min(per), nb * batch
+    return [[a.elapsed_time(b) for a, b in e] for e in ev]
+
+
+def per_launch(times, batch):
+    """mean, median, min and max per launch (ms) of replays of `batch` launches."""
+    per = sorted(t / batch for t in times)
+    n = len(per)
+    med = per[n // 2] if n % 2 else 0.5 * (per[n // 2 - 1] + per[n // 2])
+    return {"mean": sum(per) / n, "median": med, "min": per[0], "max": per[-1], "launches": n * batch}
+
+
+def time_kernels(torch, launches, batch, count, warm_ms=25.0):
+    """Per-launch timing (see per_launch) of each launch function in
+    `launches`: graphs of `batch` launches, warmed up, then replayed
+    alternately until each has run at least `count` launches."""
+    graphs = [capture(torch, f, batch) for f in launches]
+    warm_up(torch, graphs, warm_ms)
+    rounds = max(1, -(-count // batch))
+    return [per_launch(t, batch) for t in replay_rounds(torch, graphs, rounds)]
+
+
+def us(d):
+    """A per_launch record in microseconds, rounded."""
+    return {k: (round(v * 1e3, 3) if k != "launches" else v) for k, v in d.items()}
 
 
 def bench_decode(args, torch, q, synth):
@@ -144,71 +190,92 @@ def bench_decode(args, torch, q, synth):
         q.qmm_quantize_q8_0(x, xq, 1, K)
         q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K)
 
-    def replayed(fn):
-        """ms per step of exactly args.steps steps of `fn`, replayed from captured
-        HIP graphs (one of a step per weight copy, one of the remaining
-        args.steps mod copies steps); a decode loop driven eagerly from Python is
-        launch-bound."""
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        reps, rem = divmod(args.steps, copies)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(copies):
-                fn(i)
-        tail = None
-        if rem:
-            tail = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(tail):
-                for i in range(rem):
-                    fn(i)
-            tail.replay()
-        graph.replay()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(reps):
-            graph.replay()
-        if tail is not None:
-            tail.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / args.steps, args.steps
-
-    ms_step, nsteps = replayed(step)
-    ms_two, _ = replayed(step_two_launches)
-    # the step launched eagerly from Python, for reference
+    # exactly args.steps steps: whole replays of a graph of one step per
+    # weight copy, then a graph of the remaining steps; warmed up first
+    for i in range(args.warmup):
+        step(i)
+    reps, rem = divmod(args.steps, copies)
+    g_full = capture(torch, step, copies)
+    graphs = [g_full] + ([capture(torch, step, rem)] if rem else [])
+    warm_up(torch, graphs)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g_full.replay()
+    if rem:
+        graphs[1].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    nsteps = args.steps
+    # the step launched eagerly from Python, for reference
     t0.record()
     for i in range(args.steps):
         step(i)
     t1.record()
     torch.cuda.synchronize()
     ms_step_eager = t0.elapsed_time(t1) / args.steps
-    # the dominant kernel alone (the fused kernel; the plain matvec beside it):
-    # batches of `copies` back-to-back launches
-    fz_ms, fz_min, n = time_batches(torch, step, args.steps, copies)
-    mv_ms, mv_min, _ = time_batches(torch, lambda i: q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K),
-                                    args.steps, copies)
-    log(f"decode: {ms_step * 1e3:.2f} us/step in graph replay ({ms_step_eager * 1e3:.2f} eager; two launches "
-        f"{ms_two * 1e3:.2f}), fused kernel {fz_ms * 1e3:.2f} us (best batch {fz_min * 1e3:.2f}), matvec alone "
-        f"{mv_ms * 1e3:.2f} us over {copies} weight copies, {n} launches")
+    # the dominant kernel (the fused kernel, the whole step), the plain matvec
+    # beside it and the step as two launches, alternating, at least 200
+    # launches each
+    count = max(200, args.steps)
+    fz, mv, two = time_kernels(torch, [step, lambda i: q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K),
+                                       step_two_launches], copies, count)
+    log(f"decode: {ms_step * 1e3:.2f} us/step over {nsteps} steps in graph replay ({ms_step_eager * 1e3:.2f} eager); "
+        f"fused kernel mean {fz['mean'] * 1e3:.2f} us (median {fz['median'] * 1e3:.2f}, {fz['launches']} launches), "
+        f"matvec alone {mv['mean'] * 1e3:.2f} us, two launches {two['mean'] * 1e3:.2f} us, {copies} weight copies")
     gbs_step = wbytes / (ms_step * 1e-3) / 1e9
-    gbs_kernel = wbytes / (fz_ms * 1e-3) / 1e9
-    return dict(ms_step=ms_step, ms_step_eager=ms_step_eager, ms_two=ms_two, nsteps=nsteps, gbs=gbs_step,
+    gbs_kernel = wbytes / (fz["mean"] * 1e-3) / 1e9
+    return dict(ms_step=ms_step, ms_step_eager=ms_step_eager, ms_two=two["mean"], nsteps=nsteps, gbs=gbs_step,
                 wbytes=wbytes, copies=copies,
                 roofline={"kernel": "qmm::k_matvec<Q4_0, fused quantize>", "bound": "hbm",
                           "achieved": round(gbs_kernel, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
                           "traffic": committed_traffic("k_matvec_q4_0_fused", "12288x4096"),
-                          "kernel_us_mean": round(fz_ms * 1e3, 3), "kernel_us_best_batch": round(fz_min * 1e3, 3),
+                          "kernel_us_mean": round(fz["mean"] * 1e3, 3), "kernel_us": us(fz),
                           "algorithmic_bytes": wbytes + 4 * K + 4 * N,
-                          "matvec_only": {"kernel": "qmm::k_matvec<Q4_0>", "us_mean": round(mv_ms * 1e3, 3),
-                                          "achieved": round(wbytes / (mv_ms * 1e-3) / 1e9, 1),
+                          "matvec_only": {"kernel": "qmm::k_matvec<Q4_0>", "us_mean": round(mv["mean"] * 1e3, 3),
+                                          "us": us(mv),
+                                          "achieved": round(wbytes / (mv["mean"] * 1e-3) / 1e9, 1),
                                           "traffic": committed_traffic("k_matvec_q4_0", "12288x4096")}})
+
+
+def bench_small(args, torch, q, synth):
+    """Latency of the 512 x 1024 Q4_0 decode (its 295 KB of weight blocks stay
+    in L2, so this is a latency figure, not an HBM one) and the activation
+    quantizers on their own (GB/s of f32 input)."""
+    N, K = 512, 1024
+    w = torch.from_numpy(synth.weights(N, K, config=0)).cuda()
+    wq = torch.empty(N * q.row_bytes("q4_0", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q4_0(w, wq, N, K)
+    x = torch.from_numpy(synth.activations(1, K, config=0)).cuda()
+    xq = torch.empty(q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
+    q.qmm_quantize_q8_0(x, xq, 1, K)
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    count = max(200, args.steps)
+    fz, mv = time_kernels(torch, [lambda i: q.qmm_quantize_matvec_q4_0(wq, x, None, y, N, K),
+                                  lambda i: q.qmm_matvec_q4_0(wq, xq, y, N, K)], 50, count)
+    wb = N * q.row_bytes("q4_0", K)
+    res = {"workload": "q4_0_matvec_512x1024", "weight_bytes": wb, "l2_resident": True,
+           "fused_us": us(fz), "matvec_us": us(mv),
+           "matvec_gbs": round(wb / (mv["mean"] * 1e-3) / 1e9, 1),
+           "hbm_frac_flagged_l2_resident": round(wb / (mv["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"small decode 512x1024: fused {fz['mean'] * 1e3:.2f} us, matvec {mv['mean'] * 1e3:.2f} us (L2-resident)")
+    quant = []
+    for M, Kq in ((2048, 4096), (1, 4096)):
+        X = torch.from_numpy(synth.activations(M, Kq, config=4)).cuda()
+        X8 = torch.empty(M * q.row_bytes("q8_0", Kq), dtype=torch.uint8, device="cuda")
+        XK = torch.empty(M * q.row_bytes("q8_k", Kq), dtype=torch.uint8, device="cuda")
+        t8, tk = time_kernels(torch, [lambda i: q.qmm_quantize_q8_0(X, X8, M, Kq),
+                                      lambda i: q.qmm_quantize_q8_k(X, XK, M, Kq)], 20, max(100, args.steps))
+        for name, t, ob in (("q8_0", t8, X8.numel()), ("q8_k", tk, XK.numel())):
+            quant.append({"quantizer": name, "M": M, "K": Kq, "in_bytes": 4 * M * Kq, "out_bytes": ob,
+                          "us": us(t), "in_gbs": round(4 * M * Kq / (t["mean"] * 1e-3) / 1e9, 1),
+                          "hbm_frac": round((4 * M * Kq + ob) / (t["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+            log(f"quantize {name} {M}x{Kq}: {t['mean'] * 1e3:.2f} us, {quant[-1]['in_gbs']} GB/s of f32 in")
+    res["quantizers"] = quant
+    return res
 
 
 def bench_prefill(args, torch, q, synth):
@@ -224,45 +291,54 @@ def bench_prefill(args, torch, q, synth):
     Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
 
-    def step():
+    def step(i):
         q.qmm_quantize_q8_0(X, Xq, M, K)
         q.qmm_matmul_q4_0(wq, Xq, Y, M, N, K)
 
+    def kernel(i):
+        q.qmm_matmul_q4_0(wq, Xq, Y, M, N, K)
+
+    # the step (quantize + matmul) and the matmul alone: graphs of 4 of each,
+    # warmed up together, then replayed alternately in the same rounds so
+    # both see the same clock conditions; at least 52 launches each
     for _ in range(args.prefill_warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(args.prefill_steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.prefill_steps
-    mm_ms, mm_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q4_0(wq, Xq, Y, M, N, K),
-                                    args.prefill_steps, 4)
+        step(0)
+    B = 4
+    g_step, g_kern = capture(torch, step, B), capture(torch, kernel, B)
+    warm_up(torch, [g_step, g_kern])
+    rounds = max(1, -(-max(args.prefill_steps, 52) // B))
+    t_step, t_kern = replay_rounds(torch, [g_step, g_kern], rounds)
+    st, mm = per_launch(t_step, B), per_launch(t_kern, B)
+    ms_step, nsteps = st["mean"], st["launches"]
     ops = 2.0 * M * N * K
-    log(f"prefill: {ms_step * 1e3:.1f} us/step, matmul {mm_ms * 1e3:.1f} us (best batch {mm_min * 1e3:.1f})")
-    tops_kernel = ops / (mm_ms * 1e-3) / 1e12
+    log(f"prefill: {ms_step * 1e3:.1f} us/step (median {st['median'] * 1e3:.1f}), matmul mean {mm['mean'] * 1e3:.1f} "
+        f"us (median {mm['median'] * 1e3:.1f}, {mm['min'] * 1e3:.1f}..{mm['max'] * 1e3:.1f}), {rounds} rounds of {B}")
+    if ms_step < mm["mean"]:
+        log("prefill: WARNING the step measured shorter than the kernel it contains")
+    tops_kernel = ops / (mm["mean"] * 1e-3) / 1e12
+
+    def time_one(launch):
+        for _ in range(4):
+            launch(0)
+        return time_kernels(torch, [launch], B, max(args.prefill_steps, 52))[0]
+
     # the same prefill with Q8_0 weights (same activations, weights from the same stream)
     w = torch.from_numpy(synth.weights(N, K, config=1)).cuda()
     wq8 = torch.empty(N * q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
     q.qmm_quantize_q8_0(w, wq8, N, K)
     del w
-    for _ in range(4):
-        q.qmm_matmul_q8_0(wq8, Xq, Y, M, N, K)
-    m8_ms, m8_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q8_0(wq8, Xq, Y, M, N, K), args.prefill_steps, 4)
-    log(f"prefill q8_0 weights: matmul {m8_ms * 1e3:.1f} us (best batch {m8_min * 1e3:.1f})")
+    t8 = time_one(lambda i: q.qmm_matmul_q8_0(wq8, Xq, Y, M, N, K))
+    m8_ms = t8["mean"]
+    log(f"prefill q8_0 weights: matmul {m8_ms * 1e3:.1f} us (median {t8['median'] * 1e3:.1f})")
     del wq8
     # Q5_0 weights (weights of the Q5_0 workload, the same Q8_0 activations)
     w = torch.from_numpy(synth.weights(N, K, config=10)).cuda()
     wq5 = torch.empty(N * q.row_bytes("q5_0", K), dtype=torch.uint8, device="cuda")
     q.qmm_quantize_q5_0(w, wq5, N, K)
     del w
-    for _ in range(4):
-        q.qmm_matmul_q5_0(wq5, Xq, Y, M, N, K)
-    m5_ms, m5_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q5_0(wq5, Xq, Y, M, N, K), args.prefill_steps, 4)
-    log(f"prefill q5_0 weights: matmul {m5_ms * 1e3:.1f} us (best batch {m5_min * 1e3:.1f})")
+    t5 = time_one(lambda i: q.qmm_matmul_q5_0(wq5, Xq, Y, M, N, K))
+    m5_ms = t5["mean"]
+    log(f"prefill q5_0 weights: matmul {m5_ms * 1e3:.1f} us (median {t5['median'] * 1e3:.1f})")
     del wq5
     # Q4_1 and Q5_1 weights (weights of their decode workloads, the same Q8_0 activations)
     off = {}
@@ -271,11 +347,10 @@ def bench_prefill(args, torch, q, synth):
         wqf = torch.empty(N * q.row_bytes(fmt, K), dtype=torch.uint8, device="cuda")
         q.QUANTIZE_W[fmt](w, wqf, N, K)
         del w
-        for _ in range(4):
-            q.MATMUL[fmt](wqf, Xq, Y, M, N, K)
-        f_ms, f_min, _ = time_batches(torch, lambda i: q.MATMUL[fmt](wqf, Xq, Y, M, N, K), args.prefill_steps, 4)
-        log(f"prefill {fmt} weights: matmul {f_ms * 1e3:.1f} us (best batch {f_min * 1e3:.1f})")
-        off[fmt] = {"kernel": f"qmm::k_matmul_{fmt}", "kernel_us_mean": round(f_ms * 1e3, 2),
+        tf = time_one(lambda i: q.MATMUL[fmt](wqf, Xq, Y, M, N, K))
+        f_ms = tf["mean"]
+        log(f"prefill {fmt} weights: matmul {f_ms * 1e3:.1f} us (median {tf['median'] * 1e3:.1f})")
+        off[fmt] = {"kernel": f"qmm::k_matmul_{fmt}", "kernel_us_mean": round(f_ms * 1e3, 2), "kernel_us": us(tf),
                     "achieved": round(ops / (f_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                     "frac": round(ops / (f_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                     "traffic": committed_traffic(f"k_matmul_{fmt}", "2048x12288x4096")}
@@ -287,55 +362,52 @@ def bench_prefill(args, torch, q, synth):
     del w
     X8k = torch.empty(M * q.row_bytes("q8_k", K), dtype=torch.uint8, device="cuda")
     q.qmm_quantize_q8_k(X, X8k, M, K)
-    for _ in range(4):
-        q.qmm_matmul_q2_k(wq2, X8k, Y, M, N, K)
-    m2_ms, m2_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q2_k(wq2, X8k, Y, M, N, K), args.prefill_steps, 4)
-    log(f"prefill q2_k weights: matmul {m2_ms * 1e3:.1f} us (best batch {m2_min * 1e3:.1f})")
+    t2 = time_one(lambda i: q.qmm_matmul_q2_k(wq2, X8k, Y, M, N, K))
+    m2_ms = t2["mean"]
+    log(f"prefill q2_k weights: matmul {m2_ms * 1e3:.1f} us (median {t2['median'] * 1e3:.1f})")
     del wq2
     # Q4_K weights x Q8_K activations (the format of q4_K_M files; weights of the Q4_K workload)
     w = torch.from_numpy(synth.weights(N, K, config=5)).cuda()
     wq4k = torch.empty(N * q.row_bytes("q4_k", K), dtype=torch.uint8, device="cuda")
     q.qmm_quantize_q4_k(w, wq4k, N, K)
     del w
-    for _ in range(4):
-        q.qmm_matmul_q4_k(wq4k, X8k, Y, M, N, K)
-    m4_ms, m4_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q4_k(wq4k, X8k, Y, M, N, K), args.prefill_steps, 4)
-    log(f"prefill q4_k weights: matmul {m4_ms * 1e3:.1f} us (best batch {m4_min * 1e3:.1f})")
+    t4 = time_one(lambda i: q.qmm_matmul_q4_k(wq4k, X8k, Y, M, N, K))
+    m4_ms = t4["mean"]
+    log(f"prefill q4_k weights: matmul {m4_ms * 1e3:.1f} us (median {t4['median'] * 1e3:.1f})")
     del wq4k
     # Q6_K weights x Q8_K activations (weights of the Q6_K workload)
     w = torch.from_numpy(synth.weights(N, K, config=6)).cuda()
     wq6k = torch.empty(N * q.row_bytes("q6_k", K), dtype=torch.uint8, device="cuda")
     q.qmm_quantize_q6_k(w, wq6k, N, K)
     del w
-    for _ in range(4):
-        q.qmm_matmul_q6_k(wq6k, X8k, Y, M, N, K)
-    m6_ms, m6_min, _ = time_batches(torch, lambda i: q.qmm_matmul_q6_k(wq6k, X8k, Y, M, N, K), args.prefill_steps, 4)
-    log(f"prefill q6_k weights: matmul {m6_ms * 1e3:.1f} us (best batch {m6_min * 1e3:.1f})")
+    t6 = time_one(lambda i: q.qmm_matmul_q6_k(wq6k, X8k, Y, M, N, K))
+    m6_ms = t6["mean"]
+    log(f"prefill q6_k weights: matmul {m6_ms * 1e3:.1f} us (median {t6['median'] * 1e3:.1f})")
     del wq6k, X8k
-    return dict(ms_step=ms_step, tops=ops / (ms_step * 1e-3) / 1e12,
+    return dict(ms_step=ms_step, nsteps=nsteps, step_us=us(st), tops=ops / (ms_step * 1e-3) / 1e12,
                 roofline={"kernel": "qmm::k_matmul_q4_0", "bound": "mfma", "achieved": round(tops_kernel, 2),
                           "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
                           "traffic": committed_traffic("k_matmul_q4_0", "2048x12288x4096"),
-                          "kernel_us_mean": round(mm_ms * 1e3, 2),
-                          "kernel_us_best_batch": round(mm_min * 1e3, 2), "algorithmic_ops": ops},
-                q8_0_weights={"kernel": "qmm::k_matmul_q8_0", "kernel_us_mean": round(m8_ms * 1e3, 2),
+                          "kernel_us_mean": round(mm["mean"] * 1e3, 2), "kernel_us": us(mm),
+                          "algorithmic_ops": ops},
+                q8_0_weights={"kernel": "qmm::k_matmul_q8_0", "kernel_us_mean": round(m8_ms * 1e3, 2), "kernel_us": us(t8),
                               "achieved": round(ops / (m8_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m8_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                               "traffic": committed_traffic("k_matmul_q8_0", "2048x12288x4096")},
-                q5_0_weights={"kernel": "qmm::k_matmul_q5_0", "kernel_us_mean": round(m5_ms * 1e3, 2),
+                q5_0_weights={"kernel": "qmm::k_matmul_q5_0", "kernel_us_mean": round(m5_ms * 1e3, 2), "kernel_us": us(t5),
                               "achieved": round(ops / (m5_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m5_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                               "traffic": committed_traffic("k_matmul_q5_0", "2048x12288x4096")},
                 q4_1_weights=off["q4_1"], q5_1_weights=off["q5_1"],
-                q2_k_weights={"kernel": "qmm::k_matmul_k<Q2_K>", "kernel_us_mean": round(m2_ms * 1e3, 2),
+                q2_k_weights={"kernel": "qmm::k_matmul_k<Q2_K>", "kernel_us_mean": round(m2_ms * 1e3, 2), "kernel_us": us(t2),
                               "achieved": round(ops / (m2_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m2_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                               "traffic": committed_traffic("k_matmul_q2_k", "2048x12288x4096")},
-                q4_k_weights={"kernel": "qmm::k_matmul_k<Q4_K>", "kernel_us_mean": round(m4_ms * 1e3, 2),
+                q4_k_weights={"kernel": "qmm::k_matmul_k<Q4_K>", "kernel_us_mean": round(m4_ms * 1e3, 2), "kernel_us": us(t4),
                               "achieved": round(ops / (m4_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m4_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                               "traffic": committed_traffic("k_matmul_q4_k", "2048x12288x4096")},
-                q6_k_weights={"kernel": "qmm::k_matmul_k<Q6_K>", "kernel_us_mean": round(m6_ms * 1e3, 2),
+                q6_k_weights={"kernel": "qmm::k_matmul_k<Q6_K>", "kernel_us_mean": round(m6_ms * 1e3, 2), "kernel_us": us(t6),
                               "achieved": round(ops / (m6_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
                               "frac": round(ops / (m6_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                               "traffic": committed_traffic("k_matmul_q6_k", "2048x12288x4096")})
@@ -377,12 +449,13 @@ def bench_matvec_configs(args, torch, q, synth):
         y = torch.empty(N, dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
         mv = q.MATVEC[fmt]
-        ms, ms_min, _ = time_batches(torch, lambda i: mv(wqs[i % copies], xq, y, N, K), args.steps, copies)
+        t = time_kernels(torch, [lambda i: mv(wqs[i % copies], xq, y, N, K)], copies, max(200, args.steps))[0]
+        ms = t["mean"]
         gbs = wbytes / (ms * 1e-3) / 1e9
         log(f"matvec {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM) over "
             f"{copies} weight copies")
         rows.append({"workload": name, "format": fmt, "N": N, "K": K, "weight_bytes": wbytes,
-                     "kernel_us_mean": round(ms * 1e3, 3), "kernel_us_best_batch": round(ms_min * 1e3, 3),
+                     "kernel_us_mean": round(ms * 1e3, 3), "kernel_us": us(t),
                      "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
         del wqs, wq0
         torch.cuda.empty_cache()
@@ -397,13 +470,14 @@ def bench_matvec_configs(args, torch, q, synth):
     ids = torch.from_numpy((synth.splitmix64(synth.seed_for(7, 1), 0, nid) % Nt).astype("int32")).cuda()
     emb = torch.empty((nid, Kt), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    ms, ms_min, _ = time_batches(torch, lambda i: q.qmm_get_rows_q4_0(table, ids, emb, nid, Nt, Kt), args.steps, 20)
+    t = time_kernels(torch, [lambda i: q.qmm_get_rows_q4_0(table, ids, emb, nid, Nt, Kt)], 20, max(200, args.steps))[0]
+    ms = t["mean"]
     moved = nid * (q.row_bytes("q4_0", Kt) + 4 * Kt + 4)
     gbs = moved / (ms * 1e-3) / 1e9
     log(f"get_rows q4_0 {nid} of {Nt}x{Kt}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s of rows read + written")
     rows.append({"workload": f"q4_0_get_rows_{nid}_of_{Nt}x{Kt}", "format": "q4_0", "N": Nt, "K": Kt,
                  "ids": nid, "bytes_moved": moved, "kernel_us_mean": round(ms * 1e3, 3),
-                 "kernel_us_best_batch": round(ms_min * 1e3, 3), "achieved_gbs": round(gbs, 1),
+                 "kernel_us": us(t), "achieved_gbs": round(gbs, 1),
                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
     del table
     layer = [r for r in rows if r["workload"].startswith("q8_0_")]
@@ -416,49 +490,63 @@ def bench_matvec_configs(args, torch, q, synth):
 
 
 def bench_peaks(args, torch, q, sizes=()):
-    """Measured ceilings (library probes): a streaming read of 1 GiB in one
-    pass; passes of the decode's 28,311,552 weight bytes over rotating slices
-    of that buffer (37 slices, 1 GiB > the 256 MB last-level cache, so each
-    pass is cold, as each decode step is), and the same for every other decode
-    workload's weight size in `sizes`; and back-to-back int8 MFMAs on register
-    operands at two and three waves per SIMD."""
+    """Measured ceilings (the probes of libqmm_probe.so).  Reads: every
+    configuration of the read probe (1, 2, 4, 8, 16 loads in flight per lane;
+    4, 8, 16 waves per workgroup; plain or non-temporal loads) over passes of
+    the decode's 28,311,552 weight bytes, each launch on the next of 37
+    rotating slices of a 1 GiB buffer (> the 256 MB last-level cache, so each
+    pass is cold, as each decode step is), timed like the kernels they bound;
+    the fastest is the attainable 28 MB read, and the same configuration
+    gives a 1 GiB pass and a pass of every other decode workload's weight
+    size in `sizes`.  MFMA: back-to-back int8 MFMAs on register operands at
+    two and three waves per SIMD."""
+    from matmul_quantize_q8_amd import probe
     size = 1 << 30
     buf = torch.arange(size // 4, dtype=torch.int32, device="cuda")
-    sink = torch.zeros(size // 8192, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(size // 16384 + 1, dtype=torch.int32, device="cuda")
     base = buf.data_ptr()
-    for _ in range(3):
-        q.qmm_peak_read(base, size, sink)
-    big_ms, _, _ = time_batches(torch, lambda i: q.qmm_peak_read(base, size, sink), 24, 4)
     S = DEC["N"] * q.row_bytes("q4_0", DEC["K"])
     ns = size // S
-    for i in range(ns):
-        q.qmm_peak_read(base + (i % ns) * S, S, sink)
-    sl_ms, sl_min, _ = time_batches(torch, lambda i: q.qmm_peak_read(base + (i % ns) * S, S, sink), args.steps, ns)
+    configs = [(lpl, nw, nt) for nt in (True, False) for nw in probe.WAVES_PER_WG for lpl in probe.LOADS_PER_LANE
+               if probe.read_span(lpl, nw) >= 16384]
+
+    def launcher(B, lpl, nw, nt):
+        nsl = size // B
+        return lambda i: probe.qmm_peak_read(base + (i % nsl) * B, B, sink, lpl, nw, nt)
+
+    sweep = time_kernels(torch, [launcher(S, *c) for c in configs], ns, max(2 * ns, 74), warm_ms=25.0)
+    best = min(range(len(configs)), key=lambda k: sweep[k]["mean"])
+    bl, bw, bn = configs[best]
+    sl = sweep[best]
+    big = time_kernels(torch, [lambda i: probe.qmm_peak_read(base, size, sink, bl, bw, bn)], 4, 24)[0]
     by_size = {}
     for B in sorted(set(sizes)):
-        nb_ = size // B
-        b_ms, _, _ = time_batches(torch, lambda i: q.qmm_peak_read(base + (i % nb_) * B, B, sink), args.steps, nb_)
-        by_size[str(B)] = round(b_ms * 1e3, 3)
+        tb = time_kernels(torch, [launcher(B, bl, bw, bn)], size // B, max(2 * (size // B), 74), warm_ms=5.0)[0]
+        by_size[str(B)] = round(tb["mean"] * 1e3, 3)
     del buf
     mfma = []
     for wg, iters in ((512, 4000), (768, 2700)):
         out = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
-        q.qmm_peak_mfma_i8(out, wg, iters)
+        probe.qmm_peak_mfma_i8(out, wg, iters)
         torch.cuda.synchronize()
         if not bool((out == 2048 * iters).all()):
             raise RuntimeError("int8 MFMA probe returned wrong sums")
-        ms, _, _ = time_batches(torch, lambda i: q.qmm_peak_mfma_i8(out, wg, iters), 8, 2)
+        tm = time_kernels(torch, [lambda i: probe.qmm_peak_mfma_i8(out, wg, iters)], 2, 8)[0]
         ops = wg * 4 * 4 * iters * 2.0 * 32 * 32 * 32
-        mfma.append((ops / (ms * 1e-3) / 1e12, wg * 4 // 1024, ms))   # 4 waves per workgroup, 1024 SIMDs
+        mfma.append((ops / (tm["mean"] * 1e-3) / 1e12, wg * 4 // 1024, tm["mean"]))   # 4 waves per workgroup, 1024 SIMDs
     tops, waves, mms = max(mfma)
-    res = {"hbm_read_1GiB_gbs": round(size / (big_ms * 1e-3) / 1e9, 1),
-           "hbm_read_28MB_gbs": round(S / (sl_ms * 1e-3) / 1e9, 1),
-           "hbm_read_28MB_us_mean": round(sl_ms * 1e3, 3), "hbm_read_28MB_us_best_batch": round(sl_min * 1e3, 3),
+    res = {"hbm_read_1GiB_gbs": round(size / (big["mean"] * 1e-3) / 1e9, 1),
+           "hbm_read_28MB_gbs": round(S / (sl["mean"] * 1e-3) / 1e9, 1),
+           "hbm_read_28MB_us": us(sl),
+           "hbm_read_best": {"loads_per_lane": bl, "waves_per_wg": bw, "nontemporal": bn},
+           "hbm_read_28MB_sweep_us": {f"lpl{c[0]}_w{c[1]}_{'nt' if c[2] else 'plain'}": round(t["mean"] * 1e3, 3)
+                                      for c, t in zip(configs, sweep)},
            "hbm_read_us_by_bytes": by_size,
            "int8_mfma_tops": round(tops, 1), "int8_mfma_waves_per_simd": waves,
-           "kernels": ["qmm::k_peak_read", "qmm::k_peak_mfma_i8"]}
+           "kernels": ["qmm::k_probe_read", "qmm::k_peak_mfma_i8"]}
     log(f"peaks: read 1 GiB {res['hbm_read_1GiB_gbs']} GB/s, 28 MB passes {res['hbm_read_28MB_gbs']} GB/s "
-        f"({sl_ms * 1e3:.2f} us), int8 MFMA {tops:.0f} TOPS at {waves} waves/SIMD")
+        f"({sl['mean'] * 1e3:.2f} us, best of {len(configs)}: {bl} loads/lane, {bw} waves, "
+        f"{'non-temporal' if bn else 'plain'}), int8 MFMA {tops:.0f} TOPS at {waves} waves/SIMD")
     return res
 
 
@@ -481,13 +569,13 @@ def bench_few_tokens(args, torch, q, synth):
             xq = torch.empty(M * q.row_bytes(q.ACT_FORMAT[fmt], K), dtype=torch.uint8, device="cuda")
             q.QUANTIZE_X[fmt](x, xq, M, K)
             y = torch.empty(M * N, dtype=torch.float32, device="cuda")
-            ms, ms_min, _ = time_batches(torch, lambda i: q.MATMUL[fmt](wqs[i % copies], xq, y, M, N, K),
-                                         args.steps, copies)
-            mv, _, _ = time_batches(torch, lambda i: q.MATVEC[fmt](wqs[i % copies], xq, y, N, K),
-                                    args.steps, copies)
+            tm, tv = time_kernels(torch, [lambda i: q.MATMUL[fmt](wqs[i % copies], xq, y, M, N, K),
+                                          lambda i: q.MATVEC[fmt](wqs[i % copies], xq, y, N, K)],
+                                  copies, max(2 * copies, args.steps), warm_ms=10.0)
+            ms, mv = tm["mean"], tv["mean"]
             log(f"few tokens {fmt} M={M}: {ms * 1e3:.2f} us ({M} decode launches {M * mv * 1e3:.2f} us)")
             rows.append({"format": fmt, "M": M, "N": N, "K": K, "kernel_us_mean": round(ms * 1e3, 3),
-                         "kernel_us_best_batch": round(ms_min * 1e3, 3),
+                         "kernel_us": us(tm),
                          "tops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 3),
                          "m_decode_launches_us": round(M * mv * 1e3, 3)})
         del wqs, wq0
@@ -496,8 +584,24 @@ def bench_few_tokens(args, torch, q, synth):
 
 
 def cpu_threads():
+    """Threads for the oracle: every core this process may run on, capped by
+    OMP_NUM_THREADS when the host sets it (a shared host's CPU share for this
+    job), and the host's logical CPU count beside it."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    return max(1, min(n, 16))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n), os.cpu_count()
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline_decode(args, q, synth):
@@ -506,7 +610,7 @@ def cpu_baseline_decode(args, q, synth):
     w = synth.weights(N, K, config=1)
     x = synth.activations(1, K, config=1, outlier_frac=0.01, outlier_factor=20.0)
     wq = oracle.quantize_q4_0_w(w)
-    thr = cpu_threads()
+    thr, host = cpu_threads()
     reps, t_total = 0, 0.0
     while t_total < args.cpu_seconds or reps < 1:
         t = time.perf_counter()
@@ -526,42 +630,37 @@ def cpu_baseline_decode(args, q, synth):
     per1 = t1 / reps1
     return {"value": round(wq.nbytes / per / 1e9, 3), "unit": "GB/s", "cores": thr, "kind": "oracle",
             "sample": f"full {N}x{K} decode step (quantize + matvec), {reps} repeats, {per * 1e3:.1f} ms each",
+            "host_logical_cpus": host, "cpu_model": cpu_model(),
             "single_core": {"value": round(wq.nbytes / per1 / 1e9, 3), "unit": "GB/s", "cores": 1,
                             "sample": f"the same step, {reps1} repeats, {per1 * 1e3:.1f} ms each"}}
 
 
 def cpu_baseline_prefill(args, q, synth):
+    """The whole 2048-token prefill (quantize + product) on all the threads,
+    and the scalar oracle on one core over the first 64 tokens, extrapolated
+    to 2048 (the product's cost is linear in the token count)."""
     import oracle
     M, N, K = PRE["M"], PRE["N"], PRE["K"]
     w = synth.weights(N, K, config=1)
     wq = oracle.quantize_q4_0_w(w)
-    thr = cpu_threads()
-    m = 8
-    while True:
-        x = synth.activations(m, K, config=4)
-        t = time.perf_counter()
-        xq = oracle.quantize_q8_0(x)
-        oracle.matmul("q4_0", wq, xq, m, N, K, threads=thr, want=("y",))
-        dt = time.perf_counter() - t
-        if dt * 4 > args.cpu_seconds or m >= M:
-            break
-        m = min(M, m * 4)
-    ops = 2.0 * m * N * K
-    # the scalar oracle on one core: token count grown the same way within a quarter of the budget
-    m1 = 1
-    while True:
-        x = synth.activations(m1, K, config=4)
-        t = time.perf_counter()
-        xq = oracle.quantize_q8_0(x)
-        oracle.matmul("q4_0", wq, xq, m1, N, K, threads=1, want=("y",))
-        dt1 = time.perf_counter() - t
-        if dt1 * 4 > args.cpu_seconds / 4 or m1 >= M:
-            break
-        m1 = min(M, m1 * 4)
+    thr, host = cpu_threads()
+    x = synth.activations(M, K, config=4)
+    t = time.perf_counter()
+    xq = oracle.quantize_q8_0(x)
+    oracle.matmul("q4_0", wq, xq, M, N, K, threads=thr, want=("y",))
+    dt = time.perf_counter() - t
+    m1 = 64
+    t = time.perf_counter()
+    xq1 = oracle.quantize_q8_0(x[:m1])
+    oracle.matmul("q4_0", wq, xq1, m1, N, K, threads=1, want=("y",))
+    dt1 = time.perf_counter() - t
+    ops = 2.0 * M * N * K
     return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": thr, "kind": "oracle",
-            "sample": f"first {m} of {M} tokens of the {M}x{N}x{K} prefill ({dt:.1f} s)",
+            "sample": f"all {M} tokens of the {M}x{N}x{K} prefill ({dt:.1f} s)",
+            "host_logical_cpus": host, "cpu_model": cpu_model(),
             "single_core": {"value": round(2.0 * m1 * N * K / dt1 / 1e12, 6), "unit": "TOPS", "cores": 1,
-                            "sample": f"first {m1} of {M} tokens ({dt1:.1f} s)"}}
+                            "sample": f"first {m1} of {M} tokens ({dt1:.1f} s), extrapolated to {M}: "
+                                      f"{dt1 * M / m1:.0f} s"}}
 
 
 def main():
@@ -594,6 +693,7 @@ def main():
     sizes = [N * q.row_bytes(fmt, K) for fmt, N, K, *_ in MATVEC_CONFIGS] if args.only in ("all", "configs") else []
     peaks = bench_peaks(args, torch, q, sizes)
     dec = bench_decode(args, torch, q, synth) if args.only in ("all", "decode") else None
+    small = bench_small(args, torch, q, synth) if args.only in ("all", "decode") else None
     pre = bench_prefill(args, torch, q, synth) if args.only in ("all", "prefill") else None
     cfgs = bench_matvec_configs(args, torch, q, synth) if args.only in ("all", "configs") else None
     few = bench_few_tokens(args, torch, q, synth) if args.only in ("all", "configs") else None
@@ -618,15 +718,20 @@ def main():
                     "config": {"workload": "q4_0_matvec_12288x4096", "M": 1, "N": DEC["N"], "K": DEC["K"],
                                "weight_bytes": dec["wbytes"], "weight_copies": dec["copies"],
                                "step": "quantize_matvec_q4_0 (quantize + matvec in one launch), replayed "
-                                       "from a HIP graph",
+                                       "from HIP graphs after a warm-up",
                                "hbm_frac_step": round(dec["gbs"] / HBM_PEAK_GBS, 4),
                                "ms_per_step_eager_python": round(dec["ms_step_eager"], 5),
                                "ms_per_step_two_launches": round(dec["ms_two"], 5)},
                     "roofline": dec["roofline"], "cpu_baseline": cpu_dec})
+    if small is not None:
+        out["small_and_quantizers"] = small
     if pre is not None:
         pf = {"workload": "q4_0_matmul_2048x12288x4096", "value": round(pre["tops"], 2), "unit": "TOPS",
-              "steps": args.prefill_steps, "warmup": args.prefill_warmup, "ms_per_step": round(pre["ms_step"], 4),
-              "step": "quantize_q8_0 (2048x4096) + matmul_q4_0", "roofline": pre["roofline"],
+              "steps": pre["nsteps"], "warmup": args.prefill_warmup, "ms_per_step": round(pre["ms_step"], 4),
+              "step_us": pre["step_us"],
+              "step_ge_kernel": pre["ms_step"] >= pre["roofline"]["kernel_us_mean"] * 1e-3,
+              "step": "quantize_q8_0 (2048x4096) + matmul_q4_0, graphs of 4 steps alternating with graphs of "
+                      "4 matmuls in the same rounds", "roofline": pre["roofline"],
               "q8_0_weights": pre["q8_0_weights"], "q2_k_weights": pre["q2_k_weights"],
               "q5_0_weights": pre["q5_0_weights"], "q4_1_weights": pre["q4_1_weights"],
               "q5_1_weights": pre["q5_1_weights"], "q4_k_weights": pre["q4_k_weights"],

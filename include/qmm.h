@@ -273,27 +273,6 @@ qmm_status qmm_get_rows_q5_0(const void *w, const int32_t *ids, float *out, int6
 qmm_status qmm_get_rows_q5_1(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
                              void *stream);
 
-/* ---- attainable-peak probes (measurement only) ------------------------------
- *
- * Not part of the product: they measure the ceilings that the product kernels
- * are reported against beside the published peaks.
- *
- * qmm_peak_read streams `bytes` of device memory once: workgroup b of 256
- * lanes reads bytes [8192 b, 8192 b + 8192) with 16-byte loads and writes the
- * XOR of their 32-bit words to sink[b] (for the host to check).
- *   buf   : device memory, 16-byte aligned, read only.
- *   bytes : > 0, a multiple of 16, at most 2^40.
- *   sink  : uint32 [ceil(bytes / 8192)] in device memory, 4-byte aligned, written.
- * qmm_peak_mfma_i8 runs `workgroups` workgroups of four waves, each wave four
- * independent chains of `iters` back-to-back v_mfma_i32_32x32x32_i8 on
- * register operands (2 * 32 * 32 * 32 operations each); with every operand
- * byte 1, out[t] = 2048 * iters for every lane t.
- *   out        : int32 [workgroups * 256], device memory, 16-byte aligned, written.
- *   workgroups : 1 .. 2^20.   iters : 1 .. 1,000,000 (out stays below 2^31).
- * Both return QMM_E_SHAPE for sizes outside these ranges. */
-qmm_status qmm_peak_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
-qmm_status qmm_peak_mfma_i8(int32_t *out, int64_t workgroups, int64_t iters, void *stream);
-
 #ifdef __cplusplus
 }
 #endif

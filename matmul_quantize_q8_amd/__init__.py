@@ -70,16 +70,12 @@ def lib() -> ctypes.CDLL:
         for name in ["qmm_matmul_" + f for f in WEIGHT_FORMATS]:
             getattr(L, name).argtypes = [P, P, P, I64, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
-        L.qmm_peak_read.argtypes = [P, I64, P, P]
-        L.qmm_peak_read.restype = ctypes.c_int
-        L.qmm_peak_mfma_i8.argtypes = [P, I64, I64, P]
-        L.qmm_peak_mfma_i8.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
 EXPORTS = tuple(["qmm_status_string", "qmm_abi_version", "qmm_quantize_q8_k",
-                 "qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0", "qmm_peak_read", "qmm_peak_mfma_i8"] +
+                 "qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0"] +
                 [p + f for p in ("qmm_quantize_", "qmm_matvec_", "qmm_matmul_", "qmm_get_rows_")
                  for f in WEIGHT_FORMATS])
 
@@ -251,17 +247,6 @@ qmm_get_rows_q4_1 = _get_rows("q4_1")
 qmm_get_rows_q5_0 = _get_rows("q5_0")
 qmm_get_rows_q5_1 = _get_rows("q5_1")
 
-
-
-# -- attainable-peak probes (measurement only) ------------------------------------
-def qmm_peak_read(buf, nbytes: int, sink, stream=None) -> None:
-    """Stream nbytes of the device buffer buf once; sink[b] = XOR of the words of bytes [8192 b, 8192 b + 8192)."""
-    _call("qmm_peak_read", _addr(buf), nbytes, _addr(sink), _stream(stream))
-
-
-def qmm_peak_mfma_i8(out, workgroups: int, iters: int, stream=None) -> None:
-    """workgroups x 4 waves x 4 chains of iters int8 MFMAs; out[t] = 2048 * iters."""
-    _call("qmm_peak_mfma_i8", _addr(out), workgroups, iters, _stream(stream))
 
 
 QUANTIZE_W = {f: globals()["qmm_quantize_" + f] for f in WEIGHT_FORMATS}

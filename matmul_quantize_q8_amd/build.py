@@ -1,4 +1,5 @@
-"""Build libqmm.so (all HIP kernels + the C ABI) for gfx950 with hipcc.
+"""Build libqmm.so (all HIP kernels + the C ABI) and libqmm_probe.so (the
+measurement probes) for gfx950 with hipcc.
 
 Flags: -O3; -ffp-contract=off so no multiply and add are fused unless the
 source asks for fmaf (the quantizers are bit-exact only without contraction);
@@ -28,8 +29,18 @@ FLAGS = [
 ]
 
 
+PROBE_LIB = os.path.join(HERE, "libqmm_probe.so")
+PROBE_SOURCES = ("peaks.hip",)      # the measurement probes: a library of their own
+
+
 def sources():
-    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    """The product library's sources."""
+    return sorted(f for f in glob.glob(os.path.join(HERE, "csrc", "*.hip"))
+                  if os.path.basename(f) not in PROBE_SOURCES)
+
+
+def probe_sources():
+    return [os.path.join(HERE, "csrc", f) for f in PROBE_SOURCES]
 
 
 def _filtered(text: str) -> str:
@@ -38,12 +49,19 @@ def _filtered(text: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libqmm.so (always recompiles)."""
+    """Compile every HIP source and link libqmm.so and libqmm_probe.so (always
+    recompiles)."""
+    _build(sources(), LIB, verbose)
+    _build(probe_sources(), PROBE_LIB, verbose)
+    return LIB
+
+
+def _build(srcs, lib_path: str, verbose: bool) -> None:
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
     tmpdir = tempfile.mkdtemp(prefix="qmm_build_", dir=HERE)
     try:
         jobs = []
-        for src in sources():
+        for src in srcs:
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
             cmd = [HIPCC] + FLAGS + inc + ["-c", "-o", obj, src]
             if verbose:
@@ -59,17 +77,16 @@ def build(verbose: bool = False) -> str:
             elif verbose and out.strip():
                 print(out)
         if failed:
-            raise RuntimeError("hipcc failed building libqmm.so")
-        tmp = LIB + ".tmp%d" % os.getpid()
+            raise RuntimeError("hipcc failed building " + os.path.basename(lib_path))
+        tmp = lib_path + ".tmp%d" % os.getpid()
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [obj for _, obj, _ in jobs]
         proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
         if proc.returncode != 0:
             sys.stderr.write(_filtered(proc.stdout) + "\n")
-            raise RuntimeError("hipcc failed linking libqmm.so")
-        os.replace(tmp, LIB)
+            raise RuntimeError("hipcc failed linking " + os.path.basename(lib_path))
+        os.replace(tmp, lib_path)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
-    return LIB
 
 
 if __name__ == "__main__":

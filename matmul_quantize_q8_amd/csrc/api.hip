@@ -40,8 +40,6 @@ hipError_t launch_matmul_q2_k_mfma(const void *w, const void *xq, float *y, int 
 hipError_t launch_matmul_q4_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
 hipError_t launch_matmul_q6_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st);
 int64_t matmul_k_max_blocks();
-hipError_t launch_peak_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t st);
-hipError_t launch_peak_mfma_i8(int32_t *out, int64_t workgroups, int iters, hipStream_t st);
 
 }  // namespace qmm
 
@@ -325,23 +323,6 @@ qmm_status qmm_get_rows_q5_0(const void *w, const int32_t *ids, float *out, int6
 qmm_status qmm_get_rows_q5_1(const void *w, const int32_t *ids, float *out, int64_t n_ids, int64_t N, int64_t K,
                              void *stream) {
     return get_rows(qmm::F_Q5_1, w, ids, out, n_ids, N, K, 32, qmm::kQ51Bytes, stream);
-}
-
-qmm_status qmm_peak_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
-    if (bytes <= 0 || bytes % 16 != 0 || bytes > kMaxBytes) return QMM_E_SHAPE;
-    if (!buf || !sink) return QMM_E_NULL;
-    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return QMM_E_ALIGN;
-    qmm_status s = check_device();
-    if (s != QMM_OK) return s;
-    return launched(qmm::launch_peak_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
-}
-
-qmm_status qmm_peak_mfma_i8(int32_t *out, int64_t workgroups, int64_t iters, void *stream) {
-    if (workgroups < 1 || workgroups > (int64_t(1) << 20) || iters < 1 || iters > 1000000) return QMM_E_SHAPE;
-    qmm_status s = check_ptrs({out});
-    if (s != QMM_OK) return s;
-    if ((s = check_device()) != QMM_OK) return s;
-    return launched(qmm::launch_peak_mfma_i8(out, workgroups, (int)iters, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

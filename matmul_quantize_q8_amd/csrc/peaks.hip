@@ -1,32 +1,59 @@
-// Attainable-peak probes, the measured ceilings that the product kernels are
-// compared with beside the published ones: a streaming read of a device
-// buffer (HBM, the bound of every decode kernel) and a back-to-back int8 MFMA
-// loop (the matrix cores, the bound of the prefill).  Neither computes
-// anything of the product path.
+// Attainable-peak probes (libqmm_probe.so, declared in include/qmm_probe.h):
+// the measured ceilings that the product kernels are compared with beside the
+// published ones -- a streaming read of a device buffer (HBM, the bound of
+// every decode kernel) and a back-to-back int8 MFMA loop (the matrix cores,
+// the bound of the prefill).  Neither computes anything of the product path,
+// and the product library neither contains nor calls them.
+#include <atomic>
+#include <cstring>
+
 #include "qmm_device.h"
+#include "qmm_probe.h"
 
 namespace qmm {
 
-// One pass with a full grid: workgroup b reads bytes [8192 b, 8192 b + 8192)
-// of the buffer, two 16-byte loads per lane, and stores the XOR of their
-// 32-bit words to sink[b].  No grid-stride loop (a grid sized to the buffer
-// keeps more loads in flight early in the pass) and no atomics (thousands
-// of atomic updates would serialise at the L2 and be timed instead of the
-// reads); the host can check every chunk.
-constexpr int kPeakChunk = 8192;   // bytes per workgroup
-
-__global__ __launch_bounds__(256) void k_peak_read(const uint4 *__restrict__ p, int64_t n16, uint32_t *sink) {
-    __shared__ uint32_t red[4];
-    const int64_t i = (int64_t)blockIdx.x * (kPeakChunk / 16) + threadIdx.x;
-    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
-    if (i < n16) a = p[i];
-    if (i + 256 < n16) b = p[i + 256];
-    uint32_t acc = (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w);
+// One pass over `bytes` with a full grid.  Workgroup b of NW waves covers the
+// span [S b, S b + S), S = NW * LPL * 1024; wave w of it the 1 KB chunks
+// (b NW + w) LPL .. + LPL - 1, lane l bytes [16 l, 16 l + 16) of each, all LPL
+// loads issued before any is used (LPL loads in flight per lane).  NT: the
+// loads carry the non-temporal cache policy.  sink[b] = XOR of the span's
+// 32-bit words (words past the end count as 0).  No grid-stride loop and no
+// atomics: one store per workgroup.
+template <int LPL, int NW, bool NT>
+__global__ __launch_bounds__(64 * NW) void k_probe_read(const uint4 *__restrict__ p, int64_t n16,
+                                                        uint32_t *__restrict__ sink) {
+    __shared__ uint32_t red[NW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = ((int64_t)blockIdx.x * NW + wave) * LPL * 64 + lane;   // first 16-byte granule
+    uint4 v[LPL];
+#pragma unroll
+    for (int k = 0; k < LPL; ++k) {
+        const int64_t c = c0 + 64 * k;
+        if (c < n16) {
+            if constexpr (NT) {
+                typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+                const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p + c));
+                v[k] = make_uint4(t.x, t.y, t.z, t.w);
+            } else {
+                v[k] = p[c];
+            }
+        } else {
+            v[k] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int k = 0; k < LPL; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    if (lane == 0) red[wave] = acc;
     __syncthreads();
-    if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+    if (threadIdx.x == 0) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s ^= red[w];
+        sink[blockIdx.x] = s;
+    }
 }
 
 // Four independent accumulator chains of v_mfma_i32_32x32x32_i8 per wave, the
@@ -47,18 +74,96 @@ __global__ __launch_bounds__(256) void k_peak_mfma_i8(int32_t *__restrict__ out,
     out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-hipError_t launch_peak_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t st) {
-    const int64_t n16 = bytes / 16;
-    const int64_t grid = (bytes + kPeakChunk - 1) / kPeakChunk;
-    hipLaunchKernelGGL(k_peak_read, dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint4 *>(buf), n16,
-                       sink);
+template <int LPL, int NW, bool NT>
+static hipError_t launch_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t st) {
+    const int64_t span = (int64_t)NW * LPL * 1024;
+    const int64_t grid = (bytes + span - 1) / span;
+    hipLaunchKernelGGL((k_probe_read<LPL, NW, NT>), dim3((unsigned)grid), dim3(64 * NW), 0, st,
+                       static_cast<const uint4 *>(buf), bytes / 16, sink);
     return hipGetLastError();
 }
 
-hipError_t launch_peak_mfma_i8(int32_t *out, int64_t workgroups, int iters, hipStream_t st) {
-    hipLaunchKernelGGL(k_peak_mfma_i8, dim3((unsigned)workgroups), dim3(256), 0, st, out, iters, 0x01010101,
-                       0x01010101);
-    return hipGetLastError();
+template <int LPL, bool NT>
+static hipError_t launch_read_nw(int nw, const void *buf, int64_t bytes, uint32_t *sink, hipStream_t st) {
+    switch (nw) {
+        case 4: return launch_read<LPL, 4, NT>(buf, bytes, sink, st);
+        case 8: return launch_read<LPL, 8, NT>(buf, bytes, sink, st);
+        case 16: return launch_read<LPL, 16, NT>(buf, bytes, sink, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool NT>
+static hipError_t launch_read_lpl(int lpl, int nw, const void *buf, int64_t bytes, uint32_t *sink, hipStream_t st) {
+    switch (lpl) {
+        case 1: return launch_read_nw<1, NT>(nw, buf, bytes, sink, st);
+        case 2: return launch_read_nw<2, NT>(nw, buf, bytes, sink, st);
+        case 4: return launch_read_nw<4, NT>(nw, buf, bytes, sink, st);
+        case 8: return launch_read_nw<8, NT>(nw, buf, bytes, sink, st);
+        case 16: return launch_read_nw<16, NT>(nw, buf, bytes, sink, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace qmm
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QMM_PROBE_E_DEVICE;
+    int s = g_device_state[dev].load(std::memory_order_acquire);
+    if (s == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return QMM_PROBE_E_DEVICE;
+        s = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_state[dev].store(s, std::memory_order_release);
+    }
+    return s == 1 ? QMM_PROBE_OK : QMM_PROBE_E_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? QMM_PROBE_OK : QMM_PROBE_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t qmm_probe_read_span(int loads_per_lane, int waves_per_wg) {
+    if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8 &&
+        loads_per_lane != 16)
+        return 0;
+    if (waves_per_wg != 4 && waves_per_wg != 8 && waves_per_wg != 16) return 0;
+    return (int64_t)loads_per_lane * waves_per_wg * 1024;
+}
+
+int qmm_peak_read(const void *buf, int64_t bytes, uint32_t *sink, int loads_per_lane, int waves_per_wg,
+                  int nontemporal, void *stream) {
+    const int64_t span = qmm_probe_read_span(loads_per_lane, waves_per_wg);
+    if (span == 0 || bytes <= 0 || bytes % 16 != 0 || bytes > (int64_t(1) << 40) ||
+        (bytes + span - 1) / span > 0x7fffffff)
+        return QMM_PROBE_E_SHAPE;
+    if (!buf || !sink) return QMM_PROBE_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+        return QMM_PROBE_E_ALIGN;
+    int s = check_device();
+    if (s != QMM_PROBE_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return launched(nontemporal ? qmm::launch_read_lpl<true>(loads_per_lane, waves_per_wg, buf, bytes, sink, st)
+                                : qmm::launch_read_lpl<false>(loads_per_lane, waves_per_wg, buf, bytes, sink, st));
+}
+
+int qmm_peak_mfma_i8(int32_t *out, int64_t workgroups, int64_t iters, void *stream) {
+    if (workgroups < 1 || workgroups > (int64_t(1) << 20) || iters < 1 || iters > 1000000) return QMM_PROBE_E_SHAPE;
+    if (!out) return QMM_PROBE_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(out) & 15u) != 0) return QMM_PROBE_E_ALIGN;
+    int s = check_device();
+    if (s != QMM_PROBE_OK) return s;
+    hipLaunchKernelGGL(qmm::k_peak_mfma_i8, dim3((unsigned)workgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       out, (int)iters, 0x01010101, 0x01010101);
+    return launched(hipGetLastError());
+}
+
+}  // extern "C"

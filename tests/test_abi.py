@@ -92,21 +92,64 @@ A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced
     (lambda L: L.qmm_matmul_q2_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
     (lambda L: L.qmm_matmul_q4_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
     (lambda L: L.qmm_matmul_q6_k(A, A, A, 4, 8, 256 * ((2**31 - 1) // (128 * 292) + 1), None), 1),
-    # the attainable-peak probes
-    (lambda L: L.qmm_peak_read(A, 0, A, None), 1),
-    (lambda L: L.qmm_peak_read(A, 24, A, None), 1),            # not a multiple of 16
-    (lambda L: L.qmm_peak_read(None, 32, A, None), 2),
-    (lambda L: L.qmm_peak_read(A, 32, None, None), 2),
-    (lambda L: L.qmm_peak_read(A + 8, 32, A, None), 3),
-    (lambda L: L.qmm_peak_read(A, 32, A + 2, None), 3),
+])
+def test_argument_errors_without_device(q, call, code):
+    assert call(q.lib()) == code
+
+
+# ---------------------------------------------------------------------------
+# The measurement probes: a library and header of their own (qmm_probe.h,
+# libqmm_probe.so); the product library does not export them.
+# ---------------------------------------------------------------------------
+PROBE_HEADER = os.path.join(ROOT, "include", "qmm_probe.h")
+
+
+def _probe_declared():
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def probe():
+    from matmul_quantize_q8_amd import probe
+    probe.lib()
+    return probe
+
+
+def test_probe_library_exports_its_header_and_product_does_not(q, probe):
+    plib = ctypes.CDLL(probe.LIB_PATH)
+    assert set(_probe_declared()) == set(probe.EXPORTS)
+    for n in _probe_declared():
+        assert hasattr(plib, n), n
+    prod = ctypes.CDLL(q.LIB_PATH)
+    for n in _probe_declared():
+        assert not hasattr(prod, n), n
+    assert not set(_probe_declared()) & set(_declared())
+
+
+def test_probe_read_span(probe):
+    assert probe.read_span(4, 4) == 16384
+    assert probe.read_span(16, 16) == 262144
+    assert probe.read_span(3, 4) == 0 and probe.read_span(4, 5) == 0
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda L: L.qmm_peak_read(A, 0, A, 4, 4, 1, None), 1),
+    (lambda L: L.qmm_peak_read(A, 24, A, 4, 4, 1, None), 1),            # not a multiple of 16
+    (lambda L: L.qmm_peak_read(A, 32, A, 3, 4, 1, None), 1),            # unsupported loads per lane
+    (lambda L: L.qmm_peak_read(A, 32, A, 4, 2, 0, None), 1),            # unsupported waves
+    (lambda L: L.qmm_peak_read(None, 32, A, 4, 4, 1, None), 2),
+    (lambda L: L.qmm_peak_read(A, 32, None, 4, 4, 1, None), 2),
+    (lambda L: L.qmm_peak_read(A + 8, 32, A, 4, 4, 1, None), 3),
+    (lambda L: L.qmm_peak_read(A, 32, A + 2, 4, 4, 1, None), 3),
     (lambda L: L.qmm_peak_mfma_i8(A, 0, 10, None), 1),
     (lambda L: L.qmm_peak_mfma_i8(A, 8, 1000001, None), 1),      # out would pass 2^31
     (lambda L: L.qmm_peak_mfma_i8(A, (1 << 20) + 1, 10, None), 1),
     (lambda L: L.qmm_peak_mfma_i8(None, 8, 10, None), 2),
     (lambda L: L.qmm_peak_mfma_i8(A + 4, 8, 10, None), 3),
 ])
-def test_argument_errors_without_device(q, call, code):
-    assert call(q.lib()) == code
+def test_probe_argument_errors_without_device(probe, call, code):
+    assert call(probe.lib()) == code
 
 
 def test_empty_problem_is_a_shape_error(q):

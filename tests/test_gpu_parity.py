@@ -315,10 +315,21 @@ MATMUL_CASES = [
     ("q5_0", 129, 257, 64), ("q5_0", 128, 128, 4096),
     # long rows: 1025 blocks (an odd count), 128 super-blocks
     ("q4_0", 129, 65, 32800), ("q5_1", 65, 33, 32800), ("q2_k", 65, 129, 32768), ("q6_k", 33, 65, 32768),
-    # more than 256 output tiles of 128 x 128: K in one part (the cases above
-    # with 4 blocks or more have at most 256 tiles and split K in two)
-    ("q4_0", 129, 16640, 160), ("q8_0", 130, 16512, 128), ("q5_0", 257, 8320, 224),
-    # exactly 256 tiles: the largest split launch
+    # more than 256 output tiles (128 x 128; 128 x 256 for Q2_K and Q4_K):
+    # K in one part, the kernels the 2048-token prefill runs (the cases above
+    # with 4 blocks or more have at most 256 tiles and split K in two); per
+    # format an odd block or super-block count (the last stage shifted back
+    # one block, or a last stage of one super-block) and an even one, with
+    # ragged M and N
+    ("q4_0", 129, 16640, 160), ("q4_0", 257, 16577, 256),
+    ("q8_0", 130, 16512, 128), ("q8_0", 257, 16640, 160),
+    ("q5_0", 257, 16640, 160), ("q5_0", 129, 16577, 256),
+    ("q4_1", 257, 16640, 160), ("q4_1", 129, 16577, 256),
+    ("q5_1", 257, 16640, 160), ("q5_1", 129, 16577, 256),
+    ("q2_k", 257, 33024, 768), ("q2_k", 129, 33025, 512),
+    ("q4_k", 257, 33024, 768), ("q4_k", 129, 33025, 512),
+    ("q6_k", 257, 16640, 768), ("q6_k", 129, 16577, 512),
+    # exactly 256 tiles (1 x 256): the largest launch that still splits K
     ("q5_1", 100, 32768, 128),
 ]
 
@@ -364,27 +375,21 @@ def test_matmul_matches_oracle(env, fmt, M, N, K):
     _check(y, ref["y64"], ref["mag"], (fmt, M, N, K))
 
 
-def test_matmul_prefill_full_size_sampled(env):
-    """The 2048 x 12288 x 4096 prefill, checked on 20000 sampled outputs plus
-    whole rows and columns at the tile edges."""
+def test_matmul_prefill_full_size_every_output(env):
+    """The 2048 x 12288 x 4096 prefill with the bench's weights and
+    activations, every one of its 25.2 million outputs against the oracle
+    (run on 16 host threads)."""
     torch, q, orc = env
     M, N, K = 2048, 12288, 4096
-    _say("matmul q4_0 full", M, N, K)
+    _say("matmul q4_0 full, every output", M, N, K)
     w = synth.weights(N, K, config=1)
     x = synth.activations(M, K, config=4)
     wq = orc.quantize_q4_0_w(w)
     xq = orc.quantize_q8_0(x)
     y = _run_matmul(env, "q4_0", wq, xq, M, N, K)
     assert np.isfinite(y).all()
-    rng = synth.splitmix64(77, 0, 40000)
-    mi = (rng[:20000] % np.uint64(M)).astype(np.int64)
-    ni = (rng[20000:] % np.uint64(N)).astype(np.int64)
-    edge_m = np.array([0, 1, 127, 128, 1919, 2047])
-    edge_n = np.array([0, 31, 32, 127, 128, 12287])
-    mi = np.concatenate([mi, np.repeat(edge_m, N // 64), np.tile(np.arange(0, M, 7), len(edge_n))])
-    ni = np.concatenate([ni, np.tile(np.arange(0, N, 64), len(edge_m)), np.repeat(edge_n, len(range(0, M, 7)))])
-    ref, mag = orc.matmul_sampled("q4_0", wq, xq, mi, ni, K)
-    _check(y[mi, ni], ref, mag, "prefill sampled")
+    ref = orc.matmul("q4_0", wq, xq, M, N, K, threads=16, want=("y64", "mag"))
+    _check(y, ref["y64"], ref["mag"], "prefill, every output")
 
 
 def test_matmul_q8_0_full_size_sampled(env):
@@ -589,19 +594,23 @@ def test_products_on_degenerate_inputs(env, fmt):
         _check(yv, ref["y64"][m], ref["mag"][m], (fmt, "matvec", m))
 
 
-def test_matmul_rows_equal_matvec(env):
+@pytest.mark.parametrize("M,N,K", [(40, 300, 2048), (40, 33000, 1024)])
+def test_matmul_rows_equal_matvec(env, M, N, K):
     """Row m of the prefill product and the decode product of token m are two
-    evaluations of the same outputs: both within the bound of the oracle."""
+    evaluations of the same outputs, each within the bound of the oracle.  M
+    is past the few-token switch, so the rows come from the MFMA kernels: K
+    split in two at N = 300 (3 tiles), in one part at N = 33000 (258 tiles)."""
     torch, q, orc = env
-    M, N, K = 6, 300, 2048
-    wq, xq = _inputs("q4_0", M, N, K, 7000)
+    _say("matmul rows vs matvec", M, N, K)
+    wq, xq = _inputs("q4_0", M, N, K, 7000 + N)
     ref = orc.matmul("q4_0", wq, xq, M, N, K, threads=8, want=("y64", "mag"))
     y = _run_matmul(env, "q4_0", wq, xq, M, N, K)
     xr = xq.reshape(M, -1)
     for m in range(M):
         yv = _run_matvec(env, "q4_0", wq, xr[m], N, K)
         _check(yv, ref["y64"][m], ref["mag"][m], ("matvec row", m))
-        _check(y[m], ref["y64"][m], 2 * ref["mag"][m], ("matmul row", m))
+        _check(y[m], ref["y64"][m], ref["mag"][m], ("matmul row", m))
+        # two values within TOL * mag of the exact one differ by at most twice that
         assert np.all(np.abs(y[m].astype(np.float64) - yv) <= 2 * TOL * ref["mag"][m])
 
 
@@ -664,32 +673,37 @@ def test_split_k_matmul_overwrites_and_is_deterministic(env, fmt):
     _check(first.cpu().numpy(), ref["y64"], ref["mag"], (fmt, M, N, K))
 
 
+@pytest.mark.parametrize("lpl,nw,nt", [(1, 4, 0), (4, 4, 1), (16, 8, 1), (2, 16, 0), (8, 16, 1)])
 @pytest.mark.parametrize("nbytes", [16, 4096, 16 * 1025, 1 << 20, (28311552 // 16 + 3) * 16])
-def test_peak_read_probe_reads_every_word(env, nbytes):
-    """The streaming-read probe XORs every 32-bit word of the buffer (one
-    grid-stride pass, ragged tails included)."""
+def test_peak_read_probe_reads_every_word(env, nbytes, lpl, nw, nt):
+    """The streaming-read probe XORs every 32-bit word of the buffer, each
+    workgroup its own span, ragged tails included, and writes nothing past
+    its last workgroup."""
+    from matmul_quantize_q8_amd import probe
     torch, q, _ = env
-    _say("peak_read", nbytes)
+    _say("peak_read", nbytes, lpl, nw, nt)
     words = synth.splitmix64(101, 0, nbytes // 4).astype(np.uint32)
     buf = _dev(torch, words.view(np.int32))
-    nchunk = -(-nbytes // 8192)
+    span = probe.read_span(lpl, nw)
+    nchunk = -(-nbytes // span)
     sink = torch.full((nchunk + 1,), -1, dtype=torch.int32, device="cuda")
-    q.qmm_peak_read(buf, nbytes, sink)
+    probe.qmm_peak_read(buf, nbytes, sink, lpl, nw, bool(nt))
     torch.cuda.synchronize()
     got = sink.cpu().numpy().view(np.uint32)
-    padded = np.zeros(nchunk * 2048, dtype=np.uint32)
+    padded = np.zeros(nchunk * (span // 4), dtype=np.uint32)
     padded[:words.size] = words
-    assert np.array_equal(got[:nchunk], np.bitwise_xor.reduce(padded.reshape(nchunk, 2048), axis=1))
-    assert got[nchunk] == 0xFFFFFFFF   # nothing written past the last chunk
+    assert np.array_equal(got[:nchunk], np.bitwise_xor.reduce(padded.reshape(nchunk, span // 4), axis=1))
+    assert got[nchunk] == 0xFFFFFFFF   # nothing written past the last workgroup
 
 
 @pytest.mark.parametrize("wg,iters", [(1, 1), (3, 17), (512, 100)])
 def test_peak_mfma_probe_sums(env, wg, iters):
     """Every lane of the int8 MFMA probe ends with 4 chains x 16 results x 32 x iters."""
+    from matmul_quantize_q8_amd import probe
     torch, q, _ = env
     _say("peak_mfma", wg, iters)
     out = torch.full((wg * 256,), -1, dtype=torch.int32, device="cuda")
-    q.qmm_peak_mfma_i8(out, wg, iters)
+    probe.qmm_peak_mfma_i8(out, wg, iters)
     torch.cuda.synchronize()
     assert bool((out == 2048 * iters).all())
 

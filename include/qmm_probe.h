@@ -6,10 +6,12 @@
  * beside them, against ceilings measured on the same part with these
  * probes: a streaming read of device memory (the bound of every decode
  * product, which streams its weights once per token -- minfer section 2.1,
- * "The bandwidth argument") and a loop of back-to-back int8 MFMAs (the bound
+ * "The bandwidth argument"), a loop of back-to-back int8 MFMAs (the bound
  * of the prefill product, a dense contraction once weights are reused across
- * tokens -- kvad "Batched prefill, and i8mm").  Nothing here computes any
- * part of the quantized products.
+ * tokens -- kvad "Batched prefill, and i8mm"), and an issue-rate loop of f32
+ * FMAs and int8 MFMAs (the prefill's per-block scale fold runs on the vector
+ * ALU beside the MFMAs).  Nothing here computes any part of the quantized
+ * products.
  *
  * Conventions as in qmm.h: device pointers on the current HIP device, a
  * hipStream_t passed as void* (NULL = the null stream), asynchronous work,
@@ -49,6 +51,21 @@ int64_t qmm_probe_read_span(int loads_per_lane, int waves_per_wg);
  *   sink  : uint32 [ceil(bytes / S)], device memory, 4-byte aligned, written. */
 int qmm_peak_read(const void *buf, int64_t bytes, uint32_t *sink, int loads_per_lane, int waves_per_wg,
                   int nontemporal, void *stream);
+
+/* Issue-rate loop: 256 workgroups of 4 * waves_per_simd waves (one workgroup
+ * per CU, so waves_per_simd waves on every SIMD), each wave `iters`
+ * iterations of
+ *   mode 0: 128 v_fma_f32 (16 independent chains c = c * 0.9999 + 1.0001),
+ *   mode 1: 4 v_mfma_i32_32x32x32_i8 (4 independent accumulators),
+ *   mode 2: both, 32 of the FMAs after each MFMA.
+ * Timing the three modes gives the cost of an FMA and of an MFMA per SIMD and
+ * how much of an MFMA's time the vector ALU keeps for FMAs issued beside it.
+ *   out  : float [256 * 256 * waves_per_simd], device memory, 4-byte aligned,
+ *          written with each lane's sum of its chains (finite).
+ *   outi : int32 [same count], device memory, 4-byte aligned, written:
+ *          2048 * iters in modes 1 and 2, 0 in mode 0.
+ *   mode 0..2, waves_per_simd 1 or 2, iters 1 .. 1,000,000. */
+int qmm_probe_issue(int mode, int waves_per_simd, int64_t iters, float *out, int32_t *outi, void *stream);
 
 /* `workgroups` workgroups of four waves, each wave four independent chains of
  * `iters` back-to-back v_mfma_i32_32x32x32_i8 on register operands

@@ -1,9 +1,11 @@
 // Attainable-peak probes (libqmm_probe.so, declared in include/qmm_probe.h):
 // the measured ceilings that the product kernels are compared with beside the
 // published ones -- a streaming read of a device buffer (HBM, the bound of
-// every decode kernel) and a back-to-back int8 MFMA loop (the matrix cores,
-// the bound of the prefill).  Neither computes anything of the product path,
-// and the product library neither contains nor calls them.
+// every decode kernel), a back-to-back int8 MFMA loop (the matrix cores) and
+// an issue-rate loop of f32 FMAs, int8 MFMAs or both interleaved (what bounds
+// a prefill whose per-block scale fold runs on the vector ALU).  None computes
+// anything of the product path, and the product library neither contains nor
+// calls them.
 #include <atomic>
 #include <cstring>
 
@@ -72,6 +74,65 @@ __global__ __launch_bounds__(256) void k_peak_mfma_i8(int32_t *__restrict__ out,
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
     out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// Issue-rate loop, WPS waves per SIMD (workgroups of 4 * WPS waves, one per
+// CU).  Per iteration and wave: MODE 0 issues 128 v_fma_f32 (16 independent
+// chains c = c * b + a), MODE 1 four v_mfma_i32_32x32x32_i8 (four
+// independent accumulators), MODE 2 both, 32 FMAs after each MFMA.  With
+// every MFMA operand byte 1, outi = 2048 * iters for MODES 1 and 2 (0 for
+// MODE 0); out holds the FMA chains' sum (finite for a in (0, 2), b in (0, 1)).
+template <int MODE, int WPS>
+__global__ __launch_bounds__(256 * WPS) void k_probe_issue(float *__restrict__ out, int32_t *__restrict__ outi,
+                                                           int iters, float a, float b, int ones) {
+    const v4i va = {ones, ones, ones, ones};
+    v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    float c[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[r] = a + (float)r;
+    auto fmas = [&]() {
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c[r] = fmaf(c[r], b, a);
+    };
+    for (int i = 0; i < iters; ++i) {
+        if constexpr (MODE != 0) c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c0, 0, 0, 0);
+        if constexpr (MODE != 1) fmas();
+        if constexpr (MODE != 0) c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c1, 0, 0, 0);
+        if constexpr (MODE != 1) fmas();
+        if constexpr (MODE != 0) c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c2, 0, 0, 0);
+        if constexpr (MODE != 1) fmas();
+        if constexpr (MODE != 0) c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c3, 0, 0, 0);
+        if constexpr (MODE != 1) fmas();
+    }
+    int si = 0;
+    float sf = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        si += c0[r] + c1[r] + c2[r] + c3[r];
+        sf += c[r];
+    }
+    const int64_t t = (int64_t)blockIdx.x * (256 * WPS) + threadIdx.x;
+    out[t] = sf;
+    outi[t] = si;
+}
+
+template <int MODE, int WPS>
+static hipError_t launch_issue(float *out, int32_t *outi, int iters, hipStream_t st) {
+    hipLaunchKernelGGL((k_probe_issue<MODE, WPS>), dim3(256), dim3(256 * WPS), 0, st, out, outi, iters, 1.0001f,
+                       0.9999f, 0x01010101);
+    return hipGetLastError();
+}
+
+template <int WPS>
+static hipError_t launch_issue_mode(int mode, float *out, int32_t *outi, int iters, hipStream_t st) {
+    switch (mode) {
+        case 0: return launch_issue<0, WPS>(out, outi, iters, st);
+        case 1: return launch_issue<1, WPS>(out, outi, iters, st);
+        case 2: return launch_issue<2, WPS>(out, outi, iters, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int LPL, int NW, bool NT>
@@ -153,6 +214,19 @@ int qmm_peak_read(const void *buf, int64_t bytes, uint32_t *sink, int loads_per_
     hipStream_t st = static_cast<hipStream_t>(stream);
     return launched(nontemporal ? qmm::launch_read_lpl<true>(loads_per_lane, waves_per_wg, buf, bytes, sink, st)
                                 : qmm::launch_read_lpl<false>(loads_per_lane, waves_per_wg, buf, bytes, sink, st));
+}
+
+int qmm_probe_issue(int mode, int waves_per_simd, int64_t iters, float *out, int32_t *outi, void *stream) {
+    if (mode < 0 || mode > 2 || (waves_per_simd != 1 && waves_per_simd != 2) || iters < 1 || iters > 1000000)
+        return QMM_PROBE_E_SHAPE;
+    if (!out || !outi) return QMM_PROBE_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0 || (reinterpret_cast<uintptr_t>(outi) & 3u) != 0)
+        return QMM_PROBE_E_ALIGN;
+    int s = check_device();
+    if (s != QMM_PROBE_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return launched(waves_per_simd == 1 ? qmm::launch_issue_mode<1>(mode, out, outi, (int)iters, st)
+                                        : qmm::launch_issue_mode<2>(mode, out, outi, (int)iters, st));
 }
 
 int qmm_peak_mfma_i8(int32_t *out, int64_t workgroups, int64_t iters, void *stream) {

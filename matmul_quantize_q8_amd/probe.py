@@ -10,7 +10,7 @@ from . import QmmError, _addr, _stream
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmm_probe.so")
-EXPORTS = ("qmm_probe_read_span", "qmm_peak_read", "qmm_peak_mfma_i8")
+EXPORTS = ("qmm_probe_read_span", "qmm_peak_read", "qmm_peak_mfma_i8", "qmm_probe_issue")
 LOADS_PER_LANE = (1, 2, 4, 8, 16)
 WAVES_PER_WG = (4, 8, 16)
 _STATUS = {0: "QMM_PROBE_OK", 1: "QMM_PROBE_E_SHAPE", 2: "QMM_PROBE_E_NULL", 3: "QMM_PROBE_E_ALIGN",
@@ -31,6 +31,8 @@ def lib() -> ctypes.CDLL:
         L.qmm_peak_read.restype = I32
         L.qmm_peak_mfma_i8.argtypes = [P, I64, I64, P]
         L.qmm_peak_mfma_i8.restype = I32
+        L.qmm_probe_issue.argtypes = [I32, I32, I64, P, P, P]
+        L.qmm_probe_issue.restype = I32
         _lib = L
     return _lib
 
@@ -55,3 +57,14 @@ def qmm_peak_read(buf, nbytes: int, sink, loads_per_lane: int = 4, waves_per_wg:
 def qmm_peak_mfma_i8(out, workgroups: int, iters: int, stream=None) -> None:
     """workgroups x 4 waves x 4 chains of iters int8 MFMAs; out[t] = 2048 * iters."""
     _check("qmm_peak_mfma_i8", lib().qmm_peak_mfma_i8(_addr(out), workgroups, iters, _stream(stream)))
+
+
+ISSUE_MODES = {"fma": 0, "mfma": 1, "mixed": 2}
+
+
+def qmm_probe_issue(mode: str, waves_per_simd: int, iters: int, out, outi, stream=None) -> None:
+    """Issue-rate loop on every SIMD: per wave and iteration 128 f32 FMAs
+    ("fma"), 4 int8 MFMAs ("mfma") or both interleaved ("mixed"); outi[t] =
+    2048 * iters when MFMAs run."""
+    _check("qmm_probe_issue", lib().qmm_probe_issue(ISSUE_MODES[mode], waves_per_simd, iters, _addr(out), _addr(outi),
+                                                    _stream(stream)))

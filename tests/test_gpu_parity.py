@@ -708,6 +708,23 @@ def test_peak_mfma_probe_sums(env, wg, iters):
     assert bool((out == 2048 * iters).all())
 
 
+@pytest.mark.parametrize("mode,wps", [("fma", 1), ("mfma", 2), ("mixed", 2)])
+def test_issue_probe_results(env, mode, wps):
+    """The issue-rate probe runs every iteration: 2048 * iters per lane when
+    MFMAs run, 0 otherwise; the FMA chains' sums are finite."""
+    from matmul_quantize_q8_amd import probe
+    torch, q, _ = env
+    iters = 37
+    _say("probe_issue", mode, wps, iters)
+    n = 256 * 256 * wps
+    out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    outi = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    probe.qmm_probe_issue(mode, wps, iters, out, outi)
+    torch.cuda.synchronize()
+    assert bool((outi == (0 if mode == "fma" else 2048 * iters)).all())
+    assert bool(torch.isfinite(out).all())
+
+
 def test_device_errors_are_reported(env):
     torch, q, _ = env
     buf = torch.zeros(4096, dtype=torch.uint8, device="cuda")

@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--only", choices=["all", "decode", "prefill", "configs"], default="all")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of each oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-peaks", action="store_true",
+                    help="leave out the attainable-peak probes (for counter runs of the product kernels)")
     ap.add_argument("--copies-mb", type=float, default=600.0, help="total size of the rotated weight copies")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one plain 256 MiB device-to-device copy (scales HBM byte counters)")
@@ -718,7 +720,7 @@ def main():
         return
 
     sizes = [N * q.row_bytes(fmt, K) for fmt, N, K, *_ in MATVEC_CONFIGS] if args.only in ("all", "configs") else []
-    peaks = bench_peaks(args, torch, q, sizes)
+    peaks = None if args.skip_peaks else bench_peaks(args, torch, q, sizes)
     dec = bench_decode(args, torch, q, synth) if args.only in ("all", "decode") else None
     small = bench_small(args, torch, q, synth) if args.only in ("all", "decode") else None
     pre = bench_prefill(args, torch, q, synth) if args.only in ("all", "prefill") else None
@@ -735,9 +737,9 @@ def main():
 
     out = {"metric": METRIC, "n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "int8", "data": "synthetic"}
-    if dec is not None:
+    if dec is not None and peaks is not None:
         dec["roofline"]["frac_of_attainable"] = round(dec["roofline"]["achieved"] / peaks["hbm_read_28MB_gbs"], 4)
-    if pre is not None:
+    if pre is not None and peaks is not None:
         pre["roofline"]["frac_of_attainable"] = round(pre["roofline"]["achieved"] / peaks["int8_mfma_tops"], 4)
     if dec is not None:
         out.update({"value": round(dec["gbs"], 1), "unit": "GB/s", "steps": dec["nsteps"], "warmup": args.warmup,
@@ -771,14 +773,15 @@ def main():
             out["prefill"] = pf
     if cfgs is not None:
         for r in cfgs["rows"]:
-            att = peaks["hbm_read_us_by_bytes"].get(str(r.get("weight_bytes")))
+            att = peaks["hbm_read_us_by_bytes"].get(str(r.get("weight_bytes"))) if peaks is not None else None
             if att is not None:
                 r["attainable_read_us"] = att
                 r["frac_of_attainable"] = round(att / r["kernel_us_mean"], 4)
         out["matvec_configs"] = cfgs
     if few is not None:
         out["few_tokens"] = few
-    out["attainable"] = peaks
+    if peaks is not None:
+        out["attainable"] = peaks
     print(json.dumps(out), flush=True)
 
 

@@ -17,10 +17,13 @@ Also in the line: the other decode workloads (the Q8_0 matrices of one
 each; the prefill matmul (M = 2048, same weights), int8 TOP/s;
 for each, the dominant kernel's roofline (achieved / MI355X peak, with the
 average kernel time from HIP events on the launch stream around graph
-replays of batches of back-to-back launches of that kernel) and the oracle timed on the host cores
-over a bounded sample of the same workload.  `attainable` holds the measured
-ceilings (a streaming read, at 1 GiB and at the decode's 28.3 MB, and an int8
-MFMA loop); each roofline also gives its fraction of the matching one.
+replays of batches of back-to-back launches of that kernel, warmed up and
+alternated with the kernels it is compared with) and the oracle timed on the
+host cores over a bounded sample of the same workload.  `attainable` holds
+the measured ceilings of the probe library (a streaming read in 24 launch
+shapes, at the decode's 28.3 MB, at 1 GiB and at every decode weight size;
+an int8 MFMA loop; an issue-rate loop of f32 FMAs and int8 MFMAs); each
+roofline also gives its fraction of the matching one.
 
 Synthetic data: seeded Gaussian weights (std 0.02) and activations (std 1,
 1% outliers x20 for decode), quantized on the GPU by the library.

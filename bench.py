@@ -504,9 +504,10 @@ def bench_peaks(args, torch, q, sizes=()):
     the fastest is the attainable 28 MB read, and the same configuration
     gives a 1 GiB pass and a pass of every other decode workload's weight
     size in `sizes`.  MFMA: back-to-back int8 MFMAs on register operands at
-    two and three waves per SIMD.  Issue: f32 FMAs, int8 MFMAs and both
-    interleaved at two waves per SIMD, giving the vector-ALU cost of an FMA
-    and the share of an MFMA's time that FMAs issued beside it can use."""
+    two and three waves per SIMD.  Issue: f32 FMAs (vector-register operands,
+    as in the prefill folds), int8 MFMAs, both interleaved, and the FMAs with a
+    scalar operand, at two waves per SIMD: the vector-ALU cost of an FMA and
+    the FMA issue time an MFMA takes when both run."""
     from matmul_quantize_q8_amd import probe
     size = 1 << 30
     buf = torch.arange(size // 4, dtype=torch.int32, device="cuda")
@@ -543,23 +544,26 @@ def bench_peaks(args, torch, q, sizes=()):
         mfma.append((ops / (tm["mean"] * 1e-3) / 1e12, wg * 4 // 1024, tm["mean"]))   # 4 waves per workgroup, 1024 SIMDs
     tops, waves, mms = max(mfma)
     # issue rates at two waves per SIMD (the prefill kernels' occupancy): f32
-    # FMAs alone, int8 MFMAs alone, both interleaved; clocks at 2.4 GHz
+    # FMAs with vector-register operands (the folds' form) alone, int8 MFMAs
+    # alone, both interleaved, and the FMAs with one scalar operand; clocks at
+    # 2.4 GHz
     it, wps = 2000, 2
     n = 256 * 256 * wps
     fo = torch.empty(n, dtype=torch.float32, device="cuda")
     io = torch.empty(n, dtype=torch.int32, device="cuda")
-    for mode in ("fma", "mfma", "mixed"):
+    modes = ("fma", "mfma", "mixed", "fma_sgpr")
+    for mode in modes:
         probe.qmm_probe_issue(mode, wps, it, fo, io)
         torch.cuda.synchronize()
-        if not bool((io == (0 if mode == "fma" else 2048 * it)).all()) or not bool(torch.isfinite(fo).all()):
+        if not bool((io == (0 if mode.startswith("fma") else 2048 * it)).all()) or not bool(torch.isfinite(fo).all()):
             raise RuntimeError(f"issue probe ({mode}) returned wrong results")
-    ti = time_kernels(torch, [lambda i, m=m: probe.qmm_probe_issue(m, wps, it, fo, io) for m in ("fma", "mfma", "mixed")],
-                      2, 8)
-    t_fma, t_mfma, t_mix = (t["mean"] * 1e-3 for t in ti)
+    ti = time_kernels(torch, [lambda i, m=m: probe.qmm_probe_issue(m, wps, it, fo, io) for m in modes], 2, 8)
+    t_fma, t_mfma, t_mix, t_sg = (t["mean"] * 1e-3 for t in ti)
     n_fma, n_mfma = wps * it * 128, wps * it * 4          # per SIMD
-    issue = {"waves_per_simd": wps, "iters": it, "us": {"fma": round(t_fma * 1e6, 2), "mfma": round(t_mfma * 1e6, 2),
-                                                         "mixed": round(t_mix * 1e6, 2)},
-             "clk_per_fma": round(t_fma * 2.4e9 / n_fma, 3), "clk_per_mfma": round(t_mfma * 2.4e9 / n_mfma, 2),
+    issue = {"waves_per_simd": wps, "iters": it,
+             "us": {m: round(t * 1e6, 2) for m, t in zip(modes, (t_fma, t_mfma, t_mix, t_sg))},
+             "clk_per_fma": round(t_fma * 2.4e9 / n_fma, 3), "clk_per_fma_sgpr_operand": round(t_sg * 2.4e9 / n_fma, 3),
+             "clk_per_mfma": round(t_mfma * 2.4e9 / n_mfma, 2),
              "fma_clk_taken_per_mfma_when_mixed": round((t_mix - t_fma) * 2.4e9 / n_mfma, 2),
              "mfma_time_hidden_frac": round(1.0 - (t_mix - t_fma) / t_mfma, 3),
              "clock_assumed_ghz": 2.4}
@@ -577,7 +581,8 @@ def bench_peaks(args, torch, q, sizes=()):
     log(f"peaks: read 1 GiB {res['hbm_read_1GiB_gbs']} GB/s, 28 MB passes {res['hbm_read_28MB_gbs']} GB/s "
         f"({sl['mean'] * 1e3:.2f} us, best of {len(configs)}: {bl} loads/lane, {bw} waves, "
         f"{'non-temporal' if bn else 'plain'}), int8 MFMA {tops:.0f} TOPS at {waves} waves/SIMD; "
-        f"issue: {issue['clk_per_fma']} clk/FMA, {issue['clk_per_mfma']} clk/MFMA, mixed: "
+        f"issue: {issue['clk_per_fma']} clk/FMA ({issue['clk_per_fma_sgpr_operand']} with a scalar operand), "
+        f"{issue['clk_per_mfma']} clk/MFMA, mixed: "
         f"{issue['fma_clk_taken_per_mfma_when_mixed']} FMA clk per MFMA")
     return res
 

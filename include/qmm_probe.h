@@ -55,16 +55,19 @@ int qmm_peak_read(const void *buf, int64_t bytes, uint32_t *sink, int loads_per_
 /* Issue-rate loop: 256 workgroups of 4 * waves_per_simd waves (one workgroup
  * per CU, so waves_per_simd waves on every SIMD), each wave `iters`
  * iterations of
- *   mode 0: 128 v_fma_f32 (16 independent chains c = c * 0.9999 + 1.0001),
+ *   mode 0: 128 v_fma_f32 with vector-register operands (16 independent
+ *           chains c = c * 0.9999 + 1.0001),
  *   mode 1: 4 v_mfma_i32_32x32x32_i8 (4 independent accumulators),
- *   mode 2: both, 32 of the FMAs after each MFMA.
- * Timing the three modes gives the cost of an FMA and of an MFMA per SIMD and
- * how much of an MFMA's time the vector ALU keeps for FMAs issued beside it.
+ *   mode 2: both, 32 of the FMAs after each MFMA,
+ *   mode 3: mode 0's FMAs with one operand in a scalar register.
+ * Timing the modes gives the cost of an FMA and of an MFMA per SIMD, how
+ * much FMA issue time an MFMA takes when both run, and what a scalar operand
+ * costs an FMA.
  *   out  : float [256 * 256 * waves_per_simd], device memory, 4-byte aligned,
  *          written with each lane's sum of its chains (finite).
  *   outi : int32 [same count], device memory, 4-byte aligned, written:
  *          2048 * iters in modes 1 and 2, 0 in mode 0.
- *   mode 0..2, waves_per_simd 1 or 2, iters 1 .. 1,000,000. */
+ *   mode 0..3, waves_per_simd 1 or 2, iters 1 .. 1,000,000. */
 int qmm_probe_issue(int mode, int waves_per_simd, int64_t iters, float *out, int32_t *outi, void *stream);
 
 /* `workgroups` workgroups of four waves, each wave four independent chains of

@@ -77,33 +77,40 @@ __global__ __launch_bounds__(256) void k_peak_mfma_i8(int32_t *__restrict__ out,
 }
 
 // Issue-rate loop, WPS waves per SIMD (workgroups of 4 * WPS waves, one per
-// CU).  Per iteration and wave: MODE 0 issues 128 v_fma_f32 (16 independent
-// chains c = c * b + a), MODE 1 four v_mfma_i32_32x32x32_i8 (four
-// independent accumulators), MODE 2 both, 32 FMAs after each MFMA.  With
-// every MFMA operand byte 1, outi = 2048 * iters for MODES 1 and 2 (0 for
-// MODE 0); out holds the FMA chains' sum (finite for a in (0, 2), b in (0, 1)).
+// CU).  Per iteration and wave: MODE 0 issues 128 v_fma_f32 whose operands
+// are all vector registers (16 independent chains c = c * b + a), MODE 1 four
+// v_mfma_i32_32x32x32_i8 (four independent accumulators), MODE 2 both, 32
+// FMAs after each MFMA, MODE 3 the FMAs of MODE 0 with b read from a scalar
+// register (the form a kernel argument takes).  The prefill folds use the
+// vector-register form; the scalar-operand form issues at about half its rate
+// with two waves per SIMD (it is not issued two at a time).  With every MFMA
+// operand byte 1, outi = 2048 * iters for MODES 1 and 2 (0 otherwise); out
+// holds the FMA chains' sum (finite for a in (0, 2), b in (0, 1)).
 template <int MODE, int WPS>
 __global__ __launch_bounds__(256 * WPS) void k_probe_issue(float *__restrict__ out, int32_t *__restrict__ outi,
                                                            int iters, float a, float b, int ones) {
     const v4i va = {ones, ones, ones, ones};
     v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    // per-lane copies of a and b: vector registers, the fold's operand form
+    float av = a + 0.0f * (float)threadIdx.x, bv = b + 0.0f * (float)threadIdx.x;
+    asm volatile("" : "+v"(av), "+v"(bv));
     float c[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) c[r] = a + (float)r;
+    for (int r = 0; r < 16; ++r) c[r] = av + (float)r;
     auto fmas = [&]() {
 #pragma unroll
         for (int k = 0; k < 2; ++k)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) c[r] = fmaf(c[r], b, a);
+            for (int r = 0; r < 16; ++r) c[r] = fmaf(c[r], MODE == 3 ? b : bv, av);
     };
     for (int i = 0; i < iters; ++i) {
-        if constexpr (MODE != 0) c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c0, 0, 0, 0);
+        if constexpr (MODE == 1 || MODE == 2) c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c0, 0, 0, 0);
         if constexpr (MODE != 1) fmas();
-        if constexpr (MODE != 0) c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c1, 0, 0, 0);
+        if constexpr (MODE == 1 || MODE == 2) c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c1, 0, 0, 0);
         if constexpr (MODE != 1) fmas();
-        if constexpr (MODE != 0) c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c2, 0, 0, 0);
+        if constexpr (MODE == 1 || MODE == 2) c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c2, 0, 0, 0);
         if constexpr (MODE != 1) fmas();
-        if constexpr (MODE != 0) c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c3, 0, 0, 0);
+        if constexpr (MODE == 1 || MODE == 2) c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, va, c3, 0, 0, 0);
         if constexpr (MODE != 1) fmas();
     }
     int si = 0;
@@ -131,6 +138,7 @@ static hipError_t launch_issue_mode(int mode, float *out, int32_t *outi, int ite
         case 0: return launch_issue<0, WPS>(out, outi, iters, st);
         case 1: return launch_issue<1, WPS>(out, outi, iters, st);
         case 2: return launch_issue<2, WPS>(out, outi, iters, st);
+        case 3: return launch_issue<3, WPS>(out, outi, iters, st);
     }
     return hipErrorInvalidValue;
 }
@@ -217,7 +225,7 @@ int qmm_peak_read(const void *buf, int64_t bytes, uint32_t *sink, int loads_per_
 }
 
 int qmm_probe_issue(int mode, int waves_per_simd, int64_t iters, float *out, int32_t *outi, void *stream) {
-    if (mode < 0 || mode > 2 || (waves_per_simd != 1 && waves_per_simd != 2) || iters < 1 || iters > 1000000)
+    if (mode < 0 || mode > 3 || (waves_per_simd != 1 && waves_per_simd != 2) || iters < 1 || iters > 1000000)
         return QMM_PROBE_E_SHAPE;
     if (!out || !outi) return QMM_PROBE_E_NULL;
     if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0 || (reinterpret_cast<uintptr_t>(outi) & 3u) != 0)

@@ -59,12 +59,13 @@ def qmm_peak_mfma_i8(out, workgroups: int, iters: int, stream=None) -> None:
     _check("qmm_peak_mfma_i8", lib().qmm_peak_mfma_i8(_addr(out), workgroups, iters, _stream(stream)))
 
 
-ISSUE_MODES = {"fma": 0, "mfma": 1, "mixed": 2}
+ISSUE_MODES = {"fma": 0, "mfma": 1, "mixed": 2, "fma_sgpr": 3}
 
 
 def qmm_probe_issue(mode: str, waves_per_simd: int, iters: int, out, outi, stream=None) -> None:
-    """Issue-rate loop on every SIMD: per wave and iteration 128 f32 FMAs
-    ("fma"), 4 int8 MFMAs ("mfma") or both interleaved ("mixed"); outi[t] =
-    2048 * iters when MFMAs run."""
+    """Issue-rate loop on every SIMD: per wave and iteration 128 f32 FMAs with
+    vector-register operands ("fma"), 4 int8 MFMAs ("mfma"), both interleaved
+    ("mixed"), or the FMAs with one scalar-register operand ("fma_sgpr");
+    outi[t] = 2048 * iters when MFMAs run."""
     _check("qmm_probe_issue", lib().qmm_probe_issue(ISSUE_MODES[mode], waves_per_simd, iters, _addr(out), _addr(outi),
                                                     _stream(stream)))

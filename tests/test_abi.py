@@ -147,7 +147,7 @@ def test_probe_read_span(probe):
     (lambda L: L.qmm_peak_mfma_i8(A, (1 << 20) + 1, 10, None), 1),
     (lambda L: L.qmm_peak_mfma_i8(None, 8, 10, None), 2),
     (lambda L: L.qmm_peak_mfma_i8(A + 4, 8, 10, None), 3),
-    (lambda L: L.qmm_probe_issue(3, 2, 10, A, A, None), 1),        # no mode 3
+    (lambda L: L.qmm_probe_issue(4, 2, 10, A, A, None), 1),        # no mode 4
     (lambda L: L.qmm_probe_issue(0, 4, 10, A, A, None), 1),        # 1 or 2 waves per SIMD
     (lambda L: L.qmm_probe_issue(2, 2, 0, A, A, None), 1),
     (lambda L: L.qmm_probe_issue(2, 2, 1000001, A, A, None), 1),

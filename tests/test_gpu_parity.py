@@ -708,7 +708,7 @@ def test_peak_mfma_probe_sums(env, wg, iters):
     assert bool((out == 2048 * iters).all())
 
 
-@pytest.mark.parametrize("mode,wps", [("fma", 1), ("mfma", 2), ("mixed", 2)])
+@pytest.mark.parametrize("mode,wps", [("fma", 1), ("mfma", 2), ("mixed", 2), ("fma_sgpr", 2)])
 def test_issue_probe_results(env, mode, wps):
     """The issue-rate probe runs every iteration: 2048 * iters per lane when
     MFMAs run, 0 otherwise; the FMA chains' sums are finite."""
@@ -721,7 +721,7 @@ def test_issue_probe_results(env, mode, wps):
     outi = torch.full((n,), -1, dtype=torch.int32, device="cuda")
     probe.qmm_probe_issue(mode, wps, iters, out, outi)
     torch.cuda.synchronize()
-    assert bool((outi == (0 if mode == "fma" else 2048 * iters)).all())
+    assert bool((outi == (0 if mode.startswith("fma") else 2048 * iters)).all())
     assert bool(torch.isfinite(out).all())
 
 

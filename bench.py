@@ -15,11 +15,13 @@ the GPU).
 Also in the line: the other decode workloads (the Q8_0 matrices of one
 7B-style layer, Q2_K, Q4_K and Q6_K at 12288x4096), kernel time and GB/s
 each; the prefill matmul (M = 2048, same weights), int8 TOP/s;
-for each, the dominant kernel's roofline (achieved / MI355X peak, with the
-average kernel time from HIP events on the launch stream around graph
-replays of batches of back-to-back launches of that kernel, warmed up and
-alternated with the kernels it is compared with) and the oracle timed on the
-host cores over a bounded sample of the same workload.  `attainable` holds
+for each, the dominant kernel's roofline (achieved / MI355X peak) and the
+oracle timed on the host cores over a bounded sample of the same workload.
+The decode kernel is the whole step, so its roofline takes the timed region's
+time per launch; every other kernel time comes from HIP events on the launch
+stream around windows of back-to-back graph replays of that kernel (each
+window at least half a millisecond of work), warmed up and alternated with
+the kernels it is compared with.  `attainable` holds
 the measured ceilings of the probe library (a streaming read in 24 launch
 shapes, at the decode's 28.3 MB, at 1 GiB and at every decode weight size;
 an int8 MFMA loop; an issue-rate loop of f32 FMAs and int8 MFMAs); each
@@ -114,56 +116,69 @@ def capture(torch, launch, batch):
 def warm_up(torch, graphs, min_ms=25.0, max_reps=400):
     """Replay the graphs round-robin until at least min_ms of GPU time has
     passed, so that clocks have settled before anything is timed (the first
-    milliseconds after a quiet period run measurably slower)."""
+    milliseconds after a quiet period run measurably slower).  Returns the
+    mean time of one replay (ms) over the warm-up's last round."""
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    done, reps = 0.0, 0
+    done, reps, last = 0.0, 0, 0.0
     while done < min_ms and reps < max_reps:
         t0.record()
         for g in graphs:
             g.replay()
         t1.record()
         torch.cuda.synchronize()
-        done += t0.elapsed_time(t1)
+        last = t0.elapsed_time(t1)
+        done += last
         reps += 1
+    return last / len(graphs)
 
 
-def replay_rounds(torch, graphs, rounds):
-    """Times `rounds` replays of every graph, alternating between the graphs
-    (so that all see the same clock conditions), with HIP events on the
-    launch stream around each replay.  Returns per graph the list of replay
-    durations in ms.  A replay's duration includes the short gaps between the
-    kernels of its batch, so it slightly over-states the kernels' own time.
-    (Timing Python launches instead would measure the interpreter for kernels
-    of a few microseconds.)"""
+def replay_rounds(torch, graphs, rounds, per_window=1):
+    """Times `rounds` windows of every graph, alternating between the graphs
+    (so that all see the same clock conditions); a window is `per_window`
+    back-to-back replays of one graph between two HIP events on the launch
+    stream.  Returns per graph the list of window durations in ms.  The two
+    markers of a window add about 5 us of queue start-up to it (measured:
+    22 decode launches per window 7.59 us each, the same launches in one
+    window of 18 replays 7.37 us), which windows of at least half a
+    millisecond of work (time_kernels) keep under 1 %.  (Timing Python
+    launches instead would measure the interpreter for kernels of a few
+    microseconds.)"""
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
           for _ in graphs]
     for r in range(rounds):
         for k, g in enumerate(graphs):
             a, b = ev[k][r]
             a.record()
-            g.replay()
+            for _ in range(per_window):
+                g.replay()
             b.record()
     torch.cuda.synchronize()
     return [[a.elapsed_time(b) for a, b in e] for e in ev]
 
 
-def per_launch(times, batch):
-    """mean, median, min and max per launch (ms) of replays of `batch` launches."""
-    per = sorted(t / batch for t in times)
+def per_launch(times, launches):
+    """mean, median, min and max per launch (ms) of windows of `launches` launches."""
+    per = sorted(t / launches for t in times)
     n = len(per)
     med = per[n // 2] if n % 2 else 0.5 * (per[n // 2 - 1] + per[n // 2])
-    return {"mean": sum(per) / n, "median": med, "min": per[0], "max": per[-1], "launches": n * batch}
+    return {"mean": sum(per) / n, "median": med, "min": per[0], "max": per[-1], "launches": n * launches}
+
+
+WINDOW_MS = 0.5
 
 
 def time_kernels(torch, launches, batch, count, warm_ms=25.0):
     """Per-launch timing (see per_launch) of each launch function in
-    `launches`: graphs of `batch` launches, warmed up, then replayed
-    alternately until each has run at least `count` launches."""
+    `launches`: graphs of `batch` launches, warmed up, then timed in
+    alternating windows of back-to-back replays, each window at least
+    WINDOW_MS of GPU work, until each has run at least `count` launches."""
     graphs = [capture(torch, f, batch) for f in launches]
-    warm_up(torch, graphs, warm_ms)
-    rounds = max(1, -(-count // batch))
-    return [per_launch(t, batch) for t in replay_rounds(torch, graphs, rounds)]
+    replay_ms = warm_up(torch, graphs, warm_ms)
+    per_window = max(1, min(16, -(-WINDOW_MS // max(replay_ms, 1e-3))))
+    per_window = int(per_window)
+    rounds = max(1, -(-count // (batch * per_window)))
+    return [per_launch(t, batch * per_window) for t in replay_rounds(torch, graphs, rounds, per_window)]
 
 
 def us(d):
@@ -221,9 +236,10 @@ def bench_decode(args, torch, q, synth):
     t1.record()
     torch.cuda.synchronize()
     ms_step_eager = t0.elapsed_time(t1) / args.steps
-    # the dominant kernel (the fused kernel, the whole step), the plain matvec
-    # beside it and the step as two launches, alternating, at least 200
-    # launches each
+    # the dominant kernel is the fused kernel, the whole step: its duration
+    # for the roofline is the timed region's per launch.  Beside it, timed in
+    # alternating windows: the same kernel, the plain matvec and the step as
+    # two launches, at least 200 launches each
     count = max(200, args.steps)
     fz, mv, two = time_kernels(torch, [step, lambda i: q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K),
                                        step_two_launches], copies, count)
@@ -231,15 +247,19 @@ def bench_decode(args, torch, q, synth):
         f"fused kernel mean {fz['mean'] * 1e3:.2f} us (median {fz['median'] * 1e3:.2f}, {fz['launches']} launches), "
         f"matvec alone {mv['mean'] * 1e3:.2f} us, two launches {two['mean'] * 1e3:.2f} us, {copies} weight copies")
     gbs_step = wbytes / (ms_step * 1e-3) / 1e9
-    gbs_kernel = wbytes / (fz["mean"] * 1e-3) / 1e9
+    alg = wbytes + 4 * K + 4 * N
+    gbs_kernel = alg / (ms_step * 1e-3) / 1e9
     return dict(ms_step=ms_step, ms_step_eager=ms_step_eager, ms_two=two["mean"], nsteps=nsteps, gbs=gbs_step,
                 wbytes=wbytes, copies=copies,
                 roofline={"kernel": "qmm::k_matvec<Q4_0, fused quantize>", "bound": "hbm",
                           "achieved": round(gbs_kernel, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
                           "traffic": committed_traffic("k_matvec_q4_0_fused", "12288x4096"),
-                          "kernel_us_mean": round(fz["mean"] * 1e3, 3), "kernel_us": us(fz),
-                          "algorithmic_bytes": wbytes + 4 * K + 4 * N,
+                          "kernel_us_mean": round(ms_step * 1e3, 3),
+                          "kernel_us_basis": f"the timed region: {nsteps} back-to-back launches of this kernel "
+                                             "between two HIP events",
+                          "kernel_us_windows": us(fz),
+                          "algorithmic_bytes": alg,
                           "matvec_only": {"kernel": "qmm::k_matvec<Q4_0>", "us_mean": round(mv["mean"] * 1e3, 3),
                                           "us": us(mv),
                                           "achieved": round(wbytes / (mv["mean"] * 1e-3) / 1e9, 1),
@@ -746,7 +766,8 @@ def main():
     out = {"metric": METRIC, "n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "int8", "data": "synthetic"}
     if dec is not None and peaks is not None:
-        dec["roofline"]["frac_of_attainable"] = round(dec["roofline"]["achieved"] / peaks["hbm_read_28MB_gbs"], 4)
+        dec["roofline"]["frac_of_attainable"] = round(peaks["hbm_read_28MB_us"]["mean"] / dec["roofline"]["kernel_us_mean"],
+                                                      4)
     if pre is not None and peaks is not None:
         pre["roofline"]["frac_of_attainable"] = round(pre["roofline"]["achieved"] / peaks["int8_mfma_tops"], 4)
     if dec is not None:

@@ -133,8 +133,52 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
     case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
 // Wait until at most n vector-memory loads of this wave are outstanding
 // (n wave-uniform; above 30 it waits for all of them, which is only stricter).
+// s_waitcnt takes its count as an immediate, so a count known only at run
+// time selects one of 31 instructions.  The counts a decode wave meets (below
+// 8) go through one short compare chain in which each count jumps straight to
+// its own wait and then past the rest; the compiler lowers a switch to a
+// binary tree of about five compares and taken branches per wait, which with
+// three such waits per wave cost the Q2_K 12288 x 4096 decode 0.4 us (6.2
+// against 5.8 us per launch) and the Q4_0 one 0.1 us.
+__device__ __forceinline__ void wait_vmcnt_small(int n) {
+    asm volatile(
+        "s_cmp_eq_u32 %0, 0\n\t"
+        "s_cbranch_scc1 10f\n\t"
+        "s_cmp_eq_u32 %0, 1\n\t"
+        "s_cbranch_scc1 11f\n\t"
+        "s_cmp_eq_u32 %0, 2\n\t"
+        "s_cbranch_scc1 12f\n\t"
+        "s_cmp_eq_u32 %0, 3\n\t"
+        "s_cbranch_scc1 13f\n\t"
+        "s_cmp_eq_u32 %0, 4\n\t"
+        "s_cbranch_scc1 14f\n\t"
+        "s_cmp_eq_u32 %0, 5\n\t"
+        "s_cbranch_scc1 15f\n\t"
+        "s_cmp_eq_u32 %0, 6\n\t"
+        "s_cbranch_scc1 16f\n\t"
+        "s_waitcnt vmcnt(7)\n\t"
+        "s_branch 19f\n"
+        "10:\n\ts_waitcnt vmcnt(0)\n\ts_branch 19f\n"
+        "11:\n\ts_waitcnt vmcnt(1)\n\ts_branch 19f\n"
+        "12:\n\ts_waitcnt vmcnt(2)\n\ts_branch 19f\n"
+        "13:\n\ts_waitcnt vmcnt(3)\n\ts_branch 19f\n"
+        "14:\n\ts_waitcnt vmcnt(4)\n\ts_branch 19f\n"
+        "15:\n\ts_waitcnt vmcnt(5)\n\ts_branch 19f\n"
+        "16:\n\ts_waitcnt vmcnt(6)\n"
+        "19:"
+        :: "s"(n) : "memory", "scc");
+}
 __device__ __forceinline__ void wait_vmcnt(int n) {
-    switch (uniform(n)) {
+    if (__builtin_constant_p(n) && n == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+    }
+    n = uniform(n);
+    if ((unsigned)n < 8u) {
+        wait_vmcnt_small(n);
+        return;
+    }
+    switch (n) {
         QMM_VMCNT_CASE(0) QMM_VMCNT_CASE(1) QMM_VMCNT_CASE(2) QMM_VMCNT_CASE(3) QMM_VMCNT_CASE(4)
         QMM_VMCNT_CASE(5) QMM_VMCNT_CASE(6) QMM_VMCNT_CASE(7) QMM_VMCNT_CASE(8) QMM_VMCNT_CASE(9)
         QMM_VMCNT_CASE(10) QMM_VMCNT_CASE(11) QMM_VMCNT_CASE(12) QMM_VMCNT_CASE(13) QMM_VMCNT_CASE(14)

@@ -82,13 +82,42 @@ __device__ __forceinline__ void lds_q8_0_block(const uint8_t *l8, uint32_t o, in
     d = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(l8 + o));
 }
 
+// The same with the codes' byte offset (o + 2) mod 4 known to the caller.
+template <int SH>
+__device__ __forceinline__ void lds_q8_0_block_at(const uint8_t *l8, uint32_t o, int *q, float &d) {
+    const uint32_t *l32 = reinterpret_cast<const uint32_t *>(l8);
+    const uint32_t qd = (o + 2) >> 2;
+    if constexpr (SH == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = (int)l32[qd + k];
+    } else {
+        uint32_t v[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) v[k] = l32[qd + k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = (int)align_bytes(v[k + 1], v[k], SH);
+    }
+    d = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(l8 + o));
+}
+
+// A paired unit's activation blocks: rows of an even block count start on
+// 4-byte boundaries and xoff keeps that alignment, so block 0's codes sit 2
+// bytes past a dword boundary and block 1's on one.
 template <int F, bool PAIRED>
 __device__ __forceinline__ void load_xu(const uint8_t *xl, uint32_t xoff, int u, XU<F, PAIRED> &x) {
     if constexpr (!kIsK<F>) {
         constexpr int P = Unit<F, PAIRED>::BPU;
 #pragma unroll
         for (int j = 0; j < P; ++j) {
-            lds_q8_0_block(xl, xoff + (uint32_t)(P * u + j) * kQ80Bytes, x.q + 8 * j, x.d[j]);
+            const uint32_t o = xoff + (uint32_t)(P * u + j) * kQ80Bytes;
+            if constexpr (P == 2) {
+                if (j == 0)
+                    lds_q8_0_block_at<2>(xl, o, x.q, x.d[0]);
+                else
+                    lds_q8_0_block_at<0>(xl, o, x.q + 8, x.d[1]);
+            } else {
+                lds_q8_0_block(xl, o, x.q + 8 * j, x.d[j]);
+            }
             int s = 0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) s = dot4(x.q[8 * j + k], 0x01010101, s);
@@ -513,9 +542,13 @@ template <int F, bool PAIRED> struct UnitW {
         return unit_dot<F, PAIRED>(sl, bo, u, x, acc);
     }
 };
+// Paired Q4_0: the codes are held as signed bytes 16 (nib - 8) (the nibble in
+// the byte's top half, XOR 0x80; krafla "Weight packing"), so a token's dot is
+// 16 I with no activation code sum; dw / 16 and 16 I are exact, so each fold
+// rounds the same product as unit_dot's.
 template <> struct UnitW<F_Q4_0, true> {
     uint32_t c[16];   // block j: low nibbles of qs bytes 4k.. in c[8j + k], high nibbles in c[8j + 4 + k]
-    float dw[2];
+    float dw16[2];
     __device__ __forceinline__ void load(const uint8_t *sl, uint32_t bo, int) {
         const uint32_t *l32 = reinterpret_cast<const uint32_t *>(sl + bo);
         uint32_t v[9];
@@ -524,13 +557,13 @@ template <> struct UnitW<F_Q4_0, true> {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const uint32_t q0 = align_bytes(v[k + 1], v[k], 2), q1 = v[5 + k];
-            c[k] = q0 & 0x0f0f0f0fu;
-            c[4 + k] = (q0 >> 4) & 0x0f0f0f0fu;
-            c[8 + k] = q1 & 0x0f0f0f0fu;
-            c[12 + k] = (q1 >> 4) & 0x0f0f0f0fu;
+            c[k] = ((q0 << 4) & 0xf0f0f0f0u) ^ 0x80808080u;
+            c[4 + k] = (q0 & 0xf0f0f0f0u) ^ 0x80808080u;
+            c[8 + k] = ((q1 << 4) & 0xf0f0f0f0u) ^ 0x80808080u;
+            c[12 + k] = (q1 & 0xf0f0f0f0u) ^ 0x80808080u;
         }
-        dw[0] = f16_bits_to_f32(v[0]);
-        dw[1] = f16_bits_to_f32(v[4] >> 16);
+        dw16[0] = f16_bits_to_f32(v[0]) * 0.0625f;
+        dw16[1] = f16_bits_to_f32(v[4] >> 16) * 0.0625f;
     }
     __device__ __forceinline__ float dot(const XU<F_Q4_0, true> &x, float acc) const {
         int s0 = 0, s1 = 0;
@@ -541,8 +574,8 @@ template <> struct UnitW<F_Q4_0, true> {
             s1 = dot4((int)c[8 + k], x.q[8 + k], s1);
             s1 = dot4((int)c[12 + k], x.q[12 + k], s1);
         }
-        acc = fmaf(dw[0] * x.d[0], (float)(s0 - x.sx8[0]), acc);
-        return fmaf(dw[1] * x.d[1], (float)(s1 - x.sx8[1]), acc);
+        acc = fmaf(dw16[0] * x.d[0], (float)s0, acc);
+        return fmaf(dw16[1] * x.d[1], (float)s1, acc);
     }
 };
 

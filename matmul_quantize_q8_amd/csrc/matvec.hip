@@ -13,7 +13,13 @@ hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipS
 // that is walked by one wave in segments of 64 units (4.4 KB of Q8_0), so
 // that the slices stay small and every workgroup fits in LDS at once (Q8_0
 // 4096 x 11008: 11.3 us against 12.4 us with whole-row slices of 11.7 KB,
-// which left room for two workgroups per CU and ran in two rounds).
+// which left room for two workgroups per CU and ran in two rounds).  A
+// launch also keeps at least 2048 waves (8 per CU) where the matrix has the
+// rows: fewer, longer-working waves leave the CUs idle and put several rows'
+// arithmetic behind the last byte (Q4_0 512 x 1024, fused step: 8 rows per
+// wave 4.89 us, 1 row 2.80 us; 2048 x 4096: 2 rows 3.98 us, 1 row 3.76 us;
+// 8192 x 1024: 8 rows 5.61 us, 4 rows 4.34 us).
+constexpr int64_t kMinDecodeWaves = 2048;
 template <int F, bool PAIRED, bool XF32>
 static hipError_t pick_mv(const void *w, const void *xin, uint8_t *xq_out, float *y, int M, int N, int nb,
                           hipStream_t st) {
@@ -27,7 +33,7 @@ static hipError_t pick_mv(const void *w, const void *xin, uint8_t *xq_out, float
     constexpr int NW1 = XF32 ? 8 : 4;
     const int nu = (nb / UT::BPU) * UT::UPB;
     const int64_t rb = (int64_t)nb * FB::BB;
-    const int64_t g = 5000 / rb;
+    const int64_t g = min(5000 / rb, max((int64_t)1, (int64_t)N / kMinDecodeWaves));
     if (nu > kWave && g == 0) return launch_mv<F, PAIRED, 1, 1, XF32>(w, xin, xq_out, y, M, N, nb, st);
     if (nu <= kWave) {
         if (g >= 8) return launch_mv<F, PAIRED, 8, 1, XF32, NW1>(w, xin, xq_out, y, M, N, nb, st);

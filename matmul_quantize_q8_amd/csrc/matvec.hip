@@ -19,7 +19,6 @@ hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipS
 // arithmetic behind the last byte (Q4_0 512 x 1024, fused step: 8 rows per
 // wave 4.89 us, 1 row 2.80 us; 2048 x 4096: 2 rows 3.98 us, 1 row 3.76 us;
 // 8192 x 1024: 8 rows 5.61 us, 4 rows 4.34 us).
-constexpr int64_t kMinDecodeWaves = 2048;
 template <int F, bool PAIRED, bool XF32>
 static hipError_t pick_mv(const void *w, const void *xin, uint8_t *xq_out, float *y, int M, int N, int nb,
                           hipStream_t st) {

@@ -1003,6 +1003,10 @@ __global__ __launch_bounds__(64 * NW) void k_matvec(const uint8_t *__restrict__ 
 }
 
 // --- launch configuration -----------------------------------------------------
+// The launchers choose the rows per wave so that a launch keeps at least this
+// many waves (8 per CU of MI355X) where the matrix has the rows.
+constexpr int64_t kMinDecodeWaves = 2048;
+
 template <int F, bool PAIRED, int G, int MAXU, bool XF32, int NW = 4, int TT = 1>
 static hipError_t launch_mv(const void *w, const void *xin, uint8_t *xq_out, float *y, int M, int N, int nb,
                             hipStream_t st) {

@@ -16,7 +16,10 @@ hipError_t launch_matvec_q5_1(const void *w, const void *xq, float *y, int N, in
 
 // A few tokens at once (the product entry points for small M): the decode
 // kernel with TT tokens per grid row and the rows per wave chosen as for
-// decode, a row of more than 64 units or 5 KB walked in 64-unit segments, so
+// decode (about 5 KB per wave, at least 2048 waves over the grid's rows of
+// tokens where the matrix has the rows: Q4_0 512 x 1024, M = 8, 8 rows per
+// wave 12.1 us, 1 row 4.8 us; 2048 x 4096, M = 16, 1 row 7.4 us, 2 rows 7.0
+// us), a row of more than 64 units or 5 KB walked in 64-unit segments, so
 // that TT activation segments and the slices fit in LDS.
 template <int F, bool PAIRED, int TT>
 static hipError_t pick_mv_tokens(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {
@@ -24,7 +27,8 @@ static hipError_t pick_mv_tokens(const void *w, const void *xq, float *y, int M,
     using UT = Unit<F, PAIRED>;
     constexpr int NW = TT >= 8 ? 8 : 4;   // eight waves share the larger activation copy of 8 tokens
     const int nu = (nb / UT::BPU) * UT::UPB;
-    const int64_t g = 5000 / ((int64_t)nb * FB::BB);
+    const int64_t gy = (M + TT - 1) / TT;
+    const int64_t g = min(5000 / ((int64_t)nb * FB::BB), max((int64_t)1, (int64_t)N * gy / kMinDecodeWaves));
     if (nu > kWave || g < 2) return launch_mv<F, PAIRED, 1, 1, false, NW, TT>(w, xq, nullptr, y, M, N, nb, st);
     if (g >= 8) return launch_mv<F, PAIRED, 8, 1, false, NW, TT>(w, xq, nullptr, y, M, N, nb, st);
     if (g >= 4) return launch_mv<F, PAIRED, 4, 1, false, NW, TT>(w, xq, nullptr, y, M, N, nb, st);

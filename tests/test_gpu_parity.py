@@ -177,8 +177,13 @@ MATVEC_CASES = [
     ("q4_0", 12288, 4096),   # FFN-gate decode
     ("q4_0", 1, 32), ("q4_0", 3, 96), ("q4_0", 17, 160), ("q4_0", 5, 2080), ("q4_0", 7, 8192),
     ("q4_0", 9, 20480),      # two row segments
-    ("q4_0", 45, 1024), ("q8_0", 37, 256), ("q8_0", 3, 64),     # 8 rows per wave, ragged last wave
-    ("q4_0", 13, 2048), ("q4_0", 7, 4000),                       # 4 rows x 1 unit; 2 rows x 4 single units
+    ("q4_0", 45, 1024), ("q8_0", 37, 256), ("q8_0", 3, 64),     # small N: one row per wave
+    ("q4_0", 13, 2048), ("q4_0", 7, 4000),                       # one row x 1 unit; one row x 4 single units
+    # rows per wave past the 2048-wave floor, ragged last wave: 8 rows (K <= 1024
+    # at N >= 16384), 4 rows, 2 rows x 4 single units (odd block count)
+    ("q4_0", 16389, 1024), ("q4_0", 8197, 2048), ("q4_0", 4099, 4000), ("q8_0", 16411, 256),
+    ("q2_k", 16390, 256), ("q4_k", 16391, 512), ("q6_k", 16387, 512), ("q4_1", 16389, 512),
+    ("q5_0", 16389, 1024),
     ("q8_0", 5, 16384), ("q8_0", 3, 40960),                      # > 64 KB of LDS; paired segments
     ("q8_0", 12288, 4096), ("q8_0", 22016, 4096), ("q8_0", 4096, 11008),   # one 7B-style layer
     ("q8_0", 1, 32), ("q8_0", 5, 96), ("q8_0", 11, 4128), ("q8_0", 3, 20000),
@@ -206,7 +211,8 @@ FUSED_CASES = [
     ("q4_0", 512, 1024), ("q4_0", 12288, 4096),
     ("q4_0", 1, 32), ("q4_0", 3, 96), ("q4_0", 17, 160), ("q4_0", 5, 2080), ("q4_0", 7, 8192),
     ("q4_0", 9, 20480), ("q4_0", 45, 1024), ("q4_0", 13, 2048), ("q4_0", 7, 4000),
-    ("q8_0", 37, 256), ("q8_0", 3, 64), ("q8_0", 5, 16384), ("q8_0", 3, 40960),
+    ("q4_0", 16389, 1024), ("q4_0", 8197, 2048),                # 8 and 4 rows per wave
+    ("q8_0", 37, 256), ("q8_0", 3, 64), ("q8_0", 5, 16384), ("q8_0", 3, 40960), ("q8_0", 16411, 256),
     ("q8_0", 12288, 4096), ("q8_0", 22016, 4096), ("q8_0", 4096, 11008),
     ("q8_0", 1, 32), ("q8_0", 11, 4128), ("q8_0", 3, 20000),
 ]
@@ -352,6 +358,9 @@ SMALL_M_CASES = [
     # those counts run on the MFMA kernels
     ("q6_k", 8, 65, 2304), ("q6_k", 7, 33, 11008), ("q8_0", 10, 70, 11008), ("q8_0", 9, 257, 4096),
     ("q5_0", 10, 9, 8192), ("q2_k", 10, 33, 11008), ("q2_k", 9, 130, 4096),
+    # rows per wave past the 2048-wave floor over the grid's token rows: 8 rows
+    # (one pass of 8 tokens), 4 rows (4 tokens), 4 rows (two passes of 8)
+    ("q4_0", 8, 16389, 1024), ("q8_0", 4, 8197, 1024), ("q4_k", 16, 4101, 512),
 ]
 
 

@@ -46,6 +46,11 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (no sparsity)
 
 DEC = dict(M=1, N=12288, K=4096)
 PRE = dict(M=2048, N=12288, K=4096)
+# The host-side leg checks the benchmarked outputs against the oracle: the
+# whole decode output and the first CHECK_ROWS token rows of the prefill,
+# each output within TOL times the sum of the magnitudes of its terms.
+CHECK_ROWS = 64
+TOL = 1e-5
 
 
 def log(*a):
@@ -243,6 +248,11 @@ def bench_decode(args, torch, q, synth):
     count = max(200, args.steps)
     fz, mv, two = time_kernels(torch, [step, lambda i: q.qmm_matvec_q4_0(wqs[i % copies], xq, y, N, K),
                                        step_two_launches], copies, count)
+    # the output of one more step, for the check against the oracle in the
+    # host-side leg (every weight copy holds the same bytes)
+    step(0)
+    torch.cuda.synchronize()
+    y_check = y.cpu().numpy().copy()
     log(f"decode: {ms_step * 1e3:.2f} us/step over {nsteps} steps in graph replay ({ms_step_eager * 1e3:.2f} eager); "
         f"fused kernel mean {fz['mean'] * 1e3:.2f} us (median {fz['median'] * 1e3:.2f}, {fz['launches']} launches), "
         f"matvec alone {mv['mean'] * 1e3:.2f} us, two launches {two['mean'] * 1e3:.2f} us, {copies} weight copies")
@@ -250,7 +260,7 @@ def bench_decode(args, torch, q, synth):
     alg = wbytes + 4 * K + 4 * N
     gbs_kernel = alg / (ms_step * 1e-3) / 1e9
     return dict(ms_step=ms_step, ms_step_eager=ms_step_eager, ms_two=two["mean"], nsteps=nsteps, gbs=gbs_step,
-                wbytes=wbytes, copies=copies,
+                wbytes=wbytes, copies=copies, y_check=y_check,
                 roofline={"kernel": "qmm::k_matvec<Q4_0, fused quantize>", "bound": "hbm",
                           "achieved": round(gbs_kernel, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
@@ -341,6 +351,11 @@ def bench_prefill(args, torch, q, synth):
     if ms_step < mm["mean"]:
         log("prefill: WARNING the step measured shorter than the kernel it contains")
     tops_kernel = ops / (mm["mean"] * 1e-3) / 1e12
+    # the first rows of one more step, for the check against the oracle in
+    # the host-side leg
+    step(0)
+    torch.cuda.synchronize()
+    y_check = Y[:CHECK_ROWS].cpu().numpy().copy()
 
     def time_one(launch):
         for _ in range(4):
@@ -409,7 +424,7 @@ def bench_prefill(args, torch, q, synth):
     m6_ms = t6["mean"]
     log(f"prefill q6_k weights: matmul {m6_ms * 1e3:.1f} us (median {t6['median'] * 1e3:.1f})")
     del wq6k, X8k
-    return dict(ms_step=ms_step, nsteps=nsteps, step_us=us(st), tops=ops / (ms_step * 1e-3) / 1e12,
+    return dict(ms_step=ms_step, nsteps=nsteps, step_us=us(st), tops=ops / (ms_step * 1e-3) / 1e12, y_check=y_check,
                 roofline={"kernel": "qmm::k_matmul_q4_0", "bound": "mfma", "achieved": round(tops_kernel, 2),
                           "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
                           "traffic": committed_traffic("k_matmul_q4_0", "2048x12288x4096"),
@@ -661,7 +676,17 @@ def cpu_model():
     return None
 
 
-def cpu_baseline_decode(args, q, synth):
+def output_check(y, ref):
+    """The benchmarked outputs y against the oracle's exact values and term
+    magnitudes (ref from oracle.matmul with want=("y64", "mag"))."""
+    import numpy as np
+    y64, mag = ref["y64"].reshape(y.shape), ref["mag"].reshape(y.shape)
+    worst = float(np.max(np.abs(y.astype(np.float64) - y64) / (TOL * np.maximum(mag, 1e-300))))
+    return {"outputs": int(y.size), "bound": f"|y - exact| <= {TOL:g} * sum of |terms| per output",
+            "max_err_over_bound": round(worst, 4), "ok": bool(worst <= 1.0)}
+
+
+def cpu_baseline_decode(args, q, synth, y_gpu=None):
     import oracle
     N, K = DEC["N"], DEC["K"]
     w = synth.weights(N, K, config=1)
@@ -685,14 +710,19 @@ def cpu_baseline_decode(args, q, synth):
         t1 += time.perf_counter() - t
         reps1 += 1
     per1 = t1 / reps1
-    return {"value": round(wq.nbytes / per / 1e9, 3), "unit": "GB/s", "cores": thr, "kind": "oracle",
-            "sample": f"full {N}x{K} decode step (quantize + matvec), {reps} repeats, {per * 1e3:.1f} ms each",
-            "host_logical_cpus": host, "cpu_model": cpu_model(),
-            "single_core": {"value": round(wq.nbytes / per1 / 1e9, 3), "unit": "GB/s", "cores": 1,
-                            "sample": f"the same step, {reps1} repeats, {per1 * 1e3:.1f} ms each"}}
+    res = {"value": round(wq.nbytes / per / 1e9, 3), "unit": "GB/s", "cores": thr, "kind": "oracle",
+           "sample": f"full {N}x{K} decode step (quantize + matvec), {reps} repeats, {per * 1e3:.1f} ms each",
+           "host_logical_cpus": host, "cpu_model": cpu_model(),
+           "single_core": {"value": round(wq.nbytes / per1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                           "sample": f"the same step, {reps1} repeats, {per1 * 1e3:.1f} ms each"}}
+    if y_gpu is not None:   # untimed: the benchmarked step's output against the oracle
+        ref = oracle.matmul("q4_0", wq, oracle.quantize_q8_0(x), 1, N, K, threads=thr, want=("y64", "mag"))
+        res["output_check"] = output_check(y_gpu, ref)
+        log(f"decode output check: {res['output_check']}")
+    return res
 
 
-def cpu_baseline_prefill(args, q, synth):
+def cpu_baseline_prefill(args, q, synth, y_gpu=None):
     """The whole 2048-token prefill (quantize + product) on all the threads,
     and the scalar oracle on one core over the first 64 tokens, extrapolated
     to 2048 (the product's cost is linear in the token count)."""
@@ -712,12 +742,18 @@ def cpu_baseline_prefill(args, q, synth):
     oracle.matmul("q4_0", wq, xq1, m1, N, K, threads=1, want=("y",))
     dt1 = time.perf_counter() - t
     ops = 2.0 * M * N * K
-    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": thr, "kind": "oracle",
+    res = {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": thr, "kind": "oracle",
             "sample": f"all {M} tokens of the {M}x{N}x{K} prefill ({dt:.1f} s)",
             "host_logical_cpus": host, "cpu_model": cpu_model(),
             "single_core": {"value": round(2.0 * m1 * N * K / dt1 / 1e12, 6), "unit": "TOPS", "cores": 1,
                             "sample": f"first {m1} of {M} tokens ({dt1:.1f} s), extrapolated to {M}: "
                                       f"{dt1 * M / m1:.0f} s"}}
+    if y_gpu is not None:   # untimed: the benchmarked step's first rows against the oracle
+        r = y_gpu.shape[0]
+        ref = oracle.matmul("q4_0", wq, oracle.quantize_q8_0(x[:r]), r, N, K, threads=thr, want=("y64", "mag"))
+        res["output_check"] = output_check(y_gpu, ref)
+        log(f"prefill output check ({r} token rows): {res['output_check']}")
+    return res
 
 
 def main():
@@ -759,9 +795,9 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the host cores")
         if dec is not None:
-            cpu_dec = cpu_baseline_decode(args, q, synth)
+            cpu_dec = cpu_baseline_decode(args, q, synth, dec["y_check"])
         if pre is not None:
-            cpu_pre = cpu_baseline_prefill(args, q, synth)
+            cpu_pre = cpu_baseline_prefill(args, q, synth, pre["y_check"])
 
     out = {"metric": METRIC, "n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "int8", "data": "synthetic"}

@@ -104,6 +104,26 @@ template <int WFMT> struct WF {
     static_assert(XQ * kWave == BM * XC && WQ * kWave == BN * WC && (XQ + WQ) % 4 == 0,
                   "stage splits into whole wave loads, evenly over the waves");
 };
+
+// Narrow tile for launches of up to 64 tokens: 32 tokens x 128 weight rows,
+// wave w alone on weight rows 32w .. 32w+31 (one 32 x 32 MFMA tile per
+// block).  A stage image is the tile's 32 activation rows (160 chunks, three
+// wave loads; lanes past the last chunk re-load it into padding slots), then
+// per wave its own 32 weight rows (2 or 3 wave loads).  Every wave issues one
+// activation load (wave 3 repeats wave 2's: the same bytes to the same
+// place) and its weight loads, so all waves wait for the same count.
+constexpr int NBM = 32;                    // tokens per narrow tile
+constexpr int NXL = 3;                     // wave loads of activation chunks
+template <int WFMT> struct WN {
+    using F = WF<WFMT>;
+    static constexpr int WL = (32 * F::WC + kWave - 1) / kWave;   // 2, or 3 for Q8_0 weights
+    static constexpr int PER_WAVE = 1 + WL;
+    static constexpr int AREA = NXL * 1024;                        // activation chunks of a stage
+    static constexpr int STAGE = AREA + 4 * WL * 1024;             // 11,264 or 15,360 bytes
+    static constexpr int DXF = NBUF * STAGE;
+    static constexpr int LDS_BYTES = DXF + 4 * F::DXW;
+    static_assert(NBM * XC <= NXL * kWave && 32 * F::WC <= WL * kWave, "chunks fit the wave loads");
+};
 }  // namespace mm
 
 // BYTES (4 or 16) per lane from a buffer into LDS: lane i's bytes land at LDS
@@ -132,14 +152,19 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
 // Workgroup barrier that orders LDS accesses but does not wait for
 // outstanding vector-memory loads (the LDS-DMA copies in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-template <int WFMT, bool SPLIT>
+template <int WFMT, bool SPLIT, bool NARROW = false>
 __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restrict__ w,
                                             const uint8_t *__restrict__ xq, float *__restrict__ y, int M, int N,
                                             int nb, int tiles_m) {
     using namespace mm;
     using F = WF<WFMT>;
     constexpr bool Q8W = F::Q8W, Q5 = F::Q5, MIN = F::MIN;
-    constexpr int WC = F::WC, WQ = F::WQ, STAGE = F::STAGE, PER_WAVE = F::PER_WAVE, DXF = F::DXF;
+    constexpr int WC = F::WC, WQ = F::WQ;
+    constexpr int STAGE = NARROW ? WN<WFMT>::STAGE : F::STAGE;
+    constexpr int PER_WAVE = NARROW ? WN<WFMT>::PER_WAVE : F::PER_WAVE;
+    constexpr int DXF = NARROW ? WN<WFMT>::DXF : F::DXF;
+    constexpr int TBM = NARROW ? NBM : BM;           // tokens per tile
+    constexpr int TI = NARROW ? 1 : 2, TJ = NARROW ? 1 : 2;   // A and B tiles per wave
     const int t = threadIdx.x, lane = t & 63;
     const int wave = uniform(t >> 6);
     // SPLIT: the grid holds every tile twice; part 0 takes the first kb1
@@ -149,7 +174,7 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const int tiles = (int)gridDim.x / ksplit;
     const int tile = (int)blockIdx.x % tiles, part = (int)blockIdx.x / tiles;
     const int mt = tile % tiles_m, nt = tile / tiles_m;
-    const int m0 = mt * BM, n0 = nt * BN;
+    const int m0 = mt * TBM, n0 = nt * BN;
     const uint32_t xrow = (uint32_t)nb * kQ80Bytes, wrow = (uint32_t)nb * F::WB;
     const int kb1 = SPLIT ? 2 * ((nb + 2) / 4) : nb;
     const int kb0 = part ? kb1 : 0, nbp = part ? nb - kb1 : kb1;   // this part's first block and count
@@ -164,52 +189,78 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     // and block 0 a copy of the block before it, whose weight scales are
     // taken as 0 (it adds nothing).
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(xq + (int64_t)m0 * xrow), 0, (int)((uint32_t)min(M - m0, BM) * xrow), 0x00020000);
+        (void *)(xq + (int64_t)m0 * xrow), 0, (int)((uint32_t)min(M - m0, TBM) * xrow), 0x00020000);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(w + (int64_t)n0 * wrow), 0, (int)((uint32_t)min(N - n0, BN) * wrow), 0x00020000);
     uint32_t voff[PER_WAVE];
+    uint32_t m0k[PER_WAVE];   // narrow: the LDS base of each of this wave's loads
+    if constexpr (!NARROW) {
 #pragma unroll
-    for (int k = 0; k < PER_WAVE; ++k) {
-        const int q = wave + 4 * k;
-        if (q < XQ) {
-            const int f = kWave * q + lane, row = f / XC, c = f - XC * row;
-            voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (uint32_t)xchunk(c);
-        } else {
-            const int f = kWave * (q - XQ) + lane, row = f / WC, c = f - WC * row;
-            voff[k] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + (uint32_t)F::wchunk(c);
+        for (int k = 0; k < PER_WAVE; ++k) {
+            const int q = wave + 4 * k;
+            if (q < XQ) {
+                const int f = kWave * q + lane, row = f / XC, c = f - XC * row;
+                voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (uint32_t)xchunk(c);
+            } else {
+                const int f = kWave * (q - XQ) + lane, row = f / WC, c = f - WC * row;
+                voff[k] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + (uint32_t)F::wchunk(c);
+            }
         }
     }
     // the low half of a generic LDS address is the LDS offset
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
     const uint32_t m0w = (uint32_t)uniform((int)(lds0 + 1024u * wave));
+    if constexpr (NARROW) {
+        const int a = min(wave, NXL - 1);
+#pragma unroll
+        for (int k = 0; k < PER_WAVE; ++k) {
+            if (k == 0) {
+                const int f = min(kWave * a + lane, NBM * XC - 1), row = f / XC, c = f - XC * row;
+                voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (uint32_t)xchunk(c);
+                m0k[k] = (uint32_t)uniform((int)(lds0 + 1024u * a));
+            } else {
+                const int f = min(kWave * (k - 1) + lane, 32 * WC - 1), row = f / WC, c = f - WC * row;
+                voff[k] = (uint32_t)(min(n0 + 32 * wave + row, N - 1) - n0) * wrow + (uint32_t)F::wchunk(c);
+                m0k[k] = (uint32_t)uniform((int)(lds0 + WN<WFMT>::AREA + 1024u * (WN<WFMT>::WL * wave + k - 1)));
+            }
+        }
+    }
     // stage s starts at block kb0 + 2s, or one block earlier for the last
     // stage of an odd count (kb0 >= 2 whenever part 1 has an odd count)
     auto seg = [&](int s) { return kb0 + 2 * s - (2 * s + 1 == nbp ? 1 : 0); };
     auto dma_load = [&](auto kc, int s, int b) {
         constexpr int k = decltype(kc)::value;
         const int sx = seg(s) * kQ80Bytes, sw = seg(s) * F::WB;
-        const uint32_t base = m0w + (uint32_t)(b * STAGE);
-        // load 2: activation chunks for waves 0 and 1, weight chunks for 2 and 3
-        const bool isw = k == 2 ? wave >= 2 : k >= 3;
-        buffer_to_lds<16, 4096 * k>(isw ? wr : xr, base, voff[k], isw ? sw : sx);
+        if constexpr (NARROW) {
+            buffer_to_lds<16, 0>(k >= 1 ? wr : xr, m0k[k] + (uint32_t)(b * STAGE), voff[k], k >= 1 ? sw : sx);
+        } else {
+            const uint32_t base = m0w + (uint32_t)(b * STAGE);
+            // load 2: activation chunks for waves 0 and 1, weight chunks for 2 and 3
+            const bool isw = k == 2 ? wave >= 2 : k >= 3;
+            buffer_to_lds<16, 4096 * k>(isw ? wr : xr, base, voff[k], isw ? sw : sx);
+        }
     };
-    static_assert(XQ == 10 && (WQ == 6 || WQ == 10) && PER_WAVE == (XQ + WQ) / 4,
+    static_assert(NARROW || (XQ == 10 && (WQ == 6 || WQ == 10) && PER_WAVE == (XQ + WQ) / 4),
                   "the load roles above are written for these splits");
     auto dma = [&](int s, int b) {
         dma_load(std::integral_constant<int, 0>(), s, b);
         dma_load(std::integral_constant<int, 1>(), s, b);
         dma_load(std::integral_constant<int, 2>(), s, b);
-        dma_load(std::integral_constant<int, 3>(), s, b);
+        if constexpr (PER_WAVE >= 4) dma_load(std::integral_constant<int, 3>(), s, b);
         if constexpr (PER_WAVE == 5) dma_load(std::integral_constant<int, 4>(), s, b);
     };
 
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = NARROW ? 0 : wave & 1, wn = NARROW ? wave : wave >> 1;
     const int lr = lane & 31, lh = lane >> 5;
-    const int xa = 16 * XC * (64 * wm + lr);             // A row 64wm+lr (tile i: +32 rows)
+    // A row 64wm+lr (tile i: +32 rows); narrow: row lr of the tile's 32
+    const int xa = NARROW ? 16 * XC * lr : 16 * XC * (64 * wm + lr);
     const int xa_main = xa + (lh ? 0 : 16);              // block 0: chunk 1 (half 0) or 0 (half 1); block 1: +32
-    const int wb = WOFF + 16 * WC * (64 * wn + lr);      // B row 64wn+lr (tile j: +32 rows)
+    // B row 64wn+lr (tile j: +32 rows); narrow: row lr of this wave's 32
+    const int wb = NARROW ? WN<WFMT>::AREA + 1024 * WN<WFMT>::WL * wave + 16 * WC * lr
+                          : WOFF + 16 * WC * (64 * wn + lr);
     const int wb_main = wb + (lh ? 0 : 16);              // Q8_0 weights: as xa_main
-    const int xd = 16 * XC * (64 * wm + lane);           // the row whose dx this lane converts
+    // the row whose dx this lane converts (narrow: lanes 32..63 repeat 0..31)
+    const int xd = NARROW ? 16 * XC * lr : 16 * XC * (64 * wm + lane);
     const int dxw = DXF + F::DXW * wave;                 // this wave's f32 dx: [block][64 rows 64wm..]
     const uint32_t selA = lh ? 0x03020504u : 0x03020100u;   // half 1: codes 30, 31 into bytes 0, 1
     const uint32_t selB = lh ? 0x07060100u : 0x03020504u;   // block 0, first dword: which bytes take low nibbles
@@ -223,11 +274,11 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     // allocator rebuilds it from scalar registers in every unrolled stage
     // (8 v_mov_b64 reading the scalar bus, which do not issue in pairs)
     asm volatile("" : "+v"(bias));
-    float acc[2][2][16];
+    float acc[TI][TJ][16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -333,13 +384,13 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     };
     auto load_raw = [&](const uint8_t *sb, Raw &r) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < TI; ++i) {
             r.a0[i] = rd16(sb + xa_main + 16 * XC * 32 * i);
             r.a1[i] = rd16(sb + xa_main + 32 + 16 * XC * 32 * i);
             r.a4[i] = rd16(sb + xa + 64 + 16 * XC * 32 * i);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
             if constexpr (Q8W) {
                 r.b0[j] = rd16(sb + wb_main + 16 * WC * 32 * j);
                 r.b1[j] = rd16(sb + wb_main + 32 + 16 * WC * 32 * j);
@@ -362,12 +413,12 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     };
     auto build0 = [&](const Raw &r, bool absent, Ops &o) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < TI; ++i) {
             const uint4 c = r.a0[i];   // chunk 1 (half 0) or chunk 0 (half 1)
             o.a[i] = v4i{(int)__builtin_amdgcn_perm(r.a1[i].x, c.x, selA), (int)c.y, (int)c.z, (int)c.w};
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
             if constexpr (Q8W) {
                 const uint4 c = r.b0[j];
                 o.b[j] = v4i{(int)__builtin_amdgcn_perm(r.b1[j].x, c.x, selA), (int)c.y, (int)c.z, (int)c.w};
@@ -414,13 +465,13 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     };
     auto build1 = [&](const Raw &r, Ops &o) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < TI; ++i) {
             const uint4 c = r.a1[i];   // chunk 3 (half 0) or chunk 2 (half 1)
             const uint32_t d0 = lh ? r.a4[i].w : c.x;
             o.a[i] = v4i{(int)d0, (int)c.y, (int)c.z, (int)c.w};
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
             if constexpr (Q8W) {
                 const uint4 c = r.b1[j];
                 const uint32_t d0 = lh ? r.b4[j].w : c.x;
@@ -468,9 +519,9 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     auto offset_operands = [&](const Raw &r, bool absent0, float (&ao)[2], float (&bo)[2]) {
         const float *d = reinterpret_cast<const float *>(lds + dxw);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) ao[i] = d[128 + 64 * lh + 32 * i + lr];
+        for (int i = 0; i < TI; ++i) ao[i] = d[128 + 64 * lh + 32 * i + lr];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
             if constexpr (MIN) {
                 const uint32_t sc = lh ? (F::Q41 ? r.w1[j].y : r.w1[j].z) : r.w0[j].x;
                 const float c = fmaf(half_lo(sc), 128.0f, half_hi(sc) * (1.0f / F::OUT_SCALE));
@@ -497,59 +548,85 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
         Raw r;
         Ops o0, o1;
         float dxa[16], dxb[16];
-        auto dma_after = [&](auto kc) {
-            dma_load(kc, sd, bd);
+        if constexpr (NARROW) {
+            // one tile: the MFMA of block 1 is issued before the fold of block 0
+            float ao[2], bo[2];
+            convert_dx(sb);
+            load_raw(sb, r);
+            if constexpr (MIN) offset_operands(r, absent0, ao, bo);
+            load_dx(0, 0, dxa);
+            load_dx(1, 0, dxb);
+            build0(r, absent0, o0);
+            v16i d0 = mfma(o0.a[0], o0.b[0]);
             __builtin_amdgcn_sched_barrier(0);
-        };
-        float ao[2], bo[2];
-        convert_dx(sb);
-        load_raw(sb, r);
-        if constexpr (MIN) offset_operands(r, absent0, ao, bo);
-        load_dx(0, 0, dxa);
-        build0(r, absent0, o0);
-        v16i d0 = mfma(o0.a[0], o0.b[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        load_dx(0, 1, dxb);
-        v16i d1 = mfma(o0.a[0], o0.b[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        fold(d0, 0, 0, dxa, o0.dw[0], o0.nb[0]);
-        dma_after(std::integral_constant<int, 0>());
-        d0 = mfma(o0.a[1], o0.b[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        fold(d1, 0, 1, dxa, o0.dw[1], o0.nb[1]);
-        dma_after(std::integral_constant<int, 1>());
-        d1 = mfma(o0.a[1], o0.b[1]);
-        load_dx(1, 0, dxa);
-        __builtin_amdgcn_sched_barrier(0);
-        fold(d0, 1, 0, dxb, o0.dw[0], o0.nb[0]);
-        dma_after(std::integral_constant<int, 2>());
-        build1(r, o1);
-        d0 = mfma(o1.a[0], o1.b[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        fold(d1, 1, 1, dxb, o0.dw[1], o0.nb[1]);
-        dma_after(std::integral_constant<int, 3>());
-        d1 = mfma(o1.a[0], o1.b[1]);
-        load_dx(1, 1, dxb);
-        __builtin_amdgcn_sched_barrier(0);
-        fold(d0, 0, 0, dxa, o1.dw[0], o1.nb[0]);
-        if constexpr (PER_WAVE == 5) dma_load(std::integral_constant<int, 4>(), sd, bd);
-        __builtin_amdgcn_sched_barrier(0);
-        d0 = mfma(o1.a[1], o1.b[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        fold(d1, 0, 1, dxa, o1.dw[1], o1.nb[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        d1 = mfma(o1.a[1], o1.b[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        fold(d0, 1, 0, dxb, o1.dw[0], o1.nb[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        fold(d1, 1, 1, dxb, o1.dw[1], o1.nb[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (MIN) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) offset_mfma(i, j, ao[i], bo[j]);
+            dma(sd, bd);
             __builtin_amdgcn_sched_barrier(0);
+            build1(r, o1);
+            v16i d1 = mfma(o1.a[0], o1.b[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d0, 0, 0, dxa, o0.dw[0], o0.nb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d1, 0, 0, dxb, o1.dw[0], o1.nb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (MIN) {
+                offset_mfma(0, 0, ao[0], bo[0]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            auto dma_after = [&](auto kc) {
+                dma_load(kc, sd, bd);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            float ao[2], bo[2];
+            convert_dx(sb);
+            load_raw(sb, r);
+            if constexpr (MIN) offset_operands(r, absent0, ao, bo);
+            load_dx(0, 0, dxa);
+            build0(r, absent0, o0);
+            v16i d0 = mfma(o0.a[0], o0.b[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_dx(0, 1, dxb);
+            v16i d1 = mfma(o0.a[0], o0.b[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d0, 0, 0, dxa, o0.dw[0], o0.nb[0]);
+            dma_after(std::integral_constant<int, 0>());
+            d0 = mfma(o0.a[1], o0.b[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d1, 0, 1, dxa, o0.dw[1], o0.nb[1]);
+            dma_after(std::integral_constant<int, 1>());
+            d1 = mfma(o0.a[1], o0.b[1]);
+            load_dx(1, 0, dxa);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d0, 1, 0, dxb, o0.dw[0], o0.nb[0]);
+            dma_after(std::integral_constant<int, 2>());
+            build1(r, o1);
+            d0 = mfma(o1.a[0], o1.b[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d1, 1, 1, dxb, o0.dw[1], o0.nb[1]);
+            dma_after(std::integral_constant<int, 3>());
+            d1 = mfma(o1.a[0], o1.b[1]);
+            load_dx(1, 1, dxb);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d0, 0, 0, dxa, o1.dw[0], o1.nb[0]);
+            if constexpr (PER_WAVE == 5) dma_load(std::integral_constant<int, 4>(), sd, bd);
+            __builtin_amdgcn_sched_barrier(0);
+            d0 = mfma(o1.a[1], o1.b[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d1, 0, 1, dxa, o1.dw[1], o1.nb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            d1 = mfma(o1.a[1], o1.b[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d0, 1, 0, dxb, o1.dw[0], o1.nb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            fold(d1, 1, 1, dxb, o1.dw[1], o1.nb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (MIN) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) offset_mfma(i, j, ao[i], bo[j]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -563,8 +640,10 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
         constexpr int b = decltype(bc)::value;
         if constexpr (PER_WAVE == 5)
             asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-        else
+        else if constexpr (PER_WAVE == 4)
             asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
         lds_barrier();
         compute(lds + b * STAGE, 2 * s + 1 == nbp, min(s + 2, nst - 1), (b + 2) % NBUF);
     };
@@ -580,14 +659,14 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
 
     // store: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + 64 * wn + 32 * j + lr;
+        for (int j = 0; j < TJ; ++j) {
+            const int n = n0 + (NARROW ? 32 * wave : 64 * wn + 32 * j) + lr;
             if (n >= N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const int m = m0 + (NARROW ? 0 : 64 * wm + 32 * i) + 8 * (r >> 2) + 4 * lh + (r & 3);
                 if (m >= M) continue;
                 // two addends on a zeroed output: the same sum in either order
                 if constexpr (SPLIT)
@@ -666,6 +745,16 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_1_split(const uint8_t *
                                                                 int M, int N, int nb, int tiles_m) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q5_1>::LDS_BYTES];
     matmul_body<F_Q5_1, true>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+// The narrow tile (32 tokens x 128 weight rows) for launches of up to 64
+// tokens, every 32-value format, K in one part or split in two.
+template <int WFMT, bool SPLIT>
+__global__ __launch_bounds__(mm::NT, 2) void k_matmul_narrow(const uint8_t *__restrict__ w,
+                                                            const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                            int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WN<WFMT>::LDS_BYTES];
+    matmul_body<WFMT, SPLIT, true>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 // K = 32: one block per row, too short for the two-block stages above (the
@@ -776,7 +865,10 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
         hipLaunchKernelGGL(one, dim3((unsigned)grid), dim3(256), 0, st, wp, xp, y, M, N);
         return hipGetLastError();
     }
-    int tiles_m = (M + mm::BM - 1) / mm::BM;
+    // up to 64 tokens: the 32-token tile (a 128-token tile would compute
+    // and drop the rows past M)
+    const bool narrow = M <= 2 * mm::NBM;
+    int tiles_m = narrow ? (M + mm::NBM - 1) / mm::NBM : (M + mm::BM - 1) / mm::BM;
     const int64_t tiles = (int64_t)tiles_m * ((N + mm::BN - 1) / mm::BN);
     // A launch of at most one workgroup per CU leaves the CUs half idle and
     // each workgroup alone on its CU: split K in two, the parts adding into
@@ -788,7 +880,9 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
     }
     const int ksplit = split ? 2 : 1;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
-    const void *kern = WFMT == F_Q8_0   ? (split ? (const void *)k_matmul_q8_0_split : (const void *)k_matmul_q8_0)
+    const void *kern = narrow           ? (split ? (const void *)k_matmul_narrow<WFMT, true>
+                                                 : (const void *)k_matmul_narrow<WFMT, false>)
+                       : WFMT == F_Q8_0 ? (split ? (const void *)k_matmul_q8_0_split : (const void *)k_matmul_q8_0)
                        : WFMT == F_Q5_0 ? (split ? (const void *)k_matmul_q5_0_split : (const void *)k_matmul_q5_0)
                        : WFMT == F_Q4_1 ? (split ? (const void *)k_matmul_q4_1_split : (const void *)k_matmul_q4_1)
                        : WFMT == F_Q5_1 ? (split ? (const void *)k_matmul_q5_1_split : (const void *)k_matmul_q5_1)

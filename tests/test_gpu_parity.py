@@ -321,6 +321,11 @@ MATMUL_CASES = [
     ("q5_0", 129, 257, 64), ("q5_0", 128, 128, 4096),
     # long rows: 1025 blocks (an odd count), 128 super-blocks
     ("q4_0", 129, 65, 32800), ("q5_1", 65, 33, 32800), ("q2_k", 65, 129, 32768), ("q6_k", 33, 65, 32768),
+    # 17-64 tokens: the 32-token tile; odd block counts, K split in two and
+    # in one part (fewer than 4 blocks, or more than 256 tiles), ragged M and N
+    ("q4_0", 17, 300, 160), ("q4_0", 33, 129, 96), ("q4_0", 64, 16577, 256), ("q4_0", 32, 12288, 4096),
+    ("q8_0", 50, 260, 4128), ("q8_0", 64, 16512, 128), ("q5_0", 20, 130, 2080), ("q4_1", 45, 257, 1024),
+    ("q5_1", 32, 128, 4096), ("q5_1", 17, 16641, 160),
     # more than 256 output tiles (128 x 128; 128 x 256 for Q2_K and Q4_K):
     # K in one part, the kernels the 2048-token prefill runs (the cases above
     # with 4 blocks or more have at most 256 tiles and split K in two); per

@@ -65,6 +65,7 @@
 #include "qmm_device.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace qmm {
 
@@ -112,6 +113,14 @@ template <int WFMT> struct WF {
 // per wave its own 32 weight rows (2 or 3 wave loads).  Every wave issues one
 // activation load (wave 3 repeats wave 2's: the same bytes to the same
 // place) and its weight loads, so all waves wait for the same count.
+// A split launch of fewer workgroups than CUs runs eight waves per workgroup
+// instead: two K groups of four, each with its own stage buffers on half of
+// the part's stages, stepping through the same barriers; at the end group 1
+// passes its sums to group 0 through LDS, which adds them to its own before
+// the store (the same order on every call).  With one workgroup of four
+// waves per CU or fewer, the stage chain of a lone wave per SIMD sets the
+// time; two waves per SIMD halve the chain (Q4_0 M = 8, N = 12288, K = 4096:
+// 18.4 -> 14.5 us).
 constexpr int NBM = 32;                    // tokens per narrow tile
 constexpr int NXL = 3;                     // wave loads of activation chunks
 template <int WFMT> struct WN {
@@ -120,9 +129,12 @@ template <int WFMT> struct WN {
     static constexpr int PER_WAVE = 1 + WL;
     static constexpr int AREA = NXL * 1024;                        // activation chunks of a stage
     static constexpr int STAGE = AREA + 4 * WL * 1024;             // 11,264 or 15,360 bytes
-    static constexpr int DXF = NBUF * STAGE;
-    static constexpr int LDS_BYTES = DXF + 4 * F::DXW;
+    static constexpr int NBUF = 3;                                 // stage buffers per K group
+    // G = 1 or 2 groups of 4 waves, each on its own part of K
+    template <int G> static constexpr int DXF = G * NBUF * STAGE;
+    template <int G> static constexpr int LDS_BYTES = DXF<G> + 4 * G * F::DXW;
     static_assert(NBM * XC <= NXL * kWave && 32 * F::WC <= WL * kWave, "chunks fit the wave loads");
+    static_assert(2 * LDS_BYTES<1> <= 160 * 1024 && LDS_BYTES<2> <= 160 * 1024, "LDS of one CU");
 };
 }  // namespace mm
 
@@ -149,10 +161,16 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 #pragma clang diagnostic pop
 
+// fn(integral_constant<I>) for each I of the sequence, in order
+template <int... I, class Fn>
+__device__ __forceinline__ void each_index(std::integer_sequence<int, I...>, Fn &&fn) {
+    (fn(std::integral_constant<int, I>()), ...);
+}
+
 // Workgroup barrier that orders LDS accesses but does not wait for
 // outstanding vector-memory loads (the LDS-DMA copies in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-template <int WFMT, bool SPLIT, bool NARROW = false>
+template <int WFMT, bool SPLIT, bool NARROW = false, int G = 1>
 __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restrict__ w,
                                             const uint8_t *__restrict__ xq, float *__restrict__ y, int M, int N,
                                             int nb, int tiles_m) {
@@ -162,23 +180,36 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     constexpr int WC = F::WC, WQ = F::WQ;
     constexpr int STAGE = NARROW ? WN<WFMT>::STAGE : F::STAGE;
     constexpr int PER_WAVE = NARROW ? WN<WFMT>::PER_WAVE : F::PER_WAVE;
-    constexpr int DXF = NARROW ? WN<WFMT>::DXF : F::DXF;
+    constexpr int DXF = NARROW ? WN<WFMT>::template DXF<G> : F::DXF;
+    constexpr int NB = NARROW ? WN<WFMT>::NBUF : NBUF;   // stage buffers; the DMA runs NB - 1 stages ahead
+    static_assert(G == 1 || (G == 2 && NARROW), "K groups only on the narrow tile");
     constexpr int TBM = NARROW ? NBM : BM;           // tokens per tile
     constexpr int TI = NARROW ? 1 : 2, TJ = NARROW ? 1 : 2;   // A and B tiles per wave
     const int t = threadIdx.x, lane = t & 63;
-    const int wave = uniform(t >> 6);
-    // SPLIT: the grid holds every tile twice; part 0 takes the first kb1
-    // blocks of each row (whole stages), part 1 the rest, and both add into
-    // the zeroed output.
+    const int wave = uniform((t >> 6) & 3);
+    const int grp = G == 1 ? 0 : uniform(t >> 8);   // K group: its own stage buffers and blocks
+    // SPLIT: the grid holds every tile twice, one per part of K, and both
+    // parts add into the zeroed output.  Part p of P = ksplit * G (grid part
+    // and K group) takes stages [p S / P, (p + 1) S / P) of the S = ceil(nb /
+    // 2) two-block stages of a row (the caller keeps S >= P).
     constexpr int ksplit = SPLIT ? 2 : 1;
+    constexpr int P = ksplit * G;
     const int tiles = (int)gridDim.x / ksplit;
-    const int tile = (int)blockIdx.x % tiles, part = (int)blockIdx.x / tiles;
+    const int tile = (int)blockIdx.x % tiles, gpart = (int)blockIdx.x / tiles;
     const int mt = tile % tiles_m, nt = tile / tiles_m;
     const int m0 = mt * TBM, n0 = nt * BN;
     const uint32_t xrow = (uint32_t)nb * kQ80Bytes, wrow = (uint32_t)nb * F::WB;
-    const int kb1 = SPLIT ? 2 * ((nb + 2) / 4) : nb;
-    const int kb0 = part ? kb1 : 0, nbp = part ? nb - kb1 : kb1;   // this part's first block and count
+    const int S_all = (nb + 1) >> 1;
+    auto first_stage = [&](int p) { return p * S_all / P; };
+    const int part = G * gpart + grp;
+    const int kb0 = 2 * first_stage(part);                               // this part's first block
+    const int nbp = min(2 * first_stage(part + 1), nb) - kb0;           // and its block count
     const int nst = (nbp + 1) >> 1;   // an odd block count leaves a last stage of one block
+    // every wave of the workgroup passes the same barriers: the K groups
+    // step together for the larger of their stage counts
+    const int nst_wg = G == 1 ? nst
+                              : max(first_stage(G * gpart + 1) - first_stage(G * gpart),
+                                    first_stage(G * gpart + 2) - first_stage(G * gpart + 1));
 
     // DMA: wave load q = w + 4k (k < 4) of a stage is chunk load q of the
     // stage image (activation chunks for q < 10, weight chunks after) and
@@ -208,7 +239,8 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
         }
     }
     // the low half of a generic LDS address is the LDS offset
-    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+    uint8_t *const ldsg = lds + grp * (NB * STAGE);   // this K group's stage buffers
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(ldsg);
     const uint32_t m0w = (uint32_t)uniform((int)(lds0 + 1024u * wave));
     if constexpr (NARROW) {
         const int a = min(wave, NXL - 1);
@@ -261,7 +293,7 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const int wb_main = wb + (lh ? 0 : 16);              // Q8_0 weights: as xa_main
     // the row whose dx this lane converts (narrow: lanes 32..63 repeat 0..31)
     const int xd = NARROW ? 16 * XC * lr : 16 * XC * (64 * wm + lane);
-    const int dxw = DXF + F::DXW * wave;                 // this wave's f32 dx: [block][64 rows 64wm..]
+    const int dxw = DXF + F::DXW * (4 * grp + wave);     // this wave's f32 dx: [block][64 rows 64wm..]
     const uint32_t selA = lh ? 0x03020504u : 0x03020100u;   // half 1: codes 30, 31 into bytes 0, 1
     const uint32_t selB = lh ? 0x07060100u : 0x03020504u;   // block 0, first dword: which bytes take low nibbles
     const uint32_t shHi = lh ? 4u : 0u;                  // shift for a dword that half 0 takes high nibbles of
@@ -630,32 +662,44 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
         }
     };
 
-    // Stage s lives in buffer s % 3.  At step s this wave's loads of stage s
-    // have landed once at most the 4 of stage s+1 are outstanding; the
-    // barrier publishes every wave's and frees buffer (s-1) % 3, which the
-    // DMA of stage s+2 then fills.  The last two steps have no stage s+2 and
-    // copy the last stage again into that idle buffer instead, so that every
-    // step issues the same 4 loads and waits for the same count.
+    // Stage s lives in buffer s % NB.  At step s this wave's loads of stage
+    // s have landed once at most the PER_WAVE loads of each later stage in
+    // flight are outstanding; the barrier publishes every wave's and frees
+    // buffer (s-1) % NB, which the DMA of stage s+NB-1 then fills.  The last
+    // steps have no such stage and copy the last stage again into that idle
+    // buffer instead, so that every step issues the same loads and waits for
+    // the same count.  A K group with fewer stages than the other passes its
+    // extra step's barrier without work or loads.
     auto step = [&](int s, auto bc) {
         constexpr int b = decltype(bc)::value;
-        if constexpr (PER_WAVE == 5)
-            asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-        else if constexpr (PER_WAVE == 4)
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" :: "i"((NB - 2) * PER_WAVE) : "memory");
         lds_barrier();
-        compute(lds + b * STAGE, 2 * s + 1 == nbp, min(s + 2, nst - 1), (b + 2) % NBUF);
+        if (G == 1 || s < nst) compute(ldsg + b * STAGE, 2 * s + 1 == nbp, min(s + NB - 1, nst - 1), (b + NB - 1) % NB);
     };
-    dma(0, 0);
-    dma(min(1, nst - 1), 1);
-    for (int s = 0; s < nst; s += NBUF) {
-        step(s, std::integral_constant<int, 0>());
-        if (s + 1 < nst) step(s + 1, std::integral_constant<int, 1>());
-        if (s + 2 < nst) step(s + 2, std::integral_constant<int, 2>());
+#pragma unroll
+    for (int k = 0; k + 1 < NB; ++k) dma(min(k, nst - 1), k);
+    for (int s = 0; s < nst_wg; s += NB) {
+        each_index(std::make_integer_sequence<int, NB>(), [&](auto bc) {
+            if (decltype(bc)::value == 0 || s + decltype(bc)::value < nst_wg) step(s + decltype(bc)::value, bc);
+        });
     }
     // no LDS-DMA write may still be in flight when the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (G == 2) {
+        // group 1 hands its sums to group 0 through LDS ([wave][r][lane],
+        // over the stage buffers), which adds them to its own: the same
+        // order on every call
+        float *red = reinterpret_cast<float *>(lds) + 1024 * wave + lane;
+        lds_barrier();
+        if (grp == 1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[64 * r] = acc[0][0][r];
+        }
+        lds_barrier();
+        if (grp == 1) return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][0][r] += red[64 * r];
+    }
 
     // store: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32
 #pragma unroll
@@ -753,8 +797,18 @@ template <int WFMT, bool SPLIT>
 __global__ __launch_bounds__(mm::NT, 2) void k_matmul_narrow(const uint8_t *__restrict__ w,
                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                             int M, int N, int nb, int tiles_m) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WN<WFMT>::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WN<WFMT>::template LDS_BYTES<1>];
     matmul_body<WFMT, SPLIT, true>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+// The narrow tile with two groups of four waves, each on half of the
+// workgroup's part of K, for split launches of fewer workgroups than CUs.
+template <int WFMT>
+__global__ __launch_bounds__(2 * mm::NT, 1) void k_matmul_narrow2(const uint8_t *__restrict__ w,
+                                                                 const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                                 int M, int N, int nb, int tiles_m) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WN<WFMT>::template LDS_BYTES<2>];
+    matmul_body<WFMT, true, true, 2>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 // K = 32: one block per row, too short for the two-block stages above (the
@@ -879,8 +933,12 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
         if (e != hipSuccess) return e;
     }
     const int ksplit = split ? 2 : 1;
+    // Fewer narrow workgroups than CUs: two groups of four waves per
+    // workgroup, each on half of its part of K (at least four stages each).
+    const bool groups = narrow && split && tiles * 2 < kCUs && nb >= 16;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
-    const void *kern = narrow           ? (split ? (const void *)k_matmul_narrow<WFMT, true>
+    const void *kern = groups           ? (const void *)k_matmul_narrow2<WFMT>
+                       : narrow         ? (split ? (const void *)k_matmul_narrow<WFMT, true>
                                                  : (const void *)k_matmul_narrow<WFMT, false>)
                        : WFMT == F_Q8_0 ? (split ? (const void *)k_matmul_q8_0_split : (const void *)k_matmul_q8_0)
                        : WFMT == F_Q5_0 ? (split ? (const void *)k_matmul_q5_0_split : (const void *)k_matmul_q5_0)
@@ -888,7 +946,7 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
                        : WFMT == F_Q5_1 ? (split ? (const void *)k_matmul_q5_1_split : (const void *)k_matmul_q5_1)
                        : split          ? (const void *)k_matmul_q4_0_split
                                         : (const void *)k_matmul_q4_0;
-    return hipLaunchKernel(kern, dim3((unsigned)(tiles * ksplit)), dim3(mm::NT), args, 0, st);
+    return hipLaunchKernel(kern, dim3((unsigned)(tiles * ksplit)), dim3(groups ? 2 * mm::NT : mm::NT), args, 0, st);
 }
 
 hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st) {

@@ -25,14 +25,17 @@ enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4, F_Q4_1 = 
 
 // Token counts up to small_tokens(format) run the products on the decode
 // kernel with several tokens per weight pass; larger counts run the MFMA
-// prefill kernels, whose 128-token tiles cost about the same for any
-// M <= 128 (N = 12288, K = 4096, K split in two: 30-47 us by format).  The
-// switch is where the two meet at that size: the decode kernel's cost grows
-// with each group of up to 8 tokens, fastest for the formats with the most
-// unpacking per token (Q6_K), slowest for Q4_K, whose units stay in
-// registers and whose MFMA kernel is the slowest at small M.
+// prefill kernels.  The decode kernel's cost is flat within each group of
+// tokens that share a weight pass (up to 2, 4 or 8) and steps up at the next
+// group; the MFMA kernels cost about the same for any M up to a tile (32
+// tokens for the 32-value formats, 128 for the K-quants).  The switch is
+// where the two meet at N = 12288, K = 4096 (us, decode kernel / MFMA):
+// Q4_0 M = 8 13.1 / 14.5, M = 10 22.1 / 15.3; Q4_1 M = 4 12.1 / 17.9, M = 6
+// 19.2 / 17.4; Q4_K keeps the decode kernel longest, its units staying in
+// registers and its MFMA kernel the slowest at small M; Q6_K, with the most
+// unpacking per token, leaves it first among the K-quants.
 constexpr int small_tokens(int fmt) {
-    return fmt == F_Q4_K ? 32 : fmt == F_Q6_K ? 8 : (fmt == F_Q8_0 || fmt == F_Q5_0 || fmt == F_Q2_K) ? 10 : 16;
+    return fmt == F_Q4_K ? 32 : fmt == F_Q2_K ? 10 : (fmt == F_Q4_0 || fmt == F_Q6_K) ? 8 : 4;
 }
 hipError_t launch_matvec_tokens(int fmt, const void *w, const void *xq, float *y, int M, int N, int nb,
                                 hipStream_t st);
@@ -120,9 +123,10 @@ inline hipError_t allow_dynamic_lds(const void *kernel, size_t bytes, int (&done
     return e;
 }
 
+constexpr int64_t kCUs = 256;   // compute units of the chip
 // Prefill launches of at most this many output tiles (one workgroup per CU
 // or fewer) split K in two, the parts adding into an output zeroed first.
-constexpr int64_t kSplitTiles = 256;
+constexpr int64_t kSplitTiles = kCUs;
 // Zero n floats at y (16-byte aligned) on stream st.
 hipError_t launch_zero_f32(float *y, int64_t n, hipStream_t st);
 

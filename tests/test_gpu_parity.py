@@ -358,11 +358,18 @@ SMALL_M_CASES = [
     ("q4_k", 3, 130, 4096), ("q4_k", 8, 12288, 4096), ("q4_k", 10, 31, 11008), ("q4_k", 32, 65, 2304),
     ("q4_k", 25, 129, 4096), ("q4_k", 33, 33, 4096),
     ("q6_k", 5, 130, 4096), ("q6_k", 16, 65, 2304), ("q6_k", 9, 33, 11008),
-    # the largest token counts on the decode kernel for the formats that
-    # switch early (Q6_K at 8; Q8_0, Q5_0, Q2_K at 10); the cases above past
+    # the largest token counts on the decode kernel (8 for Q4_0 and Q6_K, 10
+    # for Q2_K, 32 for Q4_K, 4 for the other formats); the cases above past
     # those counts run on the MFMA kernels
     ("q6_k", 8, 65, 2304), ("q6_k", 7, 33, 11008), ("q8_0", 10, 70, 11008), ("q8_0", 9, 257, 4096),
     ("q5_0", 10, 9, 8192), ("q2_k", 10, 33, 11008), ("q2_k", 9, 130, 4096),
+    ("q5_0", 4, 130, 4096), ("q5_0", 3, 70, 11008), ("q4_1", 4, 130, 4096), ("q5_1", 4, 33, 4128),
+    ("q8_0", 3, 70, 11008), ("q4_0", 7, 65, 8192), ("q4_1", 5, 70, 4128), ("q5_1", 5, 130, 8192),
+    # the first counts on the 32-token MFMA tile, with two K groups per
+    # workgroup (K of 16 and 17 blocks: two stages per group, and an odd
+    # last stage) and without (K of 3 blocks, no split)
+    ("q4_0", 9, 130, 512), ("q8_0", 9, 257, 544), ("q5_0", 5, 9, 544), ("q4_1", 9, 33, 96),
+    ("q5_1", 12, 200, 512),
     # rows per wave past the 2048-wave floor over the grid's token rows: 8 rows
     # (one pass of 8 tokens), 4 rows (4 tokens), 4 rows (two passes of 8)
     ("q4_0", 8, 16389, 1024), ("q8_0", 4, 8197, 1024), ("q4_k", 16, 4101, 512),

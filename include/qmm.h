@@ -202,11 +202,11 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
 /* Matmul, M tokens (prefill, or a few tokens at once).
  *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.
  *   y  : f32 [M][N], written.
- * Up to 8 tokens (Q4_0, Q6_K; 4 for Q8_0, Q4_1, Q5_0 and Q5_1, 10 for Q2_K,
- * 32 for Q4_K) run on the decode matvec kernel, which streams each weight
- * slice once per group of 2, 4 or 8 tokens (one token: the decode launch
- * itself); more tokens run on the MFMA kernels below (32-token tiles up to
- * 64 tokens for the 32-value formats, 128-token tiles otherwise).  Results
+ * Up to 8 tokens (Q4_0; 2 for Q2_K, 4 for the other formats) run on the
+ * decode matvec kernel, which streams each weight slice once per group of
+ * 2, 4 or 8 tokens (one token: the decode launch itself); more tokens run
+ * on the MFMA kernels below (32-token tiles up to 64 tokens, 128-token
+ * tiles beyond).  Results
  * agree within the same tolerance either way (they are not bitwise
  * identical: the two paths sum the blocks in different orders).
  * An MFMA launch of at most 256 output tiles (32 or 128 tokens x 128 or 256

@@ -96,6 +96,33 @@ template <int F> struct KW {
     static_assert(NW * 32 * TI == BM * BN / 32, "the waves cover the workgroup tile");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
+
+// Narrow tile for launches of up to 64 tokens: 32 tokens x 128 weight rows
+// per group of four waves, wave w alone on weight rows 32w .. 32w+31 (one A
+// tile), so that a few tokens do not pay for the 96 rows of a 128-token tile
+// past M.  A stage image is the 32 activation rows (608 chunks in ten wave
+// loads; lanes past the last chunk re-load it into padding), then the 128
+// weight rows.  A split launch of fewer workgroups than CUs runs two such
+// groups per workgroup (G = 2), each with its own stage buffers on half of
+// the part's super-blocks, stepping through the same barriers; group 1 hands
+// its sums to group 0 through LDS at the end (the same order on every call).
+constexpr int NBM = 32;                        // tokens per narrow tile
+constexpr int NXQ = 10;                        // wave loads of activation chunks
+template <int F, int G> struct KN {
+    using W = KW<F>;
+    static constexpr int NW = 4 * G;                         // waves per workgroup
+    static constexpr int BN = 128;                           // weight rows per workgroup tile
+    static constexpr int WQ = BN * W::WC / kWave;            // 14, 18 or 28 wave loads of weight chunks
+    static constexpr int NQ = NXQ + WQ;                      // 24, 28 or 38
+    static constexpr int PER_WAVE = (NQ + 3) / 4;            // 6, 7 or 10
+    static constexpr int WOFF = NXQ * 1024;
+    static constexpr int STAGE = NQ * 1024;                  // 24,576, 28,672 or 38,912 bytes
+    static constexpr int D8 = G * NBUF * STAGE;              // per-wave f32 d8 of its 32 rows
+    static constexpr int LDS_BYTES = D8 + NW * 32 * 4;
+    static_assert(NBM * XC <= NXQ * kWave && WQ * kWave == BN * W::WC && NQ > 4 * (PER_WAVE - 1),
+                  "a stage splits into whole wave loads; only the last round of loads has gaps");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
+};
 }  // namespace mk
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -132,79 +159,108 @@ __device__ __forceinline__ void q4k_sc_m(uint32_t s0, uint32_t s1, uint32_t s2, 
     }
 }
 
-template <int F, bool SPLIT>
+template <int F, bool SPLIT, bool NARROW = false, int G = 1>
 __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
                                               float *__restrict__ y, int M, int N, int ns, int tiles_m) {
     using namespace mk;
     using W = KW<F>;
-    constexpr int WC = W::WC, WQ = W::WQ, NQ = W::NQ, PER_WAVE = W::PER_WAVE, WROW = W::WROW, STAGE = W::STAGE,
-                  D8 = W::D8, BN = W::BN, TI = W::TI;
-    (void)WQ;
+    using KT = KN<F, G>;
+    static_assert(G == 1 || (G == 2 && NARROW && SPLIT), "K groups only on split launches of the narrow tile");
+    constexpr int WC = W::WC, WROW = W::WROW;
+    constexpr int NWG = NARROW ? 4 : NW;                 // waves per K group
+    constexpr int XQN = NARROW ? NXQ : XQ;               // wave loads of activation chunks
+    constexpr int NQ = NARROW ? KT::NQ : W::NQ, PER_WAVE = NARROW ? KT::PER_WAVE : W::PER_WAVE;
+    constexpr int STAGE = NARROW ? KT::STAGE : W::STAGE, D8 = NARROW ? KT::D8 : W::D8;
+    constexpr int BN = NARROW ? KT::BN : W::BN, TI = NARROW ? 1 : W::TI, TBM = NARROW ? NBM : BM;
+    constexpr int WO = NARROW ? KT::WOFF : WOFF;         // weight rows start (bytes into a stage buffer)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63;
-    const int wave = uniform(t >> 6);
-    // SPLIT: the grid holds every tile twice; part 0 takes the first half
-    // of each row's super-blocks, part 1 the rest, and both add into the
-    // zeroed output.
+    const int wave = uniform(NARROW ? (t >> 6) & 3 : t >> 6);
+    const int grp = G == 1 ? 0 : uniform(t >> 8);       // K group: its own stage buffers and super-blocks
+    // SPLIT: the grid holds every tile twice, one per part of K, and both
+    // parts add into the zeroed output.  Part p of P = ksplit * G (grid part
+    // and K group) takes super-blocks [ceil(p ns / P), ceil((p + 1) ns / P))
+    // (the caller keeps ns >= P).
     constexpr int ksplit = SPLIT ? 2 : 1;
+    constexpr int P = ksplit * G;
     const int tiles = (int)gridDim.x / ksplit;
-    const int tile = (int)blockIdx.x % tiles, part = (int)blockIdx.x / tiles;
+    const int tile = (int)blockIdx.x % tiles, gpart = (int)blockIdx.x / tiles;
     const int mt = tile % tiles_m, nt = tile / tiles_m;
-    const int m0 = mt * BM, n0 = nt * BN;
-    const int sh = SPLIT ? (ns + 1) / 2 : ns;
-    const int s0 = part ? sh : 0, s1 = part ? ns : sh;   // this part's super-blocks [s0, s1)
+    const int m0 = mt * TBM, n0 = nt * BN;
+    auto first_sb = [&](int p) { return (p * ns + P - 1) / P; };
+    const int s0 = first_sb(G * gpart + grp), s1 = first_sb(G * gpart + grp + 1);   // this part's [s0, s1)
+    // every wave of the workgroup passes the same barriers: the K groups
+    // step together for the larger of their super-block counts
+    const int nsteps = G == 1 ? s1 - s0
+                              : max(first_sb(G * gpart + 1) - first_sb(G * gpart),
+                                    first_sb(G * gpart + 2) - first_sb(G * gpart + 1));
     const uint32_t xrow = (uint32_t)ns * kQ8KBytes, wrow = (uint32_t)ns * W::WB;
 
-    // DMA: wave load q = wave + 8k (k < PER_WAVE) of a stage is chunk load q
-    // of the stage image (activation chunks for q < 38, weight chunks after)
-    // and lands at byte 1024 q of the stage buffer; a wave whose last q is
-    // past NQ repeats its previous load instead (same bytes to the same
-    // place), so that every wave issues the same count.  Rows past the matrix
-    // re-read its last row (their results are not stored).
+    // DMA: wave load q = wave + 8k (k < PER_WAVE; narrow: 4k) of a stage is
+    // chunk load q of the stage image (activation chunks for q < 38, or 10,
+    // weight chunks after) and lands at byte 1024 q of the stage buffer; a
+    // wave whose last q is past NQ repeats its previous load instead (same
+    // bytes to the same place), so that every wave issues the same count.
+    // Rows past the matrix re-read its last row (their results are not
+    // stored).
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(xq + (int64_t)m0 * xrow), 0, (int)((uint32_t)min(M - m0, BM) * xrow), 0x00020000);
+        (void *)(xq + (int64_t)m0 * xrow), 0, (int)((uint32_t)min(M - m0, TBM) * xrow), 0x00020000);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(w + (int64_t)n0 * wrow), 0, (int)((uint32_t)min(N - n0, BN) * wrow), 0x00020000);
     uint32_t voff[PER_WAVE];
 #pragma unroll
     for (int k = 0; k < PER_WAVE; ++k) {
-        const int q = wave + NW * k;
+        const int q = wave + NWG * k;
         if (q >= NQ) {
             voff[k] = voff[k - 1];
-        } else if (q < XQ) {
-            const int f = kWave * q + lane, row = f / XC, c = f - XC * row;
+        } else if (q < XQN) {
+            const int f0 = kWave * q + lane, f = NARROW ? min(f0, NBM * XC - 1) : f0;
+            const int row = f / XC, c = f - XC * row;
             voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (uint32_t)xchunk(c);
         } else {
-            const int f = kWave * (q - XQ) + lane, row = f / WC, c = f - WC * row;
+            const int f = kWave * (q - XQN) + lane, row = f / WC, c = f - WC * row;
             voff[k] = (uint32_t)(min(n0 + row, N - 1) - n0) * wrow + (uint32_t)W::wchunk(c);
         }
     }
-    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+    uint8_t *const ldsg = lds + grp * (NBUF * STAGE);   // this K group's stage buffers
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(ldsg);
     const uint32_t m0w = (uint32_t)uniform((int)(lds0 + 1024u * wave));
     constexpr int KL = PER_WAVE - 1;
     // LDS offset of the last load of a stage (or of the load it repeats)
-    const uint32_t last_off = (uint32_t)uniform(1024 * NW * (wave + NW * KL >= NQ ? KL - 1 : KL));
+    const uint32_t last_off = (uint32_t)uniform(1024 * NWG * (wave + NWG * KL >= NQ ? KL - 1 : KL));
     auto dma = [&](int s, int b) __attribute__((always_inline)) {
         const int sx = s * kQ8KBytes, sw = s * W::WB;
         const uint32_t base = m0w + (uint32_t)(b * STAGE);
         auto one = [&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
-            const bool isw = wave + NW * k >= XQ;   // a repeated load is a weight load
+            const bool isw = wave + NWG * k >= XQN;   // a repeated load is a weight load
             const int soff = uniform(isw ? sw : sx);
             if constexpr (k == KL)
                 buffer16_to_lds<0>(isw ? wr : xr, base + last_off, voff[k], soff);
             else
-                buffer16_to_lds<1024 * NW * k>(isw ? wr : xr, base, voff[k], soff);
+                buffer16_to_lds<1024 * NWG * k>(isw ? wr : xr, base, voff[k], soff);
         };
         for_each_index(one, std::make_integer_sequence<int, PER_WAVE>());
     };
 
     const int lr = lane & 31, lh = lane >> 5;
     // the wave's tokens 32 TI wm .. and weight rows 32 wn ..
-    const int wm = TI == 4 ? 0 : wave & 1, wn = TI == 4 ? wave : wave >> 1;
+    const int wm = (NARROW || TI == 4) ? 0 : wave & 1, wn = (NARROW || TI == 4) ? wave : wave >> 1;
     const int xa = XROW * (32 * TI * wm + lr);           // A row lr of the wave (tile i: +32i rows)
-    const int wb = WOFF + WROW * (32 * wn + lr);         // B row 32 wn + lr
-    float *d8w = reinterpret_cast<float *>(lds + D8 + 4 * 32 * TI * wave);
+    const int wb = WO + WROW * (32 * wn + lr);           // B row 32 wn + lr
+    float *d8w = reinterpret_cast<float *>(lds + D8 + 4 * 32 * TI * (NWG * grp + wave));
+    // d8 of the wave's activation rows into its private array (narrow: 32
+    // rows, lanes 32..63 writing the same values as 0..31)
+    auto store_d8 = [&](const uint8_t *sb) __attribute__((always_inline)) {
+        if constexpr (NARROW) {
+            d8w[lr] = *reinterpret_cast<const float *>(sb + XROW * lr + 288);
+        } else if constexpr (TI == 4) {
+            d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * lane + 288);
+            d8w[64 + lane] = *reinterpret_cast<const float *>(sb + XROW * (64 + lane) + 288);
+        } else {
+            d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * (64 * wm + lane) + 288);
+        }
+    };
 
     v16i bias;
 #pragma unroll
@@ -246,9 +302,7 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
     // (128 tokens), so that each B operand is built once per workgroup.
     auto compute = [&](const uint8_t *sb) __attribute__((always_inline)) {
         if constexpr (F == F_Q2_K) {
-            // d8 of the 128 activation rows into the wave's private array
-            d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * lane + 288);
-            d8w[64 + lane] = *reinterpret_cast<const float *>(sb + XROW * (64 + lane) + 288);
+            store_d8(sb);
             // the B tile's 16 scale bytes and d, dmin
             const uint4 scl = rd16(sb + wb);
             const uint32_t dd = rd4(sb + wb + 92);
@@ -266,15 +320,15 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
                 return b;
             };
             // value term: eight K-steps of int8 MFMA, int32 accumulation from the bias
-            v16i v[4];
+            v16i v[TI];
     #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = bias;
+            for (int i = 0; i < TI; ++i) v[i] = bias;
     #pragma unroll
             for (int kt = 0; kt < 8; ++kt) {
                 if (kt == 4) qs = rd16(sb + wb + 16 + 32 + 16 * lh);
                 const v4i b = build_b(kt, qs);
     #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < TI; ++i) {
                     const v4i a = as_v4i(rd16(sb + xa + XROW * 32 * i + 32 * kt + 16 * lh));
                     v[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v[i], 0, 0, 0);
                 }
@@ -290,7 +344,7 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
             const v8h bm = mins_to_h(mlo, mhi);
             const v16f z = {};
     #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < TI; ++i) {
                 const v8h am = i16x8_to_h(rd16(sb + xa + XROW * 32 * i + 256 + 16 * lh));
                 const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(am, bm, z, 0, 0, 0);
                 // d8 of output rows 8a4 + 4lh + c, four at a time
@@ -310,9 +364,7 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
                 }
             }
         } else if constexpr (F == F_Q4_K) {
-            // d8 of the 128 activation rows into the wave's private array
-            d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * lane + 288);
-            d8w[64 + lane] = *reinterpret_cast<const float *>(sb + XROW * (64 + lane) + 288);
+            store_d8(sb);
             // the B tile row's d, dmin and packed scales
             const uint32_t dd = rd4(sb + wb), s0 = rd4(sb + wb + 4), s1 = rd4(sb + wb + 8), s2 = rd4(sb + wb + 12);
             int sc[8], mm[8];
@@ -321,40 +373,48 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
             // value term: sub-block kt is K-step kt, the 4-bit codes of qs
             // chunk kt/2 (low nibbles for even kt, high for odd); one exact
             // int32 tile per sub-block, V += sc * I in int32
-            int V[4][16];
+            int V[TI][16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) V[i][r] = 0;
-            // The 32 steps t = 4 kt + i are software-pipelined: the MFMA of
+            // The 8 TI steps t = TI kt + i are software-pipelined: the MFMA of
             // step t+1 is issued before the scale mads of step t (two int32
             // tiles live), its A operand is read one step ahead and each
-            // 16-byte code chunk (K-steps 2c, 2c+1) three steps before its
-            // first use, so that neither the LDS reads nor the MFMA latency
-            // stall the wave.
+            // 16-byte code chunk (K-steps 2c, 2c+1) before its first use (TI
+            // = 4: three steps; narrow: one, right after the last B operand
+            // from the chunk before), so that neither the LDS reads nor the
+            // MFMA latency stall the wave.
             auto nibbles = [](const uint4 &q, int kt) __attribute__((always_inline)) {
                 const uint32_t sh = 4u * (uint32_t)(kt & 1);
                 return v4i{(int)((q.x >> sh) & 0x0f0f0f0fu), (int)((q.y >> sh) & 0x0f0f0f0fu),
                            (int)((q.z >> sh) & 0x0f0f0f0fu), (int)((q.w >> sh) & 0x0f0f0f0fu)};
             };
             auto read_a = [&](int t) __attribute__((always_inline)) {
-                return as_v4i(rd16(sb + xa + XROW * 32 * (t & 3) + 32 * (t >> 2) + 16 * lh));
+                return as_v4i(rd16(sb + xa + XROW * 32 * (t % TI) + 32 * (t / TI) + 16 * lh));
             };
+            constexpr int T = 8 * TI;
             const v16i zero = {};
             uint4 qs = rd16(sb + wb + 16 + 16 * lh);   // chunk 0
             v4i b = nibbles(qs, 0);
             v4i an = read_a(1);
             v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(read_a(0), b, zero, 0, 0, 0);
 #pragma unroll
-            for (int t = 0; t < 32; ++t) {
-                const int kt = t >> 2, i = t & 3;
+            for (int t = 0; t < T; ++t) {
+                const int kt = t / TI, i = t % TI;
                 v16i In = zero;
-                if (t + 1 < 32) {
-                    if (((t + 1) & 3) == 0) b = nibbles(qs, (t + 1) >> 2);
+                if (t + 1 < T) {
+                    const int kn = (t + 1) / TI;
+                    if ((t + 1) % TI == 0) b = nibbles(qs, kn);
                     In = __builtin_amdgcn_mfma_i32_32x32x32_i8(an, b, zero, 0, 0, 0);
-                    if (t + 2 < 32) an = read_a(t + 2);
+                    if (t + 2 < T) an = read_a(t + 2);
                     // the next chunk, once the last B operand built from this one is out
-                    if (i == 0 && (kt & 1) == 1 && kt < 7) qs = rd16(sb + wb + 16 + 32 * ((kt + 1) >> 1) + 16 * lh);
+                    if constexpr (TI == 4) {
+                        if (i == 0 && (kt & 1) == 1 && kt < 7) qs = rd16(sb + wb + 16 + 32 * ((kt + 1) >> 1) + 16 * lh);
+                    } else {
+                        if ((t + 1) % TI == 0 && (kn & 1) == 1 && kn < 7)
+                            qs = rd16(sb + wb + 16 + 32 * ((kn + 1) >> 1) + 16 * lh);
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -379,7 +439,7 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
             for (int e = 0; e < 8; ++e) bm[e] = (_Float16)(lh ? mm[4 + (e >> 1)] : mm[e >> 1]);
             const v16f z = {};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < TI; ++i) {
                 const v8h am = i16x8_to_h(rd16(sb + xa + XROW * 32 * i + 256 + 16 * lh));
                 const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(am, bm, z, 0, 0, 0);
                 // d8 of output rows 8a4 + 4lh + c, four at a time
@@ -405,20 +465,19 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
             // I_g = sum q x; V = sum_g sc_g I_g in int32 (v_mad_i32_i24), and
             // the offset of 32 is sum_g 32 sc_g bsum_g, one f16 MFMA over the
             // block sums: the product is d8 d (V - Mn).
-            // d8 of the wave's 64 activation rows into its private array
-            d8w[lane] = *reinterpret_cast<const float *>(sb + XROW * (64 * wm + lane) + 288);
+            store_d8(sb);
             const uint4 scl = rd16(sb + wb + 192);
             auto scale = [&](int g) __attribute__((always_inline)) {
                 const uint32_t sw = g < 4 ? scl.x : g < 8 ? scl.y : g < 12 ? scl.z : scl.w;
                 return (int)(int8_t)(sw >> (8 * (g & 3)));
             };
             auto rd8 = [](const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); };
-            int V[2][16];
+            int V[TI][16];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) V[i][r] = 0;
-            // Steps t = 8 (2 hh + gg) + 2 k + i, software-pipelined as for
+            // Steps t = TI (4 (2 hh + gg) + k) + i, software-pipelined as for
             // Q4_K: the MFMA of step t+1 goes out before the mads of step t,
             // A operands are read one step ahead, and the code bytes of the
             // next (hh, gg) pair (this lane's 8 values of its groups 8hh + 2k
@@ -431,7 +490,11 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
                 return Codes{rd8(sb + wb + 64 * hh + 16 * gg + 8 * lh), rd8(sb + wb + 64 * hh + 32 + 16 * gg + 8 * lh),
                              rd8(sb + wb + 128 + 32 * hh + 16 * gg + 8 * lh)};
             };
-            auto group = [](int t) { return 8 * (t >> 4) + 2 * ((t >> 1) & 3) + ((t >> 3) & 1); };
+            // group of step t: index gi = t / TI = 4 (2 hh + gg) + k
+            auto group = [](int t) {
+                const int gi = t / TI;
+                return 8 * (gi >> 3) + 2 * (gi & 3) + ((gi >> 2) & 1);
+            };
             auto build_b = [](const Codes &q, int k) __attribute__((always_inline)) {
                 const uint2 ql = (k & 1) ? q.qb : q.qa;
                 const uint32_t nsh = 4u * (uint32_t)(k >> 1), hsh = 2u * (uint32_t)k;
@@ -440,29 +503,30 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
                 return (long)(((uint64_t)b1 << 32) | b0);
             };
             auto read_a = [&](int t) __attribute__((always_inline)) {
-                const uint2 av = rd8(sb + xa + XROW * 32 * (t & 1) + 16 * group(t) + 8 * lh);
+                const uint2 av = rd8(sb + xa + XROW * 32 * (t % TI) + 16 * group(t) + 8 * lh);
                 return (long)(((uint64_t)av.y << 32) | av.x);
             };
+            constexpr int T = 16 * TI;
             const v16i zero = {};
             Codes qc = read_codes(0), qn = read_codes(1);
             long b = build_b(qc, 0);
             long an = read_a(1);
             v16i I = __builtin_amdgcn_mfma_i32_32x32x16_i8(read_a(0), b, zero, 0, 0, 0);
 #pragma unroll
-            for (int t = 0; t < 32; ++t) {
-                const int i = t & 1;
+            for (int t = 0; t < T; ++t) {
+                const int i = t % TI;
                 v16i In = zero;
-                if (t + 1 < 32) {
-                    const int t1 = t + 1;
-                    if ((t1 & 1) == 0) {                       // a new group: new B operand
-                        if ((t1 & 7) == 0) {                   // and a new (hh, gg) pair
+                if (t + 1 < T) {
+                    const int t1 = t + 1, g1 = t1 / TI;
+                    if (t1 % TI == 0) {                        // a new group: new B operand
+                        if ((g1 & 3) == 0) {                   // and a new (hh, gg) pair
                             qc = qn;
-                            if ((t1 >> 3) + 1 < 4) qn = read_codes((t1 >> 3) + 1);
+                            if ((g1 >> 2) + 1 < 4) qn = read_codes((g1 >> 2) + 1);
                         }
-                        b = build_b(qc, (t1 >> 1) & 3);
+                        b = build_b(qc, g1 & 3);
                     }
                     In = __builtin_amdgcn_mfma_i32_32x32x16_i8(an, b, zero, 0, 0, 0);
-                    if (t + 2 < 32) an = read_a(t + 2);
+                    if (t + 2 < T) an = read_a(t + 2);
                 }
                 const int sc = scale(group(t));
 #pragma unroll
@@ -483,7 +547,7 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
             for (int e = 0; e < 8; ++e) bm[e] = (_Float16)(32 * (lh ? scale(8 + e) : scale(e)));
             const v16f z = {};
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < TI; ++i) {
                 const v8h am = i16x8_to_h(rd16(sb + xa + XROW * 32 * i + 256 + 16 * lh));
                 const v16f mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(am, bm, z, 0, 0, 0);
                 const float4 *p = reinterpret_cast<const float4 *>(d8w + 32 * i + 4 * lh);
@@ -502,17 +566,33 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
         }
     };
 
-    // Super-block s lives in buffer (s - s0) % 2.  At step s: wait for this
-    // wave's loads of s, the barrier publishes every wave's (and tells that
-    // s-1's buffer is free), the DMA of s+1 goes into it, then s is computed.
+    // Super-block s0 + j lives in buffer j % 2.  At step j: wait for this
+    // wave's loads of it, the barrier publishes every wave's (and tells that
+    // the previous one's buffer is free), the DMA of the next goes into it,
+    // then it is computed.  A K group with fewer super-blocks than the other
+    // passes its extra step's barrier without work or loads.
     dma(s0, 0);
-    for (int s = s0; s < s1; ++s) {
+    for (int j = 0; j < nsteps; ++j) {
         asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (s + 1 < s1) dma(s + 1, (s + 1 - s0) & 1);
-        compute(lds + ((s - s0) & 1) * STAGE);
+        if (s0 + j + 1 < s1) dma(s0 + j + 1, (j + 1) & 1);
+        if (G == 1 || s0 + j < s1) compute(ldsg + (j & 1) * STAGE);
     }
     // no LDS-DMA write may still be in flight when the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (G == 2) {
+        // group 1 hands its sums to group 0 through LDS ([wave][r][lane],
+        // over the stage buffers), which adds them to its own
+        float *red = reinterpret_cast<float *>(lds) + 1024 * wave + lane;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (grp == 1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[64 * r] = acc[0][r];
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (grp == 1) return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][r] += red[64 * r];
+    }
 
     const int n = n0 + 32 * wn + lr;
     if (n < N) {
@@ -544,6 +624,16 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k_split(const uint8_t *__rest
     matmul_k_body<F, true>(w, xq, y, M, N, ns, tiles_m);
 }
 
+// The narrow tile (32 tokens x 128 weight rows) for launches of up to 64
+// tokens: one group of four waves, K whole or split in two, or (G = 2) two
+// groups on the halves of each split part.
+template <int F, bool SPLIT, int G>
+__global__ __launch_bounds__(256 * G) void k_matmul_k_narrow(const uint8_t *__restrict__ w,
+                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                             int M, int N, int ns, int tiles_m) {
+    matmul_k_body<F, SPLIT, true, G>(w, xq, y, M, N, ns, tiles_m);
+}
+
 // Largest super-block count whose tile offsets fit the 32-bit buffer offsets
 // (128 activation rows of ns * 292 bytes; 256 weight rows take fewer).
 constexpr int64_t kMatmulKMaxBlocks = (((int64_t)1 << 31) - 1) / (mk::BM * kQ8KBytes);
@@ -556,12 +646,26 @@ static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N
     if (M <= small_tokens(F)) return launch_matvec_tokens(F, w, xq, y, M, N, ns, st);
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
-    int tiles_m = (M + mk::BM - 1) / mk::BM;
-    const int64_t tiles = (int64_t)tiles_m * ((N + mk::KW<F>::BN - 1) / mk::KW<F>::BN);
+    // up to 64 tokens: the 32-token tile (a 128-token tile would compute
+    // and drop the rows past M)
+    const bool narrow = M <= 2 * mk::NBM;
+    const int bm = narrow ? mk::NBM : mk::BM, bn = narrow ? mk::KN<F, 1>::BN : mk::KW<F>::BN;
+    int tiles_m = (M + bm - 1) / bm;
+    const int64_t tiles = (int64_t)tiles_m * ((N + bn - 1) / bn);
     const bool split = tiles <= kSplitTiles && ns >= 2;
-    const void *kern = split ? (const void *)k_matmul_k_split<F> : (const void *)k_matmul_k<F>;
-    static int lds_ok[kLdsDevices] = {}, lds_ok_split[kLdsDevices] = {};
-    const hipError_t e = allow_dynamic_lds(kern, (size_t)mk::KW<F>::LDS_BYTES, split ? lds_ok_split : lds_ok);
+    // fewer narrow workgroups than CUs: two K groups per workgroup, each on
+    // half of its part of K (at least one super-block each)
+    const bool groups = narrow && split && tiles * 2 < kCUs && ns >= 4;
+    static int lds_ok[5][kLdsDevices] = {};
+    const int v = groups ? 4 : narrow ? (split ? 3 : 2) : (split ? 1 : 0);
+    const void *kern = v == 4   ? (const void *)k_matmul_k_narrow<F, true, 2>
+                       : v == 3 ? (const void *)k_matmul_k_narrow<F, true, 1>
+                       : v == 2 ? (const void *)k_matmul_k_narrow<F, false, 1>
+                       : v == 1 ? (const void *)k_matmul_k_split<F>
+                                : (const void *)k_matmul_k<F>;
+    const int lds_bytes = groups ? mk::KN<F, 2>::LDS_BYTES : narrow ? mk::KN<F, 1>::LDS_BYTES : mk::KW<F>::LDS_BYTES;
+    const int threads = groups ? 512 : narrow ? 256 : mk::NT;
+    const hipError_t e = allow_dynamic_lds(kern, (size_t)lds_bytes, lds_ok[v]);
     if (e != hipSuccess) return e;
     if (split) {
         const hipError_t ez = launch_zero_f32(y, (int64_t)M * N, st);
@@ -569,8 +673,7 @@ static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N
     }
     const int ksplit = split ? 2 : 1;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&ns, (void *)&tiles_m};
-    return hipLaunchKernel(kern, dim3((unsigned)(tiles * ksplit)), dim3(mk::NT), args, (size_t)mk::KW<F>::LDS_BYTES,
-                           st);
+    return hipLaunchKernel(kern, dim3((unsigned)(tiles * ksplit)), dim3(threads), args, (size_t)lds_bytes, st);
 }
 
 hipError_t launch_matmul_q2_k_mfma(const void *w, const void *xq, float *y, int M, int N, int ns, hipStream_t st) {

@@ -27,15 +27,13 @@ enum Fmt { F_Q4_0 = 0, F_Q8_0 = 1, F_Q2_K = 2, F_Q4_K = 3, F_Q6_K = 4, F_Q4_1 = 
 // kernel with several tokens per weight pass; larger counts run the MFMA
 // prefill kernels.  The decode kernel's cost is flat within each group of
 // tokens that share a weight pass (up to 2, 4 or 8) and steps up at the next
-// group; the MFMA kernels cost about the same for any M up to a tile (32
-// tokens for the 32-value formats, 128 for the K-quants).  The switch is
-// where the two meet at N = 12288, K = 4096 (us, decode kernel / MFMA):
-// Q4_0 M = 8 13.1 / 14.5, M = 10 22.1 / 15.3; Q4_1 M = 4 12.1 / 17.9, M = 6
-// 19.2 / 17.4; Q4_K keeps the decode kernel longest, its units staying in
-// registers and its MFMA kernel the slowest at small M; Q6_K, with the most
-// unpacking per token, leaves it first among the K-quants.
+// group; the MFMA kernels cost about the same for any M up to their 32-token
+// tile.  The switch is where the two meet at N = 12288, K = 4096 (us,
+// decode kernel / MFMA): Q4_0 M = 8 13.1 / 14.5, M = 10 22.1 / 15.3; Q4_1
+// M = 4 12.1 / 17.9, M = 6 19.2 / 17.4; Q4_K M = 4 9.1 / 11.2, M = 8 13.7 /
+// 11.3; Q2_K M = 2 7.2 / 10.2, M = 4 10.7 / 10.1.
 constexpr int small_tokens(int fmt) {
-    return fmt == F_Q4_K ? 32 : fmt == F_Q2_K ? 10 : (fmt == F_Q4_0 || fmt == F_Q6_K) ? 8 : 4;
+    return fmt == F_Q2_K ? 2 : fmt == F_Q4_0 ? 8 : 4;
 }
 hipError_t launch_matvec_tokens(int fmt, const void *w, const void *xq, float *y, int M, int N, int nb,
                                 hipStream_t st);

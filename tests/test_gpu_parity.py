@@ -310,6 +310,13 @@ MATMUL_CASES = [
     ("q4_k", 128, 256, 256), ("q4_k", 130, 257, 512), ("q4_k", 257, 300, 2304), ("q4_k", 3, 520, 7936),
     ("q6_k", 1, 8, 256), ("q6_k", 9, 70, 1024), ("q6_k", 5, 33, 1280),
     ("q6_k", 128, 128, 256), ("q6_k", 130, 257, 512), ("q6_k", 257, 129, 2304), ("q6_k", 65, 300, 7936),
+    # the K-quants' 32-token tile: two K groups per workgroup (uneven
+    # super-block counts, one super-block per group, 64 tokens in two tiles),
+    # one group with K split in two (2 super-blocks) or whole (1, or a grid of
+    # more than 256 tiles)
+    ("q4_k", 50, 129, 1280), ("q2_k", 17, 129, 1024), ("q6_k", 64, 257, 4096), ("q6_k", 12, 130, 2304),
+    ("q6_k", 40, 200, 512), ("q2_k", 20, 70, 256), ("q4_k", 64, 300, 256), ("q2_k", 40, 16641, 512),
+    ("q4_k", 45, 16390, 768), ("q2_k", 31, 260, 8192),
     # Q4_1 and Q5_1 on the same kernel, the offset term on an f32 MFMA
     ("q4_1", 1, 8, 32), ("q4_1", 9, 70, 1024), ("q4_1", 5, 3, 96), ("q4_1", 130, 129, 160),
     ("q4_1", 131, 255, 128), ("q4_1", 65, 130, 96), ("q4_1", 63, 127, 2048), ("q4_1", 129, 257, 64),
@@ -358,21 +365,25 @@ SMALL_M_CASES = [
     ("q4_k", 3, 130, 4096), ("q4_k", 8, 12288, 4096), ("q4_k", 10, 31, 11008), ("q4_k", 32, 65, 2304),
     ("q4_k", 25, 129, 4096), ("q4_k", 33, 33, 4096),
     ("q6_k", 5, 130, 4096), ("q6_k", 16, 65, 2304), ("q6_k", 9, 33, 11008),
-    # the largest token counts on the decode kernel (8 for Q4_0 and Q6_K, 10
-    # for Q2_K, 32 for Q4_K, 4 for the other formats); the cases above past
-    # those counts run on the MFMA kernels
+    # the largest token counts on the decode kernel (8 for Q4_0, 2 for Q2_K,
+    # 4 for the other formats), and the first past them on the MFMA kernels;
+    # the cases above past those counts run on the MFMA kernels
     ("q6_k", 8, 65, 2304), ("q6_k", 7, 33, 11008), ("q8_0", 10, 70, 11008), ("q8_0", 9, 257, 4096),
     ("q5_0", 10, 9, 8192), ("q2_k", 10, 33, 11008), ("q2_k", 9, 130, 4096),
     ("q5_0", 4, 130, 4096), ("q5_0", 3, 70, 11008), ("q4_1", 4, 130, 4096), ("q5_1", 4, 33, 4128),
     ("q8_0", 3, 70, 11008), ("q4_0", 7, 65, 8192), ("q4_1", 5, 70, 4128), ("q5_1", 5, 130, 8192),
+    ("q2_k", 3, 70, 4096), ("q4_k", 4, 33, 11008), ("q4_k", 5, 130, 2304), ("q6_k", 4, 65, 4096),
+    ("q6_k", 5, 70, 2304),
     # the first counts on the 32-token MFMA tile, with two K groups per
     # workgroup (K of 16 and 17 blocks: two stages per group, and an odd
     # last stage) and without (K of 3 blocks, no split)
     ("q4_0", 9, 130, 512), ("q8_0", 9, 257, 544), ("q5_0", 5, 9, 544), ("q4_1", 9, 33, 96),
     ("q5_1", 12, 200, 512),
     # rows per wave past the 2048-wave floor over the grid's token rows: 8 rows
-    # (one pass of 8 tokens), 4 rows (4 tokens), 4 rows (two passes of 8)
-    ("q4_0", 8, 16389, 1024), ("q8_0", 4, 8197, 1024), ("q4_k", 16, 4101, 512),
+    # (one pass of 8 tokens), 4 rows (4 tokens, Q8_0 and Q4_K)
+    ("q4_0", 8, 16389, 1024), ("q8_0", 4, 8197, 1024), ("q4_k", 4, 8203, 512),
+    # the 32-token tile on a ragged 4101 rows
+    ("q4_k", 16, 4101, 512),
 ]
 
 

@@ -186,7 +186,7 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     constexpr int TBM = NARROW ? NBM : BM;           // tokens per tile
     constexpr int TI = NARROW ? 1 : 2, TJ = NARROW ? 1 : 2;   // A and B tiles per wave
     const int t = threadIdx.x, lane = t & 63;
-    const int wave = uniform((t >> 6) & 3);
+    const int wave = uniform(G == 1 ? t >> 6 : (t >> 6) & 3);
     const int grp = G == 1 ? 0 : uniform(t >> 8);   // K group: its own stage buffers and blocks
     // SPLIT: the grid holds every tile twice, one per part of K, and both
     // parts add into the zeroed output.  Part p of P = ksplit * G (grid part
@@ -202,8 +202,9 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const int S_all = (nb + 1) >> 1;
     auto first_stage = [&](int p) { return p * S_all / P; };
     const int part = G * gpart + grp;
-    const int kb0 = 2 * first_stage(part);                               // this part's first block
-    const int nbp = min(2 * first_stage(part + 1), nb) - kb0;           // and its block count
+    const int kb1 = 2 * ((nb + 2) / 4);   // G = 1: part 0's blocks (whole stages)
+    const int kb0 = G == 1 ? (part ? kb1 : 0) : 2 * first_stage(part);                     // this part's first block
+    const int nbp = G == 1 ? (SPLIT ? (part ? nb - kb1 : kb1) : nb) : min(2 * first_stage(part + 1), nb) - kb0;   // its count
     const int nst = (nbp + 1) >> 1;   // an odd block count leaves a last stage of one block
     // every wave of the workgroup passes the same barriers: the K groups
     // step together for the larger of their stage counts

@@ -188,7 +188,9 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
     const int mt = tile % tiles_m, nt = tile / tiles_m;
     const int m0 = mt * TBM, n0 = nt * BN;
     auto first_sb = [&](int p) { return (p * ns + P - 1) / P; };
-    const int s0 = first_sb(G * gpart + grp), s1 = first_sb(G * gpart + grp + 1);   // this part's [s0, s1)
+    const int sh = (ns + 1) / 2;
+    const int s0 = G == 1 ? (gpart ? sh : 0) : first_sb(G * gpart + grp);       // this part's [s0, s1)
+    const int s1 = G == 1 ? (SPLIT && !gpart ? sh : ns) : first_sb(G * gpart + grp + 1);
     // every wave of the workgroup passes the same barriers: the K groups
     // step together for the larger of their super-block counts
     const int nsteps = G == 1 ? s1 - s0
@@ -572,10 +574,18 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
     // then it is computed.  A K group with fewer super-blocks than the other
     // passes its extra step's barrier without work or loads.
     dma(s0, 0);
-    for (int j = 0; j < nsteps; ++j) {
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (s0 + j + 1 < s1) dma(s0 + j + 1, (j + 1) & 1);
-        if (G == 1 || s0 + j < s1) compute(ldsg + (j & 1) * STAGE);
+    if constexpr (G == 1) {
+        for (int s = s0; s < s1; ++s) {
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (s + 1 < s1) dma(s + 1, (s + 1 - s0) & 1);
+            compute(lds + ((s - s0) & 1) * STAGE);
+        }
+    } else {
+        for (int j = 0; j < nsteps; ++j) {
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (s0 + j + 1 < s1) dma(s0 + j + 1, (j + 1) & 1);
+            if (s0 + j < s1) compute(ldsg + (j & 1) * STAGE);
+        }
     }
     // no LDS-DMA write may still be in flight when the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

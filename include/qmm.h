@@ -205,10 +205,11 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
  * Up to 8 tokens (Q4_0; 2 for Q2_K, 4 for the other formats) run on the
  * decode matvec kernel, which streams each weight slice once per group of
  * 2, 4 or 8 tokens (one token: the decode launch itself); more tokens run
- * on the MFMA kernels below (32-token tiles up to 64 tokens, 128-token
- * tiles beyond).  Results
- * agree within the same tolerance either way (they are not bitwise
- * identical: the two paths sum the blocks in different orders).
+ * on the MFMA kernels below (32-token tiles up to 128 tokens for Q4_0,
+ * Q5_0, Q2_K and Q4_K and up to 64 for the other formats, 128-token tiles
+ * beyond).  Results agree within the same tolerance either way (they are
+ * not bitwise identical: the two paths sum the blocks in different
+ * orders).
  * An MFMA launch of at most 256 output tiles (32 or 128 tokens x 128 or 256
  * weight rows) splits K in two: y is first zeroed on the stream, then the two
  * halves of each output are added into it with f32 atomic adds (device

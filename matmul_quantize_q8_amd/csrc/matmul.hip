@@ -106,7 +106,7 @@ template <int WFMT> struct WF {
                   "stage splits into whole wave loads, evenly over the waves");
 };
 
-// Narrow tile for launches of up to 64 tokens: 32 tokens x 128 weight rows,
+// Narrow tile for launches of a few tokens: 32 tokens x 128 weight rows,
 // wave w alone on weight rows 32w .. 32w+31 (one 32 x 32 MFMA tile per
 // block).  A stage image is the tile's 32 activation rows (160 chunks, three
 // wave loads; lanes past the last chunk re-load it into padding slots), then
@@ -122,6 +122,13 @@ template <int WFMT> struct WF {
 // time; two waves per SIMD halve the chain (Q4_0 M = 8, N = 12288, K = 4096:
 // 18.4 -> 14.5 us).
 constexpr int NBM = 32;                    // tokens per narrow tile
+// Token counts up to which the narrow tile runs.  Past 64 tokens it runs
+// three or four token tiles per weight tile, which still beats the full
+// tile for Q4_0 and Q5_0 but not for the formats with more weight bytes per
+// block (12288 x 4096, us, full / narrow: Q4_0 M = 65 39.3 / 36.5, M = 128
+// 44.0 / 39.1; Q5_0 42.4 / 40.0, 47.6 / 43.5; Q8_0 38.2 / 47.5; Q4_1 44.7 /
+// 50.1; Q5_1 48.7 / 54.0).
+constexpr int narrow_tokens(int wfmt) { return (wfmt == F_Q4_0 || wfmt == F_Q5_0) ? 4 * NBM : 2 * NBM; }
 constexpr int NXL = 3;                     // wave loads of activation chunks
 template <int WFMT> struct WN {
     using F = WF<WFMT>;
@@ -792,8 +799,8 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_1_split(const uint8_t *
     matmul_body<F_Q5_1, true>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
-// The narrow tile (32 tokens x 128 weight rows) for launches of up to 64
-// tokens, every 32-value format, K in one part or split in two.
+// The narrow tile (32 tokens x 128 weight rows) for launches of up to
+// narrow_tokens tokens, every 32-value format, K in one part or split in two.
 template <int WFMT, bool SPLIT>
 __global__ __launch_bounds__(mm::NT, 2) void k_matmul_narrow(const uint8_t *__restrict__ w,
                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
@@ -920,9 +927,9 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
         hipLaunchKernelGGL(one, dim3((unsigned)grid), dim3(256), 0, st, wp, xp, y, M, N);
         return hipGetLastError();
     }
-    // up to 64 tokens: the 32-token tile (a 128-token tile would compute
+    // up to narrow_tokens: the 32-token tile (a 128-token tile would compute
     // and drop the rows past M)
-    const bool narrow = M <= 2 * mm::NBM;
+    const bool narrow = M <= mm::narrow_tokens(WFMT);
     int tiles_m = narrow ? (M + mm::NBM - 1) / mm::NBM : (M + mm::BM - 1) / mm::BM;
     const int64_t tiles = (int64_t)tiles_m * ((N + mm::BN - 1) / mm::BN);
     // A launch of at most one workgroup per CU leaves the CUs half idle and

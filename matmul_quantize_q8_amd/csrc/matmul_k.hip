@@ -97,7 +97,7 @@ template <int F> struct KW {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
 
-// Narrow tile for launches of up to 64 tokens: 32 tokens x 128 weight rows
+// Narrow tile for launches of a few tokens: 32 tokens x 128 weight rows
 // per group of four waves, wave w alone on weight rows 32w .. 32w+31 (one A
 // tile), so that a few tokens do not pay for the 96 rows of a 128-token tile
 // past M.  A stage image is the 32 activation rows (608 chunks in ten wave
@@ -107,6 +107,12 @@ template <int F> struct KW {
 // the part's super-blocks, stepping through the same barriers; group 1 hands
 // its sums to group 0 through LDS at the end (the same order on every call).
 constexpr int NBM = 32;                        // tokens per narrow tile
+// Token counts up to which the narrow tile runs: up to 128 for Q2_K and
+// Q4_K, whose full tiles of 256 weight rows leave half the CUs idle below
+// 129 tokens, 64 for Q6_K (12288 x 4096, us, full / narrow: Q2_K M = 65 32.1
+// / 24.0, M = 128 37.1 / 25.7; Q4_K 46.2 / 35.9, 52.7 / 37.3; Q6_K 44.3 /
+// 62.3, 49.8 / 63.7).
+constexpr int narrow_tokens(int f) { return f == F_Q6_K ? 2 * NBM : 4 * NBM; }
 constexpr int NXQ = 10;                        // wave loads of activation chunks
 template <int F, int G> struct KN {
     using W = KW<F>;
@@ -634,9 +640,9 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k_split(const uint8_t *__rest
     matmul_k_body<F, true>(w, xq, y, M, N, ns, tiles_m);
 }
 
-// The narrow tile (32 tokens x 128 weight rows) for launches of up to 64
-// tokens: one group of four waves, K whole or split in two, or (G = 2) two
-// groups on the halves of each split part.
+// The narrow tile (32 tokens x 128 weight rows) for launches of up to
+// narrow_tokens tokens: one group of four waves, K whole or split in two,
+// or (G = 2) two groups on the halves of each split part.
 template <int F, bool SPLIT, int G>
 __global__ __launch_bounds__(256 * G) void k_matmul_k_narrow(const uint8_t *__restrict__ w,
                                                              const uint8_t *__restrict__ xq, float *__restrict__ y,
@@ -656,9 +662,9 @@ static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N
     if (M <= small_tokens(F)) return launch_matvec_tokens(F, w, xq, y, M, N, ns, st);
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xq);
-    // up to 64 tokens: the 32-token tile (a 128-token tile would compute
+    // up to narrow_tokens: the 32-token tile (a 128-token tile would compute
     // and drop the rows past M)
-    const bool narrow = M <= 2 * mk::NBM;
+    const bool narrow = M <= mk::narrow_tokens(F);
     const int bm = narrow ? mk::NBM : mk::BM, bn = narrow ? mk::KN<F, 1>::BN : mk::KW<F>::BN;
     int tiles_m = (M + bm - 1) / bm;
     const int64_t tiles = (int64_t)tiles_m * ((N + bn - 1) / bn);

@@ -317,6 +317,10 @@ MATMUL_CASES = [
     ("q4_k", 50, 129, 1280), ("q2_k", 17, 129, 1024), ("q6_k", 64, 257, 4096), ("q6_k", 12, 130, 2304),
     ("q6_k", 40, 200, 512), ("q2_k", 20, 70, 256), ("q4_k", 64, 300, 256), ("q2_k", 40, 16641, 512),
     ("q4_k", 45, 16390, 768), ("q2_k", 31, 260, 8192),
+    # 65-128 tokens on the 32-token tiles (Q4_0, Q5_0, Q2_K, Q4_K): three or
+    # four token tiles, two K groups, a split without groups, no split
+    ("q4_0", 96, 4100, 1024), ("q4_0", 100, 130, 4096), ("q5_0", 120, 16500, 512), ("q5_0", 70, 257, 2080),
+    ("q2_k", 100, 8200, 1024), ("q2_k", 65, 129, 512), ("q4_k", 127, 300, 2304), ("q4_k", 128, 16390, 256),
     # Q4_1 and Q5_1 on the same kernel, the offset term on an f32 MFMA
     ("q4_1", 1, 8, 32), ("q4_1", 9, 70, 1024), ("q4_1", 5, 3, 96), ("q4_1", 130, 129, 160),
     ("q4_1", 131, 255, 128), ("q4_1", 65, 130, 96), ("q4_1", 63, 127, 2048), ("q4_1", 129, 257, 64),

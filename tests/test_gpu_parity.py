@@ -299,7 +299,9 @@ MATMUL_CASES = [
     # even block counts (the dword-plane kernel): 1..7 stages, ragged tiles
     ("q4_0", 1, 129, 64), ("q4_0", 131, 255, 128), ("q4_0", 70, 130, 192), ("q4_0", 257, 129, 256),
     ("q4_0", 3, 300, 320), ("q4_0", 200, 100, 448),
-    # token counts one past and one short of 64 (half a 128-token tile)
+    # token counts one past and one short of 64: Q8_0's last on the 32-token
+    # tile and first on the 128-token tile (Q4_0 and Q5_0 keep the 32-token
+    # tile up to 128)
     ("q4_0", 65, 130, 96), ("q4_0", 63, 127, 2048), ("q8_0", 65, 129, 160), ("q8_0", 63, 255, 2048),
     ("q8_0", 1, 8, 32), ("q8_0", 37, 200, 1024), ("q8_0", 128, 128, 4096), ("q8_0", 130, 129, 160),
     ("q8_0", 5, 3, 96), ("q8_0", 131, 255, 128), ("q8_0", 257, 129, 256), ("q8_0", 300, 700, 2080),
@@ -332,7 +334,7 @@ MATMUL_CASES = [
     ("q5_0", 129, 257, 64), ("q5_0", 128, 128, 4096),
     # long rows: 1025 blocks (an odd count), 128 super-blocks
     ("q4_0", 129, 65, 32800), ("q5_1", 65, 33, 32800), ("q2_k", 65, 129, 32768), ("q6_k", 33, 65, 32768),
-    # 17-64 tokens: the 32-token tile; odd block counts, K split in two and
+    # 17-64 tokens on the 32-token tile; odd block counts, K split in two and
     # in one part (fewer than 4 blocks, or more than 256 tiles), ragged M and N
     ("q4_0", 17, 300, 160), ("q4_0", 33, 129, 96), ("q4_0", 64, 16577, 256), ("q4_0", 32, 12288, 4096),
     ("q8_0", 50, 260, 4128), ("q8_0", 64, 16512, 128), ("q5_0", 20, 130, 2080), ("q4_1", 45, 257, 1024),
@@ -356,9 +358,10 @@ MATMUL_CASES = [
 ]
 
 
-# Few tokens (up to 8, 10, 16 or 32 by format): the decode kernel with 2, 4 or 8 tokens per weight pass;
-# ragged token groups, odd block counts (unpaired units), rows walked in
-# segments (K = 8192 and 11008), every format.
+# Few tokens: up to 2, 4 or 8 by format on the decode kernel with 2, 4 or 8
+# tokens per weight pass (ragged token groups, odd block counts: unpaired
+# units, rows walked in segments: K = 8192 and 11008), and the counts just
+# past that on the 32-token MFMA tiles, every format.
 SMALL_M_CASES = [
     ("q4_0", 2, 130, 4096), ("q4_0", 3, 77, 4128), ("q4_0", 8, 12288, 4096), ("q4_0", 9, 65, 8192),
     ("q4_0", 15, 33, 11008), ("q4_0", 16, 129, 1024), ("q4_0", 5, 9, 32), ("q4_0", 17, 65, 4096),
@@ -538,13 +541,15 @@ def test_matmul_q4_k_full_size_sampled(env):
 
 @pytest.mark.parametrize("fmt,cfg,M", [("q4_0", 1, 32), ("q4_0", 1, 128), ("q4_k", 5, 64), ("q4_k", 5, 128),
                                        ("q6_k", 6, 100)])
-def test_matmul_split_k_bench_shapes_sampled(env, fmt, cfg, M):
-    """The few-token products the bench times on the MFMA kernels (12288 x 4096,
-    M <= 128: at most 256 tiles, so K split in two), checked on whole rows and
-    sampled outputs."""
+def test_matmul_bench_few_token_shapes_sampled(env, fmt, cfg, M):
+    """The few-token products the bench times on the MFMA kernels (12288 x
+    4096): the 32-token tiles (K split in two at Q4_0 M = 32, two K groups
+    per workgroup, and at Q4_K M = 64; K in one part at M = 128) and Q6_K's
+    128-token tile with K split in two, checked on whole rows and sampled
+    outputs."""
     torch, q, orc = env
     N, K = 12288, 4096
-    _say("matmul split-k bench shape", fmt, M, N, K)
+    _say("matmul few-token bench shape", fmt, M, N, K)
     wq = orc.quantize_w(fmt, synth.weights(N, K, config=cfg))
     xq = orc.quantize_x(fmt, synth.activations(M, K, config=cfg))
     y = _run_matmul(env, fmt, wq, xq, M, N, K)
@@ -556,7 +561,7 @@ def test_matmul_split_k_bench_shapes_sampled(env, fmt, cfg, M):
     mi = np.concatenate([mi, np.repeat(rows, N)])
     ni = np.concatenate([ni, np.tile(np.arange(N), len(rows))])
     ref, mag = orc.matmul_sampled(fmt, wq, xq, mi, ni, K)
-    _check(y[mi, ni], ref, mag, (fmt, M, "split-k sampled"))
+    _check(y[mi, ni], ref, mag, (fmt, M, "few-token sampled"))
 
 
 def test_matmul_q6_k_full_size_sampled(env):
@@ -634,8 +639,9 @@ def test_products_on_degenerate_inputs(env, fmt):
 def test_matmul_rows_equal_matvec(env, M, N, K):
     """Row m of the prefill product and the decode product of token m are two
     evaluations of the same outputs, each within the bound of the oracle.  M
-    is past the few-token switch, so the rows come from the MFMA kernels: K
-    split in two at N = 300 (3 tiles), in one part at N = 33000 (258 tiles)."""
+    is past the few-token switch, so the rows come from the 32-token MFMA
+    tiles: K split in two and two K groups per workgroup at N = 300 (6
+    tiles), K in one part at N = 33000 (516 tiles)."""
     torch, q, orc = env
     _say("matmul rows vs matvec", M, N, K)
     wq, xq = _inputs("q4_0", M, N, K, 7000 + N)
@@ -685,13 +691,17 @@ def test_outputs_are_overwritten_not_accumulated(env):
     assert np.array_equal(y.cpu().numpy(), y1)
 
 
+@pytest.mark.parametrize("M", [40, 200])
 @pytest.mark.parametrize("fmt", ["q4_0", "q5_1", "q2_k", "q4_k", "q6_k"])
-def test_split_k_matmul_overwrites_and_is_deterministic(env, fmt):
+def test_split_k_matmul_overwrites_and_is_deterministic(env, fmt, M):
     """A prefill launch of few tiles splits K in two and adds the halves into
     a zeroed output: calling it twice on a garbage-filled output gives the
-    same bits each time (two addends sum the same in either order)."""
+    same bits each time (two addends sum the same in either order).  M = 40
+    runs the 32-token tiles with two K groups per workgroup (each group's
+    sums handed over through LDS in a fixed order), M = 200 the 128-token
+    tiles."""
     torch, q, orc = env
-    M, N, K = 40, 1000, 4096
+    N, K = 1000, 4096
     _say("split-k repeat", fmt, M, N, K)
     wq, xq = _inputs(fmt, M, N, K, 8100)
     wd, xd = _dev(torch, wq), _dev(torch, xq)

@@ -205,17 +205,16 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
  * Up to 8 tokens (Q4_0; 2 for Q2_K, 4 for the other formats) run on the
  * decode matvec kernel, which streams each weight slice once per group of
  * 2, 4 or 8 tokens (one token: the decode launch itself); more tokens run
- * on the MFMA kernels below (32-token tiles up to 128 tokens for Q4_0,
- * Q5_0, Q2_K and Q4_K and up to 64 for the other formats, 128-token tiles
- * beyond).  Results agree within the same tolerance either way (they are
- * not bitwise identical: the two paths sum the blocks in different
- * orders).
+ * on the MFMA kernels below (32-token tiles up to 128 tokens for Q2_K and
+ * Q4_K and up to 64 for the other formats, 128-token tiles beyond).  Results
+ * agree within the same tolerance either way (they are not bitwise
+ * identical: the two paths sum the blocks in different orders).
  * An MFMA launch of at most 256 output tiles (32 or 128 tokens x 128 or 256
  * weight rows) splits K in two: y is first zeroed on the stream, then the two
  * halves of each output are added into it with f32 atomic adds (device
  * memory from hipMalloc; two addends give the same bits in either order, so
- * repeated calls are bitwise reproducible; a 32-token tile may first sum
- * its half from two quarters, in a fixed order).
+ * repeated calls are bitwise reproducible; a launch of fewer than 128
+ * tiles first sums each half from two quarters, in a fixed order).
  * The 32-value formats (Q4_0, Q8_0, Q4_1, Q5_0, Q5_1) run on int8 MFMA (4-bit
  * codes enter as 16 * (q - 8), 5-bit codes as 8 * (q - 16); the offset term
  * of Q4_1 / Q5_1, m * dx * sum x per block, runs on an f32 MFMA) and also

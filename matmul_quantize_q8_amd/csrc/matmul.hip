@@ -11,7 +11,9 @@
 // Workgroup tile: 128 tokens x 128 weight rows, 4 waves of 64 x 64 (2 x 2
 // MFMA tiles of 32 x 32); two workgroups share a CU, so the two waves on a
 // SIMD belong to different workgroups and do not meet at the same barriers.
-// The K loop moves two blocks per stage.
+// The K loop moves two blocks per stage.  Launches of up to 64 tokens run a
+// narrow tile of 32 tokens, and launches of fewer workgroups than CUs two K
+// groups per workgroup (both below).
 //
 // Staging.  A stage is copied into LDS by buffer LDS-DMA loads of 16 bytes
 // per lane (these loads accept the 2-byte aligned addresses of the blocks).
@@ -96,6 +98,9 @@ template <int WFMT> struct WF {
     static constexpr int DXF = NBUF * STAGE;
     static constexpr int DXW = (MIN ? 4 : 2) * 64 * 4;        // bytes per wave
     static constexpr int LDS_BYTES = DXF + 4 * DXW;
+    // two K groups of four waves, each with its own stage buffers
+    static constexpr int DXF2 = 2 * NBUF * STAGE;
+    static constexpr int LDS_BYTES2 = DXF2 + 8 * DXW;
     // 4-bit codes enter as 16*(q-8), 5-bit codes as 8*(q-16)
     static constexpr float OUT_SCALE = Q8W ? 1.0f : Q5 ? 0.125f : 0.0625f;
     // segment offsets of the weight chunks (segment = two blocks): Q4_0 36
@@ -113,22 +118,22 @@ template <int WFMT> struct WF {
 // per wave its own 32 weight rows (2 or 3 wave loads).  Every wave issues one
 // activation load (wave 3 repeats wave 2's: the same bytes to the same
 // place) and its weight loads, so all waves wait for the same count.
-// A split launch of fewer workgroups than CUs runs eight waves per workgroup
-// instead: two K groups of four, each with its own stage buffers on half of
-// the part's stages, stepping through the same barriers; at the end group 1
-// passes its sums to group 0 through LDS, which adds them to its own before
-// the store (the same order on every call).  With one workgroup of four
-// waves per CU or fewer, the stage chain of a lone wave per SIMD sets the
-// time; two waves per SIMD halve the chain (Q4_0 M = 8, N = 12288, K = 4096:
-// 18.4 -> 14.5 us).
+// A split launch of fewer workgroups than CUs (narrow or full tile) runs
+// eight waves per workgroup instead: two K groups of four, each with its own
+// stage buffers on half of the part's stages, stepping through the same
+// barriers; at the end group 1 passes its sums to group 0 through LDS, which
+// adds them to its own before the store (the same order on every call).
+// With one workgroup of four waves per CU or fewer, the stage chain of a
+// lone wave per SIMD sets the time; two waves per SIMD halve the chain
+// (N = 12288, K = 4096: narrow Q4_0 M = 8 18.4 -> 14.5 us; full Q5_1 M = 65
+// 48.4 -> 39.8 us, Q8_0 37.9 -> 33.9 us).
 constexpr int NBM = 32;                    // tokens per narrow tile
-// Token counts up to which the narrow tile runs.  Past 64 tokens it runs
-// three or four token tiles per weight tile, which still beats the full
-// tile for Q4_0 and Q5_0 but not for the formats with more weight bytes per
-// block (12288 x 4096, us, full / narrow: Q4_0 M = 65 39.3 / 36.5, M = 128
-// 44.0 / 39.1; Q5_0 42.4 / 40.0, 47.6 / 43.5; Q8_0 38.2 / 47.5; Q4_1 44.7 /
-// 50.1; Q5_1 48.7 / 54.0).
-constexpr int narrow_tokens(int wfmt) { return (wfmt == F_Q4_0 || wfmt == F_Q5_0) ? 4 * NBM : 2 * NBM; }
+// Token counts up to which the narrow tile runs.  Past 64 tokens it would
+// run three or four token tiles per weight tile, and the full tile with two
+// K groups per workgroup is faster for every format (12288 x 4096, us,
+// narrow / full with two K groups: Q4_0 M = 65 36.1 / 32.2, M = 128 39.8 /
+// 37.2; Q5_0 39.5 / 34.7, 44.1 / 39.8).
+constexpr int narrow_tokens(int) { return 2 * NBM; }
 constexpr int NXL = 3;                     // wave loads of activation chunks
 template <int WFMT> struct WN {
     using F = WF<WFMT>;
@@ -187,9 +192,9 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     constexpr int WC = F::WC, WQ = F::WQ;
     constexpr int STAGE = NARROW ? WN<WFMT>::STAGE : F::STAGE;
     constexpr int PER_WAVE = NARROW ? WN<WFMT>::PER_WAVE : F::PER_WAVE;
-    constexpr int DXF = NARROW ? WN<WFMT>::template DXF<G> : F::DXF;
+    constexpr int DXF = NARROW ? WN<WFMT>::template DXF<G> : G == 2 ? F::DXF2 : F::DXF;
     constexpr int NB = NARROW ? WN<WFMT>::NBUF : NBUF;   // stage buffers; the DMA runs NB - 1 stages ahead
-    static_assert(G == 1 || (G == 2 && NARROW), "K groups only on the narrow tile");
+    static_assert(G == 1 || (G == 2 && SPLIT), "two K groups on split launches");
     constexpr int TBM = NARROW ? NBM : BM;           // tokens per tile
     constexpr int TI = NARROW ? 1 : 2, TJ = NARROW ? 1 : 2;   // A and B tiles per wave
     const int t = threadIdx.x, lane = t & 63;
@@ -694,19 +699,27 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     // no LDS-DMA write may still be in flight when the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (G == 2) {
-        // group 1 hands its sums to group 0 through LDS ([wave][r][lane],
+        // group 1 hands its sums to group 0 through LDS ([tile][wave][r][lane],
         // over the stage buffers), which adds them to its own: the same
         // order on every call
         float *red = reinterpret_cast<float *>(lds) + 1024 * wave + lane;
         lds_barrier();
         if (grp == 1) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[64 * r] = acc[0][0][r];
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[4096 * (TJ * i + j) + 64 * r] = acc[i][j][r];
         }
         lds_barrier();
         if (grp == 1) return;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[0][0][r] += red[64 * r];
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] += red[4096 * (TJ * i + j) + 64 * r];
     }
 
     // store: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32
@@ -797,6 +810,17 @@ __global__ __launch_bounds__(mm::NT, 2) void k_matmul_q5_1_split(const uint8_t *
                                                                 int M, int N, int nb, int tiles_m) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<F_Q5_1>::LDS_BYTES];
     matmul_body<F_Q5_1, true>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
+// The 128-token tile with two groups of four waves, each on half of the
+// workgroup's part of K, for split launches of fewer workgroups than CUs.
+template <int WFMT>
+__global__ __launch_bounds__(2 * mm::NT, 1) void k_matmul_wide2(const uint8_t *__restrict__ w,
+                                                               const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                               int M, int N, int nb, int tiles_m) {
+    static_assert(mm::WF<WFMT>::LDS_BYTES2 <= 160 * 1024, "LDS of one CU");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WF<WFMT>::LDS_BYTES2];
+    matmul_body<WFMT, true, false, 2>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 // The narrow tile (32 tokens x 128 weight rows) for launches of up to
@@ -943,9 +967,9 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
     const int ksplit = split ? 2 : 1;
     // Fewer narrow workgroups than CUs: two groups of four waves per
     // workgroup, each on half of its part of K (at least four stages each).
-    const bool groups = narrow && split && tiles * 2 < kCUs && nb >= 16;
+    const bool groups = split && tiles * 2 < kCUs && nb >= 16;
     void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
-    const void *kern = groups           ? (const void *)k_matmul_narrow2<WFMT>
+    const void *kern = groups           ? (narrow ? (const void *)k_matmul_narrow2<WFMT> : (const void *)k_matmul_wide2<WFMT>)
                        : narrow         ? (split ? (const void *)k_matmul_narrow<WFMT, true>
                                                  : (const void *)k_matmul_narrow<WFMT, false>)
                        : WFMT == F_Q8_0 ? (split ? (const void *)k_matmul_q8_0_split : (const void *)k_matmul_q8_0)

@@ -299,9 +299,8 @@ MATMUL_CASES = [
     # even block counts (the dword-plane kernel): 1..7 stages, ragged tiles
     ("q4_0", 1, 129, 64), ("q4_0", 131, 255, 128), ("q4_0", 70, 130, 192), ("q4_0", 257, 129, 256),
     ("q4_0", 3, 300, 320), ("q4_0", 200, 100, 448),
-    # token counts one past and one short of 64: Q8_0's last on the 32-token
-    # tile and first on the 128-token tile (Q4_0 and Q5_0 keep the 32-token
-    # tile up to 128)
+    # token counts one past and one short of 64: the last on the 32-token
+    # tile and the first on the 128-token tile
     ("q4_0", 65, 130, 96), ("q4_0", 63, 127, 2048), ("q8_0", 65, 129, 160), ("q8_0", 63, 255, 2048),
     ("q8_0", 1, 8, 32), ("q8_0", 37, 200, 1024), ("q8_0", 128, 128, 4096), ("q8_0", 130, 129, 160),
     ("q8_0", 5, 3, 96), ("q8_0", 131, 255, 128), ("q8_0", 257, 129, 256), ("q8_0", 300, 700, 2080),
@@ -319,8 +318,9 @@ MATMUL_CASES = [
     ("q4_k", 50, 129, 1280), ("q2_k", 17, 129, 1024), ("q6_k", 64, 257, 4096), ("q6_k", 12, 130, 2304),
     ("q6_k", 40, 200, 512), ("q2_k", 20, 70, 256), ("q4_k", 64, 300, 256), ("q2_k", 40, 16641, 512),
     ("q4_k", 45, 16390, 768), ("q2_k", 31, 260, 8192),
-    # 65-128 tokens on the 32-token tiles (Q4_0, Q5_0, Q2_K, Q4_K): three or
-    # four token tiles, two K groups, a split without groups, no split
+    # 65-128 tokens: the K-quants' 32-token tiles (Q2_K, Q4_K: three or four
+    # token tiles, two K groups, a split without groups, no split) and the
+    # 128-token tile (Q4_0, Q5_0: two K groups, one part)
     ("q4_0", 96, 4100, 1024), ("q4_0", 100, 130, 4096), ("q5_0", 120, 16500, 512), ("q5_0", 70, 257, 2080),
     ("q2_k", 100, 8200, 1024), ("q2_k", 65, 129, 512), ("q4_k", 127, 300, 2304), ("q4_k", 128, 16390, 256),
     # Q4_1 and Q5_1 on the same kernel, the offset term on an f32 MFMA
@@ -355,6 +355,11 @@ MATMUL_CASES = [
     ("q6_k", 257, 16640, 768), ("q6_k", 129, 16577, 512),
     # exactly 256 tiles (1 x 256): the largest launch that still splits K
     ("q5_1", 100, 32768, 128),
+    # 128-token tiles with K split in two: one group of four waves (130 and
+    # 256 tiles), two K groups (fewer than 128 tiles; 16 and 17 blocks, an
+    # uneven group step, ragged M and N)
+    ("q4_1", 130, 8200, 1024), ("q8_0", 200, 16384, 544), ("q8_0", 100, 130, 512), ("q5_1", 70, 257, 544),
+    ("q4_0", 150, 200, 1056), ("q5_0", 255, 300, 4096),
 ]
 
 
@@ -697,9 +702,9 @@ def test_split_k_matmul_overwrites_and_is_deterministic(env, fmt, M):
     """A prefill launch of few tiles splits K in two and adds the halves into
     a zeroed output: calling it twice on a garbage-filled output gives the
     same bits each time (two addends sum the same in either order).  M = 40
-    runs the 32-token tiles with two K groups per workgroup (each group's
-    sums handed over through LDS in a fixed order), M = 200 the 128-token
-    tiles."""
+    runs the 32-token tiles and M = 200 the 128-token tiles, both with two K
+    groups per workgroup (each group's sums handed over through LDS in a
+    fixed order) except Q2_K, Q4_K and Q6_K at M = 200."""
     torch, q, orc = env
     N, K = 1000, 4096
     _say("split-k repeat", fmt, M, N, K)

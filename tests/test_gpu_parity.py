@@ -360,6 +360,11 @@ MATMUL_CASES = [
     # uneven group step, ragged M and N)
     ("q4_1", 130, 8200, 1024), ("q8_0", 200, 16384, 544), ("q8_0", 100, 130, 512), ("q5_1", 70, 257, 544),
     ("q4_0", 150, 200, 1056), ("q5_0", 255, 300, 4096),
+    # the edge of two K groups per workgroup: 127 tiles (two groups) and 128
+    # (one), on the 32-token tile, the 128-token tile and the K-quants'
+    # 32-token tile
+    ("q4_0", 20, 16256, 512), ("q4_0", 20, 16384, 512), ("q8_0", 100, 16256, 512), ("q8_0", 100, 16384, 512),
+    ("q4_k", 20, 16256, 1024), ("q4_k", 20, 16384, 1024),
 ]
 
 

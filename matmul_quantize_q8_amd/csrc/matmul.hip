@@ -201,9 +201,11 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const int wave = uniform(G == 1 ? t >> 6 : (t >> 6) & 3);
     const int grp = G == 1 ? 0 : uniform(t >> 8);   // K group: its own stage buffers and blocks
     // SPLIT: the grid holds every tile twice, one per part of K, and both
-    // parts add into the zeroed output.  Part p of P = ksplit * G (grid part
-    // and K group) takes stages [p S / P, (p + 1) S / P) of the S = ceil(nb /
-    // 2) two-block stages of a row (the caller keeps S >= P).
+    // parts add into the zeroed output.  With one K group part 0 takes the
+    // first kb1 blocks of each row (whole stages) and part 1 the rest; with
+    // G groups part p of P = ksplit * G (grid part and K group) takes stages
+    // [p S / P, (p + 1) S / P) of the S = ceil(nb / 2) two-block stages of a
+    // row (the caller keeps S >= P).
     constexpr int ksplit = SPLIT ? 2 : 1;
     constexpr int P = ksplit * G;
     const int tiles = (int)gridDim.x / ksplit;

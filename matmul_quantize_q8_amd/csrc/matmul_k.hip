@@ -108,10 +108,10 @@ template <int F> struct KW {
 // its sums to group 0 through LDS at the end (the same order on every call).
 constexpr int NBM = 32;                        // tokens per narrow tile
 // Token counts up to which the narrow tile runs: up to 128 for Q2_K and
-// Q4_K, whose full tiles of 256 weight rows leave half the CUs idle below
-// 129 tokens, 64 for Q6_K (12288 x 4096, us, full / narrow: Q2_K M = 65 32.1
-// / 24.0, M = 128 37.1 / 25.7; Q4_K 46.2 / 35.9, 52.7 / 37.3; Q6_K 44.3 /
-// 62.3, 49.8 / 63.7).
+// Q4_K, whose full tiles of 256 weight rows leave most CUs idle below 129
+// tokens (96 workgroups at N = 12288), 64 for Q6_K (12288 x 4096, us, full
+// / narrow: Q2_K M = 65 32.1 / 24.0, M = 128 37.1 / 25.7; Q4_K 46.2 / 35.9,
+// 52.7 / 37.3; Q6_K 44.3 / 62.3, 49.8 / 63.7).
 constexpr int narrow_tokens(int f) { return f == F_Q6_K ? 2 * NBM : 4 * NBM; }
 constexpr int NXQ = 10;                        // wave loads of activation chunks
 template <int F, int G> struct KN {

@@ -855,9 +855,12 @@ def test_concurrent_calls_from_host_threads(env):
 def test_graph_replay_matches_eager(env):
     """Decode and prefill launches captured into a HIP graph: every replay, with
     eager work and synchronizations in between, equals the eager result bit for
-    bit (the kernels are deterministic and keep no state)."""
+    bit (the kernels are deterministic and keep no state).  The products reach
+    the 32-token tiles with two K groups (M = 64), the 128-token tile with two
+    K groups (M = 100) and the few-token decode kernel (M = 4), each split
+    launch with its fill kernel."""
     torch, q, orc = env
-    N, K, M = 1024, 4096, 64
+    N, K, M, M2, M3 = 1024, 4096, 64, 100, 4
     w = synth.weights(N, K, config=1)
     x = synth.activations(M, K, config=4)
     wq = _dev(torch, orc.quantize_q4_0_w(w))
@@ -867,7 +870,11 @@ def test_graph_replay_matches_eager(env):
     yv = torch.empty(N, dtype=torch.float32, device="cuda")
     yf = torch.empty(N, dtype=torch.float32, device="cuda")
     ym = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    # the K-quant prefill kernels (dynamic LDS of up to 152 KB) in the same graph
+    x2 = _dev(torch, synth.activations(M2, K, config=5))
+    xq2 = torch.empty(M2 * q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
+    ym2 = torch.empty((M2, N), dtype=torch.float32, device="cuda")
+    ym3 = torch.empty((M3, N), dtype=torch.float32, device="cuda")
+    # the K-quant prefill kernels (dynamic LDS of up to 153 KB) in the same graph
     wk = {f: _dev(torch, orc.quantize_w(f, w)) for f in ("q2_k", "q4_k", "q6_k")}
     x8k = torch.empty(M * q.row_bytes("q8_k", K), dtype=torch.uint8, device="cuda")
     yk = {f: torch.empty((M, N), dtype=torch.float32, device="cuda") for f in wk}
@@ -877,6 +884,9 @@ def test_graph_replay_matches_eager(env):
         q.qmm_matvec_q4_0(wq, xq, yv, N, K)
         q.qmm_quantize_matvec_q4_0(wq, xd[1], xq1, yf, N, K)
         q.qmm_matmul_q4_0(wq, xq, ym, M, N, K)
+        q.qmm_quantize_q8_0(x2, xq2, M2, K)
+        q.qmm_matmul_q4_0(wq, xq2, ym2, M2, N, K)
+        q.qmm_matmul_q4_0(wq, xq, ym3, M3, N, K)
         q.qmm_quantize_q8_k(xd, x8k, M, K)
         for f in wk:
             q.MATMUL[f](wk[f], x8k, yk[f], M, N, K)
@@ -884,6 +894,7 @@ def test_graph_replay_matches_eager(env):
     work()
     torch.cuda.synchronize()
     ref_v, ref_m, ref_q, ref_f, ref_q1 = yv.clone(), ym.clone(), xq.clone(), yf.clone(), xq1.clone()
+    ref_m2, ref_m3 = ym2.clone(), ym3.clone()
     ref_k = {f: yk[f].clone() for f in yk}
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -892,6 +903,8 @@ def test_graph_replay_matches_eager(env):
         yv.fill_(float("nan"))
         yf.fill_(float("nan"))
         ym.fill_(float("nan"))
+        ym2.fill_(float("nan"))
+        ym3.fill_(float("nan"))
         for f in yk:
             yk[f].fill_(float("nan"))
         xq.zero_()
@@ -902,6 +915,8 @@ def test_graph_replay_matches_eager(env):
         assert torch.equal(xq, ref_q), rep
         assert torch.equal(yv, ref_v), rep
         assert torch.equal(ym, ref_m), rep
+        assert torch.equal(ym2, ref_m2), rep
+        assert torch.equal(ym3, ref_m3), rep
         assert torch.equal(yf, ref_f), rep
         assert torch.equal(xq1, ref_q1), rep
         for f in yk:

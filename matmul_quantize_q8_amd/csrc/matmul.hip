@@ -118,15 +118,18 @@ template <int WFMT> struct WF {
 // per wave its own 32 weight rows (2 or 3 wave loads).  Every wave issues one
 // activation load (wave 3 repeats wave 2's: the same bytes to the same
 // place) and its weight loads, so all waves wait for the same count.
-// A split launch of fewer workgroups than CUs (narrow or full tile) runs
-// eight waves per workgroup instead: two K groups of four, each with its own
-// stage buffers on half of the part's stages, stepping through the same
-// barriers; at the end group 1 passes its sums to group 0 through LDS, which
-// adds them to its own before the store (the same order on every call).
-// With one workgroup of four waves per CU or fewer, the stage chain of a
-// lone wave per SIMD sets the time; two waves per SIMD halve the chain
-// (N = 12288, K = 4096: narrow Q4_0 M = 8 18.4 -> 14.5 us; full Q5_1 M = 65
-// 48.4 -> 39.8 us, Q8_0 37.9 -> 33.9 us).
+// A launch of fewer workgroups than CUs runs eight waves per workgroup
+// instead, in K groups, each with its own stage buffers on its share of the
+// stages, stepping through the same barriers; at the end groups 1.. pass
+// their sums to group 0 through LDS, which adds them to its own before the
+// store (the same order on every call).  With one workgroup of four waves
+// per CU or fewer, the stage chain of a lone wave per SIMD sets the time;
+// two waves per SIMD halve it.  The narrow tile runs four groups of two
+// waves on 64 weight rows and K whole (no fill kernel, no atomic adds:
+// Q4_0 M = 32, N = 12288, K = 4096: 19.9 us with one group and K split in
+// two, 17.2 with two groups of four, 14.8 with four of two); the full tile
+// runs two groups of four on each half of a split launch (Q5_1 M = 65 48.4
+// -> 39.8 us, Q8_0 37.9 -> 33.9 us).
 constexpr int NBM = 32;                    // tokens per narrow tile
 // Token counts up to which the narrow tile runs.  Past 64 tokens it would
 // run three or four token tiles per weight tile, and the full tile with two
@@ -135,18 +138,18 @@ constexpr int NBM = 32;                    // tokens per narrow tile
 // 37.2; Q5_0 39.5 / 34.7, 44.1 / 39.8).
 constexpr int narrow_tokens(int) { return 2 * NBM; }
 constexpr int NXL = 3;                     // wave loads of activation chunks
-template <int WFMT> struct WN {
+template <int WFMT, int WPG = 4> struct WN {   // WPG waves per K group (32 weight rows each)
     using F = WF<WFMT>;
     static constexpr int WL = (32 * F::WC + kWave - 1) / kWave;   // 2, or 3 for Q8_0 weights
-    static constexpr int PER_WAVE = 1 + WL;
+    static constexpr int NA = (NXL + WPG - 1) / WPG;              // activation loads per wave
+    static constexpr int PER_WAVE = NA + WL;
     static constexpr int AREA = NXL * 1024;                        // activation chunks of a stage
-    static constexpr int STAGE = AREA + 4 * WL * 1024;             // 11,264 or 15,360 bytes
+    static constexpr int STAGE = AREA + WPG * WL * 1024;           // 11,264 or 15,360 bytes (WPG = 4)
     static constexpr int NBUF = 3;                                 // stage buffers per K group
-    // G = 1 or 2 groups of 4 waves, each on its own part of K
+    // G groups of WPG waves, each on its own part of K
     template <int G> static constexpr int DXF = G * NBUF * STAGE;
-    template <int G> static constexpr int LDS_BYTES = DXF<G> + 4 * G * F::DXW;
+    template <int G> static constexpr int LDS_BYTES = DXF<G> + WPG * G * F::DXW;
     static_assert(NBM * XC <= NXL * kWave && 32 * F::WC <= WL * kWave, "chunks fit the wave loads");
-    static_assert(2 * LDS_BYTES<1> <= 160 * 1024 && LDS_BYTES<2> <= 160 * 1024, "LDS of one CU");
 };
 }  // namespace mm
 
@@ -182,7 +185,7 @@ __device__ __forceinline__ void each_index(std::integer_sequence<int, I...>, Fn 
 // Workgroup barrier that orders LDS accesses but does not wait for
 // outstanding vector-memory loads (the LDS-DMA copies in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-template <int WFMT, bool SPLIT, bool NARROW = false, int G = 1>
+template <int WFMT, bool SPLIT, bool NARROW = false, int G = 1, int WPG = 4>
 __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restrict__ w,
                                             const uint8_t *__restrict__ xq, float *__restrict__ y, int M, int N,
                                             int nb, int tiles_m) {
@@ -190,16 +193,19 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     using F = WF<WFMT>;
     constexpr bool Q8W = F::Q8W, Q5 = F::Q5, MIN = F::MIN;
     constexpr int WC = F::WC, WQ = F::WQ;
-    constexpr int STAGE = NARROW ? WN<WFMT>::STAGE : F::STAGE;
-    constexpr int PER_WAVE = NARROW ? WN<WFMT>::PER_WAVE : F::PER_WAVE;
-    constexpr int DXF = NARROW ? WN<WFMT>::template DXF<G> : G == 2 ? F::DXF2 : F::DXF;
-    constexpr int NB = NARROW ? WN<WFMT>::NBUF : NBUF;   // stage buffers; the DMA runs NB - 1 stages ahead
-    static_assert(G == 1 || (G == 2 && SPLIT), "two K groups on split launches");
+    using NW_ = WN<WFMT, WPG>;
+    constexpr int STAGE = NARROW ? NW_::STAGE : F::STAGE;
+    constexpr int PER_WAVE = NARROW ? NW_::PER_WAVE : F::PER_WAVE;
+    constexpr int DXF = NARROW ? NW_::template DXF<G> : G == 2 ? F::DXF2 : F::DXF;
+    constexpr int NB = NARROW ? NW_::NBUF : NBUF;        // stage buffers; the DMA runs NB - 1 stages ahead
+    static_assert(G == 1 || (G == 2 && SPLIT && !NARROW) || (G == 4 && NARROW && WPG == 2 && !SPLIT),
+                  "two K groups on split full-tile launches; four groups of two waves on unsplit narrow launches");
+    static_assert(NARROW || WPG == 4, "the full tile has four waves per K group");
     constexpr int TBM = NARROW ? NBM : BM;           // tokens per tile
     constexpr int TI = NARROW ? 1 : 2, TJ = NARROW ? 1 : 2;   // A and B tiles per wave
     const int t = threadIdx.x, lane = t & 63;
-    const int wave = uniform(G == 1 ? t >> 6 : (t >> 6) & 3);
-    const int grp = G == 1 ? 0 : uniform(t >> 8);   // K group: its own stage buffers and blocks
+    const int wave = uniform(G == 1 ? t >> 6 : (t >> 6) % WPG);
+    const int grp = G == 1 ? 0 : uniform((t >> 6) / WPG);   // K group: its own stage buffers and blocks
     // SPLIT: the grid holds every tile twice, one per part of K, and both
     // parts add into the zeroed output.  With one K group part 0 takes the
     // first kb1 blocks of each row (whole stages) and part 1 the rest; with
@@ -211,7 +217,8 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const int tiles = (int)gridDim.x / ksplit;
     const int tile = (int)blockIdx.x % tiles, gpart = (int)blockIdx.x / tiles;
     const int mt = tile % tiles_m, nt = tile / tiles_m;
-    const int m0 = mt * TBM, n0 = nt * BN;
+    constexpr int TBN = NARROW ? 32 * WPG : BN;          // weight rows per tile
+    const int m0 = mt * TBM, n0 = nt * TBN;
     const uint32_t xrow = (uint32_t)nb * kQ80Bytes, wrow = (uint32_t)nb * F::WB;
     const int S_all = (nb + 1) >> 1;
     auto first_stage = [&](int p) { return p * S_all / P; };
@@ -222,9 +229,10 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const int nst = (nbp + 1) >> 1;   // an odd block count leaves a last stage of one block
     // every wave of the workgroup passes the same barriers: the K groups
     // step together for the larger of their stage counts
-    const int nst_wg = G == 1 ? nst
-                              : max(first_stage(G * gpart + 1) - first_stage(G * gpart),
-                                    first_stage(G * gpart + 2) - first_stage(G * gpart + 1));
+    int nst_wg = nst;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        if (G > 1) nst_wg = max(nst_wg, first_stage(G * gpart + g + 1) - first_stage(G * gpart + g));
 
     // DMA: wave load q = w + 4k (k < 4) of a stage is chunk load q of the
     // stage image (activation chunks for q < 10, weight chunks after) and
@@ -237,7 +245,7 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(xq + (int64_t)m0 * xrow), 0, (int)((uint32_t)min(M - m0, TBM) * xrow), 0x00020000);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(w + (int64_t)n0 * wrow), 0, (int)((uint32_t)min(N - n0, BN) * wrow), 0x00020000);
+        (void *)(w + (int64_t)n0 * wrow), 0, (int)((uint32_t)min(N - n0, TBN) * wrow), 0x00020000);
     uint32_t voff[PER_WAVE];
     uint32_t m0k[PER_WAVE];   // narrow: the LDS base of each of this wave's loads
     if constexpr (!NARROW) {
@@ -258,17 +266,20 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(ldsg);
     const uint32_t m0w = (uint32_t)uniform((int)(lds0 + 1024u * wave));
     if constexpr (NARROW) {
-        const int a = min(wave, NXL - 1);
+        constexpr int NA = NW_::NA;
 #pragma unroll
         for (int k = 0; k < PER_WAVE; ++k) {
-            if (k == 0) {
+            if (k < NA) {
+                // activation load min(wave + WPG k, NXL - 1): the last one may
+                // repeat another wave's (the same bytes to the same place)
+                const int a = min(wave + WPG * k, NXL - 1);
                 const int f = min(kWave * a + lane, NBM * XC - 1), row = f / XC, c = f - XC * row;
                 voff[k] = (uint32_t)(min(m0 + row, M - 1) - m0) * xrow + (uint32_t)xchunk(c);
                 m0k[k] = (uint32_t)uniform((int)(lds0 + 1024u * a));
             } else {
-                const int f = min(kWave * (k - 1) + lane, 32 * WC - 1), row = f / WC, c = f - WC * row;
+                const int f = min(kWave * (k - NA) + lane, 32 * WC - 1), row = f / WC, c = f - WC * row;
                 voff[k] = (uint32_t)(min(n0 + 32 * wave + row, N - 1) - n0) * wrow + (uint32_t)F::wchunk(c);
-                m0k[k] = (uint32_t)uniform((int)(lds0 + WN<WFMT>::AREA + 1024u * (WN<WFMT>::WL * wave + k - 1)));
+                m0k[k] = (uint32_t)uniform((int)(lds0 + NW_::AREA + 1024u * (NW_::WL * wave + k - NA)));
             }
         }
     }
@@ -279,7 +290,8 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
         constexpr int k = decltype(kc)::value;
         const int sx = seg(s) * kQ80Bytes, sw = seg(s) * F::WB;
         if constexpr (NARROW) {
-            buffer_to_lds<16, 0>(k >= 1 ? wr : xr, m0k[k] + (uint32_t)(b * STAGE), voff[k], k >= 1 ? sw : sx);
+            constexpr bool isw = k >= NW_::NA;
+            buffer_to_lds<16, 0>(isw ? wr : xr, m0k[k] + (uint32_t)(b * STAGE), voff[k], isw ? sw : sx);
         } else {
             const uint32_t base = m0w + (uint32_t)(b * STAGE);
             // load 2: activation chunks for waves 0 and 1, weight chunks for 2 and 3
@@ -303,12 +315,12 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     const int xa = NARROW ? 16 * XC * lr : 16 * XC * (64 * wm + lr);
     const int xa_main = xa + (lh ? 0 : 16);              // block 0: chunk 1 (half 0) or 0 (half 1); block 1: +32
     // B row 64wn+lr (tile j: +32 rows); narrow: row lr of this wave's 32
-    const int wb = NARROW ? WN<WFMT>::AREA + 1024 * WN<WFMT>::WL * wave + 16 * WC * lr
+    const int wb = NARROW ? NW_::AREA + 1024 * NW_::WL * wave + 16 * WC * lr
                           : WOFF + 16 * WC * (64 * wn + lr);
     const int wb_main = wb + (lh ? 0 : 16);              // Q8_0 weights: as xa_main
     // the row whose dx this lane converts (narrow: lanes 32..63 repeat 0..31)
     const int xd = NARROW ? 16 * XC * lr : 16 * XC * (64 * wm + lane);
-    const int dxw = DXF + F::DXW * (4 * grp + wave);     // this wave's f32 dx: [block][64 rows 64wm..]
+    const int dxw = DXF + F::DXW * (WPG * grp + wave);   // this wave's f32 dx: [block][64 rows 64wm..]
     const uint32_t selA = lh ? 0x03020504u : 0x03020100u;   // half 1: codes 30, 31 into bytes 0, 1
     const uint32_t selB = lh ? 0x07060100u : 0x03020504u;   // block 0, first dword: which bytes take low nibbles
     const uint32_t shHi = lh ? 4u : 0u;                  // shift for a dword that half 0 takes high nibbles of
@@ -700,28 +712,31 @@ __device__ __forceinline__ void matmul_body(uint8_t *lds, const uint8_t *__restr
     }
     // no LDS-DMA write may still be in flight when the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (G == 2) {
-        // group 1 hands its sums to group 0 through LDS ([tile][wave][r][lane],
-        // over the stage buffers), which adds them to its own: the same
-        // order on every call
+    if constexpr (G > 1) {
+        // groups 1 .. G-1 hand their sums to group 0 through LDS
+        // ([group - 1][tile][wave][r][lane], over the stage buffers), which
+        // adds them to its own in group order: the same order on every call
+        constexpr int TS = 1024 * WPG;                   // floats per tile and group
         float *red = reinterpret_cast<float *>(lds) + 1024 * wave + lane;
         lds_barrier();
-        if (grp == 1) {
+        if (grp > 0) {
 #pragma unroll
             for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int j = 0; j < TJ; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) red[4096 * (TJ * i + j) + 64 * r] = acc[i][j][r];
+                    for (int r = 0; r < 16; ++r) red[TS * (TI * TJ * (grp - 1) + TJ * i + j) + 64 * r] = acc[i][j][r];
         }
         lds_barrier();
-        if (grp == 1) return;
+        if (grp > 0) return;
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int g = 1; g < G; ++g)
 #pragma unroll
-            for (int j = 0; j < TJ; ++j)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] += red[4096 * (TJ * i + j) + 64 * r];
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += red[TS * (TI * TJ * (g - 1) + TJ * i + j) + 64 * r];
     }
 
     // store: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32
@@ -825,24 +840,28 @@ __global__ __launch_bounds__(2 * mm::NT, 1) void k_matmul_wide2(const uint8_t *_
     matmul_body<WFMT, true, false, 2>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
+// The narrow tile of 32 tokens x 64 weight rows with four groups of two
+// waves, each on a quarter of K, for launches of fewer narrow workgroups
+// than CUs: the K parallelism of a split launch with two groups, without
+// the fill kernel and the atomic adds.
+template <int WFMT>
+__global__ __launch_bounds__(2 * mm::NT, 1) void k_matmul_narrow4(const uint8_t *__restrict__ w,
+                                                                 const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                                 int M, int N, int nb, int tiles_m) {
+    static_assert(mm::WN<WFMT, 2>::template LDS_BYTES<4> <= 160 * 1024, "LDS of one CU");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WN<WFMT, 2>::template LDS_BYTES<4>];
+    matmul_body<WFMT, false, true, 4, 2>(lds, w, xq, y, M, N, nb, tiles_m);
+}
+
 // The narrow tile (32 tokens x 128 weight rows) for launches of up to
 // narrow_tokens tokens, every 32-value format, K in one part or split in two.
 template <int WFMT, bool SPLIT>
 __global__ __launch_bounds__(mm::NT, 2) void k_matmul_narrow(const uint8_t *__restrict__ w,
                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                             int M, int N, int nb, int tiles_m) {
+    static_assert(2 * mm::WN<WFMT>::template LDS_BYTES<1> <= 160 * 1024, "two workgroups per CU");
     __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WN<WFMT>::template LDS_BYTES<1>];
     matmul_body<WFMT, SPLIT, true>(lds, w, xq, y, M, N, nb, tiles_m);
-}
-
-// The narrow tile with two groups of four waves, each on half of the
-// workgroup's part of K, for split launches of fewer workgroups than CUs.
-template <int WFMT>
-__global__ __launch_bounds__(2 * mm::NT, 1) void k_matmul_narrow2(const uint8_t *__restrict__ w,
-                                                                 const uint8_t *__restrict__ xq, float *__restrict__ y,
-                                                                 int M, int N, int nb, int tiles_m) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[mm::WN<WFMT>::template LDS_BYTES<2>];
-    matmul_body<WFMT, true, true, 2>(lds, w, xq, y, M, N, nb, tiles_m);
 }
 
 // K = 32: one block per row, too short for the two-block stages above (the
@@ -958,6 +977,15 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
     const bool narrow = M <= mm::narrow_tokens(WFMT);
     int tiles_m = narrow ? (M + mm::NBM - 1) / mm::NBM : (M + mm::BM - 1) / mm::BM;
     const int64_t tiles = (int64_t)tiles_m * ((N + mm::BN - 1) / mm::BN);
+    void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
+    // Fewer narrow workgroups than CUs: four groups of two waves on 64
+    // weight rows per workgroup, each on a quarter of K (at least two stages
+    // each), written with plain stores.
+    if (narrow && tiles * 2 < kCUs && nb >= 16) {
+        const int64_t tiles64 = (int64_t)tiles_m * ((N + 63) / 64);
+        return hipLaunchKernel((const void *)k_matmul_narrow4<WFMT>, dim3((unsigned)tiles64), dim3(2 * mm::NT), args,
+                               0, st);
+    }
     // A launch of at most one workgroup per CU leaves the CUs half idle and
     // each workgroup alone on its CU: split K in two, the parts adding into
     // an output zeroed first.
@@ -967,11 +995,10 @@ static hipError_t launch_mm(const void *w, const void *xq, float *y, int M, int 
         if (e != hipSuccess) return e;
     }
     const int ksplit = split ? 2 : 1;
-    // Fewer narrow workgroups than CUs: two groups of four waves per
+    // Fewer full-tile workgroups than CUs: two groups of four waves per
     // workgroup, each on half of its part of K (at least four stages each).
-    const bool groups = split && tiles * 2 < kCUs && nb >= 16;
-    void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&nb, (void *)&tiles_m};
-    const void *kern = groups           ? (narrow ? (const void *)k_matmul_narrow2<WFMT> : (const void *)k_matmul_wide2<WFMT>)
+    const bool groups = !narrow && split && tiles * 2 < kCUs && nb >= 16;
+    const void *kern = groups           ? (const void *)k_matmul_wide2<WFMT>
                        : narrow         ? (split ? (const void *)k_matmul_narrow<WFMT, true>
                                                  : (const void *)k_matmul_narrow<WFMT, false>)
                        : WFMT == F_Q8_0 ? (split ? (const void *)k_matmul_q8_0_split : (const void *)k_matmul_q8_0)

@@ -360,9 +360,10 @@ MATMUL_CASES = [
     # uneven group step, ragged M and N)
     ("q4_1", 130, 8200, 1024), ("q8_0", 200, 16384, 544), ("q8_0", 100, 130, 512), ("q5_1", 70, 257, 544),
     ("q4_0", 150, 200, 1056), ("q5_0", 255, 300, 4096),
-    # the edge of two K groups per workgroup: 127 tiles (two groups) and 128
-    # (one), on the 32-token tile, the 128-token tile and the K-quants'
-    # 32-token tile
+    # the edge of K groups per workgroup: 127 tiles (four groups for the
+    # 32-value formats' 32-token tile, two elsewhere) and 128 (one group, K
+    # split in two), on the 32-token tile, the 128-token tile and the
+    # K-quants' 32-token tile
     ("q4_0", 20, 16256, 512), ("q4_0", 20, 16384, 512), ("q8_0", 100, 16256, 512), ("q8_0", 100, 16384, 512),
     ("q4_k", 20, 16256, 1024), ("q4_k", 20, 16384, 1024),
 ]
@@ -553,10 +554,10 @@ def test_matmul_q4_k_full_size_sampled(env):
                                        ("q6_k", 6, 100)])
 def test_matmul_bench_few_token_shapes_sampled(env, fmt, cfg, M):
     """The few-token products the bench times on the MFMA kernels (12288 x
-    4096): the 32-token tiles (K split in two at Q4_0 M = 32, two K groups
-    per workgroup, and at Q4_K M = 64; K in one part at M = 128) and Q6_K's
-    128-token tile with K split in two, checked on whole rows and sampled
-    outputs."""
+    4096): the 32-token tiles (Q4_0 M = 32: four K groups per workgroup;
+    Q4_K M = 64: K split in two; Q4_K M = 128: K in one part), Q4_0's
+    128-token tile with two K groups at M = 128 and Q6_K's with K split in
+    two, checked on whole rows and sampled outputs."""
     torch, q, orc = env
     N, K = 12288, 4096
     _say("matmul few-token bench shape", fmt, M, N, K)
@@ -650,8 +651,8 @@ def test_matmul_rows_equal_matvec(env, M, N, K):
     """Row m of the prefill product and the decode product of token m are two
     evaluations of the same outputs, each within the bound of the oracle.  M
     is past the few-token switch, so the rows come from the 32-token MFMA
-    tiles: K split in two and two K groups per workgroup at N = 300 (6
-    tiles), K in one part at N = 33000 (516 tiles)."""
+    tiles: four K groups per workgroup at N = 300, one group and K in one
+    part at N = 33000 (516 tiles)."""
     torch, q, orc = env
     _say("matmul rows vs matvec", M, N, K)
     wq, xq = _inputs("q4_0", M, N, K, 7000 + N)
@@ -707,9 +708,10 @@ def test_split_k_matmul_overwrites_and_is_deterministic(env, fmt, M):
     """A prefill launch of few tiles splits K in two and adds the halves into
     a zeroed output: calling it twice on a garbage-filled output gives the
     same bits each time (two addends sum the same in either order).  M = 40
-    runs the 32-token tiles and M = 200 the 128-token tiles, both with two K
-    groups per workgroup (each group's sums handed over through LDS in a
-    fixed order) except Q2_K, Q4_K and Q6_K at M = 200."""
+    runs the 32-token tiles (Q4_0, Q5_1: K whole in four groups per
+    workgroup and plain stores; the K-quants: K split, two groups) and M =
+    200 the 128-token tiles (two groups for Q4_0 and Q5_1); the groups' sums
+    are handed over through LDS in a fixed order."""
     torch, q, orc = env
     N, K = 1000, 4096
     _say("split-k repeat", fmt, M, N, K)
@@ -856,9 +858,10 @@ def test_graph_replay_matches_eager(env):
     """Decode and prefill launches captured into a HIP graph: every replay, with
     eager work and synchronizations in between, equals the eager result bit for
     bit (the kernels are deterministic and keep no state).  The products reach
-    the 32-token tiles with two K groups (M = 64), the 128-token tile with two
-    K groups (M = 100) and the few-token decode kernel (M = 4), each split
-    launch with its fill kernel."""
+    the 32-token tiles with K groups (M = 64: four for Q4_0, two with K split
+    for the K-quants), the 128-token tile with two K groups and K split (M =
+    100) and the few-token decode kernel (M = 4), each split launch with its
+    fill kernel."""
     torch, q, orc = env
     N, K, M, M2, M3 = 1024, 4096, 64, 100, 4
     w = synth.weights(N, K, config=1)

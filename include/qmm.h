@@ -215,9 +215,9 @@ qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, flo
  * memory from hipMalloc; two addends give the same bits in either order, so
  * repeated calls are bitwise reproducible; a launch of fewer than 128
  * tiles first sums each half from two quarters, in a fixed order).  The
- * 32-value formats' 32-token launches of fewer than 128 such tiles instead
- * sum all of K inside each workgroup (four quarters, in a fixed order) and
- * write y with plain stores.
+ * 32-token launches of fewer than 128 such tiles (every format but Q6_K)
+ * instead sum all of K inside each workgroup (four quarters, in a fixed
+ * order) and write y with plain stores.
  * The 32-value formats (Q4_0, Q8_0, Q4_1, Q5_0, Q5_1) run on int8 MFMA (4-bit
  * codes enter as 16 * (q - 8), 5-bit codes as 8 * (q - 16); the offset term
  * of Q4_1 / Q5_1, m * dx * sum x per block, runs on an f32 MFMA) and also

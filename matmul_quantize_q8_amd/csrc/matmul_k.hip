@@ -102,10 +102,15 @@ template <int F> struct KW {
 // tile), so that a few tokens do not pay for the 96 rows of a 128-token tile
 // past M.  A stage image is the 32 activation rows (608 chunks in ten wave
 // loads; lanes past the last chunk re-load it into padding), then the 128
-// weight rows.  A split launch of fewer workgroups than CUs runs two such
-// groups per workgroup (G = 2), each with its own stage buffers on half of
-// the part's super-blocks, stepping through the same barriers; group 1 hands
-// its sums to group 0 through LDS at the end (the same order on every call).
+// weight rows.  A launch of fewer workgroups than CUs runs K groups per
+// workgroup, each with its own stage buffers on its share of the
+// super-blocks, stepping through the same barriers; groups 1.. hand their
+// sums to group 0 through LDS at the end (the same order on every call).
+// Q2_K and Q4_K run four groups of two waves on 64 weight rows with K whole
+// and plain stores (no fill kernel, no atomic adds: Q4_K M = 32, N = 12288,
+// K = 4096: 13.5 us with two groups on a split launch, 11.3 with four);
+// Q6_K, whose four groups of stage buffers do not fit LDS, two groups of
+// four on each half of a split launch.
 constexpr int NBM = 32;                        // tokens per narrow tile
 // Token counts up to which the narrow tile runs: up to 128 for Q2_K and
 // Q4_K, whose full tiles of 256 weight rows leave most CUs idle below 129
@@ -114,20 +119,19 @@ constexpr int NBM = 32;                        // tokens per narrow tile
 // 52.7 / 37.3; Q6_K 44.3 / 62.3, 49.8 / 63.7).
 constexpr int narrow_tokens(int f) { return f == F_Q6_K ? 2 * NBM : 4 * NBM; }
 constexpr int NXQ = 10;                        // wave loads of activation chunks
-template <int F, int G> struct KN {
+template <int F, int G, int WPG = 4> struct KN {   // G groups of WPG waves (32 weight rows each)
     using W = KW<F>;
-    static constexpr int NW = 4 * G;                         // waves per workgroup
-    static constexpr int BN = 128;                           // weight rows per workgroup tile
-    static constexpr int WQ = BN * W::WC / kWave;            // 14, 18 or 28 wave loads of weight chunks
+    static constexpr int NW = WPG * G;                       // waves per workgroup
+    static constexpr int BN = 32 * WPG;                      // weight rows per workgroup tile
+    static constexpr int WQ = BN * W::WC / kWave;            // 14, 18 or 28 wave loads of weight chunks (WPG = 4)
     static constexpr int NQ = NXQ + WQ;                      // 24, 28 or 38
-    static constexpr int PER_WAVE = (NQ + 3) / 4;            // 6, 7 or 10
+    static constexpr int PER_WAVE = (NQ + WPG - 1) / WPG;    // 6, 7 or 10
     static constexpr int WOFF = NXQ * 1024;
     static constexpr int STAGE = NQ * 1024;                  // 24,576, 28,672 or 38,912 bytes
     static constexpr int D8 = G * NBUF * STAGE;              // per-wave f32 d8 of its 32 rows
     static constexpr int LDS_BYTES = D8 + NW * 32 * 4;
-    static_assert(NBM * XC <= NXQ * kWave && WQ * kWave == BN * W::WC && NQ > 4 * (PER_WAVE - 1),
+    static_assert(NBM * XC <= NXQ * kWave && WQ * kWave == BN * W::WC && NQ > WPG * (PER_WAVE - 1),
                   "a stage splits into whole wave loads; only the last round of loads has gaps");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
 }  // namespace mk
 
@@ -165,15 +169,16 @@ __device__ __forceinline__ void q4k_sc_m(uint32_t s0, uint32_t s1, uint32_t s2, 
     }
 }
 
-template <int F, bool SPLIT, bool NARROW = false, int G = 1>
+template <int F, bool SPLIT, bool NARROW = false, int G = 1, int WPG = 4>
 __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
                                               float *__restrict__ y, int M, int N, int ns, int tiles_m) {
     using namespace mk;
     using W = KW<F>;
-    using KT = KN<F, G>;
-    static_assert(G == 1 || (G == 2 && NARROW && SPLIT), "K groups only on split launches of the narrow tile");
+    using KT = KN<F, G, WPG>;
+    static_assert(G == 1 || (G == 2 && NARROW && SPLIT && WPG == 4) || (G == 4 && NARROW && !SPLIT && WPG == 2),
+                  "two K groups on split narrow launches, four groups of two waves on unsplit ones");
     constexpr int WC = W::WC, WROW = W::WROW;
-    constexpr int NWG = NARROW ? 4 : NW;                 // waves per K group
+    constexpr int NWG = NARROW ? WPG : NW;               // waves per K group
     constexpr int XQN = NARROW ? NXQ : XQ;               // wave loads of activation chunks
     constexpr int NQ = NARROW ? KT::NQ : W::NQ, PER_WAVE = NARROW ? KT::PER_WAVE : W::PER_WAVE;
     constexpr int STAGE = NARROW ? KT::STAGE : W::STAGE, D8 = NARROW ? KT::D8 : W::D8;
@@ -181,8 +186,8 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
     constexpr int WO = NARROW ? KT::WOFF : WOFF;         // weight rows start (bytes into a stage buffer)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63;
-    const int wave = uniform(NARROW ? (t >> 6) & 3 : t >> 6);
-    const int grp = G == 1 ? 0 : uniform(t >> 8);       // K group: its own stage buffers and super-blocks
+    const int wave = uniform(NARROW ? (t >> 6) % WPG : t >> 6);
+    const int grp = G == 1 ? 0 : uniform((t >> 6) / WPG);   // K group: its own stage buffers and super-blocks
     // SPLIT: the grid holds every tile twice, one per part of K, and both
     // parts add into the zeroed output.  Part p of P = ksplit * G (grid part
     // and K group) takes super-blocks [ceil(p ns / P), ceil((p + 1) ns / P))
@@ -199,9 +204,10 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
     const int s1 = G == 1 ? (SPLIT && !gpart ? sh : ns) : first_sb(G * gpart + grp + 1);
     // every wave of the workgroup passes the same barriers: the K groups
     // step together for the larger of their super-block counts
-    const int nsteps = G == 1 ? s1 - s0
-                              : max(first_sb(G * gpart + 1) - first_sb(G * gpart),
-                                    first_sb(G * gpart + 2) - first_sb(G * gpart + 1));
+    int nsteps = s1 - s0;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        if (G > 1) nsteps = max(nsteps, first_sb(G * gpart + g + 1) - first_sb(G * gpart + g));
     const uint32_t xrow = (uint32_t)ns * kQ8KBytes, wrow = (uint32_t)ns * W::WB;
 
     // DMA: wave load q = wave + 8k (k < PER_WAVE; narrow: 4k) of a stage is
@@ -595,19 +601,22 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
     }
     // no LDS-DMA write may still be in flight when the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (G == 2) {
-        // group 1 hands its sums to group 0 through LDS ([wave][r][lane],
-        // over the stage buffers), which adds them to its own
+    if constexpr (G > 1) {
+        // groups 1 .. G-1 hand their sums to group 0 through LDS ([group -
+        // 1][wave][r][lane], over the stage buffers), which adds them to its
+        // own in group order
         float *red = reinterpret_cast<float *>(lds) + 1024 * wave + lane;
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (grp == 1) {
+        if (grp > 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[64 * r] = acc[0][r];
+            for (int r = 0; r < 16; ++r) red[1024 * NWG * (grp - 1) + 64 * r] = acc[0][r];
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (grp == 1) return;
+        if (grp > 0) return;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[0][r] += red[64 * r];
+        for (int g = 1; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[0][r] += red[1024 * NWG * (g - 1) + 64 * r];
     }
 
     const int n = n0 + 32 * wn + lr;
@@ -643,11 +652,12 @@ __global__ __launch_bounds__(mk::NT) void k_matmul_k_split(const uint8_t *__rest
 // The narrow tile (32 tokens x 128 weight rows) for launches of up to
 // narrow_tokens tokens: one group of four waves, K whole or split in two,
 // or (G = 2) two groups on the halves of each split part.
-template <int F, bool SPLIT, int G>
-__global__ __launch_bounds__(256 * G) void k_matmul_k_narrow(const uint8_t *__restrict__ w,
-                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
-                                                             int M, int N, int ns, int tiles_m) {
-    matmul_k_body<F, SPLIT, true, G>(w, xq, y, M, N, ns, tiles_m);
+template <int F, bool SPLIT, int G, int WPG = 4>
+__global__ __launch_bounds__(64 * WPG * G) void k_matmul_k_narrow(const uint8_t *__restrict__ w,
+                                                                  const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                                  int M, int N, int ns, int tiles_m) {
+    static_assert(mk::KN<F, G, WPG>::LDS_BYTES <= 160 * 1024, "LDS of one CU");
+    matmul_k_body<F, SPLIT, true, G, WPG>(w, xq, y, M, N, ns, tiles_m);
 }
 
 // Largest super-block count whose tile offsets fit the 32-bit buffer offsets
@@ -668,9 +678,26 @@ static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N
     const int bm = narrow ? mk::NBM : mk::BM, bn = narrow ? mk::KN<F, 1>::BN : mk::KW<F>::BN;
     int tiles_m = (M + bm - 1) / bm;
     const int64_t tiles = (int64_t)tiles_m * ((N + bn - 1) / bn);
+    void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&ns, (void *)&tiles_m};
+    // Fewer narrow workgroups than CUs (Q2_K, Q4_K): four groups of two
+    // waves on 64 weight rows per workgroup, each on a quarter of K (at
+    // least two super-blocks each), written with plain stores.  Four groups
+    // of Q6_K stage buffers do not fit one CU's LDS.
+    if constexpr (F != F_Q6_K) {
+        if (narrow && tiles * 2 < kCUs && ns >= 8) {
+            using K4 = mk::KN<F, 4, 2>;
+            static int lds_ok4[kLdsDevices] = {};
+            const void *k4 = (const void *)k_matmul_k_narrow<F, false, 4, 2>;
+            const hipError_t e4 = allow_dynamic_lds(k4, (size_t)K4::LDS_BYTES, lds_ok4);
+            if (e4 != hipSuccess) return e4;
+            const int64_t tiles4 = (int64_t)tiles_m * ((N + K4::BN - 1) / K4::BN);
+            return hipLaunchKernel(k4, dim3((unsigned)tiles4), dim3(64 * K4::NW), args, (size_t)K4::LDS_BYTES, st);
+        }
+    }
     const bool split = tiles <= kSplitTiles && ns >= 2;
-    // fewer narrow workgroups than CUs: two K groups per workgroup, each on
-    // half of its part of K (at least one super-block each)
+    // fewer narrow workgroups than CUs otherwise: two K groups per
+    // workgroup, each on half of its part of K (at least one super-block
+    // each)
     const bool groups = narrow && split && tiles * 2 < kCUs && ns >= 4;
     static int lds_ok[5][kLdsDevices] = {};
     const int v = groups ? 4 : narrow ? (split ? 3 : 2) : (split ? 1 : 0);
@@ -688,7 +715,6 @@ static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N
         if (ez != hipSuccess) return ez;
     }
     const int ksplit = split ? 2 : 1;
-    void *args[] = {(void *)&wp, (void *)&xp, (void *)&y, (void *)&M, (void *)&N, (void *)&ns, (void *)&tiles_m};
     return hipLaunchKernel(kern, dim3((unsigned)(tiles * ksplit)), dim3(threads), args, (size_t)lds_bytes, st);
 }
 

@@ -108,9 +108,11 @@ template <int F> struct KW {
 // sums to group 0 through LDS at the end (the same order on every call).
 // Q2_K and Q4_K run four groups of two waves on 64 weight rows with K whole
 // and plain stores (no fill kernel, no atomic adds: Q4_K M = 32, N = 12288,
-// K = 4096: 13.5 us with two groups on a split launch, 11.3 with four);
-// Q6_K, whose four groups of stage buffers do not fit LDS, two groups of
-// four on each half of a split launch.
+// K = 4096: 13.5 us with two groups on a split launch, 11.3 with four), and
+// up to two workgroups per CU two groups of two waves (M = 64: 25.6 us with
+// one group on a split launch, 23.9 with two); Q6_K, whose four groups of
+// stage buffers do not fit LDS, two groups of four on each half of a split
+// launch.
 constexpr int NBM = 32;                        // tokens per narrow tile
 // Token counts up to which the narrow tile runs: up to 128 for Q2_K and
 // Q4_K, whose full tiles of 256 weight rows leave most CUs idle below 129
@@ -175,8 +177,8 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
     using namespace mk;
     using W = KW<F>;
     using KT = KN<F, G, WPG>;
-    static_assert(G == 1 || (G == 2 && NARROW && SPLIT && WPG == 4) || (G == 4 && NARROW && !SPLIT && WPG == 2),
-                  "two K groups on split narrow launches, four groups of two waves on unsplit ones");
+    static_assert(G == 1 || (G == 2 && NARROW && SPLIT && WPG == 4) || ((G == 2 || G == 4) && NARROW && !SPLIT && WPG == 2),
+                  "two K groups on split narrow launches, groups of two waves on unsplit ones");
     constexpr int WC = W::WC, WROW = W::WROW;
     constexpr int NWG = NARROW ? WPG : NW;               // waves per K group
     constexpr int XQN = NARROW ? NXQ : XQ;               // wave loads of activation chunks
@@ -692,6 +694,18 @@ static hipError_t launch_k(const void *w, const void *xq, float *y, int M, int N
             if (e4 != hipSuccess) return e4;
             const int64_t tiles4 = (int64_t)tiles_m * ((N + K4::BN - 1) / K4::BN);
             return hipLaunchKernel(k4, dim3((unsigned)tiles4), dim3(64 * K4::NW), args, (size_t)K4::LDS_BYTES, st);
+        }
+        // up to two such workgroups per CU: two groups of two waves, each on
+        // half of K (at least two super-blocks each)
+        if (narrow && tiles <= kCUs && ns >= 4) {
+            using K2 = mk::KN<F, 2, 2>;
+            static_assert(2 * K2::LDS_BYTES <= 160 * 1024, "two workgroups per CU");
+            static int lds_ok2[kLdsDevices] = {};
+            const void *k2 = (const void *)k_matmul_k_narrow<F, false, 2, 2>;
+            const hipError_t e2 = allow_dynamic_lds(k2, (size_t)K2::LDS_BYTES, lds_ok2);
+            if (e2 != hipSuccess) return e2;
+            const int64_t tiles2 = (int64_t)tiles_m * ((N + K2::BN - 1) / K2::BN);
+            return hipLaunchKernel(k2, dim3((unsigned)tiles2), dim3(64 * K2::NW), args, (size_t)K2::LDS_BYTES, st);
         }
     }
     const bool split = tiles <= kSplitTiles && ns >= 2;

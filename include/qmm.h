@@ -198,6 +198,23 @@ qmm_status qmm_quantize_matvec_q4_0(const void *w, const float *x, void *xq, flo
                                     void *stream);
 qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, float *y, int64_t N, int64_t K,
                                     void *stream);
+/* The same fused decode step for the K-quant weights (minfer "The payoff: a
+ * K-quant dot kernel, walked": they pair with Q8_K activations): every
+ * workgroup quantizes the row to Q8_K super-blocks in LDS with the arithmetic
+ * of qmm_quantize_q8_k, so the result equals qmm_quantize_q8_k followed by
+ * qmm_matvec_q2_k / _q4_k / _q6_k bit for bit; rows of more than 4096 values
+ * with a non-NULL xq8k run those two launches.
+ *   w    : N rows of K/256 Q2_K, Q4_K or Q6_K super-blocks (K % 256 == 0).
+ *   x    : f32 [K], read only.
+ *   xq8k : NULL, or a Q8_K row of K/256 blocks (K/256*292 bytes, 16-byte
+ *          aligned) that receives the quantized activation.
+ *   y    : f32 [N], written. */
+qmm_status qmm_quantize_matvec_q2_k(const void *w, const float *x, void *xq8k, float *y, int64_t N, int64_t K,
+                                    void *stream);
+qmm_status qmm_quantize_matvec_q4_k(const void *w, const float *x, void *xq8k, float *y, int64_t N, int64_t K,
+                                    void *stream);
+qmm_status qmm_quantize_matvec_q6_k(const void *w, const float *x, void *xq8k, float *y, int64_t N, int64_t K,
+                                    void *stream);
 
 /* Matmul, M tokens (prefill, or a few tokens at once).
  *   w  : N rows of weight blocks.   xq : M rows of Q8_0 (Q8_K) blocks.

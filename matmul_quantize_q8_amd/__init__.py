@@ -26,6 +26,8 @@ BLOCK_VALUES = {"q4_0": 32, "q8_0": 32, "q2_k": 256, "q8_k": 256, "q4_k": 256, "
 ACT_FORMAT = {"q4_0": "q8_0", "q8_0": "q8_0", "q2_k": "q8_k", "q4_k": "q8_k", "q6_k": "q8_k",
               "q4_1": "q8_0", "q5_0": "q8_0", "q5_1": "q8_0"}
 WEIGHT_FORMATS = ("q4_0", "q8_0", "q4_1", "q5_0", "q5_1", "q2_k", "q4_k", "q6_k")
+# Weight formats with a fused quantize + matvec decode entry point.
+FUSED_FORMATS = ("q4_0", "q8_0", "q2_k", "q4_k", "q6_k")
 
 STATUS = {0: "QMM_OK", 1: "QMM_E_SHAPE", 2: "QMM_E_NULL", 3: "QMM_E_ALIGN", 4: "QMM_E_DEVICE", 5: "QMM_E_LAUNCH"}
 
@@ -61,7 +63,7 @@ def lib() -> ctypes.CDLL:
         for name in ["qmm_matvec_" + f for f in WEIGHT_FORMATS]:
             getattr(L, name).argtypes = [P, P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
-        for name in ("qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0"):
+        for name in ["qmm_quantize_matvec_" + f for f in FUSED_FORMATS]:
             getattr(L, name).argtypes = [P, P, P, P, I64, I64, P]
             getattr(L, name).restype = ctypes.c_int
         for name in ["qmm_get_rows_" + f for f in WEIGHT_FORMATS]:
@@ -74,8 +76,8 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-EXPORTS = tuple(["qmm_status_string", "qmm_abi_version", "qmm_quantize_q8_k",
-                 "qmm_quantize_matvec_q4_0", "qmm_quantize_matvec_q8_0"] +
+EXPORTS = tuple(["qmm_status_string", "qmm_abi_version", "qmm_quantize_q8_k"] +
+                ["qmm_quantize_matvec_" + f for f in FUSED_FORMATS] +
                 [p + f for p in ("qmm_quantize_", "qmm_matvec_", "qmm_matmul_", "qmm_get_rows_")
                  for f in WEIGHT_FORMATS])
 
@@ -175,6 +177,22 @@ def qmm_quantize_matvec_q8_0(w, x, xq, y, N: int, K: int, stream=None) -> None:
     _call("qmm_quantize_matvec_q8_0", _addr(w), _addr(x), _addr(xq), _addr(y), N, K, _stream(stream))
 
 
+def qmm_quantize_matvec_q2_k(w, x, xq8k, y, N: int, K: int, stream=None) -> None:
+    """Fused decode step for Q2_K weights: quantize f32 x [K] to Q8_K (written
+    to xq8k unless it is None) and y = W x, in one launch."""
+    _call("qmm_quantize_matvec_q2_k", _addr(w), _addr(x), _addr(xq8k), _addr(y), N, K, _stream(stream))
+
+
+def qmm_quantize_matvec_q4_k(w, x, xq8k, y, N: int, K: int, stream=None) -> None:
+    """As qmm_quantize_matvec_q2_k, for Q4_K weights."""
+    _call("qmm_quantize_matvec_q4_k", _addr(w), _addr(x), _addr(xq8k), _addr(y), N, K, _stream(stream))
+
+
+def qmm_quantize_matvec_q6_k(w, x, xq8k, y, N: int, K: int, stream=None) -> None:
+    """As qmm_quantize_matvec_q2_k, for Q6_K weights."""
+    _call("qmm_quantize_matvec_q6_k", _addr(w), _addr(x), _addr(xq8k), _addr(y), N, K, _stream(stream))
+
+
 def qmm_matmul_q4_0(w, xq, y, M: int, N: int, K: int, stream=None) -> None:
     _call("qmm_matmul_q4_0", _addr(w), _addr(xq), _addr(y), M, N, K, _stream(stream))
 
@@ -253,5 +271,7 @@ QUANTIZE_W = {f: globals()["qmm_quantize_" + f] for f in WEIGHT_FORMATS}
 QUANTIZE_X = {f: (qmm_quantize_q8_k if ACT_FORMAT[f] == "q8_k" else qmm_quantize_q8_0) for f in WEIGHT_FORMATS}
 MATVEC = {f: globals()["qmm_matvec_" + f] for f in WEIGHT_FORMATS}
 MATMUL = {f: globals()["qmm_matmul_" + f] for f in WEIGHT_FORMATS}
-QUANTIZE_MATVEC = {"q4_0": qmm_quantize_matvec_q4_0, "q8_0": qmm_quantize_matvec_q8_0}
+QUANTIZE_MATVEC = {"q4_0": qmm_quantize_matvec_q4_0, "q8_0": qmm_quantize_matvec_q8_0,
+                   "q2_k": qmm_quantize_matvec_q2_k, "q4_k": qmm_quantize_matvec_q4_k,
+                   "q6_k": qmm_quantize_matvec_q6_k}
 GET_ROWS = {f: globals()["qmm_get_rows_" + f] for f in WEIGHT_FORMATS}

@@ -29,6 +29,12 @@ hipError_t launch_matvec_q4_k(const void *w, const void *xq, float *y, int N, in
 hipError_t launch_matvec_q6_k(const void *w, const void *xq, float *y, int N, int ns, hipStream_t st);
 hipError_t launch_quantize_matvec_q4_0(const void *w, const float *x, void *xq, float *y, int N, int nb,
                                        hipStream_t st);
+hipError_t launch_quantize_matvec_q2_k(const void *w, const float *x, void *xq, float *y, int N, int nb,
+                                       hipStream_t st);
+hipError_t launch_quantize_matvec_q4_k(const void *w, const float *x, void *xq, float *y, int N, int nb,
+                                       hipStream_t st);
+hipError_t launch_quantize_matvec_q6_k(const void *w, const float *x, void *xq, float *y, int N, int nb,
+                                       hipStream_t st);
 hipError_t launch_quantize_matvec_q8_0(const void *w, const float *x, void *xq, float *y, int N, int nb,
                                        hipStream_t st);
 hipError_t launch_matmul_q4_0(const void *w, const void *xq, float *y, int M, int N, int nb, hipStream_t st);
@@ -205,24 +211,39 @@ qmm_status qmm_matvec_q6_k(const void *w, const void *xq8k, float *y, int64_t N,
 typedef hipError_t (*qmv_launch)(const void *, const float *, void *, float *, int, int, hipStream_t);
 
 static qmm_status quantize_matvec(qmv_launch fn, const void *w, const float *x, void *xq, float *y, int64_t N,
-                                  int64_t K, int64_t wbytes, void *stream) {
-    qmm_status s = check_shape(1, N, K, 32);
+                                  int64_t K, int64_t blk, int64_t wbytes, void *stream) {
+    qmm_status s = check_shape(1, N, K, blk);
     if (s != QMM_OK) return s;
-    if (!size_ok(N, K, 32, wbytes) || !size_ok(1, K, 32, 128)) return QMM_E_SHAPE;
+    if (!size_ok(N, K, blk, wbytes) || !size_ok(1, K, blk, 4 * blk)) return QMM_E_SHAPE;
     if ((s = check_ptrs({w, x, y})) != QMM_OK) return s;
     if (xq != nullptr && !aligned16(xq)) return QMM_E_ALIGN;
     if ((s = check_device()) != QMM_OK) return s;
-    return launched(fn(w, x, xq, y, (int)N, (int)(K / 32), static_cast<hipStream_t>(stream)));
+    return launched(fn(w, x, xq, y, (int)N, (int)(K / blk), static_cast<hipStream_t>(stream)));
 }
 
 qmm_status qmm_quantize_matvec_q4_0(const void *w, const float *x, void *xq, float *y, int64_t N, int64_t K,
                                     void *stream) {
-    return quantize_matvec(qmm::launch_quantize_matvec_q4_0, w, x, xq, y, N, K, qmm::kQ40Bytes, stream);
+    return quantize_matvec(qmm::launch_quantize_matvec_q4_0, w, x, xq, y, N, K, 32, qmm::kQ40Bytes, stream);
 }
 
 qmm_status qmm_quantize_matvec_q8_0(const void *w, const float *x, void *xq, float *y, int64_t N, int64_t K,
                                     void *stream) {
-    return quantize_matvec(qmm::launch_quantize_matvec_q8_0, w, x, xq, y, N, K, qmm::kQ80Bytes, stream);
+    return quantize_matvec(qmm::launch_quantize_matvec_q8_0, w, x, xq, y, N, K, 32, qmm::kQ80Bytes, stream);
+}
+
+qmm_status qmm_quantize_matvec_q2_k(const void *w, const float *x, void *xq8k, float *y, int64_t N, int64_t K,
+                                    void *stream) {
+    return quantize_matvec(qmm::launch_quantize_matvec_q2_k, w, x, xq8k, y, N, K, 256, qmm::kQ2KBytes, stream);
+}
+
+qmm_status qmm_quantize_matvec_q4_k(const void *w, const float *x, void *xq8k, float *y, int64_t N, int64_t K,
+                                    void *stream) {
+    return quantize_matvec(qmm::launch_quantize_matvec_q4_k, w, x, xq8k, y, N, K, 256, qmm::kQ4KBytes, stream);
+}
+
+qmm_status qmm_quantize_matvec_q6_k(const void *w, const float *x, void *xq8k, float *y, int64_t N, int64_t K,
+                                    void *stream) {
+    return quantize_matvec(qmm::launch_quantize_matvec_q6_k, w, x, xq8k, y, N, K, 256, qmm::kQ6KBytes, stream);
 }
 
 typedef hipError_t (*mm_launch)(const void *, const void *, float *, int, int, int, hipStream_t);

@@ -5,6 +5,7 @@
 namespace qmm {
 
 hipError_t launch_quantize_q8_0(const float *x, void *out, int64_t nblocks, hipStream_t st);
+hipError_t launch_quantize_q8_k(const float *x, void *out, int64_t nblocks, hipStream_t st);
 
 // Rows per wave: a slice of about 5 KB.  Measured on MI355X over 28-96 MB
 // of weights, slices of 3-5 KB per wave (Q4_0 K=4096: 2 rows, Q8_0: 1 row,
@@ -74,9 +75,9 @@ template <int F>
 static hipError_t quantize_matvec(const void *w, const float *x, void *xq, float *y, int N, int nb,
                                   hipStream_t st) {
     const bool paired = !kIsK<F> && nb % 2 == 0;
-    const int nu = paired ? nb / 2 : nb;
+    const int nu = kIsK<F> ? 4 * nb : paired ? nb / 2 : nb;   // units per row (a K-quant super-block: 4)
     if (xq != nullptr && nu > kWave) {
-        const hipError_t e = launch_quantize_q8_0(x, xq, nb, st);
+        const hipError_t e = kIsK<F> ? launch_quantize_q8_k(x, xq, nb, st) : launch_quantize_q8_0(x, xq, nb, st);
         if (e != hipSuccess) return e;
         return dispatch_mv<F>(w, xq, nullptr, y, 1, N, nb, st);
     }
@@ -90,6 +91,19 @@ hipError_t launch_quantize_matvec_q4_0(const void *w, const float *x, void *xq, 
 hipError_t launch_quantize_matvec_q8_0(const void *w, const float *x, void *xq, float *y, int N, int nb,
                                        hipStream_t st) {
     return quantize_matvec<F_Q8_0>(w, x, xq, y, N, nb, st);
+}
+// K-quant weights: Q8_K activations, nb = super-blocks per row
+hipError_t launch_quantize_matvec_q2_k(const void *w, const float *x, void *xq, float *y, int N, int nb,
+                                       hipStream_t st) {
+    return quantize_matvec<F_Q2_K>(w, x, xq, y, N, nb, st);
+}
+hipError_t launch_quantize_matvec_q4_k(const void *w, const float *x, void *xq, float *y, int N, int nb,
+                                       hipStream_t st) {
+    return quantize_matvec<F_Q4_K>(w, x, xq, y, N, nb, st);
+}
+hipError_t launch_quantize_matvec_q6_k(const void *w, const float *x, void *xq, float *y, int N, int nb,
+                                       hipStream_t st) {
+    return quantize_matvec<F_Q6_K>(w, x, xq, y, N, nb, st);
 }
 
 hipError_t launch_matvec_q4_1(const void *w, const void *xq, float *y, int N, int nb, hipStream_t st) {

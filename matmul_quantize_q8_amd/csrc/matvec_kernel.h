@@ -34,8 +34,12 @@
 // 16-byte pieces of the row before the weight copies are issued, waits for
 // those loads alone, quantizes them with the same arithmetic as the Q8_0
 // quantizer kernel, and writes the codes to LDS in a lane-friendly layout
-// (per unit: the blocks' 32 codes, then their scales as f32).  One workgroup
-// per token also stores the Q8_0 row to global memory when asked to.
+// (per unit: the blocks' 32 codes, then their scales as f32).  For the
+// K-quant weights the activation is Q8_K: each wave quantizes whole 256-value
+// super-blocks (the Q8_K quantizer's arithmetic, lane L holding values
+// 4L..4L+3) and writes them to LDS in the row's own 292-byte layout, which
+// the K-quant units then read as in the plain kernel.  One workgroup per
+// token also stores the quantized row to global memory when asked to.
 #include "qmm_device.h"
 
 namespace qmm {
@@ -839,13 +843,16 @@ __global__ __launch_bounds__(64 * NW) void k_matvec(const uint8_t *__restrict__ 
                                                 int ss, uint8_t *__restrict__ xq_out, int M) {
     using FB = FmtBytes<F>;
     using UT = Unit<F, PAIRED>;
-    static_assert(!XF32 || !kIsK<F>, "the fused quantizer produces Q8_0 activations");
     static_assert(!XF32 || TT == 1, "the fused quantizer serves one token");
     extern __shared__ uint4 lds_dyn[];
     constexpr int SEGU = kWave * MAXU;                 // units per segment
     constexpr int NT = kWave * NW;                     // threads per workgroup
-    // 16-byte f32 activation pieces per thread and segment (XF32)
-    constexpr int XL = XF32 ? (8 * MAXU * UT::BPU + NW - 1) / NW : 1;
+    // 16-byte f32 activation pieces per thread and segment (XF32): Q8_0,
+    // 8 per block over the workgroup; Q8_K, one super-block per wave, 4
+    // values per lane
+    constexpr int XL = !XF32 ? 1
+                       : kIsK<F> ? (SEGU / UT::UPB + NW - 1) / NW
+                                 : (8 * MAXU * UT::BPU + NW - 1) / NW;
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -874,7 +881,13 @@ __global__ __launch_bounds__(64 * NW) void k_matvec(const uint8_t *__restrict__ 
         uint32_t xoff = 0, xofft[TT];
         const int nch = 8 * (b1 - b0);                 // its 16-byte f32 pieces (XF32)
         v4f xv[XL];
-        if constexpr (XF32) {
+        if constexpr (XF32 && kIsK<F>) {
+            // super-block j of the segment is wave j % NW's, i = j / NW
+            const uint8_t *xseg = xin + xtok + (int64_t)b0 * 1024;
+#pragma unroll
+            for (int i = 0; i < XL; ++i)
+                xv[i] = global_load16_async(xseg, 1024u * (uint32_t)min(wave + NW * i, b1 - b0 - 1) + 16u * lane);
+        } else if constexpr (XF32) {
             const uint8_t *xseg = xin + xtok + (int64_t)b0 * 128;
 #pragma unroll
             for (int i = 0; i < XL; ++i)
@@ -903,7 +916,28 @@ __global__ __launch_bounds__(64 * NW) void k_matvec(const uint8_t *__restrict__ 
             wissued = dma_span<TT == 1>(w, lo, hi, slice, lane, 0, 1);
         }
         wait_vmcnt(wissued);                           // this wave's activation loads have landed
-        if constexpr (XF32) {
+        if constexpr (XF32 && kIsK<F>) {
+            // the segment's Q8_K super-blocks, laid out in LDS as in the
+            // activation row (292 bytes each from offset 0), as the plain
+            // kernel's copy lands them
+            uint8_t *xw8 = reinterpret_cast<uint8_t *>(xlds);
+            uint8_t *xq_row = (xq_out != nullptr && blockIdx.x == 0)
+                                  ? xq_out + (int64_t)blockIdx.y * nb * kQ8KBytes + (int64_t)b0 * kQ8KBytes
+                                  : nullptr;
+#pragma unroll
+            for (int i = 0; i < XL; ++i) {
+                pin_after_wait(xv[i]);
+                const int j = wave + NW * i;
+                int gsum;
+                float d;
+                const uint32_t packed = q8_k_wave(make_float4(xv[i][0], xv[i][1], xv[i][2], xv[i][3]), gsum, d);
+                if (j < b1 - b0) {
+                    store_q8_k_lane(xw8 + j * kQ8KBytes, lane, packed, gsum, d);
+                    if (xq_row != nullptr) store_q8_k_lane(xq_row + (int64_t)j * kQ8KBytes, lane, packed, gsum, d);
+                }
+            }
+            wait_lds_reads();                          // the codes are in LDS
+        } else if constexpr (XF32) {
             constexpr int US = XLayout<UT::BPU>::US;
             uint8_t *xw8 = reinterpret_cast<uint8_t *>(xlds);
             uint8_t *xq_row = (xq_out != nullptr && blockIdx.x == 0)
@@ -962,7 +996,7 @@ __global__ __launch_bounds__(64 * NW) void k_matvec(const uint8_t *__restrict__ 
 #pragma unroll
         for (int i = 0; i < MAXU; ++i) {
             const int ul = min(lane + kWave * i, u1 - u0 - 1);
-            if constexpr (XF32)
+            if constexpr (XF32 && !kIsK<F>)
                 load_xu_q<F, PAIRED>(xl8, ul, xu[i]);
             else
                 load_xu<F, PAIRED>(xl8, xoff, ul, xu[i]);
@@ -1019,13 +1053,13 @@ static hipError_t launch_mv(const void *w, const void *xin, uint8_t *xq_out, flo
     // whole 1 KB chunk groups (dma_span may fill a full last group) after up to
     // 15 bytes of misalignment at each end
     const int ss = (int)(((span + 32 + 1023) / 1024) * 1024);
-    const int xs = XF32 ? (XLayout<UT::BPU>::US * segu + 15) / 16 * 16
-                        : (int)((((int64_t)segb * FB::XB + 32 + 1023) / 1024) * 1024);
+    const int xs = (XF32 && !kIsK<F>) ? (XLayout<UT::BPU>::US * segu + 15) / 16 * 16
+                                      : (int)((((int64_t)segb * FB::XB + 32 + 1023) / 1024) * 1024);
     const int64_t waves = ((int64_t)N + G - 1) / G;
     const int64_t grid = (waves + NW - 1) / NW;
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *xp = static_cast<const uint8_t *>(xin);
-    int64_t xrow = XF32 ? (int64_t)nb * 128 : (int64_t)nb * FB::XB;
+    int64_t xrow = XF32 ? (int64_t)nb * (kIsK<F> ? 1024 : 128) : (int64_t)nb * FB::XB;   // f32: 4 bytes a value
     const auto kern = k_matvec<F, PAIRED, G, MAXU, XF32, NW, TT>;
     const size_t lds = (size_t)TT * xs + (size_t)NW * ss;
     static int lds_ok[kLdsDevices] = {};

@@ -225,6 +225,27 @@ __device__ __forceinline__ float max8_lanes(float a) {
     return fmaxf(a, dpp_f32<kDppHalfRowMirror>(a));
 }
 
+// Maximum over the whole wave (every lane gets it): each 16-lane row's by
+// DPP (the 8-lane maxima, then the other half row's by a rotation of 8),
+// then the four rows' read into scalar registers.  No LDS trip, so it does
+// not queue behind DMA traffic into LDS.  Exact in any order.
+__device__ __forceinline__ float max64_lanes(float a) {
+    a = max8_lanes(a);
+    a = fmaxf(a, dpp_f32<kDppRowRor8>(a));
+    const int b = __builtin_bit_cast(int, a);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Sum over each aligned quad of lanes (every lane of the quad gets it).
+__device__ __forceinline__ int sum4_lanes(int s) {
+    s += __builtin_amdgcn_update_dpp(0, s, kDppQuadXor1, 0xF, 0xF, false);
+    return s + __builtin_amdgcn_update_dpp(0, s, kDppQuadXor2, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ uint32_t q8_0_part(float4 v, float &d) {
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     a = max8_lanes(a);
@@ -250,6 +271,40 @@ __device__ __forceinline__ void store_q8_0_part(uint8_t *blk, int part, uint32_t
     o16[0] = (uint16_t)(packed & 0xffffu);
     o16[1] = (uint16_t)(packed >> 16);
     if (part == 0) *reinterpret_cast<uint16_t *>(blk) = (uint16_t)f32_to_f16_bits(d);
+}
+
+// Q8_K quantization (minfer quantize_row_q8_k_buf) of one 256-value
+// super-block held by a whole wave, lane L with values 4L..4L+3 (group L/4
+// of 16 values): amax over the wave (max64_lanes), d = amax/127 (kept f32), id = amax ?
+// 127/amax : 0, q = saturate(rne(x*id)) to [-128, 127].  Returns the lane's
+// four codes packed little-endian and sets gsum to its group's code sum (the
+// same in the group's four lanes) and d.  The same single correctly rounded
+// f32 steps as q8_0_part, so every kernel using it yields the same bytes.
+// All 64 lanes must call it together.
+__device__ __forceinline__ uint32_t q8_k_wave(float4 v, int &gsum, float &d) {
+    const float a = max64_lanes(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    d = a / 127.0f;
+    const float id = (a != 0.0f) ? 127.0f / a : 0.0f;
+    int q[4];
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float r = rintf(vv[k] * id);
+        r = fminf(fmaxf(r, -128.0f), 127.0f);
+        q[k] = (int)r;
+    }
+    gsum = sum4_lanes(q[0] + q[1] + q[2] + q[3]);
+    return (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) | ((uint32_t)(q[2] & 0xff) << 16) |
+           ((uint32_t)(q[3] & 0xff) << 24);
+}
+
+// Store one lane's share of a Q8_K block at `blk` (4-byte aligned, 292
+// bytes: f32 d, 256 codes, 16 int16 group sums): its four codes, its group's
+// sum from the group's first lane and d from lane 0.
+__device__ __forceinline__ void store_q8_k_lane(uint8_t *blk, int lane, uint32_t packed, int gsum, float d) {
+    *reinterpret_cast<uint32_t *>(blk + 4 + 4 * lane) = packed;
+    if ((lane & 3) == 0) *reinterpret_cast<int16_t *>(blk + 260 + 2 * (lane >> 2)) = (int16_t)gsum;
+    if (lane == 0) *reinterpret_cast<float *>(blk) = d;
 }
 
 }  // namespace qmm

@@ -41,31 +41,10 @@ __global__ __launch_bounds__(256) void k_quantize_q8_k(const float4 *__restrict_
     const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (blk >= nblocks) return;                               // whole wave exits together
     const float4 v = x[blk * 64 + lane];
-
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) a = fmaxf(a, xor_shfl(a, m));
-
-    const float d = a / 127.0f;
-    const float id = (a != 0.0f) ? 127.0f / a : 0.0f;
-    int q[4];
-    const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float r = rintf(vv[k] * id);
-        r = fminf(fmaxf(r, -128.0f), 127.0f);
-        q[k] = (int)r;
-    }
-    const uint32_t packed = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
-                            ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
-    int s = q[0] + q[1] + q[2] + q[3];
-    s += xor_shfl(s, 1);
-    s += xor_shfl(s, 2);
-
-    uint8_t *ob = out + blk * kQ8KBytes;                      // 292 = 4 * 73: 4-byte aligned
-    *reinterpret_cast<uint32_t *>(ob + 4 + 4 * lane) = packed;
-    if ((lane & 3) == 0) *reinterpret_cast<int16_t *>(ob + 260 + 2 * (lane >> 2)) = (int16_t)s;
-    if (lane == 0) *reinterpret_cast<float *>(ob) = d;
+    int gsum;
+    float d;
+    const uint32_t packed = q8_k_wave(v, gsum, d);
+    store_q8_k_lane(out + blk * kQ8KBytes, lane, packed, gsum, d);   // 292 = 4 * 73: 4-byte aligned
 }
 
 // ---------------------------------------------------------------------------

@@ -75,6 +75,9 @@ A = 1 << 20          # a 16-byte aligned fake device address (never dereferenced
     (lambda L: L.qmm_quantize_matvec_q8_0(A, A, A, None, 8, 64, None), 2),   # y NULL
     (lambda L: L.qmm_quantize_matvec_q8_0(A, A, A + 2, A, 8, 64, None), 3),  # xq misaligned
     (lambda L: L.qmm_quantize_matvec_q4_0(A, A + 4, None, A, 8, 64, None), 3),
+    (lambda L: L.qmm_quantize_matvec_q2_k(A, A, A, A, 8, 32 * 9, None), 1),   # K % 256
+    (lambda L: L.qmm_quantize_matvec_q4_k(A, A, A + 4, A, 8, 256, None), 3),  # xq8k misaligned
+    (lambda L: L.qmm_quantize_matvec_q6_k(None, A, A, A, 8, 256, None), 2),   # w NULL
     (lambda L: L.qmm_matvec_q4_k(A, A, A, 8, 32 * 9, None), 1),                # K % 256
     (lambda L: L.qmm_matmul_q6_k(A, A, A, 2, 8, 256 + 32, None), 1),
     (lambda L: L.qmm_quantize_q6_k(A, A, 1, 128, None), 1),
@@ -170,6 +173,7 @@ def test_empty_problem_is_a_shape_error(q):
     assert L.qmm_quantize_q8_0(None, None, 0, 64, None) == 1
     assert L.qmm_quantize_q8_k(None, None, 0, 256, None) == 1
     assert L.qmm_quantize_matvec_q4_0(None, None, None, None, 0, 64, None) == 1
+    assert L.qmm_quantize_matvec_q6_k(None, None, None, None, 0, 256, None) == 1
     assert L.qmm_get_rows_q4_0(None, None, None, 0, 8, 32, None) == 1
     assert L.qmm_get_rows_q4_0(None, None, None, 4, 0, 32, None) == 1
 

@@ -45,6 +45,7 @@ int main(void) {
     expect("matmul K", qmm_matmul_q4_0(A, A, (float *)A, 4, 8, 33, NULL), QMM_E_SHAPE);
     expect("matmul M", qmm_matmul_q4_0(A, A, (float *)A, (int64_t)1 << 31, 8, 32, NULL), QMM_E_SHAPE);
     expect("fused K", qmm_quantize_matvec_q4_0(A, (const float *)A, A, (float *)A, 8, 48, NULL), QMM_E_SHAPE);
+    expect("fused K-quant K", qmm_quantize_matvec_q4_k(A, (const float *)A, A, (float *)A, 8, 288, NULL), QMM_E_SHAPE);
     expect("matmul M = 0", qmm_matmul_q4_0(NULL, NULL, NULL, 0, 8, 32, NULL), QMM_E_SHAPE);
     expect("matmul N = 0", qmm_matmul_q4_0(NULL, NULL, NULL, 4, 0, 32, NULL), QMM_E_SHAPE);
     expect("matvec N = 0", qmm_matvec_q8_0(NULL, NULL, NULL, 0, 32, NULL), QMM_E_SHAPE);

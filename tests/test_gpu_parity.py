@@ -215,13 +215,20 @@ FUSED_CASES = [
     ("q8_0", 37, 256), ("q8_0", 3, 64), ("q8_0", 5, 16384), ("q8_0", 3, 40960), ("q8_0", 16411, 256),
     ("q8_0", 12288, 4096), ("q8_0", 22016, 4096), ("q8_0", 4096, 11008),
     ("q8_0", 1, 32), ("q8_0", 11, 4128), ("q8_0", 3, 20000),
+    # K-quant weights with Q8_K activations: one segment (up to 16 super-blocks,
+    # 2 per wave of eight), 8 rows per wave, ragged waves; longer rows run the
+    # quantizer and the plain kernel when xq is requested
+    ("q2_k", 12288, 4096), ("q4_k", 12288, 4096), ("q6_k", 12288, 4096),
+    ("q2_k", 1, 256), ("q4_k", 3, 768), ("q6_k", 5, 1280), ("q4_k", 45, 512), ("q6_k", 37, 512),
+    ("q2_k", 16390, 256), ("q4_k", 16391, 512), ("q6_k", 4099, 3840),
+    ("q2_k", 13, 9216), ("q4_k", 2, 40960), ("q6_k", 13, 9216),
 ]
 
 
 def _run_fused(env, fmt, wq, x, N, K, want_xq=True):
     torch, q, _ = env
     y = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
-    xq = torch.full((q.row_bytes("q8_0", K),), 0xA5, dtype=torch.uint8, device="cuda") if want_xq else None
+    xq = torch.full((q.row_bytes(q.ACT_FORMAT[fmt], K),), 0xA5, dtype=torch.uint8, device="cuda") if want_xq else None
     q.QUANTIZE_MATVEC[fmt](_dev(torch, wq), _dev(torch, x), xq, y, N, K)
     torch.cuda.synchronize()
     return y.cpu().numpy(), (xq.cpu().numpy() if want_xq else None)
@@ -230,8 +237,8 @@ def _run_fused(env, fmt, wq, x, N, K, want_xq=True):
 @pytest.mark.parametrize("fmt,N,K", FUSED_CASES)
 def test_fused_quantize_matvec_matches_oracle(env, fmt, N, K):
     """One launch quantizes the f32 activation and applies the weights: the
-    Q8_0 row it writes is the oracle's byte for byte, the output is within the
-    bound of the oracle's product on that row."""
+    Q8_0 (Q8_K) row it writes is the oracle's byte for byte, the output is
+    within the bound of the oracle's product on that row."""
     _, _, orc = env
     _say("quantize_matvec", fmt, N, K)
     seed = 9000 + N + K
@@ -246,7 +253,11 @@ def test_fused_quantize_matvec_matches_oracle(env, fmt, N, K):
         x[0, 64] = 127.0
     if K >= 128:
         x[0, 96:128] *= 1e-30                         # tiny but inside the contract
-    xq_ref = orc.quantize_q8_0(x)
+    if K >= 512:
+        x[0, 256:512] = 0.0                           # zero super-block
+    if K >= 768:
+        x[0, 512:768] = np.arange(256, dtype=np.float32) - 128.0   # amax 128: x * 127/128 ties at .5
+    xq_ref = orc.quantize_x(fmt, x)
     y, xq = _run_fused(env, fmt, wq, x, N, K)
     assert np.array_equal(xq, xq_ref.reshape(-1))
     ref = orc.matmul(fmt, wq, xq_ref, 1, N, K, threads=8, want=("y64", "mag"))
@@ -255,7 +266,9 @@ def test_fused_quantize_matvec_matches_oracle(env, fmt, N, K):
 
 @pytest.mark.parametrize("fmt,N,K", [("q4_0", 1000, 4096), ("q4_0", 37, 8192), ("q4_0", 9, 20480),
                                      ("q4_0", 5, 2080), ("q4_0", 45, 1024), ("q8_0", 300, 4096),
-                                     ("q8_0", 3, 40960), ("q8_0", 11, 4128)])
+                                     ("q8_0", 3, 40960), ("q8_0", 11, 4128),
+                                     ("q2_k", 300, 4096), ("q4_k", 37, 8192), ("q6_k", 9, 20480),
+                                     ("q2_k", 13, 9216), ("q4_k", 5, 40960), ("q6_k", 45, 1280)])
 def test_fused_without_xq_output_equals_two_launches(env, fmt, N, K):
     """xq = NULL (always the single fused launch, also for long rows): y is
     within the bound of the oracle and bit-identical to the two-launch path
@@ -265,13 +278,14 @@ def test_fused_without_xq_output_equals_two_launches(env, fmt, N, K):
     wq = orc.quantize_w(fmt, synth.gaussian_f32((N, K), 0.02, 9500 + K))
     x = synth.with_outliers(synth.gaussian_f32((1, K), 1.0, 9501 + K), 0.01, 20.0, 9502 + K)
     y, _ = _run_fused(env, fmt, wq, x, N, K, want_xq=False)
-    xq_d = torch.empty(q.row_bytes("q8_0", K), dtype=torch.uint8, device="cuda")
-    q.qmm_quantize_q8_0(_dev(torch, x), xq_d, 1, K)
+    act = q.ACT_FORMAT[fmt]
+    xq_d = torch.empty(q.row_bytes(act, K), dtype=torch.uint8, device="cuda")
+    getattr(q, "qmm_quantize_" + act)(_dev(torch, x), xq_d, 1, K)
     y2 = torch.empty(N, dtype=torch.float32, device="cuda")
     q.MATVEC[fmt](_dev(torch, wq), xq_d, y2, N, K)
     torch.cuda.synchronize()
     assert np.array_equal(y, y2.cpu().numpy())
-    ref = orc.matmul(fmt, wq, orc.quantize_q8_0(x), 1, N, K, threads=8, want=("y64", "mag"))
+    ref = orc.matmul(fmt, wq, orc.quantize_x(fmt, x), 1, N, K, threads=8, want=("y64", "mag"))
     _check(y, ref["y64"][0], ref["mag"][0], ("fused no xq", fmt, N, K))
 
 

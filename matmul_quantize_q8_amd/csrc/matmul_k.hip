@@ -40,13 +40,13 @@
 //
 // Q4_K weights (the same staging, weight rows of 144 bytes in nine chunks):
 // sub-block j of 32 values has a 6-bit scale sc_j and min m_j (minfer "The
-// payoff: a K-quant dot kernel, walked"), and sc_j q <= 63 * 15 is no int8,
-// so K-step t (= sub-block t) gets its own exact int32 tile
-// I_t = sum q x (one v_mfma_i32_32x32x32_i8 on the 4-bit codes) and
-// V = sum_t sc_t I_t accumulates in int32 with one v_mad_i32_i24 per output
-// (|I_t| <= 32*15*128 < 2^23, |V| < 2^25); the min term is the same f16
-// MFMA over the block sums (m <= 63, |Mn| < 2^22, exact), and the fold is
-// acc += d8 * ((float)V * d - dmin * Mn).
+// payoff: a K-quant dot kernel, walked"), and sc_j q <= 63 * 15 is no int8;
+// but sc_j = 8 sh_j + sl_j with sh_j, sl_j <= 7, and sh_j q, sl_j q <= 105
+// are, so two 256-deep int8 contractions A1 = sum sh q x and A2 = sum sl q x
+// (eight v_mfma_i32_32x32x32_i8 each, int32, |A| < 2^22) give
+// V = sum_j sc_j sum q x = 8 A1 + A2 exactly (|V| < 2^25); the min term is
+// the same f16 MFMA over the block sums (m <= 63, |Mn| < 2^22, exact), and
+// the fold is acc += d8 * ((float)V * d - dmin * Mn).
 // Output lane layout of a 32x32 MFMA tile: lane l, register r holds row
 // 8(r/4) + 4(l/32) + r%4 and column l%32.
 #include "qmm_device.h"
@@ -138,6 +138,7 @@ template <int F, int G, int WPG = 4> struct KN {   // G groups of WPG waves (32 
 }  // namespace mk
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // BYTES per lane from a buffer into LDS at m0base + OFF + 16 * lane (see the
 // Q4_0 prefill kernel: inline assembly so that the compiler neither waits for
@@ -386,63 +387,43 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
             int sc[8], mm[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) q4k_sc_m(s0, s1, s2, j, sc[j], mm[j]);
-            // value term: sub-block kt is K-step kt, the 4-bit codes of qs
-            // chunk kt/2 (low nibbles for even kt, high for odd); one exact
-            // int32 tile per sub-block, V += sc * I in int32
-            int V[TI][16];
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) V[i][r] = 0;
-            // The 8 TI steps t = TI kt + i are software-pipelined: the MFMA of
-            // step t+1 is issued before the scale mads of step t (two int32
-            // tiles live), its A operand is read one step ahead and each
-            // 16-byte code chunk (K-steps 2c, 2c+1) before its first use (TI
-            // = 4: three steps; narrow: one, right after the last B operand
-            // from the chunk before), so that neither the LDS reads nor the
-            // MFMA latency stall the wave.
-            auto nibbles = [](const uint4 &q, int kt) __attribute__((always_inline)) {
-                const uint32_t sh = 4u * (uint32_t)(kt & 1);
-                return v4i{(int)((q.x >> sh) & 0x0f0f0f0fu), (int)((q.y >> sh) & 0x0f0f0f0fu),
-                           (int)((q.z >> sh) & 0x0f0f0f0fu), (int)((q.w >> sh) & 0x0f0f0f0fu)};
-            };
-            auto read_a = [&](int t) __attribute__((always_inline)) {
-                return as_v4i(rd16(sb + xa + XROW * 32 * (t % TI) + 32 * (t / TI) + 16 * lh));
-            };
-            constexpr int T = 8 * TI;
+            // value term: sub-block kt is K-step kt, on the 4-bit codes of qs
+            // chunk kt/2 (low nibbles for even kt, high for odd).  The scale
+            // splits as sc = 8 sh + sl (sh, sl <= 7), so sh q and sl q (<= 105)
+            // are exact int8 operands: two 256-deep int32 contractions
+            // A1 = sum sh q x and A2 = sum sl q x on MFMA give
+            // V = sum sc I = 8 A1 + A2 (|A1|, |A2| <= 256*105*128 < 2^22),
+            // with no vector work per sub-block and output (one v_mad_i32_i24
+            // per sub-block and output before: four VALU cycles each, twice
+            // the MFMA time)
+            v16i A1[TI], A2[TI];
             const v16i zero = {};
-            uint4 qs = rd16(sb + wb + 16 + 16 * lh);   // chunk 0
-            v4i b = nibbles(qs, 0);
-            v4i an = read_a(1);
-            v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(read_a(0), b, zero, 0, 0, 0);
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int kt = t / TI, i = t % TI;
-                v16i In = zero;
-                if (t + 1 < T) {
-                    const int kn = (t + 1) / TI;
-                    if ((t + 1) % TI == 0) b = nibbles(qs, kn);
-                    In = __builtin_amdgcn_mfma_i32_32x32x32_i8(an, b, zero, 0, 0, 0);
-                    if (t + 2 < T) an = read_a(t + 2);
-                    // the next chunk, once the last B operand built from this one is out
-                    if constexpr (TI == 4) {
-                        if (i == 0 && (kt & 1) == 1 && kt < 7) qs = rd16(sb + wb + 16 + 32 * ((kt + 1) >> 1) + 16 * lh);
-                    } else {
-                        if ((t + 1) % TI == 0 && (kn & 1) == 1 && kn < 7)
-                            qs = rd16(sb + wb + 16 + 32 * ((kn + 1) >> 1) + 16 * lh);
-                    }
+            for (int i = 0; i < TI; ++i) A1[i] = A2[i] = zero;
+            uint4 qs = rd16(sb + wb + 16 + 16 * lh);   // chunk 0 (K-steps 0, 1)
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                if (kt >= 2 && (kt & 1) == 0) qs = rd16(sb + wb + 16 + 32 * (kt >> 1) + 16 * lh);
+                const uint32_t sft = 4u * (uint32_t)(kt & 1);
+                // byte-wise products by a multiply of the two 16-bit halves
+                // (v_pk_mul_lo_u16): each half holds two codes b0 + 256 b1,
+                // and b0 s <= 105, 256 b1 s < 2^16, so no carry crosses a byte
+                const unsigned short sh = (unsigned short)(sc[kt] >> 3), sl = (unsigned short)(sc[kt] & 7);
+                const u16x2 sh2 = {sh, sh}, sl2 = {sl, sl};
+                const uint32_t q4[4] = {qs.x, qs.y, qs.z, qs.w};
+                v4i b1, b2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const u16x2 nib = __builtin_bit_cast(u16x2, (q4[e] >> sft) & 0x0f0f0f0fu);   // four codes
+                    b1[e] = __builtin_bit_cast(int, nib * sh2);
+                    b2[e] = __builtin_bit_cast(int, nib * sl2);
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int e = I[r];
-                    V[i][r] = __mul24(sc[kt], e) + V[i][r];   // v_mad_i32_i24
-                    // pin the running sum: left to itself the compiler
-                    // re-associates the accumulation across K-steps and
-                    // keeps the products of several steps live
-                    asm volatile("" : "+v"(V[i][r]));
+                for (int i = 0; i < TI; ++i) {
+                    const v4i a = as_v4i(rd16(sb + xa + XROW * 32 * i + 32 * kt + 16 * lh));
+                    A1[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, A1[i], 0, 0, 0);
+                    A2[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b2, A2[i], 0, 0, 0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                I = In;
             }
             float dw = half_lo(dd), ndm = -half_hi(dd);
             // keep the f32 values (an f16 operand would make each fold FMA a
@@ -467,7 +448,8 @@ __device__ __forceinline__ void matmul_k_body(const uint8_t *__restrict__ w, con
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const int r = 4 * a4 + c;
-                        const float tt = fmaf(ndm, mn[r], (float)V[i][r] * dw);
+                        const int V = A1[i][r] * 8 + A2[i][r];   // |V| < 2^25
+                        const float tt = fmaf(ndm, mn[r], (float)V * dw);
                         acc[i][r] = fmaf(tt, d8[c], acc[i][r]);
                     }
                 }

@@ -453,8 +453,9 @@ def bench_prefill(args, torch, q, synth):
                               "traffic": committed_traffic("k_matmul_q6_k", "2048x12288x4096")})
 
 
-# The other decode workloads, one matvec launch each, weights rotated like the
-# headline's: the Q8_0 set of one 7B-style layer (fused QKV and gate+up share
+# The other decode workloads, one matvec launch each (and, for the formats with
+# a fused entry point, the fused quantize + matvec step beside it, with no
+# quantized-row output), weights rotated like the headline's: the Q8_0 set of one 7B-style layer (fused QKV and gate+up share
 # the 4096-wide activation, down takes an independent 11008-wide one), Q2_K,
 # the K-quants of q4_K_M files and the other 32-value formats.  (format, N, K, workload id, weight
 # stream, activation stream, name); the ids seed the synthetic inputs.
@@ -489,14 +490,24 @@ def bench_matvec_configs(args, torch, q, synth):
         y = torch.empty(N, dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
         mv = q.MATVEC[fmt]
-        t = time_kernels(torch, [lambda i: mv(wqs[i % copies], xq, y, N, K)], copies, max(200, args.steps))[0]
+        launches = [lambda i: mv(wqs[i % copies], xq, y, N, K)]
+        fz = q.QUANTIZE_MATVEC.get(fmt)
+        if fz is not None:
+            # the decode step from the f32 activation: one fused launch
+            launches.append(lambda i: fz(wqs[i % copies], x, None, y, N, K))
+        ts = time_kernels(torch, launches, copies, max(200, args.steps))
+        t = ts[0]
         ms = t["mean"]
         gbs = wbytes / (ms * 1e-3) / 1e9
         log(f"matvec {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM) over "
-            f"{copies} weight copies")
-        rows.append({"workload": name, "format": fmt, "N": N, "K": K, "weight_bytes": wbytes,
-                     "kernel_us_mean": round(ms * 1e3, 3), "kernel_us": us(t),
-                     "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+            f"{copies} weight copies" + (f"; fused step {ts[1]['mean'] * 1e3:.2f} us" if fz is not None else ""))
+        row = {"workload": name, "format": fmt, "N": N, "K": K, "weight_bytes": wbytes,
+               "kernel_us_mean": round(ms * 1e3, 3), "kernel_us": us(t),
+               "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if fz is not None:
+            row["fused_step_us_mean"] = round(ts[1]["mean"] * 1e3, 3)
+            row["fused_step_us"] = us(ts[1])
+        rows.append(row)
         del wqs, wq0
         torch.cuda.empty_cache()
     # embedding rows: 2048 token ids into a Q4_0 table of 151936 x 896 (the
